@@ -1,0 +1,367 @@
+"""graph_mini_pipeline_amd -- Python binding of libgnnmb.so, the MI355X (gfx950) GNN mini-batch path.
+
+Argument marshalling only: torch tensors become device pointers and the current torch stream
+becomes the hipStream_t.  Every step of the path (sampling, relabel, gather, aggregation) runs in
+the library's HIP kernels; torch supplies device memory and streams.  The functions carry the C
+names of include/gnnmb.h and raise GnnError on a negative status.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _abi
+from ._abi import (GNN_ERR_CAPACITY, GNN_ERR_HIP, GNN_ERR_INTERNAL, GNN_ERR_INVALID_ARG,  # noqa
+                   GNN_ERR_OUT_OF_RANGE, GNN_ERR_UNSUPPORTED, GNN_MAX_HOPS, GNN_OK, GNN_SYNC,
+                   GNN_TIMER_EVENTS)
+
+__all__ = [
+    "GnnError", "DeviceGraph", "Blocks", "MinibatchOut", "FeatureStore", "Timer", "Options",
+    "gnn_status_string", "gnn_batch_seed", "gnn_capacity", "gnn_workspace_size", "gnn_sample_khop",
+    "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
+    "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_minibatch",
+    "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
+    "gnn_timer_elapsed", "lib",
+]
+
+lib = _abi.lib
+
+
+class GnnError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {gnn_status_string(status)} ({status})")
+
+
+def _ok(status: int, what: str) -> None:
+    if status != GNN_OK:
+        raise GnnError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _need(t: torch.Tensor, dtype, name: str, device=True) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+def gnn_status_string(status: int) -> str:
+    return lib().gnn_status_string(status).decode()
+
+
+def gnn_batch_seed(rng_seed: int, b: int) -> int:
+    return int(lib().gnn_batch_seed(rng_seed & 0xFFFFFFFFFFFFFFFF, b))
+
+
+@dataclass
+class Options:
+    group_max_deg: int = 0
+    wave_max_deg: int = 0
+    sync: bool = False
+
+    def c(self) -> _abi.gnn_options:
+        o = _abi.gnn_options()
+        o.group_max_deg = self.group_max_deg
+        o.wave_max_deg = self.wave_max_deg
+        o.flags = GNN_SYNC if self.sync else 0
+        return o
+
+
+@dataclass
+class DeviceGraph:
+    """CSR by destination in device memory (indptr int32 or int64, indices int32)."""
+    num_nodes: int
+    indptr: torch.Tensor
+    indices: torch.Tensor
+
+    def c(self) -> _abi.gnn_graph:
+        _need(self.indices, torch.int32, "indices")
+        if self.indptr.dtype not in (torch.int32, torch.int64) or not self.indptr.is_cuda:
+            raise TypeError("indptr: int32 or int64 device tensor")
+        g = _abi.gnn_graph()
+        g.num_nodes = self.num_nodes
+        g.num_edges = self.indices.numel()
+        g.indptr = self.indptr.data_ptr()
+        g.indptr_bytes = self.indptr.element_size()
+        g.indices = self.indices.data_ptr() if self.indices.numel() else None
+        return g
+
+
+def gnn_capacity(n_seeds: int, fanouts: Sequence[int], num_nodes: int) -> _abi.gnn_caps:
+    caps = _abi.gnn_caps()
+    fo = (ctypes.c_int32 * len(fanouts))(*fanouts)
+    _ok(lib().gnn_capacity(n_seeds, fo, len(fanouts), num_nodes, ctypes.byref(caps)), "gnn_capacity")
+    return caps
+
+
+def gnn_workspace_size(caps: _abi.gnn_caps, num_nodes: int, group: int = 1) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(lib().gnn_workspace_size(ctypes.byref(caps), num_nodes, group, ctypes.byref(n)),
+        "gnn_workspace_size")
+    return int(n.value)
+
+
+def gnn_relabel_workspace_size(id_bound: int) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(lib().gnn_relabel_workspace_size(id_bound, ctypes.byref(n)), "gnn_relabel_workspace_size")
+    return int(n.value)
+
+
+class Blocks:
+    """Device buffers of the K blocks of one batch, allocated at the given caps."""
+
+    def __init__(self, caps: _abi.gnn_caps, device="cuda"):
+        self.caps = caps
+        K = caps.num_hops
+        i32 = torch.int32
+        self.counts = torch.zeros(2 * K, dtype=torch.int64, device=device)
+        self.indptr, self.gid, self.lid, self.dst_lid, self.nodes = [], [], [], [], []
+        for l in range(K):
+            self.indptr.append(torch.empty(caps.frontier[l] + 1, dtype=i32, device=device))
+            self.gid.append(torch.empty(max(caps.edges[l], 1), dtype=i32, device=device))
+            self.lid.append(torch.empty(max(caps.edges[l], 1), dtype=i32, device=device))
+            self.dst_lid.append(torch.empty(max(caps.frontier[l], 1), dtype=i32, device=device))
+            self.nodes.append(torch.empty(max(caps.nodes[l], 1), dtype=i32, device=device))
+
+    def c(self) -> _abi.gnn_blocks:
+        b = _abi.gnn_blocks()
+        b.caps = self.caps
+        for l in range(self.caps.num_hops):
+            h = b.hop[l]
+            h.indptr = self.indptr[l].data_ptr()
+            h.gid = self.gid[l].data_ptr()
+            h.lid = self.lid[l].data_ptr()
+            h.dst_lid = self.dst_lid[l].data_ptr()
+            h.nodes = self.nodes[l].data_ptr()
+        b.counts = self.counts.data_ptr()
+        return b
+
+    def host(self):
+        """Per-hop (indptr, gid, lid, dst_lid, nodes) trimmed to the device counts (syncs)."""
+        cnt = self.counts.cpu().tolist()
+        out = []
+        F = self.caps.n_seeds
+        for l in range(self.caps.num_hops):
+            E, V = cnt[2 * l], cnt[2 * l + 1]
+            out.append((self.indptr[l][:F + 1].cpu().numpy(), self.gid[l][:E].cpu().numpy(),
+                        self.lid[l][:E].cpu().numpy(), self.dst_lid[l][:F].cpu().numpy(),
+                        self.nodes[l][:V].cpu().numpy()))
+            F = V
+        return out
+
+
+def gnn_sample_khop(graph: DeviceGraph, seeds: torch.Tensor, fanouts: Sequence[int], seed64: int,
+                    blocks: Blocks, ws: torch.Tensor, opts: Optional[Options] = None,
+                    stream=None) -> int:
+    _need(seeds, torch.int32, "seeds")
+    g = graph.c()
+    b = blocks.c()
+    fo = (ctypes.c_int32 * len(fanouts))(*fanouts)
+    o = opts.c() if opts else None
+    st = lib().gnn_sample_khop(ctypes.byref(g), _ptr(seeds) if seeds.numel() else None,
+                               seeds.numel(), fo, len(fanouts), seed64 & 0xFFFFFFFFFFFFFFFF,
+                               ctypes.byref(b), _ptr(ws), ws.numel() * ws.element_size(),
+                               ctypes.byref(o) if o else None, _stream(stream))
+    _ok(st, "gnn_sample_khop")
+    return st
+
+
+def gnn_unique_relabel(keep: torch.Tensor, add: torch.Tensor, id_bound: int, uniq: torch.Tensor,
+                       d_n_uniq: torch.Tensor, add_lid: torch.Tensor, keep_lid: torch.Tensor,
+                       ws: torch.Tensor, d_n_add: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    for t, n in ((keep, "keep"), (add, "add"), (uniq, "uniq"), (add_lid, "add_lid"),
+                 (keep_lid, "keep_lid")):
+        _need(t, torch.int32, n)
+    _need(d_n_uniq, torch.int64, "d_n_uniq")
+    st = lib().gnn_unique_relabel(_ptr(keep), keep.numel(), _ptr(add), _ptr(d_n_add), add.numel(),
+                                  id_bound, _ptr(uniq), uniq.numel(), _ptr(d_n_uniq), _ptr(add_lid),
+                                  _ptr(keep_lid), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    _ok(st, "gnn_unique_relabel")
+
+
+class FeatureStore:
+    """Owns a gnn_feature_store handle; keeps the table (and hot order) tensors alive."""
+
+    def __init__(self, handle: ctypes.c_void_p, table: torch.Tensor, d: int, ld: int):
+        self.handle = handle
+        self.table = table
+        self.d = d
+        self.ld = ld
+
+    def close(self):
+        if self.handle:
+            lib().gnn_feature_store_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gnn_feature_store_create(table: torch.Tensor, d: int, cache_rows: int = 0,
+                             hot_order: Optional[torch.Tensor] = None) -> FeatureStore:
+    """table: float32 [N, ld] on the device, or pinned host memory (table.is_pinned())."""
+    on_host = not table.is_cuda
+    if on_host and not table.is_pinned():
+        raise ValueError("a host feature table must be pinned")
+    _need(table, torch.float32, "table", device=not on_host)
+    if hot_order is not None:
+        _need(hot_order, torch.int32, "hot_order")
+    h = ctypes.c_void_p()
+    st = lib().gnn_feature_store_create(_ptr(table), 1 if on_host else 0, table.shape[0], d,
+                                        table.shape[1], cache_rows, _ptr(hot_order),
+                                        ctypes.byref(h))
+    _ok(st, "gnn_feature_store_create")
+    return FeatureStore(h, table, d, table.shape[1])
+
+
+def gnn_feature_store_destroy(fs: FeatureStore) -> None:
+    fs.close()
+
+
+def gnn_gather_features(fs: FeatureStore, ids: torch.Tensor, out: torch.Tensor,
+                        d_n: Optional[torch.Tensor] = None, d_hits: Optional[torch.Tensor] = None,
+                        d_status: Optional[torch.Tensor] = None, stream=None) -> None:
+    _need(ids, torch.int32, "ids")
+    _need(out, torch.float32, "out")
+    if out.dim() != 2 or out.shape[0] < ids.numel():
+        raise ValueError("out: [>= len(ids), ld_out]")
+    st = lib().gnn_gather_features(fs.handle, _ptr(ids), _ptr(d_n), ids.numel(), _ptr(out),
+                                   out.shape[1], _ptr(d_hits), _ptr(d_status), _stream(stream))
+    _ok(st, "gnn_gather_features")
+
+
+def gnn_mean_aggregate(indptr: torch.Tensor, lid: torch.Tensor, src: torch.Tensor, d: int,
+                       out: torch.Tensor, d_n_dst: Optional[torch.Tensor] = None,
+                       d_status: Optional[torch.Tensor] = None, stream=None) -> None:
+    _need(indptr, torch.int32, "indptr")
+    _need(lid, torch.int32, "lid")
+    _need(src, torch.float32, "src")
+    _need(out, torch.float32, "out")
+    n_dst = indptr.numel() - 1
+    if out.shape[0] < n_dst:
+        raise ValueError("out has fewer rows than destinations")
+    st = lib().gnn_mean_aggregate(_ptr(indptr), _ptr(lid), lid.numel(), _ptr(d_n_dst), n_dst,
+                                  _ptr(src), src.shape[1], src.shape[0], d, _ptr(out),
+                                  out.shape[1], _ptr(d_status), _stream(stream))
+    _ok(st, "gnn_mean_aggregate")
+
+
+class MinibatchOut:
+    """Blocks plus X and h_0..h_{K-1} of one (sub-)batch."""
+
+    def __init__(self, caps: _abi.gnn_caps, d: int, ld_h: Optional[int] = None, device="cuda"):
+        self.blocks = Blocks(caps, device)
+        self.d = d
+        self.ld_h = ld_h if ld_h is not None else (d + 3) // 4 * 4
+        K = caps.num_hops
+        f32 = torch.float32
+        self.x = torch.empty(max(caps.nodes[K - 1], 1), self.ld_h, dtype=f32, device=device)
+        self.h = [torch.empty(max(caps.n_seeds if l == 0 else caps.nodes[l - 1], 1), self.ld_h,
+                              dtype=f32, device=device) for l in range(K)]
+
+    def c(self) -> _abi.gnn_minibatch_out:
+        m = _abi.gnn_minibatch_out()
+        m.blocks = self.blocks.c()
+        m.x = self.x.data_ptr()
+        for l, t in enumerate(self.h):
+            m.h[l] = t.data_ptr()
+        m.ld_h = self.ld_h
+        return m
+
+
+class Timer:
+    def __init__(self, n_records: int):
+        h = ctypes.c_void_p()
+        _ok(lib().gnn_timer_create(n_records, ctypes.byref(h)), "gnn_timer_create")
+        self.handle = h
+        self.n_records = n_records
+
+    def reset(self):
+        _ok(lib().gnn_timer_reset(self.handle), "gnn_timer_reset")
+
+    def elapsed(self):
+        """List of per-call stage times in ms: [sample+relabel, gather, outer mean, other means]."""
+        n = ctypes.c_int32(0)
+        buf = (ctypes.c_float * (self.n_records * (GNN_TIMER_EVENTS - 1)))()
+        _ok(lib().gnn_timer_elapsed(self.handle, ctypes.byref(n), buf), "gnn_timer_elapsed")
+        k = GNN_TIMER_EVENTS - 1
+        return [list(buf[r * k:(r + 1) * k]) for r in range(n.value)]
+
+    def close(self):
+        if self.handle:
+            lib().gnn_timer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gnn_timer_create(n_records: int) -> Timer:
+    return Timer(n_records)
+
+
+def gnn_timer_destroy(t: Timer) -> None:
+    t.close()
+
+
+def gnn_timer_reset(t: Timer) -> None:
+    t.reset()
+
+
+def gnn_timer_elapsed(t: Timer):
+    return t.elapsed()
+
+
+def gnn_minibatch(graph: DeviceGraph, fs: FeatureStore, seeds: torch.Tensor,
+                  batch_ptr: Sequence[int], fanouts: Sequence[int], seed64: int,
+                  outs: List[MinibatchOut], ws: torch.Tensor, opts: Optional[Options] = None,
+                  stream=None, timer: Optional[Timer] = None) -> int:
+    _need(seeds, torch.int32, "seeds")
+    G = len(batch_ptr) - 1
+    if len(outs) != G:
+        raise ValueError("one MinibatchOut per sub-batch")
+    g = graph.c()
+    bp = (ctypes.c_int64 * (G + 1))(*batch_ptr)
+    fo = (ctypes.c_int32 * len(fanouts))(*fanouts)
+    mo = (_abi.gnn_minibatch_out * G)(*[o.c() for o in outs])
+    o = opts.c() if opts else None
+    st = lib().gnn_minibatch(ctypes.byref(g), fs.handle, _ptr(seeds) if seeds.numel() else None,
+                             bp, G, fo, len(fanouts), seed64 & 0xFFFFFFFFFFFFFFFF, mo, _ptr(ws),
+                             ws.numel() * ws.element_size(), ctypes.byref(o) if o else None,
+                             _stream(stream), timer.handle if timer else None)
+    _ok(st, "gnn_minibatch")
+    return st
+
+
+def gnn_read_device_status(ws: torch.Tensor, stream=None) -> int:
+    out = ctypes.c_int32(0)
+    _ok(lib().gnn_read_device_status(_ptr(ws), _stream(stream), ctypes.byref(out)),
+        "gnn_read_device_status")
+    return int(out.value)

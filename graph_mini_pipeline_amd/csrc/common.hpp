@@ -1,0 +1,202 @@
+// Shared device/host helpers of the gfx950 mini-batch library (internal; not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gnnmb.h"
+
+namespace gnnmb {
+
+// SplitMix64 increment (odd integer nearest 2^64 / golden ratio).
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ULL;
+
+// SplitMix64 output function (Steele, Lea, Flood, OOPSLA 2014).  The pages fix no generator; this
+// hash makes the neighbour draw deterministic and counter-based.
+__host__ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+// Division of n < 2^32 by a fixed divisor with one multiply-high and a shift (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", PLDI 1994, round-up variant):
+// s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1, q = (mulhi(n, m) + n) >> s.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    const uint64_t m = (((1ull << 32) * ((1ull << s) - d)) / d) + 1;
+    return FastDiv{d, static_cast<uint32_t>(m), s};
+}
+
+__host__ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+    const uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> 32);
+    return static_cast<uint32_t>((static_cast<uint64_t>(t) + n) >> f.s);
+}
+
+// First device error wins; later ones are dropped.  A NULL status word drops every error.
+__device__ __forceinline__ void set_status(int32_t *st, int32_t code) {
+    if (st != nullptr) atomicCAS(st, 0, code);
+}
+
+__device__ __forceinline__ int64_t load_count(const int64_t *d_n, int64_t cap) {
+    if (d_n == nullptr) return cap;
+    const int64_t n = *d_n;
+    return n < 0 ? 0 : (n < cap ? n : cap);
+}
+
+__device__ __forceinline__ int64_t row_ptr(const void *indptr, int ib, int64_t v) {
+    return ib == 8 ? static_cast<const int64_t *>(indptr)[v]
+                   : static_cast<int64_t>(static_cast<const int32_t *>(indptr)[v]);
+}
+
+// Orders LDS traffic between lanes of one wavefront (compiler code-motion barrier plus
+// wavefront-scope fences; LDS operations of one wavefront execute in order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x & 63u); }
+
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const T t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Exclusive scan over a workgroup of NT threads; `smem` holds NT/64 entries.  Every thread of
+// the workgroup must call it.  Returns the exclusive prefix; *total receives the block total.
+template <typename T, int NT>
+__device__ __forceinline__ T block_exclusive_scan(T v, T *total, T *smem) {
+    constexpr int NW = NT / 64;
+    const int lane = lane_id();
+    const int w = static_cast<int>(threadIdx.x >> 6);
+    const T inc = wave_inclusive_scan(v);
+    if (lane == 63) smem[w] = inc;
+    __syncthreads();
+    T before = T(0), tot = T(0);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const T s = smem[i];
+        if (i < w) before += s;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + inc - v;
+}
+
+// ---- launch helpers (host) ----------------------------------------------------------------------
+
+inline unsigned grid_for(int64_t items, int per_block, unsigned max_blocks) {
+    int64_t b = (items + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > static_cast<int64_t>(max_blocks)) b = max_blocks;
+    return static_cast<unsigned>(b);
+}
+
+// Degree classes of the sampler.
+enum : int32_t { kFull = 0, kGroup = 1, kWave = 2, kBlock = 3, kNumClasses = 4 };
+
+// Candidate capacities per class (LDS) and the fanout each supports (capacity >= 4 * fanout).
+constexpr int kGroupLanes = 16;
+constexpr int kGroupCap = 128;
+constexpr int kWaveCap = 512;
+constexpr int kBlockThreads = 512;
+constexpr int kBlockCap = 4096;
+constexpr int kMaxFanout = kBlockCap / 4;
+
+// One sampling hop.
+struct HopArgs {
+    const void *indptr;
+    const int32_t *indices;
+    int64_t num_nodes;
+    const int32_t *front;   // destinations V_{l-1}
+    const int64_t *d_F;     // device count of front (NULL: F_cap)
+    int64_t F_cap;
+    int32_t ib;             // indptr bytes
+    int32_t k;              // fanout
+    uint64_t hop_seed;
+    int32_t group_max, wave_max;
+    int32_t *blk_indptr;    // [F_cap+1]
+    int32_t *blk_gid;       // [E_cap]
+    int64_t E_cap;
+    int64_t *d_E;           // receives |E_l|
+    int32_t *packed;        // [F_cap] (c << 2) | class
+    int32_t *lists;         // [4 * F_cap] class work-lists
+    uint32_t *bsum_c;       // [nb] per-block edge counts, then offsets
+    uint32_t *bsum_cls;     // [4 * nb] per-block class counts, then offsets
+    uint32_t *class_count;  // [4]
+    uint32_t *work;         // [4] dynamic work counters
+    int32_t *status;
+    int32_t nb;             // classify blocks
+};
+
+// One relabel: uniq = ascending unique of keep and add, with ranks.
+struct RelabelArgs {
+    const int32_t *keep;
+    const int64_t *d_keep;
+    int64_t keep_cap;
+    const int32_t *add;
+    const int64_t *d_add;
+    int64_t add_cap;
+    int64_t id_bound;
+    uint32_t *bitmap;   // [W]
+    uint32_t *wprefix;  // [W]
+    uint32_t *bsum;     // [nbw]
+    int64_t W;
+    int32_t nbw;
+    int32_t *uniq;
+    int64_t uniq_cap;
+    int64_t *d_uniq;
+    int32_t *add_lid;
+    int32_t *keep_lid;
+    int32_t *status;
+    int32_t check_dup_keep;
+};
+
+constexpr int kClassifyThreads = 256;
+constexpr int kClassifyItems = 4;
+constexpr int kClassifyTile = kClassifyThreads * kClassifyItems;
+constexpr int kBitmapThreads = 256;
+constexpr int kBitmapWordsPerThread = 8;
+constexpr int kBitmapTile = kBitmapThreads * kBitmapWordsPerThread;
+
+// Kernel launchers (each returns hipGetLastError()).
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);
+hipError_t launch_classify(const HopArgs &a, hipStream_t s);
+hipError_t launch_sample(const HopArgs &a, hipStream_t s);
+hipError_t launch_relabel(const RelabelArgs &a, hipStream_t s);
+hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
+                         int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
+                         int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
+                         int32_t *status, hipStream_t s);
+hipError_t launch_mean(const int32_t *indptr, const int32_t *lid, int64_t e_cap,
+                       const int64_t *d_n, int64_t n_cap, const float *src, int64_t ld_src,
+                       int64_t n_src, int64_t d, float *out, int64_t ld_out, int32_t *status,
+                       hipStream_t s);
+hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t num_rows,
+                             const int32_t *hot, int64_t rows, float *cache, int32_t *slot,
+                             int32_t *status, hipStream_t s);
+
+}  // namespace gnnmb

@@ -1,0 +1,143 @@
+// Feature-row gather (gfx950): X[i, 0..d) = table row ids[i], bit for bit.
+//
+// GARDEN: Efficient GPU-Accelerated Billion-Scale GNN Training via Caching-Sampling-Batching
+// Co-Design, Sec. II.B ("Nfeat-selecting" is bandwidth-bound; misses of the GPU feature cache are
+// served from pinned host memory) and Sec. IV.B (hot feature rows cached in GPU memory); LEO:
+// Enabling Efficient Communication-Computation Pipeline for GNN via Hierarchical Caching,
+// Sec. 2.3 (GPU kernels read pinned host features directly, zero-copy).
+//
+// The (row, 16-byte chunk) pairs of the output are flattened and spread over all lanes, so
+// consecutive lanes read consecutive 16-byte chunks of a row and a wavefront moves 1 KiB per
+// instruction whatever the row length.  Each lane keeps U chunks in flight.  A row is read from
+// the HBM hot-row cache when slot[v] >= 0, else from the table (HBM, or pinned host memory through
+// its mapped device address).  HBM-bandwidth bound: no arithmetic.
+#include "common.hpp"
+
+namespace gnnmb {
+
+struct GatherArgs {
+    const float *table;
+    const float *cache;
+    const int32_t *slot;
+    int64_t ld;
+    int32_t d;
+    int64_t num_rows;
+    const int32_t *ids;
+    const int64_t *d_n;
+    int64_t n_cap;
+    float *out;
+    int64_t ld_out;
+    int64_t *d_hits;
+    int32_t *status;
+    FastDiv cpr;  // chunks per row
+};
+
+template <int VEC, int U>
+__global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
+    using vec_t = typename std::conditional<VEC == 4, float4, float>::type;
+    const int64_t n = load_count(g.d_n, g.n_cap);
+    const uint32_t total = static_cast<uint32_t>(n) * g.cpr.d;
+    const uint32_t stride = gridDim.x * 256u * U;
+    uint32_t hits = 0;
+    for (uint32_t base = blockIdx.x * 256u * U + threadIdx.x; base < total; base += stride) {
+        vec_t val[U];
+        float *dst[U];
+        int rem[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t idx = base + u * 256u;
+            dst[u] = nullptr;
+            rem[u] = 0;
+            if (idx < total) {
+                const uint32_t row = fast_div(idx, g.cpr);
+                const uint32_t ch = idx - row * g.cpr.d;
+                const int32_t v = g.ids[row];
+                if (v < 0 || v >= g.num_rows) {
+                    set_status(g.status, GNN_ERR_OUT_OF_RANGE);
+                    continue;
+                }
+                const float *src;
+                const int32_t sl = g.slot ? g.slot[v] : -1;
+                if (sl >= 0) {
+                    src = g.cache + static_cast<int64_t>(sl) * g.ld;
+                    hits += ch == 0;
+                } else {
+                    src = g.table + static_cast<int64_t>(v) * g.ld;
+                }
+                const int col = static_cast<int>(ch) * VEC;
+                dst[u] = g.out + static_cast<int64_t>(row) * g.ld_out + col;
+                rem[u] = g.d - col;
+                if (VEC == 1 || rem[u] >= VEC) {
+                    val[u] = *reinterpret_cast<const vec_t *>(src + col);
+                } else {
+                    float t[4] = {0.f, 0.f, 0.f, 0.f};
+                    for (int q = 0; q < rem[u]; ++q) t[q] = src[col + q];
+                    if constexpr (VEC == 4) val[u] = make_float4(t[0], t[1], t[2], t[3]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (dst[u] == nullptr) continue;
+            if (VEC == 1 || rem[u] >= VEC) {
+                *reinterpret_cast<vec_t *>(dst[u]) = val[u];
+            } else if constexpr (VEC == 4) {
+                const float t[4] = {val[u].x, val[u].y, val[u].z, val[u].w};
+                for (int q = 0; q < rem[u]; ++q) dst[u][q] = t[q];
+            }
+        }
+    }
+    if (g.d_hits) {
+        hits = wave_sum(hits);
+        if (lane_id() == 0 && hits) atomicAdd(reinterpret_cast<unsigned long long *>(g.d_hits),
+                                              static_cast<unsigned long long>(hits));
+    }
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
+                         int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
+                         int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
+                         int32_t *status, hipStream_t s) {
+    if (n_cap <= 0 || d <= 0) return hipSuccess;
+    const bool v4 = ld % 4 == 0 && ld_out % 4 == 0 && aligned16(table) && aligned16(out) &&
+                    (cache == nullptr || aligned16(cache));
+    const int vec = v4 ? 4 : 1;
+    const int64_t cpr = (d + vec - 1) / vec;
+    GatherArgs g{table, cache, slot, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
+                 out, ld_out, d_hits, status, make_fastdiv(static_cast<uint32_t>(cpr))};
+    constexpr int U = 4;
+    const unsigned grid = grid_for(n_cap * cpr, 256 * U, 2048);
+    if (v4) hipLaunchKernelGGL((k_gather<4, U>), dim3(grid), dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_gather<1, U>), dim3(grid), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+// Setup: cache[r] = table row hot[r]; slot[hot[r]] = r.
+__global__ __launch_bounds__(256) void k_cache_fill(const float *table, int64_t ld, int64_t d,
+                                                   int64_t num_rows, const int32_t *hot,
+                                                   int64_t rows, float *cache, int32_t *slot,
+                                                   int32_t *status) {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const int32_t v = hot[r];
+        if (v < 0 || v >= num_rows) {
+            if (threadIdx.x == 0) set_status(status, GNN_ERR_OUT_OF_RANGE);
+            continue;
+        }
+        for (int64_t t = threadIdx.x; t < d; t += blockDim.x)
+            cache[r * ld + t] = table[static_cast<int64_t>(v) * ld + t];
+        if (threadIdx.x == 0) slot[v] = static_cast<int32_t>(r);
+    }
+}
+
+hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t num_rows,
+                             const int32_t *hot, int64_t rows, float *cache, int32_t *slot,
+                             int32_t *status, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_cache_fill, dim3(grid_for(rows, 1, 65536)), dim3(256), 0, s, table, ld,
+                       d, num_rows, hot, rows, cache, slot, status);
+    return hipGetLastError();
+}
+
+}  // namespace gnnmb

@@ -1,0 +1,273 @@
+/*
+ * gnnmb.h -- C ABI of the MI355X (gfx950) sampling-based GNN mini-batch hot path.
+ *
+ * The path is the per-iteration pipeline that the three source pages share:
+ *   GARDEN: Efficient GPU-Accelerated Billion-Scale GNN Training via Caching-Sampling-Batching
+ *     Co-Design -- Sec. II.A eq. (1) (mean AGGREGATE over in-neighbours), Sec. II.B with Fig. 1
+ *     (layer-wise sampling, one bipartite block per layer), Sec. IV.B (feature cache with pinned
+ *     host fallback), Sec. IV.C (grouping-based parallel sampler, full vs random nodes), Sec. IV.D
+ *     with Alg. 1 (super-batch degree classifier);
+ *   LEO: Enabling Efficient Communication-Computation Pipeline for GNN via Hierarchical Caching --
+ *     Sec. 2.2 (sample, extract features, train) and Sec. 2.3 (zero-copy feature reads from pinned
+ *     host memory);
+ *   FastGL: A GPU-Efficient Framework for Accelerating Sampling-Based GNN Training at Large Scale --
+ *     the sample / ship features / compute iteration and the Fused-Map id remapping.
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers unless marked "host".  The caller allocates and owns every
+ *    input, output and workspace buffer; the library keeps no pointer after a call returns, except
+ *    that a feature store borrows its table.  No call allocates device memory on the hot path.
+ *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and return without
+ *    waiting.  Outputs are valid once the stream has been synchronised.  Data-dependent sizes stay
+ *    in device memory ("counts").
+ *  - Host-checkable errors return a negative gnn_status and enqueue nothing.  Errors found on the
+ *    device (an id out of range, a duplicate seed, a buffer too small) are written to a status
+ *    word in the workspace; read it with gnn_read_device_status.  After any error the output
+ *    contents are unspecified.  No exception crosses the ABI and the library never aborts.
+ *  - Node ids are int32 (num_nodes < 2^31).  Block-local sizes are int32.
+ *  - Concurrent calls on different streams are safe when their workspaces are disjoint.
+ */
+#ifndef GNNMB_H
+#define GNNMB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GNN_MAX_HOPS 8
+
+typedef int32_t gnn_status;
+#define GNN_OK 0
+#define GNN_ERR_INVALID_ARG (-1)  /* bad argument, or a duplicate seed (device) */
+#define GNN_ERR_CAPACITY (-2)     /* an output or workspace buffer is too small */
+#define GNN_ERR_OUT_OF_RANGE (-3) /* a node id outside [0, num_nodes) (device) */
+#define GNN_ERR_HIP (-4)          /* a HIP runtime call failed */
+#define GNN_ERR_UNSUPPORTED (-5)  /* a size or option this build does not handle */
+#define GNN_ERR_INTERNAL (-6)     /* a device-side invariant failed (never expected) */
+
+typedef void *gnn_stream; /* hipStream_t */
+
+/* Flags for gnn_options.flags. */
+#define GNN_SYNC 1u /* synchronise the stream at the end of the call and return the device status */
+
+/*
+ * Graph in CSR form by destination: row v lists the sources u of the edges (u, v), which is the
+ * neighbourhood N(v) = {u | (u, v) in E} of GARDEN Sec. II.A.  Borrowed, read-only.
+ */
+typedef struct gnn_graph {
+    int64_t num_nodes;     /* N */
+    int64_t num_edges;     /* |E| = indptr[N] */
+    const void *indptr;    /* [N+1], int32 or int64 (indptr_bytes) */
+    int32_t indptr_bytes;  /* 4 or 8 */
+    const int32_t *indices; /* [num_edges] neighbour ids */
+} gnn_graph;
+
+/* Worst-case element counts per hop, l = 1..K at index l-1. */
+typedef struct gnn_caps {
+    int32_t num_hops;                /* K */
+    int64_t n_seeds;                 /* |V_0| */
+    int64_t frontier[GNN_MAX_HOPS];  /* |V_{l-1}| bound: destinations of block l */
+    int64_t edges[GNN_MAX_HOPS];     /* |E_l| bound: sampled edges of block l */
+    int64_t nodes[GNN_MAX_HOPS];     /* |V_l| bound: sources of block l */
+} gnn_caps;
+
+/*
+ * Block l (GARDEN Sec. II.B, Fig. 1): destinations V_{l-1}, sources V_l.  Arrays sized by the caps
+ * the caller allocated with (gnn_blocks.caps).
+ */
+typedef struct gnn_block {
+    int32_t *indptr;  /* [frontier+1] destination i owns edges [indptr[i], indptr[i+1]) */
+    int32_t *gid;     /* [edges] global id of each sampled neighbour, ascending CSR position
+                         within a destination */
+    int32_t *lid;     /* [edges] index of gid[e] in nodes (V_l) */
+    int32_t *dst_lid; /* [frontier] index of destination i (V_{l-1}[i]) in nodes (V_l) */
+    int32_t *nodes;   /* [nodes] V_l: ascending unique global ids of V_{l-1} and gid */
+} gnn_block;
+
+typedef struct gnn_blocks {
+    gnn_caps caps;                 /* the sizes the arrays below were allocated with */
+    gnn_block hop[GNN_MAX_HOPS];   /* hop[l-1] = block l */
+    int64_t *counts;               /* [2K] device: counts[2(l-1)] = |E_l|, counts[2(l-1)+1] = |V_l| */
+} gnn_blocks;
+
+/* Tuning knobs; results never depend on them.  NULL means defaults (all fields 0). */
+typedef struct gnn_options {
+    int32_t group_max_deg; /* degree bound of the 16-lane class (default 256) */
+    int32_t wave_max_deg;  /* degree bound of the one-wavefront class (default 4096); higher
+                              degrees take one workgroup per node */
+    uint32_t flags;        /* GNN_SYNC */
+    int32_t reserved[5];
+} gnn_options;
+
+/* Text for a status code (static storage). */
+const char *gnn_status_string(gnn_status s);
+
+/*
+ * Seed of batch b of a run seeded with rng_seed (a deterministic per-batch seed; the pages fix no
+ * generator, this is output b+1 of a SplitMix64 stream started at rng_seed).  Host function.
+ */
+uint64_t gnn_batch_seed(uint64_t rng_seed, uint64_t b);
+
+/*
+ * Worst-case sizes for K = num_hops hops from n_seeds seeds with the given fanouts (host array
+ * [num_hops], each >= 1), on a graph of num_nodes nodes: frontier[0] = n_seeds,
+ * edges[l] = frontier[l] * fanouts[l], nodes[l] = min(num_nodes, frontier[l] + edges[l]),
+ * frontier[l+1] = nodes[l].  Host function, writes *out (host).  GNN_ERR_INVALID_ARG on bad input,
+ * GNN_ERR_UNSUPPORTED if a size does not fit int32.
+ */
+gnn_status gnn_capacity(int64_t n_seeds, const int32_t *fanouts, int32_t num_hops,
+                        int64_t num_nodes, gnn_caps *out);
+
+/*
+ * Workspace bytes for gnn_sample_khop / gnn_minibatch with these caps on a graph of num_nodes
+ * nodes, for a super-batch of `group` sub-batches whose caps are all <= `caps` (group = 1 for a
+ * plain batch).  Writes *out_bytes (host).
+ */
+gnn_status gnn_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t group,
+                              size_t *out_bytes);
+
+/*
+ * k-hop neighbour sampling and relabel for one batch (GARDEN Sec. II.B, Fig. 1; Sec. IV.C; the
+ * draw is the bottom-k of per-edge SplitMix64 keys):
+ *   for l = 1..K, destinations V_{l-1} (V_0 = seeds, caller order):
+ *     destination i = node v keeps all of row v if deg(v) <= fanouts[l-1] (a "full node"),
+ *     otherwise the fanouts[l-1] positions j with the smallest (key(l, v, j), j), where
+ *     key(l, v, j) = mix64(s_{l,v} + G*(j+1)), s_{l,v} = mix64(mix64(seed64 + G*l) ^ v),
+ *     G = 0x9E3779B97F4A7C15 and mix64 is the SplitMix64 output function;
+ *     the chosen neighbours are listed in ascending position;
+ *     V_l = ascending unique of V_{l-1} and the sampled ids; lid / dst_lid are ranks in V_l.
+ * seeds: [n_seeds] distinct ids in [0, N).  fanouts: host [num_hops].  out: host struct whose
+ * device arrays hold at least out->caps; out->caps.n_seeds must equal n_seeds.
+ * ws: device workspace of ws_bytes >= gnn_workspace_size(&out->caps, N, 1).
+ * Device errors: GNN_ERR_OUT_OF_RANGE (seed outside [0,N)), GNN_ERR_INVALID_ARG (duplicate
+ * seed), GNN_ERR_CAPACITY (a count exceeds out->caps).
+ */
+gnn_status gnn_sample_khop(const gnn_graph *g, const int32_t *seeds, int64_t n_seeds,
+                           const int32_t *fanouts, int32_t num_hops, uint64_t seed64,
+                           gnn_blocks *out, void *ws, size_t ws_bytes,
+                           const gnn_options *opt, gnn_stream stream);
+
+/*
+ * Sort-unique relabel of two id lists (FastGL's id remapping; GARDEN Alg. 1 line 2 dedup):
+ *   uniq = ascending unique of keep[0..n_keep) and add[0..n_add);
+ *   keep_lid[i] = index of keep[i] in uniq, add_lid[e] = index of add[e] in uniq.
+ * Every id must lie in [0, id_bound).  n_add is the length of `add`, or, if d_n_add is not NULL,
+ * an upper bound and *d_n_add (device int64) the actual length.  *d_n_uniq (device int64)
+ * receives |uniq|.  uniq has room for cap_uniq ids.  ws: device workspace of ws_bytes >=
+ * gnn_relabel_workspace_size(id_bound).
+ * Device errors: GNN_ERR_OUT_OF_RANGE, GNN_ERR_CAPACITY.
+ */
+gnn_status gnn_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t *add,
+                              const int64_t *d_n_add, int64_t n_add, int64_t id_bound,
+                              int32_t *uniq, int64_t cap_uniq, int64_t *d_n_uniq,
+                              int32_t *add_lid, int32_t *keep_lid, void *ws, size_t ws_bytes,
+                              gnn_stream stream);
+
+gnn_status gnn_relabel_workspace_size(int64_t id_bound, size_t *out_bytes);
+
+/*
+ * Feature store: the table of node features (fp32, row-major, row stride ld >= d) in HBM, or in
+ * pinned host memory read zero-copy (LEO Sec. 2.3; GARDEN Sec. II.B misses served from pinned
+ * host memory), optionally with an HBM hot-row cache (GARDEN Sec. IV.B) holding the rows
+ * hot_order[0..cache_rows).
+ *   table: device pointer, or (table_on_host = 1) a host pointer allocated pinned and mapped
+ *     (hipHostMalloc); borrowed for the store's lifetime.
+ *   hot_order: device [cache_rows] distinct ids; may be NULL when cache_rows = 0.
+ * Setup call: allocates the cache and the id->slot map with hipMalloc and synchronises.
+ * Errors: GNN_ERR_INVALID_ARG, GNN_ERR_HIP (allocation or host mapping failed).
+ */
+typedef struct gnn_feature_store gnn_feature_store;
+gnn_status gnn_feature_store_create(const float *table, int32_t table_on_host, int64_t num_nodes,
+                                    int64_t d, int64_t ld, int64_t cache_rows,
+                                    const int32_t *hot_order, gnn_feature_store **out);
+gnn_status gnn_feature_store_destroy(gnn_feature_store *fs);
+
+/*
+ * Feature-row gather (GARDEN Sec. II.B "Nfeat-selecting"; LEO Sec. 2.2 feature extraction):
+ *   out[i, 0..d) = table row ids[i], bit for bit, for i < n.
+ * n is the number of ids, or, if d_n is not NULL, an upper bound and *d_n (device int64) the
+ * actual number.  out: device [n, ld_out], ld_out >= d.  With a cache, a row is read from the
+ * HBM cache when cached, else from the table; *d_hits (device int64, may be NULL) is increased by
+ * the number of cached rows read.
+ * Device errors: GNN_ERR_OUT_OF_RANGE (written to *d_status if not NULL).
+ */
+gnn_status gnn_gather_features(const gnn_feature_store *fs, const int32_t *ids,
+                               const int64_t *d_n, int64_t n, float *out, int64_t ld_out,
+                               int64_t *d_hits, int32_t *d_status, gnn_stream stream);
+
+/*
+ * Mean aggregation of one block (GARDEN Sec. II.A eq. (1) with AGGREGATE = mean):
+ *   out[i, 0..d) = (1/c_i) * sum_{e in [indptr[i], indptr[i+1])} src[lid[e], 0..d),
+ *   c_i = indptr[i+1] - indptr[i]; the zero vector when c_i = 0.  fp32 accumulation in
+ *   ascending e, then one division by c_i.
+ * n_dst is the number of destinations, or, if d_n_dst is not NULL, an upper bound and *d_n_dst
+ * (device int64) the actual number.  indptr: [n_dst+1]; lid: [n_lid] (edge offsets are clamped
+ * to n_lid); src: [n_src, ld_src]; out: [n_dst, ld_out].
+ * Device errors: GNN_ERR_INTERNAL if a lid lies outside [0, n_src) (written to *d_status if not
+ * NULL; that edge then reads row 0).
+ */
+gnn_status gnn_mean_aggregate(const int32_t *indptr, const int32_t *lid, int64_t n_lid,
+                              const int64_t *d_n_dst, int64_t n_dst, const float *src,
+                              int64_t ld_src, int64_t n_src, int64_t d, float *out,
+                              int64_t ld_out, int32_t *d_status, gnn_stream stream);
+
+/*
+ * Outputs of one (sub-)batch of gnn_minibatch.
+ *   x    = X = h_K: [caps.nodes[K-1], ld_h], row i = feature row of V_K[i];
+ *   h[l] = h_l for l = 0..K-1: h_0 is [n_seeds, ld_h] (seed order), h_l is [caps.nodes[l-1],
+ *          ld_h] (V_l order).
+ */
+typedef struct gnn_minibatch_out {
+    gnn_blocks blocks;
+    float *x;
+    float *h[GNN_MAX_HOPS];
+    int64_t ld_h;
+} gnn_minibatch_out;
+
+/*
+ * One mini-batch, or a super-batch of `group` sub-batches (GARDEN Sec. IV.D, Alg. 1), end to end:
+ * sampling and relabel for every hop (as gnn_sample_khop), the feature gather of V_K into x, then
+ * mean aggregation from h_K = x down to h_0 (UPDATE is the identity; no learnable weights).
+ *   seeds: device, the sub-batches' seeds concatenated; batch_ptr: host [group+1] offsets.
+ *   All sub-batches use the one seed64, so a node shared by two sub-batches at the same hop has
+ *   the same sample in both; each sub-batch's outputs equal a separate run with that seed64.
+ *   outs: host [group]; outs[g].blocks.caps.n_seeds = batch_ptr[g+1] - batch_ptr[g].
+ *   ws: ws_bytes >= gnn_workspace_size(caps >= every sub-batch's caps, N, group).
+ *   timer: NULL, or a timer that records the stage boundaries of this call (gnn_timer_*).
+ * Errors: as gnn_sample_khop and gnn_gather_features.
+ */
+typedef struct gnn_timer gnn_timer;
+gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const int32_t *seeds,
+                         const int64_t *batch_ptr, int32_t group, const int32_t *fanouts,
+                         int32_t num_hops, uint64_t seed64, gnn_minibatch_out *outs, void *ws,
+                         size_t ws_bytes, const gnn_options *opt, gnn_stream stream,
+                         gnn_timer *timer);
+
+/*
+ * Device status word of a workspace: synchronises `stream`, returns the first device error
+ * recorded by the last call that used ws (GNN_OK if none) in *out (host).
+ */
+gnn_status gnn_read_device_status(const void *ws, gnn_stream stream, gnn_status *out);
+
+/*
+ * Stage timer (HIP events recorded on the call's stream).  A gnn_minibatch call given a timer
+ * records GNN_TIMER_EVENTS events into the next free record: call start, end of sampling and
+ * relabel (all hops), end of the feature gather, end of the outermost block's mean aggregation,
+ * end of all aggregation.  gnn_timer_elapsed synchronises on the last recorded event and writes
+ * (GNN_TIMER_EVENTS-1) stage durations in milliseconds per record to ms (host
+ * [n_records*(GNN_TIMER_EVENTS-1)]); gnn_timer_reset rewinds to record 0.
+ */
+#define GNN_TIMER_EVENTS 5
+gnn_status gnn_timer_create(int32_t n_records, gnn_timer **out);
+gnn_status gnn_timer_destroy(gnn_timer *t);
+gnn_status gnn_timer_reset(gnn_timer *t);
+gnn_status gnn_timer_elapsed(gnn_timer *t, int32_t *n_records, float *ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GNNMB_H */

@@ -1,0 +1,317 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on small graphs and edge cases.
+
+Bit-exact: sampled blocks, relabel maps, gathered rows.  Aggregation: max |err| <= 1e-5 * max|X|
+per layer (fp32 sums of at most `fanout` terms against a double-accumulated reference).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+from tests import helpers as H
+from tests.gpu_util import compare_with_oracle, device_graph, device_table, run_minibatch
+
+pytestmark = pytest.mark.gpu
+
+gm = pytest.importorskip("graph_mini_pipeline_amd")
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = synth.CONFIGS["tiny"]
+    g = synth.build_graph(cfg)
+    x = torch.empty(cfg.num_nodes, cfg.d, dtype=torch.float32)
+    synth.make_features(cfg, x)
+    order = synth.epoch_seed_order(cfg)
+    return cfg, g.indptr.numpy(), g.indices.numpy(), x.numpy(), order.numpy()
+
+
+def _store(x, ld=None):
+    n, d = x.shape
+    ld = ld or (d + 3) // 4 * 4
+    return gm.gnn_feature_store_create(device_table(x, ld), d)
+
+
+@pytest.mark.parametrize("batch", [0, 1, 2, 38])
+def test_tiny_pipeline_matches_oracle(tiny, batch):
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    seeds = order[batch * cfg.batch:(batch + 1) * cfg.batch]
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, batch)
+    outs, st = run_minibatch(dg, fs, seeds, cfg.fanouts, seed64)
+    assert st == gm.GNN_OK
+    ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64)
+    compare_with_oracle(outs[0], ref, cfg.d)
+
+
+@pytest.mark.parametrize("group_max,wave_max", [(1, 1), (8, 32), (16, 100), (256, 4096),
+                                                (100000, 100000)])
+def test_degree_classes_do_not_change_results(tiny, group_max, wave_max):
+    # (1,1) sends every random node to the workgroup class, (100000,100000) to the 16-lane class
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    seeds = order[:cfg.batch]
+    seed64 = gm.gnn_batch_seed(7, 0)
+    outs, st = run_minibatch(dg, fs, seeds, [25, 10, 3], seed64,
+                             gm.Options(group_max_deg=group_max, wave_max_deg=wave_max))
+    assert st == gm.GNN_OK
+    ref = oracle.minibatch(indptr, indices, x, seeds, [25, 10, 3], seed64)
+    compare_with_oracle(outs[0], ref, cfg.d)
+
+
+@pytest.mark.parametrize("graph", ["star", "bigstar", "path", "complete", "hand", "random64"])
+@pytest.mark.parametrize("fanouts", [[1], [3, 3], [5, 2, 7], [25, 10]])
+def test_hand_graphs(graph, fanouts):
+    if graph == "star":
+        indptr, indices = H.star(40)
+    elif graph == "bigstar":
+        indptr, indices = H.star(20000)       # a hub far above every class bound
+    elif graph == "path":
+        indptr, indices = H.path(50)
+    elif graph == "complete":
+        indptr, indices = H.complete(30)
+    elif graph == "hand":
+        indptr, indices, _, _ = H.read_hand_graph()
+    else:
+        indptr, indices = H.random_csr(2000, 40, seed=3, max_deg=600, indptr_dtype=np.int64)
+    n = indptr.shape[0] - 1
+    x = np.random.default_rng(n).standard_normal((n, 6)).astype(np.float32)
+    dg = device_graph(indptr, indices)
+    fs = _store(x, ld=6)            # ld = d = 6: the unaligned (scalar) gather/mean path
+    seeds = np.arange(0, n, max(1, n // 37), dtype=np.int32)[::-1].copy()
+    for seed64 in (0, 99):
+        outs, st = run_minibatch(dg, fs, seeds, fanouts, seed64)
+        assert st == gm.GNN_OK
+        ref = oracle.minibatch(indptr, indices, x, seeds, fanouts, seed64)
+        compare_with_oracle(outs[0], ref, 6)
+
+
+def test_empty_seeds(tiny):
+    cfg, indptr, indices, x, order = tiny
+    outs, st = run_minibatch(device_graph(indptr, indices), _store(x), order[:0], [4, 2], 1)
+    assert st == gm.GNN_OK
+    assert outs[0].blocks.counts.cpu().tolist() == [0, 0, 0, 0]
+    assert outs[0].blocks.indptr[0][0].item() == 0
+
+
+def test_isolated_seed_and_zero_degree():
+    indptr, indices = H.csr_from_rows([[], [0], [], [1, 2]])
+    x = np.arange(8, dtype=np.float32).reshape(4, 2)
+    outs, st = run_minibatch(device_graph(indptr, indices), _store(x, 4),
+                             np.array([0, 2], np.int32), [3], 5)
+    assert st == gm.GNN_OK
+    ref = oracle.minibatch(indptr, indices, x, np.array([0, 2], np.int32), [3], 5)
+    compare_with_oracle(outs[0], ref, 2)
+    assert np.all(outs[0].h[0][:2, :2].cpu().numpy() == 0)
+
+
+def test_duplicate_seed_reported(tiny):
+    cfg, indptr, indices, x, order = tiny
+    seeds = np.array([5, 17, 5], np.int32)
+    _, st = run_minibatch(device_graph(indptr, indices), _store(x), seeds, [3], 1)
+    assert st == gm.GNN_ERR_INVALID_ARG
+
+
+def test_out_of_range_seed_reported(tiny):
+    cfg, indptr, indices, x, order = tiny
+    seeds = np.array([5, cfg.num_nodes, 7], np.int32)
+    _, st = run_minibatch(device_graph(indptr, indices), _store(x), seeds, [3, 2], 1)
+    assert st == gm.GNN_ERR_OUT_OF_RANGE
+
+
+def test_capacity_overflow_reported(tiny):
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    seeds = torch.from_numpy(order[:64].copy()).cuda()
+    caps = gm.gnn_capacity(64, [10, 5], cfg.num_nodes)
+    caps.edges[1] = 7          # far below what hop 2 samples
+    blocks = gm.Blocks(caps)
+    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes), dtype=torch.uint8, device="cuda")
+    gm.gnn_sample_khop(dg, seeds, [10, 5], 3, blocks, ws)
+    assert gm.gnn_read_device_status(ws) == gm.GNN_ERR_CAPACITY
+
+
+def test_sync_flag_returns_device_status(tiny):
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    seeds = torch.tensor([3, 3], dtype=torch.int32, device="cuda")
+    caps = gm.gnn_capacity(2, [4], cfg.num_nodes)
+    blocks = gm.Blocks(caps)
+    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes), dtype=torch.uint8, device="cuda")
+    with pytest.raises(gm.GnnError) as e:
+        gm.gnn_sample_khop(dg, seeds, [4], 3, blocks, ws, gm.Options(sync=True))
+    assert e.value.status == gm.GNN_ERR_INVALID_ARG
+
+
+def test_sample_khop_alone_matches_oracle(tiny):
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    seeds = order[300:812]
+    caps = gm.gnn_capacity(len(seeds), [8, 4, 2], cfg.num_nodes)
+    blocks = gm.Blocks(caps)
+    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes), dtype=torch.uint8, device="cuda")
+    gm.gnn_sample_khop(dg, torch.from_numpy(seeds.copy()).cuda(), [8, 4, 2], 12345, blocks, ws)
+    assert gm.gnn_read_device_status(ws) == gm.GNN_OK
+    ref = oracle.sample_khop(indptr, indices, seeds, [8, 4, 2], 12345)
+    for got, rb in zip(blocks.host(), ref):
+        assert np.array_equal(got[0], rb.indptr) and np.array_equal(got[1], rb.gid)
+        assert np.array_equal(got[2], rb.lid) and np.array_equal(got[3], rb.dst_lid)
+        assert np.array_equal(got[4], rb.nodes)
+
+
+@pytest.mark.parametrize("n_keep,n_add,bound", [(0, 0, 1), (1, 0, 5), (300, 2000, 5000),
+                                                (5000, 200000, 233000), (7, 50000, 64)])
+def test_unique_relabel_standalone(n_keep, n_add, bound):
+    rng = np.random.default_rng(n_add)
+    keep = rng.choice(bound, size=n_keep, replace=False).astype(np.int32)
+    add = rng.integers(0, bound, size=n_add).astype(np.int32)
+    dev = lambda a: torch.from_numpy(a).cuda() if a.size else torch.zeros(0, dtype=torch.int32, device="cuda")
+    uniq = torch.full((n_keep + n_add + 1,), -7, dtype=torch.int32, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int64, device="cuda")
+    add_lid = torch.empty(max(n_add, 1), dtype=torch.int32, device="cuda")[:n_add]
+    keep_lid = torch.empty(max(n_keep, 1), dtype=torch.int32, device="cuda")[:n_keep]
+    ws = torch.empty(gm.gnn_relabel_workspace_size(bound), dtype=torch.uint8, device="cuda")
+    gm.gnn_unique_relabel(dev(keep), dev(add), bound, uniq, nu, add_lid, keep_lid, ws)
+    assert gm.gnn_read_device_status(ws) == gm.GNN_OK
+    u, lid, dl = oracle.relabel(keep, add)
+    assert nu.item() == len(u)
+    assert np.array_equal(uniq[:len(u)].cpu().numpy(), u)
+    assert np.array_equal(add_lid.cpu().numpy(), lid)
+    assert np.array_equal(keep_lid.cpu().numpy(), dl)
+
+
+def test_unique_relabel_device_count():
+    add = torch.tensor([9, 3, 9, 1, 7, 7], dtype=torch.int32, device="cuda")
+    keep = torch.tensor([4], dtype=torch.int32, device="cuda")
+    n_add = torch.tensor([4], dtype=torch.int64, device="cuda")   # only the first 4 count
+    uniq = torch.full((8,), -1, dtype=torch.int32, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int64, device="cuda")
+    add_lid = torch.full((6,), -1, dtype=torch.int32, device="cuda")
+    keep_lid = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(gm.gnn_relabel_workspace_size(10), dtype=torch.uint8, device="cuda")
+    gm.gnn_unique_relabel(keep, add, 10, uniq, nu, add_lid, keep_lid, ws, d_n_add=n_add)
+    assert nu.item() == 4
+    assert uniq[:4].tolist() == [1, 3, 4, 9]
+    assert add_lid[:4].tolist() == [3, 1, 3, 0] and keep_lid.tolist() == [2]
+
+
+@pytest.mark.parametrize("d,ld", [(602, 604), (13, 13), (64, 64), (100, 100), (128, 132), (3, 4)])
+def test_gather_standalone(d, ld):
+    rng = np.random.default_rng(d)
+    n = 3000
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    fs = _store(x, ld)
+    ids = rng.integers(0, n, size=1777).astype(np.int32)
+    out = torch.full((1777, ld + 4), 7.0, dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gm.gnn_gather_features(fs, torch.from_numpy(ids).cuda(), out, d_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    ref = oracle.gather(x, ids, d)
+    assert np.array_equal(out[:, :d].cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert torch.all(out[:, d:] == 7.0)       # columns past d untouched
+
+
+def test_gather_out_of_range_reported():
+    x = np.ones((10, 4), np.float32)
+    fs = _store(x, 4)
+    out = torch.zeros(3, 4, dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gm.gnn_gather_features(fs, torch.tensor([1, 10, -1], dtype=torch.int32, device="cuda"), out,
+                           d_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == gm.GNN_ERR_OUT_OF_RANGE
+
+
+@pytest.mark.parametrize("d,ld", [(602, 604), (7, 7), (128, 128)])
+def test_mean_standalone(d, ld):
+    rng = np.random.default_rng(d + 1)
+    n_src, n_dst = 500, 300
+    src = rng.uniform(-1, 1, size=(n_src, d)).astype(np.float32)
+    counts = rng.integers(0, 26, size=n_dst)
+    counts[:5] = 0
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    lid = rng.integers(0, n_src, size=int(counts.sum())).astype(np.int32)
+    out = torch.zeros(n_dst, ld, dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gm.gnn_mean_aggregate(torch.from_numpy(indptr).cuda(), torch.from_numpy(lid).cuda(),
+                          device_table(src, ld), d, out, d_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    ref = oracle.mean_aggregate(indptr, lid, src)
+    err = np.abs(out[:, :d].cpu().numpy().astype(np.float64) - ref).max()
+    assert err <= 1e-5 * np.abs(src).max()
+    assert np.all(out[:5, :d].cpu().numpy() == 0)
+
+
+def test_feature_cache_is_transparent(tiny):
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    table = device_table(x, 64)
+    plain = gm.gnn_feature_store_create(table, 64)
+    deg = np.diff(indptr)
+    hot = np.argsort(-deg, kind="stable")[:3000].astype(np.int32)
+    cached = gm.gnn_feature_store_create(table, 64, 3000, torch.from_numpy(hot).cuda())
+    seeds = order[:cfg.batch]
+    a, sa = run_minibatch(dg, plain, seeds, cfg.fanouts, 3)
+    b, sb = run_minibatch(dg, cached, seeds, cfg.fanouts, 3)
+    assert sa == sb == gm.GNN_OK
+    nodes = b[0].blocks.host()[-1][4]
+    nv = len(nodes)
+    assert torch.equal(a[0].x[:nv], b[0].x[:nv]) and torch.equal(a[0].h[0], b[0].h[0])
+    # the gather reports the rows it took from the cache
+    hits = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = torch.empty(len(nodes), 64, dtype=torch.float32, device="cuda")
+    gm.gnn_gather_features(cached, torch.from_numpy(nodes).cuda(), out, d_hits=hits)
+    assert hits.item() == len(np.intersect1d(nodes, hot))
+    assert torch.equal(out, b[0].x[:len(nodes)])
+
+
+def test_host_resident_table_zero_copy(tiny):
+    cfg, indptr, indices, x, order = tiny
+    host = torch.zeros(cfg.num_nodes, 64, dtype=torch.float32, pin_memory=True)
+    host.copy_(torch.from_numpy(x))
+    fs_host = gm.gnn_feature_store_create(host, 64)
+    deg = np.diff(indptr)
+    hot = np.argsort(-deg, kind="stable")[:1000].astype(np.int32)
+    fs_mix = gm.gnn_feature_store_create(host, 64, 1000, torch.from_numpy(hot).cuda())
+    dg = device_graph(indptr, indices)
+    seeds = order[:cfg.batch]
+    ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, 11)
+    for fs in (fs_host, fs_mix):
+        outs, st = run_minibatch(dg, fs, seeds, cfg.fanouts, 11)
+        assert st == gm.GNN_OK
+        compare_with_oracle(outs[0], ref, cfg.d)
+
+
+def test_repeat_runs_identical(tiny):
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    seeds = order[:cfg.batch]
+    a, _ = run_minibatch(dg, fs, seeds, [15, 10, 5], 21)
+    b, _ = run_minibatch(dg, fs, seeds, [15, 10, 5], 21)
+    cnt = a[0].blocks.counts.cpu().tolist()
+    rows = [len(seeds), cnt[1], cnt[3]]
+    for l in range(3):
+        assert torch.equal(a[0].h[l][:rows[l]], b[0].h[l][:rows[l]])
+    assert torch.equal(a[0].x[:cnt[5]], b[0].x[:cnt[5]])
+    for ha, hb in zip(a[0].blocks.host(), b[0].blocks.host()):
+        for u, v in zip(ha, hb):
+            assert np.array_equal(u, v)
+
+
+def test_superbatch_equals_separate_runs(tiny):
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    seeds = order[:700]
+    ptr = [0, 256, 256, 600, 700]
+    outs, st = run_minibatch(dg, fs, seeds, cfg.fanouts, 77, group_ptr=ptr)
+    assert st == gm.GNN_OK
+    for g in range(4):
+        ref = oracle.minibatch(indptr, indices, x, seeds[ptr[g]:ptr[g + 1]], cfg.fanouts, 77)
+        compare_with_oracle(outs[g], ref, cfg.d)
