@@ -49,7 +49,10 @@ def algorithmic_bytes(counts, n_seeds, d, K):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=147)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (default: one epoch)")
+    ap.add_argument("--group", type=int, default=1,
+                    help="mini-batches per super-batch (one step = one super-batch)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dense")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -78,41 +81,63 @@ def main():
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t0
     n_batches = (order.numel() + cfg.batch - 1) // cfg.batch
+    G = args.group
+    n_super = (n_batches + G - 1) // G
+    steps = args.steps or n_super
     K = len(cfg.fanouts)
 
     dg = gm.DeviceGraph(cfg.num_nodes, graph.indptr, graph.indices)
     fs = gm.gnn_feature_store_create(table, cfg.d)
     caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
-    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes), dtype=torch.uint8, device=dev)
+    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
 
-    def out_for(n):
-        return gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes), cfg.d, cfg.ld)
+    outs = {}   # one output set per (position in the super-batch, seed count)
 
-    outs = {}
+    def batch_range(s):
+        b0 = s * G
+        return list(range(b0, min(b0 + G, n_batches)))
 
-    def step(b, timer=None):
-        s = b % n_batches
-        n = min(cfg.batch, order.numel() - s * cfg.batch)
-        if n not in outs:
-            outs[n] = out_for(n)
-        seeds = order[s * cfg.batch: s * cfg.batch + n]
-        gm.gnn_minibatch(dg, fs, seeds, [0, n], cfg.fanouts, gm.gnn_batch_seed(cfg.rng_seed, s),
-                         [outs[n]], ws, timer=timer)
-        return n
+    def step(st, timer=None):
+        """Super-batch st (mod the epoch): its batches share one seed.  Returns [(b, n, out)]."""
+        s = st % n_super
+        bs = batch_range(s)
+        lo = bs[0] * cfg.batch
+        hi = min(order.numel(), (bs[-1] + 1) * cfg.batch)
+        ptr = [min(b * cfg.batch, order.numel()) - lo for b in bs] + [hi - lo]
+        mine = []
+        for j, b in enumerate(bs):
+            n = ptr[j + 1] - ptr[j]
+            if (j, n) not in outs:
+                outs[(j, n)] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
+                                               cfg.d, cfg.ld)
+            mine.append((b, n, outs[(j, n)]))
+        gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, gm.gnn_batch_seed(cfg.rng_seed, s),
+                         [m[2] for m in mine], ws, timer=timer)
+        return s, mine
 
     for b in range(args.warmup):
         step(b)
     torch.cuda.synchronize()
     assert gm.gnn_read_device_status(ws) == gm.GNN_OK
 
-    timer = gm.Timer(args.steps)
+    # Timed region 1: the headline throughput, nothing but the steps on the stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for b in range(args.steps):
-        step(b, timer)
+    for b in range(steps):
+        step(b)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     status = gm.gnn_read_device_status(ws)
+
+    # Timed region 2: the same steps with HIP events at the stage boundaries (the events cost a few
+    # microseconds each, so they stay out of region 1).
+    timer = gm.Timer(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for b in range(steps):
+        step(b, timer)
+    torch.cuda.synchronize()
+    wall_events = time.perf_counter() - t0
     stages = np.array(timer.elapsed(), dtype=np.float64)      # [steps, 4] ms
 
     # Sizes of each timed batch: sampling is a pure function of the batch, so an untimed re-run
@@ -121,22 +146,27 @@ def main():
     gb_bytes = []
     mean_bytes = []
     payload = []
-    for b in range(args.steps):
-        n = step(b)
-        cnt = outs[n].blocks.counts.cpu().tolist()
-        g_b, m_b, E, V = algorithmic_bytes(cnt, n, cfg.d, K)
-        tot_edges += sum(E)
-        gb_bytes.append(g_b)
-        mean_bytes.append(m_b)
-        payload.append(V[K - 1] * cfg.d * 4)
+    for b in range(steps):
+        _, mine = step(b)
+        g_s, m_s, p_s = 0, [0] * K, 0
+        for _, n, out in mine:
+            cnt = out.blocks.counts.cpu().tolist()
+            g_b, m_b, E, V = algorithmic_bytes(cnt, n, cfg.d, K)
+            tot_edges += sum(E)
+            g_s += g_b
+            m_s = [x + y for x, y in zip(m_s, m_b)]
+            p_s += V[K - 1] * cfg.d * 4
+        gb_bytes.append(g_s)
+        mean_bytes.append(m_s)
+        payload.append(p_s)
     gb_bytes = np.array(gb_bytes, dtype=np.float64)
     mean_outer = np.array([m[K - 1] for m in mean_bytes], dtype=np.float64)
     mean_all = np.array([sum(m) for m in mean_bytes], dtype=np.float64)
 
     t_sample, t_gather, t_mean_outer, t_mean_rest = (stages[:, i].sum() / 1e3 for i in range(4))
     kern = {
-        "gather": (gb_bytes.sum() / t_gather / 1e9, t_gather / args.steps * 1e3),
-        "mean_outer": (mean_outer.sum() / t_mean_outer / 1e9, t_mean_outer / args.steps * 1e3),
+        "gather": (gb_bytes.sum() / t_gather / 1e9, t_gather / steps / G * 1e3),
+        "mean_outer": (mean_outer.sum() / t_mean_outer / 1e9, t_mean_outer / steps / G * 1e3),
     }
     dom = "gather" if t_gather >= t_mean_outer else "mean_outer"
     ach, avg_ms = kern[dom]
@@ -147,43 +177,45 @@ def main():
         "value": tot_edges / wall,
         "unit": "sampled edges/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
+        "ms_per_step": wall / steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": workload_name(cfg), "batches_per_epoch": n_batches,
-                   "super_batch": 1},
+                   "super_batch": G, "step": f"one super-batch of {G} mini-batch(es)"},
+        "ms_per_minibatch": wall / sum(len(batch_range(b % n_super)) for b in range(steps)) * 1e3,
         "status": gm.gnn_status_string(status),
         "sampled_edges_per_s_sampling_stage": tot_edges / t_sample,
         "gathered_GBps": float(np.sum(payload) / t_gather / 1e9),
         "gather_aggregate_hbm_frac": ga_frac,
-        "stage_ms_per_step": {"sample_relabel": t_sample / args.steps * 1e3,
-                              "gather": t_gather / args.steps * 1e3,
-                              "mean_outer_block": t_mean_outer / args.steps * 1e3,
-                              "mean_other_blocks": t_mean_rest / args.steps * 1e3},
+        "stage_ms_per_step": {"sample_relabel": t_sample / steps * 1e3,
+                              "gather": t_gather / steps * 1e3,
+                              "mean_outer_block": t_mean_outer / steps * 1e3,
+                              "mean_other_blocks": t_mean_rest / steps * 1e3},
         "roofline": {"bound": "hbm", "kernel": "k_gather" if dom == "gather" else "k_mean_v4",
                      "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBPS, "traffic": None,
-                     "avg_launch_ms": avg_ms},
+                     "avg_launch_ms": avg_ms, "launches_per_step": G},
         "other_kernel": {"name": "k_mean_v4" if dom == "gather" else "k_gather",
                          "achieved_GBps": kern["mean_outer" if dom == "gather" else "gather"][0],
                          "avg_launch_ms": kern["mean_outer" if dom == "gather" else "gather"][1]},
+        "ms_per_step_with_stage_events": wall_events / steps * 1e3,
         "input_generation_s": t_gen,
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, graph, table, order, outs, step, args.cpu_seconds,
+        result["cpu_baseline"] = cpu_baseline(cfg, graph, table, order, step, args.cpu_seconds,
                                               tot_edges / wall)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(cfg, graph, table, order, outs, step, budget_s, gpu_value):
-    """The oracle (single-threaded C) on the first batches of the same epoch, until budget_s of
-    CPU work has been spent; checks its results against the GPU path's on those batches."""
+def cpu_baseline(cfg, graph, table, order, step, budget_s, gpu_value):
+    """The oracle (single-threaded C) on the first super-batches of the same epoch, until budget_s
+    of CPU work has been spent; checks its results against the GPU path's on those batches."""
     import numpy as np
 
     import oracle
@@ -193,32 +225,33 @@ def cpu_baseline(cfg, graph, table, order, outs, step, budget_s, gpu_value):
     x = table.cpu().numpy()
     order_h = order.cpu().numpy()
     K = len(cfg.fanouts)
-    spent, edges, batches, parity = 0.0, 0, 0, True
+    spent, edges, batches, parity, st = 0.0, 0, 0, True, 0
     while spent < budget_s and batches < 64:
-        b = batches
-        n = min(cfg.batch, order_h.size - b * cfg.batch)
-        seeds = order_h[b * cfg.batch: b * cfg.batch + n]
-        seed64 = oracle.batch_seed(cfg.rng_seed, b)
-        t0 = time.perf_counter()
-        ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
-        spent += time.perf_counter() - t0
-        edges += sum(len(bl.gid) for bl in ref.blocks)
-        batches += 1
-        n_gpu = step(b)
-        got = outs[n_gpu]
-        host = got.blocks.host()
-        for l in range(K):
-            parity &= bool(np.array_equal(host[l][1], ref.blocks[l].gid)
-                           and np.array_equal(host[l][4], ref.blocks[l].nodes))
-        nv = len(ref.blocks[-1].nodes)
-        parity &= bool(np.array_equal(got.x[:nv, :cfg.d].cpu().numpy(), ref.x))
-        err = float(np.abs(got.h[0][:n, :cfg.d].cpu().numpy() - ref.h[0]).max())
-        parity &= err <= 1e-5 * float(np.abs(ref.x).max())
+        s, mine = step(st)
+        st += 1
+        seed64 = oracle.batch_seed(cfg.rng_seed, s)
+        for b, n, got in mine:
+            if spent >= budget_s and batches > 0:
+                break
+            seeds = order_h[b * cfg.batch: b * cfg.batch + n]
+            t0 = time.perf_counter()
+            ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+            spent += time.perf_counter() - t0
+            edges += sum(len(bl.gid) for bl in ref.blocks)
+            batches += 1
+            host = got.blocks.host()
+            for l in range(K):
+                parity &= bool(np.array_equal(host[l][1], ref.blocks[l].gid)
+                               and np.array_equal(host[l][4], ref.blocks[l].nodes))
+            nv = len(ref.blocks[-1].nodes)
+            parity &= bool(np.array_equal(got.x[:nv, :cfg.d].cpu().numpy(), ref.x))
+            err = float(np.abs(got.h[0][:n, :cfg.d].cpu().numpy() - ref.h[0]).max())
+            parity &= err <= 1e-5 * float(np.abs(ref.x).max())
     value = edges / spent
     return {"value": value, "unit": "sampled edges/s", "cores": 1, "kind": "oracle",
-            "sample": f"the first {batches} batches of the epoch (seeds in epoch order, same "
-                      f"seed per batch as the GPU run), whole path: sampling, relabel, gather, "
-                      f"mean; {spent:.1f} s single-threaded",
+            "sample": f"the first {batches} mini-batches of the epoch (same seeds and batch seed as "
+                      f"the GPU run), whole path: sampling, relabel, gather, mean; "
+                      f"{spent:.1f} s single-threaded",
             "gpu_over_cpu": gpu_value / value, "parity_on_sample": parity}
 
 

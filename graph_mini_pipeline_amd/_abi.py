@@ -11,6 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgnnmb.so")
 
 GNN_MAX_HOPS = 8
+GNN_MAX_GROUP = 16
 GNN_TIMER_EVENTS = 5
 GNN_SYNC = 1
 
@@ -32,7 +33,8 @@ class gnn_graph(ctypes.Structure):
 
 
 class gnn_caps(ctypes.Structure):
-    _fields_ = [("num_hops", i32), ("n_seeds", i64), ("frontier", i64 * GNN_MAX_HOPS),
+    _fields_ = [("num_hops", i32), ("fanouts", i32 * GNN_MAX_HOPS), ("n_seeds", i64),
+                ("frontier", i64 * GNN_MAX_HOPS),
                 ("edges", i64 * GNN_MAX_HOPS), ("nodes", i64 * GNN_MAX_HOPS)]
 
 

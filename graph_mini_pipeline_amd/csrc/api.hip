@@ -52,45 +52,73 @@ struct Carver {
 
 struct Workspace {
     int32_t *status;       // [1] at offset 0
-    uint32_t *class_count; // [4]
-    uint32_t *work;        // [4]
-    int32_t *packed;       // [F_max]
-    int32_t *lists;        // [4 F_max]
-    uint32_t *bsum_c;      // [nb_max]
-    uint32_t *bsum_cls;    // [4 nb_max]
-    uint32_t *bitmap;      // [W]
-    uint32_t *wprefix;     // [W]
-    uint32_t *bsum_w;      // [nbw]
-    int64_t F_max, nb_max, W, nbw;
+    uint32_t *totals;      // [5] classification totals
+    int64_t *d_U;          // |U| of a super-batch hop
+    int64_t *d_uE;         // edges of the union block
+    int32_t *packed;       // [FU_max]
+    int32_t *lists;        // [4 FU_max]
+    uint32_t *bsum;        // [5 nb_max]
+    uint32_t *bitmaps;     // [nbm * W]: G = 1: one bitmap; G > 1: the union bitmap, then G
+    uint32_t *wprefix;     // [nbm * W]
+    uint32_t *bsum_w;      // [nbm * nbw]
+    int32_t *U;            // super-batch only: union frontier, union block, distribution sums
+    int32_t *u_indptr;
+    int32_t *u_gid;
+    uint32_t *bsum_dist;
+    int64_t W, nbw, nbm;
     size_t bytes;
 };
 
-Workspace carve(int64_t F_max, int64_t num_nodes, void *ws) {
-    Workspace w{};
-    Carver c{static_cast<char *>(ws)};
-    w.F_max = F_max < 1 ? 1 : F_max;
-    w.nb_max = (w.F_max + kClassifyTile - 1) / kClassifyTile;
-    w.W = (num_nodes + 31) / 32;
-    w.nbw = (w.W + kBitmapTile - 1) / kBitmapTile;
-    if (w.nbw < 1) w.nbw = 1;
-    w.status = c.take<int32_t>(64);
-    w.class_count = c.take<uint32_t>(64);
-    w.work = c.take<uint32_t>(64);
-    w.packed = c.take<int32_t>(w.F_max);
-    w.lists = c.take<int32_t>(4 * w.F_max);
-    w.bsum_c = c.take<uint32_t>(w.nb_max);
-    w.bsum_cls = c.take<uint32_t>(4 * w.nb_max);
-    w.bitmap = c.take<uint32_t>(w.W);
-    w.wprefix = c.take<uint32_t>(w.W);
-    w.bsum_w = c.take<uint32_t>(w.nbw);
-    w.bytes = c.off;
-    return w;
+// Union frontier bound of hop l of a super-batch: min(N, G * per-sub-batch frontier bound).
+int64_t union_cap(const gnn_caps &mc, int l, int G, int64_t N) {
+    const int64_t u = static_cast<int64_t>(G) * mc.frontier[l];
+    return u < N ? u : N;
 }
 
-int64_t caps_fmax(const gnn_caps &caps) {
-    int64_t f = 1;
-    for (int l = 0; l < caps.num_hops; ++l) f = caps.frontier[l] > f ? caps.frontier[l] : f;
-    return f;
+int64_t tiles_for(int64_t n) {
+    const int64_t t = (n + kClassifyTile - 1) / kClassifyTile;
+    return t < 1 ? 1 : t;
+}
+
+// mc: element-wise bound of every sub-batch's caps; G sub-batches.
+Workspace carve(const gnn_caps &mc, int64_t N, int G, void *ws) {
+    Workspace w{};
+    Carver c{static_cast<char *>(ws)};
+    int64_t FU = 1, U_max = 1, uE_max = 1, F_max = 1;
+    for (int l = 0; l < mc.num_hops; ++l) {
+        F_max = mc.frontier[l] > F_max ? mc.frontier[l] : F_max;
+        const int64_t u = G == 1 ? mc.frontier[l] : union_cap(mc, l, G, N);
+        FU = u > FU ? u : FU;
+        if (G > 1) {
+            U_max = u > U_max ? u : U_max;
+            const int64_t e = u * mc.fanouts[l];
+            uE_max = e > uE_max ? e : uE_max;
+        }
+    }
+    const int64_t nb_max = tiles_for(FU);
+    w.W = (N + 31) / 32;
+    w.nbw = (w.W + kBitmapTile - 1) / kBitmapTile;
+    if (w.nbw < 1) w.nbw = 1;
+    w.nbm = G == 1 ? 1 : 1 + G;
+    w.status = c.take<int32_t>(64);
+    w.totals = c.take<uint32_t>(64);
+    int64_t *cnt = c.take<int64_t>(32);
+    w.d_U = cnt;
+    w.d_uE = cnt ? cnt + 1 : nullptr;
+    w.packed = c.take<int32_t>(FU);
+    w.lists = c.take<int32_t>(4 * FU);
+    w.bsum = c.take<uint32_t>(5 * nb_max);
+    w.bitmaps = c.take<uint32_t>(w.nbm * w.W);
+    w.wprefix = c.take<uint32_t>(w.nbm * w.W);
+    w.bsum_w = c.take<uint32_t>(w.nbm * w.nbw);
+    if (G > 1) {
+        w.U = c.take<int32_t>(U_max);
+        w.u_indptr = c.take<int32_t>(U_max + 1);
+        w.u_gid = c.take<int32_t>(uE_max);
+        w.bsum_dist = c.take<uint32_t>(static_cast<int64_t>(G) * tiles_for(F_max));
+    }
+    w.bytes = c.off;
+    return w;
 }
 
 struct Opts {
@@ -128,13 +156,14 @@ gnn_status check_fanouts(const int32_t *fanouts, int32_t K) {
     return GNN_OK;
 }
 
-// Caps must chain (frontier[0] = n_seeds, frontier[l] = nodes[l-1]), fit int32, and every array
-// a non-empty cap refers to must exist.
-gnn_status check_blocks(const gnn_blocks *b, int64_t n_seeds, int32_t K) {
+// Caps must chain (frontier[0] = n_seeds, frontier[l] = nodes[l-1]), carry the call's fanouts,
+// fit int32, and every array a non-empty cap refers to must exist.
+gnn_status check_blocks(const gnn_blocks *b, int64_t n_seeds, const int32_t *fanouts, int32_t K) {
     if (!b || !b->counts) return GNN_ERR_INVALID_ARG;
     const gnn_caps &c = b->caps;
     if (c.num_hops != K || c.n_seeds != n_seeds || c.frontier[0] != n_seeds) return GNN_ERR_INVALID_ARG;
     for (int l = 0; l < K; ++l) {
+        if (c.fanouts[l] != fanouts[l]) return GNN_ERR_INVALID_ARG;
         if (c.frontier[l] < 0 || c.edges[l] < 0 || c.nodes[l] < 0) return GNN_ERR_INVALID_ARG;
         if (c.frontier[l] > kInt32Max || c.edges[l] > kInt32Max || c.nodes[l] > kInt32Max)
             return GNN_ERR_UNSUPPORTED;
@@ -148,60 +177,132 @@ gnn_status check_blocks(const gnn_blocks *b, int64_t n_seeds, int32_t K) {
     return GNN_OK;
 }
 
-// Sampling and relabel of every hop of one batch; no host synchronisation.
-gnn_status run_sample_khop(const gnn_graph &g, const int32_t *seeds, int64_t n_seeds,
-                           const int32_t *fanouts, int32_t K, uint64_t seed64, gnn_blocks &out,
-                           const Workspace &w, const Opts &o, hipStream_t s) {
-    const gnn_caps &c = out.caps;
+HopArgs hop_args(const gnn_graph &g, const int32_t *front, const int64_t *d_F, int64_t F_cap,
+                 int32_t k, uint64_t hop_seed, int32_t *blk_indptr, int32_t *blk_gid,
+                 int64_t E_cap, int64_t *d_E, const Workspace &w, const Opts &o) {
+    HopArgs h{};
+    h.indptr = g.indptr;
+    h.indices = g.indices;
+    h.num_nodes = g.num_nodes;
+    h.front = front;
+    h.d_F = d_F;
+    h.F_cap = F_cap;
+    h.ib = g.indptr_bytes;
+    h.k = k;
+    h.hop_seed = hop_seed;
+    h.group_max = o.group_max;
+    h.wave_max = o.wave_max;
+    h.blk_indptr = blk_indptr;
+    h.blk_gid = blk_gid;
+    h.E_cap = E_cap;
+    h.d_E = d_E;
+    h.packed = w.packed;
+    h.lists = w.lists;
+    h.bsum = w.bsum;
+    h.totals = w.totals;
+    h.status = w.status;
+    h.nb = static_cast<int32_t>(tiles_for(F_cap));
+    return h;
+}
+
+RelabelArgs relabel_args(const gnn_graph &g, const Workspace &w, int first_bitmap, int nbm) {
+    RelabelArgs r{};
+    r.nbm = nbm;
+    r.id_bound = g.num_nodes;
+    r.bitmap = w.bitmaps + first_bitmap * w.W;
+    r.wprefix = w.wprefix + first_bitmap * w.W;
+    r.bsum = w.bsum_w + first_bitmap * w.nbw;
+    r.W = w.W;
+    r.nbw = static_cast<int32_t>(w.nbw);
+    r.status = w.status;
+    r.bitmap_cleared = 1;
+    return r;
+}
+
+// Sampling and relabel of every hop of G sub-batches (G = 1: one batch); no host synchronisation.
+// seeds_g[g] / n_seeds_g[g] are the sub-batches' seeds, outs[g] their blocks.
+gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const int64_t *n_seeds_g,
+                      int G, const int32_t *fanouts, int32_t K, uint64_t seed64,
+                      gnn_blocks *const *outs, const Workspace &w, const Opts &o, hipStream_t s) {
+    if (G > 1) GNN_TRY_HIP(launch_fill_u32(w.bitmaps, w.W, 0u, s));  // union bitmap of hop 1
+    gnn_caps mc = outs[0]->caps;
+    for (int gi = 1; gi < G; ++gi)
+        for (int l = 0; l < K; ++l)
+            mc.frontier[l] = outs[gi]->caps.frontier[l] > mc.frontier[l] ? outs[gi]->caps.frontier[l]
+                                                                          : mc.frontier[l];
     for (int l = 0; l < K; ++l) {
-        HopArgs h{};
-        h.indptr = g.indptr;
-        h.indices = g.indices;
-        h.num_nodes = g.num_nodes;
-        h.front = l == 0 ? seeds : out.hop[l - 1].nodes;
-        h.d_F = l == 0 ? nullptr : out.counts + 2 * (l - 1) + 1;
-        h.F_cap = c.frontier[l];
-        h.ib = g.indptr_bytes;
-        h.k = fanouts[l];
-        h.hop_seed = mix64(seed64 + kGamma * static_cast<uint64_t>(l + 1));
-        h.group_max = o.group_max;
-        h.wave_max = o.wave_max;
-        h.blk_indptr = out.hop[l].indptr;
-        h.blk_gid = out.hop[l].gid;
-        h.E_cap = c.edges[l];
-        h.d_E = out.counts + 2 * l;
-        h.packed = w.packed;
-        h.lists = w.lists;
-        h.bsum_c = w.bsum_c;
-        h.bsum_cls = w.bsum_cls;
-        h.class_count = w.class_count;
-        h.work = w.work;
-        h.status = w.status;
-        h.nb = static_cast<int32_t>((h.F_cap + kClassifyTile - 1) / kClassifyTile);
-        if (h.nb < 1) h.nb = 1;
+        const uint64_t hs = mix64(seed64 + kGamma * static_cast<uint64_t>(l + 1));
+        auto front = [&](int gi) { return l == 0 ? seeds_g[gi] : outs[gi]->hop[l - 1].nodes; };
+        auto d_F = [&](int gi) -> const int64_t * {
+            return l == 0 ? nullptr : outs[gi]->counts + 2 * (l - 1) + 1;
+        };
+        auto F_cap = [&](int gi) { return l == 0 ? n_seeds_g[gi] : outs[gi]->caps.frontier[l]; };
+        if (G == 1) {
+            gnn_blocks &out = *outs[0];
+            const gnn_caps &c = out.caps;
+            HopArgs h = hop_args(g, front(0), d_F(0), F_cap(0), fanouts[l], hs, out.hop[l].indptr,
+                                 out.hop[l].gid, c.edges[l], out.counts + 2 * l, w, o);
+            h.clear_ptr = w.bitmaps;
+            h.clear_n = w.W;
+            GNN_TRY_HIP(launch_classify(h, s));
+            GNN_TRY_HIP(launch_sample(h, s));
+            RelabelArgs r = relabel_args(g, w, 0, 1);
+            r.nlist = 2;
+            r.list[0] = IdList{front(0), d_F(0), F_cap(0), out.hop[l].dst_lid, 0, l == 0 ? 1 : 0};
+            r.list[1] = IdList{out.hop[l].gid, out.counts + 2 * l, c.edges[l], out.hop[l].lid, 0, 0};
+            r.out[0] = BitmapOut{out.hop[l].nodes, c.nodes[l], out.counts + 2 * l + 1};
+            GNN_TRY_HIP(launch_relabel(r, s));
+            continue;
+        }
+        // Super-batch: union of the G frontiers (bitmap 0), sampled once.
+        const int64_t Ucap = union_cap(mc, l, G, g.num_nodes);
+        const int64_t uEcap = Ucap * fanouts[l];
+        RelabelArgs ru = relabel_args(g, w, 0, 1);
+        ru.nlist = G;
+        for (int gi = 0; gi < G; ++gi) ru.list[gi] = IdList{front(gi), d_F(gi), F_cap(gi), nullptr, 0, 0};
+        ru.out[0] = BitmapOut{w.U, Ucap, w.d_U};
+        GNN_TRY_HIP(launch_relabel(ru, s));
+        HopArgs h = hop_args(g, w.U, w.d_U, Ucap, fanouts[l], hs, w.u_indptr, w.u_gid, uEcap,
+                             w.d_uE, w, o);
+        h.clear_ptr = w.bitmaps + w.W;  // the sub-batch bitmaps, zeroed before their relabel
+        h.clear_n = static_cast<int64_t>(G) * w.W;
         GNN_TRY_HIP(launch_classify(h, s));
         GNN_TRY_HIP(launch_sample(h, s));
-        RelabelArgs r{};
-        r.keep = h.front;
-        r.d_keep = h.d_F;
-        r.keep_cap = h.F_cap;
-        r.add = h.blk_gid;
-        r.d_add = h.d_E;
-        r.add_cap = h.E_cap;
-        r.id_bound = g.num_nodes;
-        r.bitmap = w.bitmap;
-        r.wprefix = w.wprefix;
-        r.bsum = w.bsum_w;
-        r.W = w.W;
-        r.nbw = static_cast<int32_t>(w.nbw);
-        r.uniq = out.hop[l].nodes;
-        r.uniq_cap = c.nodes[l];
-        r.d_uniq = out.counts + 2 * l + 1;
-        r.add_lid = out.hop[l].lid;
-        r.keep_lid = out.hop[l].dst_lid;
-        r.status = w.status;
-        r.check_dup_keep = l == 0 ? 1 : 0;
-        GNN_TRY_HIP(launch_relabel(r, s));
+        DistArgs da{};
+        da.G = G;
+        int32_t tiles = 0;
+        for (int gi = 0; gi < G; ++gi) {
+            gnn_blocks &out = *outs[gi];
+            const int32_t nt = static_cast<int32_t>(tiles_for(F_cap(gi)));
+            da.sub[gi] = DistSub{front(gi), d_F(gi), F_cap(gi), out.hop[l].indptr, out.hop[l].gid,
+                                 out.caps.edges[l], out.counts + 2 * l, tiles, nt};
+            tiles += nt;
+        }
+        da.ntiles = tiles;
+        da.bm0 = w.bitmaps;
+        da.wprefix0 = w.wprefix;
+        da.id_bound = g.num_nodes;
+        da.u_indptr = w.u_indptr;
+        da.u_gid = w.u_gid;
+        da.uE_cap = uEcap;
+        da.d_U = w.d_U;
+        da.U_cap = Ucap;
+        da.bsum = w.bsum_dist;
+        da.status = w.status;
+        GNN_TRY_HIP(launch_dist(da, s));
+        // Per-sub-batch relabel into bitmaps 1..G; the union bitmap is zeroed for the next hop.
+        RelabelArgs rs = relabel_args(g, w, 1, G);
+        rs.nlist = 2 * G;
+        for (int gi = 0; gi < G; ++gi) {
+            gnn_blocks &out = *outs[gi];
+            rs.list[2 * gi] = IdList{front(gi), d_F(gi), F_cap(gi), out.hop[l].dst_lid, gi, l == 0 ? 1 : 0};
+            rs.list[2 * gi + 1] = IdList{out.hop[l].gid, out.counts + 2 * l, out.caps.edges[l],
+                                         out.hop[l].lid, gi, 0};
+            rs.out[gi] = BitmapOut{out.hop[l].nodes, out.caps.nodes[l], out.counts + 2 * l + 1};
+        }
+        rs.clear_ptr = w.bitmaps;
+        rs.clear_n = w.W;
+        GNN_TRY_HIP(launch_relabel(rs, s));
     }
     return GNN_OK;
 }
@@ -244,6 +345,7 @@ gnn_status gnn_capacity(int64_t n_seeds, const int32_t *fanouts, int32_t num_hop
     c.n_seeds = n_seeds;
     int64_t f = n_seeds;
     for (int l = 0; l < num_hops; ++l) {
+        c.fanouts[l] = fanouts[l];
         c.frontier[l] = f;
         const int64_t e = f * fanouts[l];
         if (f > kInt32Max || e > kInt32Max) return GNN_ERR_UNSUPPORTED;
@@ -258,8 +360,9 @@ gnn_status gnn_capacity(int64_t n_seeds, const int32_t *fanouts, int32_t num_hop
 gnn_status gnn_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t group,
                               size_t *out_bytes) {
     if (!caps || !out_bytes || num_nodes < 1 || group < 1) return GNN_ERR_INVALID_ARG;
+    if (group > GNN_MAX_GROUP) return GNN_ERR_UNSUPPORTED;
     if (caps->num_hops < 1 || caps->num_hops > GNN_MAX_HOPS) return GNN_ERR_INVALID_ARG;
-    *out_bytes = carve(caps_fmax(*caps), num_nodes, nullptr).bytes;
+    *out_bytes = carve(*caps, num_nodes, group, nullptr).bytes;
     return GNN_OK;
 }
 
@@ -271,23 +374,27 @@ gnn_status gnn_sample_khop(const gnn_graph *g, const int32_t *seeds, int64_t n_s
     if (st == GNN_OK) st = check_fanouts(fanouts, num_hops);
     if (st != GNN_OK) return st;
     if (n_seeds < 0 || (n_seeds > 0 && !seeds)) return GNN_ERR_INVALID_ARG;
-    if ((st = check_blocks(out, n_seeds, num_hops)) != GNN_OK) return st;
+    if ((st = check_blocks(out, n_seeds, fanouts, num_hops)) != GNN_OK) return st;
     Opts o;
     if ((st = read_opts(opt, &o)) != GNN_OK) return st;
     if (!ws) return GNN_ERR_INVALID_ARG;
-    const Workspace need = carve(caps_fmax(out->caps), g->num_nodes, nullptr);
+    const Workspace need = carve(out->caps, g->num_nodes, 1, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
-    const Workspace w = carve(caps_fmax(out->caps), g->num_nodes, ws);
+    const Workspace w = carve(out->caps, g->num_nodes, 1, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
     GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
-    st = run_sample_khop(*g, seeds, n_seeds, fanouts, num_hops, seed64, *out, w, o, s);
+    const int32_t *sp[1] = {seeds};
+    const int64_t ns[1] = {n_seeds};
+    gnn_blocks *ob[1] = {out};
+    st = run_sample(*g, sp, ns, 1, fanouts, num_hops, seed64, ob, w, o, s);
     if (st != GNN_OK) return st;
     return finish(o, w, s);
 }
 
 gnn_status gnn_relabel_workspace_size(int64_t id_bound, size_t *out_bytes) {
     if (!out_bytes || id_bound < 1 || id_bound > kInt32Max + 1) return GNN_ERR_INVALID_ARG;
-    *out_bytes = carve(1, id_bound, nullptr).bytes;
+    gnn_caps none{};
+    *out_bytes = carve(none, id_bound, 1, nullptr).bytes;
     return GNN_OK;
 }
 
@@ -302,31 +409,26 @@ gnn_status gnn_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t
         return GNN_ERR_INVALID_ARG;
     if (!d_n_uniq || (cap_uniq > 0 && !uniq) || !ws) return GNN_ERR_INVALID_ARG;
     if (n_keep > kInt32Max || n_add > kInt32Max) return GNN_ERR_UNSUPPORTED;
-    const Workspace need = carve(1, id_bound, nullptr);
+    gnn_caps none{};
+    const Workspace need = carve(none, id_bound, 1, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
-    const Workspace w = carve(1, id_bound, ws);
+    const Workspace w = carve(none, id_bound, 1, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
     GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
     RelabelArgs r{};
-    r.keep = keep;
-    r.d_keep = nullptr;
-    r.keep_cap = n_keep;
-    r.add = add;
-    r.d_add = d_n_add;
-    r.add_cap = n_add;
+    r.nlist = 2;
+    r.list[0] = IdList{keep, nullptr, n_keep, keep_lid, 0, 0};
+    r.list[1] = IdList{add, d_n_add, n_add, add_lid, 0, 0};
+    r.nbm = 1;
+    r.out[0] = BitmapOut{uniq, cap_uniq, d_n_uniq};
     r.id_bound = id_bound;
-    r.bitmap = w.bitmap;
+    r.bitmap = w.bitmaps;
     r.wprefix = w.wprefix;
     r.bsum = w.bsum_w;
     r.W = w.W;
     r.nbw = static_cast<int32_t>(w.nbw);
-    r.uniq = uniq;
-    r.uniq_cap = cap_uniq;
-    r.d_uniq = d_n_uniq;
-    r.add_lid = add_lid;
-    r.keep_lid = keep_lid;
     r.status = w.status;
-    r.check_dup_keep = 0;
+    r.bitmap_cleared = 0;
     GNN_TRY_HIP(launch_relabel(r, s));
     return GNN_OK;
 }
@@ -422,17 +524,21 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     if (st != GNN_OK) return st;
     if (!fs || fs->num_nodes != g->num_nodes || !batch_ptr || !outs || group < 1 || !ws)
         return GNN_ERR_INVALID_ARG;
+    if (group > GNN_MAX_GROUP) return GNN_ERR_UNSUPPORTED;
     if (batch_ptr[0] != 0) return GNN_ERR_INVALID_ARG;
     Opts o;
     if ((st = read_opts(opt, &o)) != GNN_OK) return st;
-    int64_t F_max = 1;
     const int K = num_hops;
     const int64_t d = fs->d;
+    gnn_caps mc = outs[0].blocks.caps;
+    const int32_t *sp[GNN_MAX_GROUP];
+    int64_t nsg[GNN_MAX_GROUP];
+    gnn_blocks *ob[GNN_MAX_GROUP];
     for (int gi = 0; gi < group; ++gi) {
         const int64_t ns = batch_ptr[gi + 1] - batch_ptr[gi];
         if (ns < 0 || (ns > 0 && !seeds)) return GNN_ERR_INVALID_ARG;
         gnn_minibatch_out &mo = outs[gi];
-        if ((st = check_blocks(&mo.blocks, ns, K)) != GNN_OK) return st;
+        if ((st = check_blocks(&mo.blocks, ns, fanouts, K)) != GNN_OK) return st;
         if (mo.ld_h < d) return GNN_ERR_INVALID_ARG;
         const gnn_caps &c = mo.blocks.caps;
         if (c.nodes[K - 1] > 0 && !mo.x) return GNN_ERR_INVALID_ARG;
@@ -440,12 +546,17 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
             const int64_t rows = l == 0 ? ns : c.nodes[l - 1];
             if (rows > 0 && !mo.h[l]) return GNN_ERR_INVALID_ARG;
             if (c.nodes[l] * d > kFlatMax || rows * d > kFlatMax) return GNN_ERR_UNSUPPORTED;
+            mc.frontier[l] = c.frontier[l] > mc.frontier[l] ? c.frontier[l] : mc.frontier[l];
+            mc.edges[l] = c.edges[l] > mc.edges[l] ? c.edges[l] : mc.edges[l];
+            mc.nodes[l] = c.nodes[l] > mc.nodes[l] ? c.nodes[l] : mc.nodes[l];
         }
-        F_max = caps_fmax(c) > F_max ? caps_fmax(c) : F_max;
+        sp[gi] = seeds ? seeds + batch_ptr[gi] : nullptr;
+        nsg[gi] = ns;
+        ob[gi] = &mo.blocks;
     }
-    const Workspace need = carve(F_max, g->num_nodes, nullptr);
+    const Workspace need = carve(mc, g->num_nodes, group, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
-    const Workspace w = carve(F_max, g->num_nodes, ws);
+    const Workspace w = carve(mc, g->num_nodes, group, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t *ev = nullptr;
     if (timer) {
@@ -456,12 +567,8 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     }
     GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
     // Stage 1: sampling and relabel of every sub-batch (one shared seed64).
-    for (int gi = 0; gi < group; ++gi) {
-        const int64_t ns = batch_ptr[gi + 1] - batch_ptr[gi];
-        st = run_sample_khop(*g, seeds + batch_ptr[gi], ns, fanouts, K, seed64, outs[gi].blocks,
-                             w, o, s);
-        if (st != GNN_OK) return st;
-    }
+    st = run_sample(*g, sp, nsg, group, fanouts, K, seed64, ob, w, o, s);
+    if (st != GNN_OK) return st;
     if (ev) GNN_TRY_HIP(hipEventRecord(ev[1], s));
     // Stage 2: feature gather X = rows of V_K.
     for (int gi = 0; gi < group; ++gi) {

@@ -143,35 +143,81 @@ struct HopArgs {
     int64_t *d_E;           // receives |E_l|
     int32_t *packed;        // [F_cap] (c << 2) | class
     int32_t *lists;         // [4 * F_cap] class work-lists
-    uint32_t *bsum_c;       // [nb] per-block edge counts, then offsets
-    uint32_t *bsum_cls;     // [4 * nb] per-block class counts, then offsets
-    uint32_t *class_count;  // [4]
-    uint32_t *work;         // [4] dynamic work counters
+    uint32_t *bsum;         // [5 * nb] per-block edge counts then the four class counts
+    uint32_t *totals;       // [5] |E_l| then the four class sizes
+    uint32_t *clear_ptr;    // words the classification clears (the relabel bitmap of this hop)
+    int64_t clear_n;
     int32_t *status;
     int32_t nb;             // classify blocks
 };
 
-// One relabel: uniq = ascending unique of keep and add, with ranks.
-struct RelabelArgs {
-    const int32_t *keep;
-    const int64_t *d_keep;
-    int64_t keep_cap;
-    const int32_t *add;
-    const int64_t *d_add;
-    int64_t add_cap;
-    int64_t id_bound;
-    uint32_t *bitmap;   // [W]
-    uint32_t *wprefix;  // [W]
-    uint32_t *bsum;     // [nbw]
-    int64_t W;
-    int32_t nbw;
+// Largest super-batch (sub-batches per call).
+constexpr int kMaxGroup = GNN_MAX_GROUP;
+
+// An id list to relabel: marked into bitmap `bitmap`; if lid is not NULL, lid[i] receives the
+// rank of ids[i] in that bitmap's unique list.  Lists of pass 1 are marked first, alone, and a
+// repeated id among them is reported as a duplicate.
+struct IdList {
+    const int32_t *ids;
+    const int64_t *d_n;  // device count (NULL: cap)
+    int64_t cap;
+    int32_t *lid;
+    int32_t bitmap;
+    int32_t pass;
+};
+
+// The sorted unique list of one bitmap.
+struct BitmapOut {
     int32_t *uniq;
     int64_t uniq_cap;
     int64_t *d_uniq;
-    int32_t *add_lid;
-    int32_t *keep_lid;
+};
+
+struct RelabelArgs {
+    IdList list[2 * kMaxGroup];
+    int32_t nlist;
+    int64_t list_off[2 * kMaxGroup + 1];  // filled by launch_relabel
+    BitmapOut out[kMaxGroup];
+    int32_t nbm;              // bitmaps (one per BitmapOut)
+    int64_t id_bound;
+    uint32_t *bitmap;         // [nbm * W]
+    uint32_t *wprefix;        // [nbm * W]
+    uint32_t *bsum;           // [nbm * nbw]
+    int64_t W;
+    int32_t nbw;              // tiles per bitmap
+    uint32_t *clear_ptr;      // optional region zeroed by the popcount pass
+    int64_t clear_n;
     int32_t *status;
-    int32_t check_dup_keep;
+    int32_t bitmap_cleared;   // the bitmaps are already zero on this stream
+};
+
+// One sub-batch of a super-batch hop: its destinations and the block it receives.
+struct DistSub {
+    const int32_t *front;
+    const int64_t *d_F;
+    int64_t F_cap;
+    int32_t *blk_indptr;
+    int32_t *blk_gid;
+    int64_t E_cap;
+    int64_t *d_E;
+    int32_t tile0;  // first tile of this sub-batch in the launch
+    int32_t ntile;
+};
+
+struct DistArgs {
+    DistSub sub[kMaxGroup];
+    int32_t G;
+    int32_t ntiles;
+    const uint32_t *bm0;       // union bitmap and its word prefixes
+    const uint32_t *wprefix0;
+    int64_t id_bound;
+    const int32_t *u_indptr;   // union block
+    const int32_t *u_gid;
+    int64_t uE_cap;
+    const int64_t *d_U;
+    int64_t U_cap;
+    uint32_t *bsum;            // [ntiles]
+    int32_t *status;
 };
 
 constexpr int kClassifyThreads = 256;
@@ -186,7 +232,8 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);
 hipError_t launch_classify(const HopArgs &a, hipStream_t s);
 hipError_t launch_sample(const HopArgs &a, hipStream_t s);
-hipError_t launch_relabel(const RelabelArgs &a, hipStream_t s);
+hipError_t launch_relabel(RelabelArgs a, hipStream_t s);
+hipError_t launch_dist(const DistArgs &a, hipStream_t s);
 hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,

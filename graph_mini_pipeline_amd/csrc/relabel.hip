@@ -13,6 +13,9 @@
 // order (this is the sorted unique list), and the rank of id v is
 //   prefix[v >> 5] + popcount(word[v >> 5] & ((1 << (v & 31)) - 1)).
 // Work is O(id_bound / 32) words plus O(list length); every output position comes from a scan.
+//
+// One launch sequence serves several bitmaps at once: each id list names the bitmap it marks
+// (a super-batch marks every sub-batch's lists into its own bitmap, or all frontiers into one).
 #include "common.hpp"
 
 namespace gnnmb {
@@ -30,43 +33,62 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t *p, int64_t n, int32_t
 }
 
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n, 256 * 4, 2048)), dim3(256), 0, s, p, n, value);
     return hipGetLastError();
 }
 
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_fill_i32, dim3(grid_for(n, 256 * 4, 2048)), dim3(256), 0, s, p, n, value);
     return hipGetLastError();
 }
 
-// Marks both lists.  With check_dup_keep, a keep id whose bit was already set by another keep id
-// is a duplicate (the keep list is marked by its own launch before the add list).
-__global__ __launch_bounds__(256) void k_mark(const int32_t *ids, const int64_t *d_n, int64_t cap,
-                                             uint32_t *bitmap, int64_t id_bound, int32_t *status,
-                                             int32_t check_dup) {
-    const int64_t n = load_count(d_n, cap);
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int32_t v = ids[i];
-        if (v < 0 || v >= id_bound) {
-            set_status(status, GNN_ERR_OUT_OF_RANGE);
+// List of flattened thread index t: the last list whose offset is <= t.
+__device__ __forceinline__ int find_list(const RelabelArgs &a, int64_t t) {
+    int l = 0;
+    while (l + 1 < a.nlist && a.list_off[l + 1] <= t) ++l;
+    return l;
+}
+
+// Marks the ids of the lists of the given pass.  In pass 1 (the seed lists, marked before
+// anything else) an id whose bit is already set is a duplicate within that list's bitmap.
+__global__ __launch_bounds__(256) void k_mark(RelabelArgs a, int32_t pass) {
+    const int64_t total = a.list_off[a.nlist];
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
+         t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int l = find_list(a, t);
+        const IdList &L = a.list[l];
+        if (L.pass != pass) continue;
+        const int64_t i = t - a.list_off[l];
+        if (i >= load_count(L.d_n, L.cap)) continue;
+        const int32_t v = L.ids[i];
+        if (v < 0 || v >= a.id_bound) {
+            set_status(a.status, GNN_ERR_OUT_OF_RANGE);
             continue;
         }
         const uint32_t bit = 1u << (v & 31);
-        const uint32_t old = atomicOr(&bitmap[v >> 5], bit);
-        if (check_dup && (old & bit)) set_status(status, GNN_ERR_INVALID_ARG);
+        const uint32_t old = atomicOr(&a.bitmap[static_cast<int64_t>(L.bitmap) * a.W + (v >> 5)], bit);
+        if (pass == 1 && (old & bit)) set_status(a.status, GNN_ERR_INVALID_ARG);
     }
 }
 
-// Per-workgroup popcount of kBitmapTile consecutive words.
+// Per-tile popcounts; tile t covers kBitmapTile words of bitmap t / nbw.  Also zeroes the
+// optional clear region (a bitmap no longer needed by this stream).
 __global__ __launch_bounds__(kBitmapThreads) void k_popc_tiles(RelabelArgs a) {
     __shared__ uint32_t red[kBitmapThreads / 64];
-    const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kBitmapTile +
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < a.clear_n;
+         t += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        a.clear_ptr[t] = 0u;
+    const int bm = static_cast<int>(blockIdx.x) / a.nbw;
+    const int lt = static_cast<int>(blockIdx.x) - bm * a.nbw;
+    const uint32_t *words = a.bitmap + static_cast<int64_t>(bm) * a.W;
+    const int64_t w0 = static_cast<int64_t>(lt) * kBitmapTile +
                        static_cast<int64_t>(threadIdx.x) * kBitmapWordsPerThread;
     uint32_t c = 0;
 #pragma unroll
     for (int q = 0; q < kBitmapWordsPerThread; ++q)
-        if (w0 + q < a.W) c += __popc(a.bitmap[w0 + q]);
+        if (w0 + q < a.W) c += __popc(words[w0 + q]);
     c = wave_sum(c);
     if (lane_id() == 0) red[threadIdx.x >> 6] = c;
     __syncthreads();
@@ -77,98 +99,150 @@ __global__ __launch_bounds__(kBitmapThreads) void k_popc_tiles(RelabelArgs a) {
     }
 }
 
-// One workgroup: exclusive scan of the tile popcounts in place; |uniq| to *d_uniq.
+// Many tiles: workgroup b scans the tile popcounts of bitmap b in place and writes its size.
 __global__ __launch_bounds__(1024) void k_popc_scan(RelabelArgs a) {
     __shared__ uint32_t smem[16];
+    const int bm = blockIdx.x;
+    uint32_t *bs = a.bsum + static_cast<int64_t>(bm) * a.nbw;
     const int nb = a.nbw;
     const int per = (nb + 1023) / 1024;
     const int b0 = threadIdx.x * per;
     uint32_t local = 0;
     for (int t = 0; t < per; ++t)
-        if (b0 + t < nb) local += a.bsum[b0 + t];
+        if (b0 + t < nb) local += bs[b0 + t];
     uint32_t total;
     uint32_t run = block_exclusive_scan<uint32_t, 1024>(local, &total, smem);
     for (int t = 0; t < per; ++t) {
         if (b0 + t < nb) {
-            const uint32_t x = a.bsum[b0 + t];
-            a.bsum[b0 + t] = run;
+            const uint32_t x = bs[b0 + t];
+            bs[b0 + t] = run;
             run += x;
         }
     }
     if (threadIdx.x == 0) {
-        *a.d_uniq = total;
-        if (static_cast<int64_t>(total) > a.uniq_cap) set_status(a.status, GNN_ERR_CAPACITY);
+        const BitmapOut &o = a.out[bm];
+        *o.d_uniq = total;
+        if (static_cast<int64_t>(total) > o.uniq_cap) set_status(a.status, GNN_ERR_CAPACITY);
     }
 }
 
-// Word prefixes and the sorted unique ids.
-__global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a) {
+// Word prefixes and the sorted unique ids.  With few tiles (pre_scanned = 0) each workgroup sums
+// the popcounts of the tiles of its bitmap before it, and the bitmap's first tile writes its size.
+__global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a, int32_t pre_scanned) {
     __shared__ uint32_t smem[kBitmapThreads / 64];
-    const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kBitmapTile +
+    __shared__ uint32_t s_red[2][kBitmapThreads / 64];
+    __shared__ uint32_t s_base;
+    const int bm = static_cast<int>(blockIdx.x) / a.nbw;
+    const int lt = static_cast<int>(blockIdx.x) - bm * a.nbw;
+    const BitmapOut &o = a.out[bm];
+    const uint32_t *bs = a.bsum + static_cast<int64_t>(bm) * a.nbw;
+    if (pre_scanned) {
+        if (threadIdx.x == 0) s_base = bs[lt];
+    } else {
+        uint32_t before = 0, all = 0;
+        for (int b = threadIdx.x; b < a.nbw; b += blockDim.x) {
+            const uint32_t x = bs[b];
+            all += x;
+            if (b < lt) before += x;
+        }
+        before = wave_sum(before);
+        all = wave_sum(all);
+        if (lane_id() == 0) {
+            s_red[0][threadIdx.x >> 6] = before;
+            s_red[1][threadIdx.x >> 6] = all;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t b0 = 0, tot = 0;
+            for (int i = 0; i < kBitmapThreads / 64; ++i) {
+                b0 += s_red[0][i];
+                tot += s_red[1][i];
+            }
+            s_base = b0;
+            if (lt == 0) {
+                *o.d_uniq = tot;
+                if (static_cast<int64_t>(tot) > o.uniq_cap) set_status(a.status, GNN_ERR_CAPACITY);
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t *words = a.bitmap + static_cast<int64_t>(bm) * a.W;
+    uint32_t *wpre = a.wprefix + static_cast<int64_t>(bm) * a.W;
+    const int64_t w0 = static_cast<int64_t>(lt) * kBitmapTile +
                        static_cast<int64_t>(threadIdx.x) * kBitmapWordsPerThread;
-    uint32_t words[kBitmapWordsPerThread];
+    uint32_t wv[kBitmapWordsPerThread];
     uint32_t c = 0;
 #pragma unroll
     for (int q = 0; q < kBitmapWordsPerThread; ++q) {
-        words[q] = w0 + q < a.W ? a.bitmap[w0 + q] : 0u;
-        c += __popc(words[q]);
+        wv[q] = w0 + q < a.W ? words[w0 + q] : 0u;
+        c += __popc(wv[q]);
     }
     uint32_t total;
     uint32_t run = block_exclusive_scan<uint32_t, kBitmapThreads>(c, &total, smem);
-    run += a.bsum[blockIdx.x];
+    run += s_base;
 #pragma unroll
     for (int q = 0; q < kBitmapWordsPerThread; ++q) {
         const int64_t w = w0 + q;
         if (w >= a.W) break;
-        a.wprefix[w] = run;
-        uint32_t bits = words[q];
+        wpre[w] = run;
+        uint32_t bits = wv[q];
         while (bits) {
             const int b = __ffs(bits) - 1;
             bits &= bits - 1u;
-            if (static_cast<int64_t>(run) < a.uniq_cap)
-                a.uniq[run] = static_cast<int32_t>(w * 32 + b);
+            if (static_cast<int64_t>(run) < o.uniq_cap) o.uniq[run] = static_cast<int32_t>(w * 32 + b);
             ++run;
         }
     }
 }
 
-// Ranks of both lists (keep first, then add) in the unique list.
+// Ranks of every list that asks for them, in its bitmap's unique list.
 __global__ __launch_bounds__(256) void k_rank(RelabelArgs a) {
-    const int64_t nk = load_count(a.d_keep, a.keep_cap);
-    const int64_t na = load_count(a.d_add, a.add_cap);
-    const int64_t total = a.keep_cap + a.add_cap;
+    const int64_t total = a.list_off[a.nlist];
     for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
          t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const bool is_keep = t < a.keep_cap;
-        const int64_t i = is_keep ? t : t - a.keep_cap;
-        if (i >= (is_keep ? nk : na)) continue;
-        const int32_t v = is_keep ? a.keep[i] : a.add[i];
+        const int l = find_list(a, t);
+        const IdList &L = a.list[l];
+        if (L.lid == nullptr) continue;
+        const int64_t i = t - a.list_off[l];
+        if (i >= load_count(L.d_n, L.cap)) continue;
+        const int32_t v = L.ids[i];
         int32_t r = -1;
         if (v >= 0 && v < a.id_bound) {
-            const uint32_t word = a.bitmap[v >> 5];
-            r = static_cast<int32_t>(a.wprefix[v >> 5] + __popc(word & ((1u << (v & 31)) - 1u)));
+            const int64_t w = static_cast<int64_t>(L.bitmap) * a.W + (v >> 5);
+            r = static_cast<int32_t>(a.wprefix[w] + __popc(a.bitmap[w] & ((1u << (v & 31)) - 1u)));
         }
-        if (is_keep) a.keep_lid[i] = r;
-        else a.add_lid[i] = r;
+        L.lid[i] = r;
     }
 }
 
-hipError_t launch_relabel(const RelabelArgs &a, hipStream_t s) {
-    hipError_t e = launch_fill_u32(a.bitmap, a.W, 0u, s);
-    if (e != hipSuccess) return e;
-    if (a.keep_cap > 0)
-        hipLaunchKernelGGL(k_mark, dim3(grid_for(a.keep_cap, 256, 4096)), dim3(256), 0, s, a.keep,
-                           a.d_keep, a.keep_cap, a.bitmap, a.id_bound, a.status,
-                           a.check_dup_keep);
-    if (a.add_cap > 0)
-        hipLaunchKernelGGL(k_mark, dim3(grid_for(a.add_cap, 256, 4096)), dim3(256), 0, s, a.add,
-                           a.d_add, a.add_cap, a.bitmap, a.id_bound, a.status, 0);
-    hipLaunchKernelGGL(k_popc_tiles, dim3(a.nbw), dim3(kBitmapThreads), 0, s, a);
-    hipLaunchKernelGGL(k_popc_scan, dim3(1), dim3(1024), 0, s, a);
-    hipLaunchKernelGGL(k_emit, dim3(a.nbw), dim3(kBitmapThreads), 0, s, a);
-    if (a.keep_cap + a.add_cap > 0)
-        hipLaunchKernelGGL(k_rank, dim3(grid_for(a.keep_cap + a.add_cap, 256, 4096)), dim3(256),
-                           0, s, a);
+// Tiles per bitmap at or below which k_emit computes its own offsets.
+constexpr int kSelfScanMaxTiles = 512;
+
+hipError_t launch_relabel(RelabelArgs a, hipStream_t s) {
+    int64_t total = 0;
+    bool any_rank = false, any_pass1 = false;
+    for (int l = 0; l < a.nlist; ++l) {
+        a.list_off[l] = total;
+        total += a.list[l].cap;
+        any_rank |= a.list[l].lid != nullptr;
+        any_pass1 |= a.list[l].pass == 1;
+    }
+    a.list_off[a.nlist] = total;
+    if (!a.bitmap_cleared) {
+        hipError_t e = launch_fill_u32(a.bitmap, static_cast<int64_t>(a.nbm) * a.W, 0u, s);
+        if (e != hipSuccess) return e;
+    }
+    if (total > 0) {
+        const unsigned grid = grid_for(total, 256, 4096);
+        if (any_pass1) hipLaunchKernelGGL(k_mark, dim3(grid), dim3(256), 0, s, a, 1);
+        hipLaunchKernelGGL(k_mark, dim3(grid), dim3(256), 0, s, a, 0);
+    }
+    hipLaunchKernelGGL(k_popc_tiles, dim3(a.nbm * a.nbw), dim3(kBitmapThreads), 0, s, a);
+    const int pre = a.nbw > kSelfScanMaxTiles ? 1 : 0;
+    if (pre) hipLaunchKernelGGL(k_popc_scan, dim3(a.nbm), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(k_emit, dim3(a.nbm * a.nbw), dim3(kBitmapThreads), 0, s, a, pre);
+    if (any_rank && total > 0)
+        hipLaunchKernelGGL(k_rank, dim3(grid_for(total, 256, 4096)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

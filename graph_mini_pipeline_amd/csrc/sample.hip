@@ -19,8 +19,8 @@
 //   GROUP  k < deg <= group_max   16 lanes per node (4 nodes per wavefront)
 //   WAVE   group_max < deg <= wave_max   one wavefront per node
 //   BLOCK  deg > wave_max          one 512-thread workgroup per node
-// Random classes fetch work dynamically from a per-class counter; results do not depend on the
-// order in which nodes are processed.
+// Each class walks its work-list with a static stride (no shared work counter); results do not
+// depend on the order in which nodes are processed.
 #include <math.h>
 
 #include "common.hpp"
@@ -38,6 +38,10 @@ __device__ __forceinline__ int32_t node_class(int64_t deg, int k, int group_max,
 
 __global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) {
     __shared__ uint32_t red[5][kClassifyThreads / 64];
+    // The relabel bitmap of this hop is cleared here, long before the relabel reads it.
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < a.clear_n;
+         t += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        a.clear_ptr[t] = 0u;
     const int64_t F = load_count(a.d_F, a.F_cap);
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kClassifyTile +
                          static_cast<int64_t>(threadIdx.x) * kClassifyItems;
@@ -71,18 +75,17 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) 
     if (threadIdx.x < 5) {
         uint32_t s = 0;
         for (int i = 0; i < kClassifyThreads / 64; ++i) s += red[threadIdx.x][i];
-        if (threadIdx.x == 0) a.bsum_c[blockIdx.x] = s;
-        else a.bsum_cls[(threadIdx.x - 1) * a.nb + blockIdx.x] = s;
+        a.bsum[static_cast<int64_t>(threadIdx.x) * a.nb + blockIdx.x] = s;
     }
 }
 
-// One workgroup scans the per-block sums (edge counts and the four class counts) in place.
+// Many blocks: one workgroup scans the per-block sums (edge counts, four class counts) in place.
 __global__ __launch_bounds__(1024) void k_classify_scan(HopArgs a) {
     __shared__ uint32_t smem[16];
     const int nb = a.nb;
     const int per = (nb + 1023) / 1024;
     for (int col = 0; col < 5; ++col) {
-        uint32_t *arr = col == 0 ? a.bsum_c : a.bsum_cls + static_cast<int64_t>(col - 1) * nb;
+        uint32_t *arr = a.bsum + static_cast<int64_t>(col) * nb;
         const int b0 = threadIdx.x * per;
         uint32_t local = 0;
         for (int t = 0; t < per; ++t)
@@ -96,24 +99,64 @@ __global__ __launch_bounds__(1024) void k_classify_scan(HopArgs a) {
                 run += x;
             }
         }
-        if (threadIdx.x == 0) {
-            if (col == 0) {
-                const int64_t F = load_count(a.d_F, a.F_cap);
-                a.blk_indptr[F] = static_cast<int32_t>(total);
-                *a.d_E = total;
-                if (static_cast<int64_t>(total) > a.E_cap) set_status(a.status, GNN_ERR_CAPACITY);
-            } else {
-                a.class_count[col - 1] = total;
-                a.work[col - 1] = 0;
-            }
-        }
+        if (threadIdx.x == 0) a.totals[col] = total;
     }
 }
 
-__global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a) {
+// Places every frontier node: block indptr (exclusive scan of c) and the stable class lists.
+// With few blocks (pre_scanned = 0) each block sums the partials of the blocks before it;
+// otherwise k_classify_scan has already turned them into offsets and totals.
+__global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a, int32_t pre_scanned) {
     __shared__ uint32_t sm_c[kClassifyThreads / 64];
     __shared__ uint64_t sm_k[kClassifyThreads / 64];
+    __shared__ uint32_t s_off[5];
+    __shared__ uint32_t s_tot[5];
+    __shared__ uint32_t s_red[10][kClassifyThreads / 64];
     const int64_t F = load_count(a.d_F, a.F_cap);
+    if (pre_scanned) {
+        if (threadIdx.x < 5) {
+            s_off[threadIdx.x] = a.bsum[static_cast<int64_t>(threadIdx.x) * a.nb + blockIdx.x];
+            s_tot[threadIdx.x] = a.totals[threadIdx.x];
+        }
+    } else {
+        uint32_t before[5] = {0, 0, 0, 0, 0}, all[5] = {0, 0, 0, 0, 0};
+        for (int b = threadIdx.x; b < a.nb; b += blockDim.x) {
+#pragma unroll
+            for (int col = 0; col < 5; ++col) {
+                const uint32_t x = a.bsum[static_cast<int64_t>(col) * a.nb + b];
+                all[col] += x;
+                if (b < static_cast<int>(blockIdx.x)) before[col] += x;
+            }
+        }
+        const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+        for (int col = 0; col < 5; ++col) {
+            const uint32_t s0 = wave_sum(before[col]);
+            const uint32_t s1 = wave_sum(all[col]);
+            if (lane == 0) {
+                s_red[col][w] = s0;
+                s_red[5 + col][w] = s1;
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < 10) {
+            uint32_t s = 0;
+            for (int i = 0; i < kClassifyThreads / 64; ++i) s += s_red[threadIdx.x][i];
+            if (threadIdx.x < 5) s_off[threadIdx.x] = s;
+            else s_tot[threadIdx.x - 5] = s;
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x < 5) {
+        const uint32_t total = s_tot[threadIdx.x];
+        if (!pre_scanned) a.totals[threadIdx.x] = total;
+        if (threadIdx.x == 0) {
+            a.blk_indptr[F] = static_cast<int32_t>(total);
+            *a.d_E = total;
+            if (static_cast<int64_t>(total) > a.E_cap) set_status(a.status, GNN_ERR_CAPACITY);
+        }
+    }
+    __syncthreads();
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kClassifyTile +
                          static_cast<int64_t>(threadIdx.x) * kClassifyItems;
     int32_t pk[kClassifyItems];
@@ -132,7 +175,7 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a
     uint64_t ktot;
     uint32_t coff = block_exclusive_scan<uint32_t, kClassifyThreads>(csum, &ctot, sm_c);
     uint64_t koff = block_exclusive_scan<uint64_t, kClassifyThreads>(kc, &ktot, sm_k);
-    coff += a.bsum_c[blockIdx.x];
+    coff += s_off[0];
 #pragma unroll
     for (int q = 0; q < kClassifyItems; ++q) {
         if (pk[q] < 0) continue;
@@ -142,26 +185,7 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a
         coff += static_cast<uint32_t>(pk[q] >> 2);
         const uint32_t r = static_cast<uint32_t>((koff >> (16 * cls)) & 0xFFFF);
         koff += 1ull << (16 * cls);
-        const uint32_t pos = a.bsum_cls[static_cast<int64_t>(cls) * a.nb + blockIdx.x] + r;
-        a.lists[static_cast<int64_t>(cls) * a.F_cap + pos] = static_cast<int32_t>(i);
-    }
-}
-
-// ---- FULL: one lane per node --------------------------------------------------------------------
-
-__global__ __launch_bounds__(256) void k_sample_full(HopArgs a) {
-    const int64_t n = a.class_count[kFull];
-    const int32_t *list = a.lists;
-    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
-         t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int32_t i = list[t];
-        const int32_t v = a.front[i];
-        if (v < 0 || v >= a.num_nodes) continue;
-        const int64_t s = row_ptr(a.indptr, a.ib, v);
-        const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - s;
-        const int64_t o = a.blk_indptr[i];
-        for (int64_t j = 0; j < deg; ++j)
-            if (o + j < a.E_cap) a.blk_gid[o + j] = a.indices[s + j];
+        a.lists[static_cast<int64_t>(cls) * a.F_cap + s_off[1 + cls] + r] = static_cast<int32_t>(i);
     }
 }
 
@@ -201,95 +225,128 @@ __device__ __forceinline__ bool next_tau(int cnt, int k, int cap, uint64_t &tau,
     return true;
 }
 
-// ---- GROUP and WAVE: G lanes per node -----------------------------------------------------------
-
+// ---- one random node on G lanes of a wavefront ---------------------------------------------------
+//
+// Control flow is uniform across the G lanes of the group; other groups of the same wavefront may
+// be elsewhere.  s_key / s_pos are the group's private LDS candidate arrays of CAP entries.
 template <int G, int CAP>
-__global__ __launch_bounds__(256) void k_sample_lanes(HopArgs a, int32_t cls) {
-    constexpr int NG = 64 / G;       // nodes per wavefront
-    constexpr int SLOTS = 4 * NG;    // nodes per workgroup
-    __shared__ uint64_t s_key[SLOTS][CAP];
-    __shared__ int32_t s_pos[SLOTS][CAP];
-    const int lane = lane_id();
-    const int grp = lane / G;
-    const int gl = lane % G;
-    const int slot = static_cast<int>(threadIdx.x >> 6) * NG + grp;
-    const uint64_t gmask = G == 64 ? ~0ull : (((1ull << G) - 1ull) << (grp * G));
-    const uint64_t below = (1ull << lane) - 1ull;  // lanes below this one
-    const int64_t n = a.class_count[cls];
-    const int32_t *list = a.lists + static_cast<int64_t>(cls) * a.F_cap;
+__device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, uint64_t *s_key,
+                                                  int32_t *s_pos, int gl, uint64_t gmask,
+                                                  uint64_t below) {
     const int k = a.k;
-    for (;;) {
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&a.work[cls], static_cast<uint32_t>(NG));
-        base = __shfl(base, 0, 64);
-        if (static_cast<int64_t>(base) >= n) break;
-        const int64_t item = static_cast<int64_t>(base) + grp;
-        if (item < n) {
-            const int32_t i = list[item];
+    const int32_t v = a.front[i];
+    const int64_t start = row_ptr(a.indptr, a.ib, v);
+    const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - start;
+    const int64_t out0 = a.blk_indptr[i];
+    const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
+    uint64_t tau = initial_tau(deg, k), lo = 0, hi = 0;
+    bool has_lo = false, has_hi = false, fail = false;
+    int cnt = 0;
+    for (int it = 0; it < 128; ++it) {
+        cnt = 0;
+        uint64_t z = ns + kGamma * static_cast<uint64_t>(gl + 1);
+        const uint64_t step = kGamma * static_cast<uint64_t>(G);
+        for (int64_t j0 = 0; j0 < deg; j0 += G) {
+            const int64_t j = j0 + gl;
+            const uint64_t key = mix64(z);
+            z += step;
+            const bool p = j < deg && key <= tau;
+            const uint64_t m = __ballot(p) & gmask;
+            if (p) {
+                const int pos = cnt + __popcll(m & below);
+                if (pos < CAP) {
+                    s_key[pos] = key;
+                    s_pos[pos] = static_cast<int32_t>(j);
+                }
+            }
+            cnt += __popcll(m);
+        }
+        if (!next_tau(cnt, k, CAP, tau, lo, hi, has_lo, has_hi, fail)) break;
+    }
+    if (fail || cnt < k || cnt > CAP) {
+        if (gl == 0) set_status(a.status, GNN_ERR_INTERNAL);
+        cnt = 0;
+    }
+    wave_lds_sync();
+    // Candidates sit in ascending position; keep those of rank < k among (key, pos).
+    int outc = 0;
+    for (int c0 = 0; c0 < cnt; c0 += G) {
+        const int c = c0 + gl;
+        bool sel = false;
+        int32_t jc = 0;
+        if (c < cnt) {
+            const uint64_t kc = s_key[c];
+            jc = s_pos[c];
+            int r = 0;
+            for (int t = 0; t < cnt; ++t) {
+                const uint64_t kt = s_key[t];
+                const int32_t jt = s_pos[t];
+                r += (kt < kc) | ((kt == kc) & (jt < jc));
+            }
+            sel = r < k;
+        }
+        const uint64_t m = __ballot(sel) & gmask;
+        if (sel) {
+            const int64_t o = out0 + outc + __popcll(m & below);
+            if (o < a.E_cap) a.blk_gid[o] = a.indices[start + jc];
+        }
+        outc += __popcll(m);
+    }
+    wave_lds_sync();
+}
+
+// ---- FULL, GROUP and WAVE classes in one launch ---------------------------------------------------
+//
+// Workgroups [0, nb_wave) take WAVE nodes (one wavefront each), the next nb_group workgroups take
+// GROUP nodes (16 lanes each), the rest FULL nodes (one lane each).  Each role walks its class list
+// with a static stride, so no two wavefronts contend for a shared counter.
+constexpr int kSmallLds = 4 * kWaveCap;  // = 16 * kGroupCap candidate entries per workgroup
+static_assert(4 * kWaveCap == 16 * kGroupCap, "the two roles share one LDS layout");
+
+__global__ __launch_bounds__(256) void k_sample_small(HopArgs a, int32_t nb_wave, int32_t nb_group) {
+    __shared__ uint64_t s_key[kSmallLds];
+    __shared__ int32_t s_pos[kSmallLds];
+    const int lane = lane_id();
+    const int wv = static_cast<int>(threadIdx.x >> 6);
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int bid = static_cast<int>(blockIdx.x);
+    if (bid < nb_wave) {
+        const int64_t n = a.totals[1 + kWave];
+        const int32_t *list = a.lists + static_cast<int64_t>(kWave) * a.F_cap;
+        for (int64_t item = static_cast<int64_t>(bid) * 4 + wv; item < n;
+             item += static_cast<int64_t>(nb_wave) * 4)
+            sample_node_lanes<64, kWaveCap>(a, list[item], s_key + wv * kWaveCap,
+                                            s_pos + wv * kWaveCap, lane, ~0ull, below);
+    } else if (bid < nb_wave + nb_group) {
+        constexpr int G = kGroupLanes;
+        const int grp = lane / G;
+        const int slot = wv * (64 / G) + grp;
+        const uint64_t gmask = ((1ull << G) - 1ull) << (grp * G);
+        const int64_t n = a.totals[1 + kGroup];
+        const int32_t *list = a.lists + static_cast<int64_t>(kGroup) * a.F_cap;
+        for (int64_t item = static_cast<int64_t>(bid - nb_wave) * 16 + slot; item < n;
+             item += static_cast<int64_t>(nb_group) * 16)
+            sample_node_lanes<G, kGroupCap>(a, list[item], s_key + slot * kGroupCap,
+                                            s_pos + slot * kGroupCap, lane % G, gmask, below);
+    } else {
+        const int64_t n = a.totals[1 + kFull];
+        const int32_t *list = a.lists;
+        const int64_t nb_full = static_cast<int64_t>(gridDim.x) - nb_wave - nb_group;
+        for (int64_t t = static_cast<int64_t>(bid - nb_wave - nb_group) * 256 + threadIdx.x; t < n;
+             t += nb_full * 256) {
+            const int32_t i = list[t];
             const int32_t v = a.front[i];
-            const int64_t start = row_ptr(a.indptr, a.ib, v);
-            const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - start;
-            const int64_t out0 = a.blk_indptr[i];
-            const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
-            uint64_t tau = initial_tau(deg, k), lo = 0, hi = 0;
-            bool has_lo = false, has_hi = false, fail = false;
-            int cnt = 0;
-            for (int it = 0; it < 128; ++it) {
-                cnt = 0;
-                uint64_t z = ns + kGamma * static_cast<uint64_t>(gl + 1);
-                const uint64_t step = kGamma * static_cast<uint64_t>(G);
-                for (int64_t j0 = 0; j0 < deg; j0 += G) {
-                    const int64_t j = j0 + gl;
-                    const uint64_t key = mix64(z);
-                    z += step;
-                    const bool p = j < deg && key <= tau;
-                    const uint64_t m = __ballot(p) & gmask;
-                    if (p) {
-                        const int pos = cnt + __popcll(m & below);
-                        if (pos < CAP) {
-                            s_key[slot][pos] = key;
-                            s_pos[slot][pos] = static_cast<int32_t>(j);
-                        }
-                    }
-                    cnt += __popcll(m);
-                }
-                if (!next_tau(cnt, k, CAP, tau, lo, hi, has_lo, has_hi, fail)) break;
-            }
-            if (fail || cnt < k || cnt > CAP) {
-                if (gl == 0) set_status(a.status, GNN_ERR_INTERNAL);
-                cnt = 0;
-            }
-            wave_lds_sync();
-            // Candidates sit in ascending position; keep those of rank < k among (key, pos).
-            int outc = 0;
-            for (int c0 = 0; c0 < cnt; c0 += G) {
-                const int c = c0 + gl;
-                bool sel = false;
-                int32_t jc = 0;
-                if (c < cnt) {
-                    const uint64_t kc = s_key[slot][c];
-                    jc = s_pos[slot][c];
-                    int r = 0;
-                    for (int t = 0; t < cnt; ++t) {
-                        const uint64_t kt = s_key[slot][t];
-                        const int32_t jt = s_pos[slot][t];
-                        r += (kt < kc) | ((kt == kc) & (jt < jc));
-                    }
-                    sel = r < k;
-                }
-                const uint64_t m = __ballot(sel) & gmask;
-                if (sel) {
-                    const int64_t o = out0 + outc + __popcll(m & below);
-                    if (o < a.E_cap) a.blk_gid[o] = a.indices[start + jc];
-                }
-                outc += __popcll(m);
-            }
-            wave_lds_sync();
+            if (v < 0 || v >= a.num_nodes) continue;
+            const int64_t st = row_ptr(a.indptr, a.ib, v);
+            const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - st;
+            const int64_t o = a.blk_indptr[i];
+            for (int64_t j = 0; j < deg; ++j)
+                if (o + j < a.E_cap) a.blk_gid[o + j] = a.indices[st + j];
         }
     }
 }
 
-// ---- BLOCK: one workgroup per node --------------------------------------------------------------
+// ---- BLOCK: one workgroup per node ----------------------------------------------------------------
 
 __global__ __launch_bounds__(kBlockThreads) void k_sample_block(HopArgs a) {
     constexpr int NT = kBlockThreads;
@@ -298,17 +355,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample_block(HopArgs a) {
     __shared__ int32_t s_pos[CAP];
     __shared__ uint8_t s_sel[CAP];
     __shared__ uint32_t s_cnt;
-    __shared__ uint32_t s_item;
     const int lane = lane_id();
     const uint64_t below = (1ull << lane) - 1ull;
-    const int64_t n = a.class_count[kBlock];
+    const int64_t n = a.totals[1 + kBlock];
     const int32_t *list = a.lists + static_cast<int64_t>(kBlock) * a.F_cap;
     const int k = a.k;
-    for (;;) {
-        if (threadIdx.x == 0) s_item = atomicAdd(&a.work[kBlock], 1u);
-        __syncthreads();
-        const int64_t item = s_item;
-        if (item >= n) break;
+    for (int64_t item = blockIdx.x; item < n; item += gridDim.x) {
         const int32_t i = list[item];
         const int32_t v = a.front[i];
         const int64_t start = row_ptr(a.indptr, a.ib, v);
@@ -351,6 +403,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample_block(HopArgs a) {
             if (threadIdx.x == 0) set_status(a.status, GNN_ERR_INTERNAL);
             cnt = 0;
         }
+        // Candidates are in arbitrary order: rank by (key, pos), then place by position.
         for (int c = threadIdx.x; c < cnt; c += NT) {
             const uint64_t kc = s_key[c];
             const int32_t jc = s_pos[c];
@@ -376,22 +429,26 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample_block(HopArgs a) {
 
 // ---- launchers ---------------------------------------------------------------------------------
 
+// Blocks of the classification at or below which each scatter workgroup sums the partials of the
+// workgroups before it (one launch fewer than a separate scan).
+constexpr int kSelfScanMaxBlocks = 512;
+
 hipError_t launch_classify(const HopArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_classify_count, dim3(a.nb), dim3(kClassifyThreads), 0, s, a);
-    hipLaunchKernelGGL(k_classify_scan, dim3(1), dim3(1024), 0, s, a);
-    hipLaunchKernelGGL(k_classify_scatter, dim3(a.nb), dim3(kClassifyThreads), 0, s, a);
+    const int pre = a.nb > kSelfScanMaxBlocks ? 1 : 0;
+    if (pre) hipLaunchKernelGGL(k_classify_scan, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(k_classify_scatter, dim3(a.nb), dim3(kClassifyThreads), 0, s, a, pre);
     return hipGetLastError();
 }
 
 hipError_t launch_sample(const HopArgs &a, hipStream_t s) {
     const int64_t F = a.F_cap;
-    hipLaunchKernelGGL(k_sample_full, dim3(grid_for(F, 256, 1024)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_sample_lanes<kGroupLanes, kGroupCap>),
-                       dim3(grid_for(F, 4 * (64 / kGroupLanes), 2048)), dim3(256), 0, s, a,
-                       static_cast<int32_t>(kGroup));
-    hipLaunchKernelGGL((k_sample_lanes<64, kWaveCap>), dim3(grid_for(F, 4, 2048)), dim3(256), 0,
-                       s, a, static_cast<int32_t>(kWave));
-    hipLaunchKernelGGL(k_sample_block, dim3(grid_for(F, 1, 512)), dim3(kBlockThreads), 0, s, a);
+    const int nb_wave = static_cast<int>(grid_for(F, 4, 2048));
+    const int nb_group = static_cast<int>(grid_for(F, 16, 1024));
+    const int nb_full = static_cast<int>(grid_for(F, 256, 256));
+    hipLaunchKernelGGL(k_sample_small, dim3(nb_wave + nb_group + nb_full), dim3(256), 0, s, a,
+                       nb_wave, nb_group);
+    hipLaunchKernelGGL(k_sample_block, dim3(grid_for(F, 1, 1024)), dim3(kBlockThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ extern "C" {
 #endif
 
 #define GNN_MAX_HOPS 8
+#define GNN_MAX_GROUP 16 /* sub-batches per super-batch */
 
 typedef int32_t gnn_status;
 #define GNN_OK 0
@@ -68,6 +69,7 @@ typedef struct gnn_graph {
 /* Worst-case element counts per hop, l = 1..K at index l-1. */
 typedef struct gnn_caps {
     int32_t num_hops;                /* K */
+    int32_t fanouts[GNN_MAX_HOPS];   /* k_l */
     int64_t n_seeds;                 /* |V_0| */
     int64_t frontier[GNN_MAX_HOPS];  /* |V_{l-1}| bound: destinations of block l */
     int64_t edges[GNN_MAX_HOPS];     /* |E_l| bound: sampled edges of block l */

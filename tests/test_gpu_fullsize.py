@@ -1,0 +1,81 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The dense-neighbourhood workload (233,000 nodes, 115M edges, 602-d rows with stride 604, batches
+of 1024 seeds, fanouts [25, 10]) is generated on the GPU; whole batches are compared with the
+oracle (bit-exact blocks and rows, means within 1e-5 * max|X|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import compare_with_oracle
+
+pytestmark = pytest.mark.gpu
+
+gm = pytest.importorskip("graph_mini_pipeline_amd")
+
+
+@pytest.fixture(scope="module")
+def dense():
+    cfg = synth.CONFIGS["dense"]
+    dev = torch.device("cuda")
+    g = synth.build_graph(cfg, device=dev)
+    table = torch.empty(cfg.num_nodes, cfg.ld, dtype=torch.float32, device=dev)
+    synth.make_features(cfg, table)
+    order = synth.epoch_seed_order(cfg, 0, device=dev).contiguous()
+    host = (g.indptr.cpu().numpy(), g.indices.cpu().numpy(), table.cpu().numpy(),
+            order.cpu().numpy())
+    return cfg, g, table, order, host
+
+
+def _run(cfg, g, table, order, batches, seed64):
+    dg = gm.DeviceGraph(cfg.num_nodes, g.indptr, g.indices)
+    fs = gm.gnn_feature_store_create(table, cfg.d)
+    lo = batches[0] * cfg.batch
+    hi = min(order.numel(), (batches[-1] + 1) * cfg.batch)
+    ptr = [b * cfg.batch - lo for b in batches] + [hi - lo]
+    outs = [gm.MinibatchOut(gm.gnn_capacity(ptr[j + 1] - ptr[j], cfg.fanouts, cfg.num_nodes),
+                            cfg.d, cfg.ld) for j in range(len(batches))]
+    caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
+    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, len(batches)), dtype=torch.uint8,
+                     device="cuda")
+    gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, seed64, outs, ws)
+    assert gm.gnn_read_device_status(ws) == gm.GNN_OK
+    return outs, ptr
+
+
+@pytest.mark.parametrize("b", [0, 146])
+def test_dense_single_batch(dense, b):
+    cfg, g, table, order, (indptr, indices, x, order_h) = dense
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, b)
+    outs, _ = _run(cfg, g, table, order, [b], seed64)
+    seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
+    ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+    compare_with_oracle(outs[0], ref, cfg.d)
+
+
+def test_dense_superbatch_of_8(dense):
+    cfg, g, table, order, (indptr, indices, x, order_h) = dense
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 3)
+    batches = list(range(24, 32))
+    outs, ptr = _run(cfg, g, table, order, batches, seed64)
+    for j in (0, 5):
+        b = batches[j]
+        seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
+        ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+        compare_with_oracle(outs[j], ref, cfg.d)
+
+
+def test_dense_superbatch_last_partial(dense):
+    # the epoch's last super-batch of 8: batches 144..146, the last one short (496 seeds)
+    cfg, g, table, order, (indptr, indices, x, order_h) = dense
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 18)
+    batches = [144, 145, 146]
+    outs, ptr = _run(cfg, g, table, order, batches, seed64)
+    b = 146
+    seeds = order_h[b * cfg.batch:]
+    assert len(seeds) == 496
+    ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+    compare_with_oracle(outs[2], ref, cfg.d)

@@ -315,3 +315,34 @@ def test_superbatch_equals_separate_runs(tiny):
     for g in range(4):
         ref = oracle.minibatch(indptr, indices, x, seeds[ptr[g]:ptr[g + 1]], cfg.fanouts, 77)
         compare_with_oracle(outs[g], ref, cfg.d)
+
+
+def test_superbatch_of_16_with_overlap(tiny):
+    # 16 sub-batches; sub-batches may share seeds (each must be distinct within itself)
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    parts = [order[i * 40:(i + 1) * 40 + 13] for i in range(16)]   # consecutive parts overlap
+    seeds = np.concatenate(parts)
+    ptr = np.concatenate([[0], np.cumsum([len(p) for p in parts])]).tolist()
+    outs, st = run_minibatch(dg, fs, seeds, [12, 6, 3], 5150, group_ptr=ptr)
+    assert st == gm.GNN_OK
+    for g in (0, 7, 15):
+        ref = oracle.minibatch(indptr, indices, x, parts[g], [12, 6, 3], 5150)
+        compare_with_oracle(outs[g], ref, cfg.d)
+
+
+def test_superbatch_duplicate_within_sub_batch_reported(tiny):
+    cfg, indptr, indices, x, order = tiny
+    seeds = np.array([1, 2, 3, 3, 4], np.int32)      # sub-batch 1 holds 3 twice
+    _, st = run_minibatch(device_graph(indptr, indices), _store(x), seeds, [3], 1,
+                          group_ptr=[0, 2, 5])
+    assert st == gm.GNN_ERR_INVALID_ARG
+
+
+def test_superbatch_too_large_rejected(tiny):
+    cfg, indptr, indices, x, order = tiny
+    with pytest.raises(gm.GnnError) as e:
+        run_minibatch(device_graph(indptr, indices), _store(x), order[:17], [3], 1,
+                      group_ptr=list(range(18)))
+    assert e.value.status == gm.GNN_ERR_UNSUPPORTED
