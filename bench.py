@@ -51,10 +51,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps (default: one epoch)")
-    ap.add_argument("--group", type=int, default=1,
+    ap.add_argument("--group", type=int, default=8,
                     help="mini-batches per super-batch (one step = one super-batch)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dense")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="HIP streams the super-batches are issued on, round robin; each stream has "
+                         "its own workspace and outputs, so one stream's sampling overlaps another's "
+                         "gather and aggregation")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -89,17 +93,21 @@ def main():
     dg = gm.DeviceGraph(cfg.num_nodes, graph.indptr, graph.indices)
     fs = gm.gnn_feature_store_create(table, cfg.d)
     caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
-    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
-
-    outs = {}   # one output set per (position in the super-batch, seed count)
+    S = max(1, args.streams)
+    wss = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
+           for _ in range(S)]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(S)] if S > 1 else [None]
+    outs = [{} for _ in range(S)]   # per stream: one output set per (position, seed count)
 
     def batch_range(s):
         b0 = s * G
         return list(range(b0, min(b0 + G, n_batches)))
 
     def step(st, timer=None):
-        """Super-batch st (mod the epoch): its batches share one seed.  Returns [(b, n, out)]."""
+        """Super-batch st (mod the epoch) on stream st % S: its batches share one seed.
+        Returns (super-batch index, [(b, n, out)])."""
         s = st % n_super
+        q = st % S
         bs = batch_range(s)
         lo = bs[0] * cfg.batch
         hi = min(order.numel(), (bs[-1] + 1) * cfg.batch)
@@ -107,18 +115,19 @@ def main():
         mine = []
         for j, b in enumerate(bs):
             n = ptr[j + 1] - ptr[j]
-            if (j, n) not in outs:
-                outs[(j, n)] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
-                                               cfg.d, cfg.ld)
-            mine.append((b, n, outs[(j, n)]))
+            if (j, n) not in outs[q]:
+                outs[q][(j, n)] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
+                                                  cfg.d, cfg.ld)
+            mine.append((b, n, outs[q][(j, n)]))
         gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, gm.gnn_batch_seed(cfg.rng_seed, s),
-                         [m[2] for m in mine], ws, timer=timer)
+                         [m[2] for m in mine], wss[q], timer=timer, stream=streams[q])
         return s, mine
 
-    for b in range(args.warmup):
+    torch.cuda.synchronize()
+    for b in range(max(args.warmup, S)):
         step(b)
     torch.cuda.synchronize()
-    assert gm.gnn_read_device_status(ws) == gm.GNN_OK
+    assert all(gm.gnn_read_device_status(w) == gm.GNN_OK for w in wss)
 
     # Timed region 1: the headline throughput, nothing but the steps on the stream.
     torch.cuda.synchronize()
@@ -127,7 +136,7 @@ def main():
         step(b)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    status = gm.gnn_read_device_status(ws)
+    status = min(gm.gnn_read_device_status(w) for w in wss)
 
     # Timed region 2: the same steps with HIP events at the stage boundaries (the events cost a few
     # microseconds each, so they stay out of region 1).
@@ -148,6 +157,7 @@ def main():
     payload = []
     for b in range(steps):
         _, mine = step(b)
+        torch.cuda.synchronize()
         g_s, m_s, p_s = 0, [0] * K, 0
         for _, n, out in mine:
             cnt = out.blocks.counts.cpu().tolist()
@@ -186,7 +196,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": workload_name(cfg), "batches_per_epoch": n_batches,
-                   "super_batch": G, "step": f"one super-batch of {G} mini-batch(es)"},
+                   "super_batch": G, "streams": S,
+                   "step": f"one super-batch of {G} mini-batch(es)"},
         "ms_per_minibatch": wall / sum(len(batch_range(b % n_super)) for b in range(steps)) * 1e3,
         "status": gm.gnn_status_string(status),
         "sampled_edges_per_s_sampling_stage": tot_edges / t_sample,
@@ -206,6 +217,15 @@ def main():
         "ms_per_step_with_stage_events": wall_events / steps * 1e3,
         "input_generation_s": t_gen,
     }
+
+    # Counter calibration: one plain 1 GiB device copy by k_copy_probe (untimed).  Profiling runs
+    # of this command read its fetched / written bytes to scale the other kernels' counters.
+    probe_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    probe_dst = torch.empty_like(probe_src)
+    gm.gnn_copy_probe(probe_src, probe_dst)
+    torch.cuda.synchronize()
+    result["copy_probe_bytes"] = probe_src.numel() * 4
+    del probe_src, probe_dst
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, graph, table, order, step, args.cpu_seconds,
@@ -228,6 +248,7 @@ def cpu_baseline(cfg, graph, table, order, step, budget_s, gpu_value):
     spent, edges, batches, parity, st = 0.0, 0, 0, True, 0
     while spent < budget_s and batches < 64:
         s, mine = step(st)
+        torch.cuda.synchronize()
         st += 1
         seed64 = oracle.batch_seed(cfg.rng_seed, s)
         for b, n, got in mine:

@@ -16,7 +16,7 @@ import torch
 from . import _abi
 from ._abi import (GNN_ERR_CAPACITY, GNN_ERR_HIP, GNN_ERR_INTERNAL, GNN_ERR_INVALID_ARG,  # noqa
                    GNN_ERR_OUT_OF_RANGE, GNN_ERR_UNSUPPORTED, GNN_MAX_HOPS, GNN_OK, GNN_SYNC,
-                   GNN_TIMER_EVENTS)
+                   GNN_TIMER_STAGES)
 
 __all__ = [
     "GnnError", "DeviceGraph", "Blocks", "MinibatchOut", "FeatureStore", "Timer", "Options",
@@ -24,7 +24,7 @@ __all__ = [
     "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
     "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_minibatch",
     "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
-    "gnn_timer_elapsed", "lib",
+    "gnn_timer_elapsed", "gnn_copy_probe", "lib",
 ]
 
 lib = _abi.lib
@@ -193,6 +193,8 @@ def gnn_unique_relabel(keep: torch.Tensor, add: torch.Tensor, id_bound: int, uni
                  (keep_lid, "keep_lid")):
         _need(t, torch.int32, n)
     _need(d_n_uniq, torch.int64, "d_n_uniq")
+    if add_lid.numel() < add.numel() or keep_lid.numel() < keep.numel():
+        raise ValueError("add_lid / keep_lid shorter than add / keep")
     st = lib().gnn_unique_relabel(_ptr(keep), keep.numel(), _ptr(add), _ptr(d_n_add), add.numel(),
                                   id_bound, _ptr(uniq), uniq.numel(), _ptr(d_n_uniq), _ptr(add_lid),
                                   _ptr(keep_lid), _ptr(ws), ws.numel() * ws.element_size(),
@@ -306,9 +308,9 @@ class Timer:
     def elapsed(self):
         """List of per-call stage times in ms: [sample+relabel, gather, outer mean, other means]."""
         n = ctypes.c_int32(0)
-        buf = (ctypes.c_float * (self.n_records * (GNN_TIMER_EVENTS - 1)))()
+        buf = (ctypes.c_float * (self.n_records * GNN_TIMER_STAGES))()
         _ok(lib().gnn_timer_elapsed(self.handle, ctypes.byref(n), buf), "gnn_timer_elapsed")
-        k = GNN_TIMER_EVENTS - 1
+        k = GNN_TIMER_STAGES
         return [list(buf[r * k:(r + 1) * k]) for r in range(n.value)]
 
     def close(self):
@@ -358,6 +360,14 @@ def gnn_minibatch(graph: DeviceGraph, fs: FeatureStore, seeds: torch.Tensor,
                              _stream(stream), timer.handle if timer else None)
     _ok(st, "gnn_minibatch")
     return st
+
+
+def gnn_copy_probe(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Plain device copy of src into dst (same byte size) by k_copy_probe; calibrates counters."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _ok(lib().gnn_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "gnn_copy_probe")
 
 
 def gnn_read_device_status(ws: torch.Tensor, stream=None) -> int:

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "libgnnmb.so")
 
 GNN_MAX_HOPS = 8
 GNN_MAX_GROUP = 16
-GNN_TIMER_EVENTS = 5
+GNN_TIMER_STAGES = 4
 GNN_SYNC = 1
 
 GNN_OK = 0
@@ -78,6 +78,8 @@ SIGNATURES = {
     "gnn_timer_destroy": (i32, [vp]),
     "gnn_timer_reset": (i32, [vp]),
     "gnn_timer_elapsed": (i32, [vp, P(i32), P(ctypes.c_float)]),
+    # measurement helper (include/gnnmb_probe.h)
+    "gnn_copy_probe": (i32, [vp, vp, size_t, vp]),
 }
 
 _lib = None

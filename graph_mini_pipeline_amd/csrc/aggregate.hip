@@ -16,27 +16,41 @@
 
 namespace gnnmb {
 
-struct MeanArgs {
+// One block to aggregate (a segment of a batched launch).
+struct MeanSeg {
     const int32_t *indptr;
     const int32_t *lid;
+    int64_t e_cap;   // entries of lid: edge offsets are clamped to it
     const int64_t *d_n;
     int64_t n_cap;
     const float *src;
-    int64_t ld_src;
     int64_t n_src;   // rows of src: a local id outside [0, n_src) is an error
-    int64_t e_cap;   // entries of lid: edge offsets are clamped to it
+    float *out;
+    uint32_t item0;  // first work item of this segment in the launch
+};
+
+struct MeanArgs {
+    MeanSeg seg[kMaxMeanSegs];
+    int32_t nseg;
+    uint32_t items;  // total work items (segments' caps times slabs)
+    int64_t ld_src;
+    int64_t ld_out;
     int32_t *status;
     int32_t d;
-    float *out;
-    int64_t ld_out;
     FastDiv cpr;
 };
 
 // A local id outside the source rows (only after an earlier device error) reads row 0 instead.
-__device__ __forceinline__ int32_t valid_lid(const MeanArgs &m, int32_t u) {
-    if (u >= 0 && u < m.n_src) return u;
+__device__ __forceinline__ int32_t valid_lid(const MeanArgs &m, const MeanSeg &S, int32_t u) {
+    if (u >= 0 && u < S.n_src) return u;
     set_status(m.status, GNN_ERR_INTERNAL);
     return 0;
+}
+
+__device__ __forceinline__ int find_seg(const MeanArgs &m, uint32_t it) {
+    int sgi = 0;
+    while (sgi + 1 < m.nseg && m.seg[sgi + 1].item0 <= it) ++sgi;
+    return sgi;
 }
 
 __device__ __forceinline__ float4 f4add(float4 a, float4 b) {
@@ -50,40 +64,91 @@ __device__ __forceinline__ float4 load_chunk4(const float *row, int col, int rem
     return make_float4(t[0], t[1], t[2], t[3]);
 }
 
+// One group of G lanes per (destination, slab of G 16-byte chunks).  The group reads the
+// destination's local ids once (lane t holds edge e0 + t) and passes them round with cross-lane
+// reads, so every lane issues its row loads back to back (UNR in flight) with no dependent id load
+// in between.  Small fanouts keep UNR = 8 with a one-by-one tail: there, occupancy (more
+// wavefronts in flight) beats a deeper load queue per wavefront, which costs four registers per
+// load.  Large fanouts issue 16 loads and a predicated tail.
+template <int G, int UNR, bool PRED_TAIL>
 __global__ __launch_bounds__(256) void k_mean_v4(MeanArgs m) {
-    const int64_t n = load_count(m.d_n, m.n_cap);
-    const uint32_t total = static_cast<uint32_t>(n) * m.cpr.d;
-    for (uint32_t idx = blockIdx.x * 256u + threadIdx.x; idx < total; idx += gridDim.x * 256u) {
-        const uint32_t row = fast_div(idx, m.cpr);
-        const int col = static_cast<int>(idx - row * m.cpr.d) * 4;
+    const int lane = lane_id();
+    const int grp = lane / G;
+    const int gl = lane % G;
+    const uint32_t cpr = m.cpr.d;
+    const uint32_t slabs = (cpr + G - 1) / G;
+    __shared__ uint32_t s_n[kMaxMeanSegs];  // destination count of each segment
+    if (threadIdx.x < static_cast<unsigned>(m.nseg))
+        s_n[threadIdx.x] = static_cast<uint32_t>(load_count(m.seg[threadIdx.x].d_n, m.seg[threadIdx.x].n_cap));
+    __syncthreads();
+    const uint32_t g0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (64 / G) + grp;
+    const uint32_t gstride = gridDim.x * 4u * (64 / G);
+    for (uint32_t it = g0; it < m.items; it += gstride) {
+        const int sgi = find_seg(m, it);
+        const MeanSeg &S = m.seg[sgi];
+        const uint32_t li = it - S.item0;
+        const uint32_t i = li / slabs;
+        const uint32_t p = li - i * slabs;
+        if (i >= s_n[sgi]) continue;
+        int64_t e0 = S.indptr[i], e1 = S.indptr[i + 1];
+        e0 = e0 < 0 ? 0 : (e0 > S.e_cap ? S.e_cap : e0);
+        e1 = e1 < e0 ? e0 : (e1 > S.e_cap ? S.e_cap : e1);
+        const uint32_t ch = p * G + gl;
+        const bool active = ch < cpr;
+        const int col = static_cast<int>(ch) * 4;
         const int rem = m.d - col;
-        int64_t e0 = m.indptr[row], e1 = m.indptr[row + 1];
-        e0 = e0 < 0 ? 0 : (e0 > m.e_cap ? m.e_cap : e0);
-        e1 = e1 < e0 ? e0 : (e1 > m.e_cap ? m.e_cap : e1);
+        const float *src = S.src + col;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        int64_t e = e0;
-        for (; e + 4 <= e1; e += 4) {
-            const int32_t u0 = valid_lid(m, m.lid[e]), u1 = valid_lid(m, m.lid[e + 1]);
-            const int32_t u2 = valid_lid(m, m.lid[e + 2]), u3 = valid_lid(m, m.lid[e + 3]);
-            const float4 a0 = load_chunk4(m.src + static_cast<int64_t>(u0) * m.ld_src, col, rem);
-            const float4 a1 = load_chunk4(m.src + static_cast<int64_t>(u1) * m.ld_src, col, rem);
-            const float4 a2 = load_chunk4(m.src + static_cast<int64_t>(u2) * m.ld_src, col, rem);
-            const float4 a3 = load_chunk4(m.src + static_cast<int64_t>(u3) * m.ld_src, col, rem);
-            acc = f4add(acc, a0);
-            acc = f4add(acc, a1);
-            acc = f4add(acc, a2);
-            acc = f4add(acc, a3);
+        for (int64_t eb = e0; eb < e1; eb += G) {
+            const int nb = static_cast<int>(e1 - eb < G ? e1 - eb : G);
+            const int32_t mine = gl < nb ? valid_lid(m, S, S.lid[eb + gl]) : 0;
+            int e = 0;
+            for (; e + UNR <= nb; e += UNR) {
+                float4 v[UNR];
+#pragma unroll
+                for (int q = 0; q < UNR; ++q) {
+                    int32_t u;
+                    if constexpr (G == 64) u = __builtin_amdgcn_readlane(mine, e + q);
+                    else u = __shfl(mine, grp * G + e + q, 64);
+                    v[q] = active ? load_chunk4(src + static_cast<int64_t>(u) * m.ld_src, 0, rem)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int q = 0; q < UNR; ++q) acc = f4add(acc, v[q]);
+            }
+            if constexpr (!PRED_TAIL) {
+                for (; e < nb; ++e) {
+                    int32_t u;
+                    if constexpr (G == 64) u = __builtin_amdgcn_readlane(mine, e);
+                    else u = __shfl(mine, grp * G + e, 64);
+                    if (active) acc = f4add(acc, load_chunk4(src + static_cast<int64_t>(u) * m.ld_src, 0, rem));
+                }
+            } else if (e < nb) {
+                // Remainder (< UNR edges): predicated loads, all issued before the sums.
+                float4 v[UNR];
+#pragma unroll
+                for (int q = 0; q < UNR; ++q) {
+                    int32_t u;
+                    const int src_lane = e + q < nb ? e + q : e;
+                    if constexpr (G == 64) u = __builtin_amdgcn_readlane(mine, src_lane);
+                    else u = __shfl(mine, grp * G + src_lane, 64);
+                    v[q] = (active && e + q < nb)
+                               ? load_chunk4(src + static_cast<int64_t>(u) * m.ld_src, 0, rem)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int q = 0; q < UNR; ++q)
+                    if (e + q < nb) acc = f4add(acc, v[q]);
+            }
         }
-        for (; e < e1; ++e)
-            acc = f4add(acc, load_chunk4(m.src + static_cast<int64_t>(valid_lid(m, m.lid[e])) * m.ld_src,
-                                         col, rem));
+        if (!active) continue;
         const int32_t c = static_cast<int32_t>(e1 - e0);
         float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
         if (c > 0) {
             const float fc = static_cast<float>(c);
             r = make_float4(acc.x / fc, acc.y / fc, acc.z / fc, acc.w / fc);
         }
-        float *o = m.out + static_cast<int64_t>(row) * m.ld_out + col;
+        float *o = S.out + static_cast<int64_t>(i) * m.ld_out + col;
         if (rem >= 4) {
             *reinterpret_cast<float4 *>(o) = r;
         } else {
@@ -94,37 +159,73 @@ __global__ __launch_bounds__(256) void k_mean_v4(MeanArgs m) {
 }
 
 __global__ __launch_bounds__(256) void k_mean_v1(MeanArgs m) {
-    const int64_t n = load_count(m.d_n, m.n_cap);
-    const uint32_t total = static_cast<uint32_t>(n) * m.cpr.d;
-    for (uint32_t idx = blockIdx.x * 256u + threadIdx.x; idx < total; idx += gridDim.x * 256u) {
-        const uint32_t row = fast_div(idx, m.cpr);
-        const int col = static_cast<int>(idx - row * m.cpr.d);
-        int64_t e0 = m.indptr[row], e1 = m.indptr[row + 1];
-        e0 = e0 < 0 ? 0 : (e0 > m.e_cap ? m.e_cap : e0);
-        e1 = e1 < e0 ? e0 : (e1 > m.e_cap ? m.e_cap : e1);
+    __shared__ uint32_t s_n[kMaxMeanSegs];
+    if (threadIdx.x < static_cast<unsigned>(m.nseg))
+        s_n[threadIdx.x] = static_cast<uint32_t>(load_count(m.seg[threadIdx.x].d_n, m.seg[threadIdx.x].n_cap));
+    __syncthreads();
+    const uint32_t cpr = m.cpr.d;
+    for (uint32_t it = blockIdx.x * 256u + threadIdx.x; it < m.items; it += gridDim.x * 256u) {
+        const int sgi = find_seg(m, it);
+        const MeanSeg &S = m.seg[sgi];
+        const uint32_t li = it - S.item0;
+        const uint32_t row = fast_div(li, m.cpr);
+        const int col = static_cast<int>(li - row * cpr);
+        if (row >= s_n[sgi]) continue;
+        int64_t e0 = S.indptr[row], e1 = S.indptr[row + 1];
+        e0 = e0 < 0 ? 0 : (e0 > S.e_cap ? S.e_cap : e0);
+        e1 = e1 < e0 ? e0 : (e1 > S.e_cap ? S.e_cap : e1);
         float acc = 0.f;
         for (int64_t e = e0; e < e1; ++e)
-            acc += m.src[static_cast<int64_t>(valid_lid(m, m.lid[e])) * m.ld_src + col];
+            acc += S.src[static_cast<int64_t>(valid_lid(m, S, S.lid[e])) * m.ld_src + col];
         const int32_t c = static_cast<int32_t>(e1 - e0);
-        m.out[static_cast<int64_t>(row) * m.ld_out + col] = c > 0 ? acc / static_cast<float>(c) : 0.f;
+        S.out[static_cast<int64_t>(row) * m.ld_out + col] = c > 0 ? acc / static_cast<float>(c) : 0.f;
     }
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-hipError_t launch_mean(const int32_t *indptr, const int32_t *lid, int64_t e_cap,
-                       const int64_t *d_n, int64_t n_cap, const float *src, int64_t ld_src,
-                       int64_t n_src, int64_t d, float *out, int64_t ld_out, int32_t *status,
-                       hipStream_t s) {
-    if (n_cap <= 0 || d <= 0) return hipSuccess;
-    const bool v4 = ld_src % 4 == 0 && ld_out % 4 == 0 && aligned16(src) && aligned16(out);
+hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out, int64_t d,
+                       int32_t max_c, int32_t *status, hipStream_t s) {
+    if (njobs <= 0 || d <= 0) return hipSuccess;
+    bool v4 = ld_src % 4 == 0 && ld_out % 4 == 0;
+    for (int j = 0; j < njobs; ++j) v4 = v4 && aligned16(jobs[j].src) && aligned16(jobs[j].out);
     const int vec = v4 ? 4 : 1;
     const int64_t cpr = (d + vec - 1) / vec;
-    MeanArgs m{indptr, lid, d_n, n_cap, src, ld_src, n_src, e_cap, status,
-               static_cast<int32_t>(d), out, ld_out, make_fastdiv(static_cast<uint32_t>(cpr))};
-    const unsigned grid = grid_for(n_cap * cpr, 256, 8192);
-    if (v4) hipLaunchKernelGGL(k_mean_v4, dim3(grid), dim3(256), 0, s, m);
-    else hipLaunchKernelGGL(k_mean_v1, dim3(grid), dim3(256), 0, s, m);
+    const int G = !v4 ? 1 : (cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64));
+    const int64_t slabs = v4 ? (cpr + G - 1) / G : cpr;   // items per destination
+    for (int j0 = 0; j0 < njobs; j0 += kMaxMeanSegs) {
+        MeanArgs m{};
+        m.ld_src = ld_src;
+        m.ld_out = ld_out;
+        m.status = status;
+        m.d = static_cast<int32_t>(d);
+        m.cpr = make_fastdiv(static_cast<uint32_t>(cpr));
+        int64_t items = 0;
+        for (int j = j0; j < njobs && j < j0 + kMaxMeanSegs; ++j) {
+            const MeanJob &J = jobs[j];
+            m.seg[m.nseg++] = MeanSeg{J.indptr, J.lid, J.e_cap, J.d_n, J.n_cap, J.src, J.n_src,
+                                      J.out, static_cast<uint32_t>(items)};
+            items += J.n_cap * slabs;
+        }
+        if (items == 0) continue;
+        if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+        m.items = static_cast<uint32_t>(items);
+        if (!v4) {
+            hipLaunchKernelGGL(k_mean_v1, dim3(grid_for(items, 256, 8192)), dim3(256), 0, s, m);
+            continue;
+        }
+        const dim3 grid(grid_for(items, 4 * (64 / G), 8192));
+        const bool deep = max_c > 12;
+#define GNN_MEAN_LAUNCH(GG)                                                                   \
+    do {                                                                                      \
+        if (deep) hipLaunchKernelGGL((k_mean_v4<GG, 16, true>), grid, dim3(256), 0, s, m);    \
+        else hipLaunchKernelGGL((k_mean_v4<GG, 8, false>), grid, dim3(256), 0, s, m);         \
+    } while (0)
+        if (G == 16) GNN_MEAN_LAUNCH(16);
+        else if (G == 32) GNN_MEAN_LAUNCH(32);
+        else GNN_MEAN_LAUNCH(64);
+#undef GNN_MEAN_LAUNCH
+    }
     return hipGetLastError();
 }
 

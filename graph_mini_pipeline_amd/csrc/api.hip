@@ -19,10 +19,15 @@ struct gnn_feature_store {
     int32_t *slot;  // [num_nodes] cache slot of each node, -1 if not cached; NULL if no cache
 };
 
+// Events per record: call start, end of sampling, then per sub-batch the ends of its gather and
+// of its outermost-block mean, then the end of the call.
+constexpr int kTimerSlots = 3 + 2 * GNN_MAX_GROUP;
+
 struct gnn_timer {
     int32_t n_records;
     int32_t cursor;
-    std::vector<hipEvent_t> ev;  // n_records * GNN_TIMER_EVENTS
+    std::vector<hipEvent_t> ev;   // n_records * kTimerSlots
+    std::vector<int32_t> group;   // sub-batches of each recorded call
 };
 
 namespace {
@@ -80,6 +85,11 @@ int64_t tiles_for(int64_t n) {
     return t < 1 ? 1 : t;
 }
 
+int64_t dist_tiles(int64_t n) {
+    const int64_t t = (n + kDistTile - 1) / kDistTile;
+    return t < 1 ? 1 : t;
+}
+
 // mc: element-wise bound of every sub-batch's caps; G sub-batches.
 Workspace carve(const gnn_caps &mc, int64_t N, int G, void *ws) {
     Workspace w{};
@@ -115,7 +125,7 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, void *ws) {
         w.U = c.take<int32_t>(U_max);
         w.u_indptr = c.take<int32_t>(U_max + 1);
         w.u_gid = c.take<int32_t>(uE_max);
-        w.bsum_dist = c.take<uint32_t>(static_cast<int64_t>(G) * tiles_for(F_max));
+        w.bsum_dist = c.take<uint32_t>(static_cast<int64_t>(G) * dist_tiles(F_max));
     }
     w.bytes = c.off;
     return w;
@@ -273,7 +283,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         int32_t tiles = 0;
         for (int gi = 0; gi < G; ++gi) {
             gnn_blocks &out = *outs[gi];
-            const int32_t nt = static_cast<int32_t>(tiles_for(F_cap(gi)));
+            const int32_t nt = static_cast<int32_t>(dist_tiles(F_cap(gi)));
             da.sub[gi] = DistSub{front(gi), d_F(gi), F_cap(gi), out.hop[l].indptr, out.hop[l].gid,
                                  out.caps.edges[l], out.counts + 2 * l, tiles, nt};
             tiles += nt;
@@ -509,8 +519,9 @@ gnn_status gnn_mean_aggregate(const int32_t *indptr, const int32_t *lid, int64_t
     if (n_dst > 0 && (!indptr || !out)) return GNN_ERR_INVALID_ARG;
     if (n_lid > 0 && (!lid || !src)) return GNN_ERR_INVALID_ARG;
     if (n_dst * d > kFlatMax) return GNN_ERR_UNSUPPORTED;
-    GNN_TRY_HIP(launch_mean(indptr, lid, n_lid, d_n_dst, n_dst, src, ld_src, n_src, d, out,
-                            ld_out, d_status, static_cast<hipStream_t>(stream)));
+    const MeanJob job{indptr, lid, n_lid, d_n_dst, n_dst, src, n_src, out};
+    GNN_TRY_HIP(launch_mean(&job, 1, ld_src, ld_out, d, 16, d_status,
+                            static_cast<hipStream_t>(stream)));
     return GNN_OK;
 }
 
@@ -539,7 +550,7 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         if (ns < 0 || (ns > 0 && !seeds)) return GNN_ERR_INVALID_ARG;
         gnn_minibatch_out &mo = outs[gi];
         if ((st = check_blocks(&mo.blocks, ns, fanouts, K)) != GNN_OK) return st;
-        if (mo.ld_h < d) return GNN_ERR_INVALID_ARG;
+        if (mo.ld_h < d || mo.ld_h != outs[0].ld_h) return GNN_ERR_INVALID_ARG;
         const gnn_caps &c = mo.blocks.caps;
         if (c.nodes[K - 1] > 0 && !mo.x) return GNN_ERR_INVALID_ARG;
         for (int l = 0; l < K; ++l) {
@@ -561,7 +572,8 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     hipEvent_t *ev = nullptr;
     if (timer) {
         if (timer->cursor >= timer->n_records) return GNN_ERR_CAPACITY;
-        ev = timer->ev.data() + static_cast<size_t>(timer->cursor) * GNN_TIMER_EVENTS;
+        ev = timer->ev.data() + static_cast<size_t>(timer->cursor) * kTimerSlots;
+        timer->group[timer->cursor] = group;
         timer->cursor += 1;
         GNN_TRY_HIP(hipEventRecord(ev[0], s));
     }
@@ -570,30 +582,35 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     st = run_sample(*g, sp, nsg, group, fanouts, K, seed64, ob, w, o, s);
     if (st != GNN_OK) return st;
     if (ev) GNN_TRY_HIP(hipEventRecord(ev[1], s));
-    // Stage 2: feature gather X = rows of V_K.
+    // Stages 2 and 3, per sub-batch: gather X = rows of V_K, then the outermost block's mean,
+    // which reads X while it is still in the caches.
     for (int gi = 0; gi < group; ++gi) {
         gnn_minibatch_out &mo = outs[gi];
         const gnn_caps &c = mo.blocks.caps;
         GNN_TRY_HIP(launch_gather(fs->table, fs->cache, fs->slot, fs->ld, d, fs->num_nodes,
                                   mo.blocks.hop[K - 1].nodes, mo.blocks.counts + 2 * (K - 1) + 1,
                                   c.nodes[K - 1], mo.x, mo.ld_h, nullptr, w.status, s));
+        if (ev) GNN_TRY_HIP(hipEventRecord(ev[2 + 2 * gi], s));
+        const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
+        const MeanJob job{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].lid, c.edges[K - 1],
+                          d_n, c.frontier[K - 1], mo.x, c.nodes[K - 1], mo.h[K - 1]};
+        GNN_TRY_HIP(launch_mean(&job, 1, mo.ld_h, mo.ld_h, d, fanouts[K - 1], w.status, s));
+        if (ev) GNN_TRY_HIP(hipEventRecord(ev[3 + 2 * gi], s));
     }
-    if (ev) GNN_TRY_HIP(hipEventRecord(ev[2], s));
-    // Stage 3: mean aggregation, outermost block first: h_{l-1} from h_l, h_K = X.
-    for (int l = K; l >= 1; --l) {
+    // Stage 4: the inner blocks, h_{l-1} from h_l for l = K-1..1, every sub-batch in one launch.
+    for (int l = K - 1; l >= 1; --l) {
+        MeanJob jobs[GNN_MAX_GROUP];
         for (int gi = 0; gi < group; ++gi) {
             gnn_minibatch_out &mo = outs[gi];
             const gnn_caps &c = mo.blocks.caps;
-            const float *src = l == K ? mo.x : mo.h[l];
-            float *dst = mo.h[l - 1];
             const int64_t *d_n = l == 1 ? nullptr : mo.blocks.counts + 2 * (l - 2) + 1;
-            GNN_TRY_HIP(launch_mean(mo.blocks.hop[l - 1].indptr, mo.blocks.hop[l - 1].lid,
-                                    c.edges[l - 1], d_n, c.frontier[l - 1], src, mo.ld_h,
-                                    c.nodes[l - 1], d, dst, mo.ld_h, w.status, s));
+            jobs[gi] = MeanJob{mo.blocks.hop[l - 1].indptr, mo.blocks.hop[l - 1].lid, c.edges[l - 1],
+                               d_n, c.frontier[l - 1], mo.h[l], c.nodes[l - 1], mo.h[l - 1]};
         }
-        if (ev && l == K) GNN_TRY_HIP(hipEventRecord(ev[3], s));
+        GNN_TRY_HIP(launch_mean(jobs, group, outs[0].ld_h, outs[0].ld_h, d, fanouts[l - 1],
+                                w.status, s));
     }
-    if (ev) GNN_TRY_HIP(hipEventRecord(ev[4], s));
+    if (ev) GNN_TRY_HIP(hipEventRecord(ev[2 + 2 * group], s));
     return finish(o, w, s);
 }
 
@@ -613,7 +630,8 @@ gnn_status gnn_timer_create(int32_t n_records, gnn_timer **out) {
     if (!t) return GNN_ERR_INVALID_ARG;
     t->n_records = n_records;
     t->cursor = 0;
-    t->ev.assign(static_cast<size_t>(n_records) * GNN_TIMER_EVENTS, nullptr);
+    t->ev.assign(static_cast<size_t>(n_records) * kTimerSlots, nullptr);
+    t->group.assign(static_cast<size_t>(n_records), 0);
     for (auto &e : t->ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             gnn_timer_destroy(t);
@@ -643,14 +661,23 @@ gnn_status gnn_timer_elapsed(gnn_timer *t, int32_t *n_records, float *ms) {
     *n_records = t->cursor;
     if (t->cursor == 0) return GNN_OK;
     if (!ms) return GNN_ERR_INVALID_ARG;
-    GNN_TRY_HIP(hipEventSynchronize(t->ev[static_cast<size_t>(t->cursor) * GNN_TIMER_EVENTS - 1]));
     for (int r = 0; r < t->cursor; ++r) {
-        for (int k = 0; k + 1 < GNN_TIMER_EVENTS; ++k) {
-            float v = 0.f;
-            GNN_TRY_HIP(hipEventElapsedTime(&v, t->ev[r * GNN_TIMER_EVENTS + k],
-                                            t->ev[r * GNN_TIMER_EVENTS + k + 1]));
-            ms[r * (GNN_TIMER_EVENTS - 1) + k] = v;
+        const hipEvent_t *e = t->ev.data() + static_cast<size_t>(r) * kTimerSlots;
+        const int G = t->group[r];
+        GNN_TRY_HIP(hipEventSynchronize(e[2 + 2 * G]));
+        float v = 0.f, gat = 0.f, outer = 0.f;
+        GNN_TRY_HIP(hipEventElapsedTime(&v, e[0], e[1]));
+        ms[r * GNN_TIMER_STAGES + 0] = v;
+        for (int gi = 0; gi < G; ++gi) {
+            GNN_TRY_HIP(hipEventElapsedTime(&v, e[1 + 2 * gi], e[2 + 2 * gi]));
+            gat += v;
+            GNN_TRY_HIP(hipEventElapsedTime(&v, e[2 + 2 * gi], e[3 + 2 * gi]));
+            outer += v;
         }
+        ms[r * GNN_TIMER_STAGES + 1] = gat;
+        ms[r * GNN_TIMER_STAGES + 2] = outer;
+        GNN_TRY_HIP(hipEventElapsedTime(&v, e[1 + 2 * G], e[2 + 2 * G]));
+        ms[r * GNN_TIMER_STAGES + 3] = v;
     }
     return GNN_OK;
 }

@@ -191,6 +191,9 @@ struct RelabelArgs {
     int32_t bitmap_cleared;   // the bitmaps are already zero on this stream
 };
 
+// Destinations per workgroup of the super-batch distribution (one wavefront's lanes).
+constexpr int kDistTile = 64;
+
 // One sub-batch of a super-batch hop: its destinations and the block it receives.
 struct DistSub {
     const int32_t *front;
@@ -238,10 +241,23 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
                          int32_t *status, hipStream_t s);
-hipError_t launch_mean(const int32_t *indptr, const int32_t *lid, int64_t e_cap,
-                       const int64_t *d_n, int64_t n_cap, const float *src, int64_t ld_src,
-                       int64_t n_src, int64_t d, float *out, int64_t ld_out, int32_t *status,
-                       hipStream_t s);
+// One mean-aggregation block: destinations [0, n) (n = *d_n, or n_cap if d_n is NULL) with
+// edges indptr / lid (lid has e_cap entries), sources src [n_src rows], output out.
+struct MeanJob {
+    const int32_t *indptr;
+    const int32_t *lid;
+    int64_t e_cap;
+    const int64_t *d_n;
+    int64_t n_cap;
+    const float *src;
+    int64_t n_src;
+    float *out;
+};
+constexpr int kMaxMeanSegs = 16;
+// All jobs share d and the row strides; up to kMaxMeanSegs jobs go into one launch.  max_c is a
+// typical (or the largest) edge count per destination; it only picks the load depth.
+hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out, int64_t d,
+                       int32_t max_c, int32_t *status, hipStream_t s);
 hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                              const int32_t *hot, int64_t rows, float *cache, int32_t *slot,
                              int32_t *status, hipStream_t s);

@@ -32,9 +32,11 @@ struct GatherArgs {
     FastDiv cpr;  // chunks per row
 };
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int VEC, int U>
 __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
-    using vec_t = typename std::conditional<VEC == 4, float4, float>::type;
+    using vec_t = typename std::conditional<VEC == 4, f32x4, float>::type;
     const int64_t n = load_count(g.d_n, g.n_cap);
     const uint32_t total = static_cast<uint32_t>(n) * g.cpr.d;
     const uint32_t stride = gridDim.x * 256u * U;
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
                 } else {
                     float t[4] = {0.f, 0.f, 0.f, 0.f};
                     for (int q = 0; q < rem[u]; ++q) t[q] = src[col + q];
-                    if constexpr (VEC == 4) val[u] = make_float4(t[0], t[1], t[2], t[3]);
+                    if constexpr (VEC == 4) val[u] = f32x4{t[0], t[1], t[2], t[3]};
                 }
             }
         }
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
             if (VEC == 1 || rem[u] >= VEC) {
                 *reinterpret_cast<vec_t *>(dst[u]) = val[u];
             } else if constexpr (VEC == 4) {
-                const float t[4] = {val[u].x, val[u].y, val[u].z, val[u].w};
+                const float t[4] = {val[u][0], val[u][1], val[u][2], val[u][3]};
                 for (int q = 0; q < rem[u]; ++q) dst[u][q] = t[q];
             }
         }

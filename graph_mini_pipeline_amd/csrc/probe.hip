@@ -1,0 +1,27 @@
+// Plain streaming copy used to calibrate memory-traffic counters (see gnnmb_probe.h).
+#include "common.hpp"
+#include "gnnmb_probe.h"
+
+namespace gnnmb {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_copy_probe(const u32x4 *src, u32x4 *dst, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        dst[i] = src[i];
+}
+
+}  // namespace gnnmb
+
+extern "C" gnn_status gnn_copy_probe(const void *src, void *dst, size_t bytes, gnn_stream stream) {
+    using namespace gnnmb;
+    if (!src || !dst || bytes == 0 || bytes % 16 != 0 ||
+        (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+        return GNN_ERR_INVALID_ARG;
+    const int64_t n = static_cast<int64_t>(bytes / 16);
+    hipLaunchKernelGGL(k_copy_probe, dim3(grid_for(n, 256 * 8, 8192)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src),
+                       static_cast<u32x4 *>(dst), n);
+    return hipGetLastError() == hipSuccess ? GNN_OK : GNN_ERR_HIP;
+}

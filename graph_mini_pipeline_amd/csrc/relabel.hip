@@ -68,8 +68,13 @@ __global__ __launch_bounds__(256) void k_mark(RelabelArgs a, int32_t pass) {
             continue;
         }
         const uint32_t bit = 1u << (v & 31);
-        const uint32_t old = atomicOr(&a.bitmap[static_cast<int64_t>(L.bitmap) * a.W + (v >> 5)], bit);
-        if (pass == 1 && (old & bit)) set_status(a.status, GNN_ERR_INVALID_ARG);
+        uint32_t *word = &a.bitmap[static_cast<int64_t>(L.bitmap) * a.W + (v >> 5)];
+        if (pass == 1) {
+            const uint32_t old = atomicOr(word, bit);
+            if (old & bit) set_status(a.status, GNN_ERR_INVALID_ARG);
+        } else {
+            atomicOr(word, bit);  // result unused: the atomic is posted, the lane does not wait
+        }
     }
 }
 

@@ -14,7 +14,7 @@
 // more than the LDS capacity survive, tau is bisected and the pass repeated.  Once
 // k <= count <= capacity the k smallest candidates are exactly the k smallest keys of the row.
 //
-// Classes (per hop, per frontier node v of degree deg, fanout k):
+// Classes (per hop, per frontier node v of degree deg, fanout k), all in one launch:
 //   FULL   deg <= k                one lane per node copies the row
 //   GROUP  k < deg <= group_max   16 lanes per node (4 nodes per wavefront)
 //   WAVE   group_max < deg <= wave_max   one wavefront per node
@@ -225,6 +225,65 @@ __device__ __forceinline__ bool next_tau(int cnt, int k, int cap, uint64_t &tau,
     return true;
 }
 
+// ---- candidate collection --------------------------------------------------------------------
+//
+// Keys of positions j = gl, gl + G, ... of a row of length deg (G lanes, lane gl); the ones
+// <= tau are appended, in ascending position, to s_key / s_pos (first CAP kept).  Returns the
+// number of keys <= tau.  Two keys per lane per step; the position bound is checked only in the
+// tail.
+template <int G, int CAP>
+__device__ __forceinline__ int collect_lanes(uint64_t ns, int64_t deg, uint64_t tau, int gl,
+                                             uint64_t gmask, uint64_t below, uint64_t *s_key,
+                                             int32_t *s_pos) {
+    const uint64_t step = kGamma * static_cast<uint64_t>(G);
+    uint64_t z = ns + kGamma * static_cast<uint64_t>(gl + 1);
+    int cnt = 0;
+    const int64_t main_end = deg / (2 * G) * (2 * G);
+    int64_t j0 = 0;
+    for (; j0 < main_end; j0 += 2 * G) {
+        const uint64_t k0 = mix64(z);
+        const uint64_t k1 = mix64(z + step);
+        z += 2 * step;
+        const bool p0 = k0 <= tau, p1 = k1 <= tau;
+        const uint64_t m0 = __ballot(p0) & gmask;
+        const uint64_t m1 = __ballot(p1) & gmask;
+        if (m0 | m1) {
+            if (p0) {
+                const int pos = cnt + __popcll(m0 & below);
+                if (pos < CAP) {
+                    s_key[pos] = k0;
+                    s_pos[pos] = static_cast<int32_t>(j0 + gl);
+                }
+            }
+            cnt += __popcll(m0);
+            if (p1) {
+                const int pos = cnt + __popcll(m1 & below);
+                if (pos < CAP) {
+                    s_key[pos] = k1;
+                    s_pos[pos] = static_cast<int32_t>(j0 + G + gl);
+                }
+            }
+            cnt += __popcll(m1);
+        }
+    }
+    for (; j0 < deg; j0 += G) {
+        const int64_t j = j0 + gl;
+        const uint64_t key = mix64(z);
+        z += step;
+        const bool p = j < deg && key <= tau;
+        const uint64_t m = __ballot(p) & gmask;
+        if (p) {
+            const int pos = cnt + __popcll(m & below);
+            if (pos < CAP) {
+                s_key[pos] = key;
+                s_pos[pos] = static_cast<int32_t>(j);
+            }
+        }
+        cnt += __popcll(m);
+    }
+    return cnt;
+}
+
 // ---- one random node on G lanes of a wavefront ---------------------------------------------------
 //
 // Control flow is uniform across the G lanes of the group; other groups of the same wavefront may
@@ -243,24 +302,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
     bool has_lo = false, has_hi = false, fail = false;
     int cnt = 0;
     for (int it = 0; it < 128; ++it) {
-        cnt = 0;
-        uint64_t z = ns + kGamma * static_cast<uint64_t>(gl + 1);
-        const uint64_t step = kGamma * static_cast<uint64_t>(G);
-        for (int64_t j0 = 0; j0 < deg; j0 += G) {
-            const int64_t j = j0 + gl;
-            const uint64_t key = mix64(z);
-            z += step;
-            const bool p = j < deg && key <= tau;
-            const uint64_t m = __ballot(p) & gmask;
-            if (p) {
-                const int pos = cnt + __popcll(m & below);
-                if (pos < CAP) {
-                    s_key[pos] = key;
-                    s_pos[pos] = static_cast<int32_t>(j);
-                }
-            }
-            cnt += __popcll(m);
-        }
+        cnt = collect_lanes<G, CAP>(ns, deg, tau, gl, gmask, below, s_key, s_pos);
         if (!next_tau(cnt, k, CAP, tau, lo, hi, has_lo, has_hi, fail)) break;
     }
     if (fail || cnt < k || cnt > CAP) {
@@ -295,135 +337,174 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
     wave_lds_sync();
 }
 
-// ---- FULL, GROUP and WAVE classes in one launch ---------------------------------------------------
-//
-// Workgroups [0, nb_wave) take WAVE nodes (one wavefront each), the next nb_group workgroups take
-// GROUP nodes (16 lanes each), the rest FULL nodes (one lane each).  Each role walks its class list
-// with a static stride, so no two wavefronts contend for a shared counter.
-constexpr int kSmallLds = 4 * kWaveCap;  // = 16 * kGroupCap candidate entries per workgroup
-static_assert(4 * kWaveCap == 16 * kGroupCap, "the two roles share one LDS layout");
+// ---- one giant-row node on a whole workgroup -------------------------------------------------------
+__device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, uint64_t *s_key,
+                                                  int32_t *s_pos, uint8_t *s_sel,
+                                                  uint32_t *s_cnt) {
+    constexpr int NT = kBlockThreads;
+    constexpr int CAP = kBlockCap;
+    const int lane = lane_id();
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int k = a.k;
+    const int32_t v = a.front[i];
+    const int64_t start = row_ptr(a.indptr, a.ib, v);
+    const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - start;
+    const int64_t out0 = a.blk_indptr[i];
+    const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
+    uint64_t tau = initial_tau(deg, k), lo = 0, hi = 0;
+    bool has_lo = false, has_hi = false, fail = false;
+    int cnt = 0;
+    const uint64_t step = kGamma * static_cast<uint64_t>(NT);
+    const int64_t main_end = deg / (2 * NT) * (2 * NT);
+    for (int it = 0; it < 128; ++it) {
+        if (threadIdx.x == 0) *s_cnt = 0;
+        __syncthreads();
+        uint64_t z = ns + kGamma * static_cast<uint64_t>(threadIdx.x + 1);
+        int64_t j0 = 0;
+        for (; j0 < main_end; j0 += 2 * NT) {
+            const uint64_t k0 = mix64(z);
+            const uint64_t k1 = mix64(z + step);
+            z += 2 * step;
+            const bool p0 = k0 <= tau, p1 = k1 <= tau;
+            const uint64_t m0 = __ballot(p0), m1 = __ballot(p1);
+            if (m0 | m1) {
+                uint32_t wbase = 0;
+                if (lane == 0) wbase = atomicAdd(s_cnt, static_cast<uint32_t>(__popcll(m0) + __popcll(m1)));
+                wbase = __shfl(wbase, 0, 64);
+                if (p0) {
+                    const uint32_t pos = wbase + __popcll(m0 & below);
+                    if (pos < CAP) {
+                        s_key[pos] = k0;
+                        s_pos[pos] = static_cast<int32_t>(j0 + threadIdx.x);
+                    }
+                }
+                if (p1) {
+                    const uint32_t pos = wbase + __popcll(m0) + __popcll(m1 & below);
+                    if (pos < CAP) {
+                        s_key[pos] = k1;
+                        s_pos[pos] = static_cast<int32_t>(j0 + NT + threadIdx.x);
+                    }
+                }
+            }
+        }
+        for (; j0 < deg; j0 += NT) {
+            const int64_t j = j0 + threadIdx.x;
+            const uint64_t key = mix64(z);
+            z += step;
+            const bool p = j < deg && key <= tau;
+            const uint64_t m = __ballot(p);
+            if (m) {
+                uint32_t wbase = 0;
+                if (lane == 0) wbase = atomicAdd(s_cnt, static_cast<uint32_t>(__popcll(m)));
+                wbase = __shfl(wbase, 0, 64);
+                if (p) {
+                    const uint32_t pos = wbase + __popcll(m & below);
+                    if (pos < CAP) {
+                        s_key[pos] = key;
+                        s_pos[pos] = static_cast<int32_t>(j);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        cnt = static_cast<int>(*s_cnt);
+        __syncthreads();
+        if (!next_tau(cnt, k, CAP, tau, lo, hi, has_lo, has_hi, fail)) break;
+    }
+    if (fail || cnt < k || cnt > CAP) {
+        if (threadIdx.x == 0) set_status(a.status, GNN_ERR_INTERNAL);
+        cnt = 0;
+    }
+    // Candidates are in arbitrary order: rank by (key, pos), then place by position.
+    for (int c = threadIdx.x; c < cnt; c += NT) {
+        const uint64_t kc = s_key[c];
+        const int32_t jc = s_pos[c];
+        int r = 0;
+        for (int t = 0; t < cnt; ++t) {
+            const uint64_t kt = s_key[t];
+            r += (kt < kc) | ((kt == kc) & (s_pos[t] < jc));
+        }
+        s_sel[c] = r < k ? 1 : 0;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < cnt; c += NT) {
+        if (!s_sel[c]) continue;
+        const int32_t jc = s_pos[c];
+        int r = 0;
+        for (int t = 0; t < cnt; ++t) r += s_sel[t] & (s_pos[t] < jc);
+        const int64_t o = out0 + r;
+        if (o < a.E_cap) a.blk_gid[o] = a.indices[start + jc];
+    }
+    __syncthreads();
+}
 
-__global__ __launch_bounds__(256) void k_sample_small(HopArgs a, int32_t nb_wave, int32_t nb_group) {
-    __shared__ uint64_t s_key[kSmallLds];
-    __shared__ int32_t s_pos[kSmallLds];
+// ---- all four classes in one launch ---------------------------------------------------------------
+//
+// Workgroups of kBlockThreads lanes.  The first nb_block workgroups take BLOCK nodes (a whole
+// workgroup each), the next nb_wave take WAVE nodes (one wavefront each), the next nb_group GROUP
+// nodes (16 lanes each), the rest FULL nodes (one lane each).  The long-running giant rows are
+// dispatched first and the short classes fill the machine around them.  Each role walks its class
+// list with a static stride, so no two wavefronts contend for a shared counter.
+constexpr int kWavesPerBlock = kBlockThreads / 64;
+static_assert(kWavesPerBlock * kWaveCap == kBlockCap, "WAVE slots fill the shared LDS arrays");
+static_assert(kWavesPerBlock * (64 / kGroupLanes) * kGroupCap == kBlockCap,
+              "GROUP slots fill the shared LDS arrays");
+
+__global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_block,
+                                                         int32_t nb_wave, int32_t nb_group) {
+    __shared__ uint64_t s_key[kBlockCap];
+    __shared__ int32_t s_pos[kBlockCap];
+    __shared__ uint8_t s_sel[kBlockCap];
+    __shared__ uint32_t s_cnt;
     const int lane = lane_id();
     const int wv = static_cast<int>(threadIdx.x >> 6);
     const uint64_t below = (1ull << lane) - 1ull;
-    const int bid = static_cast<int>(blockIdx.x);
+    int bid = static_cast<int>(blockIdx.x);
+    if (bid < nb_block) {
+        const int64_t n = a.totals[1 + kBlock];
+        const int32_t *list = a.lists + static_cast<int64_t>(kBlock) * a.F_cap;
+        for (int64_t item = bid; item < n; item += nb_block)
+            sample_node_block(a, list[item], s_key, s_pos, s_sel, &s_cnt);
+        return;
+    }
+    bid -= nb_block;
     if (bid < nb_wave) {
         const int64_t n = a.totals[1 + kWave];
         const int32_t *list = a.lists + static_cast<int64_t>(kWave) * a.F_cap;
-        for (int64_t item = static_cast<int64_t>(bid) * 4 + wv; item < n;
-             item += static_cast<int64_t>(nb_wave) * 4)
+        for (int64_t item = static_cast<int64_t>(bid) * kWavesPerBlock + wv; item < n;
+             item += static_cast<int64_t>(nb_wave) * kWavesPerBlock)
             sample_node_lanes<64, kWaveCap>(a, list[item], s_key + wv * kWaveCap,
                                             s_pos + wv * kWaveCap, lane, ~0ull, below);
-    } else if (bid < nb_wave + nb_group) {
+        return;
+    }
+    bid -= nb_wave;
+    if (bid < nb_group) {
         constexpr int G = kGroupLanes;
+        constexpr int SLOTS = kWavesPerBlock * (64 / G);
         const int grp = lane / G;
         const int slot = wv * (64 / G) + grp;
         const uint64_t gmask = ((1ull << G) - 1ull) << (grp * G);
         const int64_t n = a.totals[1 + kGroup];
         const int32_t *list = a.lists + static_cast<int64_t>(kGroup) * a.F_cap;
-        for (int64_t item = static_cast<int64_t>(bid - nb_wave) * 16 + slot; item < n;
-             item += static_cast<int64_t>(nb_group) * 16)
+        for (int64_t item = static_cast<int64_t>(bid) * SLOTS + slot; item < n;
+             item += static_cast<int64_t>(nb_group) * SLOTS)
             sample_node_lanes<G, kGroupCap>(a, list[item], s_key + slot * kGroupCap,
                                             s_pos + slot * kGroupCap, lane % G, gmask, below);
-    } else {
-        const int64_t n = a.totals[1 + kFull];
-        const int32_t *list = a.lists;
-        const int64_t nb_full = static_cast<int64_t>(gridDim.x) - nb_wave - nb_group;
-        for (int64_t t = static_cast<int64_t>(bid - nb_wave - nb_group) * 256 + threadIdx.x; t < n;
-             t += nb_full * 256) {
-            const int32_t i = list[t];
-            const int32_t v = a.front[i];
-            if (v < 0 || v >= a.num_nodes) continue;
-            const int64_t st = row_ptr(a.indptr, a.ib, v);
-            const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - st;
-            const int64_t o = a.blk_indptr[i];
-            for (int64_t j = 0; j < deg; ++j)
-                if (o + j < a.E_cap) a.blk_gid[o + j] = a.indices[st + j];
-        }
+        return;
     }
-}
-
-// ---- BLOCK: one workgroup per node ----------------------------------------------------------------
-
-__global__ __launch_bounds__(kBlockThreads) void k_sample_block(HopArgs a) {
-    constexpr int NT = kBlockThreads;
-    constexpr int CAP = kBlockCap;
-    __shared__ uint64_t s_key[CAP];
-    __shared__ int32_t s_pos[CAP];
-    __shared__ uint8_t s_sel[CAP];
-    __shared__ uint32_t s_cnt;
-    const int lane = lane_id();
-    const uint64_t below = (1ull << lane) - 1ull;
-    const int64_t n = a.totals[1 + kBlock];
-    const int32_t *list = a.lists + static_cast<int64_t>(kBlock) * a.F_cap;
-    const int k = a.k;
-    for (int64_t item = blockIdx.x; item < n; item += gridDim.x) {
-        const int32_t i = list[item];
+    bid -= nb_group;
+    const int64_t n = a.totals[1 + kFull];
+    const int64_t nb_full = static_cast<int64_t>(gridDim.x) - nb_block - nb_wave - nb_group;
+    for (int64_t t = static_cast<int64_t>(bid) * kBlockThreads + threadIdx.x; t < n;
+         t += nb_full * kBlockThreads) {
+        const int32_t i = a.lists[t];
         const int32_t v = a.front[i];
-        const int64_t start = row_ptr(a.indptr, a.ib, v);
-        const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - start;
-        const int64_t out0 = a.blk_indptr[i];
-        const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
-        uint64_t tau = initial_tau(deg, k), lo = 0, hi = 0;
-        bool has_lo = false, has_hi = false, fail = false;
-        int cnt = 0;
-        for (int it = 0; it < 128; ++it) {
-            if (threadIdx.x == 0) s_cnt = 0;
-            __syncthreads();
-            uint64_t z = ns + kGamma * static_cast<uint64_t>(threadIdx.x + 1);
-            const uint64_t step = kGamma * static_cast<uint64_t>(NT);
-            for (int64_t j0 = 0; j0 < deg; j0 += NT) {
-                const int64_t j = j0 + threadIdx.x;
-                const uint64_t key = mix64(z);
-                z += step;
-                const bool p = j < deg && key <= tau;
-                const uint64_t m = __ballot(p);
-                if (m) {
-                    uint32_t wbase = 0;
-                    if (lane == 0) wbase = atomicAdd(&s_cnt, static_cast<uint32_t>(__popcll(m)));
-                    wbase = __shfl(wbase, 0, 64);
-                    if (p) {
-                        const uint32_t pos = wbase + __popcll(m & below);
-                        if (pos < CAP) {
-                            s_key[pos] = key;
-                            s_pos[pos] = static_cast<int32_t>(j);
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-            cnt = static_cast<int>(s_cnt);
-            __syncthreads();
-            if (!next_tau(cnt, k, CAP, tau, lo, hi, has_lo, has_hi, fail)) break;
-        }
-        if (fail || cnt < k || cnt > CAP) {
-            if (threadIdx.x == 0) set_status(a.status, GNN_ERR_INTERNAL);
-            cnt = 0;
-        }
-        // Candidates are in arbitrary order: rank by (key, pos), then place by position.
-        for (int c = threadIdx.x; c < cnt; c += NT) {
-            const uint64_t kc = s_key[c];
-            const int32_t jc = s_pos[c];
-            int r = 0;
-            for (int t = 0; t < cnt; ++t) {
-                const uint64_t kt = s_key[t];
-                r += (kt < kc) | ((kt == kc) & (s_pos[t] < jc));
-            }
-            s_sel[c] = r < k ? 1 : 0;
-        }
-        __syncthreads();
-        for (int c = threadIdx.x; c < cnt; c += NT) {
-            if (!s_sel[c]) continue;
-            const int32_t jc = s_pos[c];
-            int r = 0;
-            for (int t = 0; t < cnt; ++t) r += s_sel[t] & (s_pos[t] < jc);
-            const int64_t o = out0 + r;
-            if (o < a.E_cap) a.blk_gid[o] = a.indices[start + jc];
-        }
-        __syncthreads();
+        if (v < 0 || v >= a.num_nodes) continue;
+        const int64_t st = row_ptr(a.indptr, a.ib, v);
+        const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - st;
+        const int64_t o = a.blk_indptr[i];
+        for (int64_t j = 0; j < deg; ++j)
+            if (o + j < a.E_cap) a.blk_gid[o + j] = a.indices[st + j];
     }
 }
 
@@ -443,12 +524,12 @@ hipError_t launch_classify(const HopArgs &a, hipStream_t s) {
 
 hipError_t launch_sample(const HopArgs &a, hipStream_t s) {
     const int64_t F = a.F_cap;
-    const int nb_wave = static_cast<int>(grid_for(F, 4, 2048));
-    const int nb_group = static_cast<int>(grid_for(F, 16, 1024));
-    const int nb_full = static_cast<int>(grid_for(F, 256, 256));
-    hipLaunchKernelGGL(k_sample_small, dim3(nb_wave + nb_group + nb_full), dim3(256), 0, s, a,
-                       nb_wave, nb_group);
-    hipLaunchKernelGGL(k_sample_block, dim3(grid_for(F, 1, 1024)), dim3(kBlockThreads), 0, s, a);
+    const int nb_block = static_cast<int>(grid_for(F, 1, 2048));
+    const int nb_wave = static_cast<int>(grid_for(F, kWavesPerBlock, 1024));
+    const int nb_group = static_cast<int>(grid_for(F, kWavesPerBlock * (64 / kGroupLanes), 512));
+    const int nb_full = static_cast<int>(grid_for(F, kBlockThreads, 128));
+    hipLaunchKernelGGL(k_sample, dim3(nb_block + nb_wave + nb_group + nb_full), dim3(kBlockThreads),
+                       0, s, a, nb_block, nb_wave, nb_group);
     return hipGetLastError();
 }
 

@@ -46,41 +46,28 @@ __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, i
     c = static_cast<int32_t>(l1 - l0);
 }
 
-__global__ __launch_bounds__(kClassifyThreads) void k_dist_count(DistArgs a) {
-    __shared__ uint32_t red[kClassifyThreads / 64];
+// Tiles of kDistTile destinations: wavefront 0 handles one destination per lane; the whole
+// workgroup then copies the tile's rows.
+__global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
+    if (threadIdx.x >= kDistTile) return;
     const int t = blockIdx.x;
-    const int g = find_sub(a, t);
-    const DistSub &S = a.sub[g];
+    const DistSub &S = a.sub[find_sub(a, t)];
     const int64_t F = load_count(S.d_F, S.F_cap);
-    const int64_t base = static_cast<int64_t>(t - S.tile0) * kClassifyTile +
-                         static_cast<int64_t>(threadIdx.x) * kClassifyItems;
-    uint32_t csum = 0;
-#pragma unroll
-    for (int q = 0; q < kClassifyItems; ++q) {
-        if (base + q < F) {
-            int64_t lo;
-            int32_t c;
-            union_row(a, S, base + q, lo, c);
-            csum += static_cast<uint32_t>(c);
-        }
-    }
-    csum = wave_sum(csum);
-    if (lane_id() == 0) red[threadIdx.x >> 6] = csum;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t s = 0;
-        for (int i = 0; i < kClassifyThreads / 64; ++i) s += red[i];
-        a.bsum[t] = s;
-    }
+    const int64_t i = static_cast<int64_t>(t - S.tile0) * kDistTile + threadIdx.x;
+    int64_t lo;
+    int32_t c = 0;
+    if (i < F) union_row(a, S, i, lo, c);
+    const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
+    if (threadIdx.x == 0) a.bsum[t] = sum;
 }
 
-__global__ __launch_bounds__(kClassifyThreads) void k_dist_scatter(DistArgs a) {
-    __shared__ uint32_t sm[kClassifyThreads / 64];
-    __shared__ uint32_t s_red[2][kClassifyThreads / 64];
-    __shared__ uint32_t s_off;
+__global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
+    __shared__ uint32_t s_red[2][4];
+    __shared__ uint32_t s_off, s_tot;
+    __shared__ uint32_t s_item_off[kDistTile + 1];
+    __shared__ int64_t s_item_lo[kDistTile];
     const int t = blockIdx.x;
-    const int g = find_sub(a, t);
-    const DistSub &S = a.sub[g];
+    const DistSub &S = a.sub[find_sub(a, t)];
     const int lt = t - S.tile0;
     const int64_t F = load_count(S.d_F, S.F_cap);
     uint32_t before = 0, all = 0;
@@ -97,11 +84,8 @@ __global__ __launch_bounds__(kClassifyThreads) void k_dist_scatter(DistArgs a) {
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint32_t b0 = 0, tot = 0;
-        for (int i = 0; i < kClassifyThreads / 64; ++i) {
-            b0 += s_red[0][i];
-            tot += s_red[1][i];
-        }
+        const uint32_t b0 = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+        const uint32_t tot = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
         s_off = b0;
         if (lt == 0) {
             S.blk_indptr[F] = static_cast<int32_t>(tot);
@@ -110,34 +94,35 @@ __global__ __launch_bounds__(kClassifyThreads) void k_dist_scatter(DistArgs a) {
         }
     }
     __syncthreads();
-    const int64_t base = static_cast<int64_t>(lt) * kClassifyTile +
-                         static_cast<int64_t>(threadIdx.x) * kClassifyItems;
-    int64_t lo[kClassifyItems];
-    int32_t c[kClassifyItems];
-    uint32_t csum = 0;
-#pragma unroll
-    for (int q = 0; q < kClassifyItems; ++q) {
-        lo[q] = 0;
-        c[q] = 0;
-        if (base + q < F) union_row(a, S, base + q, lo[q], c[q]);
-        csum += static_cast<uint32_t>(c[q]);
+    if (threadIdx.x < kDistTile) {
+        const int64_t i = static_cast<int64_t>(lt) * kDistTile + threadIdx.x;
+        int64_t lo = 0;
+        int32_t c = 0;
+        if (i < F) union_row(a, S, i, lo, c);
+        const uint32_t inc = wave_inclusive_scan(static_cast<uint32_t>(c));
+        const uint32_t o = inc - static_cast<uint32_t>(c);
+        s_item_off[threadIdx.x] = o;
+        s_item_lo[threadIdx.x] = lo;
+        if (threadIdx.x == kDistTile - 1) s_tot = inc;
+        if (i < F) S.blk_indptr[i] = static_cast<int32_t>(s_off + o);
     }
-    uint32_t tot;
-    uint32_t o = block_exclusive_scan<uint32_t, kClassifyThreads>(csum, &tot, sm) + s_off;
-#pragma unroll
-    for (int q = 0; q < kClassifyItems; ++q) {
-        const int64_t i = base + q;
-        if (i >= F) break;
-        S.blk_indptr[i] = static_cast<int32_t>(o);
-        for (int32_t j = 0; j < c[q]; ++j)
-            if (static_cast<int64_t>(o) + j < S.E_cap) S.blk_gid[o + j] = a.u_gid[lo[q] + j];
-        o += static_cast<uint32_t>(c[q]);
+    __syncthreads();
+    const uint32_t tot = s_tot;
+    for (uint32_t p = threadIdx.x; p < tot; p += blockDim.x) {
+        int lo_i = 0, hi_i = kDistTile;  // last destination whose offset is <= p
+        while (hi_i - lo_i > 1) {
+            const int mid = (lo_i + hi_i) >> 1;
+            if (s_item_off[mid] <= p) lo_i = mid;
+            else hi_i = mid;
+        }
+        const int64_t dst = static_cast<int64_t>(s_off) + p;
+        if (dst < S.E_cap) S.blk_gid[dst] = a.u_gid[s_item_lo[lo_i] + (p - s_item_off[lo_i])];
     }
 }
 
 hipError_t launch_dist(const DistArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_dist_count, dim3(a.ntiles), dim3(kClassifyThreads), 0, s, a);
-    hipLaunchKernelGGL(k_dist_scatter, dim3(a.ntiles), dim3(kClassifyThreads), 0, s, a);
+    hipLaunchKernelGGL(k_dist_count, dim3(a.ntiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_dist_scatter, dim3(a.ntiles), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,25 @@
+/*
+ * gnnmb_probe.h -- measurement helper of libgnnmb.so (not part of the mini-batch path).
+ *
+ * gnn_copy_probe copies `bytes` bytes (a multiple of 16, both pointers 16-byte aligned, device
+ * memory) from src to dst with a plain streaming kernel, k_copy_probe.  Its hardware counters
+ * (bytes fetched from and written to memory) for a copy of known size calibrate the counter
+ * readings of the other kernels.  Enqueues on `stream` and returns; GNN_ERR_INVALID_ARG on a bad
+ * size or alignment.
+ */
+#ifndef GNNMB_PROBE_H
+#define GNNMB_PROBE_H
+
+#include "gnnmb.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+gnn_status gnn_copy_probe(const void *src, void *dst, size_t bytes, gnn_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GNNMB_PROBE_H */

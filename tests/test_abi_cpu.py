@@ -14,11 +14,11 @@ import graph_mini_pipeline_amd as gm
 from graph_mini_pipeline_amd import _abi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gnnmb.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gnnmb.h", "gnnmb_probe.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(gnn_[a-z_]+)\s*\(", text)))
 
