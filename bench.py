@@ -31,6 +31,18 @@ def workload_name(cfg) -> str:
             f"batch {cfg.batch}; fanouts {cfg.fanouts}")
 
 
+def kernel_instance(kind: str, d: int, ld: int, fanout: int) -> str:
+    """Name of the template instance the library launches for this row shape: the gather moves
+    16-byte chunks when rows are 16-byte aligned; the mean picks lanes per destination from the
+    chunks per row and its load depth from the fanout (more than 12 edges: 16 loads in flight)."""
+    if kind == "gather":
+        return "k_gather<4, 4>" if ld % 4 == 0 else "k_gather<1, 4>"
+    cpr = (d + 3) // 4
+    G = 16 if cpr <= 16 else (32 if cpr <= 32 else 64)
+    deep = fanout > 12
+    return f"k_mean_v4<{G}, {16 if deep else 8}, {'true' if deep else 'false'}>"
+
+
 def algorithmic_bytes(counts, n_seeds, d, K):
     """Per-launch algorithmic HBM bytes of the gather (a4) and of each mean block (a5).
 
@@ -181,6 +193,13 @@ def main():
     dom = "gather" if t_gather >= t_mean_outer else "mean_outer"
     ach, avg_ms = kern[dom]
     ga_frac = (gb_bytes.sum() + mean_all.sum()) / (t_gather + t_mean_outer + t_mean_rest) / 1e9 / HBM_PEAK_GBPS
+    names = {"gather": kernel_instance("gather", cfg.d, cfg.ld, cfg.fanouts[-1]),
+             "mean_outer": kernel_instance("mean", cfg.d, cfg.ld, cfg.fanouts[-1])}
+    other = "mean_outer" if dom == "gather" else "gather"
+    from graph_mini_pipeline_amd.rocprof_summary import read_traffic
+    counters = os.path.join(ROOT, "profiles", f"{cfg.name}_counters.txt")
+    traffic = {k: read_traffic(counters, names[k]) for k in names}
+    alg_per_launch = {"gather": gb_bytes.sum() / steps / G, "mean_outer": mean_outer.sum() / steps / G}
 
     result = {
         "metric": "sampled edges/s + gathered feature GB/s per mini-batch; % of HBM peak",
@@ -207,13 +226,16 @@ def main():
                               "gather": t_gather / steps * 1e3,
                               "mean_outer_block": t_mean_outer / steps * 1e3,
                               "mean_other_blocks": t_mean_rest / steps * 1e3},
-        "roofline": {"bound": "hbm", "kernel": "k_gather" if dom == "gather" else "k_mean_v4",
+        "roofline": {"bound": "hbm", "kernel": names[dom],
                      "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": traffic[dom]["bytes"] if traffic[dom] else None,
+                     "algorithmic_bytes_per_launch": alg_per_launch[dom],
                      "avg_launch_ms": avg_ms, "launches_per_step": G},
-        "other_kernel": {"name": "k_mean_v4" if dom == "gather" else "k_gather",
-                         "achieved_GBps": kern["mean_outer" if dom == "gather" else "gather"][0],
-                         "avg_launch_ms": kern["mean_outer" if dom == "gather" else "gather"][1]},
+        "other_kernel": {"name": names[other], "achieved_GBps": kern[other][0],
+                         "avg_launch_ms": kern[other][1],
+                         "algorithmic_bytes_per_launch": alg_per_launch[other],
+                         "traffic": traffic[other]["bytes"] if traffic[other] else None},
         "ms_per_step_with_stage_events": wall_events / steps * 1e3,
         "input_generation_s": t_gen,
     }
@@ -237,6 +259,7 @@ def cpu_baseline(cfg, graph, table, order, step, budget_s, gpu_value):
     """The oracle (single-threaded C) on the first super-batches of the same epoch, until budget_s
     of CPU work has been spent; checks its results against the GPU path's on those batches."""
     import numpy as np
+    import torch
 
     import oracle
 
