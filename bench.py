@@ -24,11 +24,16 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 
 
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def workload_name(cfg) -> str:
     return (f"{cfg.name}: R-MAT ({cfg.rmat[0]},{cfg.rmat[1]},{cfg.rmat[2]}) {cfg.num_nodes} nodes, "
             f"{cfg.num_edges} directed edges, int{8 * cfg.indptr_bytes} indptr; {cfg.d}-d fp32 "
             f"{'N(0,1)' if cfg.dist == 'normal' else 'U[-1,1]'} features (row stride {cfg.ld}); "
-            f"batch {cfg.batch}; fanouts {cfg.fanouts}")
+            f"batch {cfg.batch}; fanouts {cfg.fanouts}" +
+            (f"; epoch of {cfg.n_train} training seeds" if cfg.n_train else ""))
 
 
 def kernel_instance(kind: str, d: int, ld: int, fanout: int) -> str:
@@ -91,15 +96,19 @@ def main():
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
     graph = synth.build_graph(cfg, device=dev)
+    torch.cuda.synchronize()
+    progress(f"graph: {cfg.num_nodes} nodes, {graph.indices.numel()} edges in {time.perf_counter() - t0:.1f} s")
     table = torch.empty(cfg.num_nodes, cfg.ld, dtype=torch.float32, device=dev)
     synth.make_features(cfg, table)
     order = synth.epoch_seed_order(cfg, 0, device=dev).contiguous()
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t0
+    progress(f"features and seed order ready, {t_gen:.1f} s in all")
     n_batches = (order.numel() + cfg.batch - 1) // cfg.batch
     G = args.group
     n_super = (n_batches + G - 1) // G
-    steps = args.steps or n_super
+    # default: one epoch for a workload with a training set, else 40 super-batches
+    steps = args.steps or (n_super if cfg.n_train else min(n_super, 40))
     K = len(cfg.fanouts)
 
     dg = gm.DeviceGraph(cfg.num_nodes, graph.indptr, graph.indices)
@@ -149,6 +158,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     status = min(gm.gnn_read_device_status(w) for w in wss)
+    progress(f"timed region: {steps} steps in {wall:.3f} s")
 
     # Timed region 2: the same steps with HIP events at the stage boundaries (the events cost a few
     # microseconds each, so they stay out of region 1).
@@ -249,6 +259,7 @@ def main():
     result["copy_probe_bytes"] = probe_src.numel() * 4
     del probe_src, probe_dst
 
+    progress("stage timing and counts done")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, graph, table, order, step, args.cpu_seconds,
                                               tot_edges / wall)

@@ -23,11 +23,19 @@ Graph recipe (stated in full so that it can be re-implemented):
 """
 from __future__ import annotations
 
+import ctypes
 import math
+import os
+import shutil
+import subprocess
 from dataclasses import dataclass, field
 from typing import List, Optional
 
 import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libsynth.so")
+_SRC = os.path.join(_HERE, "csrc", "rmat.hip")
 
 __all__ = [
     "u32", "Graph", "rmat_csr", "node_order", "fill_features", "CONFIGS", "WorkloadConfig",
@@ -155,6 +163,108 @@ def rmat_csr(num_nodes: int, num_edges: int, a: float, b: float, c: float, seed:
     return Graph(n, indptr.to(indptr_dtype), indices)
 
 
+def build() -> str:
+    """Compile the R-MAT draw kernel (csrc/rmat.hip) into libsynth.so for gfx950."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", _SRC, "-o", tmp],
+                          stderr=subprocess.DEVNULL)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_synth_lib = None
+
+
+def _draw_lib():
+    global _synth_lib
+    if _synth_lib is None:
+        if not os.path.exists(_LIB):
+            raise RuntimeError(f"{_LIB} is missing: run synth.build()")
+        L = ctypes.CDLL(_LIB)
+        i64, u64, i32, u32, vp = (ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_uint32,
+                                  ctypes.c_void_p)
+        L.synth_rmat_draw.restype = ctypes.c_int
+        L.synth_rmat_draw.argtypes = [u64, i64, i64, i32, u32, u32, u32, i64, vp, i64, i64, vp, vp,
+                                      vp, i64, vp]
+        _synth_lib = L
+    return _synth_lib
+
+
+def rmat_csr_partitioned(num_nodes: int, num_edges: int, a: float, b: float, c: float, seed: int,
+                         indptr_dtype=torch.int64, device="cuda", draws_per_part: int = 1 << 28,
+                         draws: Optional[int] = None) -> Graph:
+    """The same graph as rmat_csr, built on a GPU for billions of edges.
+
+    The draws are regenerated by a HIP kernel once per range of (scrambled) destination ids;
+    each range keeps its distinct pairs with their first draw index; a histogram of those indices
+    finds the cut that keeps exactly the first num_edges distinct pairs in draw order.  Ranges are
+    in destination order and each is sorted, so concatenating them gives the CSR by destination."""
+    n = int(num_nodes)
+    dev = torch.device(device)
+    assert dev.type == "cuda"
+    L = max(1, math.ceil(math.log2(n)))
+    ta, tb, tc = round(a * 65536), round((a + b) * 65536), round((a + b + c) * 65536)
+    gseed = sub_seed(seed, 1)
+    new_id = _scramble(n, sub_seed(seed, 2), dev).contiguous()
+    lib = _draw_lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    D = int(draws) if draws else int(num_edges * 1.06) + (1 << 20)
+    while True:
+        parts = max(1, -(-D // draws_per_part))
+        cap = int(D / parts * 1.25) + (1 << 20)
+        keys = torch.empty(cap, dtype=torch.int64, device=dev)
+        idx = torch.empty(cap, dtype=torch.int64, device=dev)
+        cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+        per_part = []
+        for p in range(parts):
+            lo, hi = p * n // parts, (p + 1) * n // parts
+            cnt.zero_()
+            rc = lib.synth_rmat_draw(gseed, 0, D, L, ta, tb, tc, n, new_id.data_ptr(), lo, hi,
+                                     keys.data_ptr(), idx.data_ptr(), cnt.data_ptr(), cap, stream)
+            if rc != 0:
+                raise RuntimeError(f"synth_rmat_draw failed ({rc})")
+            m = int(cnt.item())
+            if m > cap:
+                raise RuntimeError("draw buffer too small for a partition")
+            uk, inv = torch.unique(keys[:m], sorted=True, return_inverse=True)
+            first = torch.full((uk.numel(),), torch.iinfo(torch.int64).max, dtype=torch.int64, device=dev)
+            first.scatter_reduce_(0, inv, idx[:m], reduce="amin")
+            del inv
+            per_part.append((uk, first))
+        del keys, idx
+        total = sum(u.numel() for u, _ in per_part)
+        if total >= num_edges:
+            break
+        del per_part
+        D = int(D * 1.25) + (1 << 20)
+    # cut: the num_edges-th smallest first-draw index over all ranges
+    shift = max(0, (D - 1).bit_length() - 22)
+    nb = (D >> shift) + 1
+    hist = torch.zeros(nb, dtype=torch.int64, device=dev)
+    for _, f in per_part:
+        hist += torch.bincount(f >> shift, minlength=nb)
+    cum = torch.cumsum(hist, 0)
+    bstar = int(torch.searchsorted(cum, torch.tensor([num_edges], device=dev)).item())
+    before = int(cum[bstar - 1].item()) if bstar > 0 else 0
+    vals = torch.sort(torch.cat([f[(f >> shift) == bstar] for _, f in per_part])).values
+    t_star = int(vals[num_edges - before - 1].item())
+    indices, deg = [], torch.zeros(n, dtype=torch.int64, device=dev)
+    for uk, f in per_part:
+        kept = uk[f <= t_star]
+        dst = kept // n
+        deg += torch.bincount(dst, minlength=n)
+        indices.append((kept - dst * n).to(torch.int32))
+        del kept, dst
+    del per_part
+    indices = torch.cat(indices)
+    assert indices.numel() == num_edges
+    indptr = torch.zeros(n + 1, dtype=torch.int64, device=dev)
+    indptr[1:] = torch.cumsum(deg, 0)
+    return Graph(n, indptr.to(indptr_dtype), indices)
+
+
 def _scramble(n: int, seed: int, dev) -> torch.Tensor:
     """Bijection [0,n) -> [0,n): new_id[v] = rank of (u32(seed, v), v)."""
     v = torch.arange(n, dtype=torch.int64, device=dev)
@@ -171,7 +281,7 @@ def node_order(n: int, seed: int, device="cpu") -> torch.Tensor:
 
 
 def fill_features(out: torch.Tensor, d: int, dist: str, seed: int, row0: int = 0,
-                  rows_per_chunk: int = 1 << 16) -> None:
+                  rows_per_chunk: Optional[int] = None) -> None:
     """Fill out[:, :d] (float32, any row stride >= d) with seeded values; padding columns get 0.
 
     Element (r, t) of the full table uses counter r*d + t.  'uniform': U[-1,1] from the top 24
@@ -179,6 +289,8 @@ def fill_features(out: torch.Tensor, d: int, dist: str, seed: int, row0: int = 0
     u1, u2 from words 2e and 2e+1 (each (w + 0.5) / 2^32)."""
     rows = out.shape[0]
     dev = out.device
+    if rows_per_chunk is None:
+        rows_per_chunk = max(1, (1 << 25) // d) if dev.type == "cuda" else 1 << 16
     if out.shape[1] > d:
         out[:, d:] = 0
     for r0 in range(0, rows, rows_per_chunk):
@@ -242,9 +354,16 @@ CONFIGS = {
 }
 
 
+# Above this many edges a GPU build regenerates draws per destination range (rmat_csr_partitioned)
+# instead of holding every draw in memory at once; both give the same graph.
+PARTITIONED_EDGES = 1 << 28
+
+
 def build_graph(cfg: WorkloadConfig, device="cpu") -> Graph:
     dt = torch.int32 if cfg.indptr_bytes == 4 else torch.int64
     a, b, c = cfg.rmat
+    if torch.device(device).type == "cuda" and cfg.num_edges >= PARTITIONED_EDGES:
+        return rmat_csr_partitioned(cfg.num_nodes, cfg.num_edges, a, b, c, cfg.rng_seed, dt, device)
     return rmat_csr(cfg.num_nodes, cfg.num_edges, a, b, c, cfg.rng_seed, dt, device)
 
 

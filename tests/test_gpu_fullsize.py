@@ -1,8 +1,9 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark times.
 
-The dense-neighbourhood workload (233,000 nodes, 115M edges, 602-d rows with stride 604, batches
-of 1024 seeds, fanouts [25, 10]) is generated on the GPU; whole batches are compared with the
-oracle (bit-exact blocks and rows, means within 1e-5 * max|X|).
+Workloads are generated on the GPU: the dense-neighbourhood one (233,000 nodes, 115M edges,
+602-d rows with stride 604, batches of 1024 seeds, fanouts [25, 10]) and the mid-scale one
+(2.45M nodes, 124M edges, 100-d, fanouts [15, 10, 5], super-batches of 8).  Whole batches are
+compared with the oracle (bit-exact blocks and rows, means within 1e-5 * max|X|).
 """
 import numpy as np
 import pytest
@@ -17,9 +18,8 @@ pytestmark = pytest.mark.gpu
 gm = pytest.importorskip("graph_mini_pipeline_amd")
 
 
-@pytest.fixture(scope="module")
-def dense():
-    cfg = synth.CONFIGS["dense"]
+def _workload(name):
+    cfg = synth.CONFIGS[name]
     dev = torch.device("cuda")
     g = synth.build_graph(cfg, device=dev)
     table = torch.empty(cfg.num_nodes, cfg.ld, dtype=torch.float32, device=dev)
@@ -28,6 +28,16 @@ def dense():
     host = (g.indptr.cpu().numpy(), g.indices.cpu().numpy(), table.cpu().numpy(),
             order.cpu().numpy())
     return cfg, g, table, order, host
+
+
+@pytest.fixture(scope="module")
+def dense():
+    return _workload("dense")
+
+
+@pytest.fixture(scope="module")
+def mid():
+    return _workload("mid")
 
 
 def _run(cfg, g, table, order, batches, seed64):
@@ -79,3 +89,15 @@ def test_dense_superbatch_last_partial(dense):
     assert len(seeds) == 496
     ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
     compare_with_oracle(outs[2], ref, cfg.d)
+
+
+def test_mid_superbatch_of_8(mid):
+    cfg, g, table, order, (indptr, indices, x, order_h) = mid
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 0)
+    batches = list(range(0, 8))
+    outs, ptr = _run(cfg, g, table, order, batches, seed64)
+    for j in (0, 7):
+        b = batches[j]
+        seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
+        ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+        compare_with_oracle(outs[j], ref, cfg.d)
