@@ -76,6 +76,8 @@ def main():
                     help="HIP streams the super-batches are issued on, round robin; each stream has "
                          "its own workspace and outputs, so one stream's sampling overlaps another's "
                          "gather and aggregation")
+    ap.add_argument("--superbatch", default="auto", choices=["auto", "full", "compact"],
+                    help="super-batch relabel mode (identical results)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,7 +143,8 @@ def main():
                                                   cfg.d, cfg.ld)
             mine.append((b, n, outs[q][(j, n)]))
         gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, gm.gnn_batch_seed(cfg.rng_seed, s),
-                         [m[2] for m in mine], wss[q], timer=timer, stream=streams[q])
+                         [m[2] for m in mine], wss[q], gm.Options(superbatch=args.superbatch),
+                         timer=timer, stream=streams[q])
         return s, mine
 
     torch.cuda.synchronize()
@@ -225,7 +228,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": workload_name(cfg), "batches_per_epoch": n_batches,
-                   "super_batch": G, "streams": S,
+                   "super_batch": G, "streams": S, "superbatch_relabel": args.superbatch,
                    "step": f"one super-batch of {G} mini-batch(es)"},
         "ms_per_minibatch": wall / sum(len(batch_range(b % n_super)) for b in range(steps)) * 1e3,
         "status": gm.gnn_status_string(status),

@@ -16,6 +16,7 @@ import torch
 from . import _abi
 from ._abi import (GNN_ERR_CAPACITY, GNN_ERR_HIP, GNN_ERR_INTERNAL, GNN_ERR_INVALID_ARG,  # noqa
                    GNN_ERR_OUT_OF_RANGE, GNN_ERR_UNSUPPORTED, GNN_MAX_HOPS, GNN_OK, GNN_SYNC,
+                   GNN_SUPERBATCH_COMPACT, GNN_SUPERBATCH_FULL,
                    GNN_TIMER_STAGES)
 
 __all__ = [
@@ -77,12 +78,16 @@ class Options:
     group_max_deg: int = 0
     wave_max_deg: int = 0
     sync: bool = False
+    superbatch: str = "auto"    # super-batch relabel: "auto", "full" or "compact"
 
     def c(self) -> _abi.gnn_options:
         o = _abi.gnn_options()
         o.group_max_deg = self.group_max_deg
         o.wave_max_deg = self.wave_max_deg
-        o.flags = GNN_SYNC if self.sync else 0
+        modes = {"auto": 0, "full": GNN_SUPERBATCH_FULL, "compact": GNN_SUPERBATCH_COMPACT}
+        if self.superbatch not in modes:
+            raise ValueError(f"superbatch must be one of {sorted(modes)}")
+        o.flags = (GNN_SYNC if self.sync else 0) | modes[self.superbatch]
         return o
 
 

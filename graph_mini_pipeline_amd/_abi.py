@@ -14,6 +14,8 @@ GNN_MAX_HOPS = 8
 GNN_MAX_GROUP = 16
 GNN_TIMER_STAGES = 4
 GNN_SYNC = 1
+GNN_SUPERBATCH_FULL = 2
+GNN_SUPERBATCH_COMPACT = 4
 
 GNN_OK = 0
 GNN_ERR_INVALID_ARG = -1

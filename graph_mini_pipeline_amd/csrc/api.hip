@@ -58,25 +58,36 @@ struct Carver {
 struct Workspace {
     int32_t *status;       // [1] at offset 0
     uint32_t *totals;      // [5] classification totals
-    int64_t *d_U;          // |U| of a super-batch hop
-    int64_t *d_uE;         // edges of the union block
+    int64_t *d_U;          // [K + 1] |U_l| of a super-batch
+    int64_t *d_uE;         // [K] edges of each union block
     int32_t *packed;       // [FU_max]
     int32_t *lists;        // [4 FU_max]
     uint32_t *bsum;        // [5 nb_max]
-    uint32_t *bitmaps;     // [nbm * W]: G = 1: one bitmap; G > 1: the union bitmap, then G
-    uint32_t *wprefix;     // [nbm * W]
-    uint32_t *bsum_w;      // [nbm * nbw]
-    int32_t *U;            // super-batch only: union frontier, union block, distribution sums
-    int32_t *u_indptr;
+    uint32_t *bitmaps;     // [W] over all node ids, then G more of W words (full super-batch
+                           // relabel) or G of Wc words (compact super-batch relabel)
+    uint32_t *wprefix;     // same layout
+    uint32_t *bsum_w;      // [nbw], then G * nbw or G * nbwc
+    // super-batch only (the union; the rest: compact relabel only)
+    int32_t *U[2];         // U_l, ping-pong by hop parity (full relabel: one buffer)
+    int32_t *u_indptr;     // union block
     int32_t *u_gid;
+    int32_t *u_pos;        // position of each union-block id in U_{l+1}
+    int32_t *umap;         // position of each element of U_l in U_{l+1}
+    int32_t *upos;         // [G * P] position of each sub-batch frontier node in U_l
+    int32_t *f_pos;        // [G * Fs] position of each sub-batch destination in U_{l+1}
+    int32_t *e_pos;        // [G * Es] position of each sub-batch sampled id in U_{l+1}
     uint32_t *bsum_dist;
-    int64_t W, nbw, nbm;
+    int64_t P, Fs, Es;     // strides of the per-sub-batch arrays
+    int64_t W, nbw, Wc, nbwc;
+    int32_t mode;          // SuperMode
     size_t bytes;
 };
 
-// Union frontier bound of hop l of a super-batch: min(N, G * per-sub-batch frontier bound).
+// Union bound of level l of a super-batch (l < K: hop l's frontier; l = K: the last node set):
+// min(N, G * per-sub-batch bound).
 int64_t union_cap(const gnn_caps &mc, int l, int G, int64_t N) {
-    const int64_t u = static_cast<int64_t>(G) * mc.frontier[l];
+    const int64_t f = l < mc.num_hops ? mc.frontier[l] : mc.nodes[mc.num_hops - 1];
+    const int64_t u = static_cast<int64_t>(G) * f;
     return u < N ? u : N;
 }
 
@@ -90,42 +101,94 @@ int64_t dist_tiles(int64_t n) {
     return t < 1 ? 1 : t;
 }
 
-// mc: element-wise bound of every sub-batch's caps; G sub-batches.
-Workspace carve(const gnn_caps &mc, int64_t N, int G, void *ws) {
+int64_t bitmap_tiles(int64_t words) {
+    const int64_t t = (words + kBitmapTile - 1) / kBitmapTile;
+    return t < 1 ? 1 : t;
+}
+
+// How a super-batch relabels its sub-batches.
+//  kSuperFull:    every sub-batch has a bitmap over all N node ids (three passes over G + 1
+//                 bitmaps of N/32 words per hop: clear, popcount, emit).
+//  kSuperCompact: the union of the sub-batches' node sets is relabelled first (one N-bit bitmap,
+//                 accumulated over the hops), and each sub-batch relabels positions in it (bitmaps
+//                 of |U_{l+1}|/32 words); extra work: marking and ranking the union block's ids.
+enum SuperMode { kSuperNone = 0, kSuperFull = 1, kSuperCompact = 2 };
+
+int64_t max_union_edges(const gnn_caps &mc, int64_t N, int G) {
+    int64_t e = 0;
+    for (int l = 0; l < mc.num_hops; ++l) {
+        const int64_t x = union_cap(mc, l, G, N) * mc.fanouts[l];
+        e = x > e ? x : e;
+    }
+    return e;
+}
+
+// Default mode: compact once the full-range bitmap passes (3 (G + 1) N/32 words a hop) outweigh
+// the union block (its ids are marked and ranked once more); the options can force either.
+SuperMode super_mode(const gnn_caps &mc, int64_t N, int G, uint32_t flags) {
+    if (G <= 1) return kSuperNone;
+    if (flags & GNN_SUPERBATCH_FULL) return kSuperFull;
+    if (flags & GNN_SUPERBATCH_COMPACT) return kSuperCompact;
+    const int64_t W = (N + 31) / 32;
+    return 3 * static_cast<int64_t>(G + 1) * W >= max_union_edges(mc, N, G) ? kSuperCompact : kSuperFull;
+}
+
+// mc: element-wise bound of every sub-batch's caps; G sub-batches relabelled the given way.
+Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) {
     Workspace w{};
     Carver c{static_cast<char *>(ws)};
-    int64_t FU = 1, U_max = 1, uE_max = 1, F_max = 1;
-    for (int l = 0; l < mc.num_hops; ++l) {
+    const int K = mc.num_hops;
+    int64_t FU = 1, U_max = 1, F_max = 1, E_max = 1;
+    for (int l = 0; l < K; ++l) {
         F_max = mc.frontier[l] > F_max ? mc.frontier[l] : F_max;
+        E_max = mc.edges[l] > E_max ? mc.edges[l] : E_max;
         const int64_t u = G == 1 ? mc.frontier[l] : union_cap(mc, l, G, N);
         FU = u > FU ? u : FU;
-        if (G > 1) {
-            U_max = u > U_max ? u : U_max;
-            const int64_t e = u * mc.fanouts[l];
-            uE_max = e > uE_max ? e : uE_max;
-        }
     }
+    const int64_t uE_max = G > 1 ? max_union_edges(mc, N, G) : 1;
     const int64_t nb_max = tiles_for(FU);
+    w.mode = mode;
     w.W = (N + 31) / 32;
-    w.nbw = (w.W + kBitmapTile - 1) / kBitmapTile;
-    if (w.nbw < 1) w.nbw = 1;
-    w.nbm = G == 1 ? 1 : 1 + G;
+    w.nbw = bitmap_tiles(w.W);
+    int64_t words = w.W, tiles = w.nbw;
+    if (mode == kSuperFull) {
+        words = (1 + static_cast<int64_t>(G)) * w.W;
+        tiles = (1 + static_cast<int64_t>(G)) * w.nbw;
+        U_max = FU;
+    } else if (mode == kSuperCompact && K > 0) {
+        U_max = union_cap(mc, K, G, N);  // the largest level
+        w.Wc = (U_max + 31) / 32;
+        w.nbwc = bitmap_tiles(w.Wc);
+        w.P = mc.nodes[K - 1] > mc.frontier[0] ? mc.nodes[K - 1] : mc.frontier[0];
+        w.Fs = F_max;
+        w.Es = E_max;
+        words += static_cast<int64_t>(G) * w.Wc;
+        tiles += static_cast<int64_t>(G) * w.nbwc;
+    }
     w.status = c.take<int32_t>(64);
     w.totals = c.take<uint32_t>(64);
     int64_t *cnt = c.take<int64_t>(32);
     w.d_U = cnt;
-    w.d_uE = cnt ? cnt + 1 : nullptr;
+    w.d_uE = cnt ? cnt + 16 : nullptr;
     w.packed = c.take<int32_t>(FU);
     w.lists = c.take<int32_t>(4 * FU);
     w.bsum = c.take<uint32_t>(5 * nb_max);
-    w.bitmaps = c.take<uint32_t>(w.nbm * w.W);
-    w.wprefix = c.take<uint32_t>(w.nbm * w.W);
-    w.bsum_w = c.take<uint32_t>(w.nbm * w.nbw);
-    if (G > 1) {
-        w.U = c.take<int32_t>(U_max);
-        w.u_indptr = c.take<int32_t>(U_max + 1);
+    w.bitmaps = c.take<uint32_t>(words);
+    w.wprefix = c.take<uint32_t>(words);
+    w.bsum_w = c.take<uint32_t>(tiles);
+    if (mode != kSuperNone) {
+        w.U[0] = c.take<int32_t>(U_max);
+        w.U[1] = mode == kSuperCompact ? c.take<int32_t>(U_max) : w.U[0];
+        w.u_indptr = c.take<int32_t>(FU + 1);
         w.u_gid = c.take<int32_t>(uE_max);
         w.bsum_dist = c.take<uint32_t>(static_cast<int64_t>(G) * dist_tiles(F_max));
+    }
+    if (mode == kSuperCompact) {
+        w.u_pos = c.take<int32_t>(uE_max);
+        w.umap = c.take<int32_t>(FU);
+        w.upos = c.take<int32_t>(static_cast<int64_t>(G) * w.P);
+        w.f_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Fs);
+        w.e_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Es);
     }
     w.bytes = c.off;
     return w;
@@ -145,6 +208,7 @@ gnn_status read_opts(const gnn_options *o, Opts *out) {
         r.flags = o->flags;
     }
     if (r.group_max < 1 || r.wave_max < r.group_max) return GNN_ERR_INVALID_ARG;
+    if ((r.flags & GNN_SUPERBATCH_FULL) && (r.flags & GNN_SUPERBATCH_COMPACT)) return GNN_ERR_INVALID_ARG;
     *out = r;
     return GNN_OK;
 }
@@ -215,13 +279,14 @@ HopArgs hop_args(const gnn_graph &g, const int32_t *front, const int64_t *d_F, i
     return h;
 }
 
-RelabelArgs relabel_args(const gnn_graph &g, const Workspace &w, int first_bitmap, int nbm) {
+// Relabel over all node ids into bitmaps first .. first + nbm - 1 of N bits.
+RelabelArgs relabel_args(const gnn_graph &g, const Workspace &w, int first = 0, int nbm = 1) {
     RelabelArgs r{};
     r.nbm = nbm;
     r.id_bound = g.num_nodes;
-    r.bitmap = w.bitmaps + first_bitmap * w.W;
-    r.wprefix = w.wprefix + first_bitmap * w.W;
-    r.bsum = w.bsum_w + first_bitmap * w.nbw;
+    r.bitmap = w.bitmaps + first * w.W;
+    r.wprefix = w.wprefix + first * w.W;
+    r.bsum = w.bsum_w + first * w.nbw;
     r.W = w.W;
     r.nbw = static_cast<int32_t>(w.nbw);
     r.status = w.status;
@@ -229,89 +294,202 @@ RelabelArgs relabel_args(const gnn_graph &g, const Workspace &w, int first_bitma
     return r;
 }
 
+// Relabel of G sub-batches over positions in a sorted union list (the G compact bitmaps).
+RelabelArgs compact_relabel_args(const Workspace &w, int G, const int32_t *ulist,
+                                 const int64_t *d_n, int64_t cap) {
+    RelabelArgs r{};
+    r.nbm = G;
+    r.id_bound = cap;
+    r.d_bound = d_n;
+    r.id_map = ulist;
+    r.bitmap = w.bitmaps + w.W;
+    r.wprefix = w.wprefix + w.W;
+    r.bsum = w.bsum_w + w.nbw;
+    r.W = w.Wc;
+    r.nbw = static_cast<int32_t>(w.nbwc);
+    r.status = w.status;
+    r.bitmap_cleared = 1;
+    return r;
+}
+
+// One hop of a super-batch with full-range sub-batch bitmaps: the union U of the G frontiers
+// (bitmap 0) is relabelled, classified and sampled once; each sub-batch takes its rows from the
+// union block (union rank by bitmap 0) and is relabelled into its own bitmap over all node ids.
+template <typename FrontFn, typename CountFn, typename CapFn>
+gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, CapFn F_cap, int G,
+                              int32_t k, uint64_t hs, int l, const gnn_caps &mc,
+                              gnn_blocks *const *outs, const Workspace &w, const Opts &o,
+                              hipStream_t s) {
+    const int64_t Ucap = union_cap(mc, l, G, g.num_nodes);
+    const int64_t uEcap = Ucap * k;
+    RelabelArgs ru = relabel_args(g, w);
+    ru.nlist = G;
+    for (int gi = 0; gi < G; ++gi) ru.list[gi] = IdList{front(gi, l), d_F(gi, l), F_cap(gi, l), nullptr, 0, 0};
+    ru.out[0] = BitmapOut{w.U[0], Ucap, w.d_U, nullptr};
+    GNN_TRY_HIP(launch_relabel(ru, s));
+    HopArgs h = hop_args(g, w.U[0], w.d_U, Ucap, k, hs, w.u_indptr, w.u_gid, uEcap, w.d_uE, w, o);
+    h.clear_ptr = w.bitmaps + w.W;  // the sub-batch bitmaps, zeroed before their relabel
+    h.clear_n = static_cast<int64_t>(G) * w.W;
+    GNN_TRY_HIP(launch_classify(h, s));
+    GNN_TRY_HIP(launch_sample(h, s));
+    DistArgs da{};
+    da.G = G;
+    int32_t tiles = 0;
+    for (int gi = 0; gi < G; ++gi) {
+        gnn_blocks &out = *outs[gi];
+        const int32_t nt = static_cast<int32_t>(dist_tiles(F_cap(gi, l)));
+        da.sub[gi] = DistSub{front(gi, l), d_F(gi, l), F_cap(gi, l), nullptr, nullptr,
+                             out.hop[l].indptr, out.hop[l].gid, nullptr, out.caps.edges[l],
+                             out.counts + 2 * l, tiles, nt};
+        tiles += nt;
+    }
+    da.ntiles = tiles;
+    da.bm0 = w.bitmaps;
+    da.wprefix0 = w.wprefix;
+    da.id_bound = g.num_nodes;
+    da.u_indptr = w.u_indptr;
+    da.u_gid = w.u_gid;
+    da.uE_cap = uEcap;
+    da.d_U = w.d_U;
+    da.U_cap = Ucap;
+    da.bsum = w.bsum_dist;
+    da.status = w.status;
+    GNN_TRY_HIP(launch_dist(da, s));
+    // Per-sub-batch relabel into bitmaps 1..G; the union bitmap is zeroed for the next hop.
+    RelabelArgs rs = relabel_args(g, w, 1, G);
+    rs.nlist = 2 * G;
+    for (int gi = 0; gi < G; ++gi) {
+        gnn_blocks &out = *outs[gi];
+        rs.list[2 * gi] = IdList{front(gi, l), d_F(gi, l), F_cap(gi, l), out.hop[l].dst_lid, gi,
+                                 l == 0 ? 1 : 0};
+        rs.list[2 * gi + 1] = IdList{out.hop[l].gid, out.counts + 2 * l, out.caps.edges[l],
+                                     out.hop[l].lid, gi, 0};
+        rs.out[gi] = BitmapOut{out.hop[l].nodes, out.caps.nodes[l], out.counts + 2 * l + 1, nullptr};
+    }
+    rs.clear_ptr = w.bitmaps;
+    rs.clear_n = w.W;
+    GNN_TRY_HIP(launch_relabel(rs, s));
+    return GNN_OK;
+}
+
 // Sampling and relabel of every hop of G sub-batches (G = 1: one batch); no host synchronisation.
 // seeds_g[g] / n_seeds_g[g] are the sub-batches' seeds, outs[g] their blocks.
+//
+// G > 1, compact relabel: the node-id bitmap accumulates the union U_l of the sub-batch frontiers
+// over the hops (U_0 = the seeds, U_{l+1} = U_l + the ids sampled from U_l); U_l is sampled once
+// per hop and every sub-batch relabels in positions of U_{l+1}.  Full relabel: run_super_full_hop.
 gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const int64_t *n_seeds_g,
                       int G, const int32_t *fanouts, int32_t K, uint64_t seed64,
                       gnn_blocks *const *outs, const Workspace &w, const Opts &o, hipStream_t s) {
-    if (G > 1) GNN_TRY_HIP(launch_fill_u32(w.bitmaps, w.W, 0u, s));  // union bitmap of hop 1
     gnn_caps mc = outs[0]->caps;
-    for (int gi = 1; gi < G; ++gi)
-        for (int l = 0; l < K; ++l)
-            mc.frontier[l] = outs[gi]->caps.frontier[l] > mc.frontier[l] ? outs[gi]->caps.frontier[l]
-                                                                          : mc.frontier[l];
+    for (int gi = 1; gi < G; ++gi) {
+        for (int l = 0; l < K; ++l) {
+            const gnn_caps &c = outs[gi]->caps;
+            mc.frontier[l] = c.frontier[l] > mc.frontier[l] ? c.frontier[l] : mc.frontier[l];
+            mc.edges[l] = c.edges[l] > mc.edges[l] ? c.edges[l] : mc.edges[l];
+            mc.nodes[l] = c.nodes[l] > mc.nodes[l] ? c.nodes[l] : mc.nodes[l];
+        }
+    }
+    auto front = [&](int gi, int l) { return l == 0 ? seeds_g[gi] : outs[gi]->hop[l - 1].nodes; };
+    auto d_F = [&](int gi, int l) -> const int64_t * {
+        return l == 0 ? nullptr : outs[gi]->counts + 2 * (l - 1) + 1;
+    };
+    auto F_cap = [&](int gi, int l) { return l == 0 ? n_seeds_g[gi] : outs[gi]->caps.frontier[l]; };
+    const bool compact = w.mode == kSuperCompact;
+    if (G > 1) GNN_TRY_HIP(launch_fill_u32(w.bitmaps, w.W, 0u, s));
+    if (compact) {
+        // U_0: the union of the seeds, and each seed's position in it.
+        RelabelArgs r0 = relabel_args(g, w);
+        r0.nlist = G;
+        for (int gi = 0; gi < G; ++gi)
+            r0.list[gi] = IdList{seeds_g[gi], nullptr, n_seeds_g[gi], w.upos + gi * w.P, 0, 0};
+        r0.out[0] = BitmapOut{w.U[0], union_cap(mc, 0, G, g.num_nodes), w.d_U, nullptr};
+        GNN_TRY_HIP(launch_relabel(r0, s));
+    }
     for (int l = 0; l < K; ++l) {
         const uint64_t hs = mix64(seed64 + kGamma * static_cast<uint64_t>(l + 1));
-        auto front = [&](int gi) { return l == 0 ? seeds_g[gi] : outs[gi]->hop[l - 1].nodes; };
-        auto d_F = [&](int gi) -> const int64_t * {
-            return l == 0 ? nullptr : outs[gi]->counts + 2 * (l - 1) + 1;
-        };
-        auto F_cap = [&](int gi) { return l == 0 ? n_seeds_g[gi] : outs[gi]->caps.frontier[l]; };
         if (G == 1) {
             gnn_blocks &out = *outs[0];
             const gnn_caps &c = out.caps;
-            HopArgs h = hop_args(g, front(0), d_F(0), F_cap(0), fanouts[l], hs, out.hop[l].indptr,
-                                 out.hop[l].gid, c.edges[l], out.counts + 2 * l, w, o);
+            HopArgs h = hop_args(g, front(0, l), d_F(0, l), F_cap(0, l), fanouts[l], hs,
+                                 out.hop[l].indptr, out.hop[l].gid, c.edges[l], out.counts + 2 * l,
+                                 w, o);
             h.clear_ptr = w.bitmaps;
             h.clear_n = w.W;
             GNN_TRY_HIP(launch_classify(h, s));
             GNN_TRY_HIP(launch_sample(h, s));
-            RelabelArgs r = relabel_args(g, w, 0, 1);
+            RelabelArgs r = relabel_args(g, w);
             r.nlist = 2;
-            r.list[0] = IdList{front(0), d_F(0), F_cap(0), out.hop[l].dst_lid, 0, l == 0 ? 1 : 0};
+            r.list[0] = IdList{front(0, l), d_F(0, l), F_cap(0, l), out.hop[l].dst_lid, 0, l == 0 ? 1 : 0};
             r.list[1] = IdList{out.hop[l].gid, out.counts + 2 * l, c.edges[l], out.hop[l].lid, 0, 0};
-            r.out[0] = BitmapOut{out.hop[l].nodes, c.nodes[l], out.counts + 2 * l + 1};
+            r.out[0] = BitmapOut{out.hop[l].nodes, c.nodes[l], out.counts + 2 * l + 1, nullptr};
             GNN_TRY_HIP(launch_relabel(r, s));
             continue;
         }
-        // Super-batch: union of the G frontiers (bitmap 0), sampled once.
+        if (!compact) {
+            const gnn_status st = run_super_full_hop(g, front, d_F, F_cap, G, fanouts[l], hs, l, mc,
+                                                     outs, w, o, s);
+            if (st != GNN_OK) return st;
+            continue;
+        }
+        // Super-batch hop l: sample U_l once.
         const int64_t Ucap = union_cap(mc, l, G, g.num_nodes);
+        const int64_t U1cap = union_cap(mc, l + 1, G, g.num_nodes);
         const int64_t uEcap = Ucap * fanouts[l];
-        RelabelArgs ru = relabel_args(g, w, 0, 1);
-        ru.nlist = G;
-        for (int gi = 0; gi < G; ++gi) ru.list[gi] = IdList{front(gi), d_F(gi), F_cap(gi), nullptr, 0, 0};
-        ru.out[0] = BitmapOut{w.U, Ucap, w.d_U};
-        GNN_TRY_HIP(launch_relabel(ru, s));
-        HopArgs h = hop_args(g, w.U, w.d_U, Ucap, fanouts[l], hs, w.u_indptr, w.u_gid, uEcap,
-                             w.d_uE, w, o);
-        h.clear_ptr = w.bitmaps + w.W;  // the sub-batch bitmaps, zeroed before their relabel
-        h.clear_n = static_cast<int64_t>(G) * w.W;
+        int32_t *Ul = w.U[l & 1];
+        int32_t *Ul1 = w.U[(l + 1) & 1];
+        HopArgs h = hop_args(g, Ul, w.d_U + l, Ucap, fanouts[l], hs, w.u_indptr, w.u_gid, uEcap,
+                             w.d_uE + l, w, o);
         GNN_TRY_HIP(launch_classify(h, s));
         GNN_TRY_HIP(launch_sample(h, s));
+        // U_{l+1} = U_l + the sampled ids: mark the ids into the accumulated node-id bitmap, rank
+        // both lists in the result.
+        RelabelArgs ru = relabel_args(g, w);
+        ru.nlist = 2;
+        ru.list[0] = IdList{w.u_gid, w.d_uE + l, uEcap, w.u_pos, 0, 0};
+        ru.list[1] = IdList{Ul, w.d_U + l, Ucap, w.umap, 0, 2};
+        ru.out[0] = BitmapOut{Ul1, U1cap, w.d_U + l + 1, nullptr};
+        GNN_TRY_HIP(launch_relabel(ru, s));
+        // Each sub-batch's block from the union block, with U_{l+1} positions of its ids.
         DistArgs da{};
         da.G = G;
         int32_t tiles = 0;
         for (int gi = 0; gi < G; ++gi) {
             gnn_blocks &out = *outs[gi];
-            const int32_t nt = static_cast<int32_t>(dist_tiles(F_cap(gi)));
-            da.sub[gi] = DistSub{front(gi), d_F(gi), F_cap(gi), out.hop[l].indptr, out.hop[l].gid,
-                                 out.caps.edges[l], out.counts + 2 * l, tiles, nt};
+            const int32_t nt = static_cast<int32_t>(dist_tiles(F_cap(gi, l)));
+            da.sub[gi] = DistSub{front(gi, l), d_F(gi, l), F_cap(gi, l), w.upos + gi * w.P,
+                                 w.f_pos + gi * w.Fs, out.hop[l].indptr, out.hop[l].gid,
+                                 w.e_pos + gi * w.Es, out.caps.edges[l], out.counts + 2 * l,
+                                 tiles, nt};
             tiles += nt;
         }
         da.ntiles = tiles;
-        da.bm0 = w.bitmaps;
-        da.wprefix0 = w.wprefix;
-        da.id_bound = g.num_nodes;
         da.u_indptr = w.u_indptr;
         da.u_gid = w.u_gid;
+        da.u_pos = w.u_pos;
+        da.umap = w.umap;
         da.uE_cap = uEcap;
-        da.d_U = w.d_U;
+        da.d_U = w.d_U + l;
         da.U_cap = Ucap;
+        da.clear_ptr = w.bitmaps + w.W;
+        da.clear_stride = w.Wc;
+        da.d_U1 = w.d_U + l + 1;
+        da.U1_cap = U1cap;
         da.bsum = w.bsum_dist;
         da.status = w.status;
         GNN_TRY_HIP(launch_dist(da, s));
-        // Per-sub-batch relabel into bitmaps 1..G; the union bitmap is zeroed for the next hop.
-        RelabelArgs rs = relabel_args(g, w, 1, G);
+        // Per-sub-batch relabel in U_{l+1} positions; the positions of V_l become the next hop's.
+        RelabelArgs rs = compact_relabel_args(w, G, Ul1, w.d_U + l + 1, U1cap);
         rs.nlist = 2 * G;
         for (int gi = 0; gi < G; ++gi) {
             gnn_blocks &out = *outs[gi];
-            rs.list[2 * gi] = IdList{front(gi), d_F(gi), F_cap(gi), out.hop[l].dst_lid, gi, l == 0 ? 1 : 0};
-            rs.list[2 * gi + 1] = IdList{out.hop[l].gid, out.counts + 2 * l, out.caps.edges[l],
+            rs.list[2 * gi] = IdList{w.f_pos + gi * w.Fs, d_F(gi, l), F_cap(gi, l),
+                                     out.hop[l].dst_lid, gi, l == 0 ? 1 : 0};
+            rs.list[2 * gi + 1] = IdList{w.e_pos + gi * w.Es, out.counts + 2 * l, out.caps.edges[l],
                                          out.hop[l].lid, gi, 0};
-            rs.out[gi] = BitmapOut{out.hop[l].nodes, out.caps.nodes[l], out.counts + 2 * l + 1};
+            rs.out[gi] = BitmapOut{out.hop[l].nodes, out.caps.nodes[l], out.counts + 2 * l + 1,
+                                   w.upos + gi * w.P};
         }
-        rs.clear_ptr = w.bitmaps;
-        rs.clear_n = w.W;
         GNN_TRY_HIP(launch_relabel(rs, s));
     }
     return GNN_OK;
@@ -372,7 +550,13 @@ gnn_status gnn_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t g
     if (!caps || !out_bytes || num_nodes < 1 || group < 1) return GNN_ERR_INVALID_ARG;
     if (group > GNN_MAX_GROUP) return GNN_ERR_UNSUPPORTED;
     if (caps->num_hops < 1 || caps->num_hops > GNN_MAX_HOPS) return GNN_ERR_INVALID_ARG;
-    *out_bytes = carve(*caps, num_nodes, group, nullptr).bytes;
+    // any relabel mode the options may pick
+    size_t b = carve(*caps, num_nodes, group, group > 1 ? kSuperFull : kSuperNone, nullptr).bytes;
+    if (group > 1) {
+        const size_t bc = carve(*caps, num_nodes, group, kSuperCompact, nullptr).bytes;
+        b = bc > b ? bc : b;
+    }
+    *out_bytes = b;
     return GNN_OK;
 }
 
@@ -388,9 +572,9 @@ gnn_status gnn_sample_khop(const gnn_graph *g, const int32_t *seeds, int64_t n_s
     Opts o;
     if ((st = read_opts(opt, &o)) != GNN_OK) return st;
     if (!ws) return GNN_ERR_INVALID_ARG;
-    const Workspace need = carve(out->caps, g->num_nodes, 1, nullptr);
+    const Workspace need = carve(out->caps, g->num_nodes, 1, kSuperNone, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
-    const Workspace w = carve(out->caps, g->num_nodes, 1, ws);
+    const Workspace w = carve(out->caps, g->num_nodes, 1, kSuperNone, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
     GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
     const int32_t *sp[1] = {seeds};
@@ -404,7 +588,7 @@ gnn_status gnn_sample_khop(const gnn_graph *g, const int32_t *seeds, int64_t n_s
 gnn_status gnn_relabel_workspace_size(int64_t id_bound, size_t *out_bytes) {
     if (!out_bytes || id_bound < 1 || id_bound > kInt32Max + 1) return GNN_ERR_INVALID_ARG;
     gnn_caps none{};
-    *out_bytes = carve(none, id_bound, 1, nullptr).bytes;
+    *out_bytes = carve(none, id_bound, 1, kSuperNone, nullptr).bytes;
     return GNN_OK;
 }
 
@@ -420,9 +604,9 @@ gnn_status gnn_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t
     if (!d_n_uniq || (cap_uniq > 0 && !uniq) || !ws) return GNN_ERR_INVALID_ARG;
     if (n_keep > kInt32Max || n_add > kInt32Max) return GNN_ERR_UNSUPPORTED;
     gnn_caps none{};
-    const Workspace need = carve(none, id_bound, 1, nullptr);
+    const Workspace need = carve(none, id_bound, 1, kSuperNone, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
-    const Workspace w = carve(none, id_bound, 1, ws);
+    const Workspace w = carve(none, id_bound, 1, kSuperNone, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
     GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
     RelabelArgs r{};
@@ -565,9 +749,10 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         nsg[gi] = ns;
         ob[gi] = &mo.blocks;
     }
-    const Workspace need = carve(mc, g->num_nodes, group, nullptr);
+    const SuperMode mode = super_mode(mc, g->num_nodes, group, o.flags);
+    const Workspace need = carve(mc, g->num_nodes, group, mode, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
-    const Workspace w = carve(mc, g->num_nodes, group, ws);
+    const Workspace w = carve(mc, g->num_nodes, group, mode, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t *ev = nullptr;
     if (timer) {

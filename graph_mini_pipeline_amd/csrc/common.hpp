@@ -163,7 +163,7 @@ struct IdList {
     int64_t cap;
     int32_t *lid;
     int32_t bitmap;
-    int32_t pass;
+    int32_t pass;        // 1: marked first, repeats reported; 0: marked; 2: ranked only
 };
 
 // The sorted unique list of one bitmap.
@@ -171,6 +171,7 @@ struct BitmapOut {
     int32_t *uniq;
     int64_t uniq_cap;
     int64_t *d_uniq;
+    int32_t *pos;        // optional: the bit positions themselves (equal to uniq unless mapped)
 };
 
 struct RelabelArgs {
@@ -178,8 +179,12 @@ struct RelabelArgs {
     int32_t nlist;
     int64_t list_off[2 * kMaxGroup + 1];  // filled by launch_relabel
     BitmapOut out[kMaxGroup];
+    int64_t out_off[kMaxGroup + 1];       // filled by launch_relabel
     int32_t nbm;              // bitmaps (one per BitmapOut)
     int64_t id_bound;
+    const int64_t *d_bound;   // optional device bound on the ids (at most id_bound); bitmap words
+                              // at or past it are ignored, whatever they hold
+    const int32_t *id_map;    // optional: bit position p stands for id id_map[p] in uniq
     uint32_t *bitmap;         // [nbm * W]
     uint32_t *wprefix;        // [nbm * W]
     uint32_t *bsum;           // [nbm * nbw]
@@ -191,6 +196,12 @@ struct RelabelArgs {
     int32_t bitmap_cleared;   // the bitmaps are already zero on this stream
 };
 
+__device__ __forceinline__ int64_t relabel_bound(const RelabelArgs &a) {
+    if (a.d_bound == nullptr) return a.id_bound;
+    const int64_t b = *a.d_bound;
+    return b < 0 ? 0 : (b < a.id_bound ? b : a.id_bound);
+}
+
 // Destinations per workgroup of the super-batch distribution (one wavefront's lanes).
 constexpr int kDistTile = 64;
 
@@ -199,8 +210,12 @@ struct DistSub {
     const int32_t *front;
     const int64_t *d_F;
     int64_t F_cap;
+    const int32_t *upos;  // [F] position of each destination in the union frontier U_l, or NULL:
+                          // the rank of front[i] in the union bitmap
+    int32_t *f_pos;       // [F] out (with upos): position of each destination in U_{l+1}
     int32_t *blk_indptr;
     int32_t *blk_gid;
+    int32_t *e_pos;       // [E_cap] out (with upos): position of each sampled id in U_{l+1}
     int64_t E_cap;
     int64_t *d_E;
     int32_t tile0;  // first tile of this sub-batch in the launch
@@ -211,14 +226,20 @@ struct DistArgs {
     DistSub sub[kMaxGroup];
     int32_t G;
     int32_t ntiles;
-    const uint32_t *bm0;       // union bitmap and its word prefixes
+    const uint32_t *bm0;       // union bitmap and its word prefixes (destinations without upos)
     const uint32_t *wprefix0;
     int64_t id_bound;
     const int32_t *u_indptr;   // union block
     const int32_t *u_gid;
+    const int32_t *u_pos;      // position in U_{l+1} of each union-block id
+    const int32_t *umap;       // position in U_{l+1} of each element of U_l
     int64_t uE_cap;
-    const int64_t *d_U;
+    const int64_t *d_U;        // |U_l|
     int64_t U_cap;
+    uint32_t *clear_ptr;       // optional: G sub-batch bitmaps of stride clear_stride words,
+    int64_t clear_stride;      // zeroed up to ceil(|U_{l+1}| / 32) words each
+    const int64_t *d_U1;       // |U_{l+1}|
+    int64_t U1_cap;
     uint32_t *bsum;            // [ntiles]
     int32_t *status;
 };

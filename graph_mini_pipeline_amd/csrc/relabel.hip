@@ -14,8 +14,11 @@
 //   prefix[v >> 5] + popcount(word[v >> 5] & ((1 << (v & 31)) - 1)).
 // Work is O(id_bound / 32) words plus O(list length); every output position comes from a scan.
 //
-// One launch sequence serves several bitmaps at once: each id list names the bitmap it marks
-// (a super-batch marks every sub-batch's lists into its own bitmap, or all frontiers into one).
+// One launch sequence serves several bitmaps at once: each id list names the bitmap it marks.
+// The ids may also be positions in a sorted list of global ids (id_map): then the bitmap covers
+// only that list, the emitted ids are id_map[position] (still ascending), and a device count
+// bounds the live part of the bitmap, so that a super-batch relabels each sub-batch in the
+// compact space of the super-batch's own sorted node set instead of the whole id range.
 #include "common.hpp"
 
 namespace gnnmb {
@@ -55,6 +58,7 @@ __device__ __forceinline__ int find_list(const RelabelArgs &a, int64_t t) {
 // anything else) an id whose bit is already set is a duplicate within that list's bitmap.
 __global__ __launch_bounds__(256) void k_mark(RelabelArgs a, int32_t pass) {
     const int64_t total = a.list_off[a.nlist];
+    const int64_t bound = relabel_bound(a);
     for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
          t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int l = find_list(a, t);
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(256) void k_mark(RelabelArgs a, int32_t pass) {
         const int64_t i = t - a.list_off[l];
         if (i >= load_count(L.d_n, L.cap)) continue;
         const int32_t v = L.ids[i];
-        if (v < 0 || v >= a.id_bound) {
+        if (v < 0 || v >= bound) {
             set_status(a.status, GNN_ERR_OUT_OF_RANGE);
             continue;
         }
@@ -78,6 +82,13 @@ __global__ __launch_bounds__(256) void k_mark(RelabelArgs a, int32_t pass) {
     }
 }
 
+// Words of each bitmap that can hold a set bit.
+__device__ __forceinline__ int64_t live_words(const RelabelArgs &a) {
+    if (a.d_bound == nullptr) return a.W;
+    const int64_t w = (relabel_bound(a) + 31) >> 5;
+    return w < a.W ? w : a.W;
+}
+
 // Per-tile popcounts; tile t covers kBitmapTile words of bitmap t / nbw.  Also zeroes the
 // optional clear region (a bitmap no longer needed by this stream).
 __global__ __launch_bounds__(kBitmapThreads) void k_popc_tiles(RelabelArgs a) {
@@ -90,10 +101,11 @@ __global__ __launch_bounds__(kBitmapThreads) void k_popc_tiles(RelabelArgs a) {
     const uint32_t *words = a.bitmap + static_cast<int64_t>(bm) * a.W;
     const int64_t w0 = static_cast<int64_t>(lt) * kBitmapTile +
                        static_cast<int64_t>(threadIdx.x) * kBitmapWordsPerThread;
+    const int64_t Wl = live_words(a);
     uint32_t c = 0;
 #pragma unroll
     for (int q = 0; q < kBitmapWordsPerThread; ++q)
-        if (w0 + q < a.W) c += __popc(words[w0 + q]);
+        if (w0 + q < Wl) c += __popc(words[w0 + q]);
     c = wave_sum(c);
     if (lane_id() == 0) red[threadIdx.x >> 6] = c;
     __syncthreads();
@@ -175,11 +187,13 @@ __global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a, int32_t 
     uint32_t *wpre = a.wprefix + static_cast<int64_t>(bm) * a.W;
     const int64_t w0 = static_cast<int64_t>(lt) * kBitmapTile +
                        static_cast<int64_t>(threadIdx.x) * kBitmapWordsPerThread;
+    const int64_t Wl = live_words(a);
+    if (static_cast<int64_t>(lt) * kBitmapTile >= Wl) return;  // whole workgroup: nothing live
     uint32_t wv[kBitmapWordsPerThread];
     uint32_t c = 0;
 #pragma unroll
     for (int q = 0; q < kBitmapWordsPerThread; ++q) {
-        wv[q] = w0 + q < a.W ? words[w0 + q] : 0u;
+        wv[q] = w0 + q < Wl ? words[w0 + q] : 0u;
         c += __popc(wv[q]);
     }
     uint32_t total;
@@ -188,23 +202,42 @@ __global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a, int32_t 
 #pragma unroll
     for (int q = 0; q < kBitmapWordsPerThread; ++q) {
         const int64_t w = w0 + q;
-        if (w >= a.W) break;
+        if (w >= Wl) break;
         wpre[w] = run;
         uint32_t bits = wv[q];
         while (bits) {
             const int b = __ffs(bits) - 1;
             bits &= bits - 1u;
-            if (static_cast<int64_t>(run) < o.uniq_cap) o.uniq[run] = static_cast<int32_t>(w * 32 + b);
+            if (static_cast<int64_t>(run) < o.uniq_cap) {
+                const int32_t p = static_cast<int32_t>(w * 32 + b);
+                o.uniq[run] = p;  // mapped through id_map by k_rank
+                if (o.pos) o.pos[run] = p;
+            }
             ++run;
         }
     }
 }
 
-// Ranks of every list that asks for them, in its bitmap's unique list.
+// Ranks of every list that asks for them, in its bitmap's unique list; with an id map, also
+// replaces each emitted position by its id (a separate pass keeps the dependent loads out of the
+// emit loop, which writes one set bit after another).
 __global__ __launch_bounds__(256) void k_rank(RelabelArgs a) {
     const int64_t total = a.list_off[a.nlist];
-    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
+    const int64_t all = total + (a.id_map ? a.out_off[a.nbm] : 0);
+    const int64_t bound = relabel_bound(a);
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < all;
          t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        if (t >= total) {
+            int b = 0;
+            while (b + 1 < a.nbm && a.out_off[b + 1] <= t - total) ++b;
+            const BitmapOut &o = a.out[b];
+            const int64_t i = t - total - a.out_off[b];
+            if (i < load_count(o.d_uniq, o.uniq_cap)) {
+                const int32_t p = o.uniq[i];
+                o.uniq[i] = p >= 0 && p < bound ? a.id_map[p] : -1;
+            }
+            continue;
+        }
         const int l = find_list(a, t);
         const IdList &L = a.list[l];
         if (L.lid == nullptr) continue;
@@ -212,7 +245,7 @@ __global__ __launch_bounds__(256) void k_rank(RelabelArgs a) {
         if (i >= load_count(L.d_n, L.cap)) continue;
         const int32_t v = L.ids[i];
         int32_t r = -1;
-        if (v >= 0 && v < a.id_bound) {
+        if (v >= 0 && v < bound) {
             const int64_t w = static_cast<int64_t>(L.bitmap) * a.W + (v >> 5);
             r = static_cast<int32_t>(a.wprefix[w] + __popc(a.bitmap[w] & ((1u << (v & 31)) - 1u)));
         }
@@ -233,6 +266,12 @@ hipError_t launch_relabel(RelabelArgs a, hipStream_t s) {
         any_pass1 |= a.list[l].pass == 1;
     }
     a.list_off[a.nlist] = total;
+    int64_t outs = 0;
+    for (int b = 0; b < a.nbm; ++b) {
+        a.out_off[b] = outs;
+        outs += a.out[b].uniq_cap;
+    }
+    a.out_off[a.nbm] = outs;
     if (!a.bitmap_cleared) {
         hipError_t e = launch_fill_u32(a.bitmap, static_cast<int64_t>(a.nbm) * a.W, 0u, s);
         if (e != hipSuccess) return e;
@@ -246,8 +285,10 @@ hipError_t launch_relabel(RelabelArgs a, hipStream_t s) {
     const int pre = a.nbw > kSelfScanMaxTiles ? 1 : 0;
     if (pre) hipLaunchKernelGGL(k_popc_scan, dim3(a.nbm), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(k_emit, dim3(a.nbm * a.nbw), dim3(kBitmapThreads), 0, s, a, pre);
-    if (any_rank && total > 0)
-        hipLaunchKernelGGL(k_rank, dim3(grid_for(total, 256, 4096)), dim3(256), 0, s, a);
+    const int64_t rank_items = (any_rank ? total : 0) + (a.id_map ? outs : 0);
+    if (rank_items > 0)
+        hipLaunchKernelGGL(k_rank, dim3(grid_for(total + (a.id_map ? outs : 0), 256, 4096)),
+                           dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

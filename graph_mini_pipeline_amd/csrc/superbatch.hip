@@ -6,11 +6,16 @@
 // appears once in the super-batch view while each mini-batch keeps its own logical result.
 //
 // Here the G sub-batches of a super-batch share one batch seed, so the sample of node v at hop l
-// is the same in every sub-batch whose frontier holds v.  The union U of the G frontiers is
-// relabelled (bitmap B0), classified and sampled once; then every sub-batch takes, for each of its
-// destinations v, the row of v in the union block: c = u_indptr[r+1] - u_indptr[r] with
-// r = rank of v in U, an exclusive scan of c within the sub-batch gives its block indptr, and the
-// row's ids are copied.  Each sub-batch's result is therefore exactly that of a separate run.
+// is the same in every sub-batch whose frontier holds v.  The union U_l of the G frontiers is
+// classified and sampled once.  (With full-range sub-batch bitmaps, a destination's union row is
+// found by its rank in the union bitmap and only the ids are copied; the compact relabel follows.)  Its sampled ids and U_l itself are relabelled into
+// U_{l+1} = U_l + sampled ids, which is the union of the G node sets V_l, so every id of every
+// sub-batch's block has a position in U_{l+1}.  Each sub-batch then takes, for destination i at
+// union position r = upos[i], the union row [u_indptr[r], u_indptr[r+1]): an exclusive scan of
+// the row lengths within the sub-batch gives its block indptr, and the row's ids and their
+// U_{l+1} positions are copied.  The sub-batch's own relabel then runs on those positions
+// (a bitmap of |U_{l+1}| bits instead of one over every node id), and its result is exactly that
+// of a separate run.
 #include "common.hpp"
 
 namespace gnnmb {
@@ -26,16 +31,25 @@ __device__ __forceinline__ int32_t union_rank(const DistArgs &a, int32_t v) {
     return static_cast<int32_t>(a.wprefix0[v >> 5] + __popc(w & ((1u << (v & 31)) - 1u)));
 }
 
-// Destination i of sub-batch g: its union row [lo, hi) (empty if the id is invalid).
+// Destination i of a sub-batch: its union row [lo, lo + c) and (compact relabel) its position in
+// U_{l+1} (-1 and an empty row for a destination without a union position: an invalid seed,
+// already reported by the union marking).
 __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, int64_t i,
-                                          int64_t &lo, int32_t &c) {
+                                          int64_t &lo, int32_t &c, int32_t &next_pos) {
     lo = 0;
     c = 0;
-    const int32_t v = S.front[i];
-    if (v < 0 || v >= a.id_bound) return;  // reported by the union marking
+    next_pos = -1;
+    int32_t r;
+    if (S.upos) {
+        r = S.upos[i];
+    } else {
+        const int32_t v = S.front[i];
+        if (v < 0 || v >= a.id_bound) return;  // reported by the union marking
+        r = union_rank(a, v);
+    }
+    if (r < 0) return;
     const int64_t nU = load_count(a.d_U, a.U_cap);
-    const int32_t r = union_rank(a, v);
-    if (r < 0 || r >= nU) {
+    if (r >= nU) {
         set_status(a.status, GNN_ERR_INTERNAL);
         return;
     }
@@ -44,19 +58,33 @@ __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, i
     l1 = l1 < l0 ? l0 : (l1 > a.uE_cap ? a.uE_cap : l1);
     lo = l0;
     c = static_cast<int32_t>(l1 - l0);
+    if (a.umap) next_pos = a.umap[r];
 }
 
-// Tiles of kDistTile destinations: wavefront 0 handles one destination per lane; the whole
-// workgroup then copies the tile's rows.
+// Tiles of kDistTile destinations: wavefront 0 handles one destination per lane.  The whole grid
+// first zeroes the live words of the sub-batch bitmaps that the sub-batch relabel marks next.
 __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
+    if (a.clear_ptr) {
+        const int64_t n1 = load_count(a.d_U1, a.U1_cap);
+        const int64_t words = (n1 + 31) >> 5;
+        const int64_t total = words * a.G;
+        for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
+             t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+            const int64_t g = t / words;
+            a.clear_ptr[g * a.clear_stride + (t - g * words)] = 0u;
+        }
+    }
     if (threadIdx.x >= kDistTile) return;
     const int t = blockIdx.x;
     const DistSub &S = a.sub[find_sub(a, t)];
     const int64_t F = load_count(S.d_F, S.F_cap);
     const int64_t i = static_cast<int64_t>(t - S.tile0) * kDistTile + threadIdx.x;
     int64_t lo;
-    int32_t c = 0;
-    if (i < F) union_row(a, S, i, lo, c);
+    int32_t c = 0, np;
+    if (i < F) {
+        union_row(a, S, i, lo, c, np);
+        if (S.f_pos) S.f_pos[i] = np;
+    }
     const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
     if (threadIdx.x == 0) a.bsum[t] = sum;
 }
@@ -97,8 +125,8 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
     if (threadIdx.x < kDistTile) {
         const int64_t i = static_cast<int64_t>(lt) * kDistTile + threadIdx.x;
         int64_t lo = 0;
-        int32_t c = 0;
-        if (i < F) union_row(a, S, i, lo, c);
+        int32_t c = 0, np;
+        if (i < F) union_row(a, S, i, lo, c, np);
         const uint32_t inc = wave_inclusive_scan(static_cast<uint32_t>(c));
         const uint32_t o = inc - static_cast<uint32_t>(c);
         s_item_off[threadIdx.x] = o;
@@ -116,7 +144,11 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
             else hi_i = mid;
         }
         const int64_t dst = static_cast<int64_t>(s_off) + p;
-        if (dst < S.E_cap) S.blk_gid[dst] = a.u_gid[s_item_lo[lo_i] + (p - s_item_off[lo_i])];
+        const int64_t src = s_item_lo[lo_i] + (p - s_item_off[lo_i]);
+        if (dst < S.E_cap) {
+            S.blk_gid[dst] = a.u_gid[src];
+            if (S.e_pos) S.e_pos[dst] = a.u_pos[src];
+        }
     }
 }
 

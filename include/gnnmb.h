@@ -53,6 +53,13 @@ typedef void *gnn_stream; /* hipStream_t */
 
 /* Flags for gnn_options.flags. */
 #define GNN_SYNC 1u /* synchronise the stream at the end of the call and return the device status */
+/* How gnn_minibatch relabels the sub-batches of a super-batch (results are identical; at most one
+ * may be set; by default the library picks from the sizes):
+ *   FULL:    each sub-batch gets a bitmap over all node ids (cheapest when num_nodes is small);
+ *   COMPACT: the union of the sub-batches' node sets is relabelled once per hop and each sub-batch
+ *            relabels positions in it (cheapest when num_nodes is large). */
+#define GNN_SUPERBATCH_FULL 2u
+#define GNN_SUPERBATCH_COMPACT 4u
 
 /*
  * Graph in CSR form by destination: row v lists the sources u of the edges (u, v), which is the
@@ -100,7 +107,7 @@ typedef struct gnn_options {
     int32_t group_max_deg; /* degree bound of the 16-lane class (default 256) */
     int32_t wave_max_deg;  /* degree bound of the one-wavefront class (default 4096); higher
                               degrees take one workgroup per node */
-    uint32_t flags;        /* GNN_SYNC */
+    uint32_t flags;        /* GNN_SYNC | GNN_SUPERBATCH_FULL | GNN_SUPERBATCH_COMPACT */
     int32_t reserved[5];
 } gnn_options;
 

@@ -1,9 +1,11 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark times.
 
 Workloads are generated on the GPU: the dense-neighbourhood one (233,000 nodes, 115M edges,
-602-d rows with stride 604, batches of 1024 seeds, fanouts [25, 10]) and the mid-scale one
-(2.45M nodes, 124M edges, 100-d, fanouts [15, 10, 5], super-batches of 8).  Whole batches are
-compared with the oracle (bit-exact blocks and rows, means within 1e-5 * max|X|).
+602-d rows with stride 604, batches of 1024 seeds, fanouts [25, 10]), the mid-scale one
+(2.45M nodes, 124M edges, 100-d, fanouts [15, 10, 5], super-batches of 8) and the large one
+(111M nodes, 1.6B edges, int64 indptr, 128-d, 57 GB of features in HBM).  Whole batches are
+compared with the oracle (bit-exact blocks and rows, means within 1e-5 * max|X|), with both
+super-batch relabel modes.
 """
 import numpy as np
 import pytest
@@ -40,7 +42,15 @@ def mid():
     return _workload("mid")
 
 
-def _run(cfg, g, table, order, batches, seed64):
+@pytest.fixture(scope="module")
+def large():
+    w = _workload("large")
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+def _run(cfg, g, table, order, batches, seed64, mode="auto"):
     dg = gm.DeviceGraph(cfg.num_nodes, g.indptr, g.indices)
     fs = gm.gnn_feature_store_create(table, cfg.d)
     lo = batches[0] * cfg.batch
@@ -51,7 +61,8 @@ def _run(cfg, g, table, order, batches, seed64):
     caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
     ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, len(batches)), dtype=torch.uint8,
                      device="cuda")
-    gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, seed64, outs, ws)
+    gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, seed64, outs, ws,
+                     gm.Options(superbatch=mode))
     assert gm.gnn_read_device_status(ws) == gm.GNN_OK
     return outs, ptr
 
@@ -66,11 +77,12 @@ def test_dense_single_batch(dense, b):
     compare_with_oracle(outs[0], ref, cfg.d)
 
 
-def test_dense_superbatch_of_8(dense):
+@pytest.mark.parametrize("mode", ["auto", "compact"])
+def test_dense_superbatch_of_8(dense, mode):
     cfg, g, table, order, (indptr, indices, x, order_h) = dense
     seed64 = gm.gnn_batch_seed(cfg.rng_seed, 3)
     batches = list(range(24, 32))
-    outs, ptr = _run(cfg, g, table, order, batches, seed64)
+    outs, ptr = _run(cfg, g, table, order, batches, seed64, mode)
     for j in (0, 5):
         b = batches[j]
         seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
@@ -91,13 +103,37 @@ def test_dense_superbatch_last_partial(dense):
     compare_with_oracle(outs[2], ref, cfg.d)
 
 
-def test_mid_superbatch_of_8(mid):
+@pytest.mark.parametrize("mode", ["auto", "compact"])
+def test_mid_superbatch_of_8(mid, mode):
     cfg, g, table, order, (indptr, indices, x, order_h) = mid
     seed64 = gm.gnn_batch_seed(cfg.rng_seed, 0)
     batches = list(range(0, 8))
-    outs, ptr = _run(cfg, g, table, order, batches, seed64)
+    outs, ptr = _run(cfg, g, table, order, batches, seed64, mode)
     for j in (0, 7):
         b = batches[j]
         seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
         ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
         compare_with_oracle(outs[j], ref, cfg.d)
+
+
+@pytest.mark.parametrize("mode,check", [("auto", (0, 7)), ("full", (3,))])
+def test_large_superbatch_of_8(large, mode, check):
+    cfg, g, table, order, (indptr, indices, x, order_h) = large
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 0)
+    batches = list(range(0, 8))
+    outs, ptr = _run(cfg, g, table, order, batches, seed64, mode)
+    for j in check:
+        b = batches[j]
+        seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
+        ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+        compare_with_oracle(outs[j], ref, cfg.d)
+
+
+def test_large_single_batch(large):
+    cfg, g, table, order, (indptr, indices, x, order_h) = large
+    b = 100_000
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, b)
+    outs, _ = _run(cfg, g, table, order, [b], seed64)
+    seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
+    ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+    compare_with_oracle(outs[0], ref, cfg.d)

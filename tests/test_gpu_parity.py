@@ -304,20 +304,26 @@ def test_repeat_runs_identical(tiny):
             assert np.array_equal(u, v)
 
 
-def test_superbatch_equals_separate_runs(tiny):
+SUPER_MODES = ["auto", "full", "compact"]
+
+
+@pytest.mark.parametrize("mode", SUPER_MODES)
+def test_superbatch_equals_separate_runs(tiny, mode):
     cfg, indptr, indices, x, order = tiny
     dg = device_graph(indptr, indices)
     fs = _store(x)
     seeds = order[:700]
     ptr = [0, 256, 256, 600, 700]
-    outs, st = run_minibatch(dg, fs, seeds, cfg.fanouts, 77, group_ptr=ptr)
+    outs, st = run_minibatch(dg, fs, seeds, cfg.fanouts, 77, group_ptr=ptr,
+                             opts=gm.Options(superbatch=mode))
     assert st == gm.GNN_OK
     for g in range(4):
         ref = oracle.minibatch(indptr, indices, x, seeds[ptr[g]:ptr[g + 1]], cfg.fanouts, 77)
         compare_with_oracle(outs[g], ref, cfg.d)
 
 
-def test_superbatch_of_16_with_overlap(tiny):
+@pytest.mark.parametrize("mode", SUPER_MODES)
+def test_superbatch_of_16_with_overlap(tiny, mode):
     # 16 sub-batches; sub-batches may share seeds (each must be distinct within itself)
     cfg, indptr, indices, x, order = tiny
     dg = device_graph(indptr, indices)
@@ -325,19 +331,62 @@ def test_superbatch_of_16_with_overlap(tiny):
     parts = [order[i * 40:(i + 1) * 40 + 13] for i in range(16)]   # consecutive parts overlap
     seeds = np.concatenate(parts)
     ptr = np.concatenate([[0], np.cumsum([len(p) for p in parts])]).tolist()
-    outs, st = run_minibatch(dg, fs, seeds, [12, 6, 3], 5150, group_ptr=ptr)
+    outs, st = run_minibatch(dg, fs, seeds, [12, 6, 3], 5150, group_ptr=ptr,
+                             opts=gm.Options(superbatch=mode))
     assert st == gm.GNN_OK
     for g in (0, 7, 15):
         ref = oracle.minibatch(indptr, indices, x, parts[g], [12, 6, 3], 5150)
         compare_with_oracle(outs[g], ref, cfg.d)
 
 
-def test_superbatch_duplicate_within_sub_batch_reported(tiny):
+@pytest.mark.parametrize("mode", SUPER_MODES)
+def test_superbatch_duplicate_within_sub_batch_reported(tiny, mode):
     cfg, indptr, indices, x, order = tiny
     seeds = np.array([1, 2, 3, 3, 4], np.int32)      # sub-batch 1 holds 3 twice
     _, st = run_minibatch(device_graph(indptr, indices), _store(x), seeds, [3], 1,
-                          group_ptr=[0, 2, 5])
+                          group_ptr=[0, 2, 5], opts=gm.Options(superbatch=mode))
     assert st == gm.GNN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("mode", SUPER_MODES)
+def test_superbatch_out_of_range_seed_reported(tiny, mode):
+    cfg, indptr, indices, x, order = tiny
+    seeds = np.array([1, 2, 3, cfg.num_nodes, 4], np.int32)
+    _, st = run_minibatch(device_graph(indptr, indices), _store(x), seeds, [3, 2], 1,
+                          group_ptr=[0, 2, 5], opts=gm.Options(superbatch=mode))
+    assert st == gm.GNN_ERR_OUT_OF_RANGE
+
+
+@pytest.mark.parametrize("mode", ["full", "compact"])
+def test_superbatch_single_node_graph_regions(mode):
+    # two sub-batches on a star: every leaf's only neighbour is the hub, the hub has them all;
+    # the union at hop 2 is the whole graph in both sub-batches
+    indptr, indices = H.star(3000)
+    x = np.random.default_rng(3).standard_normal((3001, 8)).astype(np.float32)
+    seeds = np.array([5, 17, 2999, 0, 17, 40], np.int32)
+    outs, st = run_minibatch(device_graph(indptr, indices), _store(x), seeds, [4, 3], 99,
+                             group_ptr=[0, 3, 6], opts=gm.Options(superbatch=mode))
+    assert st == gm.GNN_OK
+    for g, (a, b) in enumerate([(0, 3), (3, 6)]):
+        ref = oracle.minibatch(indptr, indices, x, seeds[a:b], [4, 3], 99)
+        compare_with_oracle(outs[g], ref, 8)
+
+
+class _BothModes(gm.Options):
+    def c(self):
+        o = super().c()
+        o.flags |= gm.GNN_SUPERBATCH_FULL | gm.GNN_SUPERBATCH_COMPACT
+        return o
+
+
+def test_superbatch_both_flags_rejected(tiny):
+    cfg, indptr, indices, x, order = tiny
+    with pytest.raises(ValueError):
+        gm.Options(superbatch="both").c()
+    with pytest.raises(gm.GnnError) as e:
+        run_minibatch(device_graph(indptr, indices), _store(x), order[:20], [3], 1,
+                      group_ptr=[0, 10, 20], opts=_BothModes())
+    assert e.value.status == gm.GNN_ERR_INVALID_ARG
 
 
 def test_superbatch_too_large_rejected(tiny):
