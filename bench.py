@@ -22,6 +22,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+PRESAMPLE_BATCHES = 64     # batches pre-sampled to rank the hot-row cache (disjoint seeds)
 
 
 def progress(msg: str) -> None:
@@ -100,21 +101,41 @@ def main():
     graph = synth.build_graph(cfg, device=dev)
     torch.cuda.synchronize()
     progress(f"graph: {cfg.num_nodes} nodes, {graph.indices.numel()} edges in {time.perf_counter() - t0:.1f} s")
-    table = torch.empty(cfg.num_nodes, cfg.ld, dtype=torch.float32, device=dev)
-    synth.make_features(cfg, table)
+    if cfg.host_features:
+        table = torch.empty(cfg.num_nodes, cfg.ld, dtype=torch.float32, pin_memory=True)
+        synth.make_features(cfg, table, device=dev)
+    else:
+        table = torch.empty(cfg.num_nodes, cfg.ld, dtype=torch.float32, device=dev)
+        synth.make_features(cfg, table)
     order = synth.epoch_seed_order(cfg, 0, device=dev).contiguous()
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t0
-    progress(f"features and seed order ready, {t_gen:.1f} s in all")
+    progress(f"features ({'pinned host' if cfg.host_features else 'HBM'}) and seed order ready, "
+             f"{t_gen:.1f} s in all")
     n_batches = (order.numel() + cfg.batch - 1) // cfg.batch
     G = args.group
     n_super = (n_batches + G - 1) // G
-    # default: one epoch for a workload with a training set, else 40 super-batches
-    steps = args.steps or (n_super if cfg.n_train else min(n_super, 40))
+    # default: one epoch for a workload with a training set, 10 super-batches with a host-resident
+    # table, else 40 super-batches
+    steps = args.steps or (n_super if cfg.n_train else min(n_super, 10 if cfg.host_features else 40))
     K = len(cfg.fanouts)
 
     dg = gm.DeviceGraph(cfg.num_nodes, graph.indptr, graph.indices)
-    fs = gm.gnn_feature_store_create(table, cfg.d)
+    cache_rows, t_rank = 0, 0.0
+    hot_order = None
+    if cfg.cache_bytes:
+        from graph_mini_pipeline_amd.hotness import presample_hot_order
+        t1 = time.perf_counter()
+        cache_rows = min(cfg.num_nodes, cfg.cache_bytes // (cfg.ld * 4))
+        pre = synth.presample_seeds(cfg, PRESAMPLE_BATCHES, device=dev)
+        if pre.numel() // cfg.batch + steps * G > n_batches:
+            raise SystemExit("pre-sampling seeds would overlap the measured batches")
+        hot_order = presample_hot_order(dg, graph.indptr, pre, cfg.batch, cfg.fanouts,
+                                        synth.sub_seed(cfg.rng_seed, 6), cache_rows)
+        t_rank = time.perf_counter() - t1
+        progress(f"hot-row order: {PRESAMPLE_BATCHES} pre-sampled batches, {cache_rows} cache rows, "
+                 f"{t_rank:.1f} s")
+    fs = gm.gnn_feature_store_create(table, cfg.d, cache_rows, hot_order)
     caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
     S = max(1, args.streams)
     wss = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
@@ -180,12 +201,18 @@ def main():
     gb_bytes = []
     mean_bytes = []
     payload = []
+    hits = torch.zeros(1, dtype=torch.int64, device=dev)
+    rows_gathered = 0
     for b in range(steps):
         _, mine = step(b)
         torch.cuda.synchronize()
         g_s, m_s, p_s = 0, [0] * K, 0
         for _, n, out in mine:
+            if cache_rows:   # hits of this batch's gather: the same gather again, counting
+                gm.gnn_gather_features(fs, out.blocks.nodes[K - 1], out.x,
+                                       d_n=out.blocks.counts[2 * K - 1:2 * K], d_hits=hits)
             cnt = out.blocks.counts.cpu().tolist()
+            rows_gathered += cnt[2 * K - 1]
             g_b, m_b, E, V = algorithmic_bytes(cnt, n, cfg.d, K)
             tot_edges += sum(E)
             g_s += g_b
@@ -262,11 +289,60 @@ def main():
     result["copy_probe_bytes"] = probe_src.numel() * 4
     del probe_src, probe_dst
 
+    if cfg.host_features:
+        n_hits = int(hits.item())
+        miss_bytes = (rows_gathered - n_hits) * cfg.d * 4
+        link = host_link(gm, table, dev)
+        miss_rate = miss_bytes / t_gather / 1e9
+        result["cache"] = {"rows": cache_rows, "bytes": cache_rows * cfg.ld * 4,
+                           "fraction_of_rows": cache_rows / cfg.num_nodes,
+                           "ranking": f"{PRESAMPLE_BATCHES} pre-sampled batches from seeds the "
+                                      f"measurement does not use; (count desc, degree desc, id asc)",
+                           "ranking_s": t_rank,
+                           "hit_rate": n_hits / max(1, rows_gathered)}
+        result["host_link"] = dict(link, miss_GB_per_step=miss_bytes / steps / 1e9,
+                                   miss_GBps_during_gather=miss_rate,
+                                   frac=miss_rate / link["B_link_GBps"])
+        # the gather's misses cross the host link: that link, not HBM, bounds the dominant kernel
+        result["roofline_hbm"] = result["roofline"]
+        result["roofline"] = {"bound": "host-link", "kernel": names["gather"],
+                              "achieved": miss_rate, "peak": link["B_link_GBps"], "unit": "GB/s",
+                              "frac": miss_rate / link["B_link_GBps"], "traffic": None,
+                              "peak_source": "measured: best of 5 hipMemcpyAsync of 1 GiB pinned host -> device",
+                              "avg_launch_ms": kern["gather"][1], "launches_per_step": G}
     progress("stage timing and counts done")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, graph, table, order, step, args.cpu_seconds,
                                               tot_edges / wall)
     print(json.dumps(result), flush=True)
+
+
+def host_link(gm, table, dev):
+    """Host -> device bandwidth: the best of 5 hipMemcpyAsync copies of 1 GiB from pinned host
+    memory (B_link), and the best of 5 zero-copy streaming reads of the same bytes by a kernel."""
+    import torch
+
+    n = (1 << 30) // 4
+    src = table.view(-1)[:n]
+    dst = torch.empty(n, dtype=torch.float32, device=dev)
+    best_copy, best_zc = 0.0, 0.0
+    for _ in range(5):
+        for kind in ("copy", "zero_copy"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if kind == "copy":
+                dst.copy_(src, non_blocking=True)
+            else:
+                gm.gnn_copy_probe_host(src, dst)
+            e1.record()
+            e1.synchronize()
+            gbps = n * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
+            if kind == "copy":
+                best_copy = max(best_copy, gbps)
+            else:
+                best_zc = max(best_zc, gbps)
+    del dst
+    return {"B_link_GBps": best_copy, "zero_copy_read_GBps": best_zc}
 
 
 def cpu_baseline(cfg, graph, table, order, step, budget_s, gpu_value):

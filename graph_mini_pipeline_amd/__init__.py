@@ -25,7 +25,7 @@ __all__ = [
     "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
     "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_minibatch",
     "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
-    "gnn_timer_elapsed", "gnn_copy_probe", "lib",
+    "gnn_timer_elapsed", "gnn_copy_probe", "gnn_copy_probe_host", "lib",
 ]
 
 lib = _abi.lib
@@ -373,6 +373,17 @@ def gnn_copy_probe(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("src and dst differ in size")
     _ok(lib().gnn_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "gnn_copy_probe")
+
+
+def gnn_copy_probe_host(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """The same copy with src in pinned host memory, read in place over the host link."""
+    if src.is_cuda or not src.is_pinned():
+        raise ValueError("src must be a pinned host tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _ok(lib().gnn_copy_probe_host(_ptr(src), _ptr(dst), nbytes, _stream(stream)),
+        "gnn_copy_probe_host")
 
 
 def gnn_read_device_status(ws: torch.Tensor, stream=None) -> int:

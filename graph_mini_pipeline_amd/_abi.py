@@ -82,6 +82,7 @@ SIGNATURES = {
     "gnn_timer_elapsed": (i32, [vp, P(i32), P(ctypes.c_float)]),
     # measurement helper (include/gnnmb_probe.h)
     "gnn_copy_probe": (i32, [vp, vp, size_t, vp]),
+    "gnn_copy_probe_host": (i32, [vp, vp, size_t, vp]),
 }
 
 _lib = None

@@ -25,3 +25,12 @@ extern "C" gnn_status gnn_copy_probe(const void *src, void *dst, size_t bytes, g
                        static_cast<u32x4 *>(dst), n);
     return hipGetLastError() == hipSuccess ? GNN_OK : GNN_ERR_HIP;
 }
+
+extern "C" gnn_status gnn_copy_probe_host(const void *host_src, void *dst, size_t bytes,
+                                          gnn_stream stream) {
+    if (!host_src) return GNN_ERR_INVALID_ARG;
+    void *mapped = nullptr;
+    if (hipHostGetDevicePointer(&mapped, const_cast<void *>(host_src), 0) != hipSuccess || !mapped)
+        return GNN_ERR_HIP;
+    return gnn_copy_probe(mapped, dst, bytes, stream);
+}

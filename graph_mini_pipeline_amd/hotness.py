@@ -1,0 +1,67 @@
+"""Hot-row ranking for the HBM feature cache, by pre-sampling (set-up, not on the mini-batch path).
+
+The caches of the pages are filled offline from access statistics: GARDEN (Sec. II.B, the
+Nfeat-cache of the Dual-Cache System; Sec. IV.B, Table III, a few pre-sampling epochs) profiles
+which feature rows sampling touches; LEO (Sec. 2.3 and its related work) names degree-ranked and
+pre-sampling-ranked hot caches.  Here P batches are sampled with the library's own sampler, each
+node counts the batches whose gathered set V_K holds it, and rows are ranked by (count descending,
+in-degree descending, id ascending).  The ranking only decides which rows sit in HBM: outputs are
+the same for any ranking.  The batches should not be the measured ones (a disjoint seed stream).
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import torch
+
+from . import (Blocks, DeviceGraph, gnn_batch_seed, gnn_capacity, gnn_read_device_status,
+               gnn_sample_khop, gnn_workspace_size, GNN_OK, GnnError)
+
+
+def presample_counts(graph: DeviceGraph, seeds: torch.Tensor, batch: int, fanouts: Sequence[int],
+                     rng_seed: int) -> torch.Tensor:
+    """int32 [N]: for each node, the number of pre-sampled batches whose V_K holds it.  Batch p
+    takes seeds[p*batch:(p+1)*batch] and the batch seed gnn_batch_seed(rng_seed, p)."""
+    N = graph.num_nodes
+    K = len(fanouts)
+    dev = seeds.device
+    counts = torch.zeros(N, dtype=torch.int32, device=dev)
+    caps = gnn_capacity(batch, fanouts, N)
+    blocks = Blocks(caps)
+    ws = torch.empty(gnn_workspace_size(caps, N), dtype=torch.uint8, device=dev)
+    P = seeds.numel() // batch
+    for p in range(P):
+        s = seeds[p * batch:(p + 1) * batch].contiguous()
+        gnn_sample_khop(graph, s, fanouts, gnn_batch_seed(rng_seed, p), blocks, ws)
+        st = gnn_read_device_status(ws)
+        if st != GNN_OK:
+            raise GnnError(st, "pre-sampling")
+        nv = int(blocks.counts[2 * K - 1].item())
+        counts.index_add_(0, blocks.nodes[K - 1][:nv].long(),
+                          torch.ones(nv, dtype=torch.int32, device=dev))
+    return counts
+
+
+def rank_rows(counts: torch.Tensor, degree: torch.Tensor, rows: int) -> torch.Tensor:
+    """int32 [rows]: the ids of the `rows` hottest rows by (count desc, degree desc, id asc)."""
+    N = counts.numel()
+    id_bits = max(1, (N - 1).bit_length())
+    cmax = int(counts.max().item()) if N else 0
+    c_bits = max(1, cmax.bit_length())
+    d_bits = 63 - id_bits - c_bits
+    if d_bits < 1:
+        raise ValueError("too many nodes or counts for the ranking key")
+    dcap = (1 << d_bits) - 1
+    ids = torch.arange(N, dtype=torch.int64, device=counts.device)
+    key = ((cmax - counts.to(torch.int64)) << (d_bits + id_bits)) \
+        | ((dcap - degree.to(torch.int64).clamp(0, dcap)) << id_bits) | ids
+    order = torch.sort(key).values & ((1 << id_bits) - 1)
+    return order[:rows].to(torch.int32).contiguous()
+
+
+def presample_hot_order(graph: DeviceGraph, indptr: torch.Tensor, seeds: torch.Tensor, batch: int,
+                        fanouts: Sequence[int], rng_seed: int, rows: int) -> torch.Tensor:
+    """Hot-row order for gnn_feature_store_create: pre-sample, count, rank (see module doc)."""
+    counts = presample_counts(graph, seeds, batch, fanouts, rng_seed)
+    degree = indptr[1:] - indptr[:-1]
+    return rank_rows(counts, degree, rows)

@@ -6,6 +6,11 @@
  * (bytes fetched from and written to memory) for a copy of known size calibrate the counter
  * readings of the other kernels.  Enqueues on `stream` and returns; GNN_ERR_INVALID_ARG on a bad
  * size or alignment.
+ *
+ * gnn_copy_probe_host runs the same kernel on a source in pinned (page-locked, mapped) host
+ * memory, read in place over the host link: the streaming ceiling of zero-copy reads, beside
+ * which the feature gather's misses to a host-resident table are measured.  host_src must come
+ * from hipHostMalloc (or torch's pin_memory); GNN_ERR_HIP if it has no device mapping.
  */
 #ifndef GNNMB_PROBE_H
 #define GNNMB_PROBE_H
@@ -17,6 +22,7 @@ extern "C" {
 #endif
 
 gnn_status gnn_copy_probe(const void *src, void *dst, size_t bytes, gnn_stream stream);
+gnn_status gnn_copy_probe_host(const void *host_src, void *dst, size_t bytes, gnn_stream stream);
 
 #ifdef __cplusplus
 }

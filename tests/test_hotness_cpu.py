@@ -1,0 +1,30 @@
+"""Host logic of the hot-row ranking (count desc, degree desc, id asc); runs on the CPU."""
+import torch
+
+from graph_mini_pipeline_amd.hotness import rank_rows
+
+
+def test_rank_order_and_ties():
+    counts = torch.tensor([0, 3, 3, 1, 0, 3], dtype=torch.int32)
+    deg = torch.tensor([9, 2, 5, 7, 1, 5])
+    # count 3: ids 1 (deg 2), 2 (deg 5), 5 (deg 5) -> 2, 5 (tie on degree: id asc), 1
+    assert rank_rows(counts, deg, 6).tolist() == [2, 5, 1, 3, 0, 4]
+    assert rank_rows(counts, deg, 2).tolist() == [2, 5]
+
+
+def test_rank_all_zero_counts_is_degree_order():
+    g = torch.Generator().manual_seed(5)
+    deg = torch.randint(0, 1000, (5000,), generator=g)
+    counts = torch.zeros(5000, dtype=torch.int32)
+    got = rank_rows(counts, deg, 5000)
+    ref = sorted(range(5000), key=lambda v: (-int(deg[v]), v))
+    assert got.tolist() == ref
+
+
+def test_rank_is_a_permutation_prefix():
+    g = torch.Generator().manual_seed(6)
+    counts = torch.randint(0, 65, (20000,), generator=g, dtype=torch.int32)
+    deg = torch.randint(0, 1 << 20, (20000,), generator=g)
+    got = rank_rows(counts, deg, 777)
+    ref = sorted(range(20000), key=lambda v: (-int(counts[v]), -int(deg[v]), v))[:777]
+    assert got.tolist() == ref
