@@ -25,7 +25,7 @@ __all__ = [
     "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
     "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_minibatch",
     "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
-    "gnn_timer_elapsed", "gnn_copy_probe", "gnn_copy_probe_host", "lib",
+    "gnn_timer_elapsed", "gnn_copy_probe", "gnn_copy_probe_host", "gnn_hash_probe", "lib",
 ]
 
 lib = _abi.lib
@@ -384,6 +384,14 @@ def gnn_copy_probe_host(src: torch.Tensor, dst: torch.Tensor, stream=None) -> No
         raise ValueError("src and dst differ in size")
     _ok(lib().gnn_copy_probe_host(_ptr(src), _ptr(dst), nbytes, _stream(stream)),
         "gnn_copy_probe_host")
+
+
+def gnn_hash_probe(seed: int, tau: int, lanes: int, per_lane: int, d_count: torch.Tensor,
+                   stream=None) -> None:
+    """lanes * per_lane sampling keys (mix64 of a stepped counter); adds the keys <= tau to d_count."""
+    _need(d_count, torch.int64, "d_count")
+    _ok(lib().gnn_hash_probe(seed, tau, lanes, per_lane, _ptr(d_count), _stream(stream)),
+        "gnn_hash_probe")
 
 
 def gnn_read_device_status(ws: torch.Tensor, stream=None) -> int:

@@ -83,6 +83,7 @@ SIGNATURES = {
     # measurement helper (include/gnnmb_probe.h)
     "gnn_copy_probe": (i32, [vp, vp, size_t, vp]),
     "gnn_copy_probe_host": (i32, [vp, vp, size_t, vp]),
+    "gnn_hash_probe": (i32, [u64, u64, i64, i64, vp, vp]),
 }
 
 _lib = None

@@ -254,7 +254,7 @@ constexpr int kBitmapTile = kBitmapThreads * kBitmapWordsPerThread;
 // Kernel launchers (each returns hipGetLastError()).
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);
-hipError_t launch_classify(const HopArgs &a, hipStream_t s);
+hipError_t launch_classify(HopArgs a, hipStream_t s);
 hipError_t launch_sample(const HopArgs &a, hipStream_t s);
 hipError_t launch_relabel(RelabelArgs a, hipStream_t s);
 hipError_t launch_dist(const DistArgs &a, hipStream_t s);

@@ -514,7 +514,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_
 // workgroups before it (one launch fewer than a separate scan).
 constexpr int kSelfScanMaxBlocks = 512;
 
-hipError_t launch_classify(const HopArgs &a, hipStream_t s) {
+// Words the classification grid clears itself (a few per thread); a larger clear region gets a
+// fill kernel of its own, sized for it.
+constexpr int64_t kClassifyClearPerThread = 16;
+
+hipError_t launch_classify(HopArgs a, hipStream_t s) {
+    if (a.clear_n > static_cast<int64_t>(a.nb) * kClassifyThreads * kClassifyClearPerThread) {
+        const hipError_t e = launch_fill_u32(a.clear_ptr, a.clear_n, 0u, s);
+        if (e != hipSuccess) return e;
+        a.clear_n = 0;
+    }
     hipLaunchKernelGGL(k_classify_count, dim3(a.nb), dim3(kClassifyThreads), 0, s, a);
     const int pre = a.nb > kSelfScanMaxBlocks ? 1 : 0;
     if (pre) hipLaunchKernelGGL(k_classify_scan, dim3(1), dim3(1024), 0, s, a);

@@ -11,6 +11,11 @@
  * memory, read in place over the host link: the streaming ceiling of zero-copy reads, beside
  * which the feature gather's misses to a host-resident table are measured.  host_src must come
  * from hipHostMalloc (or torch's pin_memory); GNN_ERR_HIP if it has no device mapping.
+ *
+ * gnn_hash_probe: `lanes` work-items (a multiple of 256) each evaluate `per_lane` (even) sampling
+ * keys, SplitMix64 mix64 of a stepped counter as in the sampler's candidate loop, and add the
+ * number of keys <= tau to *d_count (device uint64).  Keys per second of this launch are the
+ * measured ceiling of the hashing that the sampler does for every position of a long row.
  */
 #ifndef GNNMB_PROBE_H
 #define GNNMB_PROBE_H
@@ -23,6 +28,8 @@ extern "C" {
 
 gnn_status gnn_copy_probe(const void *src, void *dst, size_t bytes, gnn_stream stream);
 gnn_status gnn_copy_probe_host(const void *host_src, void *dst, size_t bytes, gnn_stream stream);
+gnn_status gnn_hash_probe(uint64_t seed, uint64_t tau, int64_t lanes, int64_t per_lane,
+                          unsigned long long *d_count, gnn_stream stream);
 
 #ifdef __cplusplus
 }

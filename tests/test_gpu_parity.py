@@ -395,3 +395,22 @@ def test_superbatch_too_large_rejected(tiny):
         run_minibatch(device_graph(indptr, indices), _store(x), order[:17], [3], 1,
                       group_ptr=list(range(18)))
     assert e.value.status == gm.GNN_ERR_UNSUPPORTED
+
+
+# Giant rows: two hubs of 10^6 and 4*10^4 in-neighbours in one frontier, with fanouts on either
+# side of the largest that the 16-lane and one-wavefront classes take.
+def _two_hubs(D1=1_000_000, D2=40_000):
+    rows = [list(range(2, 2 + D1)), list(range(3, 3 + D2))] + [[0, 1] for _ in range(D1 + 1)]
+    return H.csr_from_rows(rows)
+
+
+@pytest.mark.parametrize("fanouts", [[5, 3], [32, 2], [33, 2], [200, 1]])
+def test_giant_rows(fanouts):
+    indptr, indices = _two_hubs()
+    N = len(indptr) - 1
+    x = np.random.default_rng(11).standard_normal((N, 8)).astype(np.float32)
+    seeds = np.array([0, 1, 7, 50_000], np.int32)
+    outs, st = run_minibatch(device_graph(indptr, indices), _store(x), seeds, fanouts, 4242)
+    assert st == gm.GNN_OK
+    ref = oracle.minibatch(indptr, indices, x, seeds, fanouts, 4242)
+    compare_with_oracle(outs[0], ref, 8)
