@@ -57,26 +57,20 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-__device__ __forceinline__ float4 load_chunk4(const float *row, int col, int rem) {
-    if (rem >= 4) return *reinterpret_cast<const float4 *>(row + col);
-    float t[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < rem; ++q) t[q] = row[col + q];
-    return make_float4(t[0], t[1], t[2], t[3]);
-}
-
-// One group of G lanes per (destination, slab of G 16-byte chunks).  The group reads the
-// destination's local ids once (lane t holds edge e0 + t) and passes them round with cross-lane
-// reads, so every lane issues its row loads back to back (UNR in flight) with no dependent id load
-// in between.  Small fanouts keep UNR = 8 with a one-by-one tail: there, occupancy (more
-// wavefronts in flight) beats a deeper load queue per wavefront, which costs four registers per
-// load.  Large fanouts issue 16 loads and a predicated tail.
-template <int G, int UNR, bool PRED_TAIL>
-__global__ __launch_bounds__(256) void k_mean_v4(MeanArgs m) {
+// One group of G lanes per (destination, slab): lane gl owns the 16-byte chunks gl, gl + G, ...,
+// up to CH of them (a slab; wide rows take several slabs), so one item covers a whole row of up to
+// 4 G chunks.  The group reads the destination's local ids once (lane t holds edge e0 + t) and
+// passes them round with cross-lane reads.  Row loads are software-pipelined over a ring of R
+// edges: the sum of the oldest edge's chunks is taken and that slot is refilled with the load of
+// the edge R places later, so R edges' loads stay in flight from the first edge to the last and
+// no load waits on an id load or on the previous edge's sum.
+template <int G, int CH, int R>
+__global__ __launch_bounds__(256) void k_mean_v5(MeanArgs m) {
     const int lane = lane_id();
     const int grp = lane / G;
     const int gl = lane % G;
     const uint32_t cpr = m.cpr.d;
-    const uint32_t slabs = (cpr + G - 1) / G;
+    const uint32_t slabs = (cpr + CH * G - 1) / (CH * G);
     __shared__ uint32_t s_n[kMaxMeanSegs];  // destination count of each segment
     if (threadIdx.x < static_cast<unsigned>(m.nseg))
         s_n[threadIdx.x] = static_cast<uint32_t>(load_count(m.seg[threadIdx.x].d_n, m.seg[threadIdx.x].n_cap));
@@ -93,67 +87,66 @@ __global__ __launch_bounds__(256) void k_mean_v4(MeanArgs m) {
         int64_t e0 = S.indptr[i], e1 = S.indptr[i + 1];
         e0 = e0 < 0 ? 0 : (e0 > S.e_cap ? S.e_cap : e0);
         e1 = e1 < e0 ? e0 : (e1 > S.e_cap ? S.e_cap : e1);
-        const uint32_t ch = p * G + gl;
-        const bool active = ch < cpr;
-        const int col = static_cast<int>(ch) * 4;
-        const int rem = m.d - col;
-        const float *src = S.src + col;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint32_t ch0 = p * CH * G + gl;  // this lane's first chunk
+        bool act[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) act[q] = ch0 + q * G < cpr;
+        // Chunks are read whole: rows are 16-byte aligned with ld_src a multiple of 4, so the last
+        // chunk's padding columns are in the row; only the store honours d.
+        const float *base = S.src + static_cast<int64_t>(ch0) * 4;
+        float4 acc[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int64_t eb = e0; eb < e1; eb += G) {
             const int nb = static_cast<int>(e1 - eb < G ? e1 - eb : G);
             const int32_t mine = gl < nb ? valid_lid(m, S, S.lid[eb + gl]) : 0;
-            int e = 0;
-            for (; e + UNR <= nb; e += UNR) {
-                float4 v[UNR];
+            float4 v[R][CH];
 #pragma unroll
-                for (int q = 0; q < UNR; ++q) {
-                    int32_t u;
-                    if constexpr (G == 64) u = __builtin_amdgcn_readlane(mine, e + q);
-                    else u = __shfl(mine, grp * G + e + q, 64);
-                    v[q] = active ? load_chunk4(src + static_cast<int64_t>(u) * m.ld_src, 0, rem)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
+            for (int r = 0; r < R; ++r) {
+                int32_t u;
+                if constexpr (G == 64) u = __builtin_amdgcn_readlane(mine, r < nb ? r : 0);
+                else u = __shfl(mine, grp * G + (r < nb ? r : 0), 64);
+                const float *row = base + static_cast<int64_t>(u) * m.ld_src;
 #pragma unroll
-                for (int q = 0; q < UNR; ++q) acc = f4add(acc, v[q]);
+                for (int q = 0; q < CH; ++q)
+                    v[r][q] = (r < nb && act[q]) ? *reinterpret_cast<const float4 *>(row + q * G * 4)
+                                                 : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            if constexpr (!PRED_TAIL) {
-                for (; e < nb; ++e) {
-                    int32_t u;
-                    if constexpr (G == 64) u = __builtin_amdgcn_readlane(mine, e);
-                    else u = __shfl(mine, grp * G + e, 64);
-                    if (active) acc = f4add(acc, load_chunk4(src + static_cast<int64_t>(u) * m.ld_src, 0, rem));
-                }
-            } else if (e < nb) {
-                // Remainder (< UNR edges): predicated loads, all issued before the sums.
-                float4 v[UNR];
+            for (int e = 0; e < nb; e += R) {
 #pragma unroll
-                for (int q = 0; q < UNR; ++q) {
-                    int32_t u;
-                    const int src_lane = e + q < nb ? e + q : e;
-                    if constexpr (G == 64) u = __builtin_amdgcn_readlane(mine, src_lane);
-                    else u = __shfl(mine, grp * G + src_lane, 64);
-                    v[q] = (active && e + q < nb)
-                               ? load_chunk4(src + static_cast<int64_t>(u) * m.ld_src, 0, rem)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
+                for (int r = 0; r < R; ++r) {
 #pragma unroll
-                for (int q = 0; q < UNR; ++q)
-                    if (e + q < nb) acc = f4add(acc, v[q]);
+                    for (int q = 0; q < CH; ++q) acc[q] = f4add(acc[q], v[r][q]);
+                    const int en = e + r + R;
+                    int32_t u;
+                    if constexpr (G == 64) u = __builtin_amdgcn_readlane(mine, en < nb ? en : 0);
+                    else u = __shfl(mine, grp * G + (en < nb ? en : 0), 64);
+                    const float *row = base + static_cast<int64_t>(u) * m.ld_src;
+#pragma unroll
+                    for (int q = 0; q < CH; ++q)
+                        v[r][q] = (en < nb && act[q]) ? *reinterpret_cast<const float4 *>(row + q * G * 4)
+                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
             }
         }
-        if (!active) continue;
         const int32_t c = static_cast<int32_t>(e1 - e0);
-        float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c > 0) {
-            const float fc = static_cast<float>(c);
-            r = make_float4(acc.x / fc, acc.y / fc, acc.z / fc, acc.w / fc);
-        }
-        float *o = S.out + static_cast<int64_t>(i) * m.ld_out + col;
-        if (rem >= 4) {
-            *reinterpret_cast<float4 *>(o) = r;
-        } else {
-            const float t[4] = {r.x, r.y, r.z, r.w};
-            for (int q = 0; q < rem; ++q) o[q] = t[q];
+        float *orow = S.out + static_cast<int64_t>(i) * m.ld_out;
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            if (!act[q]) continue;
+            const int col = static_cast<int>(ch0 + q * G) * 4;
+            float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c > 0) {
+                const float fc = static_cast<float>(c);
+                r = make_float4(acc[q].x / fc, acc[q].y / fc, acc[q].z / fc, acc[q].w / fc);
+            }
+            const int rem = m.d - col;
+            if (rem >= 4) {
+                *reinterpret_cast<float4 *>(orow + col) = r;
+            } else {
+                const float t[4] = {r.x, r.y, r.z, r.w};
+                for (int w = 0; w < rem; ++w) orow[col + w] = t[w];
+            }
         }
     }
 }
@@ -192,7 +185,10 @@ hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t l
     const int vec = v4 ? 4 : 1;
     const int64_t cpr = (d + vec - 1) / vec;
     const int G = !v4 ? 1 : (cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64));
-    const int64_t slabs = v4 ? (cpr + G - 1) / G : cpr;   // items per destination
+    // chunk groups per lane in one item: G = 64 rows of up to 4 * 64 chunks take one item each
+    const int CH = !v4 || G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);
+    const int64_t slabs = v4 ? (cpr + CH * G - 1) / (CH * G) : cpr;   // items per destination
+    (void)max_c;
     for (int j0 = 0; j0 < njobs; j0 += kMaxMeanSegs) {
         MeanArgs m{};
         m.ld_src = ld_src;
@@ -215,16 +211,13 @@ hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t l
             continue;
         }
         const dim3 grid(grid_for(items, 4 * (64 / G), 8192));
-        const bool deep = max_c > 12;
-#define GNN_MEAN_LAUNCH(GG)                                                                   \
-    do {                                                                                      \
-        if (deep) hipLaunchKernelGGL((k_mean_v4<GG, 16, true>), grid, dim3(256), 0, s, m);    \
-        else hipLaunchKernelGGL((k_mean_v4<GG, 8, false>), grid, dim3(256), 0, s, m);         \
-    } while (0)
-        if (G == 16) GNN_MEAN_LAUNCH(16);
-        else if (G == 32) GNN_MEAN_LAUNCH(32);
-        else GNN_MEAN_LAUNCH(64);
-#undef GNN_MEAN_LAUNCH
+        constexpr int R = 4;
+        if (G == 16) hipLaunchKernelGGL((k_mean_v5<16, 1, R>), grid, dim3(256), 0, s, m);
+        else if (G == 32) hipLaunchKernelGGL((k_mean_v5<32, 1, R>), grid, dim3(256), 0, s, m);
+        else if (CH == 1) hipLaunchKernelGGL((k_mean_v5<64, 1, R>), grid, dim3(256), 0, s, m);
+        else if (CH == 2) hipLaunchKernelGGL((k_mean_v5<64, 2, R>), grid, dim3(256), 0, s, m);
+        else if (CH == 3) hipLaunchKernelGGL((k_mean_v5<64, 3, R>), grid, dim3(256), 0, s, m);
+        else hipLaunchKernelGGL((k_mean_v5<64, 4, R>), grid, dim3(256), 0, s, m);
     }
     return hipGetLastError();
 }

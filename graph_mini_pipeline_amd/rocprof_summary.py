@@ -24,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # Kernel name prefix -> the source file that defines it (its hash dates the counters).
 KERNEL_SOURCES = {
     "k_gather": "csrc/gather.hip",
-    "k_mean_v4": "csrc/aggregate.hip",
+    "k_mean_v5": "csrc/aggregate.hip",
     "k_mean_v1": "csrc/aggregate.hip",
     "k_sample": "csrc/sample.hip",
     "k_classify": "csrc/sample.hip",

@@ -226,7 +226,10 @@ def test_gather_out_of_range_reported():
     assert st.item() == gm.GNN_ERR_OUT_OF_RANGE
 
 
-@pytest.mark.parametrize("d,ld", [(602, 604), (7, 7), (128, 128)])
+# row widths covering every lane layout of the mean: 16 / 32 lanes per row, 64 lanes with 1-4
+# chunk groups per lane, several slabs per row (d > 1024), a ragged last chunk, a scalar path
+@pytest.mark.parametrize("d,ld", [(602, 604), (7, 7), (128, 128), (13, 16), (100, 100), (130, 132),
+                                  (300, 300), (700, 704), (1000, 1000), (1030, 1032), (2050, 2052)])
 def test_mean_standalone(d, ld):
     rng = np.random.default_rng(d + 1)
     n_src, n_dst = 500, 300
