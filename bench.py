@@ -38,15 +38,15 @@ def workload_name(cfg) -> str:
 
 
 def kernel_instance(kind: str, d: int, ld: int, fanout: int) -> str:
-    """Name of the template instance the library launches for this row shape: the gather moves
-    16-byte chunks when rows are 16-byte aligned; the mean picks lanes per destination (16, 32 or
-    64) and, with 64, chunk groups per lane (up to 4) from the 16-byte chunks per row, and keeps a
-    ring of 4 edges' loads in flight."""
-    if kind == "gather":
-        return "k_gather<4, 4>" if ld % 4 == 0 else "k_gather<1, 4>"
+    """Name of the template instance the library launches for this row shape: both kernels pick
+    lanes per row (16, 32 or 64) and, with 64, chunk groups per lane (up to 4) from the 16-byte
+    chunks per row, and keep a ring of rows (gather: 8 with 64 lanes, else 4) or edges (mean: 4)
+    in flight; a gather of rows that are not 16-byte aligned takes the flat per-element kernel."""
     cpr = (d + 3) // 4
     G = 16 if cpr <= 16 else (32 if cpr <= 32 else 64)
     CH = 1 if G < 64 else min(4, (cpr + 63) // 64)
+    if kind == "gather":
+        return f"k_gather_rows<{G}, {CH}, {8 if G == 64 else 4}>" if ld % 4 == 0 else "k_gather<1, 4>"
     return f"k_mean_v5<{G}, {CH}, 4>"
 
 

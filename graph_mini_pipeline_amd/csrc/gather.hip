@@ -6,11 +6,14 @@
 // Enabling Efficient Communication-Computation Pipeline for GNN via Hierarchical Caching,
 // Sec. 2.3 (GPU kernels read pinned host features directly, zero-copy).
 //
-// The (row, 16-byte chunk) pairs of the output are flattened and spread over all lanes, so
-// consecutive lanes read consecutive 16-byte chunks of a row and a wavefront moves 1 KiB per
-// instruction whatever the row length.  Each lane keeps U chunks in flight.  A row is read from
-// the HBM hot-row cache when slot[v] >= 0, else from the table (HBM, or pinned host memory through
-// its mapped device address).  HBM-bandwidth bound: no arithmetic.
+// Rows are copied by groups of G lanes (16, 32 or 64 by row length; with 64, a lane owns up to 4
+// of the row's 16-byte chunks), so consecutive lanes read consecutive chunks of a row.  A group
+// takes G consecutive output rows at a time: lane t loads id t (and its cache slot) once, the ids
+// are passed round with cross-lane reads, and the row loads run through a ring of R rows kept in
+// flight (a row's chunks are stored as its slot is refilled with the row R places later).  A row
+// is read from the HBM hot-row cache when slot[v] >= 0, else from the table (HBM, or pinned host
+// memory through its mapped device address).  Bandwidth bound: no arithmetic.  Rows that are not
+// 16-byte aligned take a flat (row, element) kernel.
 #include "common.hpp"
 
 namespace gnnmb {
@@ -96,6 +99,102 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
     }
 }
 
+template <int G, int CH, int R>
+__global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
+    const int lane = lane_id();
+    const int grp = lane / G;
+    const int gl = lane % G;
+    const int64_t n = load_count(g.d_n, g.n_cap);
+    const uint32_t cpr = g.cpr.d;
+    const uint32_t slabs = (cpr + CH * G - 1) / (CH * G);
+    const uint32_t units = static_cast<uint32_t>((n + G - 1) / G) * slabs;
+    const uint32_t g0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (64 / G) + grp;
+    const uint32_t gstride = gridDim.x * 4u * (64 / G);
+    uint32_t hits = 0;
+    for (uint32_t it = g0; it < units; it += gstride) {
+        const uint32_t rb = it / slabs;         // batch of G rows
+        const uint32_t p = it - rb * slabs;     // slab of the row
+        const int64_t r0 = static_cast<int64_t>(rb) * G;
+        const int nb = static_cast<int>(n - r0 < G ? n - r0 : G);
+        // lane t: id and source row base of output row r0 + t (NULL: invalid id)
+        const float *mine = nullptr;
+        if (gl < nb) {
+            const int32_t v = g.ids[r0 + gl];
+            if (v < 0 || v >= g.num_rows) {
+                set_status(g.status, GNN_ERR_OUT_OF_RANGE);
+            } else {
+                const int32_t sl = g.slot ? g.slot[v] : -1;
+                if (sl >= 0) {
+                    mine = g.cache + static_cast<int64_t>(sl) * g.ld;
+                    hits += p == 0;
+                } else {
+                    mine = g.table + static_cast<int64_t>(v) * g.ld;
+                }
+            }
+        }
+        const uint64_t mine_u = reinterpret_cast<uint64_t>(mine);
+        const uint32_t ch0 = p * CH * G + gl;
+        bool act[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) act[q] = ch0 + q * G < cpr;
+        auto row_of = [&](int r) -> const float * {
+            const int rr = r < nb ? r : 0;
+            uint64_t a;
+            if constexpr (G == 64) {
+                const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine_u), rr);
+                const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine_u >> 32), rr);
+                a = (static_cast<uint64_t>(hi) << 32) | lo;
+            } else {
+                a = __shfl(mine_u, grp * G + rr, 64);
+            }
+            return reinterpret_cast<const float *>(a);
+        };
+        f32x4 v[R][CH];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float *row = row_of(r);
+#pragma unroll
+            for (int q = 0; q < CH; ++q)
+                v[r][q] = (r < nb && row && act[q])
+                              ? *reinterpret_cast<const f32x4 *>(row + static_cast<int64_t>(ch0 + q * G) * 4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int e = 0; e < nb; e += R) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int er = e + r;
+                if (er < nb && row_of(er)) {
+                    float *o = g.out + (r0 + er) * g.ld_out;
+#pragma unroll
+                    for (int q = 0; q < CH; ++q) {
+                        if (!act[q]) continue;
+                        const int col = static_cast<int>(ch0 + q * G) * 4;
+                        const int rem = g.d - col;
+                        if (rem >= 4) {
+                            *reinterpret_cast<f32x4 *>(o + col) = v[r][q];
+                        } else {
+                            const float t[4] = {v[r][q][0], v[r][q][1], v[r][q][2], v[r][q][3]};
+                            for (int w = 0; w < rem; ++w) o[col + w] = t[w];
+                        }
+                    }
+                }
+                const int en = er + R;
+                const float *row = row_of(en);
+#pragma unroll
+                for (int q = 0; q < CH; ++q)
+                    v[r][q] = (en < nb && row && act[q])
+                                  ? *reinterpret_cast<const f32x4 *>(row + static_cast<int64_t>(ch0 + q * G) * 4)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
+    if (g.d_hits) {
+        hits = wave_sum(hits);
+        if (lane_id() == 0 && hits) atomicAdd(reinterpret_cast<unsigned long long *>(g.d_hits),
+                                              static_cast<unsigned long long>(hits));
+    }
+}
+
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
@@ -109,10 +208,26 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
     const int64_t cpr = (d + vec - 1) / vec;
     GatherArgs g{table, cache, slot, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
                  out, ld_out, d_hits, status, make_fastdiv(static_cast<uint32_t>(cpr))};
-    constexpr int U = 4;
-    const unsigned grid = grid_for(n_cap * cpr, 256 * U, 2048);
-    if (v4) hipLaunchKernelGGL((k_gather<4, U>), dim3(grid), dim3(256), 0, s, g);
-    else hipLaunchKernelGGL((k_gather<1, U>), dim3(grid), dim3(256), 0, s, g);
+    if (!v4) {
+        constexpr int U = 4;
+        hipLaunchKernelGGL((k_gather<1, U>), dim3(grid_for(n_cap * cpr, 256 * U, 2048)), dim3(256),
+                           0, s, g);
+        return hipGetLastError();
+    }
+    const int G = cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64);
+    const int CH = G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);
+    const int64_t slabs = (cpr + CH * G - 1) / (CH * G);
+    const int64_t units = (n_cap + G - 1) / G * slabs;
+    if (units > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const dim3 grid(grid_for(units, 4 * (64 / G), 8192));
+    // rows in flight per group: 8 with 64 lanes, 4 with 16 or 32 (measured best on 602-, 128-,
+    // 100- and 64-float rows)
+    if (G == 16) hipLaunchKernelGGL((k_gather_rows<16, 1, 4>), grid, dim3(256), 0, s, g);
+    else if (G == 32) hipLaunchKernelGGL((k_gather_rows<32, 1, 4>), grid, dim3(256), 0, s, g);
+    else if (CH == 1) hipLaunchKernelGGL((k_gather_rows<64, 1, 8>), grid, dim3(256), 0, s, g);
+    else if (CH == 2) hipLaunchKernelGGL((k_gather_rows<64, 2, 8>), grid, dim3(256), 0, s, g);
+    else if (CH == 3) hipLaunchKernelGGL((k_gather_rows<64, 3, 8>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_gather_rows<64, 4, 8>), grid, dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
