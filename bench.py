@@ -78,6 +78,9 @@ def main():
                     help="HIP streams the super-batches are issued on, round robin; each stream has "
                          "its own workspace and outputs, so one stream's sampling overlaps another's "
                          "gather and aggregation")
+    ap.add_argument("--pipeline-streams", type=int, default=3,
+                    help="streams of the extra pipelined-throughput region (0: skip it); the "
+                         "headline and the per-kernel timing use --streams")
     ap.add_argument("--superbatch", default="auto", choices=["auto", "full", "compact"],
                     help="super-batch relabel mode (identical results)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -139,20 +142,22 @@ def main():
     fs = gm.gnn_feature_store_create(table, cfg.d, cache_rows, hot_order)
     caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
     S = max(1, args.streams)
+    P = max(0, args.pipeline_streams)
+    SP = max(S, P)
     wss = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
-           for _ in range(S)]
-    streams = [torch.cuda.Stream(device=dev) for _ in range(S)] if S > 1 else [None]
-    outs = [{} for _ in range(S)]   # per stream: one output set per (position, seed count)
+           for _ in range(SP)]
+    streams = [None] + [torch.cuda.Stream(device=dev) for _ in range(SP - 1)]
+    outs = [{} for _ in range(SP)]   # per stream: one output set per (position, seed count)
 
     def batch_range(s):
         b0 = s * G
         return list(range(b0, min(b0 + G, n_batches)))
 
-    def step(st, timer=None):
-        """Super-batch st (mod the epoch) on stream st % S: its batches share one seed.
+    def step(st, timer=None, ns=S):
+        """Super-batch st (mod the epoch) on stream st % ns: its batches share one seed.
         Returns (super-batch index, [(b, n, out)])."""
         s = st % n_super
-        q = st % S
+        q = st % ns
         bs = batch_range(s)
         lo = bs[0] * cfg.batch
         hi = min(order.numel(), (bs[-1] + 1) * cfg.batch)
@@ -173,7 +178,7 @@ def main():
     for b in range(max(args.warmup, S)):
         step(b)
     torch.cuda.synchronize()
-    assert all(gm.gnn_read_device_status(w) == gm.GNN_OK for w in wss)
+    assert all(gm.gnn_read_device_status(w) == gm.GNN_OK for w in wss[:S])
 
     # Timed region 1: the headline throughput, nothing but the steps on the stream.
     torch.cuda.synchronize()
@@ -182,7 +187,7 @@ def main():
         step(b)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    status = min(gm.gnn_read_device_status(w) for w in wss)
+    status = min(gm.gnn_read_device_status(w) for w in wss[:S])
     progress(f"timed region: {steps} steps in {wall:.3f} s")
 
     # Timed region 2: the same steps with HIP events at the stage boundaries (the events cost a few
@@ -195,6 +200,22 @@ def main():
     torch.cuda.synchronize()
     wall_events = time.perf_counter() - t0
     stages = np.array(timer.elapsed(), dtype=np.float64)      # [steps, 4] ms
+
+    # Timed region 3 (not the headline): the same steps issued round robin on P streams, each
+    # with its own workspace and outputs, so one super-batch's sampling overlaps another's gather
+    # and aggregation.
+    wall_p = None
+    if P > 1:
+        for b in range(P):
+            step(b, ns=P)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for b in range(steps):
+            step(b, ns=P)
+        torch.cuda.synchronize()
+        wall_p = time.perf_counter() - t0
+        status = min(status, min(gm.gnn_read_device_status(w) for w in wss[:P]))
+        progress(f"pipelined region ({P} streams): {steps} steps in {wall_p:.3f} s")
 
     # Sizes of each timed batch: sampling is a pure function of the batch, so an untimed re-run
     # of the sampling gives the counts.
@@ -226,6 +247,7 @@ def main():
     mean_outer = np.array([m[K - 1] for m in mean_bytes], dtype=np.float64)
     mean_all = np.array([sum(m) for m in mean_bytes], dtype=np.float64)
 
+    n_minibatches = sum(len(batch_range(b % n_super)) for b in range(steps))
     t_sample, t_gather, t_mean_outer, t_mean_rest = (stages[:, i].sum() / 1e3 for i in range(4))
     kern = {
         "gather": (gb_bytes.sum() / t_gather / 1e9, t_gather / steps / G * 1e3),
@@ -258,7 +280,7 @@ def main():
         "config": {"workload": workload_name(cfg), "batches_per_epoch": n_batches,
                    "super_batch": G, "streams": S, "superbatch_relabel": args.superbatch,
                    "step": f"one super-batch of {G} mini-batch(es)"},
-        "ms_per_minibatch": wall / sum(len(batch_range(b % n_super)) for b in range(steps)) * 1e3,
+        "ms_per_minibatch": wall / n_minibatches * 1e3,
         "status": gm.gnn_status_string(status),
         "sampled_edges_per_s_sampling_stage": tot_edges / t_sample,
         "gathered_GBps": float(np.sum(payload) / t_gather / 1e9),
@@ -278,6 +300,12 @@ def main():
                          "algorithmic_bytes_per_launch": alg_per_launch[other],
                          "traffic": traffic[other]["bytes"] if traffic[other] else None},
         "ms_per_step_with_stage_events": wall_events / steps * 1e3,
+        "pipelined": None if wall_p is None else {
+            "streams": P, "value": tot_edges / wall_p, "unit": "sampled edges/s",
+            "ms_per_step": wall_p / steps * 1e3,
+            "ms_per_minibatch": wall_p / n_minibatches * 1e3,
+            "note": "same steps on several streams (not the headline; kernel timings above are "
+                    "single-stream)"},
         "input_generation_s": t_gen,
     }
 
