@@ -22,6 +22,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# Plain-ALU ceiling of the sampler's hashing: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12
+# lane-instructions/s (one wave64 VALU instruction per SIMD every 4 clocks), over the 21.5 VALU
+# instructions per key of the candidate loop (two SplitMix64 finalisers of 17 instructions each,
+# two 64-bit compares and the ballot/mask bookkeeping per two keys).
+ALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+VALU_PER_KEY = 21.5
+KEYS_PEAK = ALU_LANE_OPS / VALU_PER_KEY
 PRESAMPLE_BATCHES = 64     # batches pre-sampled to rank the hot-row cache (disjoint seeds)
 
 
@@ -143,21 +150,23 @@ def main():
     caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
     S = max(1, args.streams)
     P = max(0, args.pipeline_streams)
-    SP = max(S, P)
+    P = P if P > 1 else 0
+    # streams 0..S-1 (0: the default stream) time the headline and the kernels; the pipelined
+    # region has streams S..S+P-1 of its own, so a kernel trace separates the two by stream
     wss = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
-           for _ in range(SP)]
-    streams = [None] + [torch.cuda.Stream(device=dev) for _ in range(SP - 1)]
-    outs = [{} for _ in range(SP)]   # per stream: one output set per (position, seed count)
+           for _ in range(S + P)]
+    streams = [None] + [torch.cuda.Stream(device=dev) for _ in range(S + P - 1)]
+    outs = [{} for _ in range(S + P)]   # per stream: one output set per (position, seed count)
 
     def batch_range(s):
         b0 = s * G
         return list(range(b0, min(b0 + G, n_batches)))
 
-    def step(st, timer=None, ns=S):
-        """Super-batch st (mod the epoch) on stream st % ns: its batches share one seed.
+    def step(st, timer=None, first=0, ns=S):
+        """Super-batch st (mod the epoch) on stream first + st % ns: its batches share one seed.
         Returns (super-batch index, [(b, n, out)])."""
         s = st % n_super
-        q = st % ns
+        q = first + st % ns
         bs = batch_range(s)
         lo = bs[0] * cfg.batch
         hi = min(order.numel(), (bs[-1] + 1) * cfg.batch)
@@ -205,16 +214,16 @@ def main():
     # with its own workspace and outputs, so one super-batch's sampling overlaps another's gather
     # and aggregation.
     wall_p = None
-    if P > 1:
+    if P:
         for b in range(P):
-            step(b, ns=P)
+            step(b, first=S, ns=P)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for b in range(steps):
-            step(b, ns=P)
+            step(b, first=S, ns=P)
         torch.cuda.synchronize()
         wall_p = time.perf_counter() - t0
-        status = min(status, min(gm.gnn_read_device_status(w) for w in wss[:P]))
+        status = min(status, min(gm.gnn_read_device_status(w) for w in wss[S:]))
         progress(f"pipelined region ({P} streams): {steps} steps in {wall_p:.3f} s")
 
     # Sizes of each timed batch: sampling is a pure function of the batch, so an untimed re-run
@@ -225,9 +234,21 @@ def main():
     payload = []
     hits = torch.zeros(1, dtype=torch.int64, device=dev)
     rows_gathered = 0
+    keys = 0      # sampling keys hashed: over each hop's union frontier, the degrees above the fanout
+    deg = (graph.indptr[1:] - graph.indptr[:-1]).to(torch.int32)
     for b in range(steps):
         _, mine = step(b)
         torch.cuda.synchronize()
+        bs_ = batch_range(b % n_super)
+        for l in range(K):
+            if l == 0:   # the seeds of the super-batch
+                fr = [order[bs_[0] * cfg.batch:min(order.numel(), (bs_[-1] + 1) * cfg.batch)]]
+            else:        # each sub-batch's V_{l-1}
+                fr = [out.blocks.nodes[l - 1][:int(out.blocks.counts[2 * l - 1].item())]
+                      for _, _, out in mine]
+            u = torch.unique(torch.cat(fr).long())
+            dd = deg[u]
+            keys += int(dd[dd > cfg.fanouts[l]].sum().item())
         g_s, m_s, p_s = 0, [0] * K, 0
         for _, n, out in mine:
             if cache_rows:   # hits of this batch's gather: the same gather again, counting
@@ -248,7 +269,7 @@ def main():
     mean_all = np.array([sum(m) for m in mean_bytes], dtype=np.float64)
 
     n_minibatches = sum(len(batch_range(b % n_super)) for b in range(steps))
-    t_sample, t_gather, t_mean_outer, t_mean_rest = (stages[:, i].sum() / 1e3 for i in range(4))
+    t_sample, t_gather, t_mean_outer, t_mean_rest, t_hash = (stages[:, i].sum() / 1e3 for i in range(5))
     kern = {
         "gather": (gb_bytes.sum() / t_gather / 1e9, t_gather / steps / G * 1e3),
         "mean_outer": (mean_outer.sum() / t_mean_outer / 1e9, t_mean_outer / steps / G * 1e3),
@@ -288,13 +309,19 @@ def main():
         "stage_ms_per_step": {"sample_relabel": t_sample / steps * 1e3,
                               "gather": t_gather / steps * 1e3,
                               "mean_outer_block": t_mean_outer / steps * 1e3,
-                              "mean_other_blocks": t_mean_rest / steps * 1e3},
+                              "mean_other_blocks": t_mean_rest / steps * 1e3,
+                              "sampling_kernel_only": t_hash / steps * 1e3},
         "roofline": {"bound": "hbm", "kernel": names[dom],
                      "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBPS,
                      "traffic": traffic[dom]["bytes"] if traffic[dom] else None,
                      "algorithmic_bytes_per_launch": alg_per_launch[dom],
                      "avg_launch_ms": avg_ms, "launches_per_step": G},
+        "sampler": {"bound": "alu", "kernel": "k_sample", "achieved": keys / t_hash,
+                    "peak": KEYS_PEAK, "unit": "keys/s", "frac": keys / t_hash / KEYS_PEAK,
+                    "keys_per_step": keys / steps, "ms_per_step": t_hash / steps * 1e3,
+                    "peak_derivation": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz / 21.5 VALU "
+                                       "instructions per key"},
         "other_kernel": {"name": names[other], "achieved_GBps": kern[other][0],
                          "avg_launch_ms": kern[other][1],
                          "algorithmic_bytes_per_launch": alg_per_launch[other],

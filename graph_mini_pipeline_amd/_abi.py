@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "libgnnmb.so")
 
 GNN_MAX_HOPS = 8
 GNN_MAX_GROUP = 16
-GNN_TIMER_STAGES = 4
+GNN_TIMER_STAGES = 5
 GNN_SYNC = 1
 GNN_SUPERBATCH_FULL = 2
 GNN_SUPERBATCH_COMPACT = 4

@@ -20,14 +20,17 @@ struct gnn_feature_store {
 };
 
 // Events per record: call start, end of sampling, then per sub-batch the ends of its gather and
-// of its outermost-block mean, then the end of the call.
-constexpr int kTimerSlots = 3 + 2 * GNN_MAX_GROUP;
+// of its outermost-block mean, then the end of the call; then two per hop around the sampling
+// kernel (k_sample) of that hop.
+constexpr int kSampleEvents = 3 + 2 * GNN_MAX_GROUP;
+constexpr int kTimerSlots = kSampleEvents + 2 * GNN_MAX_HOPS;
 
 struct gnn_timer {
     int32_t n_records;
     int32_t cursor;
     std::vector<hipEvent_t> ev;   // n_records * kTimerSlots
     std::vector<int32_t> group;   // sub-batches of each recorded call
+    std::vector<int32_t> hops;    // hops of each recorded call
 };
 
 namespace {
@@ -319,7 +322,7 @@ template <typename FrontFn, typename CountFn, typename CapFn>
 gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, CapFn F_cap, int G,
                               int32_t k, uint64_t hs, int l, const gnn_caps &mc,
                               gnn_blocks *const *outs, const Workspace &w, const Opts &o,
-                              hipStream_t s) {
+                              hipStream_t s, hipEvent_t *sev) {
     const int64_t Ucap = union_cap(mc, l, G, g.num_nodes);
     const int64_t uEcap = Ucap * k;
     RelabelArgs ru = relabel_args(g, w);
@@ -331,7 +334,9 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
     h.clear_ptr = w.bitmaps + w.W;  // the sub-batch bitmaps, zeroed before their relabel
     h.clear_n = static_cast<int64_t>(G) * w.W;
     GNN_TRY_HIP(launch_classify(h, s));
+    if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
     GNN_TRY_HIP(launch_sample(h, s));
+    if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l + 1], s));
     DistArgs da{};
     da.G = G;
     int32_t tiles = 0;
@@ -380,7 +385,8 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
 // per hop and every sub-batch relabels in positions of U_{l+1}.  Full relabel: run_super_full_hop.
 gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const int64_t *n_seeds_g,
                       int G, const int32_t *fanouts, int32_t K, uint64_t seed64,
-                      gnn_blocks *const *outs, const Workspace &w, const Opts &o, hipStream_t s) {
+                      gnn_blocks *const *outs, const Workspace &w, const Opts &o, hipStream_t s,
+                      hipEvent_t *sev = nullptr) {
     gnn_caps mc = outs[0]->caps;
     for (int gi = 1; gi < G; ++gi) {
         for (int l = 0; l < K; ++l) {
@@ -417,7 +423,9 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
             h.clear_ptr = w.bitmaps;
             h.clear_n = w.W;
             GNN_TRY_HIP(launch_classify(h, s));
+            if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
             GNN_TRY_HIP(launch_sample(h, s));
+            if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l + 1], s));
             RelabelArgs r = relabel_args(g, w);
             r.nlist = 2;
             r.list[0] = IdList{front(0, l), d_F(0, l), F_cap(0, l), out.hop[l].dst_lid, 0, l == 0 ? 1 : 0};
@@ -428,7 +436,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         }
         if (!compact) {
             const gnn_status st = run_super_full_hop(g, front, d_F, F_cap, G, fanouts[l], hs, l, mc,
-                                                     outs, w, o, s);
+                                                     outs, w, o, s, sev);
             if (st != GNN_OK) return st;
             continue;
         }
@@ -441,7 +449,9 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         HopArgs h = hop_args(g, Ul, w.d_U + l, Ucap, fanouts[l], hs, w.u_indptr, w.u_gid, uEcap,
                              w.d_uE + l, w, o);
         GNN_TRY_HIP(launch_classify(h, s));
+        if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
         GNN_TRY_HIP(launch_sample(h, s));
+        if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l + 1], s));
         // U_{l+1} = U_l + the sampled ids: mark the ids into the accumulated node-id bitmap, rank
         // both lists in the result.
         RelabelArgs ru = relabel_args(g, w);
@@ -759,12 +769,14 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         if (timer->cursor >= timer->n_records) return GNN_ERR_CAPACITY;
         ev = timer->ev.data() + static_cast<size_t>(timer->cursor) * kTimerSlots;
         timer->group[timer->cursor] = group;
+        timer->hops[timer->cursor] = K;
         timer->cursor += 1;
         GNN_TRY_HIP(hipEventRecord(ev[0], s));
     }
     GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
     // Stage 1: sampling and relabel of every sub-batch (one shared seed64).
-    st = run_sample(*g, sp, nsg, group, fanouts, K, seed64, ob, w, o, s);
+    st = run_sample(*g, sp, nsg, group, fanouts, K, seed64, ob, w, o, s,
+                    ev ? ev + kSampleEvents : nullptr);
     if (st != GNN_OK) return st;
     if (ev) GNN_TRY_HIP(hipEventRecord(ev[1], s));
     // Stages 2 and 3, per sub-batch: gather X = rows of V_K, then the outermost block's mean,
@@ -817,6 +829,7 @@ gnn_status gnn_timer_create(int32_t n_records, gnn_timer **out) {
     t->cursor = 0;
     t->ev.assign(static_cast<size_t>(n_records) * kTimerSlots, nullptr);
     t->group.assign(static_cast<size_t>(n_records), 0);
+    t->hops.assign(static_cast<size_t>(n_records), 0);
     for (auto &e : t->ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             gnn_timer_destroy(t);
@@ -863,6 +876,12 @@ gnn_status gnn_timer_elapsed(gnn_timer *t, int32_t *n_records, float *ms) {
         ms[r * GNN_TIMER_STAGES + 2] = outer;
         GNN_TRY_HIP(hipEventElapsedTime(&v, e[1 + 2 * G], e[2 + 2 * G]));
         ms[r * GNN_TIMER_STAGES + 3] = v;
+        float smp = 0.f;
+        for (int l = 0; l < t->hops[r]; ++l) {
+            GNN_TRY_HIP(hipEventElapsedTime(&v, e[kSampleEvents + 2 * l], e[kSampleEvents + 2 * l + 1]));
+            smp += v;
+        }
+        ms[r * GNN_TIMER_STAGES + 4] = smp;
     }
     return GNN_OK;
 }

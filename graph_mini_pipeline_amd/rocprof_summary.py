@@ -1,7 +1,7 @@
 """Short text summaries of rocprofv3 output for the profiles/ folder, and the reader that turns a
 counter summary into per-launch memory traffic.
 
-    python -m graph_mini_pipeline_amd.rocprof_summary trace OUT.txt STATS.csv "COMMAND"
+    python -m graph_mini_pipeline_amd.rocprof_summary trace OUT.txt KERNEL_TRACE.csv "COMMAND"
     python -m graph_mini_pipeline_amd.rocprof_summary counters OUT.txt WORKLOAD FETCH.csv WRITE.csv "COMMAND"
 
 Counter summaries hold one machine-readable line per kernel:
@@ -55,16 +55,27 @@ def source_hash(rel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def trace_summary(stats_csv: str, command: str) -> str:
-    rows = list(csv.DictReader(open(stats_csv)))
-    out = [f"# rocprofv3 --kernel-trace --stats summary (library kernels only)",
+def trace_summary(trace_csv: str, command: str) -> str:
+    """Per-kernel duration statistics of the library's dispatches on the stream of its first
+    dispatch (the stream the benchmark's headline and per-kernel timings run on; dispatches on
+    other streams, such as a pipelined region's, overlap one another and are left out)."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "gnnmb" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    stream = rows[0]["Stream_Id"] if rows else None
+    per = defaultdict(list)
+    others = 0
+    for r in rows:
+        if r["Stream_Id"] != stream:
+            others += 1
+            continue
+        per[short_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = [f"# rocprofv3 --kernel-trace summary (library kernels on stream {stream}, the stream of "
+           f"the first library dispatch; {others} dispatches on other streams left out)",
            f"# command: {command}",
            f"# {'kernel':44s} {'calls':>7s} {'total_ms':>10s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
-    for r in rows:
-        if "gnnmb" not in r["Name"]:
-            continue
-        out.append(f"{short_name(r['Name']):46s} {int(r['Calls']):7d} {float(r['TotalDurationNs']) / 1e6:10.3f} "
-                   f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"{name:46s} {len(d):7d} {sum(d) / 1e6:10.3f} {sum(d) / len(d) / 1e3:9.2f} "
+                   f"{min(d) / 1e3:9.2f} {max(d) / 1e3:9.2f}")
     return "\n".join(out) + "\n"
 
 
@@ -136,8 +147,8 @@ def read_traffic(path: str, kernel: str, grid_free: bool = True) -> Optional[dic
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "trace":
-        out, stats, cmd = sys.argv[2:5]
-        text = trace_summary(stats, cmd)
+        out, trace, cmd = sys.argv[2:5]
+        text = trace_summary(trace, cmd)
     elif mode == "counters":
         out, workload, fcsv, wcsv, cmd = sys.argv[2:7]
         text = counter_summary(workload, fcsv, wcsv, cmd)

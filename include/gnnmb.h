@@ -265,13 +265,14 @@ gnn_status gnn_read_device_status(const void *ws, gnn_stream stream, gnn_status 
  * Stage timer (HIP events recorded on the call's stream).  A gnn_minibatch call given a timer
  * records one record: events at the call start, at the end of sampling and relabel (all hops),
  * after each sub-batch's feature gather and after its outermost-block mean (these two kernels run
- * back to back per sub-batch), and at the end of the call.  gnn_timer_elapsed synchronises on the
- * recorded events and writes GNN_TIMER_STAGES durations in milliseconds per record to ms (host
- * [n_records*GNN_TIMER_STAGES]): sampling+relabel, the gather kernels (summed over sub-batches),
- * the outermost-block mean kernels (summed), and the remaining mean blocks.  gnn_timer_reset
- * rewinds to record 0.  Each event costs a few microseconds of stream time.
+ * back to back per sub-batch), at the end of the call, and around each hop's sampling kernel.
+ * gnn_timer_elapsed synchronises on the recorded events and writes GNN_TIMER_STAGES durations in
+ * milliseconds per record to ms (host [n_records*GNN_TIMER_STAGES]): sampling+relabel, the
+ * gather kernels (summed over sub-batches), the outermost-block mean kernels (summed), the
+ * remaining mean blocks, and the sampling kernels alone (summed over hops; part of the first).
+ * gnn_timer_reset rewinds to record 0.  Each event costs a few microseconds of stream time.
  */
-#define GNN_TIMER_STAGES 4
+#define GNN_TIMER_STAGES 5
 gnn_status gnn_timer_create(int32_t n_records, gnn_timer **out);
 gnn_status gnn_timer_destroy(gnn_timer *t);
 gnn_status gnn_timer_reset(gnn_timer *t);

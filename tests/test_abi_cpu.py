@@ -164,3 +164,13 @@ def test_validation_before_device_work():
     # feature store: ld < d
     assert L.gnn_feature_store_create(8, 0, 10, 8, 4, 0, None,
                                       ctypes.byref(t)) == gm.GNN_ERR_INVALID_ARG
+
+
+def test_header_constants_match_binding():
+    import re
+    text = open(os.path.join(ROOT, "include", "gnnmb.h")).read()
+    consts = {m.group(1): int(m.group(2)) for m in
+              re.finditer(r"#define\s+(GNN_[A-Z0-9_]+)\s+\(?(-?\d+)u?\)?", text)}
+    assert consts, "no constants found"
+    for name, value in consts.items():
+        assert getattr(_abi, name) == value, name
