@@ -177,9 +177,7 @@ struct BitmapOut {
 struct RelabelArgs {
     IdList list[2 * kMaxGroup];
     int32_t nlist;
-    int64_t list_off[2 * kMaxGroup + 1];  // filled by launch_relabel
     BitmapOut out[kMaxGroup];
-    int64_t out_off[kMaxGroup + 1];       // filled by launch_relabel
     int32_t nbm;              // bitmaps (one per BitmapOut)
     int64_t id_bound;
     const int64_t *d_bound;   // optional device bound on the ids (at most id_bound); bitmap words

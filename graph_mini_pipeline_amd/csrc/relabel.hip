@@ -47,26 +47,58 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s) 
     return hipGetLastError();
 }
 
-// List of flattened thread index t: the last list whose offset is <= t.
-__device__ __forceinline__ int find_list(const RelabelArgs &a, int64_t t) {
-    int l = 0;
-    while (l + 1 < a.nlist && a.list_off[l + 1] <= t) ++l;
-    return l;
+// Marks the ids of the lists of the given pass.  In pass 1 (the seed lists, marked before
+// anything else) an id whose bit is already set is a duplicate within that list's bitmap.  The
+// whole grid walks each list up to its actual (device) length, list after list: capacities can
+// be many times the actual lengths.
+// The lists' actual lengths (then the outputs' sizes), read once per workgroup with one load
+// per list in flight, and their exclusive prefix: items of the lists are numbered 0 .. total-1
+// in list order, so the grid spreads over the actual items of all lists at once.
+__device__ __forceinline__ void list_lengths(const RelabelArgs &a, int64_t *s_len, int64_t *s_off) {
+    const int nl = a.nlist + a.nbm;
+    if (threadIdx.x < static_cast<unsigned>(a.nlist))
+        s_len[threadIdx.x] = load_count(a.list[threadIdx.x].d_n, a.list[threadIdx.x].cap);
+    else if (threadIdx.x < static_cast<unsigned>(nl))
+        s_len[threadIdx.x] = load_count(a.out[threadIdx.x - a.nlist].d_uniq,
+                                        a.out[threadIdx.x - a.nlist].uniq_cap);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t run = 0;
+        for (int l = 0; l < nl; ++l) {
+            s_off[l] = run;
+            run += s_len[l];
+        }
+        s_off[nl] = run;
+    }
+    __syncthreads();
+}
+
+// The list (among the first n of them) holding item t: the last l with s_off[l] <= t.
+__device__ __forceinline__ int item_list(const int64_t *s_off, int n, int64_t t) {
+    int lo = 0, hi = n;  // s_off[lo] <= t < s_off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    return lo;
 }
 
 // Marks the ids of the lists of the given pass.  In pass 1 (the seed lists, marked before
 // anything else) an id whose bit is already set is a duplicate within that list's bitmap.
+// Only the lists' actual items are visited (capacities can be many times the actual lengths).
 __global__ __launch_bounds__(256) void k_mark(RelabelArgs a, int32_t pass) {
-    const int64_t total = a.list_off[a.nlist];
+    __shared__ int64_t s_len[3 * kMaxGroup];
+    __shared__ int64_t s_off[3 * kMaxGroup + 1];
+    list_lengths(a, s_len, s_off);
     const int64_t bound = relabel_bound(a);
+    const int64_t total = s_off[a.nlist];
     for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
          t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int l = find_list(a, t);
+        const int l = item_list(s_off, a.nlist, t);
         const IdList &L = a.list[l];
         if (L.pass != pass) continue;
-        const int64_t i = t - a.list_off[l];
-        if (i >= load_count(L.d_n, L.cap)) continue;
-        const int32_t v = L.ids[i];
+        const int32_t v = L.ids[t - s_off[l]];
         if (v < 0 || v >= bound) {
             set_status(a.status, GNN_ERR_OUT_OF_RANGE);
             continue;
@@ -220,29 +252,28 @@ __global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a, int32_t 
 
 // Ranks of every list that asks for them, in its bitmap's unique list; with an id map, also
 // replaces each emitted position by its id (a separate pass keeps the dependent loads out of the
-// emit loop, which writes one set bit after another).
+// emit loop, which writes one set bit after another).  The grid spreads over the actual items of
+// the lists (and outputs), numbered in list order.
 __global__ __launch_bounds__(256) void k_rank(RelabelArgs a) {
-    const int64_t total = a.list_off[a.nlist];
-    const int64_t all = total + (a.id_map ? a.out_off[a.nbm] : 0);
+    __shared__ int64_t s_len[3 * kMaxGroup];
+    __shared__ int64_t s_off[3 * kMaxGroup + 1];
+    list_lengths(a, s_len, s_off);
     const int64_t bound = relabel_bound(a);
-    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < all;
+    // items: the lists' ids, then (with an id map) the outputs' positions
+    const int nl = a.id_map ? a.nlist + a.nbm : a.nlist;
+    const int64_t total = s_off[nl];
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
          t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        if (t >= total) {
-            int b = 0;
-            while (b + 1 < a.nbm && a.out_off[b + 1] <= t - total) ++b;
-            const BitmapOut &o = a.out[b];
-            const int64_t i = t - total - a.out_off[b];
-            if (i < load_count(o.d_uniq, o.uniq_cap)) {
-                const int32_t p = o.uniq[i];
-                o.uniq[i] = p >= 0 && p < bound ? a.id_map[p] : -1;
-            }
+        const int l = item_list(s_off, nl, t);
+        const int64_t i = t - s_off[l];
+        if (l >= a.nlist) {
+            const BitmapOut &o = a.out[l - a.nlist];
+            const int32_t p = o.uniq[i];
+            o.uniq[i] = p >= 0 && p < bound ? a.id_map[p] : -1;
             continue;
         }
-        const int l = find_list(a, t);
         const IdList &L = a.list[l];
         if (L.lid == nullptr) continue;
-        const int64_t i = t - a.list_off[l];
-        if (i >= load_count(L.d_n, L.cap)) continue;
         const int32_t v = L.ids[i];
         int32_t r = -1;
         if (v >= 0 && v < bound) {
@@ -260,18 +291,12 @@ hipError_t launch_relabel(RelabelArgs a, hipStream_t s) {
     int64_t total = 0;
     bool any_rank = false, any_pass1 = false;
     for (int l = 0; l < a.nlist; ++l) {
-        a.list_off[l] = total;
         total += a.list[l].cap;
         any_rank |= a.list[l].lid != nullptr;
         any_pass1 |= a.list[l].pass == 1;
     }
-    a.list_off[a.nlist] = total;
     int64_t outs = 0;
-    for (int b = 0; b < a.nbm; ++b) {
-        a.out_off[b] = outs;
-        outs += a.out[b].uniq_cap;
-    }
-    a.out_off[a.nbm] = outs;
+    for (int b = 0; b < a.nbm; ++b) outs += a.out[b].uniq_cap;
     if (!a.bitmap_cleared) {
         hipError_t e = launch_fill_u32(a.bitmap, static_cast<int64_t>(a.nbm) * a.W, 0u, s);
         if (e != hipSuccess) return e;
@@ -287,8 +312,7 @@ hipError_t launch_relabel(RelabelArgs a, hipStream_t s) {
     hipLaunchKernelGGL(k_emit, dim3(a.nbm * a.nbw), dim3(kBitmapThreads), 0, s, a, pre);
     const int64_t rank_items = (any_rank ? total : 0) + (a.id_map ? outs : 0);
     if (rank_items > 0)
-        hipLaunchKernelGGL(k_rank, dim3(grid_for(total + (a.id_map ? outs : 0), 256, 4096)),
-                           dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_rank, dim3(grid_for(rank_items, 256, 4096)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

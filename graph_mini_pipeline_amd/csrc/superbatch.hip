@@ -98,8 +98,11 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
     const DistSub &S = a.sub[find_sub(a, t)];
     const int lt = t - S.tile0;
     const int64_t F = load_count(S.d_F, S.F_cap);
+    // tiles past the actual destinations have nothing to place (tile 0 still writes the totals)
+    const int live = static_cast<int>((F + kDistTile - 1) / kDistTile);
+    if (lt > 0 && lt >= live) return;
     uint32_t before = 0, all = 0;
-    for (int b = threadIdx.x; b < S.ntile; b += blockDim.x) {
+    for (int b = threadIdx.x; b < live; b += blockDim.x) {
         const uint32_t x = a.bsum[S.tile0 + b];
         all += x;
         if (b < lt) before += x;
