@@ -70,6 +70,7 @@ struct Workspace {
                            // relabel) or G of Wc words (compact super-batch relabel)
     uint32_t *wprefix;     // same layout
     uint32_t *bsum_w;      // [nbw], then G * nbw or G * nbwc
+    uint8_t *bytemaps;     // super-batch: byte maps of the G sub-batch bitmaps (or NULL)
     // super-batch only (the union; the rest: compact relabel only)
     int32_t *U[2];         // U_l, ping-pong by hop parity (full relabel: one buffer)
     int32_t *u_indptr;     // union block
@@ -136,6 +137,9 @@ SuperMode super_mode(const gnn_caps &mc, int64_t N, int G, uint32_t flags) {
     return 3 * static_cast<int64_t>(G + 1) * W >= max_union_edges(mc, N, G) ? kSuperCompact : kSuperFull;
 }
 
+// Largest byte-map region of a super-batch's sub-batch relabels (beyond it, marks stay atomic).
+constexpr int64_t kByteMapsMax = 1LL << 30;
+
 // mc: element-wise bound of every sub-batch's caps; G sub-batches relabelled the given way.
 Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) {
     Workspace w{};
@@ -180,6 +184,10 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
     w.wprefix = c.take<uint32_t>(words);
     w.bsum_w = c.take<uint32_t>(tiles);
     if (mode != kSuperNone) {
+        // byte maps of the sub-batch relabels: marks become plain byte stores
+        const int64_t wx = mode == kSuperFull ? w.W : w.Wc;
+        const int64_t nbytes = static_cast<int64_t>(G) * wx * 32;
+        if (nbytes <= kByteMapsMax) w.bytemaps = reinterpret_cast<uint8_t *>(c.take<uint32_t>(nbytes / 4));
         w.U[0] = c.take<int32_t>(U_max);
         w.U[1] = mode == kSuperCompact ? c.take<int32_t>(U_max) : w.U[0];
         w.u_indptr = c.take<int32_t>(FU + 1);
@@ -331,8 +339,16 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
     ru.out[0] = BitmapOut{w.U[0], Ucap, w.d_U, nullptr};
     GNN_TRY_HIP(launch_relabel(ru, s));
     HopArgs h = hop_args(g, w.U[0], w.d_U, Ucap, k, hs, w.u_indptr, w.u_gid, uEcap, w.d_uE, w, o);
-    h.clear_ptr = w.bitmaps + w.W;  // the sub-batch bitmaps, zeroed before their relabel
-    h.clear_n = static_cast<int64_t>(G) * w.W;
+    if (w.bytemaps) {
+        // the sub-batch byte maps are zeroed before their relabel; the bitmaps are rewritten
+        // whole from them, except that the seeds' duplicate check needs clean bitmaps at hop 0
+        h.clear_ptr = reinterpret_cast<uint32_t *>(w.bytemaps);
+        h.clear_n = static_cast<int64_t>(G) * w.W * 8;
+        if (l == 0) GNN_TRY_HIP(launch_fill_u32(w.bitmaps + w.W, static_cast<int64_t>(G) * w.W, 0u, s));
+    } else {
+        h.clear_ptr = w.bitmaps + w.W;  // the sub-batch bitmaps, zeroed before their relabel
+        h.clear_n = static_cast<int64_t>(G) * w.W;
+    }
     GNN_TRY_HIP(launch_classify(h, s));
     if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
     GNN_TRY_HIP(launch_sample(h, s));
@@ -362,6 +378,7 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
     GNN_TRY_HIP(launch_dist(da, s));
     // Per-sub-batch relabel into bitmaps 1..G; the union bitmap is zeroed for the next hop.
     RelabelArgs rs = relabel_args(g, w, 1, G);
+    rs.bytes = w.bytemaps;
     rs.nlist = 2 * G;
     for (int gi = 0; gi < G; ++gi) {
         gnn_blocks &out = *outs[gi];
@@ -482,6 +499,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         da.d_U = w.d_U + l;
         da.U_cap = Ucap;
         da.clear_ptr = w.bitmaps + w.W;
+        da.clear_bytes = reinterpret_cast<uint32_t *>(w.bytemaps);
         da.clear_stride = w.Wc;
         da.d_U1 = w.d_U + l + 1;
         da.U1_cap = U1cap;
@@ -490,6 +508,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         GNN_TRY_HIP(launch_dist(da, s));
         // Per-sub-batch relabel in U_{l+1} positions; the positions of V_l become the next hop's.
         RelabelArgs rs = compact_relabel_args(w, G, Ul1, w.d_U + l + 1, U1cap);
+        rs.bytes = w.bytemaps;
         rs.nlist = 2 * G;
         for (int gi = 0; gi < G; ++gi) {
             gnn_blocks &out = *outs[gi];

@@ -183,6 +183,8 @@ struct RelabelArgs {
     const int64_t *d_bound;   // optional device bound on the ids (at most id_bound); bitmap words
                               // at or past it are ignored, whatever they hold
     const int32_t *id_map;    // optional: bit position p stands for id id_map[p] in uniq
+    uint8_t *bytes;           // optional [nbm * W * 32], zero: lists of pass 0 set byte[id] = 1
+                              // (plain stores) and the popcount pass packs bytes into the bitmap
     uint32_t *bitmap;         // [nbm * W]
     uint32_t *wprefix;        // [nbm * W]
     uint32_t *bsum;           // [nbm * nbw]
@@ -236,6 +238,8 @@ struct DistArgs {
     int64_t U_cap;
     uint32_t *clear_ptr;       // optional: G sub-batch bitmaps of stride clear_stride words,
     int64_t clear_stride;      // zeroed up to ceil(|U_{l+1}| / 32) words each
+    uint32_t *clear_bytes;     // optional: their byte maps (stride 8 clear_stride words), zeroed
+                               // over the same live words
     const int64_t *d_U1;       // |U_{l+1}|
     int64_t U1_cap;
     uint32_t *bsum;            // [ntiles]

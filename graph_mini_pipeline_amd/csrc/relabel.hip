@@ -105,10 +105,11 @@ __global__ __launch_bounds__(256) void k_mark(RelabelArgs a, int32_t pass) {
         }
         const uint32_t bit = 1u << (v & 31);
         uint32_t *word = &a.bitmap[static_cast<int64_t>(L.bitmap) * a.W + (v >> 5)];
+        if (a.bytes) a.bytes[static_cast<int64_t>(L.bitmap) * a.W * 32 + v] = 1;  // idempotent
         if (pass == 1) {
             const uint32_t old = atomicOr(word, bit);
             if (old & bit) set_status(a.status, GNN_ERR_INVALID_ARG);
-        } else {
+        } else if (!a.bytes) {
             atomicOr(word, bit);  // result unused: the atomic is posted, the lane does not wait
         }
     }
@@ -135,9 +136,29 @@ __global__ __launch_bounds__(kBitmapThreads) void k_popc_tiles(RelabelArgs a) {
                        static_cast<int64_t>(threadIdx.x) * kBitmapWordsPerThread;
     const int64_t Wl = live_words(a);
     uint32_t c = 0;
+    if (a.bytes) {
+        // word w = the 32 bytes of ids 32w .. 32w+31 (each 0 or 1), packed
+        uint32_t *wout = a.bitmap + static_cast<int64_t>(bm) * a.W;
+        const uint8_t *bytes = a.bytes + static_cast<int64_t>(bm) * a.W * 32;
 #pragma unroll
-    for (int q = 0; q < kBitmapWordsPerThread; ++q)
-        if (w0 + q < Wl) c += __popc(words[w0 + q]);
+        for (int q = 0; q < kBitmapWordsPerThread; ++q) {
+            const int64_t w = w0 + q;
+            if (w >= Wl) break;
+            const uint4 *p = reinterpret_cast<const uint4 *>(bytes + w * 32);
+            const uint4 lo = p[0], hi = p[1];
+            const uint32_t x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            uint32_t word = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)   // 4 bytes (0/1) -> 4 bits: products land on distinct bits
+                word |= ((((x[k] & 0x01010101u) * 0x00204081u) >> 21) & 0xFu) << (4 * k);
+            wout[w] = word;
+            c += __popc(word);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kBitmapWordsPerThread; ++q)
+            if (w0 + q < Wl) c += __popc(words[w0 + q]);
+    }
     c = wave_sum(c);
     if (lane_id() == 0) red[threadIdx.x >> 6] = c;
     __syncthreads();

@@ -73,6 +73,14 @@ __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
             const int64_t g = t / words;
             a.clear_ptr[g * a.clear_stride + (t - g * words)] = 0u;
         }
+        if (a.clear_bytes) {   // 8 words of bytes per bitmap word
+            const int64_t bw = 8 * words;
+            for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < bw * a.G;
+                 t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+                const int64_t g = t / bw;
+                a.clear_bytes[g * 8 * a.clear_stride + (t - g * bw)] = 0u;
+            }
+        }
     }
     if (threadIdx.x >= kDistTile) return;
     const int t = blockIdx.x;
