@@ -44,17 +44,28 @@ def workload_name(cfg) -> str:
             (f"; epoch of {cfg.n_train} training seeds" if cfg.n_train else ""))
 
 
-def kernel_instance(kind: str, d: int, ld: int, fanout: int) -> str:
+def kernel_instance(kind: str, d: int, ld: int, batched: bool) -> str:
     """Name of the template instance the library launches for this row shape: both kernels pick
     lanes per row (16, 32 or 64) and, with 64, chunk groups per lane (up to 4) from the 16-byte
     chunks per row, and keep a ring of rows (gather: 8 with 64 lanes, else 4) or edges (mean: 4)
-    in flight; a gather of rows that are not 16-byte aligned takes the flat per-element kernel."""
+    in flight; a gather of rows that are not 16-byte aligned takes the flat per-element kernel.
+    Batched, one gather launch serves every sub-batch (k_gather_batch)."""
     cpr = (d + 3) // 4
     G = 16 if cpr <= 16 else (32 if cpr <= 32 else 64)
     CH = 1 if G < 64 else min(4, (cpr + 63) // 64)
     if kind == "gather":
-        return f"k_gather_rows<{G}, {CH}, {8 if G == 64 else 4}>" if ld % 4 == 0 else "k_gather<1, 4>"
+        if ld % 4:
+            return "k_gather<1, 4>"
+        return f"{'k_gather_batch' if batched else 'k_gather_rows'}<{G}, {CH}, {8 if G == 64 else 4}>"
     return f"k_mean_v5<{G}, {CH}, 4>"
+
+
+def batched_gather(cfg, layout: str) -> bool:
+    """The library's gather layout: batched for a host-resident table or rows of more than 128
+    floats unless forced either way."""
+    if layout != "auto":
+        return layout == "batched"
+    return bool(cfg.host_features) or cfg.d > 128
 
 
 def algorithmic_bytes(counts, n_seeds, d, K):
@@ -90,6 +101,8 @@ def main():
                          "headline and the per-kernel timing use --streams")
     ap.add_argument("--superbatch", default="auto", choices=["auto", "full", "compact"],
                     help="super-batch relabel mode (identical results)")
+    ap.add_argument("--gather", default="auto", choices=["auto", "interleaved", "batched"],
+                    help="gather / outermost-mean launch layout (identical results)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -179,7 +192,7 @@ def main():
                                                   cfg.d, cfg.ld)
             mine.append((b, n, outs[q][(j, n)]))
         gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, gm.gnn_batch_seed(cfg.rng_seed, s),
-                         [m[2] for m in mine], wss[q], gm.Options(superbatch=args.superbatch),
+                         [m[2] for m in mine], wss[q], gm.Options(superbatch=args.superbatch, gather=args.gather),
                          timer=timer, stream=streams[q])
         return s, mine
 
@@ -269,21 +282,24 @@ def main():
     mean_all = np.array([sum(m) for m in mean_bytes], dtype=np.float64)
 
     n_minibatches = sum(len(batch_range(b % n_super)) for b in range(steps))
+    batched = batched_gather(cfg, args.gather)
+    launches = 1 if batched else G      # gather (and outermost-mean) launches per step
     t_sample, t_gather, t_mean_outer, t_mean_rest, t_hash = (stages[:, i].sum() / 1e3 for i in range(5))
     kern = {
-        "gather": (gb_bytes.sum() / t_gather / 1e9, t_gather / steps / G * 1e3),
-        "mean_outer": (mean_outer.sum() / t_mean_outer / 1e9, t_mean_outer / steps / G * 1e3),
+        "gather": (gb_bytes.sum() / t_gather / 1e9, t_gather / steps / launches * 1e3),
+        "mean_outer": (mean_outer.sum() / t_mean_outer / 1e9, t_mean_outer / steps / launches * 1e3),
     }
     dom = "gather" if t_gather >= t_mean_outer else "mean_outer"
     ach, avg_ms = kern[dom]
     ga_frac = (gb_bytes.sum() + mean_all.sum()) / (t_gather + t_mean_outer + t_mean_rest) / 1e9 / HBM_PEAK_GBPS
-    names = {"gather": kernel_instance("gather", cfg.d, cfg.ld, cfg.fanouts[-1]),
-             "mean_outer": kernel_instance("mean", cfg.d, cfg.ld, cfg.fanouts[-1])}
+    names = {"gather": kernel_instance("gather", cfg.d, cfg.ld, batched),
+             "mean_outer": kernel_instance("mean", cfg.d, cfg.ld, batched)}
     other = "mean_outer" if dom == "gather" else "gather"
     from graph_mini_pipeline_amd.rocprof_summary import read_traffic
     counters = os.path.join(ROOT, "profiles", f"{cfg.name}_counters.txt")
     traffic = {k: read_traffic(counters, names[k]) for k in names}
-    alg_per_launch = {"gather": gb_bytes.sum() / steps / G, "mean_outer": mean_outer.sum() / steps / G}
+    alg_per_launch = {"gather": gb_bytes.sum() / steps / launches,
+                      "mean_outer": mean_outer.sum() / steps / launches}
 
     result = {
         "metric": "sampled edges/s + gathered feature GB/s per mini-batch; % of HBM peak",
@@ -300,6 +316,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name(cfg), "batches_per_epoch": n_batches,
                    "super_batch": G, "streams": S, "superbatch_relabel": args.superbatch,
+                   "gather_layout": args.gather,
                    "step": f"one super-batch of {G} mini-batch(es)"},
         "ms_per_minibatch": wall / n_minibatches * 1e3,
         "status": gm.gnn_status_string(status),
@@ -316,14 +333,14 @@ def main():
                      "frac": ach / HBM_PEAK_GBPS,
                      "traffic": traffic[dom]["bytes"] if traffic[dom] else None,
                      "algorithmic_bytes_per_launch": alg_per_launch[dom],
-                     "avg_launch_ms": avg_ms, "launches_per_step": G},
+                     "avg_launch_ms": avg_ms, "launches_per_step": launches},
         "sampler": {"bound": "alu", "kernel": "k_sample", "achieved": keys / t_hash,
                     "peak": KEYS_PEAK, "unit": "keys/s", "frac": keys / t_hash / KEYS_PEAK,
                     "keys_per_step": keys / steps, "ms_per_step": t_hash / steps * 1e3,
                     "peak_derivation": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz / 21.5 VALU "
                                        "instructions per key"},
         "other_kernel": {"name": names[other], "achieved_GBps": kern[other][0],
-                         "avg_launch_ms": kern[other][1],
+                         "avg_launch_ms": kern[other][1], "launches_per_step": launches,
                          "algorithmic_bytes_per_launch": alg_per_launch[other],
                          "traffic": traffic[other]["bytes"] if traffic[other] else None},
         "ms_per_step_with_stage_events": wall_events / steps * 1e3,
@@ -365,7 +382,7 @@ def main():
                               "achieved": miss_rate, "peak": link["B_link_GBps"], "unit": "GB/s",
                               "frac": miss_rate / link["B_link_GBps"], "traffic": None,
                               "peak_source": "measured: best of 5 hipMemcpyAsync of 1 GiB pinned host -> device",
-                              "avg_launch_ms": kern["gather"][1], "launches_per_step": G}
+                              "avg_launch_ms": kern["gather"][1], "launches_per_step": launches}
     progress("stage timing and counts done")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, graph, table, order, step, args.cpu_seconds,

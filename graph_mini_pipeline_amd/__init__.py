@@ -16,7 +16,8 @@ import torch
 from . import _abi
 from ._abi import (GNN_ERR_CAPACITY, GNN_ERR_HIP, GNN_ERR_INTERNAL, GNN_ERR_INVALID_ARG,  # noqa
                    GNN_ERR_OUT_OF_RANGE, GNN_ERR_UNSUPPORTED, GNN_MAX_HOPS, GNN_OK, GNN_SYNC,
-                   GNN_SUPERBATCH_COMPACT, GNN_SUPERBATCH_FULL,
+                   GNN_SUPERBATCH_COMPACT, GNN_SUPERBATCH_FULL, GNN_GATHER_BATCHED,
+                   GNN_GATHER_INTERLEAVED,
                    GNN_TIMER_STAGES)
 
 __all__ = [
@@ -79,6 +80,7 @@ class Options:
     wave_max_deg: int = 0
     sync: bool = False
     superbatch: str = "auto"    # super-batch relabel: "auto", "full" or "compact"
+    gather: str = "auto"        # gather and outermost mean: "auto", "interleaved" or "batched"
 
     def c(self) -> _abi.gnn_options:
         o = _abi.gnn_options()
@@ -87,7 +89,10 @@ class Options:
         modes = {"auto": 0, "full": GNN_SUPERBATCH_FULL, "compact": GNN_SUPERBATCH_COMPACT}
         if self.superbatch not in modes:
             raise ValueError(f"superbatch must be one of {sorted(modes)}")
-        o.flags = (GNN_SYNC if self.sync else 0) | modes[self.superbatch]
+        gmodes = {"auto": 0, "interleaved": GNN_GATHER_INTERLEAVED, "batched": GNN_GATHER_BATCHED}
+        if self.gather not in gmodes:
+            raise ValueError(f"gather must be one of {sorted(gmodes)}")
+        o.flags = (GNN_SYNC if self.sync else 0) | modes[self.superbatch] | gmodes[self.gather]
         return o
 
 

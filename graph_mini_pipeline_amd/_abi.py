@@ -16,6 +16,8 @@ GNN_TIMER_STAGES = 5
 GNN_SYNC = 1
 GNN_SUPERBATCH_FULL = 2
 GNN_SUPERBATCH_COMPACT = 4
+GNN_GATHER_INTERLEAVED = 8
+GNN_GATHER_BATCHED = 16
 
 GNN_OK = 0
 GNN_ERR_INVALID_ARG = -1

@@ -20,7 +20,8 @@ struct gnn_feature_store {
 };
 
 // Events per record: call start, end of sampling, then per sub-batch the ends of its gather and
-// of its outermost-block mean, then the end of the call; then two per hop around the sampling
+// of its outermost-block mean (batched gather: slot 2 ends the one gather launch and slot 1 + 2G
+// the one outermost-mean launch), then the end of the call; then two per hop around the sampling
 // kernel (k_sample) of that hop.
 constexpr int kSampleEvents = 3 + 2 * GNN_MAX_GROUP;
 constexpr int kTimerSlots = kSampleEvents + 2 * GNN_MAX_HOPS;
@@ -31,6 +32,7 @@ struct gnn_timer {
     std::vector<hipEvent_t> ev;   // n_records * kTimerSlots
     std::vector<int32_t> group;   // sub-batches of each recorded call
     std::vector<int32_t> hops;    // hops of each recorded call
+    std::vector<int32_t> batched; // 1: one gather launch and one outermost-mean launch
 };
 
 namespace {
@@ -137,6 +139,9 @@ SuperMode super_mode(const gnn_caps &mc, int64_t N, int G, uint32_t flags) {
     return 3 * static_cast<int64_t>(G + 1) * W >= max_union_edges(mc, N, G) ? kSuperCompact : kSuperFull;
 }
 
+// Row width (floats) above which gnn_minibatch batches its gathers by default.
+constexpr int64_t kBatchedGatherMinD = 128;
+
 // Largest byte-map region of a super-batch's sub-batch relabels (beyond it, marks stay atomic).
 constexpr int64_t kByteMapsMax = 1LL << 30;
 
@@ -220,6 +225,7 @@ gnn_status read_opts(const gnn_options *o, Opts *out) {
     }
     if (r.group_max < 1 || r.wave_max < r.group_max) return GNN_ERR_INVALID_ARG;
     if ((r.flags & GNN_SUPERBATCH_FULL) && (r.flags & GNN_SUPERBATCH_COMPACT)) return GNN_ERR_INVALID_ARG;
+    if ((r.flags & GNN_GATHER_INTERLEAVED) && (r.flags & GNN_GATHER_BATCHED)) return GNN_ERR_INVALID_ARG;
     *out = r;
     return GNN_OK;
 }
@@ -783,12 +789,19 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
     const Workspace w = carve(mc, g->num_nodes, group, mode, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // How stages 2 and 3 run (below).  Batched by default for a host-resident table (G times as
+    // many host-link reads in flight) and for rows wider than 512 bytes (the launch start-up and
+    // drain of G gathers outweigh the cache reuse of interleaving); measured on the 602-, 128-,
+    // 100- and 64-float workloads.
+    const bool batched = !(o.flags & GNN_GATHER_INTERLEAVED) &&
+                         ((o.flags & GNN_GATHER_BATCHED) || fs->on_host || d > kBatchedGatherMinD);
     hipEvent_t *ev = nullptr;
     if (timer) {
         if (timer->cursor >= timer->n_records) return GNN_ERR_CAPACITY;
         ev = timer->ev.data() + static_cast<size_t>(timer->cursor) * kTimerSlots;
         timer->group[timer->cursor] = group;
         timer->hops[timer->cursor] = K;
+        timer->batched[timer->cursor] = batched ? 1 : 0;
         timer->cursor += 1;
         GNN_TRY_HIP(hipEventRecord(ev[0], s));
     }
@@ -798,20 +811,50 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
                     ev ? ev + kSampleEvents : nullptr);
     if (st != GNN_OK) return st;
     if (ev) GNN_TRY_HIP(hipEventRecord(ev[1], s));
-    // Stages 2 and 3, per sub-batch: gather X = rows of V_K, then the outermost block's mean,
-    // which reads X while it is still in the caches.
-    for (int gi = 0; gi < group; ++gi) {
-        gnn_minibatch_out &mo = outs[gi];
-        const gnn_caps &c = mo.blocks.caps;
-        GNN_TRY_HIP(launch_gather(fs->table, fs->cache, fs->slot, fs->ld, d, fs->num_nodes,
-                                  mo.blocks.hop[K - 1].nodes, mo.blocks.counts + 2 * (K - 1) + 1,
-                                  c.nodes[K - 1], mo.x, mo.ld_h, nullptr, w.status, s));
-        if (ev) GNN_TRY_HIP(hipEventRecord(ev[2 + 2 * gi], s));
-        const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
-        const MeanJob job{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].lid, c.edges[K - 1],
-                          d_n, c.frontier[K - 1], mo.x, c.nodes[K - 1], mo.h[K - 1]};
-        GNN_TRY_HIP(launch_mean(&job, 1, mo.ld_h, mo.ld_h, d, fanouts[K - 1], w.status, s));
-        if (ev) GNN_TRY_HIP(hipEventRecord(ev[3 + 2 * gi], s));
+    // Stages 2 and 3: gather X = rows of V_K, then the outermost block's mean.  Batched: every
+    // sub-batch's gather in one launch, then every outermost mean in one launch.  Interleaved: per
+    // sub-batch, so the mean reads X while it is still in the caches.
+    if (batched) {
+        GatherBatchArgs ga{};
+        ga.nseg = group;
+        ga.table = fs->table;
+        ga.cache = fs->cache;
+        ga.slot = fs->slot;
+        ga.ld = fs->ld;
+        ga.d = static_cast<int32_t>(d);
+        ga.num_rows = fs->num_nodes;
+        ga.ld_out = outs[0].ld_h;
+        ga.status = w.status;
+        int64_t rows_cap = 0;
+        MeanJob jobs[GNN_MAX_GROUP];
+        for (int gi = 0; gi < group; ++gi) {
+            gnn_minibatch_out &mo = outs[gi];
+            const gnn_caps &c = mo.blocks.caps;
+            ga.seg[gi] = GatherSeg{mo.blocks.hop[K - 1].nodes, mo.blocks.counts + 2 * (K - 1) + 1,
+                                   c.nodes[K - 1], mo.x};
+            rows_cap += c.nodes[K - 1];
+            const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
+            jobs[gi] = MeanJob{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].lid, c.edges[K - 1],
+                               d_n, c.frontier[K - 1], mo.x, c.nodes[K - 1], mo.h[K - 1]};
+        }
+        GNN_TRY_HIP(launch_gather_batch(ga, rows_cap, s));
+        if (ev) GNN_TRY_HIP(hipEventRecord(ev[2], s));
+        GNN_TRY_HIP(launch_mean(jobs, group, outs[0].ld_h, outs[0].ld_h, d, fanouts[K - 1], w.status, s));
+        if (ev) GNN_TRY_HIP(hipEventRecord(ev[1 + 2 * group], s));
+    } else {
+        for (int gi = 0; gi < group; ++gi) {
+            gnn_minibatch_out &mo = outs[gi];
+            const gnn_caps &c = mo.blocks.caps;
+            GNN_TRY_HIP(launch_gather(fs->table, fs->cache, fs->slot, fs->ld, d, fs->num_nodes,
+                                      mo.blocks.hop[K - 1].nodes, mo.blocks.counts + 2 * (K - 1) + 1,
+                                      c.nodes[K - 1], mo.x, mo.ld_h, nullptr, w.status, s));
+            if (ev) GNN_TRY_HIP(hipEventRecord(ev[2 + 2 * gi], s));
+            const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
+            const MeanJob job{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].lid, c.edges[K - 1],
+                              d_n, c.frontier[K - 1], mo.x, c.nodes[K - 1], mo.h[K - 1]};
+            GNN_TRY_HIP(launch_mean(&job, 1, mo.ld_h, mo.ld_h, d, fanouts[K - 1], w.status, s));
+            if (ev) GNN_TRY_HIP(hipEventRecord(ev[3 + 2 * gi], s));
+        }
     }
     // Stage 4: the inner blocks, h_{l-1} from h_l for l = K-1..1, every sub-batch in one launch.
     for (int l = K - 1; l >= 1; --l) {
@@ -849,6 +892,7 @@ gnn_status gnn_timer_create(int32_t n_records, gnn_timer **out) {
     t->ev.assign(static_cast<size_t>(n_records) * kTimerSlots, nullptr);
     t->group.assign(static_cast<size_t>(n_records), 0);
     t->hops.assign(static_cast<size_t>(n_records), 0);
+    t->batched.assign(static_cast<size_t>(n_records), 0);
     for (auto &e : t->ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             gnn_timer_destroy(t);
@@ -885,11 +929,16 @@ gnn_status gnn_timer_elapsed(gnn_timer *t, int32_t *n_records, float *ms) {
         float v = 0.f, gat = 0.f, outer = 0.f;
         GNN_TRY_HIP(hipEventElapsedTime(&v, e[0], e[1]));
         ms[r * GNN_TIMER_STAGES + 0] = v;
-        for (int gi = 0; gi < G; ++gi) {
-            GNN_TRY_HIP(hipEventElapsedTime(&v, e[1 + 2 * gi], e[2 + 2 * gi]));
-            gat += v;
-            GNN_TRY_HIP(hipEventElapsedTime(&v, e[2 + 2 * gi], e[3 + 2 * gi]));
-            outer += v;
+        if (t->batched[r]) {
+            GNN_TRY_HIP(hipEventElapsedTime(&gat, e[1], e[2]));
+            GNN_TRY_HIP(hipEventElapsedTime(&outer, e[2], e[1 + 2 * G]));
+        } else {
+            for (int gi = 0; gi < G; ++gi) {
+                GNN_TRY_HIP(hipEventElapsedTime(&v, e[1 + 2 * gi], e[2 + 2 * gi]));
+                gat += v;
+                GNN_TRY_HIP(hipEventElapsedTime(&v, e[2 + 2 * gi], e[3 + 2 * gi]));
+                outer += v;
+            }
         }
         ms[r * GNN_TIMER_STAGES + 1] = gat;
         ms[r * GNN_TIMER_STAGES + 2] = outer;

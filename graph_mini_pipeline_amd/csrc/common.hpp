@@ -264,6 +264,32 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
                          int32_t *status, hipStream_t s);
+// One sub-batch of a batched gather: out[r] = row ids[r] for r < n (n = *d_n, or n_cap).
+struct GatherSeg {
+    const int32_t *ids;
+    const int64_t *d_n;
+    int64_t n_cap;
+    float *out;
+};
+
+struct GatherBatchArgs {
+    GatherSeg seg[kMaxGroup];
+    int32_t nseg;
+    const float *table;
+    const float *cache;
+    const int32_t *slot;
+    int64_t ld;
+    int32_t d;
+    int64_t num_rows;
+    int64_t ld_out;
+    int32_t *status;
+    uint32_t cpr;      // set by the launcher
+};
+
+// Gather of up to kMaxGroup sub-batches in one launch (rows_cap: the sub-batches' total row
+// capacity).  Rows that are not 16-byte aligned take the flat kernel, one launch per sub-batch.
+hipError_t launch_gather_batch(GatherBatchArgs a, int64_t rows_cap, hipStream_t s);
+
 // One mean-aggregation block: destinations [0, n) (n = *d_n, or n_cap if d_n is NULL) with
 // edges indptr / lid (lid has e_cap entries), sources src [n_src rows], output out.
 struct MeanJob {

@@ -195,6 +195,120 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
     }
 }
 
+
+// ---- all sub-batches of a super-batch in one launch -----------------------------------------------
+//
+// Row units (G consecutive output rows of one sub-batch, one slab) are numbered over the sub-batches'
+// actual row counts, so one launch streams every sub-batch's rows: the start-up and drain of one
+// large launch replace those of G small ones, and a host-resident table keeps G times as many
+// host-link reads in flight.
+
+template <int G, int CH, int R>
+__global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
+    __shared__ int64_t s_n[kMaxGroup];
+    __shared__ uint32_t s_u0[kMaxGroup + 1];
+    const int lane = lane_id();
+    const int grp = lane / G;
+    const int gl = lane % G;
+    const uint32_t cpr = a.cpr;
+    const uint32_t slabs = (cpr + CH * G - 1) / (CH * G);
+    if (threadIdx.x < static_cast<unsigned>(a.nseg)) {
+        const GatherSeg &S = a.seg[threadIdx.x];
+        s_n[threadIdx.x] = load_count(S.d_n, S.n_cap);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t u = 0;
+        for (int sg = 0; sg < a.nseg; ++sg) {
+            s_u0[sg] = u;
+            u += static_cast<uint32_t>((s_n[sg] + G - 1) / G) * slabs;
+        }
+        s_u0[a.nseg] = u;
+    }
+    __syncthreads();
+    const uint32_t units = s_u0[a.nseg];
+    const uint32_t g0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (64 / G) + grp;
+    const uint32_t gstride = gridDim.x * 4u * (64 / G);
+    for (uint32_t it = g0; it < units; it += gstride) {
+        int sg = 0;
+        while (sg + 1 < a.nseg && s_u0[sg + 1] <= it) ++sg;
+        const GatherSeg &S = a.seg[sg];
+        const uint32_t li = it - s_u0[sg];
+        const uint32_t rb = li / slabs;
+        const uint32_t p = li - rb * slabs;
+        const int64_t r0 = static_cast<int64_t>(rb) * G;
+        const int64_t n = s_n[sg];
+        const int nb = static_cast<int>(n - r0 < G ? n - r0 : G);
+        // lane t: source row of output row r0 + t (NULL: invalid id)
+        const float *mine = nullptr;
+        if (gl < nb) {
+            const int32_t v = S.ids[r0 + gl];
+            if (v < 0 || v >= a.num_rows) {
+                set_status(a.status, GNN_ERR_OUT_OF_RANGE);
+            } else {
+                const int32_t sl = a.slot ? a.slot[v] : -1;
+                mine = sl >= 0 ? a.cache + static_cast<int64_t>(sl) * a.ld
+                               : a.table + static_cast<int64_t>(v) * a.ld;
+            }
+        }
+        const uint64_t mine_u = reinterpret_cast<uint64_t>(mine);
+        const uint32_t ch0 = p * CH * G + gl;
+        bool act[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) act[q] = ch0 + q * G < cpr;
+        auto row_of = [&](int r) -> const float * {
+            const int rr = r < nb ? r : 0;
+            uint64_t x;
+            if constexpr (G == 64) {
+                const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine_u), rr);
+                const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine_u >> 32), rr);
+                x = (static_cast<uint64_t>(hi) << 32) | lo;
+            } else {
+                x = __shfl(mine_u, grp * G + rr, 64);
+            }
+            return reinterpret_cast<const float *>(x);
+        };
+        f32x4 v[R][CH];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float *row = row_of(r);
+#pragma unroll
+            for (int q = 0; q < CH; ++q)
+                v[r][q] = (r < nb && row && act[q])
+                              ? *reinterpret_cast<const f32x4 *>(row + static_cast<int64_t>(ch0 + q * G) * 4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int e = 0; e < nb; e += R) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int er = e + r;
+                if (er < nb && row_of(er)) {
+                    float *o = S.out + (r0 + er) * a.ld_out;
+#pragma unroll
+                    for (int q = 0; q < CH; ++q) {
+                        if (!act[q]) continue;
+                        const int col = static_cast<int>(ch0 + q * G) * 4;
+                        const int rem = a.d - col;
+                        if (rem >= 4) {
+                            *reinterpret_cast<f32x4 *>(o + col) = v[r][q];
+                        } else {
+                            const float t[4] = {v[r][q][0], v[r][q][1], v[r][q][2], v[r][q][3]};
+                            for (int w = 0; w < rem; ++w) o[col + w] = t[w];
+                        }
+                    }
+                }
+                const int en = er + R;
+                const float *row = row_of(en);
+#pragma unroll
+                for (int q = 0; q < CH; ++q)
+                    v[r][q] = (en < nb && row && act[q])
+                                  ? *reinterpret_cast<const f32x4 *>(row + static_cast<int64_t>(ch0 + q * G) * 4)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
+}
+
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
@@ -228,6 +342,38 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
     else if (CH == 2) hipLaunchKernelGGL((k_gather_rows<64, 2, 8>), grid, dim3(256), 0, s, g);
     else if (CH == 3) hipLaunchKernelGGL((k_gather_rows<64, 3, 8>), grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL((k_gather_rows<64, 4, 8>), grid, dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_batch(GatherBatchArgs a, int64_t rows_cap, hipStream_t s) {
+    if (a.nseg <= 0 || a.d <= 0 || rows_cap <= 0) return hipSuccess;
+    bool v4 = a.ld % 4 == 0 && a.ld_out % 4 == 0 && aligned16(a.table) &&
+              (a.cache == nullptr || aligned16(a.cache));
+    for (int sg = 0; sg < a.nseg; ++sg) v4 = v4 && (a.seg[sg].n_cap == 0 || aligned16(a.seg[sg].out));
+    if (!v4) {
+        // rows not 16-byte aligned: the flat kernel, one launch per sub-batch
+        for (int sg = 0; sg < a.nseg; ++sg) {
+            const GatherSeg &S = a.seg[sg];
+            const hipError_t e = launch_gather(a.table, a.cache, a.slot, a.ld, a.d, a.num_rows, S.ids,
+                                               S.d_n, S.n_cap, S.out, a.ld_out, nullptr, a.status, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    const int64_t cpr = (a.d + 3) / 4;
+    a.cpr = static_cast<uint32_t>(cpr);
+    const int G = cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64);
+    const int CH = G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);
+    const int64_t slabs = (cpr + CH * G - 1) / (CH * G);
+    const int64_t units = (rows_cap + G - 1) / G * slabs + a.nseg * slabs;
+    if (units > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const dim3 grid(grid_for(units, 4 * (64 / G), 8192));
+    if (G == 16) hipLaunchKernelGGL((k_gather_batch<16, 1, 4>), grid, dim3(256), 0, s, a);
+    else if (G == 32) hipLaunchKernelGGL((k_gather_batch<32, 1, 4>), grid, dim3(256), 0, s, a);
+    else if (CH == 1) hipLaunchKernelGGL((k_gather_batch<64, 1, 8>), grid, dim3(256), 0, s, a);
+    else if (CH == 2) hipLaunchKernelGGL((k_gather_batch<64, 2, 8>), grid, dim3(256), 0, s, a);
+    else if (CH == 3) hipLaunchKernelGGL((k_gather_batch<64, 3, 8>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_gather_batch<64, 4, 8>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

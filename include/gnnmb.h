@@ -60,6 +60,16 @@ typedef void *gnn_stream; /* hipStream_t */
  *            relabels positions in it (cheapest when num_nodes is large). */
 #define GNN_SUPERBATCH_FULL 2u
 #define GNN_SUPERBATCH_COMPACT 4u
+/* How gnn_minibatch gathers X and takes the outermost mean (results are identical; at most one may
+ * be set; by default BATCHED for a host-resident table or rows of more than 128 floats, else
+ * INTERLEAVED):
+ *   INTERLEAVED: per sub-batch, the gather then the mean, which reads X while it is still in the
+ *                caches;
+ *   BATCHED:     every sub-batch's gather in one launch, then every outermost mean in one launch
+ *                (one launch's start-up and drain instead of G; G times as many host-link reads
+ *                in flight for a host-resident table). */
+#define GNN_GATHER_INTERLEAVED 8u
+#define GNN_GATHER_BATCHED 16u
 
 /*
  * Graph in CSR form by destination: row v lists the sources u of the edges (u, v), which is the
@@ -107,7 +117,7 @@ typedef struct gnn_options {
     int32_t group_max_deg; /* degree bound of the 16-lane class (default 256) */
     int32_t wave_max_deg;  /* degree bound of the one-wavefront class (default 4096); higher
                               degrees take one workgroup per node */
-    uint32_t flags;        /* GNN_SYNC | GNN_SUPERBATCH_FULL | GNN_SUPERBATCH_COMPACT */
+    uint32_t flags;        /* GNN_SYNC, GNN_SUPERBATCH_*, GNN_GATHER_* */
     int32_t reserved[5];
 } gnn_options;
 
@@ -160,7 +170,7 @@ gnn_status gnn_sample_khop(const gnn_graph *g, const int32_t *seeds, int64_t n_s
                            const gnn_options *opt, gnn_stream stream);
 
 /*
- * Sort-unique relabel of two id lists (FastGL's id remapping; GARDEN Alg. 1 line 2 dedup):
+ * Sort-unique relabel of two id lists (FastGL's id remapping; the deduplication of GARDEN Sec. IV.D, Alg. 1):
  *   uniq = ascending unique of keep[0..n_keep) and add[0..n_add);
  *   keep_lid[i] = index of keep[i] in uniq, add_lid[e] = index of add[e] in uniq.
  * Every id must lie in [0, id_bound).  n_add is the length of `add`, or, if d_n_add is not NULL,

@@ -417,3 +417,70 @@ def test_giant_rows(fanouts):
     assert st == gm.GNN_OK
     ref = oracle.minibatch(indptr, indices, x, seeds, fanouts, 4242)
     compare_with_oracle(outs[0], ref, 8)
+
+
+GATHER_MODES = {"auto": gm.Options(), "interleaved": gm.Options(gather="interleaved"),
+                "batched": gm.Options(gather="batched")}
+
+
+def _stores(x, ld, hot_rows, indptr):
+    """The four kinds of feature store over the same rows: HBM, HBM + cache, host, host + cache."""
+    n, d = x.shape
+    dev = device_table(x, ld)
+    host = torch.zeros(n, ld, dtype=torch.float32, pin_memory=True)
+    host[:, :d].copy_(torch.from_numpy(x))
+    hot = torch.from_numpy(np.argsort(-np.diff(indptr), kind="stable")[:hot_rows].astype(np.int32)).cuda()
+    return {"hbm": gm.gnn_feature_store_create(dev, d),
+            "hbm_cache": gm.gnn_feature_store_create(dev, d, hot_rows, hot),
+            "host": gm.gnn_feature_store_create(host, d),
+            "host_cache": gm.gnn_feature_store_create(host, d, hot_rows, hot)}
+
+
+@pytest.mark.parametrize("mode", sorted(GATHER_MODES))
+@pytest.mark.parametrize("store", ["hbm", "hbm_cache", "host", "host_cache"])
+def test_gather_modes_match_oracle(tiny, mode, store):
+    # a super-batch with an empty sub-batch, through each feature-store kind and gather layout
+    cfg, indptr, indices, x, order = tiny
+    fs = _stores(x, 64, 1500, indptr)[store]
+    seeds = order[:700]
+    ptr = [0, 256, 256, 600, 700]
+    outs, st = run_minibatch(device_graph(indptr, indices), fs, seeds, cfg.fanouts, 404,
+                             group_ptr=ptr, opts=GATHER_MODES[mode])
+    assert st == gm.GNN_OK
+    for g in range(4):
+        ref = oracle.minibatch(indptr, indices, x, seeds[ptr[g]:ptr[g + 1]], cfg.fanouts, 404)
+        compare_with_oracle(outs[g], ref, cfg.d)
+
+
+@pytest.mark.parametrize("d,ld", [(5, 5), (100, 100), (602, 604)])
+@pytest.mark.parametrize("store", ["hbm", "host_cache"])
+def test_batched_gather_row_widths(tiny, d, ld, store):
+    # unaligned rows (5 floats) take the flat kernel; 100 and 602 floats the 32- and 64-lane groups
+    cfg, indptr, indices, _, order = tiny
+    x = np.random.default_rng(d).standard_normal((cfg.num_nodes, d)).astype(np.float32)
+    fs = _stores(x, ld, 2000, indptr)[store]
+    seeds = order[:600]
+    ptr = [0, 100, 350, 600]
+    outs, st = run_minibatch(device_graph(indptr, indices), fs, seeds, [6, 4], 31, group_ptr=ptr,
+                             opts=gm.Options(gather="batched"))
+    assert st == gm.GNN_OK
+    for g in range(3):
+        ref = oracle.minibatch(indptr, indices, x, seeds[ptr[g]:ptr[g + 1]], [6, 4], 31)
+        compare_with_oracle(outs[g], ref, d)
+
+
+class _BothGather(gm.Options):
+    def c(self):
+        o = super().c()
+        o.flags |= gm.GNN_GATHER_INTERLEAVED | gm.GNN_GATHER_BATCHED
+        return o
+
+
+def test_gather_both_flags_rejected(tiny):
+    cfg, indptr, indices, x, order = tiny
+    with pytest.raises(ValueError):
+        gm.Options(gather="both").c()
+    with pytest.raises(gm.GnnError) as e:
+        run_minibatch(device_graph(indptr, indices), _store(x), order[:20], [3], 1,
+                      group_ptr=[0, 10, 20], opts=_BothGather())
+    assert e.value.status == gm.GNN_ERR_INVALID_ARG
