@@ -297,7 +297,8 @@ def main():
     other = "mean_outer" if dom == "gather" else "gather"
     from graph_mini_pipeline_amd.rocprof_summary import read_traffic
     counters = os.path.join(ROOT, "profiles", f"{cfg.name}_counters.txt")
-    traffic = {k: read_traffic(counters, names[k]) for k in names}
+    traffic = {"gather": read_traffic(counters, names["gather"]),
+               "mean_outer": read_traffic(counters, names["mean_outer"] + "@outer")}
     alg_per_launch = {"gather": gb_bytes.sum() / steps / launches,
                       "mean_outer": mean_outer.sum() / steps / launches}
 

@@ -6,7 +6,9 @@ counter summary into per-launch memory traffic.
 
 Counter summaries hold one machine-readable line per kernel:
     counters <kernel> dispatches=<n> fetch_kib=<avg> write_kib=<avg> source=<file> sha256=<hash>
-and one for the calibration copy (k_copy_probe, a plain copy of known size):
+(mean-aggregation kernels as <kernel>@outer for the outermost block, which follows the gather,
+and <kernel>@inner for the others) and one for the calibration copy (k_copy_probe, a plain copy of
+known size):
     calibration copy_bytes=<B> fetch_kib=<avg> write_kib=<avg>
 FETCH_SIZE and WRITE_SIZE are scaled by (copy bytes) / (counter reading of the copy) each.
 """
@@ -44,6 +46,7 @@ def short_name(name: str) -> str:
 
 
 def source_of(kernel: str) -> Optional[str]:
+    kernel = kernel.split("@")[0]
     for pre, src in KERNEL_SOURCES.items():
         if kernel.startswith(pre):
             return src
@@ -64,11 +67,17 @@ def trace_summary(trace_csv: str, command: str) -> str:
     stream = rows[0]["Stream_Id"] if rows else None
     per = defaultdict(list)
     others = 0
+    prev = ""
     for r in rows:
         if r["Stream_Id"] != stream:
             others += 1
             continue
-        per[short_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        name = short_name(r["Kernel_Name"])
+        key = name
+        if name.startswith("k_mean"):   # outermost block (right after the gather) or an inner one
+            key = name + ("@outer" if prev.startswith("k_gather") else "@inner")
+        per[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        prev = name
     out = [f"# rocprofv3 --kernel-trace summary (library kernels on stream {stream}, the stream of "
            f"the first library dispatch; {others} dispatches on other streams left out)",
            f"# command: {command}",
@@ -80,10 +89,21 @@ def trace_summary(trace_csv: str, command: str) -> str:
 
 
 def _per_kernel(path: str, counter: str) -> Dict[str, list]:
+    """Counter values per (kernel, grid size).  A mean-aggregation dispatch that directly follows a
+    gather dispatch (the outermost block, reading the rows just gathered) is named <kernel>@outer,
+    the other mean dispatches <kernel>@inner, so that the two block kinds are not averaged together."""
+    rows = [r for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and "gnnmb" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
     d = defaultdict(list)
-    for r in csv.DictReader(open(path)):
-        if r["Counter_Name"] == counter and "gnnmb" in r["Kernel_Name"]:
-            d[(short_name(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    prev = ""
+    for r in rows:
+        name = short_name(r["Kernel_Name"])
+        key = name
+        if name.startswith("k_mean"):
+            key = name + ("@outer" if prev.startswith("k_gather") else "@inner")
+        d[(key, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        prev = name
     return d
 
 

@@ -1,0 +1,43 @@
+"""The profile summaries: per-kernel counter averages, outer/inner mean tagging, calibration."""
+import csv
+import os
+
+from graph_mini_pipeline_amd import rocprof_summary as rs
+
+
+def _counter_csv(path, counter, rows):
+    cols = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for i, (name, grid, val) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Grid_Size": grid, "Kernel_Name": f"gnnmb::{name}(args)",
+                        "Counter_Name": counter, "Counter_Value": val})
+
+
+def test_counter_summary_tags_outer_mean_and_scales(tmp_path):
+    seq = [("k_sample", 100, 10.0), ("k_gather_batch<64, 3, 8>", 200, 1000.0),
+           ("k_mean_v5<64, 3, 4>", 300, 500.0), ("k_mean_v5<64, 3, 4>", 400, 50.0),
+           ("k_copy_probe", 500, 524288.0)]
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(f, "FETCH_SIZE", seq)
+    _counter_csv(w, "WRITE_SIZE", [(n, g, 2 * v) for n, g, v in seq])
+    text = rs.counter_summary("t", str(f), str(w), "cmd")
+    out = tmp_path / "c.txt"
+    out.write_text(text)
+    outer = rs.read_traffic(str(out), "k_mean_v5<64, 3, 4>@outer")
+    inner = rs.read_traffic(str(out), "k_mean_v5<64, 3, 4>@inner")
+    # calibration: the 1 GiB copy reads as 512 MiB fetched, 1 GiB written -> fetch x2, write x1
+    assert outer["fetch_scale"] == 2.0 and outer["write_scale"] == 1.0
+    assert outer["fetch_bytes"] == 500.0 * 1024 * 2 and outer["write_bytes"] == 1000.0 * 1024
+    assert inner["fetch_bytes"] == 50.0 * 1024 * 2
+    g = rs.read_traffic(str(out), "k_gather_batch<64, 3, 8>")
+    assert g["bytes"] == 1000.0 * 1024 * 2 + 2000.0 * 1024
+
+
+def test_read_traffic_stale_source_is_none(tmp_path):
+    out = tmp_path / "c.txt"
+    out.write_text("counters k_sample dispatches=1 fetch_kib=1.0 write_kib=1.0 source=csrc/sample.hip "
+                   "sha256=0000000000000000\ncalibration copy_bytes=1073741824 fetch_kib=1.0 write_kib=1.0\n")
+    assert rs.read_traffic(str(out), "k_sample") is None
+    assert rs.read_traffic(str(tmp_path / "missing.txt"), "k_sample") is None
