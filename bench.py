@@ -4,7 +4,8 @@ A step is one pass of the whole path over one mini-batch: k-hop sampling + relab
 the feature gather of V_K, and the mean aggregation of every block, all in the library's HIP
 kernels.  Inputs (graph, feature table, the epoch's seeds) are resident in HBM before timing.
 
-Prints one JSON line: throughput in sampled edges per second of whole-step time, the stage times,
+Prints one JSON line: throughput in sampled edges per second of whole-step time (steps issued round
+robin on a few streams, as an epoch would run; the single-stream figure beside it), the stage times,
 the gathered-feature bandwidth, the roofline of the dominant kernel (algorithmic bytes / its
 HIP-event-timed average duration, against the 8 TB/s HBM3E peak) and the oracle's CPU baseline on
 a bounded sample of the same batches.
@@ -87,18 +88,18 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
-                    help="timed steps (default: one epoch)")
+                    help="timed steps (default: five epochs, or 100 super-batches)")
     ap.add_argument("--group", type=int, default=8,
                     help="mini-batches per super-batch (one step = one super-batch)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dense")
     ap.add_argument("--streams", type=int, default=1,
-                    help="HIP streams the super-batches are issued on, round robin; each stream has "
-                         "its own workspace and outputs, so one stream's sampling overlaps another's "
-                         "gather and aggregation")
+                    help="streams of the single-stream regions (the stage and kernel timings)")
     ap.add_argument("--pipeline-streams", type=int, default=3,
-                    help="streams of the extra pipelined-throughput region (0: skip it); the "
-                         "headline and the per-kernel timing use --streams")
+                    help="HIP streams the headline issues the super-batches on, round robin; each "
+                         "has its own workspace and outputs, so one stream's sampling overlaps "
+                         "another's gather and aggregation (3 measured best of 2, 3, 4 and 6; "
+                         "0 or 1: the headline is the single-stream region)")
     ap.add_argument("--superbatch", default="auto", choices=["auto", "full", "compact"],
                     help="super-batch relabel mode (identical results)")
     ap.add_argument("--gather", default="auto", choices=["auto", "interleaved", "batched"],
@@ -132,16 +133,19 @@ def main():
         table = torch.empty(cfg.num_nodes, cfg.ld, dtype=torch.float32, device=dev)
         synth.make_features(cfg, table)
     order = synth.epoch_seed_order(cfg, 0, device=dev).contiguous()
-    torch.cuda.synchronize()
-    t_gen = time.perf_counter() - t0
-    progress(f"features ({'pinned host' if cfg.host_features else 'HBM'}) and seed order ready, "
-             f"{t_gen:.1f} s in all")
     n_batches = (order.numel() + cfg.batch - 1) // cfg.batch
     G = args.group
     n_super = (n_batches + G - 1) // G
-    # default: one epoch for a workload with a training set, 10 super-batches with a host-resident
-    # table, else 40 super-batches
-    steps = args.steps or (n_super if cfg.n_train else min(n_super, 10 if cfg.host_features else 40))
+    # default: five epochs for a workload with a training set (each epoch its own seed order),
+    # else 100 super-batches (30 with a host-resident table)
+    steps = args.steps or (5 * n_super if cfg.n_train else min(n_super, 30 if cfg.host_features else 100))
+    # seed order of each epoch the steps reach, made before any timing
+    orders = [order] + [synth.epoch_seed_order(cfg, e, device=dev).contiguous()
+                        for e in range(1, (steps + n_super - 1) // n_super)]
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t0
+    progress(f"features ({'pinned host' if cfg.host_features else 'HBM'}) and {len(orders)} seed "
+             f"order(s) ready, {t_gen:.1f} s in all")
     K = len(cfg.fanouts)
 
     dg = gm.DeviceGraph(cfg.num_nodes, graph.indptr, graph.indices)
@@ -164,8 +168,8 @@ def main():
     S = max(1, args.streams)
     P = max(0, args.pipeline_streams)
     P = P if P > 1 else 0
-    # streams 0..S-1 (0: the default stream) time the headline and the kernels; the pipelined
-    # region has streams S..S+P-1 of its own, so a kernel trace separates the two by stream
+    # streams 0..S-1 (0: the default stream) time the single-stream regions and the kernels; the
+    # pipelined headline has streams S..S+P-1 of its own, so a kernel trace separates the two
     wss = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
            for _ in range(S + P)]
     streams = [None] + [torch.cuda.Stream(device=dev) for _ in range(S + P - 1)]
@@ -176,14 +180,15 @@ def main():
         return list(range(b0, min(b0 + G, n_batches)))
 
     def step(st, timer=None, first=0, ns=S):
-        """Super-batch st (mod the epoch) on stream first + st % ns: its batches share one seed.
-        Returns (super-batch index, [(b, n, out)])."""
-        s = st % n_super
+        """Step st: super-batch st mod n_super of epoch st div n_super, on stream first + st % ns;
+        its batches share the batch seed of step st.  Returns (st, [(b, n, out)], its seeds)."""
+        e, s = divmod(st, n_super)
+        od = orders[e % len(orders)]
         q = first + st % ns
         bs = batch_range(s)
         lo = bs[0] * cfg.batch
-        hi = min(order.numel(), (bs[-1] + 1) * cfg.batch)
-        ptr = [min(b * cfg.batch, order.numel()) - lo for b in bs] + [hi - lo]
+        hi = min(od.numel(), (bs[-1] + 1) * cfg.batch)
+        ptr = [min(b * cfg.batch, od.numel()) - lo for b in bs] + [hi - lo]
         mine = []
         for j, b in enumerate(bs):
             n = ptr[j + 1] - ptr[j]
@@ -191,10 +196,10 @@ def main():
                 outs[q][(j, n)] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
                                                   cfg.d, cfg.ld)
             mine.append((b, n, outs[q][(j, n)]))
-        gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, gm.gnn_batch_seed(cfg.rng_seed, s),
+        gm.gnn_minibatch(dg, fs, od[lo:hi], ptr, cfg.fanouts, gm.gnn_batch_seed(cfg.rng_seed, st),
                          [m[2] for m in mine], wss[q], gm.Options(superbatch=args.superbatch, gather=args.gather),
                          timer=timer, stream=streams[q])
-        return s, mine
+        return st, mine, od[lo:hi]
 
     torch.cuda.synchronize()
     for b in range(max(args.warmup, S)):
@@ -202,30 +207,10 @@ def main():
     torch.cuda.synchronize()
     assert all(gm.gnn_read_device_status(w) == gm.GNN_OK for w in wss[:S])
 
-    # Timed region 1: the headline throughput, nothing but the steps on the stream.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for b in range(steps):
-        step(b)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    status = min(gm.gnn_read_device_status(w) for w in wss[:S])
-    progress(f"timed region: {steps} steps in {wall:.3f} s")
-
-    # Timed region 2: the same steps with HIP events at the stage boundaries (the events cost a few
-    # microseconds each, so they stay out of region 1).
-    timer = gm.Timer(steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for b in range(steps):
-        step(b, timer)
-    torch.cuda.synchronize()
-    wall_events = time.perf_counter() - t0
-    stages = np.array(timer.elapsed(), dtype=np.float64)      # [steps, 4] ms
-
-    # Timed region 3 (not the headline): the same steps issued round robin on P streams, each
-    # with its own workspace and outputs, so one super-batch's sampling overlaps another's gather
-    # and aggregation.
+    # Timed region 1, the headline: the steps issued round robin on P streams, each with its own
+    # workspace and outputs, so that one super-batch's sampling (ALU and latency bound) overlaps
+    # another's gather and aggregation (HBM bound) -- the throughput of an epoch as a training
+    # loop would run it.  Each step is still the whole path over its super-batch.
     wall_p = None
     if P:
         for b in range(P):
@@ -236,8 +221,30 @@ def main():
             step(b, first=S, ns=P)
         torch.cuda.synchronize()
         wall_p = time.perf_counter() - t0
-        status = min(status, min(gm.gnn_read_device_status(w) for w in wss[S:]))
         progress(f"pipelined region ({P} streams): {steps} steps in {wall_p:.3f} s")
+
+    # Timed region 2: the same steps one after another on one stream.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for b in range(steps):
+        step(b)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    status = min(gm.gnn_read_device_status(w) for w in wss)
+    progress(f"single-stream region: {steps} steps in {wall:.3f} s")
+
+    # Timed region 3: region 2 with HIP events at the stage boundaries, for the per-kernel times
+    # (the events cost a few microseconds each, so they stay out of regions 1 and 2).
+    timer = gm.Timer(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for b in range(steps):
+        step(b, timer)
+    torch.cuda.synchronize()
+    wall_events = time.perf_counter() - t0
+    stages = np.array(timer.elapsed(), dtype=np.float64)      # [steps, 5] ms
+    head_wall = wall_p if wall_p is not None else wall
+    head_streams = P if wall_p is not None else S
 
     # Sizes of each timed batch: sampling is a pure function of the batch, so an untimed re-run
     # of the sampling gives the counts.
@@ -250,12 +257,11 @@ def main():
     keys = 0      # sampling keys hashed: over each hop's union frontier, the degrees above the fanout
     deg = (graph.indptr[1:] - graph.indptr[:-1]).to(torch.int32)
     for b in range(steps):
-        _, mine = step(b)
+        _, mine, sb_seeds = step(b)
         torch.cuda.synchronize()
-        bs_ = batch_range(b % n_super)
         for l in range(K):
             if l == 0:   # the seeds of the super-batch
-                fr = [order[bs_[0] * cfg.batch:min(order.numel(), (bs_[-1] + 1) * cfg.batch)]]
+                fr = [sb_seeds]
             else:        # each sub-batch's V_{l-1}
                 fr = [out.blocks.nodes[l - 1][:int(out.blocks.counts[2 * l - 1].item())]
                       for _, _, out in mine]
@@ -304,22 +310,22 @@ def main():
 
     result = {
         "metric": "sampled edges/s + gathered feature GB/s per mini-batch; % of HBM peak",
-        "value": tot_edges / wall,
+        "value": tot_edges / head_wall,
         "unit": "sampled edges/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": wall / steps * 1e3,
+        "ms_per_step": head_wall / steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": workload_name(cfg), "batches_per_epoch": n_batches,
-                   "super_batch": G, "streams": S, "superbatch_relabel": args.superbatch,
+                   "super_batch": G, "streams": head_streams, "superbatch_relabel": args.superbatch,
                    "gather_layout": args.gather,
                    "step": f"one super-batch of {G} mini-batch(es)"},
-        "ms_per_minibatch": wall / n_minibatches * 1e3,
+        "ms_per_minibatch": head_wall / n_minibatches * 1e3,
         "status": gm.gnn_status_string(status),
         "sampled_edges_per_s_sampling_stage": tot_edges / t_sample,
         "gathered_GBps": float(np.sum(payload) / t_gather / 1e9),
@@ -345,12 +351,11 @@ def main():
                          "algorithmic_bytes_per_launch": alg_per_launch[other],
                          "traffic": traffic[other]["bytes"] if traffic[other] else None},
         "ms_per_step_with_stage_events": wall_events / steps * 1e3,
-        "pipelined": None if wall_p is None else {
-            "streams": P, "value": tot_edges / wall_p, "unit": "sampled edges/s",
-            "ms_per_step": wall_p / steps * 1e3,
-            "ms_per_minibatch": wall_p / n_minibatches * 1e3,
-            "note": "same steps on several streams (not the headline; kernel timings above are "
-                    "single-stream)"},
+        "single_stream": {"streams": S, "value": tot_edges / wall, "unit": "sampled edges/s",
+                          "ms_per_step": wall / steps * 1e3,
+                          "ms_per_minibatch": wall / n_minibatches * 1e3,
+                          "note": "the same steps one after another on one stream; the stage and "
+                                  "kernel timings come from this layout (with events)"},
         "input_generation_s": t_gen,
     }
 
@@ -386,8 +391,8 @@ def main():
                               "avg_launch_ms": kern["gather"][1], "launches_per_step": launches}
     progress("stage timing and counts done")
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, graph, table, order, step, args.cpu_seconds,
-                                              tot_edges / wall)
+        result["cpu_baseline"] = cpu_baseline(cfg, graph, table, step, args.cpu_seconds,
+                                              tot_edges / head_wall)
     print(json.dumps(result), flush=True)
 
 
@@ -419,7 +424,7 @@ def host_link(gm, table, dev):
     return {"B_link_GBps": best_copy, "zero_copy_read_GBps": best_zc}
 
 
-def cpu_baseline(cfg, graph, table, order, step, budget_s, gpu_value):
+def cpu_baseline(cfg, graph, table, step, budget_s, gpu_value):
     """The oracle (single-threaded C) on the first super-batches of the same epoch, until budget_s
     of CPU work has been spent; checks its results against the GPU path's on those batches."""
     import numpy as np
@@ -430,18 +435,20 @@ def cpu_baseline(cfg, graph, table, order, step, budget_s, gpu_value):
     indptr = graph.indptr.cpu().numpy()
     indices = graph.indices.cpu().numpy()
     x = table.cpu().numpy()
-    order_h = order.cpu().numpy()
     K = len(cfg.fanouts)
     spent, edges, batches, parity, st = 0.0, 0, 0, True, 0
     while spent < budget_s and batches < 64:
-        s, mine = step(st)
+        s, mine, sb_seeds = step(st)
         torch.cuda.synchronize()
         st += 1
         seed64 = oracle.batch_seed(cfg.rng_seed, s)
+        sb_h = sb_seeds.cpu().numpy()
+        off = 0
         for b, n, got in mine:
+            seeds = sb_h[off:off + n]
+            off += n
             if spent >= budget_s and batches > 0:
                 break
-            seeds = order_h[b * cfg.batch: b * cfg.batch + n]
             t0 = time.perf_counter()
             ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
             spent += time.perf_counter() - t0

@@ -815,6 +815,10 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     // sub-batch's gather in one launch, then every outermost mean in one launch.  Interleaved: per
     // sub-batch, so the mean reads X while it is still in the caches.
     if (batched) {
+        // With the table in HBM and no cache, the outermost means read the table rows of the
+        // sampled global ids: the sub-batches then share one copy of every row they have in common
+        // instead of one per sub-batch's X, so repeated rows hit the caches.
+        const bool from_table = !fs->on_host && fs->slot == nullptr;
         GatherBatchArgs ga{};
         ga.nseg = group;
         ga.table = fs->table;
@@ -834,12 +838,17 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
                                    c.nodes[K - 1], mo.x};
             rows_cap += c.nodes[K - 1];
             const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
-            jobs[gi] = MeanJob{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].lid, c.edges[K - 1],
-                               d_n, c.frontier[K - 1], mo.x, c.nodes[K - 1], mo.h[K - 1]};
+            if (from_table)   // X[lid[e]] is table row gid[e], bit for bit
+                jobs[gi] = MeanJob{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].gid, c.edges[K - 1],
+                                   d_n, c.frontier[K - 1], fs->table, fs->num_nodes, mo.h[K - 1]};
+            else
+                jobs[gi] = MeanJob{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].lid, c.edges[K - 1],
+                                   d_n, c.frontier[K - 1], mo.x, c.nodes[K - 1], mo.h[K - 1]};
         }
         GNN_TRY_HIP(launch_gather_batch(ga, rows_cap, s));
         if (ev) GNN_TRY_HIP(hipEventRecord(ev[2], s));
-        GNN_TRY_HIP(launch_mean(jobs, group, outs[0].ld_h, outs[0].ld_h, d, fanouts[K - 1], w.status, s));
+        GNN_TRY_HIP(launch_mean(jobs, group, from_table ? fs->ld : outs[0].ld_h, outs[0].ld_h, d,
+                                fanouts[K - 1], w.status, s));
         if (ev) GNN_TRY_HIP(hipEventRecord(ev[1 + 2 * group], s));
     } else {
         for (int gi = 0; gi < group; ++gi) {
