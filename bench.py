@@ -24,11 +24,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 # Plain-ALU ceiling of the sampler's hashing: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12
-# lane-instructions/s (one wave64 VALU instruction per SIMD every 4 clocks), over the 21.5 VALU
-# instructions per key of the candidate loop (two SplitMix64 finalisers of 17 instructions each,
-# two 64-bit compares and the ballot/mask bookkeeping per two keys).
+# lane-instructions/s (one wave64 VALU instruction per SIMD every 4 clocks), over the 19 VALU
+# instructions per key of the candidate loop (gfx950 assembly of k_sample: 76 per four keys --
+# four SplitMix64 finalisers of 16 instructions each on the key's high word, three 64-bit counter
+# adds, four 32-bit compares and five of loop bookkeeping).
 ALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
-VALU_PER_KEY = 21.5
+VALU_PER_KEY = 19.0
 KEYS_PEAK = ALU_LANE_OPS / VALU_PER_KEY
 PRESAMPLE_BATCHES = 64     # batches pre-sampled to rank the hot-row cache (disjoint seeds)
 
@@ -344,7 +345,7 @@ def main():
         "sampler": {"bound": "alu", "kernel": "k_sample", "achieved": keys / t_hash,
                     "peak": KEYS_PEAK, "unit": "keys/s", "frac": keys / t_hash / KEYS_PEAK,
                     "keys_per_step": keys / steps, "ms_per_step": t_hash / steps * 1e3,
-                    "peak_derivation": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz / 21.5 VALU "
+                    "peak_derivation": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz / 19 VALU "
                                        "instructions per key"},
         "other_kernel": {"name": names[other], "achieved_GBps": kern[other][0],
                          "avg_launch_ms": kern[other][1], "launches_per_step": launches,

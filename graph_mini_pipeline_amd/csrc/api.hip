@@ -212,7 +212,7 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
 
 struct Opts {
     int32_t group_max = 256;
-    int32_t wave_max = 4096;
+    int32_t wave_max = 16384;   // measured best of 1024 .. 65536 on the four large workloads
     uint32_t flags = 0;
 };
 

@@ -118,11 +118,13 @@ inline unsigned grid_for(int64_t items, int per_block, unsigned max_blocks) {
 enum : int32_t { kFull = 0, kGroup = 1, kWave = 2, kBlock = 3, kNumClasses = 4 };
 
 // Candidate capacities per class (LDS) and the fanout each supports (capacity >= 4 * fanout).
+// A sampler workgroup holds kBlockCap candidates of 12 bytes (key, position): 3328 of them keep it
+// under 40 KB, so four workgroups (32 wavefronts, the register-file limit) fit one CU's 160 KB.
 constexpr int kGroupLanes = 16;
-constexpr int kGroupCap = 128;
-constexpr int kWaveCap = 512;
+constexpr int kGroupCap = 104;
+constexpr int kWaveCap = 416;
 constexpr int kBlockThreads = 512;
-constexpr int kBlockCap = 4096;
+constexpr int kBlockCap = 3328;
 constexpr int kMaxFanout = kBlockCap / 4;
 
 // One sampling hop.

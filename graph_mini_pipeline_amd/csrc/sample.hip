@@ -189,31 +189,50 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a
     }
 }
 
-// ---- threshold selection helpers ----------------------------------------------------------------
+// Longest row the sampler handles (positions are int32).
+constexpr int64_t kMaxRowLength = 0x7FFFFFFFLL;
 
-// Threshold whose expected number of keys <= tau among deg uniform keys is ~ k + 3 sqrt(k) + 6.
-__device__ __forceinline__ uint64_t initial_tau(int64_t deg, int k) {
+// ---- threshold selection helpers ----------------------------------------------------------------
+//
+// Thresholds have the form tau = T * 2^32 + (2^32 - 1), so key <= tau exactly when the key's high
+// 32 bits are <= T: the candidate test needs only the high word of each key, and the full key is
+// formed for the candidates alone (they are ranked by (key, position)).
+
+// High 32 bits of the product of mix64's second step, and the key's high word from it.
+__device__ __forceinline__ uint64_t mix64_pre(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    return (z ^ (z >> 27)) * 0x94D049BB133111EBULL;   // mix64(z) = this ^ (this >> 31)
+}
+__device__ __forceinline__ uint32_t key_high(uint64_t w) {
+    const uint32_t h = static_cast<uint32_t>(w >> 32);
+    return h ^ (h >> 31);
+}
+__device__ __forceinline__ uint64_t key_full(uint64_t w) { return w ^ (w >> 31); }
+
+// T whose expected number of keys <= tau among deg uniform keys is ~ k + 3 sqrt(k) + 6.
+__device__ __forceinline__ uint32_t initial_tau(int64_t deg, int k) {
     const double mu = static_cast<double>(k) + 3.0 * sqrt(static_cast<double>(k)) + 6.0;
     const double p = mu / static_cast<double>(deg);
-    if (p >= 1.0) return ~0ull;
-    const double t = p * 18446744073709551616.0;
-    if (t >= 18446744073709549568.0) return ~0ull;
-    return static_cast<uint64_t>(t);
+    if (p >= 1.0) return 0xFFFFFFFFu;
+    const double t = p * 4294967296.0;
+    if (t >= 4294967295.0) return 0xFFFFFFFFu;
+    return static_cast<uint32_t>(t);
 }
 
-// Next threshold after a pass that collected `cnt` keys <= tau.  Returns false when done (k <=
-// cnt <= cap) and sets *fail when no threshold can separate the keys (identical keys only).
-__device__ __forceinline__ bool next_tau(int cnt, int k, int cap, uint64_t &tau, uint64_t &lo,
-                                         uint64_t &hi, bool &has_lo, bool &has_hi, bool &fail) {
+// Next T after a pass that collected `cnt` keys <= tau.  Returns false when done (k <= cnt <= cap)
+// and sets *fail when no threshold can separate the keys (more than cap - k keys sharing one high
+// word: never expected).
+__device__ __forceinline__ bool next_tau(int cnt, int k, int cap, uint32_t &tau, uint32_t &lo,
+                                         uint32_t &hi, bool &has_lo, bool &has_hi, bool &fail) {
     if (cnt < k) {
         has_lo = true;
         lo = tau;
         if (has_hi) tau = lo + (hi - lo) / 2;
-        else tau = tau >= (~0ull >> 2) ? ~0ull : ((tau << 2) | 3ull);
+        else tau = tau >= 0x3FFFFFFFu ? 0xFFFFFFFFu : ((tau << 2) | 3u);
     } else if (cnt > cap) {
         has_hi = true;
         hi = tau;
-        const uint64_t l = has_lo ? lo : 0ull;
+        const uint32_t l = has_lo ? lo : 0u;
         tau = l + (hi - l) / 2;
     } else {
         return false;
@@ -229,54 +248,55 @@ __device__ __forceinline__ bool next_tau(int cnt, int k, int cap, uint64_t &tau,
 //
 // Keys of positions j = gl, gl + G, ... of a row of length deg (G lanes, lane gl); the ones
 // <= tau are appended, in ascending position, to s_key / s_pos (first CAP kept).  Returns the
-// number of keys <= tau.  Two keys per lane per step; the position bound is checked only in the
-// tail.
+// number of keys <= tau.  Four keys per lane per step (positions j0 + q G + gl, q = 0..3); the
+// position bound is checked only in the tail.  Rows are shorter than 2^31 (checked by the caller).
 template <int G, int CAP>
-__device__ __forceinline__ int collect_lanes(uint64_t ns, int64_t deg, uint64_t tau, int gl,
+__device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t tau, int gl,
                                              uint64_t gmask, uint64_t below, uint64_t *s_key,
                                              int32_t *s_pos) {
+    constexpr int U = 4;
     const uint64_t step = kGamma * static_cast<uint64_t>(G);
     uint64_t z = ns + kGamma * static_cast<uint64_t>(gl + 1);
     int cnt = 0;
-    const int64_t main_end = deg / (2 * G) * (2 * G);
-    int64_t j0 = 0;
-    for (; j0 < main_end; j0 += 2 * G) {
-        const uint64_t k0 = mix64(z);
-        const uint64_t k1 = mix64(z + step);
-        z += 2 * step;
-        const bool p0 = k0 <= tau, p1 = k1 <= tau;
-        const uint64_t m0 = __ballot(p0) & gmask;
-        const uint64_t m1 = __ballot(p1) & gmask;
-        if (m0 | m1) {
-            if (p0) {
-                const int pos = cnt + __popcll(m0 & below);
-                if (pos < CAP) {
-                    s_key[pos] = k0;
-                    s_pos[pos] = static_cast<int32_t>(j0 + gl);
+    const int32_t main_end = deg / (U * G) * (U * G);
+    int32_t j0 = 0;
+    for (; j0 < main_end; j0 += U * G) {
+        uint64_t w[U];
+        bool p[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            w[q] = mix64_pre(z + step * q);
+            p[q] = key_high(w[q]) <= tau;
+        }
+        z += step * U;
+        uint64_t m[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) m[q] = __ballot(p[q]) & gmask;
+        if (m[0] | m[1] | m[2] | m[3]) {
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                if (p[q]) {
+                    const int pos = cnt + __popcll(m[q] & below);
+                    if (pos < CAP) {
+                        s_key[pos] = key_full(w[q]);
+                        s_pos[pos] = j0 + q * G + gl;
+                    }
                 }
+                cnt += __popcll(m[q]);
             }
-            cnt += __popcll(m0);
-            if (p1) {
-                const int pos = cnt + __popcll(m1 & below);
-                if (pos < CAP) {
-                    s_key[pos] = k1;
-                    s_pos[pos] = static_cast<int32_t>(j0 + G + gl);
-                }
-            }
-            cnt += __popcll(m1);
         }
     }
     for (; j0 < deg; j0 += G) {
-        const int64_t j = j0 + gl;
-        const uint64_t key = mix64(z);
+        const int32_t j = j0 + gl;
+        const uint64_t w = mix64_pre(z);
         z += step;
-        const bool p = j < deg && key <= tau;
+        const bool p = j < deg && key_high(w) <= tau;
         const uint64_t m = __ballot(p) & gmask;
         if (p) {
             const int pos = cnt + __popcll(m & below);
             if (pos < CAP) {
-                s_key[pos] = key;
-                s_pos[pos] = static_cast<int32_t>(j);
+                s_key[pos] = key_full(w);
+                s_pos[pos] = j;
             }
         }
         cnt += __popcll(m);
@@ -298,11 +318,12 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
     const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - start;
     const int64_t out0 = a.blk_indptr[i];
     const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
-    uint64_t tau = initial_tau(deg, k), lo = 0, hi = 0;
-    bool has_lo = false, has_hi = false, fail = false;
+    uint32_t tau = initial_tau(deg, k), lo = 0, hi = 0;
+    bool has_lo = false, has_hi = false, fail = deg > kMaxRowLength;
+    if (fail && gl == 0) set_status(a.status, GNN_ERR_UNSUPPORTED);   // positions are int32
     int cnt = 0;
-    for (int it = 0; it < 128; ++it) {
-        cnt = collect_lanes<G, CAP>(ns, deg, tau, gl, gmask, below, s_key, s_pos);
+    for (int it = 0; it < 128 && !fail; ++it) {
+        cnt = collect_lanes<G, CAP>(ns, static_cast<int32_t>(deg), tau, gl, gmask, below, s_key, s_pos);
         if (!next_tau(cnt, k, CAP, tau, lo, hi, has_lo, has_hi, fail)) break;
     }
     if (fail || cnt < k || cnt > CAP) {
@@ -339,59 +360,66 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
 
 // ---- one giant-row node on a whole workgroup -------------------------------------------------------
 __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, uint64_t *s_key,
-                                                  int32_t *s_pos, uint8_t *s_sel,
-                                                  uint32_t *s_cnt) {
+                                                  int32_t *s_pos, uint32_t *s_cnt) {
     constexpr int NT = kBlockThreads;
     constexpr int CAP = kBlockCap;
+    constexpr int U = 4;
     const int lane = lane_id();
     const uint64_t below = (1ull << lane) - 1ull;
     const int k = a.k;
     const int32_t v = a.front[i];
     const int64_t start = row_ptr(a.indptr, a.ib, v);
-    const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - start;
+    const int64_t deg64 = row_ptr(a.indptr, a.ib, v + 1) - start;
     const int64_t out0 = a.blk_indptr[i];
     const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
-    uint64_t tau = initial_tau(deg, k), lo = 0, hi = 0;
-    bool has_lo = false, has_hi = false, fail = false;
+    uint32_t tau = initial_tau(deg64, k), lo = 0, hi = 0;
+    bool has_lo = false, has_hi = false, fail = deg64 > kMaxRowLength;
+    if (fail && threadIdx.x == 0) set_status(a.status, GNN_ERR_UNSUPPORTED);   // positions are int32
+    const int32_t deg = fail ? 0 : static_cast<int32_t>(deg64);
     int cnt = 0;
     const uint64_t step = kGamma * static_cast<uint64_t>(NT);
-    const int64_t main_end = deg / (2 * NT) * (2 * NT);
-    for (int it = 0; it < 128; ++it) {
+    const int32_t main_end = deg / (U * NT) * (U * NT);
+    for (int it = 0; it < 128 && !fail; ++it) {
         if (threadIdx.x == 0) *s_cnt = 0;
         __syncthreads();
         uint64_t z = ns + kGamma * static_cast<uint64_t>(threadIdx.x + 1);
-        int64_t j0 = 0;
-        for (; j0 < main_end; j0 += 2 * NT) {
-            const uint64_t k0 = mix64(z);
-            const uint64_t k1 = mix64(z + step);
-            z += 2 * step;
-            const bool p0 = k0 <= tau, p1 = k1 <= tau;
-            const uint64_t m0 = __ballot(p0), m1 = __ballot(p1);
-            if (m0 | m1) {
+        int32_t j0 = 0;
+        for (; j0 < main_end; j0 += U * NT) {
+            uint64_t w[U];
+            bool p[U];
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                w[q] = mix64_pre(z + step * q);
+                p[q] = key_high(w[q]) <= tau;
+            }
+            z += step * U;
+            uint64_t m[U];
+#pragma unroll
+            for (int q = 0; q < U; ++q) m[q] = __ballot(p[q]);
+            if (m[0] | m[1] | m[2] | m[3]) {
                 uint32_t wbase = 0;
-                if (lane == 0) wbase = atomicAdd(s_cnt, static_cast<uint32_t>(__popcll(m0) + __popcll(m1)));
+                if (lane == 0)
+                    wbase = atomicAdd(s_cnt, static_cast<uint32_t>(__popcll(m[0]) + __popcll(m[1]) +
+                                                                   __popcll(m[2]) + __popcll(m[3])));
                 wbase = __shfl(wbase, 0, 64);
-                if (p0) {
-                    const uint32_t pos = wbase + __popcll(m0 & below);
-                    if (pos < CAP) {
-                        s_key[pos] = k0;
-                        s_pos[pos] = static_cast<int32_t>(j0 + threadIdx.x);
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    if (p[q]) {
+                        const uint32_t pos = wbase + __popcll(m[q] & below);
+                        if (pos < CAP) {
+                            s_key[pos] = key_full(w[q]);
+                            s_pos[pos] = j0 + q * NT + static_cast<int32_t>(threadIdx.x);
+                        }
                     }
-                }
-                if (p1) {
-                    const uint32_t pos = wbase + __popcll(m0) + __popcll(m1 & below);
-                    if (pos < CAP) {
-                        s_key[pos] = k1;
-                        s_pos[pos] = static_cast<int32_t>(j0 + NT + threadIdx.x);
-                    }
+                    wbase += __popcll(m[q]);
                 }
             }
         }
         for (; j0 < deg; j0 += NT) {
-            const int64_t j = j0 + threadIdx.x;
-            const uint64_t key = mix64(z);
+            const int32_t j = j0 + static_cast<int32_t>(threadIdx.x);
+            const uint64_t w = mix64_pre(z);
             z += step;
-            const bool p = j < deg && key <= tau;
+            const bool p = j < deg && key_high(w) <= tau;
             const uint64_t m = __ballot(p);
             if (m) {
                 uint32_t wbase = 0;
@@ -400,8 +428,8 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
                 if (p) {
                     const uint32_t pos = wbase + __popcll(m & below);
                     if (pos < CAP) {
-                        s_key[pos] = key;
-                        s_pos[pos] = static_cast<int32_t>(j);
+                        s_key[pos] = key_full(w);
+                        s_pos[pos] = j;
                     }
                 }
             }
@@ -415,8 +443,11 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
         if (threadIdx.x == 0) set_status(a.status, GNN_ERR_INTERNAL);
         cnt = 0;
     }
-    // Candidates are in arbitrary order: rank by (key, pos), then place by position.
-    for (int c = threadIdx.x; c < cnt; c += NT) {
+    // Candidates are in arbitrary order: rank by (key, pos); the selected ones (rank < k) get the
+    // sign bit of their position (positions are < 2^31), then each is placed by position.
+    static_assert((kBlockCap + NT - 1) / NT <= 32, "selection bits fit one word");
+    uint32_t sel = 0;
+    for (int c = threadIdx.x, b = 0; c < cnt; c += NT, ++b) {
         const uint64_t kc = s_key[c];
         const int32_t jc = s_pos[c];
         int r = 0;
@@ -424,14 +455,20 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
             const uint64_t kt = s_key[t];
             r += (kt < kc) | ((kt == kc) & (s_pos[t] < jc));
         }
-        s_sel[c] = r < k ? 1 : 0;
+        if (r < k) sel |= 1u << b;
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < cnt; c += NT) {
-        if (!s_sel[c]) continue;
-        const int32_t jc = s_pos[c];
+    for (int c = threadIdx.x, b = 0; c < cnt; c += NT, ++b)
+        if (sel & (1u << b)) s_pos[c] |= static_cast<int32_t>(0x80000000u);
+    __syncthreads();
+    for (int c = threadIdx.x, b = 0; c < cnt; c += NT, ++b) {
+        if (!(sel & (1u << b))) continue;
+        const int32_t jc = s_pos[c] & 0x7FFFFFFF;
         int r = 0;
-        for (int t = 0; t < cnt; ++t) r += s_sel[t] & (s_pos[t] < jc);
+        for (int t = 0; t < cnt; ++t) {
+            const int32_t pt = s_pos[t];
+            r += (pt < 0) & ((pt & 0x7FFFFFFF) < jc);
+        }
         const int64_t o = out0 + r;
         if (o < a.E_cap) a.blk_gid[o] = a.indices[start + jc];
     }
@@ -454,7 +491,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_
                                                          int32_t nb_wave, int32_t nb_group) {
     __shared__ uint64_t s_key[kBlockCap];
     __shared__ int32_t s_pos[kBlockCap];
-    __shared__ uint8_t s_sel[kBlockCap];
     __shared__ uint32_t s_cnt;
     const int lane = lane_id();
     const int wv = static_cast<int>(threadIdx.x >> 6);
@@ -464,7 +500,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_
         const int64_t n = a.totals[1 + kBlock];
         const int32_t *list = a.lists + static_cast<int64_t>(kBlock) * a.F_cap;
         for (int64_t item = bid; item < n; item += nb_block)
-            sample_node_block(a, list[item], s_key, s_pos, s_sel, &s_cnt);
+            sample_node_block(a, list[item], s_key, s_pos, &s_cnt);
         return;
     }
     bid -= nb_block;

@@ -115,7 +115,7 @@ typedef struct gnn_blocks {
 /* Tuning knobs; results never depend on them.  NULL means defaults (all fields 0). */
 typedef struct gnn_options {
     int32_t group_max_deg; /* degree bound of the 16-lane class (default 256) */
-    int32_t wave_max_deg;  /* degree bound of the one-wavefront class (default 4096); higher
+    int32_t wave_max_deg;  /* degree bound of the one-wavefront class (default 16384); higher
                               degrees take one workgroup per node */
     uint32_t flags;        /* GNN_SYNC, GNN_SUPERBATCH_*, GNN_GATHER_* */
     int32_t reserved[5];

@@ -86,9 +86,11 @@ def test_capacity_rejects(bad):
 
 
 def test_capacity_unsupported_sizes():
-    with pytest.raises(gm.GnnError) as e:
-        gm.gnn_capacity(4, [5000], 10)          # fanout above the largest LDS class
-    assert e.value.status == gm.GNN_ERR_UNSUPPORTED
+    gm.gnn_capacity(4, [832], 10)               # the largest fanout: a quarter of the LDS class
+    for f in (833, 5000):
+        with pytest.raises(gm.GnnError) as e:
+            gm.gnn_capacity(4, [f], 10)         # fanout above the largest LDS class
+        assert e.value.status == gm.GNN_ERR_UNSUPPORTED
     with pytest.raises(gm.GnnError) as e:
         gm.gnn_capacity(2**30, [4], 2**31 - 1)  # edges overflow int32
     assert e.value.status == gm.GNN_ERR_UNSUPPORTED

@@ -46,7 +46,7 @@ def test_tiny_pipeline_matches_oracle(tiny, batch):
     compare_with_oracle(outs[0], ref, cfg.d)
 
 
-@pytest.mark.parametrize("group_max,wave_max", [(1, 1), (8, 32), (16, 100), (256, 4096),
+@pytest.mark.parametrize("group_max,wave_max", [(1, 1), (8, 32), (16, 100), (256, 4096), (256, 16384),
                                                 (100000, 100000)])
 def test_degree_classes_do_not_change_results(tiny, group_max, wave_max):
     # (1,1) sends every random node to the workgroup class, (100000,100000) to the 16-lane class
@@ -401,13 +401,14 @@ def test_superbatch_too_large_rejected(tiny):
 
 
 # Giant rows: two hubs of 10^6 and 4*10^4 in-neighbours in one frontier, with fanouts on either
-# side of the largest that the 16-lane and one-wavefront classes take.
+# side of the largest that the 16-lane (26) and one-wavefront (104) classes take, and the largest
+# fanout the library supports (832: a quarter of a workgroup's candidate capacity).
 def _two_hubs(D1=1_000_000, D2=40_000):
     rows = [list(range(2, 2 + D1)), list(range(3, 3 + D2))] + [[0, 1] for _ in range(D1 + 1)]
     return H.csr_from_rows(rows)
 
 
-@pytest.mark.parametrize("fanouts", [[5, 3], [32, 2], [33, 2], [200, 1]])
+@pytest.mark.parametrize("fanouts", [[5, 3], [26, 2], [27, 2], [104, 1], [105, 1], [200, 1], [832, 1]])
 def test_giant_rows(fanouts):
     indptr, indices = _two_hubs()
     N = len(indptr) - 1
