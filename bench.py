@@ -138,8 +138,9 @@ def main():
     G = args.group
     n_super = (n_batches + G - 1) // G
     # default: five epochs for a workload with a training set (each epoch its own seed order),
-    # else 100 super-batches (30 with a host-resident table)
-    steps = args.steps or (5 * n_super if cfg.n_train else min(n_super, 30 if cfg.host_features else 100))
+    # else 100 super-batches (30 with a host-resident table), wrapping round a short seed order
+    # with a fresh batch seed per step
+    steps = args.steps or (5 * n_super if cfg.n_train else (30 if cfg.host_features else 100))
     # seed order of each epoch the steps reach, made before any timing
     orders = [order] + [synth.epoch_seed_order(cfg, e, device=dev).contiguous()
                         for e in range(1, (steps + n_super - 1) // n_super)]
