@@ -172,8 +172,8 @@ def main():
     P = P if P > 1 else 0
     # streams 0..S-1 (0: the default stream) time the single-stream regions and the kernels; the
     # pipelined headline has streams S..S+P-1 of its own, so a kernel trace separates the two
-    wss = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
-           for _ in range(S + P)]
+    wss = [torch.empty(gm.gnn_minibatch_workspace_size(caps, cfg.num_nodes, G, cfg.d),
+                       dtype=torch.uint8, device=dev) for _ in range(S + P)]
     streams = [None] + [torch.cuda.Stream(device=dev) for _ in range(S + P - 1)]
     outs = [{} for _ in range(S + P)]   # per stream: one output set per (position, seed count)
 
@@ -292,6 +292,9 @@ def main():
     n_minibatches = sum(len(batch_range(b % n_super)) for b in range(steps))
     batched = batched_gather(cfg, args.gather)
     launches = 1 if batched else G      # gather (and outermost-mean) launches per step
+    # shared outermost means: batched from a table in HBM without a cache, G > 1 (the workspace
+    # has room): one mean launch over the union frontier and one copy launch per step
+    shared = batched and not cfg.host_features and not cfg.cache_bytes and G > 1
     t_sample, t_gather, t_mean_outer, t_mean_rest, t_hash = (stages[:, i].sum() / 1e3 for i in range(5))
     kern = {
         "gather": (gb_bytes.sum() / t_gather / 1e9, t_gather / steps / launches * 1e3),
@@ -302,11 +305,18 @@ def main():
     ga_frac = (gb_bytes.sum() + mean_all.sum()) / (t_gather + t_mean_outer + t_mean_rest) / 1e9 / HBM_PEAK_GBPS
     names = {"gather": kernel_instance("gather", cfg.d, cfg.ld, batched),
              "mean_outer": kernel_instance("mean", cfg.d, cfg.ld, batched)}
+    stage_kernels = {"gather": names["gather"],
+                     "mean_outer": (f"{names['mean_outer']} over the union frontier, then "
+                                    f"{names['gather']} copying its rows to the sub-batches"
+                                    if shared else names["mean_outer"])}
     other = "mean_outer" if dom == "gather" else "gather"
     from graph_mini_pipeline_amd.rocprof_summary import read_traffic
     counters = os.path.join(ROOT, "profiles", f"{cfg.name}_counters.txt")
     traffic = {"gather": read_traffic(counters, names["gather"]),
                "mean_outer": read_traffic(counters, names["mean_outer"] + "@outer")}
+    if shared and traffic["mean_outer"]:
+        cp = read_traffic(counters, names["gather"] + "@copy")
+        traffic["mean_outer"] = ({"bytes": traffic["mean_outer"]["bytes"] + cp["bytes"]} if cp else None)
     alg_per_launch = {"gather": gb_bytes.sum() / steps / launches,
                       "mean_outer": mean_outer.sum() / steps / launches}
 
@@ -337,7 +347,7 @@ def main():
                               "mean_outer_block": t_mean_outer / steps * 1e3,
                               "mean_other_blocks": t_mean_rest / steps * 1e3,
                               "sampling_kernel_only": t_hash / steps * 1e3},
-        "roofline": {"bound": "hbm", "kernel": names[dom],
+        "roofline": {"bound": "hbm", "kernel": stage_kernels[dom],
                      "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBPS,
                      "traffic": traffic[dom]["bytes"] if traffic[dom] else None,
@@ -348,7 +358,7 @@ def main():
                     "keys_per_step": keys / steps, "ms_per_step": t_hash / steps * 1e3,
                     "peak_derivation": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz / 19 VALU "
                                        "instructions per key"},
-        "other_kernel": {"name": names[other], "achieved_GBps": kern[other][0],
+        "other_kernel": {"name": stage_kernels[other], "achieved_GBps": kern[other][0],
                          "avg_launch_ms": kern[other][1], "launches_per_step": launches,
                          "algorithmic_bytes_per_launch": alg_per_launch[other],
                          "traffic": traffic[other]["bytes"] if traffic[other] else None},

@@ -83,6 +83,12 @@ struct Workspace {
     int32_t *f_pos;        // [G * Fs] position of each sub-batch destination in U_{l+1}
     int32_t *e_pos;        // [G * Es] position of each sub-batch sampled id in U_{l+1}
     uint32_t *bsum_dist;
+    // shared outermost means of a super-batch (only with a feature width): one mean row per node of
+    // the union frontier U_{K-1}, and each sub-batch destination's position in U_{K-1}
+    float *hU;             // [U_cap(K-1), ld_u]
+    int64_t ld_u;
+    int32_t *urank;        // [G * Fl]
+    int64_t Fl;
     int64_t P, Fs, Es;     // strides of the per-sub-batch arrays
     int64_t W, nbw, Wc, nbwc;
     int32_t mode;          // SuperMode
@@ -146,7 +152,9 @@ constexpr int64_t kBatchedGatherMinD = 128;
 constexpr int64_t kByteMapsMax = 1LL << 30;
 
 // mc: element-wise bound of every sub-batch's caps; G sub-batches relabelled the given way.
-Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) {
+// d > 0 (a super-batch): also room for the shared outermost means, after everything else, so the
+// other buffers sit at the same offsets either way.
+Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws, int64_t d = 0) {
     Workspace w{};
     Carver c{static_cast<char *>(ws)};
     const int K = mc.num_hops;
@@ -205,6 +213,12 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
         w.upos = c.take<int32_t>(static_cast<int64_t>(G) * w.P);
         w.f_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Fs);
         w.e_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Es);
+    }
+    if (d > 0 && G > 1 && K > 0) {
+        w.ld_u = (d + 3) / 4 * 4;
+        w.Fl = mc.frontier[K - 1];
+        w.hU = c.take<float>(union_cap(mc, K - 1, G, N) * w.ld_u);
+        w.urank = c.take<int32_t>(static_cast<int64_t>(G) * w.Fl);
     }
     w.bytes = c.off;
     return w;
@@ -336,7 +350,7 @@ template <typename FrontFn, typename CountFn, typename CapFn>
 gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, CapFn F_cap, int G,
                               int32_t k, uint64_t hs, int l, const gnn_caps &mc,
                               gnn_blocks *const *outs, const Workspace &w, const Opts &o,
-                              hipStream_t s, hipEvent_t *sev) {
+                              hipStream_t s, hipEvent_t *sev, bool last) {
     const int64_t Ucap = union_cap(mc, l, G, g.num_nodes);
     const int64_t uEcap = Ucap * k;
     RelabelArgs ru = relabel_args(g, w);
@@ -367,7 +381,8 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
         const int32_t nt = static_cast<int32_t>(dist_tiles(F_cap(gi, l)));
         da.sub[gi] = DistSub{front(gi, l), d_F(gi, l), F_cap(gi, l), nullptr, nullptr,
                              out.hop[l].indptr, out.hop[l].gid, nullptr, out.caps.edges[l],
-                             out.counts + 2 * l, tiles, nt};
+                             out.counts + 2 * l, tiles, nt,
+                             last && w.urank ? w.urank + gi * w.Fl : nullptr};
         tiles += nt;
     }
     da.ntiles = tiles;
@@ -459,7 +474,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         }
         if (!compact) {
             const gnn_status st = run_super_full_hop(g, front, d_F, F_cap, G, fanouts[l], hs, l, mc,
-                                                     outs, w, o, s, sev);
+                                                     outs, w, o, s, sev, l == K - 1);
             if (st != GNN_OK) return st;
             continue;
         }
@@ -493,7 +508,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
             da.sub[gi] = DistSub{front(gi, l), d_F(gi, l), F_cap(gi, l), w.upos + gi * w.P,
                                  w.f_pos + gi * w.Fs, out.hop[l].indptr, out.hop[l].gid,
                                  w.e_pos + gi * w.Es, out.caps.edges[l], out.counts + 2 * l,
-                                 tiles, nt};
+                                 tiles, nt, l == K - 1 && w.urank ? w.urank + gi * w.Fl : nullptr};
             tiles += nt;
         }
         da.ntiles = tiles;
@@ -590,6 +605,20 @@ gnn_status gnn_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t g
     if (group > 1) {
         const size_t bc = carve(*caps, num_nodes, group, kSuperCompact, nullptr).bytes;
         b = bc > b ? bc : b;
+    }
+    *out_bytes = b;
+    return GNN_OK;
+}
+
+gnn_status gnn_minibatch_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t group,
+                                        int64_t feature_dim, size_t *out_bytes) {
+    if (feature_dim < 1) return GNN_ERR_INVALID_ARG;
+    gnn_status st = gnn_workspace_size(caps, num_nodes, group, out_bytes);
+    if (st != GNN_OK || group == 1) return st;
+    size_t b = *out_bytes;
+    for (SuperMode m : {kSuperFull, kSuperCompact}) {
+        const size_t x = carve(*caps, num_nodes, group, m, nullptr, feature_dim).bytes;
+        b = x > b ? x : b;
     }
     *out_bytes = b;
     return GNN_OK;
@@ -787,14 +816,21 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     const SuperMode mode = super_mode(mc, g->num_nodes, group, o.flags);
     const Workspace need = carve(mc, g->num_nodes, group, mode, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
-    const Workspace w = carve(mc, g->num_nodes, group, mode, ws);
-    hipStream_t s = static_cast<hipStream_t>(stream);
     // How stages 2 and 3 run (below).  Batched by default for a host-resident table (G times as
     // many host-link reads in flight) and for rows wider than 512 bytes (the launch start-up and
     // drain of G gathers outweigh the cache reuse of interleaving); measured on the 602-, 128-,
     // 100- and 64-float workloads.
     const bool batched = !(o.flags & GNN_GATHER_INTERLEAVED) &&
                          ((o.flags & GNN_GATHER_BATCHED) || fs->on_host || d > kBatchedGatherMinD);
+    // Batched from a table in HBM without a cache, the outermost means read table rows by global
+    // id; with room in the workspace they are then taken once per node of the union frontier
+    // U_{K-1} and copied to the sub-batches that hold it (the G sub-batches share one seed, so a
+    // node's sampled neighbours, hence its mean, are the same in each).
+    const bool from_table = batched && !fs->on_host && fs->slot == nullptr;
+    const bool shared_means = from_table && group > 1 &&
+                              ws_bytes >= carve(mc, g->num_nodes, group, mode, nullptr, d).bytes;
+    const Workspace w = carve(mc, g->num_nodes, group, mode, ws, shared_means ? d : 0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t *ev = nullptr;
     if (timer) {
         if (timer->cursor >= timer->n_records) return GNN_ERR_CAPACITY;
@@ -815,10 +851,8 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     // sub-batch's gather in one launch, then every outermost mean in one launch.  Interleaved: per
     // sub-batch, so the mean reads X while it is still in the caches.
     if (batched) {
-        // With the table in HBM and no cache, the outermost means read the table rows of the
-        // sampled global ids: the sub-batches then share one copy of every row they have in common
-        // instead of one per sub-batch's X, so repeated rows hit the caches.
-        const bool from_table = !fs->on_host && fs->slot == nullptr;
+        // From the table, the sub-batches share one copy of every row they have in common instead
+        // of one per sub-batch's X, so repeated rows hit the caches.
         GatherBatchArgs ga{};
         ga.nseg = group;
         ga.table = fs->table;
@@ -847,8 +881,35 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         }
         GNN_TRY_HIP(launch_gather_batch(ga, rows_cap, s));
         if (ev) GNN_TRY_HIP(hipEventRecord(ev[2], s));
-        GNN_TRY_HIP(launch_mean(jobs, group, from_table ? fs->ld : outs[0].ld_h, outs[0].ld_h, d,
-                                fanouts[K - 1], w.status, s));
+        if (shared_means) {
+            // the union block of the last hop: destinations U_{K-1} (in U order), global ids
+            const int64_t Ucap = union_cap(mc, K - 1, group, g->num_nodes);
+            const int64_t *d_U = w.d_U + (w.mode == kSuperCompact ? K - 1 : 0);
+            const MeanJob uj{w.u_indptr, w.u_gid, Ucap * fanouts[K - 1], d_U, Ucap, fs->table,
+                             fs->num_nodes, w.hU};
+            GNN_TRY_HIP(launch_mean(&uj, 1, fs->ld, w.ld_u, d, fanouts[K - 1], w.status, s));
+            // sub-batch destination i takes the row of its union position
+            GatherBatchArgs cp{};
+            cp.nseg = group;
+            cp.table = w.hU;
+            cp.ld = w.ld_u;
+            cp.d = static_cast<int32_t>(d);
+            cp.num_rows = Ucap;
+            cp.ld_out = outs[0].ld_h;
+            cp.status = w.status;
+            int64_t cp_rows = 0;
+            for (int gi = 0; gi < group; ++gi) {
+                gnn_minibatch_out &mo = outs[gi];
+                const gnn_caps &c = mo.blocks.caps;
+                const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
+                cp.seg[gi] = GatherSeg{w.urank + gi * w.Fl, d_n, c.frontier[K - 1], mo.h[K - 1]};
+                cp_rows += c.frontier[K - 1];
+            }
+            GNN_TRY_HIP(launch_gather_batch(cp, cp_rows, s));
+        } else {
+            GNN_TRY_HIP(launch_mean(jobs, group, from_table ? fs->ld : outs[0].ld_h, outs[0].ld_h, d,
+                                    fanouts[K - 1], w.status, s));
+        }
         if (ev) GNN_TRY_HIP(hipEventRecord(ev[1 + 2 * group], s));
     } else {
         for (int gi = 0; gi < group; ++gi) {

@@ -222,6 +222,7 @@ struct DistSub {
     int64_t *d_E;
     int32_t tile0;  // first tile of this sub-batch in the launch
     int32_t ntile;
+    int32_t *urank; // optional out [F]: position of each destination in U_l (-1: none)
 };
 
 struct DistArgs {

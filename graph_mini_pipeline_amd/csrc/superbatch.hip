@@ -35,11 +35,12 @@ __device__ __forceinline__ int32_t union_rank(const DistArgs &a, int32_t v) {
 // U_{l+1} (-1 and an empty row for a destination without a union position: an invalid seed,
 // already reported by the union marking).
 __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, int64_t i,
-                                          int64_t &lo, int32_t &c, int32_t &next_pos) {
+                                          int64_t &lo, int32_t &c, int32_t &next_pos,
+                                          int32_t &r) {
     lo = 0;
     c = 0;
     next_pos = -1;
-    int32_t r;
+    r = -1;
     if (S.upos) {
         r = S.upos[i];
     } else {
@@ -51,6 +52,7 @@ __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, i
     const int64_t nU = load_count(a.d_U, a.U_cap);
     if (r >= nU) {
         set_status(a.status, GNN_ERR_INTERNAL);
+        r = -1;
         return;
     }
     int64_t l0 = a.u_indptr[r], l1 = a.u_indptr[r + 1];
@@ -88,10 +90,11 @@ __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
     const int64_t F = load_count(S.d_F, S.F_cap);
     const int64_t i = static_cast<int64_t>(t - S.tile0) * kDistTile + threadIdx.x;
     int64_t lo;
-    int32_t c = 0, np;
+    int32_t c = 0, np, r;
     if (i < F) {
-        union_row(a, S, i, lo, c, np);
+        union_row(a, S, i, lo, c, np, r);
         if (S.f_pos) S.f_pos[i] = np;
+        if (S.urank) S.urank[i] = r;
     }
     const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
     if (threadIdx.x == 0) a.bsum[t] = sum;
@@ -136,8 +139,8 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
     if (threadIdx.x < kDistTile) {
         const int64_t i = static_cast<int64_t>(lt) * kDistTile + threadIdx.x;
         int64_t lo = 0;
-        int32_t c = 0, np;
-        if (i < F) union_row(a, S, i, lo, c, np);
+        int32_t c = 0, np, r;
+        if (i < F) union_row(a, S, i, lo, c, np, r);
         const uint32_t inc = wave_inclusive_scan(static_cast<uint32_t>(c));
         const uint32_t o = inc - static_cast<uint32_t>(c);
         s_item_off[threadIdx.x] = o;

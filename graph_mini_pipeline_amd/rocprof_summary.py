@@ -7,8 +7,9 @@ counter summary into per-launch memory traffic.
 Counter summaries hold one machine-readable line per kernel:
     counters <kernel> dispatches=<n> fetch_kib=<avg> write_kib=<avg> source=<file> sha256=<hash>
 (mean-aggregation kernels as <kernel>@outer for the outermost block, which follows the gather,
-and <kernel>@inner for the others) and one for the calibration copy (k_copy_probe, a plain copy of
-known size):
+and <kernel>@inner for the others; a gather that follows a mean, copying a super-batch's shared
+outermost means to its sub-batches, as <kernel>@copy) and one for the calibration copy
+(k_copy_probe, a plain copy of known size):
     calibration copy_bytes=<B> fetch_kib=<avg> write_kib=<avg>
 FETCH_SIZE and WRITE_SIZE are scaled by (copy bytes) / (counter reading of the copy) each.
 """
@@ -58,6 +59,17 @@ def source_hash(rel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def _role(name: str, prev: str) -> str:
+    """A dispatch's name with its role on the stream: a mean right after a gather is the outermost
+    block (@outer), other means are inner blocks (@inner); a gather right after a mean copies the
+    shared outermost means of a super-batch out to its sub-batches (@copy)."""
+    if name.startswith("k_mean"):
+        return name + ("@outer" if prev.startswith("k_gather") else "@inner")
+    if name.startswith("k_gather") and prev.startswith("k_mean"):
+        return name + "@copy"
+    return name
+
+
 def trace_summary(trace_csv: str, command: str) -> str:
     """Per-kernel duration statistics of the library's dispatches on the stream of its first
     dispatch (the stream the benchmark's headline and per-kernel timings run on; dispatches on
@@ -73,9 +85,7 @@ def trace_summary(trace_csv: str, command: str) -> str:
             others += 1
             continue
         name = short_name(r["Kernel_Name"])
-        key = name
-        if name.startswith("k_mean"):   # outermost block (right after the gather) or an inner one
-            key = name + ("@outer" if prev.startswith("k_gather") else "@inner")
+        key = _role(name, prev)
         per[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         prev = name
     out = [f"# rocprofv3 --kernel-trace summary (library kernels on stream {stream}, the stream of "
@@ -99,9 +109,7 @@ def _per_kernel(path: str, counter: str) -> Dict[str, list]:
     prev = ""
     for r in rows:
         name = short_name(r["Kernel_Name"])
-        key = name
-        if name.startswith("k_mean"):
-            key = name + ("@outer" if prev.startswith("k_gather") else "@inner")
+        key = _role(name, prev)
         d[(key, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
         prev = name
     return d

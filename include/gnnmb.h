@@ -149,6 +149,20 @@ gnn_status gnn_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t g
                               size_t *out_bytes);
 
 /*
+ * Workspace for gnn_minibatch with room for shared outermost means (feature_dim = d of the
+ * feature store, >= 1): at least gnn_workspace_size, plus, for group > 1, one row of d floats per
+ * node of the largest possible union frontier of the last hop and one position per sub-batch
+ * destination.  With such a workspace, a super-batch whose gathers are batched from a table in
+ * device memory without a cache (the default for rows of more than 128 floats) takes each
+ * outermost mean once per node of the union of the sub-batches' last frontiers -- the sub-batches
+ * share one seed, so a node's sampled neighbours and mean are the same in each -- and copies it to
+ * every sub-batch that holds the node (results identical).  A smaller workspace (>=
+ * gnn_workspace_size) takes the means per sub-batch.  Writes *out_bytes (host).
+ */
+gnn_status gnn_minibatch_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t group,
+                                        int64_t feature_dim, size_t *out_bytes);
+
+/*
  * k-hop neighbour sampling and relabel for one batch (GARDEN Sec. II.B, Fig. 1; Sec. IV.C; the
  * draw is the bottom-k of per-edge SplitMix64 keys):
  *   for l = 1..K, destinations V_{l-1} (V_0 = seeds, caller order):
@@ -254,7 +268,8 @@ typedef struct gnn_minibatch_out {
  *   All sub-batches use the one seed64, so a node shared by two sub-batches at the same hop has
  *   the same sample in both; each sub-batch's outputs equal a separate run with that seed64.
  *   outs: host [group]; outs[g].blocks.caps.n_seeds = batch_ptr[g+1] - batch_ptr[g].
- *   ws: ws_bytes >= gnn_workspace_size(caps >= every sub-batch's caps, N, group).
+ *   ws: ws_bytes >= gnn_workspace_size(caps >= every sub-batch's caps, N, group), or
+ *   gnn_minibatch_workspace_size(..., d) for shared outermost means.
  *   timer: NULL, or a timer that records the stage boundaries of this call (gnn_timer_*).
  * Errors: as gnn_sample_khop and gnn_gather_features.
  */

@@ -485,3 +485,23 @@ def test_gather_both_flags_rejected(tiny):
         run_minibatch(device_graph(indptr, indices), _store(x), order[:20], [3], 1,
                       group_ptr=[0, 10, 20], opts=_BothGather())
     assert e.value.status == gm.GNN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("mode", SUPER_MODES)
+@pytest.mark.parametrize("fanouts", [[7], [12, 6], [12, 6, 3]])
+@pytest.mark.parametrize("shared", [True, False])
+def test_shared_outer_means(tiny, mode, fanouts, shared):
+    # batched gathers from a table in HBM: with a large enough workspace the outermost means are
+    # taken once per node of the union frontier and copied out; sub-batches overlap, one is empty
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    parts = [order[i * 50:(i + 1) * 50 + 20] for i in range(6)] + [order[:0]] + [order[100:180]]
+    seeds = np.concatenate(parts)
+    ptr = np.concatenate([[0], np.cumsum([len(p) for p in parts])]).tolist()
+    outs, st = run_minibatch(dg, fs, seeds, fanouts, 808, group_ptr=ptr, shared_means=shared,
+                             opts=gm.Options(superbatch=mode, gather="batched"))
+    assert st == gm.GNN_OK
+    for g in range(len(parts)):
+        ref = oracle.minibatch(indptr, indices, x, parts[g], fanouts, 808)
+        compare_with_oracle(outs[g], ref, cfg.d)

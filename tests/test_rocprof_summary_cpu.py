@@ -41,3 +41,18 @@ def test_read_traffic_stale_source_is_none(tmp_path):
                    "sha256=0000000000000000\ncalibration copy_bytes=1073741824 fetch_kib=1.0 write_kib=1.0\n")
     assert rs.read_traffic(str(out), "k_sample") is None
     assert rs.read_traffic(str(tmp_path / "missing.txt"), "k_sample") is None
+
+
+def test_copy_after_mean_is_tagged(tmp_path):
+    seq = [("k_gather_batch<64, 3, 8>", 200, 1000.0), ("k_mean_v5<64, 3, 4>", 300, 500.0),
+           ("k_gather_batch<64, 3, 8>", 100, 30.0), ("k_mean_v5<64, 3, 4>", 400, 50.0),
+           ("k_copy_probe", 500, 524288.0)]
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(f, "FETCH_SIZE", seq)
+    _counter_csv(w, "WRITE_SIZE", seq)
+    out = tmp_path / "c.txt"
+    out.write_text(rs.counter_summary("t", str(f), str(w), "cmd"))
+    assert rs.read_traffic(str(out), "k_gather_batch<64, 3, 8>")["fetch_bytes"] == 1000.0 * 1024 * 2
+    assert rs.read_traffic(str(out), "k_gather_batch<64, 3, 8>@copy")["fetch_bytes"] == 30.0 * 1024 * 2
+    # the mean after the copy is an inner block
+    assert rs.read_traffic(str(out), "k_mean_v5<64, 3, 4>@inner")["fetch_bytes"] == 50.0 * 1024 * 2
