@@ -60,12 +60,15 @@ def source_hash(rel: str) -> str:
 
 
 def _role(name: str, prev: str) -> str:
-    """A dispatch's name with its role on the stream: a mean right after a gather is the outermost
-    block (@outer), other means are inner blocks (@inner); a gather right after a mean copies the
-    shared outermost means of a super-batch out to its sub-batches (@copy)."""
+    """A dispatch's name with its role on the stream (prev: the previous dispatch's name with its
+    role): a mean right after a gather is the outermost block (@outer), other means are inner
+    blocks (@inner); a batched gather right after an outermost mean copies the shared outermost
+    means of a super-batch out to its sub-batches (@copy; per-sub-batch gathers, k_gather_rows,
+    alternate with outermost means and are never copies)."""
     if name.startswith("k_mean"):
-        return name + ("@outer" if prev.startswith("k_gather") else "@inner")
-    if name.startswith("k_gather") and prev.startswith("k_mean"):
+        outer = prev.startswith("k_gather") and not prev.endswith("@copy")
+        return name + ("@outer" if outer else "@inner")
+    if name.startswith("k_gather_batch") and prev.startswith("k_mean") and prev.endswith("@outer"):
         return name + "@copy"
     return name
 
@@ -84,10 +87,9 @@ def trace_summary(trace_csv: str, command: str) -> str:
         if r["Stream_Id"] != stream:
             others += 1
             continue
-        name = short_name(r["Kernel_Name"])
-        key = _role(name, prev)
+        key = _role(short_name(r["Kernel_Name"]), prev)
         per[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-        prev = name
+        prev = key
     out = [f"# rocprofv3 --kernel-trace summary (library kernels on stream {stream}, the stream of "
            f"the first library dispatch; {others} dispatches on other streams left out)",
            f"# command: {command}",
@@ -108,10 +110,9 @@ def _per_kernel(path: str, counter: str) -> Dict[str, list]:
     d = defaultdict(list)
     prev = ""
     for r in rows:
-        name = short_name(r["Kernel_Name"])
-        key = _role(name, prev)
+        key = _role(short_name(r["Kernel_Name"]), prev)
         d[(key, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
-        prev = name
+        prev = key
     return d
 
 

@@ -56,3 +56,17 @@ def test_copy_after_mean_is_tagged(tmp_path):
     assert rs.read_traffic(str(out), "k_gather_batch<64, 3, 8>@copy")["fetch_bytes"] == 30.0 * 1024 * 2
     # the mean after the copy is an inner block
     assert rs.read_traffic(str(out), "k_mean_v5<64, 3, 4>@inner")["fetch_bytes"] == 50.0 * 1024 * 2
+
+
+def test_interleaved_gathers_are_not_copies(tmp_path):
+    seq = [("k_gather_rows<32, 1, 4>", 200, 100.0), ("k_mean_v5<32, 1, 4>", 300, 50.0),
+           ("k_gather_rows<32, 1, 4>", 200, 100.0), ("k_mean_v5<32, 1, 4>", 300, 50.0),
+           ("k_mean_v5<32, 1, 4>", 400, 5.0), ("k_copy_probe", 500, 524288.0)]
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(f, "FETCH_SIZE", seq)
+    _counter_csv(w, "WRITE_SIZE", seq)
+    out = tmp_path / "c.txt"
+    out.write_text(rs.counter_summary("t", str(f), str(w), "cmd"))
+    assert rs.read_traffic(str(out), "k_gather_rows<32, 1, 4>@copy") is None
+    assert rs.read_traffic(str(out), "k_mean_v5<32, 1, 4>@outer")["fetch_bytes"] == 50.0 * 1024 * 2
+    assert rs.read_traffic(str(out), "k_mean_v5<32, 1, 4>@inner")["fetch_bytes"] == 5.0 * 1024 * 2
