@@ -63,11 +63,8 @@ def kernel_instance(kind: str, d: int, ld: int, batched: bool) -> str:
 
 
 def batched_gather(cfg, layout: str) -> bool:
-    """The library's gather layout: batched for a host-resident table or rows of more than 128
-    floats unless forced either way."""
-    if layout != "auto":
-        return layout == "batched"
-    return bool(cfg.host_features) or cfg.d > 128
+    """The library's gather layout: batched unless interleaving is asked for."""
+    return layout != "interleaved"
 
 
 def algorithmic_bytes(counts, n_seeds, d, K):

@@ -145,9 +145,6 @@ SuperMode super_mode(const gnn_caps &mc, int64_t N, int G, uint32_t flags) {
     return 3 * static_cast<int64_t>(G + 1) * W >= max_union_edges(mc, N, G) ? kSuperCompact : kSuperFull;
 }
 
-// Row width (floats) above which gnn_minibatch batches its gathers by default.
-constexpr int64_t kBatchedGatherMinD = 128;
-
 // Largest byte-map region of a super-batch's sub-batch relabels (beyond it, marks stay atomic).
 constexpr int64_t kByteMapsMax = 1LL << 30;
 
@@ -816,12 +813,11 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     const SuperMode mode = super_mode(mc, g->num_nodes, group, o.flags);
     const Workspace need = carve(mc, g->num_nodes, group, mode, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
-    // How stages 2 and 3 run (below).  Batched by default for a host-resident table (G times as
-    // many host-link reads in flight) and for rows wider than 512 bytes (the launch start-up and
-    // drain of G gathers outweigh the cache reuse of interleaving); measured on the 602-, 128-,
-    // 100- and 64-float workloads.
-    const bool batched = !(o.flags & GNN_GATHER_INTERLEAVED) &&
-                         ((o.flags & GNN_GATHER_BATCHED) || fs->on_host || d > kBatchedGatherMinD);
+    // How stages 2 and 3 run (below).  Batched unless interleaving is asked for: one launch's
+    // start-up and drain instead of G, G times as many host-link reads in flight for a
+    // host-resident table, and (with a table in HBM) the shared outermost means; measured faster
+    // or equal on the 602-, 128-, 100- and 64-float workloads.
+    const bool batched = !(o.flags & GNN_GATHER_INTERLEAVED);
     // Batched from a table in HBM without a cache, the outermost means read table rows by global
     // id; with room in the workspace they are then taken once per node of the union frontier
     // U_{K-1} and copied to the sub-batches that hold it (the G sub-batches share one seed, so a

@@ -61,13 +61,14 @@ typedef void *gnn_stream; /* hipStream_t */
 #define GNN_SUPERBATCH_FULL 2u
 #define GNN_SUPERBATCH_COMPACT 4u
 /* How gnn_minibatch gathers X and takes the outermost mean (results are identical; at most one may
- * be set; by default BATCHED for a host-resident table or rows of more than 128 floats, else
- * INTERLEAVED):
+ * be set; BATCHED is the default):
  *   INTERLEAVED: per sub-batch, the gather then the mean, which reads X while it is still in the
  *                caches;
- *   BATCHED:     every sub-batch's gather in one launch, then every outermost mean in one launch
+ *   BATCHED:     every sub-batch's gather in one launch, then the outermost means in one launch
  *                (one launch's start-up and drain instead of G; G times as many host-link reads
- *                in flight for a host-resident table). */
+ *                in flight for a host-resident table; with a table in device memory and no cache
+ *                the means read the table rows, shared by the sub-batches -- once per node of the
+ *                union frontier with a workspace from gnn_minibatch_workspace_size). */
 #define GNN_GATHER_INTERLEAVED 8u
 #define GNN_GATHER_BATCHED 16u
 
