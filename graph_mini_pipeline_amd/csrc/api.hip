@@ -62,12 +62,12 @@ struct Carver {
 
 struct Workspace {
     int32_t *status;       // [1] at offset 0
-    uint32_t *totals;      // [5] classification totals
+    uint32_t *totals;      // [kCols] classification totals
     int64_t *d_U;          // [K + 1] |U_l| of a super-batch
     int64_t *d_uE;         // [K] edges of each union block
     int32_t *packed;       // [FU_max]
     int32_t *lists;        // [4 FU_max]
-    uint32_t *bsum;        // [5 nb_max]
+    uint32_t *bsum;        // [kCols nb_max]
     uint32_t *bitmaps;     // [W] over all node ids, then G more of W words (full super-batch
                            // relabel) or G of Wc words (compact super-batch relabel)
     uint32_t *wprefix;     // same layout
@@ -189,7 +189,7 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws, 
     w.d_uE = cnt ? cnt + 16 : nullptr;
     w.packed = c.take<int32_t>(FU);
     w.lists = c.take<int32_t>(4 * FU);
-    w.bsum = c.take<uint32_t>(5 * nb_max);
+    w.bsum = c.take<uint32_t>(kCols * nb_max);
     w.bitmaps = c.take<uint32_t>(words);
     w.wprefix = c.take<uint32_t>(words);
     w.bsum_w = c.take<uint32_t>(tiles);

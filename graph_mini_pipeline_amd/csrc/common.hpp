@@ -117,6 +117,11 @@ inline unsigned grid_for(int64_t items, int per_block, unsigned max_blocks) {
 // Degree classes of the sampler.
 enum : int32_t { kFull = 0, kGroup = 1, kWave = 2, kBlock = 3, kNumClasses = 4 };
 
+// Degree buckets of the one-wavefront class, and the classification's per-block columns (edges,
+// then FULL, GROUP, the buckets and BLOCK).
+constexpr int kWaveBuckets = 6;
+constexpr int kCols = 4 + kWaveBuckets;
+
 // Candidate capacities per class (LDS) and the fanout each supports (capacity >= 4 * fanout).
 // A sampler workgroup holds kBlockCap candidates of 12 bytes (key, position): 3328 of them keep it
 // under 40 KB, so four workgroups (32 wavefronts, the register-file limit) fit one CU's 160 KB.
@@ -143,10 +148,10 @@ struct HopArgs {
     int32_t *blk_gid;       // [E_cap]
     int64_t E_cap;
     int64_t *d_E;           // receives |E_l|
-    int32_t *packed;        // [F_cap] (c << 2) | class
-    int32_t *lists;         // [4 * F_cap] class work-lists
-    uint32_t *bsum;         // [5 * nb] per-block edge counts then the four class counts
-    uint32_t *totals;       // [5] |E_l| then the four class sizes
+    int32_t *packed;        // [F_cap] (c << 4) | category
+    int32_t *lists;         // [4 * F_cap] class work-lists (the WAVE list by degree bucket)
+    uint32_t *bsum;         // [kCols * nb] per-block edge counts then the category counts
+    uint32_t *totals;       // [kCols] |E_l| then the category sizes
     uint32_t *clear_ptr;    // words the classification clears (the relabel bitmap of this hop)
     int64_t clear_n;
     int32_t *status;

@@ -36,8 +36,37 @@ __device__ __forceinline__ int32_t node_class(int64_t deg, int k, int group_max,
     return kBlock;
 }
 
+// Classification categories: FULL, GROUP, the WAVE class split into kWaveBuckets degree buckets
+// listed largest first (bucket b holds degrees in [2^(13-b), 2^(14-b)), the last also all smaller
+// ones and the first all larger ones), BLOCK.  The WAVE list is ordered by bucket, so wavefronts
+// that walk it with a snake stride take the largest rows first and balance their loads.
+constexpr int kCats = 3 + kWaveBuckets;       // FULL, GROUP, WAVE buckets, BLOCK
+constexpr int kCatBlock = kCats - 1;
+static_assert(kCols == 1 + kCats, "edges, then one column per category");
+__device__ __forceinline__ int32_t node_cat(int32_t cls, int64_t deg) {
+    if (cls == kFull) return 0;
+    if (cls == kGroup) return 1;
+    if (cls == kBlock) return kCatBlock;
+    const int lg = 63 - __clzll(static_cast<unsigned long long>(deg));   // floor(log2 deg)
+    int b = 13 - lg;
+    b = b < 0 ? 0 : (b >= kWaveBuckets ? kWaveBuckets - 1 : b);
+    return 2 + b;
+}
+__device__ __forceinline__ int32_t cat_class(int32_t cat) {
+    return cat == 0 ? kFull : (cat == 1 ? kGroup : (cat == kCatBlock ? kBlock : kWave));
+}
+// Nodes of a class (totals: edges, then the categories' sizes).
+__device__ __forceinline__ int64_t class_total(const uint32_t *totals, int32_t cls) {
+    if (cls == kFull) return totals[1];
+    if (cls == kGroup) return totals[2];
+    if (cls == kBlock) return totals[1 + kCatBlock];
+    int64_t n = 0;
+    for (int b = 0; b < kWaveBuckets; ++b) n += totals[3 + b];
+    return n;
+}
+
 __global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) {
-    __shared__ uint32_t red[5][kClassifyThreads / 64];
+    __shared__ uint32_t red[kCols][kClassifyThreads / 64];
     // The relabel bitmap of this hop is cleared here, long before the relabel reads it.
     for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < a.clear_n;
          t += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -45,7 +74,9 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) 
     const int64_t F = load_count(a.d_F, a.F_cap);
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kClassifyTile +
                          static_cast<int64_t>(threadIdx.x) * kClassifyItems;
-    uint32_t csum = 0, cc[4] = {0, 0, 0, 0};
+    uint32_t vals[kCols];
+#pragma unroll
+    for (int t = 0; t < kCols; ++t) vals[t] = 0;
 #pragma unroll
     for (int q = 0; q < kClassifyItems; ++q) {
         const int64_t i = base + q;
@@ -58,21 +89,21 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) 
                 deg = row_ptr(a.indptr, a.ib, v + 1) - row_ptr(a.indptr, a.ib, v);
             }
             const int32_t c = deg <= a.k ? static_cast<int32_t>(deg) : a.k;
-            const int32_t cls = node_class(deg, a.k, a.group_max, a.wave_max);
-            a.packed[i] = (c << 2) | cls;
-            csum += static_cast<uint32_t>(c);
-            cc[cls] += 1;
+            const int32_t cat = node_cat(node_class(deg, a.k, a.group_max, a.wave_max), deg);
+            a.packed[i] = (c << 4) | cat;
+            vals[0] += static_cast<uint32_t>(c);
+#pragma unroll
+            for (int t = 0; t < kCats; ++t) vals[1 + t] += cat == t;
         }
     }
     const int lane = lane_id(), w = threadIdx.x >> 6;
-    uint32_t vals[5] = {csum, cc[0], cc[1], cc[2], cc[3]};
 #pragma unroll
-    for (int t = 0; t < 5; ++t) {
+    for (int t = 0; t < kCols; ++t) {
         const uint32_t s = wave_sum(vals[t]);
         if (lane == 0) red[t][w] = s;
     }
     __syncthreads();
-    if (threadIdx.x < 5) {
+    if (threadIdx.x < kCols) {
         uint32_t s = 0;
         for (int i = 0; i < kClassifyThreads / 64; ++i) s += red[threadIdx.x][i];
         a.bsum[static_cast<int64_t>(threadIdx.x) * a.nb + blockIdx.x] = s;
@@ -84,7 +115,7 @@ __global__ __launch_bounds__(1024) void k_classify_scan(HopArgs a) {
     __shared__ uint32_t smem[16];
     const int nb = a.nb;
     const int per = (nb + 1023) / 1024;
-    for (int col = 0; col < 5; ++col) {
+    for (int col = 0; col < kCols; ++col) {
         uint32_t *arr = a.bsum + static_cast<int64_t>(col) * nb;
         const int b0 = threadIdx.x * per;
         uint32_t local = 0;
@@ -108,21 +139,25 @@ __global__ __launch_bounds__(1024) void k_classify_scan(HopArgs a) {
 // otherwise k_classify_scan has already turned them into offsets and totals.
 __global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a, int32_t pre_scanned) {
     __shared__ uint32_t sm_c[kClassifyThreads / 64];
-    __shared__ uint64_t sm_k[kClassifyThreads / 64];
-    __shared__ uint32_t s_off[5];
-    __shared__ uint32_t s_tot[5];
-    __shared__ uint32_t s_red[10][kClassifyThreads / 64];
+    __shared__ uint64_t sm_k0[kClassifyThreads / 64];
+    __shared__ uint64_t sm_k1[kClassifyThreads / 64];
+    __shared__ uint32_t s_off[kCols];
+    __shared__ uint32_t s_tot[kCols];
+    __shared__ uint32_t s_red[2 * kCols][kClassifyThreads / 64];
+    __shared__ uint32_t s_base[kCats];   // start of each category in its class list
     const int64_t F = load_count(a.d_F, a.F_cap);
     if (pre_scanned) {
-        if (threadIdx.x < 5) {
+        if (threadIdx.x < kCols) {
             s_off[threadIdx.x] = a.bsum[static_cast<int64_t>(threadIdx.x) * a.nb + blockIdx.x];
             s_tot[threadIdx.x] = a.totals[threadIdx.x];
         }
     } else {
-        uint32_t before[5] = {0, 0, 0, 0, 0}, all[5] = {0, 0, 0, 0, 0};
+        uint32_t before[kCols], all[kCols];
+#pragma unroll
+        for (int col = 0; col < kCols; ++col) before[col] = all[col] = 0;
         for (int b = threadIdx.x; b < a.nb; b += blockDim.x) {
 #pragma unroll
-            for (int col = 0; col < 5; ++col) {
+            for (int col = 0; col < kCols; ++col) {
                 const uint32_t x = a.bsum[static_cast<int64_t>(col) * a.nb + b];
                 all[col] += x;
                 if (b < static_cast<int>(blockIdx.x)) before[col] += x;
@@ -130,24 +165,33 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a
         }
         const int lane = lane_id(), w = threadIdx.x >> 6;
 #pragma unroll
-        for (int col = 0; col < 5; ++col) {
+        for (int col = 0; col < kCols; ++col) {
             const uint32_t s0 = wave_sum(before[col]);
             const uint32_t s1 = wave_sum(all[col]);
             if (lane == 0) {
                 s_red[col][w] = s0;
-                s_red[5 + col][w] = s1;
+                s_red[kCols + col][w] = s1;
             }
         }
         __syncthreads();
-        if (threadIdx.x < 10) {
+        if (threadIdx.x < 2 * kCols) {
             uint32_t s = 0;
             for (int i = 0; i < kClassifyThreads / 64; ++i) s += s_red[threadIdx.x][i];
-            if (threadIdx.x < 5) s_off[threadIdx.x] = s;
-            else s_tot[threadIdx.x - 5] = s;
+            if (threadIdx.x < kCols) s_off[threadIdx.x] = s;
+            else s_tot[threadIdx.x - kCols] = s;
         }
     }
     __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x < 5) {
+    if (threadIdx.x == 0) {
+        // the WAVE buckets follow one another in the WAVE list, largest degrees first
+        uint32_t run = 0;
+        for (int c = 0; c < kCats; ++c) {
+            const bool wave = cat_class(c) == kWave;
+            s_base[c] = wave ? run : 0u;
+            if (wave) run += s_tot[1 + c];
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < kCols) {
         const uint32_t total = s_tot[threadIdx.x];
         if (!pre_scanned) a.totals[threadIdx.x] = total;
         if (threadIdx.x == 0) {
@@ -161,31 +205,41 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a
                          static_cast<int64_t>(threadIdx.x) * kClassifyItems;
     int32_t pk[kClassifyItems];
     uint32_t csum = 0;
-    uint64_t kc = 0;  // four 16-bit class counters
+    uint64_t kc0 = 0, kc1 = 0;  // categories 0..3 in 16-bit counters, 4..8 in 12-bit counters
 #pragma unroll
     for (int q = 0; q < kClassifyItems; ++q) {
         const int64_t i = base + q;
         pk[q] = i < F ? a.packed[i] : -1;
         if (pk[q] >= 0) {
-            csum += static_cast<uint32_t>(pk[q] >> 2);
-            kc += 1ull << (16 * (pk[q] & 3));
+            csum += static_cast<uint32_t>(pk[q] >> 4);
+            const int cat = pk[q] & 15;
+            if (cat < 4) kc0 += 1ull << (16 * cat);
+            else kc1 += 1ull << (12 * (cat - 4));
         }
     }
     uint32_t ctot;
-    uint64_t ktot;
+    uint64_t ktot0, ktot1;
     uint32_t coff = block_exclusive_scan<uint32_t, kClassifyThreads>(csum, &ctot, sm_c);
-    uint64_t koff = block_exclusive_scan<uint64_t, kClassifyThreads>(kc, &ktot, sm_k);
+    uint64_t koff0 = block_exclusive_scan<uint64_t, kClassifyThreads>(kc0, &ktot0, sm_k0);
+    uint64_t koff1 = block_exclusive_scan<uint64_t, kClassifyThreads>(kc1, &ktot1, sm_k1);
     coff += s_off[0];
 #pragma unroll
     for (int q = 0; q < kClassifyItems; ++q) {
         if (pk[q] < 0) continue;
         const int64_t i = base + q;
-        const int32_t cls = pk[q] & 3;
+        const int32_t cat = pk[q] & 15;
         a.blk_indptr[i] = static_cast<int32_t>(coff);
-        coff += static_cast<uint32_t>(pk[q] >> 2);
-        const uint32_t r = static_cast<uint32_t>((koff >> (16 * cls)) & 0xFFFF);
-        koff += 1ull << (16 * cls);
-        a.lists[static_cast<int64_t>(cls) * a.F_cap + s_off[1 + cls] + r] = static_cast<int32_t>(i);
+        coff += static_cast<uint32_t>(pk[q] >> 4);
+        uint32_t r;
+        if (cat < 4) {
+            r = static_cast<uint32_t>((koff0 >> (16 * cat)) & 0xFFFF);
+            koff0 += 1ull << (16 * cat);
+        } else {
+            r = static_cast<uint32_t>((koff1 >> (12 * (cat - 4))) & 0xFFF);
+            koff1 += 1ull << (12 * (cat - 4));
+        }
+        a.lists[static_cast<int64_t>(cat_class(cat)) * a.F_cap + s_base[cat] + s_off[1 + cat] + r] =
+            static_cast<int32_t>(i);
     }
 }
 
@@ -497,7 +551,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_
     const uint64_t below = (1ull << lane) - 1ull;
     int bid = static_cast<int>(blockIdx.x);
     if (bid < nb_block) {
-        const int64_t n = a.totals[1 + kBlock];
+        const int64_t n = class_total(a.totals, kBlock);
         const int32_t *list = a.lists + static_cast<int64_t>(kBlock) * a.F_cap;
         for (int64_t item = bid; item < n; item += nb_block)
             sample_node_block(a, list[item], s_key, s_pos, &s_cnt);
@@ -505,12 +559,18 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_
     }
     bid -= nb_block;
     if (bid < nb_wave) {
-        const int64_t n = a.totals[1 + kWave];
+        // The list is ordered by degree bucket, largest first; wavefront w takes item w of even
+        // rounds and item W-1-w of odd ones (W wavefronts), which pairs large rows with small.
+        const int64_t n = class_total(a.totals, kWave);
         const int32_t *list = a.lists + static_cast<int64_t>(kWave) * a.F_cap;
-        for (int64_t item = static_cast<int64_t>(bid) * kWavesPerBlock + wv; item < n;
-             item += static_cast<int64_t>(nb_wave) * kWavesPerBlock)
-            sample_node_lanes<64, kWaveCap>(a, list[item], s_key + wv * kWaveCap,
-                                            s_pos + wv * kWaveCap, lane, ~0ull, below);
+        const int64_t W = static_cast<int64_t>(nb_wave) * kWavesPerBlock;
+        const int64_t w = static_cast<int64_t>(bid) * kWavesPerBlock + wv;
+        for (int64_t r0 = 0, round = 0; r0 < n; r0 += W, ++round) {
+            const int64_t item = r0 + ((round & 1) ? W - 1 - w : w);
+            if (item < n)
+                sample_node_lanes<64, kWaveCap>(a, list[item], s_key + wv * kWaveCap,
+                                                s_pos + wv * kWaveCap, lane, ~0ull, below);
+        }
         return;
     }
     bid -= nb_wave;
@@ -520,7 +580,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_
         const int grp = lane / G;
         const int slot = wv * (64 / G) + grp;
         const uint64_t gmask = ((1ull << G) - 1ull) << (grp * G);
-        const int64_t n = a.totals[1 + kGroup];
+        const int64_t n = class_total(a.totals, kGroup);
         const int32_t *list = a.lists + static_cast<int64_t>(kGroup) * a.F_cap;
         for (int64_t item = static_cast<int64_t>(bid) * SLOTS + slot; item < n;
              item += static_cast<int64_t>(nb_group) * SLOTS)
@@ -529,7 +589,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_
         return;
     }
     bid -= nb_group;
-    const int64_t n = a.totals[1 + kFull];
+    const int64_t n = class_total(a.totals, kFull);
     const int64_t nb_full = static_cast<int64_t>(gridDim.x) - nb_block - nb_wave - nb_group;
     for (int64_t t = static_cast<int64_t>(bid) * kBlockThreads + threadIdx.x; t < n;
          t += nb_full * kBlockThreads) {
