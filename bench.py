@@ -169,8 +169,8 @@ def main():
     P = P if P > 1 else 0
     # streams 0..S-1 (0: the default stream) time the single-stream regions and the kernels; the
     # pipelined headline has streams S..S+P-1 of its own, so a kernel trace separates the two
-    wss = [torch.empty(gm.gnn_minibatch_workspace_size(caps, cfg.num_nodes, G, cfg.d),
-                       dtype=torch.uint8, device=dev) for _ in range(S + P)]
+    wss = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
+           for _ in range(S + P)]
     streams = [None] + [torch.cuda.Stream(device=dev) for _ in range(S + P - 1)]
     outs = [{} for _ in range(S + P)]   # per stream: one output set per (position, seed count)
 
@@ -289,8 +289,8 @@ def main():
     n_minibatches = sum(len(batch_range(b % n_super)) for b in range(steps))
     batched = batched_gather(cfg, args.gather)
     launches = 1 if batched else G      # gather (and outermost-mean) launches per step
-    # shared outermost means: batched from a table in HBM without a cache, G > 1 (the workspace
-    # has room): one mean launch over the union frontier and one copy launch per step
+    # shared outermost means: batched from a table in HBM without a cache, G > 1: one mean launch
+    # over the union frontier, storing each node's mean to every sub-batch that holds it
     shared = batched and not cfg.host_features and not cfg.cache_bytes and G > 1
     t_sample, t_gather, t_mean_outer, t_mean_rest, t_hash = (stages[:, i].sum() / 1e3 for i in range(5))
     kern = {
@@ -303,17 +303,14 @@ def main():
     names = {"gather": kernel_instance("gather", cfg.d, cfg.ld, batched),
              "mean_outer": kernel_instance("mean", cfg.d, cfg.ld, batched)}
     stage_kernels = {"gather": names["gather"],
-                     "mean_outer": (f"{names['mean_outer']} over the union frontier, then "
-                                    f"{names['gather']} copying its rows to the sub-batches"
+                     "mean_outer": (f"{names['mean_outer']} over the union frontier, each row "
+                                    f"stored to every sub-batch that holds it"
                                     if shared else names["mean_outer"])}
     other = "mean_outer" if dom == "gather" else "gather"
     from graph_mini_pipeline_amd.rocprof_summary import read_traffic
     counters = os.path.join(ROOT, "profiles", f"{cfg.name}_counters.txt")
     traffic = {"gather": read_traffic(counters, names["gather"]),
                "mean_outer": read_traffic(counters, names["mean_outer"] + "@outer")}
-    if shared and traffic["mean_outer"]:
-        cp = read_traffic(counters, names["gather"] + "@copy")
-        traffic["mean_outer"] = ({"bytes": traffic["mean_outer"]["bytes"] + cp["bytes"]} if cp else None)
     alg_per_launch = {"gather": gb_bytes.sum() / steps / launches,
                       "mean_outer": mean_outer.sum() / steps / launches}
 

@@ -22,8 +22,7 @@ from ._abi import (GNN_ERR_CAPACITY, GNN_ERR_HIP, GNN_ERR_INTERNAL, GNN_ERR_INVA
 
 __all__ = [
     "GnnError", "DeviceGraph", "Blocks", "MinibatchOut", "FeatureStore", "Timer", "Options",
-    "gnn_status_string", "gnn_batch_seed", "gnn_capacity", "gnn_workspace_size",
-    "gnn_minibatch_workspace_size", "gnn_sample_khop",
+    "gnn_status_string", "gnn_batch_seed", "gnn_capacity", "gnn_workspace_size", "gnn_sample_khop",
     "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
     "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_minibatch",
     "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
@@ -128,15 +127,6 @@ def gnn_workspace_size(caps: _abi.gnn_caps, num_nodes: int, group: int = 1) -> i
     n = ctypes.c_size_t(0)
     _ok(lib().gnn_workspace_size(ctypes.byref(caps), num_nodes, group, ctypes.byref(n)),
         "gnn_workspace_size")
-    return int(n.value)
-
-
-def gnn_minibatch_workspace_size(caps: _abi.gnn_caps, num_nodes: int, group: int,
-                                 feature_dim: int) -> int:
-    """gnn_workspace_size plus room for a super-batch's shared outermost means."""
-    n = ctypes.c_size_t(0)
-    _ok(lib().gnn_minibatch_workspace_size(ctypes.byref(caps), num_nodes, group, feature_dim,
-                                           ctypes.byref(n)), "gnn_minibatch_workspace_size")
     return int(n.value)
 
 

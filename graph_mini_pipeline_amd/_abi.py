@@ -67,7 +67,6 @@ SIGNATURES = {
     "gnn_batch_seed": (u64, [u64, u64]),
     "gnn_capacity": (i32, [i64, P(i32), i32, i64, P(gnn_caps)]),
     "gnn_workspace_size": (i32, [P(gnn_caps), i64, i32, P(size_t)]),
-    "gnn_minibatch_workspace_size": (i32, [P(gnn_caps), i64, i32, i64, P(size_t)]),
     "gnn_sample_khop": (i32, [P(gnn_graph), vp, i64, P(i32), i32, u64, P(gnn_blocks), vp, size_t,
                               P(gnn_options), vp]),
     "gnn_unique_relabel": (i32, [vp, i64, vp, vp, i64, i64, vp, i64, vp, vp, vp, vp, size_t, vp]),

@@ -38,6 +38,11 @@ struct MeanArgs {
     int32_t *status;
     int32_t d;
     FastDiv cpr;
+    // scatter (one segment): destination r's row goes to row scat[r * scat_g + g] - 1 of
+    // scat_out[g] for every g whose entry is > 0, instead of to the segment's out
+    const int32_t *scat;
+    int32_t scat_g;
+    float *scat_out[kMaxGroup];
 };
 
 // A local id outside the source rows (only after an earlier device error) reads row 0 instead.
@@ -130,22 +135,39 @@ __global__ __launch_bounds__(256) void k_mean_v5(MeanArgs m) {
             }
         }
         const int32_t c = static_cast<int32_t>(e1 - e0);
-        float *orow = S.out + static_cast<int64_t>(i) * m.ld_out;
+        float4 res[CH];
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
-            if (!act[q]) continue;
-            const int col = static_cast<int>(ch0 + q * G) * 4;
-            float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+            res[q] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c > 0) {
                 const float fc = static_cast<float>(c);
-                r = make_float4(acc[q].x / fc, acc[q].y / fc, acc[q].z / fc, acc[q].w / fc);
+                res[q] = make_float4(acc[q].x / fc, acc[q].y / fc, acc[q].z / fc, acc[q].w / fc);
             }
-            const int rem = m.d - col;
-            if (rem >= 4) {
-                *reinterpret_cast<float4 *>(orow + col) = r;
-            } else {
-                const float t[4] = {r.x, r.y, r.z, r.w};
-                for (int w = 0; w < rem; ++w) orow[col + w] = t[w];
+        }
+        auto store_row = [&](float *orow) {
+#pragma unroll
+            for (int q = 0; q < CH; ++q) {
+                if (!act[q]) continue;
+                const int col = static_cast<int>(ch0 + q * G) * 4;
+                const int rem = m.d - col;
+                if (rem >= 4) {
+                    *reinterpret_cast<float4 *>(orow + col) = res[q];
+                } else {
+                    const float t[4] = {res[q].x, res[q].y, res[q].z, res[q].w};
+                    for (int w = 0; w < rem; ++w) orow[col + w] = t[w];
+                }
+            }
+        };
+        if (m.scat == nullptr) {
+            store_row(S.out + static_cast<int64_t>(i) * m.ld_out);
+        } else {
+            // lane g of the group holds the destination's row in sub-batch g (+1; 0: absent)
+            const int32_t mypos = gl < m.scat_g ? m.scat[static_cast<int64_t>(i) * m.scat_g + gl] : 0;
+            for (int g = 0; g < m.scat_g; ++g) {
+                int32_t pos;
+                if constexpr (G == 64) pos = __builtin_amdgcn_readlane(mypos, g);
+                else pos = __shfl(mypos, grp * G + g, 64);
+                if (pos > 0) store_row(m.scat_out[g] + static_cast<int64_t>(pos - 1) * m.ld_out);
             }
         }
     }
@@ -171,14 +193,23 @@ __global__ __launch_bounds__(256) void k_mean_v1(MeanArgs m) {
         for (int64_t e = e0; e < e1; ++e)
             acc += S.src[static_cast<int64_t>(valid_lid(m, S, S.lid[e])) * m.ld_src + col];
         const int32_t c = static_cast<int32_t>(e1 - e0);
-        S.out[static_cast<int64_t>(row) * m.ld_out + col] = c > 0 ? acc / static_cast<float>(c) : 0.f;
+        const float val = c > 0 ? acc / static_cast<float>(c) : 0.f;
+        if (m.scat == nullptr) {
+            S.out[static_cast<int64_t>(row) * m.ld_out + col] = val;
+        } else {
+            for (int g = 0; g < m.scat_g; ++g) {
+                const int32_t pos = m.scat[static_cast<int64_t>(row) * m.scat_g + g];
+                if (pos > 0) m.scat_out[g][static_cast<int64_t>(pos - 1) * m.ld_out + col] = val;
+            }
+        }
     }
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out, int64_t d,
-                       int32_t max_c, int32_t *status, hipStream_t s) {
+static hipError_t launch_mean_impl(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out,
+                                   int64_t d, int32_t *status, const int32_t *scat, int scat_g,
+                                   float *const *scat_out, hipStream_t s) {
     if (njobs <= 0 || d <= 0) return hipSuccess;
     bool v4 = ld_src % 4 == 0 && ld_out % 4 == 0;
     for (int j = 0; j < njobs; ++j) v4 = v4 && aligned16(jobs[j].src) && aligned16(jobs[j].out);
@@ -188,9 +219,11 @@ hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t l
     // chunk groups per lane in one item: G = 64 rows of up to 4 * 64 chunks take one item each
     const int CH = !v4 || G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);
     const int64_t slabs = v4 ? (cpr + CH * G - 1) / (CH * G) : cpr;   // items per destination
-    (void)max_c;
     for (int j0 = 0; j0 < njobs; j0 += kMaxMeanSegs) {
         MeanArgs m{};
+        m.scat = scat;
+        m.scat_g = scat_g;
+        for (int g = 0; g < scat_g; ++g) m.scat_out[g] = scat_out[g];
         m.ld_src = ld_src;
         m.ld_out = ld_out;
         m.status = status;
@@ -220,6 +253,19 @@ hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t l
         else hipLaunchKernelGGL((k_mean_v5<64, 4, R>), grid, dim3(256), 0, s, m);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out, int64_t d,
+                       int32_t max_c, int32_t *status, hipStream_t s) {
+    (void)max_c;
+    return launch_mean_impl(jobs, njobs, ld_src, ld_out, d, status, nullptr, 0, nullptr, s);
+}
+
+hipError_t launch_mean_scatter(const MeanJob &job, const int32_t *inv, int G, float *const *outs,
+                               int64_t ld_src, int64_t ld_out, int64_t d, int32_t *status,
+                               hipStream_t s) {
+    if (G < 1 || G > kMaxGroup || inv == nullptr) return hipErrorInvalidValue;
+    return launch_mean_impl(&job, 1, ld_src, ld_out, d, status, inv, G, outs, s);
 }
 
 }  // namespace gnnmb

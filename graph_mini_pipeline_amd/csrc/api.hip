@@ -83,12 +83,9 @@ struct Workspace {
     int32_t *f_pos;        // [G * Fs] position of each sub-batch destination in U_{l+1}
     int32_t *e_pos;        // [G * Es] position of each sub-batch sampled id in U_{l+1}
     uint32_t *bsum_dist;
-    // shared outermost means of a super-batch (only with a feature width): one mean row per node of
-    // the union frontier U_{K-1}, and each sub-batch destination's position in U_{K-1}
-    float *hU;             // [U_cap(K-1), ld_u]
-    int64_t ld_u;
-    int32_t *urank;        // [G * Fl]
-    int64_t Fl;
+    // shared outermost means of a super-batch: for each node r of the last hop's union frontier
+    // and each sub-batch g, 1 + r's position among g's destinations (0: not there)
+    int32_t *inv;          // [U_cap(K-1) * G]
     int64_t P, Fs, Es;     // strides of the per-sub-batch arrays
     int64_t W, nbw, Wc, nbwc;
     int32_t mode;          // SuperMode
@@ -149,9 +146,7 @@ SuperMode super_mode(const gnn_caps &mc, int64_t N, int G, uint32_t flags) {
 constexpr int64_t kByteMapsMax = 1LL << 30;
 
 // mc: element-wise bound of every sub-batch's caps; G sub-batches relabelled the given way.
-// d > 0 (a super-batch): also room for the shared outermost means, after everything else, so the
-// other buffers sit at the same offsets either way.
-Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws, int64_t d = 0) {
+Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) {
     Workspace w{};
     Carver c{static_cast<char *>(ws)};
     const int K = mc.num_hops;
@@ -211,12 +206,7 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws, 
         w.f_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Fs);
         w.e_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Es);
     }
-    if (d > 0 && G > 1 && K > 0) {
-        w.ld_u = (d + 3) / 4 * 4;
-        w.Fl = mc.frontier[K - 1];
-        w.hU = c.take<float>(union_cap(mc, K - 1, G, N) * w.ld_u);
-        w.urank = c.take<int32_t>(static_cast<int64_t>(G) * w.Fl);
-    }
+    if (G > 1 && K > 0) w.inv = c.take<int32_t>(union_cap(mc, K - 1, G, N) * G);
     w.bytes = c.off;
     return w;
 }
@@ -356,6 +346,10 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
     ru.out[0] = BitmapOut{w.U[0], Ucap, w.d_U, nullptr};
     GNN_TRY_HIP(launch_relabel(ru, s));
     HopArgs h = hop_args(g, w.U[0], w.d_U, Ucap, k, hs, w.u_indptr, w.u_gid, uEcap, w.d_uE, w, o);
+    if (last) {   // the union positions table, filled by the distribution
+        h.inv = w.inv;
+        h.inv_g = G;
+    }
     if (w.bytemaps) {
         // the sub-batch byte maps are zeroed before their relabel; the bitmaps are rewritten
         // whole from them, except that the seeds' duplicate check needs clean bitmaps at hop 0
@@ -378,8 +372,7 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
         const int32_t nt = static_cast<int32_t>(dist_tiles(F_cap(gi, l)));
         da.sub[gi] = DistSub{front(gi, l), d_F(gi, l), F_cap(gi, l), nullptr, nullptr,
                              out.hop[l].indptr, out.hop[l].gid, nullptr, out.caps.edges[l],
-                             out.counts + 2 * l, tiles, nt,
-                             last && w.urank ? w.urank + gi * w.Fl : nullptr};
+                             out.counts + 2 * l, tiles, nt};
         tiles += nt;
     }
     da.ntiles = tiles;
@@ -393,6 +386,7 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
     da.U_cap = Ucap;
     da.bsum = w.bsum_dist;
     da.status = w.status;
+    if (last) da.inv = w.inv;
     GNN_TRY_HIP(launch_dist(da, s));
     // Per-sub-batch relabel into bitmaps 1..G; the union bitmap is zeroed for the next hop.
     RelabelArgs rs = relabel_args(g, w, 1, G);
@@ -483,6 +477,10 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         int32_t *Ul1 = w.U[(l + 1) & 1];
         HopArgs h = hop_args(g, Ul, w.d_U + l, Ucap, fanouts[l], hs, w.u_indptr, w.u_gid, uEcap,
                              w.d_uE + l, w, o);
+        if (l == K - 1) {   // the union positions table, filled by the distribution
+            h.inv = w.inv;
+            h.inv_g = G;
+        }
         GNN_TRY_HIP(launch_classify(h, s));
         if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
         GNN_TRY_HIP(launch_sample(h, s));
@@ -505,7 +503,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
             da.sub[gi] = DistSub{front(gi, l), d_F(gi, l), F_cap(gi, l), w.upos + gi * w.P,
                                  w.f_pos + gi * w.Fs, out.hop[l].indptr, out.hop[l].gid,
                                  w.e_pos + gi * w.Es, out.caps.edges[l], out.counts + 2 * l,
-                                 tiles, nt, l == K - 1 && w.urank ? w.urank + gi * w.Fl : nullptr};
+                                 tiles, nt};
             tiles += nt;
         }
         da.ntiles = tiles;
@@ -523,6 +521,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         da.U1_cap = U1cap;
         da.bsum = w.bsum_dist;
         da.status = w.status;
+        if (l == K - 1) da.inv = w.inv;
         GNN_TRY_HIP(launch_dist(da, s));
         // Per-sub-batch relabel in U_{l+1} positions; the positions of V_l become the next hop's.
         RelabelArgs rs = compact_relabel_args(w, G, Ul1, w.d_U + l + 1, U1cap);
@@ -602,20 +601,6 @@ gnn_status gnn_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t g
     if (group > 1) {
         const size_t bc = carve(*caps, num_nodes, group, kSuperCompact, nullptr).bytes;
         b = bc > b ? bc : b;
-    }
-    *out_bytes = b;
-    return GNN_OK;
-}
-
-gnn_status gnn_minibatch_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t group,
-                                        int64_t feature_dim, size_t *out_bytes) {
-    if (feature_dim < 1) return GNN_ERR_INVALID_ARG;
-    gnn_status st = gnn_workspace_size(caps, num_nodes, group, out_bytes);
-    if (st != GNN_OK || group == 1) return st;
-    size_t b = *out_bytes;
-    for (SuperMode m : {kSuperFull, kSuperCompact}) {
-        const size_t x = carve(*caps, num_nodes, group, m, nullptr, feature_dim).bytes;
-        b = x > b ? x : b;
     }
     *out_bytes = b;
     return GNN_OK;
@@ -823,9 +808,8 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     // U_{K-1} and copied to the sub-batches that hold it (the G sub-batches share one seed, so a
     // node's sampled neighbours, hence its mean, are the same in each).
     const bool from_table = batched && !fs->on_host && fs->slot == nullptr;
-    const bool shared_means = from_table && group > 1 &&
-                              ws_bytes >= carve(mc, g->num_nodes, group, mode, nullptr, d).bytes;
-    const Workspace w = carve(mc, g->num_nodes, group, mode, ws, shared_means ? d : 0);
+    const bool shared_means = from_table && group > 1;
+    const Workspace w = carve(mc, g->num_nodes, group, mode, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t *ev = nullptr;
     if (timer) {
@@ -878,30 +862,15 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         GNN_TRY_HIP(launch_gather_batch(ga, rows_cap, s));
         if (ev) GNN_TRY_HIP(hipEventRecord(ev[2], s));
         if (shared_means) {
-            // the union block of the last hop: destinations U_{K-1} (in U order), global ids
+            // the union block of the last hop (destinations U_{K-1} in U order, global ids): each
+            // union node's mean is stored to its row in every sub-batch that holds it
             const int64_t Ucap = union_cap(mc, K - 1, group, g->num_nodes);
             const int64_t *d_U = w.d_U + (w.mode == kSuperCompact ? K - 1 : 0);
             const MeanJob uj{w.u_indptr, w.u_gid, Ucap * fanouts[K - 1], d_U, Ucap, fs->table,
-                             fs->num_nodes, w.hU};
-            GNN_TRY_HIP(launch_mean(&uj, 1, fs->ld, w.ld_u, d, fanouts[K - 1], w.status, s));
-            // sub-batch destination i takes the row of its union position
-            GatherBatchArgs cp{};
-            cp.nseg = group;
-            cp.table = w.hU;
-            cp.ld = w.ld_u;
-            cp.d = static_cast<int32_t>(d);
-            cp.num_rows = Ucap;
-            cp.ld_out = outs[0].ld_h;
-            cp.status = w.status;
-            int64_t cp_rows = 0;
-            for (int gi = 0; gi < group; ++gi) {
-                gnn_minibatch_out &mo = outs[gi];
-                const gnn_caps &c = mo.blocks.caps;
-                const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
-                cp.seg[gi] = GatherSeg{w.urank + gi * w.Fl, d_n, c.frontier[K - 1], mo.h[K - 1]};
-                cp_rows += c.frontier[K - 1];
-            }
-            GNN_TRY_HIP(launch_gather_batch(cp, cp_rows, s));
+                             fs->num_nodes, nullptr};
+            float *hk[GNN_MAX_GROUP];
+            for (int gi = 0; gi < group; ++gi) hk[gi] = outs[gi].h[K - 1];
+            GNN_TRY_HIP(launch_mean_scatter(uj, w.inv, group, hk, fs->ld, outs[0].ld_h, d, w.status, s));
         } else {
             GNN_TRY_HIP(launch_mean(jobs, group, from_table ? fs->ld : outs[0].ld_h, outs[0].ld_h, d,
                                     fanouts[K - 1], w.status, s));

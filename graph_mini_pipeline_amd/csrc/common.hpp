@@ -154,6 +154,8 @@ struct HopArgs {
     uint32_t *totals;       // [kCols] |E_l| then the category sizes
     uint32_t *clear_ptr;    // words the classification clears (the relabel bitmap of this hop)
     int64_t clear_n;
+    int32_t *inv;           // optional [F * inv_g]: zeroed over the frontier by the classification
+    int32_t inv_g;
     int32_t *status;
     int32_t nb;             // classify blocks
 };
@@ -227,7 +229,6 @@ struct DistSub {
     int64_t *d_E;
     int32_t tile0;  // first tile of this sub-batch in the launch
     int32_t ntile;
-    int32_t *urank; // optional out [F]: position of each destination in U_l (-1: none)
 };
 
 struct DistArgs {
@@ -252,6 +253,8 @@ struct DistArgs {
     int64_t U1_cap;
     uint32_t *bsum;            // [ntiles]
     int32_t *status;
+    int32_t *inv;              // optional out [U_cap * G]: inv[r * G + g] = 1 + the position of
+                               // union node r among sub-batch g's destinations (0: not there)
 };
 
 constexpr int kClassifyThreads = 256;
@@ -315,6 +318,12 @@ constexpr int kMaxMeanSegs = 16;
 // typical (or the largest) edge count per destination; it only picks the load depth.
 hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out, int64_t d,
                        int32_t max_c, int32_t *status, hipStream_t s);
+// One block whose destinations are the union of G sub-batches' destinations: destination r's mean
+// is stored to row inv[r * G + g] - 1 of outs[g] for every g with inv[r * G + g] > 0 (job.out is
+// not used).
+hipError_t launch_mean_scatter(const MeanJob &job, const int32_t *inv, int G, float *const *outs,
+                               int64_t ld_src, int64_t ld_out, int64_t d, int32_t *status,
+                               hipStream_t s);
 hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                              const int32_t *hot, int64_t rows, float *cache, int32_t *slot,
                              int32_t *status, hipStream_t s);

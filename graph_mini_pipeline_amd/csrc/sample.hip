@@ -90,6 +90,8 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) 
             }
             const int32_t c = deg <= a.k ? static_cast<int32_t>(deg) : a.k;
             const int32_t cat = node_cat(node_class(deg, a.k, a.group_max, a.wave_max), deg);
+            if (a.inv)
+                for (int g = 0; g < a.inv_g; ++g) a.inv[i * a.inv_g + g] = 0;
             a.packed[i] = (c << 4) | cat;
             vals[0] += static_cast<uint32_t>(c);
 #pragma unroll

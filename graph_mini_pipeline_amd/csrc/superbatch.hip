@@ -86,7 +86,8 @@ __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
     }
     if (threadIdx.x >= kDistTile) return;
     const int t = blockIdx.x;
-    const DistSub &S = a.sub[find_sub(a, t)];
+    const int sg = find_sub(a, t);
+    const DistSub &S = a.sub[sg];
     const int64_t F = load_count(S.d_F, S.F_cap);
     const int64_t i = static_cast<int64_t>(t - S.tile0) * kDistTile + threadIdx.x;
     int64_t lo;
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
     if (i < F) {
         union_row(a, S, i, lo, c, np, r);
         if (S.f_pos) S.f_pos[i] = np;
-        if (S.urank) S.urank[i] = r;
+        if (a.inv && r >= 0) a.inv[static_cast<int64_t>(r) * a.G + sg] = static_cast<int32_t>(i + 1);
     }
     const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
     if (threadIdx.x == 0) a.bsum[t] = sum;

@@ -66,9 +66,11 @@ typedef void *gnn_stream; /* hipStream_t */
  *                caches;
  *   BATCHED:     every sub-batch's gather in one launch, then the outermost means in one launch
  *                (one launch's start-up and drain instead of G; G times as many host-link reads
- *                in flight for a host-resident table; with a table in device memory and no cache
- *                the means read the table rows, shared by the sub-batches -- once per node of the
- *                union frontier with a workspace from gnn_minibatch_workspace_size). */
+ *                in flight for a host-resident table).  With a table in device memory and no
+ *                cache, the outermost means read the table rows and are taken once per node of
+ *                the union of the sub-batches' last frontiers: the sub-batches share one seed, so
+ *                a node's sampled neighbours and mean are the same in each, and the mean is
+ *                stored to the node's row in every sub-batch that holds it. */
 #define GNN_GATHER_INTERLEAVED 8u
 #define GNN_GATHER_BATCHED 16u
 
@@ -148,20 +150,6 @@ gnn_status gnn_capacity(int64_t n_seeds, const int32_t *fanouts, int32_t num_hop
  */
 gnn_status gnn_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t group,
                               size_t *out_bytes);
-
-/*
- * Workspace for gnn_minibatch with room for shared outermost means (feature_dim = d of the
- * feature store, >= 1): at least gnn_workspace_size, plus, for group > 1, one row of d floats per
- * node of the largest possible union frontier of the last hop and one position per sub-batch
- * destination.  With such a workspace, a super-batch whose gathers are batched from a table in
- * device memory without a cache (the default for rows of more than 128 floats) takes each
- * outermost mean once per node of the union of the sub-batches' last frontiers -- the sub-batches
- * share one seed, so a node's sampled neighbours and mean are the same in each -- and copies it to
- * every sub-batch that holds the node (results identical).  A smaller workspace (>=
- * gnn_workspace_size) takes the means per sub-batch.  Writes *out_bytes (host).
- */
-gnn_status gnn_minibatch_workspace_size(const gnn_caps *caps, int64_t num_nodes, int32_t group,
-                                        int64_t feature_dim, size_t *out_bytes);
 
 /*
  * k-hop neighbour sampling and relabel for one batch (GARDEN Sec. II.B, Fig. 1; Sec. IV.C; the
@@ -269,8 +257,7 @@ typedef struct gnn_minibatch_out {
  *   All sub-batches use the one seed64, so a node shared by two sub-batches at the same hop has
  *   the same sample in both; each sub-batch's outputs equal a separate run with that seed64.
  *   outs: host [group]; outs[g].blocks.caps.n_seeds = batch_ptr[g+1] - batch_ptr[g].
- *   ws: ws_bytes >= gnn_workspace_size(caps >= every sub-batch's caps, N, group), or
- *   gnn_minibatch_workspace_size(..., d) for shared outermost means.
+ *   ws: ws_bytes >= gnn_workspace_size(caps >= every sub-batch's caps, N, group).
  *   timer: NULL, or a timer that records the stage boundaries of this call (gnn_timer_*).
  * Errors: as gnn_sample_khop and gnn_gather_features.
  */

@@ -24,9 +24,8 @@ def device_table(x: np.ndarray, ld: int) -> torch.Tensor:
 
 
 def run_minibatch(dg: gm.DeviceGraph, fs: gm.FeatureStore, seeds: np.ndarray, fanouts, seed64,
-                  opts=None, ws=None, group_ptr=None, shared_means=True):
-    """Run gnn_minibatch; returns (outs, status).  group_ptr splits seeds into sub-batches; the
-    workspace has room for shared outermost means unless shared_means is False."""
+                  opts=None, ws=None, group_ptr=None):
+    """Run gnn_minibatch; returns (outs, status).  group_ptr splits seeds into sub-batches."""
     seeds_t = torch.from_numpy(np.ascontiguousarray(seeds, dtype=np.int32)).cuda()
     ptr = group_ptr if group_ptr is not None else [0, len(seeds)]
     outs = []
@@ -37,10 +36,7 @@ def run_minibatch(dg: gm.DeviceGraph, fs: gm.FeatureStore, seeds: np.ndarray, fa
         if caps_max is None or caps.frontier[len(fanouts) - 1] > caps_max.frontier[len(fanouts) - 1]:
             caps_max = caps
     if ws is None:
-        G = len(ptr) - 1
-        need = max(gm.gnn_minibatch_workspace_size(o.blocks.caps, dg.num_nodes, G, fs.d)
-                   if shared_means else gm.gnn_workspace_size(o.blocks.caps, dg.num_nodes, G)
-                   for o in outs)
+        need = max(gm.gnn_workspace_size(o.blocks.caps, dg.num_nodes, len(ptr) - 1) for o in outs)
         ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     gm.gnn_minibatch(dg, fs, seeds_t, ptr, fanouts, seed64, outs, ws, opts)
     st = gm.gnn_read_device_status(ws)

@@ -105,18 +105,6 @@ def test_workspace_grows_with_graph():
     assert gm.gnn_relabel_workspace_size(1000) > 0
 
 
-def test_minibatch_workspace_adds_shared_means():
-    caps = gm.gnn_capacity(1024, [25, 10], 233_000)
-    plain = gm.gnn_workspace_size(caps, 233_000, 8)
-    shared = gm.gnn_minibatch_workspace_size(caps, 233_000, 8, 602)
-    # one row of 604 floats per node of the largest union frontier (min(N, 8 * 26624) nodes)
-    assert shared - plain >= min(233_000, 8 * 26_624) * 604 * 4
-    assert gm.gnn_minibatch_workspace_size(caps, 233_000, 1, 602) == gm.gnn_workspace_size(caps, 233_000, 1)
-    with pytest.raises(gm.GnnError) as e:
-        gm.gnn_minibatch_workspace_size(caps, 233_000, 8, 0)
-    assert e.value.status == gm.GNN_ERR_INVALID_ARG
-
-
 def test_status_strings():
     for s in range(-6, 1):
         assert gm.gnn_status_string(s)

@@ -59,8 +59,8 @@ def _run(cfg, g, table, order, batches, seed64, mode="auto"):
     outs = [gm.MinibatchOut(gm.gnn_capacity(ptr[j + 1] - ptr[j], cfg.fanouts, cfg.num_nodes),
                             cfg.d, cfg.ld) for j in range(len(batches))]
     caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
-    ws = torch.empty(gm.gnn_minibatch_workspace_size(caps, cfg.num_nodes, len(batches), cfg.d),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, len(batches)), dtype=torch.uint8,
+                     device="cuda")
     gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, seed64, outs, ws,
                      gm.Options(superbatch=mode))
     assert gm.gnn_read_device_status(ws) == gm.GNN_OK

@@ -489,17 +489,18 @@ def test_gather_both_flags_rejected(tiny):
 
 @pytest.mark.parametrize("mode", SUPER_MODES)
 @pytest.mark.parametrize("fanouts", [[7], [12, 6], [12, 6, 3]])
-@pytest.mark.parametrize("shared", [True, False])
-def test_shared_outer_means(tiny, mode, fanouts, shared):
-    # batched gathers from a table in HBM: with a large enough workspace the outermost means are
-    # taken once per node of the union frontier and copied out; sub-batches overlap, one is empty
+@pytest.mark.parametrize("ld", [64, 66])
+def test_shared_outer_means(tiny, mode, fanouts, ld):
+    # batched gathers from a table in HBM: the outermost means are taken once per node of the union
+    # frontier and stored to every sub-batch that holds the node; sub-batches overlap, one is
+    # empty; rows 16-byte aligned (64 floats) or not (66: the flat kernels)
     cfg, indptr, indices, x, order = tiny
     dg = device_graph(indptr, indices)
-    fs = _store(x)
+    fs = _store(x, ld)
     parts = [order[i * 50:(i + 1) * 50 + 20] for i in range(6)] + [order[:0]] + [order[100:180]]
     seeds = np.concatenate(parts)
     ptr = np.concatenate([[0], np.cumsum([len(p) for p in parts])]).tolist()
-    outs, st = run_minibatch(dg, fs, seeds, fanouts, 808, group_ptr=ptr, shared_means=shared,
+    outs, st = run_minibatch(dg, fs, seeds, fanouts, 808, group_ptr=ptr,
                              opts=gm.Options(superbatch=mode, gather="batched"))
     assert st == gm.GNN_OK
     for g in range(len(parts)):
