@@ -199,7 +199,6 @@ __global__ __launch_bounds__(1024) void k_popc_scan(RelabelArgs a) {
 // Word prefixes and the sorted unique ids.  With few tiles (pre_scanned = 0) each workgroup sums
 // the popcounts of the tiles of its bitmap before it, and the bitmap's first tile writes its size.
 __global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a, int32_t pre_scanned) {
-    __shared__ uint32_t smem[kBitmapThreads / 64];
     __shared__ uint32_t s_red[2][kBitmapThreads / 64];
     __shared__ uint32_t s_base;
     const int bm = static_cast<int>(blockIdx.x) / a.nbw;
@@ -238,26 +237,53 @@ __global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a, int32_t 
     __syncthreads();
     const uint32_t *words = a.bitmap + static_cast<int64_t>(bm) * a.W;
     uint32_t *wpre = a.wprefix + static_cast<int64_t>(bm) * a.W;
-    const int64_t w0 = static_cast<int64_t>(lt) * kBitmapTile +
-                       static_cast<int64_t>(threadIdx.x) * kBitmapWordsPerThread;
+    const int64_t tile0 = static_cast<int64_t>(lt) * kBitmapTile;
     const int64_t Wl = live_words(a);
-    if (static_cast<int64_t>(lt) * kBitmapTile >= Wl) return;  // whole workgroup: nothing live
-    uint32_t wv[kBitmapWordsPerThread];
-    uint32_t c = 0;
+    if (tile0 >= Wl) return;  // whole workgroup: nothing live
+    // Round q: thread t takes word tile0 + q * kBitmapThreads + t, so the ids that neighbouring
+    // lanes write sit a few entries apart and one store instruction touches few cache lines.
+    // The rounds' wavefront scans run two at a time on 16-bit halves (a wavefront's popcount
+    // total is at most 2048), and one barrier publishes every (round, wavefront) total.
+    constexpr int Q = kBitmapWordsPerThread;
+    constexpr int NW = kBitmapThreads / 64;
+    static_assert(Q % 2 == 0, "rounds are scanned in pairs");
+    __shared__ uint32_t s_tot[Q * NW];
+    const int wv = static_cast<int>(threadIdx.x >> 6);
+    uint32_t wd[Q];
 #pragma unroll
-    for (int q = 0; q < kBitmapWordsPerThread; ++q) {
-        wv[q] = w0 + q < Wl ? words[w0 + q] : 0u;
-        c += __popc(wv[q]);
+    for (int q = 0; q < Q; ++q) {
+        const int64_t w = tile0 + static_cast<int64_t>(q) * kBitmapThreads + threadIdx.x;
+        wd[q] = w < Wl ? words[w] : 0u;
     }
-    uint32_t total;
-    uint32_t run = block_exclusive_scan<uint32_t, kBitmapThreads>(c, &total, smem);
-    run += s_base;
+    uint32_t inc[Q];
 #pragma unroll
-    for (int q = 0; q < kBitmapWordsPerThread; ++q) {
-        const int64_t w = w0 + q;
-        if (w >= Wl) break;
+    for (int q = 0; q < Q; q += 2) {
+        const uint32_t pair =
+            wave_inclusive_scan<uint32_t>(__popc(wd[q]) | (static_cast<uint32_t>(__popc(wd[q + 1])) << 16));
+        inc[q] = pair & 0xFFFFu;
+        inc[q + 1] = pair >> 16;
+    }
+    if (lane_id() == 63) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) s_tot[q * NW + wv] = inc[q];
+    }
+    __syncthreads();
+    uint32_t base = s_base;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        uint32_t before = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const uint32_t v = s_tot[q * NW + i];
+            if (i < wv) before += v;
+            tot += v;
+        }
+        const int64_t w = tile0 + static_cast<int64_t>(q) * kBitmapThreads + threadIdx.x;
+        uint32_t run = base + before + inc[q] - __popc(wd[q]);
+        base += tot;
+        if (w >= Wl) continue;
         wpre[w] = run;
-        uint32_t bits = wv[q];
+        uint32_t bits = wd[q];
         while (bits) {
             const int b = __ffs(bits) - 1;
             bits &= bits - 1u;
