@@ -543,7 +543,7 @@ static_assert(kWavesPerBlock * kWaveCap == kBlockCap, "WAVE slots fill the share
 static_assert(kWavesPerBlock * (64 / kGroupLanes) * kGroupCap == kBlockCap,
               "GROUP slots fill the shared LDS arrays");
 
-__global__ __launch_bounds__(kBlockThreads) void k_sample(HopArgs a, int32_t nb_block,
+__global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t nb_block,
                                                          int32_t nb_wave, int32_t nb_group) {
     __shared__ uint64_t s_key[kBlockCap];
     __shared__ int32_t s_pos[kBlockCap];
