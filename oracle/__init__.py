@@ -15,6 +15,9 @@ sample / ship features / compute iteration):
   h_K = X, and for l = K..1: h_{l-1}[i] = mean of h_l over the sampled neighbours of destination i
   (0 when it has none).
 A super-batch of G sub-batches is defined as G independent runs sharing one batch seed.
+One GraphSAGE-mean layer over a block (sage_layer; GARDEN Sec. II.A eq. (1)-(2), the model of its
+Sec. VI.A): out[i] = relu([h[dst_lid[i]] || mean of h over i's sampled neighbours] @ W + bias),
+in double.
 
 Every function here is pinned by the CPU tests (published SplitMix64 outputs, brute force on
 hand-built graphs, BFS and dense-matrix special cases, uniformity statistics, exact rationals).
@@ -80,6 +83,8 @@ def lib():
         L.orc_gather.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64]
         L.orc_mean.restype = i32
         L.orc_mean.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp, i64]
+        L.orc_sage_layer.restype = i32
+        L.orc_sage_layer.argtypes = [vp, vp, vp, i64, vp, i64, i64, i64, vp, vp, i64, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -193,6 +198,41 @@ def mean_aggregate(blk_indptr: np.ndarray, lid: np.ndarray, src: np.ndarray,
                           _p(src if src.size else np.zeros((1, max(d, 1)), np.float32)),
                           src.shape[1] if src.size else d, src.shape[0], d, _p(out), d), "mean")
     return out
+
+
+def sage_layer(blk_indptr: np.ndarray, lid: np.ndarray, dst_lid: np.ndarray, src: np.ndarray,
+               W: np.ndarray, bias: Optional[np.ndarray] = None, relu: bool = True,
+               d: Optional[int] = None, with_scale: bool = False):
+    """One GraphSAGE-mean layer (GARDEN Sec. II.A eq. (1)-(2)): for destination i,
+    a = [src[dst_lid[i]] || mean of src over its sampled neighbours] and
+    out[i] = relu(a @ W + bias), W of shape [2d, d_out].  All in double; returns out [n_dst,
+    d_out] float64, and with with_scale also sum_k |a_k| |W_kn| + |bias_n| of the same shape."""
+    blk_indptr = np.ascontiguousarray(blk_indptr, dtype=np.int32)
+    lid = np.ascontiguousarray(lid, dtype=np.int32)
+    dst_lid = np.ascontiguousarray(dst_lid, dtype=np.int32)
+    src = np.ascontiguousarray(src, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    d = src.shape[1] if d is None else d
+    if W.shape[0] != 2 * d:
+        raise ValueError("W must have 2d rows")
+    d_out = W.shape[1]
+    n_dst = blk_indptr.shape[0] - 1
+    if dst_lid.shape[0] != n_dst:
+        raise ValueError("one dst_lid per destination")
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.zeros((n_dst, d_out), dtype=np.float64)
+    scale = np.zeros((n_dst, d_out), dtype=np.float64) if with_scale else None
+    one_i = np.zeros(1, np.int32)
+    _check(lib().orc_sage_layer(_p(blk_indptr), _p(lid if lid.size else one_i),
+                                _p(dst_lid if dst_lid.size else one_i), n_dst,
+                                _p(src if src.size else np.zeros((1, max(d, 1)), np.float32)),
+                                src.shape[1] if src.size else d, src.shape[0], d,
+                                _p(W if W.size else np.zeros(1, np.float32)),
+                                _p(b) if b is not None else None, d_out, 1 if relu else 0,
+                                _p(out if out.size else np.zeros(1)),
+                                (_p(scale if scale.size else np.zeros(1)) if with_scale else None)),
+           "sage layer")
+    return (out, scale) if with_scale else out
 
 
 # ---- the whole path for one batch ------------------------------------------------------------

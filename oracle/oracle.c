@@ -21,6 +21,11 @@
  *
  * Floating point: the mean accumulates in double, in ascending edge order, divides by the count
  * and rounds once to float.
+ *
+ * The GraphSAGE-mean layer (orc_sage_layer) follows GARDEN Sec. II.A eq. (1)-(2): AGGREGATE is
+ * the mean over the sampled neighbours, UPDATE a dense layer on the concatenation of the node's
+ * own previous state and that mean, then a ReLU (the layer GraphSAGE defines and GARDEN Sec. VI.A
+ * evaluates).  It is computed in double throughout and is not rounded to float.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -219,5 +224,51 @@ int orc_mean(const int32_t *indptr, const int32_t *lid, int64_t n_dst, const flo
         for (int64_t t = 0; t < d; ++t) o[t] = c > 0 ? (float)(acc[t] / (double)c) : 0.0f;
     }
     free(acc);
+    return ORC_OK;
+}
+
+/*
+ * One GraphSAGE-mean layer over one block.  For destination i with sampled edges
+ * e in [indptr[i], indptr[i+1]) (count c):
+ *   a = [ src row dst_lid[i]  ||  (1/c) * sum_e src row lid[e]  (0 when c = 0) ]   (2d values),
+ *   out[i][n] = sum_{k < 2d} a[k] * W[k][n] + (bias ? bias[n] : 0),  then max(0, .) if relu.
+ * W is row-major [2d][d_out].  Everything is double; out is [n_dst][d_out] double.  When
+ * scale is not NULL it receives sum_k |a[k]| |W[k][n]| + |bias[n]| (the magnitude an error bound
+ * of a float evaluation scales with).
+ */
+int orc_sage_layer(const int32_t *indptr, const int32_t *lid, const int32_t *dst_lid,
+                   int64_t n_dst, const float *src, int64_t ld_src, int64_t n_src, int64_t d,
+                   const float *W, const float *bias, int64_t d_out, int32_t relu, double *out,
+                   double *scale) {
+    if (d < 0 || ld_src < d || d_out < 0 || n_dst < 0) return ORC_ERR_ARG;
+    const int64_t K = 2 * d;
+    double *a = (double *)malloc(((size_t)K + 1) * sizeof(double));
+    if (!a) return ORC_ERR_NOMEM;
+    for (int64_t i = 0; i < n_dst; ++i) {
+        const int64_t self = dst_lid[i];
+        if (self < 0 || self >= n_src) { free(a); return ORC_ERR_RANGE; }
+        for (int64_t t = 0; t < d; ++t) a[t] = (double)src[self * ld_src + t];
+        for (int64_t t = 0; t < d; ++t) a[d + t] = 0.0;
+        const int64_t e0 = indptr[i], e1 = indptr[i + 1];
+        for (int64_t e = e0; e < e1; ++e) {
+            const int64_t u = lid[e];
+            if (u < 0 || u >= n_src) { free(a); return ORC_ERR_RANGE; }
+            for (int64_t t = 0; t < d; ++t) a[d + t] += (double)src[u * ld_src + t];
+        }
+        if (e1 > e0)
+            for (int64_t t = 0; t < d; ++t) a[d + t] /= (double)(e1 - e0);
+        for (int64_t n = 0; n < d_out; ++n) {
+            double acc = bias ? (double)bias[n] : 0.0;
+            double mag = bias ? (double)(bias[n] < 0 ? -bias[n] : bias[n]) : 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double w = (double)W[k * d_out + n];
+                acc += a[k] * w;
+                mag += (a[k] < 0 ? -a[k] : a[k]) * (w < 0 ? -w : w);
+            }
+            out[i * d_out + n] = (relu && acc < 0.0) ? 0.0 : acc;
+            if (scale) scale[i * d_out + n] = mag;
+        }
+    }
+    free(a);
     return ORC_OK;
 }

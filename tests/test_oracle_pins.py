@@ -258,3 +258,79 @@ def test_superbatch_is_independent_runs():
         assert np.array_equal(sb[g].h[0], one.h[0])
         for a, b in zip(sb[g].blocks, one.blocks):
             assert np.array_equal(a.gid, b.gid) and np.array_equal(a.nodes, b.nodes)
+
+
+# ---- GraphSAGE-mean layer --------------------------------------------------------------------
+
+def _random_block(rng, n_dst, n_src, max_c):
+    counts = rng.integers(0, max_c + 1, size=n_dst)
+    counts[:2] = 0   # rows without sampled neighbours
+    blk_indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    lid = rng.integers(0, n_src, size=int(counts.sum())).astype(np.int32)
+    dst_lid = rng.permutation(n_src)[:n_dst].astype(np.int32)
+    return blk_indptr, lid, dst_lid
+
+
+@pytest.mark.parametrize("relu", [False, True])
+def test_sage_layer_exact_rationals(relu):
+    """Each output against exact rational arithmetic: [self || mean] @ W + bias, then ReLU."""
+    rng = np.random.default_rng(21)
+    n_dst, n_src, d, d_out = 9, 14, 3, 5
+    blk_indptr, lid, dst_lid = _random_block(rng, n_dst, n_src, 6)
+    src = rng.uniform(-2, 2, size=(n_src, d)).astype(np.float32)
+    W = rng.uniform(-1, 1, size=(2 * d, d_out)).astype(np.float32)
+    b = rng.uniform(-1, 1, size=d_out).astype(np.float32)
+    out, scale = oracle.sage_layer(blk_indptr, lid, dst_lid, src, W, b, relu, with_scale=True)
+    for i in range(n_dst):
+        es = range(blk_indptr[i], blk_indptr[i + 1])
+        a = [Fraction(float(src[dst_lid[i], t])) for t in range(d)]
+        for t in range(d):
+            a.append(sum((Fraction(float(src[lid[e], t])) for e in es), Fraction(0)) / len(es)
+                     if len(es) else Fraction(0))
+        for n in range(d_out):
+            lin = sum((a[k] * Fraction(float(W[k, n])) for k in range(2 * d)), Fraction(float(b[n])))
+            exact = max(lin, Fraction(0)) if relu else lin
+            mag = sum((abs(a[k]) * abs(Fraction(float(W[k, n]))) for k in range(2 * d)),
+                      abs(Fraction(float(b[n]))))
+            tol = Fraction(2.0 ** -50) * mag
+            assert abs(Fraction(float(out[i, n])) - exact) <= tol, (i, n)
+            assert abs(Fraction(float(scale[i, n])) - mag) <= tol, (i, n)
+
+
+def test_sage_layer_is_dense_algebra():
+    """relu(A @ W + b) with A = [X[dst_lid] | P X], P the row-normalised block adjacency."""
+    rng = np.random.default_rng(22)
+    n_dst, n_src, d, d_out = 40, 70, 6, 11
+    blk_indptr, lid, dst_lid = _random_block(rng, n_dst, n_src, 9)
+    x = rng.standard_normal((n_src, d)).astype(np.float32)
+    W = rng.standard_normal((2 * d, d_out)).astype(np.float32)
+    b = rng.standard_normal(d_out).astype(np.float32)
+    P = np.zeros((n_dst, n_src))
+    for i in range(n_dst):
+        c = blk_indptr[i + 1] - blk_indptr[i]
+        for e in range(blk_indptr[i], blk_indptr[i + 1]):
+            P[i, lid[e]] += 1.0 / c
+    A = np.concatenate([x[dst_lid].astype(np.float64), P @ x.astype(np.float64)], axis=1)
+    ref = A @ W.astype(np.float64) + b
+    np.testing.assert_allclose(oracle.sage_layer(blk_indptr, lid, dst_lid, x, W, b, False), ref,
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.sage_layer(blk_indptr, lid, dst_lid, x, W, b, True),
+                               np.maximum(ref, 0.0), rtol=1e-12, atol=1e-12)
+
+
+def test_sage_layer_special_cases():
+    """Identity halves of W give the node's own row or the mean; W = 0 gives relu(bias)."""
+    rng = np.random.default_rng(23)
+    n_dst, n_src, d = 30, 50, 4
+    blk_indptr, lid, dst_lid = _random_block(rng, n_dst, n_src, 7)
+    x = rng.standard_normal((n_src, d)).astype(np.float32)
+    I, Z = np.eye(d, dtype=np.float32), np.zeros((d, d), np.float32)
+    own = oracle.sage_layer(blk_indptr, lid, dst_lid, x, np.concatenate([I, Z]), relu=False)
+    assert np.array_equal(own, x[dst_lid].astype(np.float64))
+    mean = oracle.sage_layer(blk_indptr, lid, dst_lid, x, np.concatenate([Z, I]), relu=False)
+    m32 = oracle.mean_aggregate(blk_indptr, lid, x)
+    assert np.array_equal(mean.astype(np.float32), m32)   # the float mean rounds the double one
+    assert np.all(mean[:2] == 0.0)
+    b = np.array([1.5, -2.0, 0.0, 3.25], np.float32)
+    only_b = oracle.sage_layer(blk_indptr, lid, dst_lid, x, np.zeros((2 * d, 4), np.float32), b)
+    assert np.array_equal(only_b, np.tile(np.maximum(b, 0).astype(np.float64), (n_dst, 1)))
