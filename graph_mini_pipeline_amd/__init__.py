@@ -24,7 +24,8 @@ __all__ = [
     "GnnError", "DeviceGraph", "Blocks", "MinibatchOut", "FeatureStore", "Timer", "Options",
     "gnn_status_string", "gnn_batch_seed", "gnn_capacity", "gnn_workspace_size", "gnn_sample_khop",
     "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
-    "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_minibatch",
+    "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_sage_layer",
+    "gnn_minibatch",
     "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
     "gnn_timer_elapsed", "gnn_copy_probe", "gnn_copy_probe_host", "gnn_hash_probe", "lib",
 ]
@@ -280,6 +281,34 @@ def gnn_mean_aggregate(indptr: torch.Tensor, lid: torch.Tensor, src: torch.Tenso
                                   _ptr(src), src.shape[1], src.shape[0], d, _ptr(out),
                                   out.shape[1], _ptr(d_status), _stream(stream))
     _ok(st, "gnn_mean_aggregate")
+
+
+def gnn_sage_layer(indptr: torch.Tensor, lid: torch.Tensor, dst_lid: torch.Tensor,
+                   src: torch.Tensor, d: int, W: torch.Tensor, bias: Optional[torch.Tensor],
+                   relu: bool, agg: torch.Tensor, out: torch.Tensor,
+                   d_n_dst: Optional[torch.Tensor] = None, d_status: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """One GraphSAGE-mean layer: agg = block means, out = act([src[dst_lid] || agg] @ W + bias).
+    W: float32 [2d, d_out] contiguous; agg: [n_dst, >= d]; out: [n_dst, >= d_out]."""
+    for t, n in ((indptr, "indptr"), (lid, "lid"), (dst_lid, "dst_lid")):
+        _need(t, torch.int32, n)
+    for t, n in ((src, "src"), (W, "W"), (agg, "agg"), (out, "out")):
+        _need(t, torch.float32, n)
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+    n_dst = indptr.numel() - 1
+    if W.dim() != 2 or W.shape[0] != 2 * d or not W.is_contiguous():
+        raise ValueError("W must be a contiguous [2d, d_out] tensor")
+    d_out = W.shape[1]
+    if bias is not None and bias.numel() < d_out:
+        raise ValueError("bias shorter than d_out")
+    if dst_lid.numel() < n_dst or agg.shape[0] < n_dst or out.shape[0] < n_dst:
+        raise ValueError("dst_lid / agg / out have fewer rows than destinations")
+    st = lib().gnn_sage_layer(_ptr(indptr), _ptr(lid), lid.numel(), _ptr(dst_lid), _ptr(d_n_dst),
+                              n_dst, _ptr(src), src.shape[1], src.shape[0], d, _ptr(W),
+                              _ptr(bias), d_out, 1 if relu else 0, _ptr(agg), agg.shape[1],
+                              _ptr(out), out.shape[1], _ptr(d_status), _stream(stream))
+    _ok(st, "gnn_sage_layer")
 
 
 class MinibatchOut:

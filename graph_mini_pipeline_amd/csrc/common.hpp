@@ -324,6 +324,13 @@ hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t l
 hipError_t launch_mean_scatter(const MeanJob &job, const int32_t *inv, int G, float *const *outs,
                                int64_t ld_src, int64_t ld_out, int64_t d, int32_t *status,
                                hipStream_t s);
+// The dense UPDATE of a GraphSAGE-mean layer: out = act([src[dst_lid] || agg] W + bias) on the
+// matrix cores (fp32); rows beyond *d_n (when given) are skipped.
+hipError_t launch_sage_update(const int32_t *dst_lid, const int64_t *d_n, int64_t n_cap,
+                              const float *src, int64_t ld_src, int64_t n_src, const float *agg,
+                              int64_t ld_agg, int64_t d, const float *W, const float *bias,
+                              int64_t d_out, int32_t relu, float *out, int64_t ld_out,
+                              int32_t *status, hipStream_t s);
 hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                              const int32_t *hot, int64_t rows, float *cache, int32_t *slot,
                              int32_t *status, hipStream_t s);

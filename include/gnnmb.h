@@ -237,6 +237,32 @@ gnn_status gnn_mean_aggregate(const int32_t *indptr, const int32_t *lid, int64_t
                               int64_t ld_out, int32_t *d_status, gnn_stream stream);
 
 /*
+ * One GraphSAGE-mean layer over one block (GARDEN Sec. II.A eq. (1)-(2): AGGREGATE = the mean
+ * over the sampled neighbours, UPDATE = one dense layer on the node's own previous state
+ * concatenated with that mean; the GraphSAGE model of GARDEN Sec. VI.A):
+ *   agg[i, 0..d) = the mean of gnn_mean_aggregate over the block (same arithmetic, bit for bit),
+ *   out[i, n] = act( sum_{k<d} src[dst_lid[i], k] * W[k, n] + sum_{k<d} agg[i, k] * W[d+k, n]
+ *                    + bias[n] ),   act(v) = (relu && v < 0) ? 0 : v.
+ * The product runs on the matrix cores in fp32 (fp32 inputs and accumulation; the summation
+ * order is the kernel's, not a sequential one).
+ * indptr, lid, n_lid, d_n_dst, n_dst, src, ld_src, n_src, d: as for gnn_mean_aggregate.
+ * dst_lid: device [n_dst], each destination's row in src (a block's dst_lid; src is then the
+ *   block's source node features, e.g. X for the outermost block).
+ * W: device fp32, row-major [2d, d_out] (the first d rows multiply the node's own row);
+ * bias: device [d_out] or NULL; 1 <= d_out <= 65536.
+ * agg: device [n_dst, ld_agg], ld_agg >= d, receives the means (caller-owned; also an output).
+ * out: device [n_dst, ld_out], ld_out >= d_out.
+ * Device errors: GNN_ERR_INTERNAL if a lid or a dst_lid lies outside [0, n_src) (written to
+ * *d_status if not NULL; that row then reads row 0).
+ */
+gnn_status gnn_sage_layer(const int32_t *indptr, const int32_t *lid, int64_t n_lid,
+                          const int32_t *dst_lid, const int64_t *d_n_dst, int64_t n_dst,
+                          const float *src, int64_t ld_src, int64_t n_src, int64_t d,
+                          const float *W, const float *bias, int64_t d_out, int32_t relu,
+                          float *agg, int64_t ld_agg, float *out, int64_t ld_out,
+                          int32_t *d_status, gnn_stream stream);
+
+/*
  * Outputs of one (sub-)batch of gnn_minibatch.
  *   x    = X = h_K: [caps.nodes[K-1], ld_h], row i = feature row of V_K[i];
  *   h[l] = h_l for l = 0..K-1: h_0 is [n_seeds, ld_h] (seed order), h_l is [caps.nodes[l-1],

@@ -157,6 +157,13 @@ def test_validation_before_device_work():
     # mean: ld below d
     assert L.gnn_mean_aggregate(8, 8, 4, None, 2, 8, 3, 4, 4, 8, 4, None,
                                 None) == gm.GNN_ERR_INVALID_ARG
+    # sage layer (each call differs from a well-formed one in one argument): d_out 0, ld_out
+    # below d_out, ld_agg below d, missing W
+    args = [8, 8, 4, 8, None, 2, 8, 4, 4, 4, 8, None, 4, 1, 8, 4, 8, 4, None, None]
+    for i, v in ((12, 0), (17, 3), (15, 3), (10, None)):
+        bad = list(args)
+        bad[i] = v
+        assert L.gnn_sage_layer(*bad) == gm.GNN_ERR_INVALID_ARG, i
     # relabel: id bound 0
     n = ctypes.c_size_t()
     assert L.gnn_relabel_workspace_size(0, ctypes.byref(n)) == gm.GNN_ERR_INVALID_ARG
