@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sage", action="store_true",
+                    help="skip the GraphSAGE-mean layer measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU: the mini-batch path is measured on "
@@ -395,11 +397,82 @@ def main():
                               "frac": miss_rate / link["B_link_GBps"], "traffic": None,
                               "peak_source": "measured: best of 5 hipMemcpyAsync of 1 GiB pinned host -> device",
                               "avg_launch_ms": kern["gather"][1], "launches_per_step": launches}
+    if not args.no_sage:
+        result["sage_layer"] = sage_layer(gm, cfg, dg, fs, order, dev)
+        progress("GraphSAGE layer timed")
     progress("stage timing and counts done")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, graph, table, step, args.cpu_seconds,
                                               tot_edges / head_wall)
     print(json.dumps(result), flush=True)
+
+
+SAGE_D_OUT = 128            # GraphSAGE hidden width of GARDEN Sec. VI.A
+FP32_MFMA_TFLOPS = 157.3    # MI355X dense fp32 matrix peak
+
+
+def sage_layer(gm, cfg, dg, fs, order, dev, reps=20):
+    """One GraphSAGE-mean layer (mean, concat, dense UPDATE to 128 features on fp32 matrix cores)
+    over the outermost block of one batch of this workload, X as its source rows.  HIP events on
+    the stream the library runs on time the whole layer and the mean alone; the UPDATE kernel's
+    time is the difference."""
+    import numpy as np
+    import torch
+    K = len(cfg.fanouts)
+    caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
+    mo = gm.MinibatchOut(caps, cfg.d, cfg.ld)
+    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, 1), dtype=torch.uint8, device=dev)
+    gm.gnn_minibatch(dg, fs, order[:cfg.batch].contiguous(), [0, cfg.batch], cfg.fanouts,
+                     gm.gnn_batch_seed(cfg.rng_seed, 0), [mo], ws)
+    cnt = mo.blocks.counts.cpu().tolist()
+    n_dst = cfg.batch if K == 1 else int(cnt[2 * (K - 2) + 1])
+    n_edges = int(cnt[2 * (K - 1)])
+    indptr = mo.blocks.indptr[K - 1][:n_dst + 1]
+    lid = mo.blocks.lid[K - 1]
+    dst_lid = mo.blocks.dst_lid[K - 1]
+    gen = torch.Generator().manual_seed(17)
+    W = (torch.randn(2 * cfg.d, SAGE_D_OUT, generator=gen) / np.sqrt(2 * cfg.d)).to(dev)
+    b = torch.randn(SAGE_D_OUT, generator=gen).to(dev)
+    agg = torch.empty(n_dst, cfg.ld, dtype=torch.float32, device=dev)
+    out = torch.empty(n_dst, SAGE_D_OUT, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def layer():
+        gm.gnn_sage_layer(indptr, lid, dst_lid, mo.x, cfg.d, W, b, True, agg, out,
+                          d_status=status)
+
+    def mean():
+        gm.gnn_mean_aggregate(indptr, lid, mo.x, cfg.d, agg)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_layer, t_mean = timed(layer), timed(mean)
+    if int(status.item()) != gm.GNN_OK:
+        raise RuntimeError("GraphSAGE layer: device status %d" % int(status.item()))
+    t_upd = max(t_layer - t_mean, 1e-6)
+    flops = 2.0 * n_dst * 2 * cfg.d * SAGE_D_OUT
+    upd_bytes = 4.0 * (n_dst * (2 * cfg.d + SAGE_D_OUT + 1) + 2 * cfg.d * SAGE_D_OUT + SAGE_D_OUT)
+    tf = flops / (t_upd * 1e-3) / 1e12
+    return {"block": f"outermost block of one batch ({n_dst} destinations, {n_edges} edges), "
+                     f"X as its source rows",
+            "d": cfg.d, "d_out": SAGE_D_OUT, "dtype": "fp32", "relu": True,
+            "layer_ms": t_layer, "mean_ms": t_mean, "update_ms": t_upd,
+            "update_flops": flops, "update_algorithmic_bytes": upd_bytes,
+            "update_GBps": upd_bytes / (t_upd * 1e-3) / 1e9,
+            "roofline": {"bound": "mfma", "kernel": "k_sage_update", "achieved": tf,
+                         "peak": FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / FP32_MFMA_TFLOPS},
+            "timing": f"HIP events over {reps} calls each of the layer and of the mean alone on "
+                      f"the library's stream; update = layer - mean"}
 
 
 def host_link(gm, table, dev):

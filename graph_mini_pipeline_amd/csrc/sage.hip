@@ -10,11 +10,13 @@
 // mean.  fp32 in, fp32 matrix-core products (v_mfma_f32_16x16x4_f32), fp32 accumulation.
 //
 // Tiling: a 256-thread workgroup owns a 64 x 64 output tile; its four wavefronts own 32 x 32
-// quarters, each four 16 x 16 MFMA accumulators.  K advances in chunks of 32 through two LDS
-// buffers: the next chunk's global loads are issued before the current chunk's MFMAs and stored
-// to the other buffer after them, so one barrier per chunk suffices.  Workgroups b and b + 8 (the
-// same XCD under round-robin dispatch) take the N tiles of one M tile, so the A rows they share
-// are fetched into one L2.
+// quarters, each four 16 x 16 MFMA accumulators (32-row tiles, which double the workgroups of a
+// small block, measured slower: each still loads whole W chunks for half the rows).  K advances
+// in chunks of 32 through two LDS buffers, with the global loads two chunks ahead of the MFMAs
+// (two register sets): chunk c + 1 is stored to the other buffer after chunk c's MFMAs, so one
+// barrier per chunk suffices.
+// Workgroups b and b + 8 (the same XCD under round-robin dispatch) take the N tiles of one M
+// tile, so the A rows they share are fetched into one L2.
 #include "common.hpp"
 
 namespace gnnmb {
@@ -51,7 +53,11 @@ struct SageArgs {
 };
 
 __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
-    __shared__ float As[2][kBM * kAStride];
+    constexpr int BM = kBM;
+    constexpr int EA = BM * kBK / kSageThreads;   // A values per thread per chunk
+    constexpr int TPR = kBK / EA;                 // threads per A row
+    constexpr int MI = BM / 32;                   // 16 x 16 accumulators per wavefront along M
+    __shared__ float As[2][BM * kAStride];
     __shared__ float Bs[2][kBK * kBStride];
     // XCD-aware tile order: 8 consecutive M tiles, then the next N tile of the same 8.
     const int b = static_cast<int>(blockIdx.x);
@@ -61,17 +67,16 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
     const int nt = in_grp / kXcds;
     if (mt >= a.m_tiles) return;   // whole workgroup
     const int64_t n_act = load_count(a.d_n, a.n_cap);
-    const int64_t m0 = static_cast<int64_t>(mt) * kBM;
+    const int64_t m0 = static_cast<int64_t>(mt) * BM;
     if (m0 >= n_act) return;       // whole workgroup
     const int64_t n0 = static_cast<int64_t>(nt) * kBN;
     const int t = static_cast<int>(threadIdx.x);
     const int lane = lane_id();
     const int wv = t >> 6;
     const int wm = wv & 1, wn = wv >> 1;
-    const int64_t K = 2 * a.d;
 
-    // This thread's A row (r) and column octet (ac) and B row (bk) and column octet (bc).
-    const int r = t >> 2, ac = (t & 3) * 8;
+    // This thread's A row (r) and its EA columns (from ac), B row (bk) and column octet (bc).
+    const int r = t / TPR, ac = (t % TPR) * EA;
     const int bk = t >> 3, bc = (t & 7) * 8;
     const int64_t m = m0 + r;
     const bool row_ok = m < n_act;
@@ -86,63 +91,87 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
         self_row = a.src + static_cast<int64_t>(dl) * a.ld_src;
         agg_row = a.agg + m * a.ld_agg;
     }
-    float ra[8], rb[8];
-    auto load_chunk = [&](int64_t k0) {
+    // K runs over two segments, each padded to whole chunks: the node's own row (W rows 0..d)
+    // then the mean (W rows d..2d), so a chunk's columns start at a multiple of 32 inside one
+    // source row.  Octets that lie inside the row use 16-byte loads when rows are 16-byte aligned.
+    const int seg_chunks = static_cast<int>((a.d + kBK - 1) / kBK);
+    const bool a_vec = (a.ld_src % 4 == 0) && (a.ld_agg % 4 == 0) &&
+                       ((reinterpret_cast<uintptr_t>(a.src) | reinterpret_cast<uintptr_t>(a.agg)) % 16 == 0);
+    const bool b_vec = (a.d_out % 4 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0);
+    auto load_chunk = [&](int c, f4 (&ra)[EA / 4], f4 (&rb)[2]) {
+        const bool own = c < seg_chunks;
+        const int64_t k0 = static_cast<int64_t>(own ? c : c - seg_chunks) * kBK;
+        const float *row = own ? self_row : agg_row;
+        const int64_t kk = k0 + ac;
+        if (!row_ok || kk >= a.d) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t kk = k0 + ac + u;
-            float v = 0.f;
-            if (row_ok && kk < K) v = kk < a.d ? self_row[kk] : agg_row[kk - a.d];
-            ra[u] = v;
+            for (int v = 0; v < EA / 4; ++v) ra[v] = f4{0.f, 0.f, 0.f, 0.f};
+        } else if (a_vec && kk + EA <= a.d) {
+            const f4 *p = reinterpret_cast<const f4 *>(row + kk);
+#pragma unroll
+            for (int v = 0; v < EA / 4; ++v) ra[v] = p[v];
+        } else {
+#pragma unroll
+            for (int u = 0; u < EA; ++u) ra[u >> 2][u & 3] = kk + u < a.d ? row[kk + u] : 0.f;
         }
         const int64_t k = k0 + bk;
+        const int64_t n = n0 + bc;
+        const float *wrow = a.W + ((own ? 0 : a.d) + k) * a.d_out;
+        if (k >= a.d || n >= a.d_out) {
+            rb[0] = rb[1] = f4{0.f, 0.f, 0.f, 0.f};
+        } else if (b_vec && n + 8 <= a.d_out) {
+            const f4 *p = reinterpret_cast<const f4 *>(wrow + n);
+            rb[0] = p[0];
+            rb[1] = p[1];
+        } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t n = n0 + bc + u;
-            rb[u] = (k < K && n < a.d_out) ? a.W[k * a.d_out + n] : 0.f;
+            for (int u = 0; u < 8; ++u) rb[u >> 2][u & 3] = n + u < a.d_out ? wrow[n + u] : 0.f;
         }
     };
-    auto store_chunk = [&](int buf) {
+    auto store_chunk = [&](int buf, const f4 (&ra)[EA / 4], const f4 (&rb)[2]) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) As[buf][r * kAStride + ac + u] = ra[u];
+        for (int u = 0; u < EA; ++u) As[buf][r * kAStride + ac + u] = ra[u >> 2][u & 3];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) Bs[buf][bk * kBStride + bc + u] = rb[u];
+        for (int u = 0; u < 8; ++u) Bs[buf][bk * kBStride + bc + u] = rb[u >> 2][u & 3];
     };
 
-    f4 acc[2][2];
+    f4 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    const int nchunks = static_cast<int>((K + kBK - 1) / kBK);
-    load_chunk(0);
-    store_chunk(0);
+    // Two chunks of loads in flight: chunk c + 1 sits in registers set (c + 1) & 1 while chunk
+    // c + 2 is being fetched into the other set.
+    const int nchunks = 2 * seg_chunks;
+    f4 ra[2][EA / 4], rb[2][2];
+    load_chunk(0, ra[0], rb[0]);
+    load_chunk(1, ra[1], rb[1]);
+    store_chunk(0, ra[0], rb[0]);
     __syncthreads();
-    const int arow = wm * 32 + (lane & 15);
+    const int arow = wm * (BM / 2) + (lane & 15);
     const int bcol = wn * 32 + (lane & 15);
     const int kq = lane >> 4;
     for (int c = 0; c < nchunks; ++c) {
         const int cur = c & 1;
-        const bool more = c + 1 < nchunks;
-        if (more) load_chunk(static_cast<int64_t>(c + 1) * kBK);
+        if (c + 2 < nchunks) load_chunk(c + 2, ra[cur], rb[cur]);
         const float *A = As[cur];
         const float *B = Bs[cur];
 #pragma unroll
         for (int ks = 0; ks < kBK / 4; ++ks) {
             const int kr = ks * 4 + kq;
-            float av[2], bv[2];
+            float av[MI], bv[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) av[i] = A[(arow + i * 16) * kAStride + kr];
+            for (int i = 0; i < MI; ++i) av[i] = A[(arow + i * 16) * kAStride + kr];
 #pragma unroll
             for (int j = 0; j < 2; ++j) bv[j] = B[kr * kBStride + bcol + j * 16];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
-        if (more) store_chunk(cur ^ 1);
+        if (c + 1 < nchunks) store_chunk(cur ^ 1, ra[cur ^ 1], rb[cur ^ 1]);
         __syncthreads();
     }
 
@@ -153,10 +182,10 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
         if (col >= a.d_out) continue;
         const float bj = a.bias ? a.bias[col] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t row = m0 + wm * 32 + i * 16 + 4 * kq + q;
+                const int64_t row = m0 + wm * (BM / 2) + i * 16 + 4 * kq + q;
                 if (row >= n_act) continue;
                 float v = acc[i][j][q] + bj;
                 if (a.relu && v < 0.f) v = 0.f;
@@ -189,9 +218,9 @@ hipError_t launch_sage_update(const int32_t *dst_lid, const int64_t *d_n, int64_
     a.relu = relu;
     a.out = out;
     a.ld_out = ld_out;
-    a.m_tiles = static_cast<int32_t>((n_cap + kBM - 1) / kBM);
     a.n_tiles = static_cast<int32_t>((d_out + kBN - 1) / kBN);
     a.status = status;
+    a.m_tiles = static_cast<int32_t>((n_cap + kBM - 1) / kBM);
     const int64_t groups = (a.m_tiles + kXcds - 1) / kXcds;
     const int64_t grid = groups * kXcds * a.n_tiles;
     hipLaunchKernelGGL(k_sage_update, dim3(static_cast<unsigned>(grid)), dim3(kSageThreads), 0, s,

@@ -61,6 +61,7 @@ CASES = [
     (130, 400, 100, 100, 15, True, True, 100, 104, 100),
     (257, 600, 602, 128, 25, True, True, 604, 604, 128),  # the dense workload's row width
     (500, 900, 5, 200, 7, False, True, 8, 5, 203),      # K = 10 < one chunk, 4 N tiles
+    (8300, 9000, 24, 256, 6, True, True, 24, 28, 256),  # enough tiles for 64-row tiles
 ]
 
 
