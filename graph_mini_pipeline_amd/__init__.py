@@ -25,7 +25,7 @@ __all__ = [
     "gnn_status_string", "gnn_batch_seed", "gnn_capacity", "gnn_workspace_size", "gnn_sample_khop",
     "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
     "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_sage_layer",
-    "gnn_minibatch",
+    "gnn_sage_update", "gnn_minibatch",
     "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
     "gnn_timer_elapsed", "gnn_copy_probe", "gnn_copy_probe_host", "gnn_hash_probe", "lib",
 ]
@@ -309,6 +309,32 @@ def gnn_sage_layer(indptr: torch.Tensor, lid: torch.Tensor, dst_lid: torch.Tenso
                               _ptr(bias), d_out, 1 if relu else 0, _ptr(agg), agg.shape[1],
                               _ptr(out), out.shape[1], _ptr(d_status), _stream(stream))
     _ok(st, "gnn_sage_layer")
+
+
+def gnn_sage_update(dst_lid: torch.Tensor, src: torch.Tensor, d: int, agg: torch.Tensor,
+                    W: torch.Tensor, bias: Optional[torch.Tensor], relu: bool, out: torch.Tensor,
+                    n_dst: Optional[int] = None, d_n_dst: Optional[torch.Tensor] = None,
+                    d_status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The UPDATE alone: out = act([src[dst_lid] || agg] @ W + bias) for n_dst rows (default:
+    dst_lid.numel()); agg holds the means."""
+    _need(dst_lid, torch.int32, "dst_lid")
+    for t, n in ((src, "src"), (W, "W"), (agg, "agg"), (out, "out")):
+        _need(t, torch.float32, n)
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+    n = dst_lid.numel() if n_dst is None else n_dst
+    if W.dim() != 2 or W.shape[0] != 2 * d or not W.is_contiguous():
+        raise ValueError("W must be a contiguous [2d, d_out] tensor")
+    d_out = W.shape[1]
+    if bias is not None and bias.numel() < d_out:
+        raise ValueError("bias shorter than d_out")
+    if dst_lid.numel() < n or agg.shape[0] < n or out.shape[0] < n:
+        raise ValueError("dst_lid / agg / out have fewer rows than destinations")
+    st = lib().gnn_sage_update(_ptr(dst_lid), _ptr(d_n_dst), n, _ptr(src), src.shape[1],
+                               src.shape[0], d, _ptr(agg), agg.shape[1], _ptr(W), _ptr(bias), d_out,
+                               1 if relu else 0, _ptr(out), out.shape[1], _ptr(d_status),
+                               _stream(stream))
+    _ok(st, "gnn_sage_update")
 
 
 class MinibatchOut:

@@ -75,6 +75,8 @@ SIGNATURES = {
     "gnn_feature_store_destroy": (i32, [vp]),
     "gnn_gather_features": (i32, [vp, vp, vp, i64, vp, i64, vp, vp, vp]),
     "gnn_mean_aggregate": (i32, [vp, vp, i64, vp, i64, vp, i64, i64, i64, vp, i64, vp, vp]),
+    "gnn_sage_update": (i32, [vp, vp, i64, vp, i64, i64, i64, vp, i64, vp, vp, i64, i32, vp, i64,
+                              vp, vp]),
     "gnn_sage_layer": (i32, [vp, vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, vp, i64, i32, vp, i64,
                              vp, i64, vp, vp]),
     "gnn_minibatch": (i32, [P(gnn_graph), vp, vp, P(i64), i32, P(i32), i32, u64,

@@ -755,20 +755,44 @@ gnn_status gnn_mean_aggregate(const int32_t *indptr, const int32_t *lid, int64_t
     return GNN_OK;
 }
 
+namespace {
+gnn_status check_sage(const int32_t *dst_lid, int64_t n_dst, const float *src, int64_t ld_src,
+                      int64_t n_src, int64_t d, const float *agg, int64_t ld_agg, const float *W,
+                      int64_t d_out, const float *out, int64_t ld_out) {
+    if (n_dst < 0 || n_src < 0 || d < 1 || ld_src < d || ld_agg < d) return GNN_ERR_INVALID_ARG;
+    if (d_out < 1 || d_out > 65536 || ld_out < d_out) return GNN_ERR_INVALID_ARG;
+    if (n_dst > 0 && (!dst_lid || !src || !W || !agg || !out || n_src < 1))
+        return GNN_ERR_INVALID_ARG;
+    if (n_dst * d > kFlatMax || n_dst * d_out > kFlatMax || n_dst > kFlatMax / 64)
+        return GNN_ERR_UNSUPPORTED;
+    return GNN_OK;
+}
+}  // namespace
+
+gnn_status gnn_sage_update(const int32_t *dst_lid, const int64_t *d_n_dst, int64_t n_dst,
+                           const float *src, int64_t ld_src, int64_t n_src, int64_t d,
+                           const float *agg, int64_t ld_agg, const float *W, const float *bias,
+                           int64_t d_out, int32_t relu, float *out, int64_t ld_out,
+                           int32_t *d_status, gnn_stream stream) {
+    const gnn_status st =
+        check_sage(dst_lid, n_dst, src, ld_src, n_src, d, agg, ld_agg, W, d_out, out, ld_out);
+    if (st != GNN_OK) return st;
+    GNN_TRY_HIP(launch_sage_update(dst_lid, d_n_dst, n_dst, src, ld_src, n_src, agg, ld_agg, d, W,
+                                   bias, d_out, relu, out, ld_out, d_status,
+                                   static_cast<hipStream_t>(stream)));
+    return GNN_OK;
+}
+
 gnn_status gnn_sage_layer(const int32_t *indptr, const int32_t *lid, int64_t n_lid,
                           const int32_t *dst_lid, const int64_t *d_n_dst, int64_t n_dst,
                           const float *src, int64_t ld_src, int64_t n_src, int64_t d,
                           const float *W, const float *bias, int64_t d_out, int32_t relu,
                           float *agg, int64_t ld_agg, float *out, int64_t ld_out,
                           int32_t *d_status, gnn_stream stream) {
-    if (n_dst < 0 || n_lid < 0 || n_src < 0 || d < 1 || ld_src < d || ld_agg < d)
-        return GNN_ERR_INVALID_ARG;
-    if (d_out < 1 || d_out > 65536 || ld_out < d_out) return GNN_ERR_INVALID_ARG;
-    if (n_dst > 0 && (!indptr || !dst_lid || !src || !W || !agg || !out || n_src < 1))
-        return GNN_ERR_INVALID_ARG;
-    if (n_lid > 0 && !lid) return GNN_ERR_INVALID_ARG;
-    if (n_dst * d > kFlatMax || n_dst * d_out > kFlatMax || n_dst > kFlatMax / 64)
-        return GNN_ERR_UNSUPPORTED;
+    gnn_status st =
+        check_sage(dst_lid, n_dst, src, ld_src, n_src, d, agg, ld_agg, W, d_out, out, ld_out);
+    if (st != GNN_OK) return st;
+    if (n_lid < 0 || (n_dst > 0 && !indptr) || (n_lid > 0 && !lid)) return GNN_ERR_INVALID_ARG;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const MeanJob job{indptr, lid, n_lid, d_n_dst, n_dst, src, n_src, agg};
     GNN_TRY_HIP(launch_mean(&job, 1, ld_src, ld_agg, d, 16, d_status, s));

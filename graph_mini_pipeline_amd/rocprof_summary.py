@@ -38,11 +38,13 @@ KERNEL_SOURCES = {
     "k_dist": "csrc/superbatch.hip",
     "k_copy_probe": "csrc/probe.hip",
     "k_fill": "csrc/relabel.hip",
+    "k_sage_update": "csrc/sage.hip",
 }
 
 
 def short_name(name: str) -> str:
-    n = name.split("(")[0].replace("void ", "").replace("gnnmb::", "").strip()
+    n = name.replace("(anonymous namespace)::", "")
+    n = n.split("(")[0].replace("void ", "").replace("gnnmb::", "").strip()
     return n
 
 

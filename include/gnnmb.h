@@ -263,6 +263,21 @@ gnn_status gnn_sage_layer(const int32_t *indptr, const int32_t *lid, int64_t n_l
                           int32_t *d_status, gnn_stream stream);
 
 /*
+ * The UPDATE of gnn_sage_layer alone, for means computed elsewhere (for instance h_{l-1} of
+ * gnn_minibatch, which holds the means of block l):
+ *   out[i, n] = act( sum_{k<d} src[dst_lid[i], k] * W[k, n] + sum_{k<d} agg[i, k] * W[d+k, n]
+ *                    + bias[n] ),   act(v) = (relu && v < 0) ? 0 : v,
+ * for i < n_dst (or < *d_n_dst when d_n_dst is not NULL).  Arguments as for gnn_sage_layer; agg is
+ * read, not written.  fp32 matrix-core products and accumulation.
+ * Device errors: GNN_ERR_INTERNAL if a dst_lid lies outside [0, n_src).
+ */
+gnn_status gnn_sage_update(const int32_t *dst_lid, const int64_t *d_n_dst, int64_t n_dst,
+                           const float *src, int64_t ld_src, int64_t n_src, int64_t d,
+                           const float *agg, int64_t ld_agg, const float *W, const float *bias,
+                           int64_t d_out, int32_t relu, float *out, int64_t ld_out,
+                           int32_t *d_status, gnn_stream stream);
+
+/*
  * Outputs of one (sub-)batch of gnn_minibatch.
  *   x    = X = h_K: [caps.nodes[K-1], ld_h], row i = feature row of V_K[i];
  *   h[l] = h_l for l = 0..K-1: h_0 is [n_seeds, ld_h] (seed order), h_l is [caps.nodes[l-1],

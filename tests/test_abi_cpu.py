@@ -164,6 +164,11 @@ def test_validation_before_device_work():
         bad = list(args)
         bad[i] = v
         assert L.gnn_sage_layer(*bad) == gm.GNN_ERR_INVALID_ARG, i
+    uargs = [8, None, 2, 8, 4, 4, 4, 8, 4, 8, None, 4, 1, 8, 4, None, None]
+    for i, v in ((11, 0), (14, 3), (8, 3), (9, None), (0, None)):
+        bad = list(uargs)
+        bad[i] = v
+        assert L.gnn_sage_update(*bad) == gm.GNN_ERR_INVALID_ARG, i
     # relabel: id bound 0
     n = ctypes.c_size_t()
     assert L.gnn_relabel_workspace_size(0, ctypes.byref(n)) == gm.GNN_ERR_INVALID_ARG

@@ -172,3 +172,12 @@ def test_sage_layer_on_dense_outermost_block():
                                  with_scale=True)
     got = out[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
     assert (np.abs(got - ref) <= _tol(mag, cfg.d, max(cfg.fanouts))).all()
+    # the UPDATE alone on the means gnn_minibatch computed (h_{K-1}) gives the same bits
+    h = mo.h[K - 1]
+    assert torch.equal(h[:n_dst, :cfg.d], agg[:n_dst, :cfg.d])
+    out2 = torch.empty_like(out)
+    gm.gnn_sage_update(_dev(dst_lid), mo.x, cfg.d, h, W.cuda(), b.cuda(), True, out2,
+                       d_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == gm.GNN_OK
+    assert torch.equal(out2, out)

@@ -70,3 +70,10 @@ def test_interleaved_gathers_are_not_copies(tmp_path):
     assert rs.read_traffic(str(out), "k_gather_rows<32, 1, 4>@copy") is None
     assert rs.read_traffic(str(out), "k_mean_v5<32, 1, 4>@outer")["fetch_bytes"] == 50.0 * 1024 * 2
     assert rs.read_traffic(str(out), "k_mean_v5<32, 1, 4>@inner")["fetch_bytes"] == 5.0 * 1024 * 2
+
+
+def test_short_name_strips_namespaces_and_arguments():
+    assert rs.short_name("void gnnmb::(anonymous namespace)::k_sage_update("
+                         "gnnmb::(anonymous namespace)::SageArgs)") == "k_sage_update"
+    assert rs.short_name("void gnnmb::k_mean_v5<64, 3, 4>(gnnmb::MeanArgs)") == "k_mean_v5<64, 3, 4>"
+    assert rs.source_of("k_sage_update") == "csrc/sage.hip"
