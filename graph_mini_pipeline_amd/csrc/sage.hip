@@ -12,8 +12,8 @@
 // Tiling: a 256-thread workgroup owns a 64 x 64 output tile; its four wavefronts own 32 x 32
 // quarters, each four 16 x 16 MFMA accumulators (32-row tiles, which double the workgroups of a
 // small block, measured slower: each still loads whole W chunks for half the rows).  K advances
-// in chunks of 32 through two LDS buffers, with the global loads two chunks ahead of the MFMAs
-// (two register sets): chunk c + 1 is stored to the other buffer after chunk c's MFMAs, so one
+// in chunks of 32 through two LDS buffers, with the global loads kDepth chunks ahead of the MFMAs
+// (kDepth register sets): chunk c + 1 is stored to the other buffer after chunk c's MFMAs, so one
 // barrier per chunk suffices.
 // Workgroups b and b + 8 (the same XCD under round-robin dispatch) take the N tiles of one M
 // tile, so the A rows they share are fetched into one L2.
@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kSageThreads = 256;
 constexpr int kBM = 64, kBN = 64, kBK = 32;
+constexpr int kDepth = 4;          // chunks of global loads in flight (measured best of 2..5)
 constexpr int kAStride = kBK + 4;    // LDS row strides chosen so that one MFMA operand read
 constexpr int kBStride = kBN + 16;   // touches 64 distinct banks
 constexpr int kXcds = 8;
@@ -56,6 +57,8 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
     constexpr int BM = kBM;
     constexpr int EA = BM * kBK / kSageThreads;   // A values per thread per chunk
     constexpr int TPR = kBK / EA;                 // threads per A row
+    constexpr int EB = kBK * kBN / kSageThreads;  // B values per thread per chunk
+    constexpr int TPB = kBN / EB;                 // threads per B row
     constexpr int MI = BM / 32;                   // 16 x 16 accumulators per wavefront along M
     __shared__ float As[2][BM * kAStride];
     __shared__ float Bs[2][kBK * kBStride];
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
 
     // This thread's A row (r) and its EA columns (from ac), B row (bk) and column octet (bc).
     const int r = t / TPR, ac = (t % TPR) * EA;
-    const int bk = t >> 3, bc = (t & 7) * 8;
+    const int bk = t / TPB, bc = (t % TPB) * EB;
     const int64_t m = m0 + r;
     const bool row_ok = m < n_act;
     const float *self_row = a.src;
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
     const bool a_vec = (a.ld_src % 4 == 0) && (a.ld_agg % 4 == 0) &&
                        ((reinterpret_cast<uintptr_t>(a.src) | reinterpret_cast<uintptr_t>(a.agg)) % 16 == 0);
     const bool b_vec = (a.d_out % 4 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0);
-    auto load_chunk = [&](int c, f4 (&ra)[EA / 4], f4 (&rb)[2]) {
+    auto load_chunk = [&](int c, f4 (&ra)[EA / 4], f4 (&rb)[EB / 4]) {
         const bool own = c < seg_chunks;
         const int64_t k0 = static_cast<int64_t>(own ? c : c - seg_chunks) * kBK;
         const float *row = own ? self_row : agg_row;
@@ -118,21 +121,22 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
         const int64_t n = n0 + bc;
         const float *wrow = a.W + ((own ? 0 : a.d) + k) * a.d_out;
         if (k >= a.d || n >= a.d_out) {
-            rb[0] = rb[1] = f4{0.f, 0.f, 0.f, 0.f};
-        } else if (b_vec && n + 8 <= a.d_out) {
+#pragma unroll
+            for (int v = 0; v < EB / 4; ++v) rb[v] = f4{0.f, 0.f, 0.f, 0.f};
+        } else if (b_vec && n + EB <= a.d_out) {
             const f4 *p = reinterpret_cast<const f4 *>(wrow + n);
-            rb[0] = p[0];
-            rb[1] = p[1];
+#pragma unroll
+            for (int v = 0; v < EB / 4; ++v) rb[v] = p[v];
         } else {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) rb[u >> 2][u & 3] = n + u < a.d_out ? wrow[n + u] : 0.f;
+            for (int u = 0; u < EB; ++u) rb[u >> 2][u & 3] = n + u < a.d_out ? wrow[n + u] : 0.f;
         }
     };
-    auto store_chunk = [&](int buf, const f4 (&ra)[EA / 4], const f4 (&rb)[2]) {
+    auto store_chunk = [&](int buf, const f4 (&ra)[EA / 4], const f4 (&rb)[EB / 4]) {
 #pragma unroll
         for (int u = 0; u < EA; ++u) As[buf][r * kAStride + ac + u] = ra[u >> 2][u & 3];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) Bs[buf][bk * kBStride + bc + u] = rb[u >> 2][u & 3];
+        for (int u = 0; u < EB; ++u) Bs[buf][bk * kBStride + bc + u] = rb[u >> 2][u & 3];
     };
 
     f4 acc[MI][2];
@@ -141,22 +145,25 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // Two chunks of loads in flight: chunk c + 1 sits in registers set (c + 1) & 1 while chunk
-    // c + 2 is being fetched into the other set.
+    // kDepth chunks of loads in flight: at chunk c, chunks c + 1 .. c + kDepth - 1 sit in register
+    // sets (c + 1) % kDepth ..., while chunk c + kDepth is fetched into set c % kDepth, whose chunk
+    // c went to LDS one step earlier.  The loop is unrolled by kDepth so that the sets are
+    // registers.
     const int nchunks = 2 * seg_chunks;
-    f4 ra[2][EA / 4], rb[2][2];
-    load_chunk(0, ra[0], rb[0]);
-    load_chunk(1, ra[1], rb[1]);
+    f4 ra[kDepth][EA / 4], rb[kDepth][EB / 4];
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q)
+        if (q < nchunks) load_chunk(q, ra[q], rb[q]);
     store_chunk(0, ra[0], rb[0]);
     __syncthreads();
     const int arow = wm * (BM / 2) + (lane & 15);
     const int bcol = wn * 32 + (lane & 15);
     const int kq = lane >> 4;
-    for (int c = 0; c < nchunks; ++c) {
-        const int cur = c & 1;
-        if (c + 2 < nchunks) load_chunk(c + 2, ra[cur], rb[cur]);
-        const float *A = As[cur];
-        const float *B = Bs[cur];
+    auto step = [&](int c, f4 (&la)[EA / 4], f4 (&lb)[EB / 4], const f4 (&sa)[EA / 4],
+                    const f4 (&sb)[EB / 4]) {
+        if (c + kDepth < nchunks) load_chunk(c + kDepth, la, lb);
+        const float *A = As[c & 1];
+        const float *B = Bs[c & 1];
 #pragma unroll
         for (int ks = 0; ks < kBK / 4; ++ks) {
             const int kr = ks * 4 + kq;
@@ -171,8 +178,14 @@ __global__ __launch_bounds__(kSageThreads) void k_sage_update(SageArgs a) {
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
-        if (c + 1 < nchunks) store_chunk(cur ^ 1, ra[cur ^ 1], rb[cur ^ 1]);
+        if (c + 1 < nchunks) store_chunk((c + 1) & 1, sa, sb);
         __syncthreads();
+    };
+    for (int c = 0; c < nchunks; c += kDepth) {
+#pragma unroll
+        for (int q = 0; q < kDepth; ++q)
+            if (c + q < nchunks)
+                step(c + q, ra[q], rb[q], ra[(q + 1) % kDepth], rb[(q + 1) % kDepth]);
     }
 
     // Lane holds rows 4 * (lane / 16) + q, column lane % 16 of each 16 x 16 accumulator.
