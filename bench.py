@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fanouts", default="",
+                    help="comma-separated fanouts replacing the workload's (fanouts[0] at hop 1), "
+                         "e.g. 5,10,15 for GARDEN's fanout-pattern sweep")
     ap.add_argument("--no-sage", action="store_true",
                     help="skip the GraphSAGE-mean layer measurement")
     args = ap.parse_args()
@@ -120,6 +123,9 @@ def main():
     import synth
 
     cfg = synth.CONFIGS[args.config]
+    if args.fanouts:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, fanouts=[int(f) for f in args.fanouts.split(",")])
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()

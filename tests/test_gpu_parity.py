@@ -46,6 +46,25 @@ def test_tiny_pipeline_matches_oracle(tiny, batch):
     compare_with_oracle(outs[0], ref, cfg.d)
 
 
+@pytest.mark.parametrize("fanouts", [[5, 10], [5, 10, 15], [5, 5, 10, 10]])
+@pytest.mark.parametrize("mode", ["full", "compact"])
+def test_fanout_patterns(tiny, fanouts, mode):
+    """GARDEN's fanout-pattern sweep (two to four hops), in super-batches of three overlapping
+    sub-batches, in both relabel modes."""
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    seeds = np.concatenate([order[:300], order[200:450], order[100:180]])   # overlapping
+    ptr = [0, 300, 550, 630]
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 5)
+    opts = gm.Options(superbatch=mode)
+    outs, st = run_minibatch(dg, fs, seeds, fanouts, seed64, opts, group_ptr=ptr)
+    assert st == gm.GNN_OK
+    for g in range(3):
+        ref = oracle.minibatch(indptr, indices, x, seeds[ptr[g]:ptr[g + 1]], fanouts, seed64)
+        compare_with_oracle(outs[g], ref, cfg.d)
+
+
 @pytest.mark.parametrize("group_max,wave_max", [(1, 1), (8, 32), (16, 100), (256, 4096), (256, 16384),
                                                 (100000, 100000)])
 def test_degree_classes_do_not_change_results(tiny, group_max, wave_max):
