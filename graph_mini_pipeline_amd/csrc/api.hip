@@ -660,7 +660,7 @@ gnn_status gnn_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t
     r.list[0] = IdList{keep, nullptr, n_keep, keep_lid, 0, 0};
     r.list[1] = IdList{add, d_n_add, n_add, add_lid, 0, 0};
     r.nbm = 1;
-    r.out[0] = BitmapOut{uniq, cap_uniq, d_n_uniq};
+    r.out[0] = BitmapOut{uniq, cap_uniq, d_n_uniq, nullptr};
     r.id_bound = id_bound;
     r.bitmap = w.bitmaps;
     r.wprefix = w.wprefix;
