@@ -112,13 +112,17 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) 
     }
 }
 
-// Many blocks: one workgroup scans the per-block sums (edge counts, four class counts) in place.
+// Many blocks: one workgroup scans the per-block sums (edges, then the category counts) in place,
+// over the blocks that hold frontier nodes (the grid is sized by the frontier bound; the blocks
+// past the actual frontier place nothing and their sums are not read).
 __global__ __launch_bounds__(1024) void k_classify_scan(HopArgs a) {
     __shared__ uint32_t smem[16];
-    const int nb = a.nb;
+    const int64_t F = load_count(a.d_F, a.F_cap);
+    const int64_t live = (F + kClassifyTile - 1) / kClassifyTile;
+    const int nb = static_cast<int>(live < a.nb ? live : a.nb);
     const int per = (nb + 1023) / 1024;
     for (int col = 0; col < kCols; ++col) {
-        uint32_t *arr = a.bsum + static_cast<int64_t>(col) * nb;
+        uint32_t *arr = a.bsum + static_cast<int64_t>(col) * a.nb;
         const int b0 = threadIdx.x * per;
         uint32_t local = 0;
         for (int t = 0; t < per; ++t)

@@ -65,6 +65,8 @@ __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, i
 
 // Tiles of kDistTile destinations: wavefront 0 handles one destination per lane.  The whole grid
 // first zeroes the live words of the sub-batch bitmaps that the sub-batch relabel marks next.
+// The grid is capped (kDistMaxGrid) and workgroups stride over the tiles, which are sized by the
+// frontier bounds: tiles past a sub-batch's actual destinations are skipped, not dispatched.
 __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
     if (a.clear_ptr) {
         const int64_t n1 = load_count(a.d_U1, a.U1_cap);
@@ -85,20 +87,23 @@ __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
         }
     }
     if (threadIdx.x >= kDistTile) return;
-    const int t = blockIdx.x;
-    const int sg = find_sub(a, t);
-    const DistSub &S = a.sub[sg];
-    const int64_t F = load_count(S.d_F, S.F_cap);
-    const int64_t i = static_cast<int64_t>(t - S.tile0) * kDistTile + threadIdx.x;
-    int64_t lo;
-    int32_t c = 0, np, r;
-    if (i < F) {
-        union_row(a, S, i, lo, c, np, r);
-        if (S.f_pos) S.f_pos[i] = np;
-        if (a.inv && r >= 0) a.inv[static_cast<int64_t>(r) * a.G + sg] = static_cast<int32_t>(i + 1);
+    for (int t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+        const int sg = find_sub(a, t);
+        const DistSub &S = a.sub[sg];
+        const int64_t F = load_count(S.d_F, S.F_cap);
+        const int64_t i0 = static_cast<int64_t>(t - S.tile0) * kDistTile;
+        if (i0 >= F) continue;   // past the destinations: k_dist_scatter reads no sum for it
+        const int64_t i = i0 + threadIdx.x;
+        int64_t lo;
+        int32_t c = 0, np, r;
+        if (i < F) {
+            union_row(a, S, i, lo, c, np, r);
+            if (S.f_pos) S.f_pos[i] = np;
+            if (a.inv && r >= 0) a.inv[static_cast<int64_t>(r) * a.G + sg] = static_cast<int32_t>(i + 1);
+        }
+        const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
+        if (threadIdx.x == 0) a.bsum[t] = sum;
     }
-    const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
-    if (threadIdx.x == 0) a.bsum[t] = sum;
 }
 
 __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
@@ -106,70 +111,75 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
     __shared__ uint32_t s_off, s_tot;
     __shared__ uint32_t s_item_off[kDistTile + 1];
     __shared__ int64_t s_item_lo[kDistTile];
-    const int t = blockIdx.x;
-    const DistSub &S = a.sub[find_sub(a, t)];
-    const int lt = t - S.tile0;
-    const int64_t F = load_count(S.d_F, S.F_cap);
-    // tiles past the actual destinations have nothing to place (tile 0 still writes the totals)
-    const int live = static_cast<int>((F + kDistTile - 1) / kDistTile);
-    if (lt > 0 && lt >= live) return;
-    uint32_t before = 0, all = 0;
-    for (int b = threadIdx.x; b < live; b += blockDim.x) {
-        const uint32_t x = a.bsum[S.tile0 + b];
-        all += x;
-        if (b < lt) before += x;
-    }
-    before = wave_sum(before);
-    all = wave_sum(all);
-    if (lane_id() == 0) {
-        s_red[0][threadIdx.x >> 6] = before;
-        s_red[1][threadIdx.x >> 6] = all;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t b0 = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
-        const uint32_t tot = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-        s_off = b0;
-        if (lt == 0) {
-            S.blk_indptr[F] = static_cast<int32_t>(tot);
-            *S.d_E = tot;
-            if (static_cast<int64_t>(tot) > S.E_cap) set_status(a.status, GNN_ERR_CAPACITY);
+    for (int t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+        const DistSub &S = a.sub[find_sub(a, t)];
+        const int lt = t - S.tile0;
+        const int64_t F = load_count(S.d_F, S.F_cap);
+        // tiles past the actual destinations have nothing to place (tile 0 still writes the totals)
+        const int live = static_cast<int>((F + kDistTile - 1) / kDistTile);
+        if (lt > 0 && lt >= live) continue;
+        uint32_t before = 0, all = 0;
+        for (int b = threadIdx.x; b < live; b += blockDim.x) {
+            const uint32_t x = a.bsum[S.tile0 + b];
+            all += x;
+            if (b < lt) before += x;
         }
-    }
-    __syncthreads();
-    if (threadIdx.x < kDistTile) {
-        const int64_t i = static_cast<int64_t>(lt) * kDistTile + threadIdx.x;
-        int64_t lo = 0;
-        int32_t c = 0, np, r;
-        if (i < F) union_row(a, S, i, lo, c, np, r);
-        const uint32_t inc = wave_inclusive_scan(static_cast<uint32_t>(c));
-        const uint32_t o = inc - static_cast<uint32_t>(c);
-        s_item_off[threadIdx.x] = o;
-        s_item_lo[threadIdx.x] = lo;
-        if (threadIdx.x == kDistTile - 1) s_tot = inc;
-        if (i < F) S.blk_indptr[i] = static_cast<int32_t>(s_off + o);
-    }
-    __syncthreads();
-    const uint32_t tot = s_tot;
-    for (uint32_t p = threadIdx.x; p < tot; p += blockDim.x) {
-        int lo_i = 0, hi_i = kDistTile;  // last destination whose offset is <= p
-        while (hi_i - lo_i > 1) {
-            const int mid = (lo_i + hi_i) >> 1;
-            if (s_item_off[mid] <= p) lo_i = mid;
-            else hi_i = mid;
+        before = wave_sum(before);
+        all = wave_sum(all);
+        if (lane_id() == 0) {
+            s_red[0][threadIdx.x >> 6] = before;
+            s_red[1][threadIdx.x >> 6] = all;
         }
-        const int64_t dst = static_cast<int64_t>(s_off) + p;
-        const int64_t src = s_item_lo[lo_i] + (p - s_item_off[lo_i]);
-        if (dst < S.E_cap) {
-            S.blk_gid[dst] = a.u_gid[src];
-            if (S.e_pos) S.e_pos[dst] = a.u_pos[src];
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t b0 = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+            const uint32_t tot = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+            s_off = b0;
+            if (lt == 0) {
+                S.blk_indptr[F] = static_cast<int32_t>(tot);
+                *S.d_E = tot;
+                if (static_cast<int64_t>(tot) > S.E_cap) set_status(a.status, GNN_ERR_CAPACITY);
+            }
         }
+        __syncthreads();
+        if (threadIdx.x < kDistTile) {
+            const int64_t i = static_cast<int64_t>(lt) * kDistTile + threadIdx.x;
+            int64_t lo = 0;
+            int32_t c = 0, np, r;
+            if (i < F) union_row(a, S, i, lo, c, np, r);
+            const uint32_t inc = wave_inclusive_scan(static_cast<uint32_t>(c));
+            const uint32_t o = inc - static_cast<uint32_t>(c);
+            s_item_off[threadIdx.x] = o;
+            s_item_lo[threadIdx.x] = lo;
+            if (threadIdx.x == kDistTile - 1) s_tot = inc;
+            if (i < F) S.blk_indptr[i] = static_cast<int32_t>(s_off + o);
+        }
+        __syncthreads();
+        const uint32_t tot = s_tot;
+        for (uint32_t p = threadIdx.x; p < tot; p += blockDim.x) {
+            int lo_i = 0, hi_i = kDistTile;  // last destination whose offset is <= p
+            while (hi_i - lo_i > 1) {
+                const int mid = (lo_i + hi_i) >> 1;
+                if (s_item_off[mid] <= p) lo_i = mid;
+                else hi_i = mid;
+            }
+            const int64_t dst = static_cast<int64_t>(s_off) + p;
+            const int64_t src = s_item_lo[lo_i] + (p - s_item_off[lo_i]);
+            if (dst < S.E_cap) {
+                S.blk_gid[dst] = a.u_gid[src];
+                if (S.e_pos) S.e_pos[dst] = a.u_pos[src];
+            }
+        }
+        __syncthreads();   // the shared arrays are rewritten by the next tile
     }
 }
 
+constexpr int kDistMaxGrid = 4096;
+
 hipError_t launch_dist(const DistArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_dist_count, dim3(a.ntiles), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_dist_scatter, dim3(a.ntiles), dim3(256), 0, s, a);
+    const unsigned grid = static_cast<unsigned>(a.ntiles < kDistMaxGrid ? a.ntiles : kDistMaxGrid);
+    hipLaunchKernelGGL(k_dist_count, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_dist_scatter, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
