@@ -65,6 +65,25 @@ def test_fanout_patterns(tiny, fanouts, mode):
         compare_with_oracle(outs[g], ref, cfg.d)
 
 
+@pytest.mark.parametrize("mode", ["full", "compact"])
+def test_max_hops(tiny, mode):
+    """GNN_MAX_HOPS = 8 hops (the last ones saturate the 10k-node graph), two sub-batches."""
+    cfg, indptr, indices, x, order = tiny
+    fanouts = [3, 2, 2, 2, 2, 2, 2, 2]
+    assert len(fanouts) == 8
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    seeds = order[:96]
+    ptr = [0, 40, 96]
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 9)
+    outs, st = run_minibatch(dg, fs, seeds, fanouts, seed64, gm.Options(superbatch=mode),
+                             group_ptr=ptr)
+    assert st == gm.GNN_OK
+    for g in range(2):
+        ref = oracle.minibatch(indptr, indices, x, seeds[ptr[g]:ptr[g + 1]], fanouts, seed64)
+        compare_with_oracle(outs[g], ref, cfg.d)
+
+
 @pytest.mark.parametrize("group_max,wave_max", [(1, 1), (8, 32), (16, 100), (256, 4096), (256, 16384),
                                                 (100000, 100000)])
 def test_degree_classes_do_not_change_results(tiny, group_max, wave_max):
