@@ -3,6 +3,11 @@ counter summary into per-launch memory traffic.
 
     python -m graph_mini_pipeline_amd.rocprof_summary trace OUT.txt KERNEL_TRACE.csv "COMMAND"
     python -m graph_mini_pipeline_amd.rocprof_summary counters OUT.txt WORKLOAD FETCH.csv WRITE.csv "COMMAND"
+    python -m graph_mini_pipeline_amd.rocprof_summary metrics OUT.txt COUNTERS.csv "COMMAND"
+
+A metrics summary averages every counter or derived metric of a --pmc run per kernel (for
+instance VALUBusy and MfmaUtil, the percentages of the active cycles in which the vector ALUs or
+the matrix cores issue).
 
 Counter summaries hold one machine-readable line per kernel:
     counters <kernel> dispatches=<n> fetch_kib=<avg> write_kib=<avg> source=<file> sha256=<hash>
@@ -148,6 +153,26 @@ def counter_summary(workload: str, fetch_csv: str, write_csv: str, command: str)
     return "\n".join(out) + "\n"
 
 
+def metrics_summary(counters_csv: str, command: str) -> str:
+    rows = [r for r in csv.DictReader(open(counters_csv)) if "gnnmb" in r["Kernel_Name"]]
+    names = sorted({r["Counter_Name"] for r in rows})
+    per = defaultdict(lambda: defaultdict(list))
+    for r in rows:
+        per[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = ["# rocprofv3 --pmc " + " ".join(names) + ": per-kernel averages over its dispatches",
+           f"# command: {command}",
+           "# kernel".ljust(40) + " dispatches " + " ".join(f"{n:>16s}" for n in names) + "  source"]
+    for k in sorted(per):
+        vals = per[k]
+        n = max(len(v) for v in vals.values())
+        src = source_of(k)
+        tag = f"{src} sha256={source_hash(src)}" if src else "-"
+        out.append(f"{k[:40]:40s} {n:10d} " +
+                   " ".join(f"{sum(vals[c]) / len(vals[c]):16.3f}" if vals.get(c) else f"{'-':>16s}"
+                            for c in names) + f"  {tag}")
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(path: str, kernel: str, grid_free: bool = True) -> Optional[dict]:
     """Calibrated bytes per dispatch of `kernel` from a counter summary, or None when the file is
     missing, lacks the kernel or the calibration, or the kernel's source changed since."""
@@ -183,6 +208,9 @@ if __name__ == "__main__":
     elif mode == "counters":
         out, workload, fcsv, wcsv, cmd = sys.argv[2:7]
         text = counter_summary(workload, fcsv, wcsv, cmd)
+    elif mode == "metrics":
+        out, ccsv, cmd = sys.argv[2:5]
+        text = metrics_summary(ccsv, cmd)
     else:
         raise SystemExit(__doc__)
     with open(out, "w") as fh:

@@ -77,3 +77,20 @@ def test_short_name_strips_namespaces_and_arguments():
                          "gnnmb::(anonymous namespace)::SageArgs)") == "k_sage_update"
     assert rs.short_name("void gnnmb::k_mean_v5<64, 3, 4>(gnnmb::MeanArgs)") == "k_mean_v5<64, 3, 4>"
     assert rs.source_of("k_sage_update") == "csrc/sage.hip"
+
+
+def test_metrics_summary_averages_per_kernel(tmp_path):
+    p = tmp_path / "m.csv"
+    cols = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for i, (k, c, v) in enumerate([("k_sample", "VALUBusy", 60.0), ("k_sample", "VALUBusy", 70.0),
+                                       ("k_sample", "MfmaUtil", 0.0), ("k_sage_update", "MfmaUtil", 40.0)]):
+            w.writerow({"Dispatch_Id": i, "Grid_Size": 1, "Kernel_Name": f"void gnnmb::{k}(a)",
+                        "Counter_Name": c, "Counter_Value": v})
+    text = rs.metrics_summary(str(p), "cmd")
+    lines = {l.split()[0]: l.split() for l in text.splitlines() if not l.startswith("#")}
+    assert lines["k_sample"][1] == "2" and float(lines["k_sample"][3]) == 65.0   # VALUBusy column
+    assert float(lines["k_sage_update"][2]) == 40.0                             # MfmaUtil column
+    assert lines["k_sage_update"][3] == "-"
