@@ -1,0 +1,42 @@
+"""The benchmark's host-side logic (CPU only): the one-GPU guard, the algorithmic byte model and
+the names of the kernel instances it reports."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    line = [l for l in r.stdout.splitlines() if l.startswith("{")][-1]
+    assert "one GPU" in json.loads(line)["error"]
+
+
+def test_algorithmic_bytes_by_hand():
+    # two hops: 3 seeds; block 1: 5 edges, |V_1| = 6; block 2: 9 edges, |V_2| = 11; d = 2
+    gather, mean, E, V = bench.algorithmic_bytes([5, 6, 9, 11], 3, 2, 2)
+    assert (E, V) == ([5, 9], [6, 11])
+    assert gather == 11 * (4 + 2 * 2 * 4)                   # id + row read + row write
+    # block 1: sources V_1 rows, 5 lids, 4 indptr entries, 3 output rows
+    assert mean[0] == 6 * 8 + 5 * 4 + 4 * 4 + 3 * 8
+    # block 2: sources V_2 rows, 9 lids, 7 indptr entries, 6 output rows
+    assert mean[1] == 11 * 8 + 9 * 4 + 7 * 4 + 6 * 8
+
+
+def test_kernel_instances_follow_row_shape():
+    assert bench.kernel_instance("gather", 602, 604, True) == "k_gather_batch<64, 3, 8>"
+    assert bench.kernel_instance("mean", 602, 604, True) == "k_mean_v5<64, 3, 4>"
+    assert bench.kernel_instance("gather", 100, 100, True) == "k_gather_batch<32, 1, 4>"
+    assert bench.kernel_instance("gather", 64, 64, False) == "k_gather_rows<16, 1, 4>"
+    assert bench.kernel_instance("gather", 13, 13, True) == "k_gather<1, 4>"   # unaligned rows
+
+
+def test_sampler_ceiling_constant():
+    # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz over 19 instructions per key
+    assert abs(bench.KEYS_PEAK - 2.07e12) / 2.07e12 < 0.01
