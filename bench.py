@@ -46,25 +46,38 @@ def workload_name(cfg) -> str:
             (f"; epoch of {cfg.n_train} training seeds" if cfg.n_train else ""))
 
 
-def kernel_instance(kind: str, d: int, ld: int, batched: bool) -> str:
+def kernel_instance(kind: str, d: int, ld: int, batched: bool, union: bool = False) -> str:
     """Name of the template instance the library launches for this row shape: both kernels pick
     lanes per row (16, 32 or 64) and, with 64, chunk groups per lane (up to 4) from the 16-byte
     chunks per row, and keep a ring of rows (gather: 8 with 64 lanes, else 4) or edges (mean: 4)
     in flight; a gather of rows that are not 16-byte aligned takes the flat per-element kernel.
-    Batched, one gather launch serves every sub-batch (k_gather_batch)."""
+    Batched, one gather launch serves every sub-batch (k_gather_batch); through the union of the
+    sub-batches' node sets, the row engine scatters each union row to its sub-batches."""
     cpr = (d + 3) // 4
     G = 16 if cpr <= 16 else (32 if cpr <= 32 else 64)
     CH = 1 if G < 64 else min(4, (cpr + 63) // 64)
     if kind == "gather":
         if ld % 4:
             return "k_gather<1, 4>"
-        return f"{'k_gather_batch' if batched else 'k_gather_rows'}<{G}, {CH}, {8 if G == 64 else 4}>"
+        R = 8 if G == 64 else 4
+        if union:
+            return f"k_gather_rows<{G}, {CH}, {R}, true>"
+        return f"{'k_gather_batch' if batched else 'k_gather_rows'}<{G}, {CH}, {R}>"
     return f"k_mean_v5<{G}, {CH}, 4>"
 
 
 def batched_gather(cfg, layout: str) -> bool:
     """The library's gather layout: batched unless interleaving is asked for."""
     return layout != "interleaved"
+
+
+UNION_GATHER_MIN_D = 128   # rows wider than this, from a table in HBM: the union gather
+
+
+def union_gather(cfg, layout: str, G: int) -> bool:
+    """Whether the library gathers a super-batch through the union of its node sets."""
+    return (batched_gather(cfg, layout) and not cfg.host_features and not cfg.cache_bytes
+            and G > 1 and cfg.d > UNION_GATHER_MIN_D and cfg.ld % 4 == 0)
 
 
 def algorithmic_bytes(counts, n_seeds, d, K):
@@ -263,9 +276,15 @@ def main():
     rows_gathered = 0
     keys = 0      # sampling keys hashed: over each hop's union frontier, the degrees above the fanout
     deg = (graph.indptr[1:] - graph.indptr[:-1]).to(torch.int32)
+    union = union_gather(cfg, args.gather, G)
     for b in range(steps):
         _, mine, sb_seeds = step(b)
         torch.cuda.synchronize()
+        if union:   # the union gather reads each row of U_K once and writes every sub-batch row
+            vk = [out.blocks.nodes[K - 1][:int(out.blocks.counts[2 * K - 1].item())] for _, _, out in mine]
+            n_union = int(torch.unique(torch.cat(vk)).numel())
+            rows = sum(int(v.numel()) for v in vk)
+            gb_union = n_union * (4 + cfg.d * 4 + G * 4) + rows * cfg.d * 4
         for l in range(K):
             if l == 0:   # the seeds of the super-batch
                 fr = [sb_seeds]
@@ -287,7 +306,7 @@ def main():
             g_s += g_b
             m_s = [x + y for x, y in zip(m_s, m_b)]
             p_s += V[K - 1] * cfg.d * 4
-        gb_bytes.append(g_s)
+        gb_bytes.append(gb_union if union else g_s)
         mean_bytes.append(m_s)
         payload.append(p_s)
     gb_bytes = np.array(gb_bytes, dtype=np.float64)
@@ -308,9 +327,11 @@ def main():
     dom = "gather" if t_gather >= t_mean_outer else "mean_outer"
     ach, avg_ms = kern[dom]
     ga_frac = (gb_bytes.sum() + mean_all.sum()) / (t_gather + t_mean_outer + t_mean_rest) / 1e9 / HBM_PEAK_GBPS
-    names = {"gather": kernel_instance("gather", cfg.d, cfg.ld, batched),
+    names = {"gather": kernel_instance("gather", cfg.d, cfg.ld, batched, union),
              "mean_outer": kernel_instance("mean", cfg.d, cfg.ld, batched)}
-    stage_kernels = {"gather": names["gather"],
+    stage_kernels = {"gather": (f"{names['gather']}: each row of the union of the sub-batches' "
+                                f"V_K read once, stored to every sub-batch that holds it"
+                                if union else names["gather"]),
                      "mean_outer": (f"{names['mean_outer']} over the union frontier, each row "
                                     f"stored to every sub-batch that holds it"
                                     if shared else names["mean_outer"])}

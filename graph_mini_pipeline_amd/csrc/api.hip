@@ -86,6 +86,11 @@ struct Workspace {
     // shared outermost means of a super-batch: for each node r of the last hop's union frontier
     // and each sub-batch g, 1 + r's position among g's destinations (0: not there)
     int32_t *inv;          // [U_cap(K-1) * G]
+    // union gather of a super-batch: for each node r of U_K (the union of the sub-batches' V_K)
+    // and each sub-batch g, 1 + r's position in g's V_K (0: not there); U_K itself (full relabel
+    // only: the compact relabel builds U_K as its last union level)
+    int32_t *invK;         // [U_cap(K) * G]
+    int32_t *uK;           // [U_cap(K)]
     int64_t P, Fs, Es;     // strides of the per-sub-batch arrays
     int64_t W, nbw, Wc, nbwc;
     int32_t mode;          // SuperMode
@@ -141,6 +146,9 @@ SuperMode super_mode(const gnn_caps &mc, int64_t N, int G, uint32_t flags) {
     const int64_t W = (N + 31) / 32;
     return 3 * static_cast<int64_t>(G + 1) * W >= max_union_edges(mc, N, G) ? kSuperCompact : kSuperFull;
 }
+
+// Narrowest rows (floats) that a super-batch gathers through the union of its node sets.
+constexpr int64_t kUnionGatherMinD = 128;
 
 // Largest byte-map region of a super-batch's sub-batch relabels (beyond it, marks stay atomic).
 constexpr int64_t kByteMapsMax = 1LL << 30;
@@ -206,7 +214,11 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
         w.f_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Fs);
         w.e_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Es);
     }
-    if (G > 1 && K > 0) w.inv = c.take<int32_t>(union_cap(mc, K - 1, G, N) * G);
+    if (G > 1 && K > 0) {
+        w.inv = c.take<int32_t>(union_cap(mc, K - 1, G, N) * G);
+        w.invK = c.take<int32_t>(union_cap(mc, K, G, N) * G);
+        if (mode == kSuperFull) w.uK = c.take<int32_t>(union_cap(mc, K, G, N));
+    }
     w.bytes = c.off;
     return w;
 }
@@ -541,6 +553,59 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
     return GNN_OK;
 }
 
+// The union gather (table in HBM, G > 1): whether the rows allow it (16-byte aligned), ...
+bool union_gather_fits(const gnn_feature_store *fs, const gnn_minibatch_out *outs, int G,
+                       const Workspace &w) {
+    bool ok = w.invK != nullptr && fs->ld % 4 == 0 && outs[0].ld_h % 4 == 0 &&
+              reinterpret_cast<uintptr_t>(fs->table) % 16 == 0;
+    for (int gi = 0; gi < G; ++gi) ok = ok && reinterpret_cast<uintptr_t>(outs[gi].x) % 16 == 0;
+    return ok;
+}
+
+// ... its preparation, part of the relabel stage: U_K (the union of the sub-batches' V_K) and,
+// for each of its nodes, the node's position in every sub-batch's V_K.  Returns U_K.
+const int32_t *union_prepare(const gnn_graph &g, const gnn_minibatch_out *outs, int G, int K,
+                             const gnn_caps &mc, const Workspace &w, hipStream_t s,
+                             gnn_status *st) {
+    *st = GNN_OK;
+    const int64_t UcapK = union_cap(mc, K, G, g.num_nodes);
+    const int32_t *uK = w.mode == kSuperCompact ? w.U[K & 1] : w.uK;
+    hipError_t e = hipSuccess;
+    if (w.mode != kSuperCompact) {
+        // the node-id bitmap was cleared by the last hop's sub-batch relabel: U_K = the union of
+        // the sub-batches' V_K, relabelled into it
+        RelabelArgs ru = relabel_args(g, w);
+        ru.nlist = G;
+        for (int gi = 0; gi < G; ++gi) {
+            const gnn_blocks &b = outs[gi].blocks;
+            ru.list[gi] = IdList{b.hop[K - 1].nodes, b.counts + 2 * (K - 1) + 1, b.caps.nodes[K - 1],
+                                 nullptr, 0, 0};
+        }
+        ru.out[0] = BitmapOut{w.uK, UcapK, w.d_U + K, nullptr};
+        e = launch_relabel(ru, s);
+    }
+    // (compact: the node-id bitmap holds U_K with its word prefixes from the last union relabel)
+    if (e == hipSuccess) {
+        UnionPosArgs up{};
+        up.bm = w.bitmaps;
+        up.wprefix = w.wprefix;
+        up.d_U = w.d_U + K;
+        up.U_cap = UcapK;
+        up.G = G;
+        for (int gi = 0; gi < G; ++gi) {
+            const gnn_blocks &b = outs[gi].blocks;
+            up.ids[gi] = b.hop[K - 1].nodes;
+            up.d_n[gi] = b.counts + 2 * (K - 1) + 1;
+            up.n_cap[gi] = b.caps.nodes[K - 1];
+        }
+        up.inv = w.invK;
+        up.status = w.status;
+        e = launch_union_positions(up, s);
+    }
+    if (e != hipSuccess) *st = GNN_ERR_HIP;
+    return uK;
+}
+
 gnn_status finish(const Opts &o, const Workspace &w, hipStream_t s) {
     if (!(o.flags & GNN_SYNC)) return GNN_OK;
     int32_t st = 0;
@@ -872,13 +937,24 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     st = run_sample(*g, sp, nsg, group, fanouts, K, seed64, ob, w, o, s,
                     ev ? ev + kSampleEvents : nullptr);
     if (st != GNN_OK) return st;
+    // From a table in HBM, a super-batch with rows wider than 128 floats gathers the union U_K of
+    // its sub-batches' V_K: each distinct row is read once and stored to the X of every sub-batch
+    // that holds it (dense 602-d workload: 3-stream throughput +5 to +7%).  Narrower rows keep the
+    // per-sub-batch gather: their 16- or 32-lane row groups pass each row's destinations round by
+    // cross-lane shuffles, which cost more than the reads saved (100-d and 128-d workloads: -1.5 to
+    // -1.8%).  U_K and the positions are relabel work and are timed with stage 1.
+    const bool union_path = from_table && group > 1 && d > kUnionGatherMinD &&
+                            union_gather_fits(fs, outs, group, w);
+    const int32_t *uK = nullptr;
+    if (union_path) {
+        uK = union_prepare(*g, outs, group, K, mc, w, s, &st);
+        if (st != GNN_OK) return st;
+    }
     if (ev) GNN_TRY_HIP(hipEventRecord(ev[1], s));
     // Stages 2 and 3: gather X = rows of V_K, then the outermost block's mean.  Batched: every
     // sub-batch's gather in one launch, then every outermost mean in one launch.  Interleaved: per
     // sub-batch, so the mean reads X while it is still in the caches.
     if (batched) {
-        // From the table, the sub-batches share one copy of every row they have in common instead
-        // of one per sub-batch's X, so repeated rows hit the caches.
         GatherBatchArgs ga{};
         ga.nseg = group;
         ga.table = fs->table;
@@ -905,7 +981,15 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
                 jobs[gi] = MeanJob{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].lid, c.edges[K - 1],
                                    d_n, c.frontier[K - 1], mo.x, c.nodes[K - 1], mo.h[K - 1]};
         }
-        GNN_TRY_HIP(launch_gather_batch(ga, rows_cap, s));
+        if (union_path) {
+            float *xs[GNN_MAX_GROUP];
+            for (int gi = 0; gi < group; ++gi) xs[gi] = outs[gi].x;
+            GNN_TRY_HIP(launch_gather_union(fs->table, fs->ld, d, fs->num_nodes, uK, w.d_U + K,
+                                            union_cap(mc, K, group, g->num_nodes), w.invK, group,
+                                            xs, outs[0].ld_h, w.status, s));
+        } else {
+            GNN_TRY_HIP(launch_gather_batch(ga, rows_cap, s));
+        }
         if (ev) GNN_TRY_HIP(hipEventRecord(ev[2], s));
         if (shared_means) {
             // the union block of the last hop (destinations U_{K-1} in U order, global ids): each

@@ -33,6 +33,12 @@ struct GatherArgs {
     int64_t *d_hits;
     int32_t *status;
     FastDiv cpr;  // chunks per row
+    // scatter (union gather of a super-batch): row r goes to row scat[r * scat_g + s] - 1 of
+    // scat_out[s] for every s with a positive entry, instead of to row r of out
+    const int32_t *scat;
+    int32_t scat_g;
+    float *scat_out[kMaxGroup];
+    int32_t rpu;  // rows per work unit (<= G; G unless the rows are few and fat)
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
     }
 }
 
-template <int G, int CH, int R>
+template <int G, int CH, int R, bool SCAT>
 __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
     const int lane = lane_id();
     const int grp = lane / G;
@@ -107,15 +113,16 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
     const int64_t n = load_count(g.d_n, g.n_cap);
     const uint32_t cpr = g.cpr.d;
     const uint32_t slabs = (cpr + CH * G - 1) / (CH * G);
-    const uint32_t units = static_cast<uint32_t>((n + G - 1) / G) * slabs;
+    const int rpu = g.rpu;
+    const uint32_t units = static_cast<uint32_t>((n + rpu - 1) / rpu) * slabs;
     const uint32_t g0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (64 / G) + grp;
     const uint32_t gstride = gridDim.x * 4u * (64 / G);
     uint32_t hits = 0;
     for (uint32_t it = g0; it < units; it += gstride) {
-        const uint32_t rb = it / slabs;         // batch of G rows
+        const uint32_t rb = it / slabs;         // batch of rpu rows
         const uint32_t p = it - rb * slabs;     // slab of the row
-        const int64_t r0 = static_cast<int64_t>(rb) * G;
-        const int nb = static_cast<int>(n - r0 < G ? n - r0 : G);
+        const int64_t r0 = static_cast<int64_t>(rb) * rpu;
+        const int nb = static_cast<int>(n - r0 < rpu ? n - r0 : rpu);
         // lane t: id and source row base of output row r0 + t (NULL: invalid id)
         const float *mine = nullptr;
         if (gl < nb) {
@@ -133,6 +140,13 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
             }
         }
         const uint64_t mine_u = reinterpret_cast<uint64_t>(mine);
+        // scatter: lane t holds the destination rows (1-based, 0: none) of union row r0 + t
+        int32_t dest[kMaxGroup];
+        if constexpr (SCAT) {
+#pragma unroll
+            for (int s2 = 0; s2 < kMaxGroup; ++s2)
+                dest[s2] = (s2 < g.scat_g && gl < nb) ? g.scat[(r0 + gl) * g.scat_g + s2] : 0;
+        }
         const uint32_t ch0 = p * CH * G + gl;
         bool act[CH];
 #pragma unroll
@@ -163,8 +177,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int er = e + r;
-                if (er < nb && row_of(er)) {
-                    float *o = g.out + (r0 + er) * g.ld_out;
+                auto store_row = [&](float *o) {
 #pragma unroll
                     for (int q = 0; q < CH; ++q) {
                         if (!act[q]) continue;
@@ -176,6 +189,20 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
                             const float t[4] = {v[r][q][0], v[r][q][1], v[r][q][2], v[r][q][3]};
                             for (int w = 0; w < rem; ++w) o[col + w] = t[w];
                         }
+                    }
+                };
+                if (er < nb && row_of(er)) {
+                    if constexpr (SCAT) {
+#pragma unroll
+                        for (int s2 = 0; s2 < kMaxGroup; ++s2) {
+                            if (s2 >= g.scat_g) break;
+                            int32_t pos;
+                            if constexpr (G == 64) pos = __builtin_amdgcn_readlane(dest[s2], er);
+                            else pos = __shfl(dest[s2], grp * G + er, 64);
+                            if (pos > 0) store_row(g.scat_out[s2] + static_cast<int64_t>(pos - 1) * g.ld_out);
+                        }
+                    } else {
+                        store_row(g.out + (r0 + er) * g.ld_out);
                     }
                 }
                 const int en = er + R;
@@ -311,6 +338,21 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// rows per work unit of the union gather: measured 16 > 8 > 4 (dense gather 232 -> 214 -> 205 us)
+constexpr int kUnionRowsPerUnit = 4;
+
+// rows in flight per group: 8 with 64 lanes, 4 with 16 or 32 (measured best on 602-, 128-, 100-
+// and 64-float rows)
+template <bool SCAT>
+void launch_rows(const GatherArgs &g, int G, int CH, dim3 grid, hipStream_t s) {
+    if (G == 16) hipLaunchKernelGGL((k_gather_rows<16, 1, 4, SCAT>), grid, dim3(256), 0, s, g);
+    else if (G == 32) hipLaunchKernelGGL((k_gather_rows<32, 1, 4, SCAT>), grid, dim3(256), 0, s, g);
+    else if (CH == 1) hipLaunchKernelGGL((k_gather_rows<64, 1, 8, SCAT>), grid, dim3(256), 0, s, g);
+    else if (CH == 2) hipLaunchKernelGGL((k_gather_rows<64, 2, 8, SCAT>), grid, dim3(256), 0, s, g);
+    else if (CH == 3) hipLaunchKernelGGL((k_gather_rows<64, 3, 8, SCAT>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_gather_rows<64, 4, 8, SCAT>), grid, dim3(256), 0, s, g);
+}
+
 hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
@@ -321,7 +363,8 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
     const int vec = v4 ? 4 : 1;
     const int64_t cpr = (d + vec - 1) / vec;
     GatherArgs g{table, cache, slot, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
-                 out, ld_out, d_hits, status, make_fastdiv(static_cast<uint32_t>(cpr))};
+                 out, ld_out, d_hits, status, make_fastdiv(static_cast<uint32_t>(cpr)),
+                 nullptr, 0, {}, 0};
     if (!v4) {
         constexpr int U = 4;
         hipLaunchKernelGGL((k_gather<1, U>), dim3(grid_for(n_cap * cpr, 256 * U, 2048)), dim3(256),
@@ -333,15 +376,36 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
     const int64_t slabs = (cpr + CH * G - 1) / (CH * G);
     const int64_t units = (n_cap + G - 1) / G * slabs;
     if (units > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    g.rpu = G;
     const dim3 grid(grid_for(units, 4 * (64 / G), 8192));
-    // rows in flight per group: 8 with 64 lanes, 4 with 16 or 32 (measured best on 602-, 128-,
-    // 100- and 64-float rows)
-    if (G == 16) hipLaunchKernelGGL((k_gather_rows<16, 1, 4>), grid, dim3(256), 0, s, g);
-    else if (G == 32) hipLaunchKernelGGL((k_gather_rows<32, 1, 4>), grid, dim3(256), 0, s, g);
-    else if (CH == 1) hipLaunchKernelGGL((k_gather_rows<64, 1, 8>), grid, dim3(256), 0, s, g);
-    else if (CH == 2) hipLaunchKernelGGL((k_gather_rows<64, 2, 8>), grid, dim3(256), 0, s, g);
-    else if (CH == 3) hipLaunchKernelGGL((k_gather_rows<64, 3, 8>), grid, dim3(256), 0, s, g);
-    else hipLaunchKernelGGL((k_gather_rows<64, 4, 8>), grid, dim3(256), 0, s, g);
+    launch_rows<false>(g, G, CH, grid, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_t num_rows,
+                               const int32_t *ids, const int64_t *d_n, int64_t n_cap,
+                               const int32_t *inv, int G_sb, float *const *outs, int64_t ld_out,
+                               int32_t *status, hipStream_t s) {
+    if (G_sb < 1 || G_sb > kMaxGroup) return hipErrorInvalidValue;
+    bool v4 = ld % 4 == 0 && ld_out % 4 == 0 && aligned16(table);
+    for (int sg = 0; sg < G_sb; ++sg) v4 = v4 && aligned16(outs[sg]);
+    if (!v4) return hipErrorInvalidValue;   // the caller gathers per sub-batch instead
+    if (n_cap <= 0 || d <= 0) return hipSuccess;
+    const int64_t cpr = (d + 3) / 4;
+    GatherArgs g{table, nullptr, nullptr, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
+                 nullptr, ld_out, nullptr, status, make_fastdiv(static_cast<uint32_t>(cpr)),
+                 inv, G_sb, {}, 0};
+    for (int sg = 0; sg < G_sb; ++sg) g.scat_out[sg] = outs[sg];
+    const int G = cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64);
+    const int CH = G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);
+    // each union row is stored several times: units of kUnionRowsPerUnit rows keep enough
+    // workgroups in flight for the union's (fewer) rows
+    g.rpu = kUnionRowsPerUnit < G ? kUnionRowsPerUnit : G;
+    const int64_t slabs = (cpr + CH * G - 1) / (CH * G);
+    const int64_t units = (n_cap + g.rpu - 1) / g.rpu * slabs;
+    if (units > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const dim3 grid(grid_for(units, 4 * (64 / G), 8192));
+    launch_rows<true>(g, G, CH, grid, s);
     return hipGetLastError();
 }
 

@@ -35,6 +35,17 @@ def test_kernel_instances_follow_row_shape():
     assert bench.kernel_instance("gather", 100, 100, True) == "k_gather_batch<32, 1, 4>"
     assert bench.kernel_instance("gather", 64, 64, False) == "k_gather_rows<16, 1, 4>"
     assert bench.kernel_instance("gather", 13, 13, True) == "k_gather<1, 4>"   # unaligned rows
+    assert bench.kernel_instance("gather", 602, 604, True, True) == "k_gather_rows<64, 3, 8, true>"
+
+
+def test_union_gather_choice():
+    import synth
+    dense, mid, billion = (synth.CONFIGS[n] for n in ("dense", "mid", "billion"))
+    assert bench.union_gather(dense, "auto", 8)
+    assert not bench.union_gather(dense, "auto", 1)           # one batch: nothing to share
+    assert not bench.union_gather(dense, "interleaved", 8)
+    assert not bench.union_gather(mid, "auto", 8)             # 100-float rows
+    assert not bench.union_gather(billion, "auto", 8)         # host-resident table
 
 
 def test_sampler_ceiling_constant():

@@ -508,6 +508,26 @@ def test_batched_gather_row_widths(tiny, d, ld, store):
         compare_with_oracle(outs[g], ref, d)
 
 
+@pytest.mark.parametrize("mode", ["full", "compact"])
+@pytest.mark.parametrize("d,ld", [(150, 152), (602, 604), (150, 151)])
+def test_union_gather(tiny, mode, d, ld):
+    """Rows wider than 128 floats from a table in HBM: a super-batch gathers the union of its
+    sub-batches' node sets once and stores each row to every sub-batch's X that holds it (rows
+    that are not 16-byte aligned, ld = 151, gather per sub-batch).  Overlapping and empty
+    sub-batches, both relabel modes."""
+    cfg, indptr, indices, _, order = tiny
+    x = np.random.default_rng(d + ld).standard_normal((cfg.num_nodes, d)).astype(np.float32)
+    fs = gm.gnn_feature_store_create(device_table(x, ld), d)
+    seeds = np.concatenate([order[:300], order[150:420], order[:0], order[400:460], order[0:50]])
+    ptr = [0, 300, 570, 570, 630, 680]
+    outs, st = run_minibatch(device_graph(indptr, indices), fs, seeds, [7, 5], 57, group_ptr=ptr,
+                             opts=gm.Options(superbatch=mode))
+    assert st == gm.GNN_OK
+    for g in range(5):
+        ref = oracle.minibatch(indptr, indices, x, seeds[ptr[g]:ptr[g + 1]], [7, 5], 57)
+        compare_with_oracle(outs[g], ref, d)
+
+
 class _BothGather(gm.Options):
     def c(self):
         o = super().c()
