@@ -86,10 +86,8 @@ struct Workspace {
     // shared outermost means of a super-batch: for each node r of the last hop's union frontier
     // and each sub-batch g, 1 + r's position among g's destinations (0: not there)
     int32_t *inv;          // [U_cap(K-1) * G]
-    // union gather of a super-batch: for each node r of U_K (the union of the sub-batches' V_K)
-    // and each sub-batch g, 1 + r's position in g's V_K (0: not there); U_K itself (full relabel
-    // only: the compact relabel builds U_K as its last union level)
-    int32_t *invK;         // [U_cap(K) * G]
+    // union gather of a super-batch (full relabel only; the compact relabel builds U_K as its
+    // last union level): U_K, the union of the sub-batches' V_K
     int32_t *uK;           // [U_cap(K)]
     int64_t P, Fs, Es;     // strides of the per-sub-batch arrays
     int64_t W, nbw, Wc, nbwc;
@@ -216,7 +214,6 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
     }
     if (G > 1 && K > 0) {
         w.inv = c.take<int32_t>(union_cap(mc, K - 1, G, N) * G);
-        w.invK = c.take<int32_t>(union_cap(mc, K, G, N) * G);
         if (mode == kSuperFull) w.uK = c.take<int32_t>(union_cap(mc, K, G, N));
     }
     w.bytes = c.off;
@@ -556,54 +553,31 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
 // The union gather (table in HBM, G > 1): whether the rows allow it (16-byte aligned), ...
 bool union_gather_fits(const gnn_feature_store *fs, const gnn_minibatch_out *outs, int G,
                        const Workspace &w) {
-    bool ok = w.invK != nullptr && fs->ld % 4 == 0 && outs[0].ld_h % 4 == 0 &&
-              reinterpret_cast<uintptr_t>(fs->table) % 16 == 0;
+    bool ok = (w.mode == kSuperCompact || w.uK != nullptr) && fs->ld % 4 == 0 &&
+              outs[0].ld_h % 4 == 0 && reinterpret_cast<uintptr_t>(fs->table) % 16 == 0;
     for (int gi = 0; gi < G; ++gi) ok = ok && reinterpret_cast<uintptr_t>(outs[gi].x) % 16 == 0;
     return ok;
 }
 
-// ... its preparation, part of the relabel stage: U_K (the union of the sub-batches' V_K) and,
-// for each of its nodes, the node's position in every sub-batch's V_K.  Returns U_K.
+// ... and U_K, the union of the sub-batches' V_K (relabel work, timed with stage 1): the compact
+// relabel has built it as its last union level; with full-range bitmaps the node-id bitmap, cleared
+// by the last hop's sub-batch relabel, takes the sub-batches' V_K.  A union row's position in
+// sub-batch g is its rank in g's relabel bitmap (by union position, or by node id in full mode).
 const int32_t *union_prepare(const gnn_graph &g, const gnn_minibatch_out *outs, int G, int K,
                              const gnn_caps &mc, const Workspace &w, hipStream_t s,
                              gnn_status *st) {
     *st = GNN_OK;
-    const int64_t UcapK = union_cap(mc, K, G, g.num_nodes);
-    const int32_t *uK = w.mode == kSuperCompact ? w.U[K & 1] : w.uK;
-    hipError_t e = hipSuccess;
-    if (w.mode != kSuperCompact) {
-        // the node-id bitmap was cleared by the last hop's sub-batch relabel: U_K = the union of
-        // the sub-batches' V_K, relabelled into it
-        RelabelArgs ru = relabel_args(g, w);
-        ru.nlist = G;
-        for (int gi = 0; gi < G; ++gi) {
-            const gnn_blocks &b = outs[gi].blocks;
-            ru.list[gi] = IdList{b.hop[K - 1].nodes, b.counts + 2 * (K - 1) + 1, b.caps.nodes[K - 1],
-                                 nullptr, 0, 0};
-        }
-        ru.out[0] = BitmapOut{w.uK, UcapK, w.d_U + K, nullptr};
-        e = launch_relabel(ru, s);
+    if (w.mode == kSuperCompact) return w.U[K & 1];
+    RelabelArgs ru = relabel_args(g, w);
+    ru.nlist = G;
+    for (int gi = 0; gi < G; ++gi) {
+        const gnn_blocks &b = outs[gi].blocks;
+        ru.list[gi] = IdList{b.hop[K - 1].nodes, b.counts + 2 * (K - 1) + 1, b.caps.nodes[K - 1],
+                             nullptr, 0, 0};
     }
-    // (compact: the node-id bitmap holds U_K with its word prefixes from the last union relabel)
-    if (e == hipSuccess) {
-        UnionPosArgs up{};
-        up.bm = w.bitmaps;
-        up.wprefix = w.wprefix;
-        up.d_U = w.d_U + K;
-        up.U_cap = UcapK;
-        up.G = G;
-        for (int gi = 0; gi < G; ++gi) {
-            const gnn_blocks &b = outs[gi].blocks;
-            up.ids[gi] = b.hop[K - 1].nodes;
-            up.d_n[gi] = b.counts + 2 * (K - 1) + 1;
-            up.n_cap[gi] = b.caps.nodes[K - 1];
-        }
-        up.inv = w.invK;
-        up.status = w.status;
-        e = launch_union_positions(up, s);
-    }
-    if (e != hipSuccess) *st = GNN_ERR_HIP;
-    return uK;
+    ru.out[0] = BitmapOut{w.uK, union_cap(mc, K, G, g.num_nodes), w.d_U + K, nullptr};
+    if (launch_relabel(ru, s) != hipSuccess) *st = GNN_ERR_HIP;
+    return w.uK;
 }
 
 gnn_status finish(const Opts &o, const Workspace &w, hipStream_t s) {
@@ -939,10 +913,10 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     if (st != GNN_OK) return st;
     // From a table in HBM, a super-batch with rows wider than 128 floats gathers the union U_K of
     // its sub-batches' V_K: each distinct row is read once and stored to the X of every sub-batch
-    // that holds it (dense 602-d workload: 3-stream throughput +5 to +7%).  Narrower rows keep the
-    // per-sub-batch gather: their 16- or 32-lane row groups pass each row's destinations round by
-    // cross-lane shuffles, which cost more than the reads saved (100-d and 128-d workloads: -1.5 to
-    // -1.8%).  U_K and the positions are relabel work and are timed with stage 1.
+    // that holds it (dense 602-d workload, union 31% of the sub-batches' rows: 3-stream throughput
+    // +12%).  With narrower rows the reads saved are smaller than the cost of building U_K and
+    // finding each row's destinations (100-d, union 43%: +1%; 128-d, union 76%: -4%), so they keep
+    // the per-sub-batch gather.  Building U_K is relabel work and is timed with stage 1.
     const bool union_path = from_table && group > 1 && d > kUnionGatherMinD &&
                             union_gather_fits(fs, outs, group, w);
     const int32_t *uK = nullptr;
@@ -984,9 +958,13 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         if (union_path) {
             float *xs[GNN_MAX_GROUP];
             for (int gi = 0; gi < group; ++gi) xs[gi] = outs[gi].x;
+            // the sub-batch relabel bitmaps of the last hop: over U_K positions (compact) or node
+            // ids (full), with their word prefixes
+            const bool compact = w.mode == kSuperCompact;
             GNN_TRY_HIP(launch_gather_union(fs->table, fs->ld, d, fs->num_nodes, uK, w.d_U + K,
-                                            union_cap(mc, K, group, g->num_nodes), w.invK, group,
-                                            xs, outs[0].ld_h, w.status, s));
+                                            union_cap(mc, K, group, g->num_nodes), w.bitmaps + w.W,
+                                            w.wprefix + w.W, compact ? w.Wc : w.W, compact ? 0 : 1,
+                                            group, xs, outs[0].ld_h, w.status, s));
         } else {
             GNN_TRY_HIP(launch_gather_batch(ga, rows_cap, s));
         }

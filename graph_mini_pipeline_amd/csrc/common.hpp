@@ -334,28 +334,16 @@ hipError_t launch_sage_update(const int32_t *dst_lid, const int64_t *d_n, int64_
                               int64_t d_out, int32_t relu, float *out, int64_t ld_out,
                               int32_t *status, hipStream_t s);
 // Gather of the union of a super-batch's gathered node sets: union row r < *d_n (global id
-// ids[r]) is read once and stored to row inv[r * G + g] - 1 of outs[g] for every sub-batch g with
-// inv[r * G + g] > 0.  Rows must be 16-byte aligned (ld and ld_out multiples of 4, aligned
-// bases): otherwise hipErrorInvalidValue is returned and nothing is launched.
+// ids[r]) is read once and stored to every sub-batch g whose relabel bitmap (bm + g * words, word
+// prefixes wp + g * words) holds the row's key -- the id when by_id, else r -- at the key's rank
+// in that bitmap.
+// Rows must be 16-byte aligned (ld and ld_out multiples of 4, aligned bases): otherwise
+// hipErrorInvalidValue is returned and nothing is launched.
 hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                                const int32_t *ids, const int64_t *d_n, int64_t n_cap,
-                               const int32_t *inv, int G, float *const *outs, int64_t ld_out,
-                               int32_t *status, hipStream_t s);
-// inv[r * G + g] = 1 + the position of union node r in sub-batch g's list ids[g] (0: absent), for
-// r < *d_U, where r is an id's rank in the union bitmap bm (word prefixes wprefix).
-struct UnionPosArgs {
-    const uint32_t *bm;
-    const uint32_t *wprefix;
-    const int64_t *d_U;
-    int64_t U_cap;
-    int32_t G;
-    const int32_t *ids[kMaxGroup];
-    const int64_t *d_n[kMaxGroup];
-    int64_t n_cap[kMaxGroup];
-    int32_t *inv;
-    int32_t *status;
-};
-hipError_t launch_union_positions(const UnionPosArgs &a, hipStream_t s);
+                               const uint32_t *bm, const uint32_t *wp, int64_t words, int by_id,
+                               int G, float *const *outs, int64_t ld_out, int32_t *status,
+                               hipStream_t s);
 hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                              const int32_t *hot, int64_t rows, float *cache, int32_t *slot,
                              int32_t *status, hipStream_t s);

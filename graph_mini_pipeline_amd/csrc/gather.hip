@@ -33,9 +33,13 @@ struct GatherArgs {
     int64_t *d_hits;
     int32_t *status;
     FastDiv cpr;  // chunks per row
-    // scatter (union gather of a super-batch): row r goes to row scat[r * scat_g + s] - 1 of
-    // scat_out[s] for every s with a positive entry, instead of to row r of out
-    const int32_t *scat;
+    // scatter (union gather of a super-batch): row r goes to scat_out[s] for every sub-batch s
+    // whose relabel bitmap (scat_bm + s * scat_w, word prefixes scat_wp + s * scat_w) holds the
+    // row's key -- its id (scat_by_id) or r itself -- at the key's rank in that bitmap
+    const uint32_t *scat_bm;
+    const uint32_t *scat_wp;
+    int64_t scat_w;
+    int32_t scat_by_id;
     int32_t scat_g;
     float *scat_out[kMaxGroup];
     int32_t rpu;  // rows per work unit (<= G; G unless the rows are few and fat)
@@ -125,8 +129,10 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
         const int nb = static_cast<int>(n - r0 < rpu ? n - r0 : rpu);
         // lane t: id and source row base of output row r0 + t (NULL: invalid id)
         const float *mine = nullptr;
+        int32_t vid = -1;
         if (gl < nb) {
             const int32_t v = g.ids[r0 + gl];
+            vid = v;
             if (v < 0 || v >= g.num_rows) {
                 set_status(g.status, GNN_ERR_OUT_OF_RANGE);
             } else {
@@ -143,9 +149,18 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
         // scatter: lane t holds the destination rows (1-based, 0: none) of union row r0 + t
         int32_t dest[kMaxGroup];
         if constexpr (SCAT) {
+            const int64_t key = g.scat_by_id ? static_cast<int64_t>(vid) : r0 + gl;
 #pragma unroll
-            for (int s2 = 0; s2 < kMaxGroup; ++s2)
-                dest[s2] = (s2 < g.scat_g && gl < nb) ? g.scat[(r0 + gl) * g.scat_g + s2] : 0;
+            for (int s2 = 0; s2 < kMaxGroup; ++s2) {
+                dest[s2] = 0;
+                if (s2 < g.scat_g && gl < nb && key >= 0 && (key >> 5) < g.scat_w) {
+                    const int64_t wi = s2 * g.scat_w + (key >> 5);
+                    const uint32_t w = g.scat_bm[wi];
+                    const uint32_t b = static_cast<uint32_t>(key & 31);
+                    if ((w >> b) & 1u)
+                        dest[s2] = static_cast<int32_t>(g.scat_wp[wi] + __popc(w & ((1u << b) - 1u))) + 1;
+                }
+            }
         }
         const uint32_t ch0 = p * CH * G + gl;
         bool act[CH];
@@ -338,7 +353,8 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// rows per work unit of the union gather: measured 16 > 8 > 4 (dense gather 232 -> 214 -> 205 us)
+// rows per work unit of the union gather (measured with 16, 8 and 4 rows: dense gather 232, 214
+// and 205 us)
 constexpr int kUnionRowsPerUnit = 4;
 
 // rows in flight per group: 8 with 64 lanes, 4 with 16 or 32 (measured best on 602-, 128-, 100-
@@ -364,7 +380,7 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
     const int64_t cpr = (d + vec - 1) / vec;
     GatherArgs g{table, cache, slot, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
                  out, ld_out, d_hits, status, make_fastdiv(static_cast<uint32_t>(cpr)),
-                 nullptr, 0, {}, 0};
+                 nullptr, nullptr, 0, 0, 0, {}, 0};
     if (!v4) {
         constexpr int U = 4;
         hipLaunchKernelGGL((k_gather<1, U>), dim3(grid_for(n_cap * cpr, 256 * U, 2048)), dim3(256),
@@ -384,8 +400,9 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
 
 hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                                const int32_t *ids, const int64_t *d_n, int64_t n_cap,
-                               const int32_t *inv, int G_sb, float *const *outs, int64_t ld_out,
-                               int32_t *status, hipStream_t s) {
+                               const uint32_t *bm, const uint32_t *wp, int64_t words, int by_id,
+                               int G_sb, float *const *outs, int64_t ld_out, int32_t *status,
+                               hipStream_t s) {
     if (G_sb < 1 || G_sb > kMaxGroup) return hipErrorInvalidValue;
     bool v4 = ld % 4 == 0 && ld_out % 4 == 0 && aligned16(table);
     for (int sg = 0; sg < G_sb; ++sg) v4 = v4 && aligned16(outs[sg]);
@@ -394,7 +411,7 @@ hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_
     const int64_t cpr = (d + 3) / 4;
     GatherArgs g{table, nullptr, nullptr, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
                  nullptr, ld_out, nullptr, status, make_fastdiv(static_cast<uint32_t>(cpr)),
-                 inv, G_sb, {}, 0};
+                 bm, wp, words, by_id, G_sb, {}, 0};
     for (int sg = 0; sg < G_sb; ++sg) g.scat_out[sg] = outs[sg];
     const int G = cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64);
     const int CH = G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);

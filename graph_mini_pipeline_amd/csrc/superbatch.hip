@@ -174,46 +174,6 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
     }
 }
 
-// Union positions of the gathered node sets (for the union gather): zero the live table, then
-// each sub-batch's entry of every node it holds.  y = sub-batch.
-__global__ __launch_bounds__(256) void k_union_pos_zero(UnionPosArgs a) {
-    const int64_t n = load_count(a.d_U, a.U_cap) * a.G;
-    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
-         t += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        a.inv[t] = 0;
-}
-
-__global__ __launch_bounds__(256) void k_union_pos_fill(UnionPosArgs a) {
-    const int g = static_cast<int>(blockIdx.y);
-    const int64_t n = load_count(a.d_n[g], a.n_cap[g]);
-    const int64_t nU = load_count(a.d_U, a.U_cap);
-    const int32_t *ids = a.ids[g];
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int32_t v = ids[i];
-        if (v < 0) {
-            set_status(a.status, GNN_ERR_INTERNAL);
-            continue;
-        }
-        const uint32_t w = a.bm[v >> 5];
-        const int64_t r = a.wprefix[v >> 5] + __popc(w & ((1u << (v & 31)) - 1u));
-        if (!(w >> (v & 31) & 1u) || r >= nU) {
-            set_status(a.status, GNN_ERR_INTERNAL);
-            continue;
-        }
-        a.inv[r * a.G + g] = static_cast<int32_t>(i + 1);
-    }
-}
-
-hipError_t launch_union_positions(const UnionPosArgs &a, hipStream_t s) {
-    if (a.G < 1 || a.G > kMaxGroup) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_union_pos_zero, dim3(grid_for(a.U_cap * a.G, 256, 2048)), dim3(256), 0, s, a);
-    int64_t n_max = 1;
-    for (int g = 0; g < a.G; ++g) n_max = a.n_cap[g] > n_max ? a.n_cap[g] : n_max;
-    hipLaunchKernelGGL(k_union_pos_fill, dim3(grid_for(n_max, 256, 512), a.G), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
 constexpr int kDistMaxGrid = 4096;
 
 hipError_t launch_dist(const DistArgs &a, hipStream_t s) {
