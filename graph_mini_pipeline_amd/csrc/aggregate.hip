@@ -52,10 +52,20 @@ __device__ __forceinline__ int32_t valid_lid(const MeanArgs &m, const MeanSeg &S
     return 0;
 }
 
+// The segment of item `it`.  Each segment's first item is a multiple of the items one wavefront
+// takes at a time (the launcher pads the segments), so the segment is the same for every active
+// lane and is found from the first one: its fields are then scalar loads, which leave the vector
+// memory counter, and with it the row loads in flight, alone.
 __device__ __forceinline__ int find_seg(const MeanArgs &m, uint32_t it) {
+    const uint32_t it0 = __builtin_amdgcn_readfirstlane(it);
     int sgi = 0;
-    while (sgi + 1 < m.nseg && m.seg[sgi + 1].item0 <= it) ++sgi;
-    return sgi;
+    while (sgi + 1 < m.nseg && m.seg[sgi + 1].item0 <= it0) ++sgi;
+    return __builtin_amdgcn_readfirstlane(sgi);
+}
+
+// A segment by an index that is the same on every active lane (kept in scalar registers).
+__device__ __forceinline__ const MeanSeg &seg_of(const MeanArgs &m, int sgi) {
+    return m.seg[__builtin_amdgcn_readfirstlane(sgi)];
 }
 
 __device__ __forceinline__ float4 f4add(float4 a, float4 b) {
@@ -84,12 +94,16 @@ __global__ __launch_bounds__(256) void k_mean_v5(MeanArgs m) {
     const uint32_t gstride = gridDim.x * 4u * (64 / G);
     for (uint32_t it = g0; it < m.items; it += gstride) {
         const int sgi = find_seg(m, it);
-        const MeanSeg &S = m.seg[sgi];
+        const MeanSeg &S = seg_of(m, sgi);
         const uint32_t li = it - S.item0;
         const uint32_t i = li / slabs;
         const uint32_t p = li - i * slabs;
         if (i >= s_n[sgi]) continue;
         int64_t e0 = S.indptr[i], e1 = S.indptr[i + 1];
+        // lane g of the group: the destination's row in sub-batch g (+1; 0: absent), loaded here so
+        // that it arrives with the local ids instead of after the rows
+        const int32_t mypos =
+            m.scat != nullptr && gl < m.scat_g ? m.scat[static_cast<int64_t>(i) * m.scat_g + gl] : 0;
         e0 = e0 < 0 ? 0 : (e0 > S.e_cap ? S.e_cap : e0);
         e1 = e1 < e0 ? e0 : (e1 > S.e_cap ? S.e_cap : e1);
         const uint32_t ch0 = p * CH * G + gl;  // this lane's first chunk
@@ -161,8 +175,6 @@ __global__ __launch_bounds__(256) void k_mean_v5(MeanArgs m) {
         if (m.scat == nullptr) {
             store_row(S.out + static_cast<int64_t>(i) * m.ld_out);
         } else {
-            // lane g of the group holds the destination's row in sub-batch g (+1; 0: absent)
-            const int32_t mypos = gl < m.scat_g ? m.scat[static_cast<int64_t>(i) * m.scat_g + gl] : 0;
             for (int g = 0; g < m.scat_g; ++g) {
                 int32_t pos;
                 if constexpr (G == 64) pos = __builtin_amdgcn_readlane(mypos, g);
@@ -174,14 +186,14 @@ __global__ __launch_bounds__(256) void k_mean_v5(MeanArgs m) {
 }
 
 __global__ __launch_bounds__(256) void k_mean_v1(MeanArgs m) {
-    __shared__ uint32_t s_n[kMaxMeanSegs];
+    __shared__ uint32_t s_n[kMaxMeanSegs];  // destination count of each segment
     if (threadIdx.x < static_cast<unsigned>(m.nseg))
         s_n[threadIdx.x] = static_cast<uint32_t>(load_count(m.seg[threadIdx.x].d_n, m.seg[threadIdx.x].n_cap));
     __syncthreads();
     const uint32_t cpr = m.cpr.d;
     for (uint32_t it = blockIdx.x * 256u + threadIdx.x; it < m.items; it += gridDim.x * 256u) {
         const int sgi = find_seg(m, it);
-        const MeanSeg &S = m.seg[sgi];
+        const MeanSeg &S = seg_of(m, sgi);
         const uint32_t li = it - S.item0;
         const uint32_t row = fast_div(li, m.cpr);
         const int col = static_cast<int>(li - row * cpr);
@@ -219,6 +231,9 @@ static hipError_t launch_mean_impl(const MeanJob *jobs, int njobs, int64_t ld_sr
     // chunk groups per lane in one item: G = 64 rows of up to 4 * 64 chunks take one item each
     const int CH = !v4 || G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);
     const int64_t slabs = v4 ? (cpr + CH * G - 1) / (CH * G) : cpr;   // items per destination
+    // items a wavefront takes at a time (64 / G groups of G lanes; one lane per item when G = 1):
+    // every segment starts at a multiple of it, so that no wavefront spans two segments
+    const int64_t per_wave = 64 / G;
     for (int j0 = 0; j0 < njobs; j0 += kMaxMeanSegs) {
         MeanArgs m{};
         m.scat = scat;
@@ -234,7 +249,7 @@ static hipError_t launch_mean_impl(const MeanJob *jobs, int njobs, int64_t ld_sr
             const MeanJob &J = jobs[j];
             m.seg[m.nseg++] = MeanSeg{J.indptr, J.lid, J.e_cap, J.d_n, J.n_cap, J.src, J.n_src,
                                       J.out, static_cast<uint32_t>(items)};
-            items += J.n_cap * slabs;
+            items += (J.n_cap * slabs + per_wave - 1) / per_wave * per_wave;
         }
         if (items == 0) continue;
         if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
@@ -244,6 +259,7 @@ static hipError_t launch_mean_impl(const MeanJob *jobs, int njobs, int64_t ld_sr
             continue;
         }
         const dim3 grid(grid_for(items, 4 * (64 / G), 8192));
+        // 4 edges in flight per group (a deeper ring costs occupancy and measured slower)
         constexpr int R = 4;
         if (G == 16) hipLaunchKernelGGL((k_mean_v5<16, 1, R>), grid, dim3(256), 0, s, m);
         else if (G == 32) hipLaunchKernelGGL((k_mean_v5<32, 1, R>), grid, dim3(256), 0, s, m);

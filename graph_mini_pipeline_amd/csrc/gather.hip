@@ -47,6 +47,17 @@ struct GatherArgs {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// A source row as a 32-bit code passed between lanes: table row v (v >= 0), cache row s
+// (-2 - s), none (-1).  The address is rebuilt from the launch's own table and cache pointers, so
+// the row loads stay global loads: a pointer passed between lanes has lost its address space and
+// would be read with flat loads, which also count on the LDS counter (a cross-lane read's wait
+// would then wait for every row in flight).
+__device__ __forceinline__ const float *row_ptr(const float *table, const float *cache, int64_t ld,
+                                                int32_t c) {
+    return c >= 0 ? table + static_cast<int64_t>(c) * ld
+                  : cache + static_cast<int64_t>(-2 - c) * ld;
+}
+
 template <int VEC, int U>
 __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
     using vec_t = typename std::conditional<VEC == 4, f32x4, float>::type;
@@ -127,8 +138,8 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
         const uint32_t p = it - rb * slabs;     // slab of the row
         const int64_t r0 = static_cast<int64_t>(rb) * rpu;
         const int nb = static_cast<int>(n - r0 < rpu ? n - r0 : rpu);
-        // lane t: id and source row base of output row r0 + t (NULL: invalid id)
-        const float *mine = nullptr;
+        // lane t: id and source row code of output row r0 + t (-1: invalid id)
+        int32_t mine = -1;
         int32_t vid = -1;
         if (gl < nb) {
             const int32_t v = g.ids[r0 + gl];
@@ -138,14 +149,13 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
             } else {
                 const int32_t sl = g.slot ? g.slot[v] : -1;
                 if (sl >= 0) {
-                    mine = g.cache + static_cast<int64_t>(sl) * g.ld;
+                    mine = -2 - sl;
                     hits += p == 0;
                 } else {
-                    mine = g.table + static_cast<int64_t>(v) * g.ld;
+                    mine = v;
                 }
             }
         }
-        const uint64_t mine_u = reinterpret_cast<uint64_t>(mine);
         // scatter: lane t holds the destination rows (1-based, 0: none) of union row r0 + t
         int32_t dest[kMaxGroup];
         if constexpr (SCAT) {
@@ -166,25 +176,19 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
         bool act[CH];
 #pragma unroll
         for (int q = 0; q < CH; ++q) act[q] = ch0 + q * G < cpr;
-        auto row_of = [&](int r) -> const float * {
+        auto code_of = [&](int r) -> int32_t {
             const int rr = r < nb ? r : 0;
-            uint64_t a;
-            if constexpr (G == 64) {
-                const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine_u), rr);
-                const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine_u >> 32), rr);
-                a = (static_cast<uint64_t>(hi) << 32) | lo;
-            } else {
-                a = __shfl(mine_u, grp * G + rr, 64);
-            }
-            return reinterpret_cast<const float *>(a);
+            if constexpr (G == 64) return __builtin_amdgcn_readlane(mine, rr);
+            else return __shfl(mine, grp * G + rr, 64);
         };
         f32x4 v[R][CH];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float *row = row_of(r);
+            const int32_t c = code_of(r);
+            const float *row = row_ptr(g.table, g.cache, g.ld, c);
 #pragma unroll
             for (int q = 0; q < CH; ++q)
-                v[r][q] = (r < nb && row && act[q])
+                v[r][q] = (r < nb && c != -1 && act[q])
                               ? *reinterpret_cast<const f32x4 *>(row + static_cast<int64_t>(ch0 + q * G) * 4)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
                         }
                     }
                 };
-                if (er < nb && row_of(er)) {
+                if (er < nb && code_of(er) != -1) {
                     if constexpr (SCAT) {
 #pragma unroll
                         for (int s2 = 0; s2 < kMaxGroup; ++s2) {
@@ -221,10 +225,11 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
                     }
                 }
                 const int en = er + R;
-                const float *row = row_of(en);
+                const int32_t c = code_of(en);
+                const float *row = row_ptr(g.table, g.cache, g.ld, c);
 #pragma unroll
                 for (int q = 0; q < CH; ++q)
-                    v[r][q] = (en < nb && row && act[q])
+                    v[r][q] = (en < nb && c != -1 && act[q])
                                   ? *reinterpret_cast<const f32x4 *>(row + static_cast<int64_t>(ch0 + q * G) * 4)
                                   : f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -259,11 +264,15 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
         s_n[threadIdx.x] = load_count(S.d_n, S.n_cap);
     }
     __syncthreads();
+    // each sub-batch's units start at a multiple of the units one wavefront takes at a time, so
+    // a wavefront's units are all in one sub-batch (the padding units have no rows): its fields are
+    // read with scalar loads, which do not wait on vector memory
     if (threadIdx.x == 0) {
         uint32_t u = 0;
         for (int sg = 0; sg < a.nseg; ++sg) {
             s_u0[sg] = u;
-            u += static_cast<uint32_t>((s_n[sg] + G - 1) / G) * slabs;
+            const uint32_t nu = static_cast<uint32_t>((s_n[sg] + G - 1) / G) * slabs;
+            u += (nu + 64 / G - 1) / (64 / G) * (64 / G);
         }
         s_u0[a.nseg] = u;
     }
@@ -272,8 +281,10 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
     const uint32_t g0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (64 / G) + grp;
     const uint32_t gstride = gridDim.x * 4u * (64 / G);
     for (uint32_t it = g0; it < units; it += gstride) {
+        const uint32_t it0 = __builtin_amdgcn_readfirstlane(it);
         int sg = 0;
-        while (sg + 1 < a.nseg && s_u0[sg + 1] <= it) ++sg;
+        while (sg + 1 < a.nseg && s_u0[sg + 1] <= it0) ++sg;
+        sg = __builtin_amdgcn_readfirstlane(sg);
         const GatherSeg &S = a.seg[sg];
         const uint32_t li = it - s_u0[sg];
         const uint32_t rb = li / slabs;
@@ -282,41 +293,33 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
         const int64_t n = s_n[sg];
         const int nb = static_cast<int>(n - r0 < G ? n - r0 : G);
         // lane t: source row of output row r0 + t (NULL: invalid id)
-        const float *mine = nullptr;
+        int32_t mine = -1;
         if (gl < nb) {
             const int32_t v = S.ids[r0 + gl];
             if (v < 0 || v >= a.num_rows) {
                 set_status(a.status, GNN_ERR_OUT_OF_RANGE);
             } else {
                 const int32_t sl = a.slot ? a.slot[v] : -1;
-                mine = sl >= 0 ? a.cache + static_cast<int64_t>(sl) * a.ld
-                               : a.table + static_cast<int64_t>(v) * a.ld;
+                mine = sl >= 0 ? -2 - sl : v;
             }
         }
-        const uint64_t mine_u = reinterpret_cast<uint64_t>(mine);
         const uint32_t ch0 = p * CH * G + gl;
         bool act[CH];
 #pragma unroll
         for (int q = 0; q < CH; ++q) act[q] = ch0 + q * G < cpr;
-        auto row_of = [&](int r) -> const float * {
+        auto code_of = [&](int r) -> int32_t {
             const int rr = r < nb ? r : 0;
-            uint64_t x;
-            if constexpr (G == 64) {
-                const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine_u), rr);
-                const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine_u >> 32), rr);
-                x = (static_cast<uint64_t>(hi) << 32) | lo;
-            } else {
-                x = __shfl(mine_u, grp * G + rr, 64);
-            }
-            return reinterpret_cast<const float *>(x);
+            if constexpr (G == 64) return __builtin_amdgcn_readlane(mine, rr);
+            else return __shfl(mine, grp * G + rr, 64);
         };
         f32x4 v[R][CH];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float *row = row_of(r);
+            const int32_t c = code_of(r);
+            const float *row = row_ptr(a.table, a.cache, a.ld, c);
 #pragma unroll
             for (int q = 0; q < CH; ++q)
-                v[r][q] = (r < nb && row && act[q])
+                v[r][q] = (r < nb && c != -1 && act[q])
                               ? *reinterpret_cast<const f32x4 *>(row + static_cast<int64_t>(ch0 + q * G) * 4)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int er = e + r;
-                if (er < nb && row_of(er)) {
+                if (er < nb && code_of(er) != -1) {
                     float *o = S.out + (r0 + er) * a.ld_out;
 #pragma unroll
                     for (int q = 0; q < CH; ++q) {
@@ -340,10 +343,11 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
                     }
                 }
                 const int en = er + R;
-                const float *row = row_of(en);
+                const int32_t c = code_of(en);
+                const float *row = row_ptr(a.table, a.cache, a.ld, c);
 #pragma unroll
                 for (int q = 0; q < CH; ++q)
-                    v[r][q] = (en < nb && row && act[q])
+                    v[r][q] = (en < nb && c != -1 && act[q])
                                   ? *reinterpret_cast<const f32x4 *>(row + static_cast<int64_t>(ch0 + q * G) * 4)
                                   : f32x4{0.f, 0.f, 0.f, 0.f};
             }

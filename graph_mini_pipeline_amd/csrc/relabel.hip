@@ -52,8 +52,10 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s) 
 // whole grid walks each list up to its actual (device) length, list after list: capacities can
 // be many times the actual lengths.
 // The lists' actual lengths (then the outputs' sizes), read once per workgroup with one load
-// per list in flight, and their exclusive prefix: items of the lists are numbered 0 .. total-1
-// in list order, so the grid spreads over the actual items of all lists at once.
+// per list in flight, and their exclusive prefix: items of the lists are numbered in list order,
+// so the grid spreads over the actual items of all lists at once.  Each list starts at a multiple
+// of 64, so the items of one wavefront belong to one list (the padding items are skipped): the
+// list's fields are then read with scalar loads, which do not wait on vector memory.
 __device__ __forceinline__ void list_lengths(const RelabelArgs &a, int64_t *s_len, int64_t *s_off) {
     const int nl = a.nlist + a.nbm;
     if (threadIdx.x < static_cast<unsigned>(a.nlist))
@@ -66,22 +68,25 @@ __device__ __forceinline__ void list_lengths(const RelabelArgs &a, int64_t *s_le
         int64_t run = 0;
         for (int l = 0; l < nl; ++l) {
             s_off[l] = run;
-            run += s_len[l];
+            run += (s_len[l] + 63) & ~int64_t{63};
         }
         s_off[nl] = run;
     }
     __syncthreads();
 }
 
-// The list (among the first n of them) holding item t: the last l with s_off[l] <= t.
+// The list (among the first n of them) holding item t: the last l with s_off[l] <= t, the same
+// for every active lane of the wavefront (found from the first one).
 __device__ __forceinline__ int item_list(const int64_t *s_off, int n, int64_t t) {
-    int lo = 0, hi = n;  // s_off[lo] <= t < s_off[hi]
+    const int64_t t0 = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t >> 32))) << 32) |
+                       __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t));
+    int lo = 0, hi = n;  // s_off[lo] <= t0 < s_off[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (s_off[mid] <= t) lo = mid;
+        if (s_off[mid] <= t0) lo = mid;
         else hi = mid;
     }
-    return lo;
+    return __builtin_amdgcn_readfirstlane(lo);
 }
 
 // Marks the ids of the lists of the given pass.  In pass 1 (the seed lists, marked before
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(256) void k_mark(RelabelArgs a, int32_t pass) {
          t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int l = item_list(s_off, a.nlist, t);
         const IdList &L = a.list[l];
-        if (L.pass != pass) continue;
+        if (L.pass != pass || t - s_off[l] >= s_len[l]) continue;
         const int32_t v = L.ids[t - s_off[l]];
         if (v < 0 || v >= bound) {
             set_status(a.status, GNN_ERR_OUT_OF_RANGE);
@@ -313,6 +318,7 @@ __global__ __launch_bounds__(256) void k_rank(RelabelArgs a) {
          t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int l = item_list(s_off, nl, t);
         const int64_t i = t - s_off[l];
+        if (i >= s_len[l]) continue;
         if (l >= a.nlist) {
             const BitmapOut &o = a.out[l - a.nlist];
             const int32_t p = o.uniq[i];
