@@ -118,8 +118,10 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
         // tiles past the actual destinations have nothing to place (tile 0 still writes the totals)
         const int live = static_cast<int>((F + kDistTile - 1) / kDistTile);
         if (lt > 0 && lt >= live) continue;
+        // the sums of the earlier tiles (tile 0: of all tiles, for the sub-batch's total)
         uint32_t before = 0, all = 0;
-        for (int b = threadIdx.x; b < live; b += blockDim.x) {
+        const int upto = lt == 0 ? live : lt;
+        for (int b = threadIdx.x; b < upto; b += blockDim.x) {
             const uint32_t x = a.bsum[S.tile0 + b];
             all += x;
             if (b < lt) before += x;
