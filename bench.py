@@ -95,13 +95,29 @@ def algorithmic_bytes(counts, n_seeds, d, K):
     return gather, mean, E, V
 
 
+# Mini-batches per super-batch where the workload does not fix it: the largest the library takes
+# (sharing grows with it; dense 1849 -> 2117M, 111M-node 1351 -> 1653M, billion-edge 1732 ->
+# 1940M sampled edges/s from 8 to 16).
+DEFAULT_GROUP = 16
+
+
+def super_batch_size(cfg, requested: int) -> int:
+    """The super-batch size of a run: the one asked for, else the workload's own, else
+    DEFAULT_GROUP."""
+    if requested:
+        return requested
+    return cfg.group if cfg.group > 1 else DEFAULT_GROUP
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps (default: five epochs, or 100 super-batches)")
-    ap.add_argument("--group", type=int, default=8,
-                    help="mini-batches per super-batch (one step = one super-batch)")
+    ap.add_argument("--group", type=int, default=0,
+                    help="mini-batches per super-batch (one step = one super-batch); default: the "
+                         "workload's own where its definition fixes one (mid: 8), else "
+                         f"{DEFAULT_GROUP}")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dense")
     ap.add_argument("--streams", type=int, default=1,
@@ -153,7 +169,7 @@ def main():
         synth.make_features(cfg, table)
     order = synth.epoch_seed_order(cfg, 0, device=dev).contiguous()
     n_batches = (order.numel() + cfg.batch - 1) // cfg.batch
-    G = args.group
+    G = super_batch_size(cfg, args.group)
     n_super = (n_batches + G - 1) // G
     # default: five epochs for a workload with a training set (each epoch its own seed order),
     # else 100 super-batches (30 with a host-resident table), wrapping round a short seed order

@@ -51,3 +51,11 @@ def test_union_gather_choice():
 def test_sampler_ceiling_constant():
     # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz over 19 instructions per key
     assert abs(bench.KEYS_PEAK - 2.07e12) / 2.07e12 < 0.01
+
+
+def test_super_batch_size_default():
+    import synth
+    assert bench.super_batch_size(synth.CONFIGS["mid"], 0) == 8      # fixed by the workload
+    assert bench.super_batch_size(synth.CONFIGS["dense"], 0) == bench.DEFAULT_GROUP
+    assert bench.super_batch_size(synth.CONFIGS["billion"], 0) == bench.DEFAULT_GROUP
+    assert bench.super_batch_size(synth.CONFIGS["mid"], 4) == 4      # asked for

@@ -5,7 +5,8 @@ Workloads are generated on the GPU: the dense-neighbourhood one (233,000 nodes, 
 (2.45M nodes, 124M edges, 100-d, fanouts [15, 10, 5], super-batches of 8) and the large one
 (111M nodes, 1.6B edges, int64 indptr, 128-d, 57 GB of features in HBM).  Whole batches are
 compared with the oracle (bit-exact blocks and rows, means within 1e-5 * max|X|), with both
-super-batch relabel modes.
+super-batch relabel modes, and with the super-batches of 16 the benchmark runs on the dense and
+large workloads.
 """
 import numpy as np
 import pytest
@@ -90,6 +91,19 @@ def test_dense_superbatch_of_8(dense, mode):
         compare_with_oracle(outs[j], ref, cfg.d)
 
 
+def test_dense_superbatch_of_16(dense):
+    # the benchmark's super-batch size on this workload
+    cfg, g, table, order, (indptr, indices, x, order_h) = dense
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 1)
+    batches = list(range(16, 32))
+    outs, ptr = _run(cfg, g, table, order, batches, seed64)
+    for j in (0, 15):
+        b = batches[j]
+        seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
+        ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+        compare_with_oracle(outs[j], ref, cfg.d)
+
+
 def test_dense_superbatch_last_partial(dense):
     # the epoch's last super-batch of 8: batches 144..146, the last one short (496 seeds)
     cfg, g, table, order, (indptr, indices, x, order_h) = dense
@@ -123,6 +137,19 @@ def test_large_superbatch_of_8(large, mode, check):
     batches = list(range(0, 8))
     outs, ptr = _run(cfg, g, table, order, batches, seed64, mode)
     for j in check:
+        b = batches[j]
+        seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
+        ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
+        compare_with_oracle(outs[j], ref, cfg.d)
+
+
+def test_large_superbatch_of_16(large):
+    # the benchmark's super-batch size on this workload
+    cfg, g, table, order, (indptr, indices, x, order_h) = large
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 2)
+    batches = list(range(32, 48))
+    outs, ptr = _run(cfg, g, table, order, batches, seed64)
+    for j in (2, 15):
         b = batches[j]
         seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
         ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
