@@ -458,7 +458,8 @@ hipError_t launch_gather_batch(GatherBatchArgs a, int64_t rows_cap, hipStream_t 
     const int G = cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64);
     const int CH = G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);
     const int64_t slabs = (cpr + CH * G - 1) / (CH * G);
-    const int64_t units = (rows_cap + G - 1) / G * slabs + a.nseg * slabs;
+    // each sub-batch: its rounded-up row units and up to 64 / G - 1 padding units
+    const int64_t units = (rows_cap + G - 1) / G * slabs + a.nseg * (slabs + 64 / G);
     if (units > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const dim3 grid(grid_for(units, 4 * (64 / G), 8192));
     if (G == 16) hipLaunchKernelGGL((k_gather_batch<16, 1, 4>), grid, dim3(256), 0, s, a);
