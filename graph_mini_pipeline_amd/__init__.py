@@ -25,7 +25,8 @@ __all__ = [
     "gnn_status_string", "gnn_batch_seed", "gnn_capacity", "gnn_workspace_size", "gnn_sample_khop",
     "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
     "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_sage_layer",
-    "gnn_sage_update", "gnn_minibatch",
+    "gnn_sage_update", "gnn_minibatch", "AdjacencyCache", "gnn_adjacency_cache_create",
+    "gnn_host_mapped_pointer",
     "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
     "gnn_timer_elapsed", "gnn_copy_probe", "gnn_copy_probe_host", "gnn_hash_probe", "lib",
 ]
@@ -97,15 +98,29 @@ class Options:
         return o
 
 
+def gnn_host_mapped_pointer(t: torch.Tensor) -> int:
+    """The device address of a pinned host tensor's memory."""
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("expected a pinned host tensor")
+    out = ctypes.c_void_p()
+    _ok(lib().gnn_host_mapped_pointer(_ptr(t), ctypes.byref(out)), "gnn_host_mapped_pointer")
+    return int(out.value)
+
+
 @dataclass
 class DeviceGraph:
-    """CSR by destination in device memory (indptr int32 or int64, indices int32)."""
+    """CSR by destination: indptr (int32 or int64) in device memory; indices (int32) in device
+    memory or in pinned host memory (read in place); optionally an HBM adjacency cache."""
     num_nodes: int
     indptr: torch.Tensor
     indices: torch.Tensor
+    adjacency: Optional["AdjacencyCache"] = None
 
     def c(self) -> _abi.gnn_graph:
-        _need(self.indices, torch.int32, "indices")
+        host = not self.indices.is_cuda
+        _need(self.indices, torch.int32, "indices", device=not host)
+        if host and self.indices.numel() and not self.indices.is_pinned():
+            raise ValueError("host-resident indices must be pinned")
         if self.indptr.dtype not in (torch.int32, torch.int64) or not self.indptr.is_cuda:
             raise TypeError("indptr: int32 or int64 device tensor")
         g = _abi.gnn_graph()
@@ -113,8 +128,52 @@ class DeviceGraph:
         g.num_edges = self.indices.numel()
         g.indptr = self.indptr.data_ptr()
         g.indptr_bytes = self.indptr.element_size()
-        g.indices = self.indices.data_ptr() if self.indices.numel() else None
+        if not self.indices.numel():
+            g.indices = None
+        elif host:
+            g.indices = gnn_host_mapped_pointer(self.indices)
+        else:
+            g.indices = self.indices.data_ptr()
+        if self.adjacency is not None:
+            _ok(lib().gnn_adjacency_cache_attach(self.adjacency.handle, ctypes.byref(g)),
+                "gnn_adjacency_cache_attach")
         return g
+
+
+class AdjacencyCache:
+    """Owns a gnn_adjacency_cache handle (the HBM copies of hot adjacency rows)."""
+
+    def __init__(self, handle: ctypes.c_void_p, rows: int, entries: int):
+        self.handle = handle
+        self.rows = rows
+        self.entries = entries
+
+    def close(self):
+        if self.handle:
+            lib().gnn_adjacency_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gnn_adjacency_cache_create(graph: DeviceGraph, hot_order: torch.Tensor,
+                               max_entries: int) -> AdjacencyCache:
+    """HBM copies of the rows of hot_order (device int32, hottest first) that fit max_entries
+    neighbour ids; attach it with DeviceGraph(..., adjacency=cache)."""
+    _need(hot_order, torch.int32, "hot_order")
+    bare = DeviceGraph(graph.num_nodes, graph.indptr, graph.indices)
+    g = bare.c()
+    h = ctypes.c_void_p()
+    rows, entries = ctypes.c_int64(), ctypes.c_int64()
+    _ok(lib().gnn_adjacency_cache_create(ctypes.byref(g), _ptr(hot_order), hot_order.numel(),
+                                         max_entries, ctypes.byref(h), ctypes.byref(rows),
+                                         ctypes.byref(entries)),
+        "gnn_adjacency_cache_create")
+    return AdjacencyCache(h, rows.value, entries.value)
 
 
 def gnn_capacity(n_seeds: int, fanouts: Sequence[int], num_nodes: int) -> _abi.gnn_caps:

@@ -33,7 +33,7 @@ size_t = ctypes.c_size_t
 
 class gnn_graph(ctypes.Structure):
     _fields_ = [("num_nodes", i64), ("num_edges", i64), ("indptr", vp), ("indptr_bytes", i32),
-                ("indices", vp)]
+                ("indices", vp), ("adj_off", vp), ("adj_rows", vp)]
 
 
 class gnn_caps(ctypes.Structure):
@@ -73,6 +73,10 @@ SIGNATURES = {
     "gnn_relabel_workspace_size": (i32, [i64, P(size_t)]),
     "gnn_feature_store_create": (i32, [vp, i32, i64, i64, i64, i64, vp, P(vp)]),
     "gnn_feature_store_destroy": (i32, [vp]),
+    "gnn_host_mapped_pointer": (i32, [vp, P(vp)]),
+    "gnn_adjacency_cache_create": (i32, [P(gnn_graph), vp, i64, i64, P(vp), P(i64), P(i64)]),
+    "gnn_adjacency_cache_attach": (i32, [vp, P(gnn_graph)]),
+    "gnn_adjacency_cache_destroy": (i32, [vp]),
     "gnn_gather_features": (i32, [vp, vp, vp, i64, vp, i64, vp, vp, vp]),
     "gnn_mean_aggregate": (i32, [vp, vp, i64, vp, i64, vp, i64, i64, i64, vp, i64, vp, vp]),
     "gnn_sage_update": (i32, [vp, vp, i64, vp, i64, i64, i64, vp, i64, vp, vp, i64, i32, vp, i64,

@@ -19,6 +19,13 @@ struct gnn_feature_store {
     int32_t *slot;  // [num_nodes] cache slot of each node, -1 if not cached; NULL if no cache
 };
 
+struct gnn_adjacency_cache {
+    int64_t num_nodes;
+    int64_t *adj_off;  // [num_nodes] offset of each node's cached row in rows, -1 if not cached
+    int32_t *rows;     // the cached rows, back to back
+    int64_t n_rows, n_entries;
+};
+
 // Events per record: call start, end of sampling, then per sub-batch the ends of its gather and
 // of its outermost-block mean (batched gather: slot 2 ends the one gather launch and slot 1 + 2G
 // the one outermost-mean launch), then the end of the call; then two per hop around the sampling
@@ -245,6 +252,7 @@ gnn_status check_graph(const gnn_graph *g) {
     if (g->indptr_bytes != 4 && g->indptr_bytes != 8) return GNN_ERR_INVALID_ARG;
     if (g->indptr_bytes == 4 && g->num_edges > kInt32Max) return GNN_ERR_INVALID_ARG;
     if (!g->indptr || (g->num_edges > 0 && !g->indices)) return GNN_ERR_INVALID_ARG;
+    if ((g->adj_off == nullptr) != (g->adj_rows == nullptr)) return GNN_ERR_INVALID_ARG;
     return GNN_OK;
 }
 
@@ -284,6 +292,8 @@ HopArgs hop_args(const gnn_graph &g, const int32_t *front, const int64_t *d_F, i
     HopArgs h{};
     h.indptr = g.indptr;
     h.indices = g.indices;
+    h.adj_off = g.adj_off;
+    h.adj_rows = g.adj_rows;
     h.num_nodes = g.num_nodes;
     h.front = front;
     h.d_F = d_F;
@@ -756,6 +766,112 @@ gnn_status gnn_feature_store_create(const float *table, int32_t table_on_host, i
         }
     }
     *out = fs;
+    return GNN_OK;
+}
+
+gnn_status gnn_host_mapped_pointer(const void *host, const void **out_device) {
+    if (!host || !out_device) return GNN_ERR_INVALID_ARG;
+    *out_device = nullptr;
+    void *p = nullptr;
+    if (hipHostGetDevicePointer(&p, const_cast<void *>(host), 0) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return GNN_ERR_HIP;
+    }
+    *out_device = p;
+    return GNN_OK;
+}
+
+gnn_status gnn_adjacency_cache_create(const gnn_graph *g, const int32_t *hot_order, int64_t n_hot,
+                                      int64_t max_entries, gnn_adjacency_cache **out,
+                                      int64_t *out_rows, int64_t *out_entries) {
+    if (!out) return GNN_ERR_INVALID_ARG;
+    *out = nullptr;
+    const gnn_status gs = check_graph(g);
+    if (gs != GNN_OK) return gs;
+    if (n_hot < 0 || n_hot > g->num_nodes || max_entries < 0 || (n_hot > 0 && !hot_order))
+        return GNN_ERR_INVALID_ARG;
+    // the hot ids and their degrees, on the host, choose the rows that fit (in order)
+    std::vector<int32_t> hot(static_cast<size_t>(n_hot));
+    std::vector<int64_t> deg(static_cast<size_t>(n_hot));
+    if (n_hot > 0) {
+        if (hipMemcpy(hot.data(), hot_order, n_hot * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+            hipSuccess)
+            return GNN_ERR_HIP;
+        for (int32_t v : hot)
+            if (v < 0 || v >= g->num_nodes) return GNN_ERR_INVALID_ARG;
+        int64_t *d_deg = nullptr;
+        bool ok = hipMalloc(reinterpret_cast<void **>(&d_deg), n_hot * sizeof(int64_t)) == hipSuccess;
+        ok = ok && launch_adj_degrees(g->indptr, g->indptr_bytes, hot_order, n_hot, d_deg,
+                                      nullptr) == hipSuccess;
+        ok = ok && hipMemcpy(deg.data(), d_deg, n_hot * sizeof(int64_t), hipMemcpyDeviceToHost) ==
+                       hipSuccess;
+        if (d_deg) (void)hipFree(d_deg);
+        if (!ok) return GNN_ERR_HIP;
+    }
+    std::vector<int32_t> node;
+    std::vector<int64_t> off;
+    int64_t used = 0;
+    for (int64_t i = 0; i < n_hot; ++i) {
+        const int64_t dv = deg[static_cast<size_t>(i)];
+        if (dv <= 0 || used + dv > max_entries) continue;   // empty, or too long for what is left
+        node.push_back(hot[static_cast<size_t>(i)]);
+        off.push_back(used);
+        used += dv;
+    }
+    gnn_adjacency_cache *c = new (std::nothrow) gnn_adjacency_cache{};
+    if (!c) return GNN_ERR_INVALID_ARG;
+    c->num_nodes = g->num_nodes;
+    const int64_t n = static_cast<int64_t>(node.size());
+    int32_t *d_node = nullptr;
+    int64_t *d_off = nullptr;
+    bool ok = hipMalloc(reinterpret_cast<void **>(&c->adj_off), g->num_nodes * sizeof(int64_t)) ==
+              hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&c->rows),
+                         (used > 0 ? used : 1) * sizeof(int32_t)) == hipSuccess;
+    ok = ok && hipMemset(c->adj_off, 0xFF, g->num_nodes * sizeof(int64_t)) == hipSuccess;  // -1
+    if (ok && n > 0) {
+        ok = hipMalloc(reinterpret_cast<void **>(&d_node), n * sizeof(int32_t)) == hipSuccess;
+        ok = ok && hipMalloc(reinterpret_cast<void **>(&d_off), n * sizeof(int64_t)) == hipSuccess;
+        ok = ok && hipMemcpy(d_node, node.data(), n * sizeof(int32_t), hipMemcpyHostToDevice) ==
+                       hipSuccess;
+        ok = ok && hipMemcpy(d_off, off.data(), n * sizeof(int64_t), hipMemcpyHostToDevice) ==
+                       hipSuccess;
+        ok = ok && launch_adj_fill(g->indptr, g->indptr_bytes, g->indices, d_node, d_off, n,
+                                   c->rows, c->adj_off, nullptr) == hipSuccess;
+    }
+    ok = ok && hipDeviceSynchronize() == hipSuccess;
+    if (d_node) (void)hipFree(d_node);
+    if (d_off) (void)hipFree(d_off);
+    if (!ok) {
+        gnn_adjacency_cache_destroy(c);
+        return GNN_ERR_HIP;
+    }
+    c->n_rows = n;
+    c->n_entries = used;
+    if (out_rows) *out_rows = n;
+    if (out_entries) *out_entries = used;
+    *out = c;
+    return GNN_OK;
+}
+
+gnn_status gnn_adjacency_cache_attach(const gnn_adjacency_cache *c, gnn_graph *g) {
+    if (!g) return GNN_ERR_INVALID_ARG;
+    if (!c) {
+        g->adj_off = nullptr;
+        g->adj_rows = nullptr;
+        return GNN_OK;
+    }
+    if (c->num_nodes != g->num_nodes) return GNN_ERR_INVALID_ARG;
+    g->adj_off = c->adj_off;
+    g->adj_rows = c->rows;
+    return GNN_OK;
+}
+
+gnn_status gnn_adjacency_cache_destroy(gnn_adjacency_cache *c) {
+    if (!c) return GNN_OK;
+    if (c->adj_off) (void)hipFree(c->adj_off);
+    if (c->rows) (void)hipFree(c->rows);
+    delete c;
     return GNN_OK;
 }
 

@@ -135,7 +135,9 @@ constexpr int kMaxFanout = kBlockCap / 4;
 // One sampling hop.
 struct HopArgs {
     const void *indptr;
-    const int32_t *indices;
+    const int32_t *indices;     // device, or pinned host memory read in place
+    const int64_t *adj_off;     // optional HBM adjacency cache: row v at adj_rows + adj_off[v]
+    const int32_t *adj_rows;
     int64_t num_nodes;
     const int32_t *front;   // destinations V_{l-1}
     const int64_t *d_F;     // device count of front (NULL: F_cap)
@@ -339,6 +341,13 @@ hipError_t launch_sage_update(const int32_t *dst_lid, const int64_t *d_n, int64_
 // in that bitmap.
 // Rows must be 16-byte aligned (ld and ld_out multiples of 4, aligned bases): otherwise
 // hipErrorInvalidValue is returned and nothing is launched.
+// Adjacency cache set-up: deg[i] = degree of hot[i]; then rows of the selected nodes copied to
+// rows + off[i] and adj_off[node[i]] = off[i].
+hipError_t launch_adj_degrees(const void *indptr, int32_t ib, const int32_t *hot, int64_t n,
+                              int64_t *deg, hipStream_t s);
+hipError_t launch_adj_fill(const void *indptr, int32_t ib, const int32_t *indices,
+                           const int32_t *node, const int64_t *off, int64_t n, int32_t *rows,
+                           int64_t *adj_off, hipStream_t s);
 hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                                const int32_t *ids, const int64_t *d_n, int64_t n_cap,
                                const uint32_t *bm, const uint32_t *wp, int64_t words, int by_id,

@@ -29,6 +29,16 @@ namespace gnnmb {
 
 // ---- classification: count, scan, scatter ------------------------------------------------------
 
+// Node v's neighbour ids: its row in the HBM adjacency cache when the cache holds it, else its
+// CSR row (HBM, or pinned host memory read in place).
+__device__ __forceinline__ const int32_t *adj_row(const HopArgs &a, int32_t v, int64_t start) {
+    if (a.adj_off != nullptr) {
+        const int64_t o = a.adj_off[v];
+        if (o >= 0) return a.adj_rows + o;
+    }
+    return a.indices + start;
+}
+
 __device__ __forceinline__ int32_t node_class(int64_t deg, int k, int group_max, int wave_max) {
     if (deg <= k) return kFull;
     if (deg <= group_max && k * 4 <= kGroupCap) return kGroup;
@@ -376,6 +386,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
     const int32_t v = a.front[i];
     const int64_t start = row_ptr(a.indptr, a.ib, v);
     const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - start;
+    const int32_t *row = adj_row(a, v, start);
     const int64_t out0 = a.blk_indptr[i];
     const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
     uint32_t tau = initial_tau(deg, k), lo = 0, hi = 0;
@@ -411,7 +422,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         const uint64_t m = __ballot(sel) & gmask;
         if (sel) {
             const int64_t o = out0 + outc + __popcll(m & below);
-            if (o < a.E_cap) a.blk_gid[o] = a.indices[start + jc];
+            if (o < a.E_cap) a.blk_gid[o] = row[jc];
         }
         outc += __popcll(m);
     }
@@ -430,6 +441,7 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
     const int32_t v = a.front[i];
     const int64_t start = row_ptr(a.indptr, a.ib, v);
     const int64_t deg64 = row_ptr(a.indptr, a.ib, v + 1) - start;
+    const int32_t *row = adj_row(a, v, start);
     const int64_t out0 = a.blk_indptr[i];
     const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
     uint32_t tau = initial_tau(deg64, k), lo = 0, hi = 0;
@@ -530,7 +542,7 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
             r += (pt < 0) & ((pt & 0x7FFFFFFF) < jc);
         }
         const int64_t o = out0 + r;
-        if (o < a.E_cap) a.blk_gid[o] = a.indices[start + jc];
+        if (o < a.E_cap) a.blk_gid[o] = row[jc];
     }
     __syncthreads();
 }
@@ -605,8 +617,38 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int64_t st = row_ptr(a.indptr, a.ib, v);
         const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - st;
         const int64_t o = a.blk_indptr[i];
+        const int32_t *row = adj_row(a, v, st);
         for (int64_t j = 0; j < deg; ++j)
-            if (o + j < a.E_cap) a.blk_gid[o + j] = a.indices[st + j];
+            if (o + j < a.E_cap) a.blk_gid[o + j] = row[j];
+    }
+}
+
+// ---- adjacency cache set-up (not on the mini-batch path) -------------------------------------
+
+__global__ __launch_bounds__(256) void k_adj_degrees(const void *indptr, int32_t ib,
+                                                     const int32_t *hot, int64_t n, int64_t *deg) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int32_t v = hot[i];
+        deg[i] = row_ptr(indptr, ib, v + 1) - row_ptr(indptr, ib, v);
+    }
+}
+
+// One wavefront per selected node: its row copied to rows + off[i], then its offset published.
+__global__ __launch_bounds__(256) void k_adj_fill(const void *indptr, int32_t ib,
+                                                  const int32_t *indices, const int32_t *node,
+                                                  const int64_t *off, int64_t n, int32_t *rows,
+                                                  int64_t *adj_off) {
+    const int lane = lane_id();
+    const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+    for (int64_t i = w0; i < n; i += nw) {
+        const int32_t v = node[i];
+        const int64_t st = row_ptr(indptr, ib, v);
+        const int64_t deg = row_ptr(indptr, ib, v + 1) - st;
+        const int64_t o = off[i];
+        for (int64_t j = lane; j < deg; j += 64) rows[o + j] = indices[st + j];
+        if (lane == 0) adj_off[v] = o;
     }
 }
 
@@ -641,6 +683,23 @@ hipError_t launch_sample(const HopArgs &a, hipStream_t s) {
     const int nb_full = static_cast<int>(grid_for(F, kBlockThreads, 128));
     hipLaunchKernelGGL(k_sample, dim3(nb_block + nb_wave + nb_group + nb_full), dim3(kBlockThreads),
                        0, s, a, nb_block, nb_wave, nb_group);
+    return hipGetLastError();
+}
+
+hipError_t launch_adj_degrees(const void *indptr, int32_t ib, const int32_t *hot, int64_t n,
+                              int64_t *deg, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_adj_degrees, dim3(grid_for(n, 256, 4096)), dim3(256), 0, s, indptr, ib,
+                       hot, n, deg);
+    return hipGetLastError();
+}
+
+hipError_t launch_adj_fill(const void *indptr, int32_t ib, const int32_t *indices,
+                           const int32_t *node, const int64_t *off, int64_t n, int32_t *rows,
+                           int64_t *adj_off, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_adj_fill, dim3(grid_for(n, 4, 8192)), dim3(256), 0, s, indptr, ib,
+                       indices, node, off, n, rows, adj_off);
     return hipGetLastError();
 }
 

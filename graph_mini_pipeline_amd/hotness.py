@@ -10,7 +10,7 @@ the same for any ranking.  The batches should not be the measured ones (a disjoi
 """
 from __future__ import annotations
 
-from typing import Sequence
+from typing import Optional, Sequence
 
 import torch
 
@@ -19,9 +19,10 @@ from . import (Blocks, DeviceGraph, gnn_batch_seed, gnn_capacity, gnn_read_devic
 
 
 def presample_counts(graph: DeviceGraph, seeds: torch.Tensor, batch: int, fanouts: Sequence[int],
-                     rng_seed: int) -> torch.Tensor:
-    """int32 [N]: for each node, the number of pre-sampled batches whose V_K holds it.  Batch p
-    takes seeds[p*batch:(p+1)*batch] and the batch seed gnn_batch_seed(rng_seed, p)."""
+                     rng_seed: int, levels: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """int32 [N]: for each node, the number of (pre-sampled batch, level l in `levels`) with v in
+    V_l; by default levels = [K], i.e. the batches whose gathered set V_K holds v.  Batch p takes
+    seeds[p*batch:(p+1)*batch] and the batch seed gnn_batch_seed(rng_seed, p)."""
     N = graph.num_nodes
     K = len(fanouts)
     dev = seeds.device
@@ -36,14 +37,19 @@ def presample_counts(graph: DeviceGraph, seeds: torch.Tensor, batch: int, fanout
         st = gnn_read_device_status(ws)
         if st != GNN_OK:
             raise GnnError(st, "pre-sampling")
-        nv = int(blocks.counts[2 * K - 1].item())
-        counts.index_add_(0, blocks.nodes[K - 1][:nv].long(),
-                          torch.ones(nv, dtype=torch.int32, device=dev))
+        for lv in (levels if levels is not None else [K]):
+            if lv == 0:
+                ids = s
+            else:
+                ids = blocks.nodes[lv - 1][:int(blocks.counts[2 * lv - 1].item())]
+            counts.index_add_(0, ids.long(), torch.ones(ids.numel(), dtype=torch.int32, device=dev))
     return counts
 
 
-def rank_rows(counts: torch.Tensor, degree: torch.Tensor, rows: int) -> torch.Tensor:
-    """int32 [rows]: the ids of the `rows` hottest rows by (count desc, degree desc, id asc)."""
+def rank_rows(counts: torch.Tensor, degree: torch.Tensor, rows: int,
+              degree_desc: bool = True) -> torch.Tensor:
+    """int32 [rows]: the ids of the `rows` hottest rows by (count desc, degree desc, id asc), or
+    with degree_desc=False by (count desc, degree asc, id asc)."""
     N = counts.numel()
     id_bits = max(1, (N - 1).bit_length())
     cmax = int(counts.max().item()) if N else 0
@@ -53,8 +59,9 @@ def rank_rows(counts: torch.Tensor, degree: torch.Tensor, rows: int) -> torch.Te
         raise ValueError("too many nodes or counts for the ranking key")
     dcap = (1 << d_bits) - 1
     ids = torch.arange(N, dtype=torch.int64, device=counts.device)
+    dkey = degree.to(torch.int64).clamp(0, dcap)
     key = ((cmax - counts.to(torch.int64)) << (d_bits + id_bits)) \
-        | ((dcap - degree.to(torch.int64).clamp(0, dcap)) << id_bits) | ids
+        | ((dcap - dkey if degree_desc else dkey) << id_bits) | ids
     order = torch.sort(key).values & ((1 << id_bits) - 1)
     return order[:rows].to(torch.int32).contiguous()
 
@@ -65,3 +72,17 @@ def presample_hot_order(graph: DeviceGraph, indptr: torch.Tensor, seeds: torch.T
     counts = presample_counts(graph, seeds, batch, fanouts, rng_seed)
     degree = indptr[1:] - indptr[:-1]
     return rank_rows(counts, degree, rows)
+
+
+def presample_adjacency_order(graph: DeviceGraph, indptr: torch.Tensor, seeds: torch.Tensor,
+                              batch: int, fanouts: Sequence[int], rng_seed: int) -> torch.Tensor:
+    """Hot order for gnn_adjacency_cache_create.  The sampler reads node v's adjacency row at hop
+    l when v is in the frontier V_{l-1}, so a node counts once per (pre-sampled batch, frontier
+    level 0..K-1) that holds it (GARDEN Sec. IV.B counts accesses along the whole sampling path,
+    eq. (4)); rows with a count are ranked by (count desc, degree asc, id asc): of equally hot
+    rows the short ones first, as they take less of the cache."""
+    K = len(fanouts)
+    counts = presample_counts(graph, seeds, batch, fanouts, rng_seed, levels=list(range(K)))
+    degree = indptr[1:] - indptr[:-1]
+    hot = int((counts > 0).sum().item())
+    return rank_rows(counts, degree, hot, degree_desc=False)

@@ -77,6 +77,13 @@ typedef void *gnn_stream; /* hipStream_t */
 /*
  * Graph in CSR form by destination: row v lists the sources u of the edges (u, v), which is the
  * neighbourhood N(v) = {u | (u, v) in E} of GARDEN Sec. II.A.  Borrowed, read-only.
+ *   indptr: device memory.
+ *   indices: device memory, or the device address of pinned host memory (gnn_host_mapped_pointer)
+ *     for an adjacency larger than HBM, read in place by the sampler (GARDEN Sec. IV.B: adjacency
+ *     served from host memory, with an adjacency cache in GPU memory).
+ *   adj_off, adj_rows: an optional HBM adjacency cache (gnn_adjacency_cache_attach sets them;
+ *     both NULL: none): row v's neighbours are adj_rows[adj_off[v] ..) when adj_off[v] >= 0.
+ * Results do not depend on where the rows are read from.
  */
 typedef struct gnn_graph {
     int64_t num_nodes;     /* N */
@@ -84,7 +91,32 @@ typedef struct gnn_graph {
     const void *indptr;    /* [N+1], int32 or int64 (indptr_bytes) */
     int32_t indptr_bytes;  /* 4 or 8 */
     const int32_t *indices; /* [num_edges] neighbour ids */
+    const int64_t *adj_off;  /* [N] or NULL */
+    const int32_t *adj_rows; /* cached rows or NULL */
 } gnn_graph;
+
+/*
+ * The device address of pinned, mapped host memory (hipHostMalloc), for a graph's indices or a
+ * feature table read in place.  Errors: GNN_ERR_INVALID_ARG, GNN_ERR_HIP (not mapped).
+ */
+gnn_status gnn_host_mapped_pointer(const void *host, const void **out_device);
+
+/*
+ * Adjacency cache (GARDEN Sec. IV.B, the adjacency part of the cache allocator): the rows of the
+ * nodes hot_order[0..n_hot) (device, distinct ids, hottest first) copied into HBM, taken in that
+ * order while they fit max_entries neighbour ids in all (a row that does not fit is skipped).
+ * The graph's indices may be host-resident.  Setup call: allocates adj_off [N] (int64) and the
+ * rows with hipMalloc and synchronises.  *out_rows / *out_entries (may be NULL) receive the
+ * numbers of rows and ids cached.
+ * Errors: GNN_ERR_INVALID_ARG (bad graph, ids out of range or repeated), GNN_ERR_HIP.
+ */
+typedef struct gnn_adjacency_cache gnn_adjacency_cache;
+gnn_status gnn_adjacency_cache_create(const gnn_graph *g, const int32_t *hot_order, int64_t n_hot,
+                                      int64_t max_entries, gnn_adjacency_cache **out,
+                                      int64_t *out_rows, int64_t *out_entries);
+/* Points g->adj_off and g->adj_rows at the cache (same num_nodes), or clears them (c = NULL). */
+gnn_status gnn_adjacency_cache_attach(const gnn_adjacency_cache *c, gnn_graph *g);
+gnn_status gnn_adjacency_cache_destroy(gnn_adjacency_cache *c);
 
 /* Worst-case element counts per hop, l = 1..K at index l-1. */
 typedef struct gnn_caps {

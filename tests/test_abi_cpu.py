@@ -42,7 +42,7 @@ def test_ctypes_layout_matches_header(tmp_path):
 #define O(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
 int main(void) {
   S(gnn_graph) S(gnn_caps) S(gnn_block) S(gnn_blocks) S(gnn_options) S(gnn_minibatch_out)
-  O(gnn_graph, indices) O(gnn_caps, nodes) O(gnn_blocks, counts) O(gnn_minibatch_out, ld_h)
+  O(gnn_graph, indices) O(gnn_graph, adj_rows) O(gnn_caps, nodes) O(gnn_blocks, counts) O(gnn_minibatch_out, ld_h)
   O(gnn_minibatch_out, x) O(gnn_options, flags) return 0; }
 ''')
     exe = tmp_path / "layout"
@@ -55,6 +55,7 @@ int main(void) {
         "gnn_options": ctypes.sizeof(_abi.gnn_options),
         "gnn_minibatch_out": ctypes.sizeof(_abi.gnn_minibatch_out),
         "gnn_graph.indices": _abi.gnn_graph.indices.offset,
+        "gnn_graph.adj_rows": _abi.gnn_graph.adj_rows.offset,
         "gnn_caps.nodes": _abi.gnn_caps.nodes.offset,
         "gnn_blocks.counts": _abi.gnn_blocks.counts.offset,
         "gnn_minibatch_out.ld_h": _abi.gnn_minibatch_out.ld_h.offset,
@@ -178,6 +179,28 @@ def test_validation_before_device_work():
     # feature store: ld < d
     assert L.gnn_feature_store_create(8, 0, 10, 8, 4, 0, None,
                                       ctypes.byref(t)) == gm.GNN_ERR_INVALID_ARG
+    # adjacency cache: no handle out, more hot ids than nodes, negative budget, missing hot
+    # order, a graph with only one of its two cache pointers; mapping a NULL host pointer
+    g.indptr_bytes = 4
+    assert L.gnn_adjacency_cache_create(ctypes.byref(g), 8, 1, 10, None, None,
+                                        None) == gm.GNN_ERR_INVALID_ARG
+    assert L.gnn_adjacency_cache_create(ctypes.byref(g), 8, 11, 10, ctypes.byref(t), None,
+                                        None) == gm.GNN_ERR_INVALID_ARG
+    assert L.gnn_adjacency_cache_create(ctypes.byref(g), 8, 1, -1, ctypes.byref(t), None,
+                                        None) == gm.GNN_ERR_INVALID_ARG
+    assert L.gnn_adjacency_cache_create(ctypes.byref(g), None, 1, 10, ctypes.byref(t), None,
+                                        None) == gm.GNN_ERR_INVALID_ARG
+    g.adj_off = 8
+    assert L.gnn_adjacency_cache_create(ctypes.byref(g), 8, 1, 10, ctypes.byref(t), None,
+                                        None) == gm.GNN_ERR_INVALID_ARG
+    assert L.gnn_sample_khop(ctypes.byref(g), 8, 4, fo, 1, 0, ctypes.byref(blocks), 8, 1 << 20,
+                             None, None) == gm.GNN_ERR_INVALID_ARG
+    g.adj_off = None
+    assert L.gnn_adjacency_cache_attach(None, None) == gm.GNN_ERR_INVALID_ARG
+    assert L.gnn_adjacency_cache_attach(None, ctypes.byref(g)) == gm.GNN_OK   # detach
+    assert L.gnn_adjacency_cache_destroy(None) == gm.GNN_OK
+    p = ctypes.c_void_p()
+    assert L.gnn_host_mapped_pointer(None, ctypes.byref(p)) == gm.GNN_ERR_INVALID_ARG
 
 
 def test_header_constants_match_binding():

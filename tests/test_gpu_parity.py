@@ -328,6 +328,40 @@ def test_host_resident_table_zero_copy(tiny):
         compare_with_oracle(outs[0], ref, cfg.d)
 
 
+@pytest.mark.parametrize("budget", [0, 3000, 40000, None])     # None: room for every row
+@pytest.mark.parametrize("where", ["host", "hbm"])
+def test_adjacency_host_resident_and_cached(tiny, where, budget):
+    """Neighbour ids read from pinned host memory in place and/or from an HBM adjacency cache of
+    several sizes: the same blocks, rows and means as the oracle (a super-batch of 8)."""
+    from graph_mini_pipeline_amd.hotness import presample_adjacency_order
+    cfg, indptr, indices, x, order = tiny
+    base = device_graph(indptr, indices)
+    if where == "host":
+        ind = torch.empty(len(indices), dtype=torch.int32, pin_memory=True)
+        ind.copy_(torch.from_numpy(indices))
+    else:
+        ind = base.indices
+    bare = gm.DeviceGraph(base.num_nodes, base.indptr, ind)
+    pre = torch.from_numpy(order[-4 * cfg.batch:].copy()).cuda()
+    hot = presample_adjacency_order(base, base.indptr, pre, cfg.batch, cfg.fanouts, 99)
+    assert torch.unique(hot).numel() == hot.numel() > 0
+    cap = len(indices) if budget is None else budget
+    cache = gm.gnn_adjacency_cache_create(bare, hot, cap)
+    deg = np.diff(indptr)[hot.cpu().numpy()]
+    assert cache.entries <= cap and cache.rows <= int((deg > 0).sum())
+    if budget is None:
+        assert cache.rows == int((deg > 0).sum()) and cache.entries == int(deg.sum())
+    dg = gm.DeviceGraph(base.num_nodes, base.indptr, ind, adjacency=cache if cap else None)
+    fs = _store(x)
+    ptr = [j * cfg.batch for j in range(9)]
+    seeds = order[:ptr[-1]]
+    outs, st = run_minibatch(dg, fs, seeds, cfg.fanouts, 13, group_ptr=ptr)
+    assert st == gm.GNN_OK
+    for j in (0, 7):
+        ref = oracle.minibatch(indptr, indices, x, seeds[ptr[j]:ptr[j + 1]], cfg.fanouts, 13)
+        compare_with_oracle(outs[j], ref, cfg.d)
+
+
 def test_repeat_runs_identical(tiny):
     cfg, indptr, indices, x, order = tiny
     dg = device_graph(indptr, indices)

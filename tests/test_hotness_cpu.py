@@ -28,3 +28,11 @@ def test_rank_is_a_permutation_prefix():
     got = rank_rows(counts, deg, 777)
     ref = sorted(range(20000), key=lambda v: (-int(counts[v]), -int(deg[v]), v))[:777]
     assert got.tolist() == ref
+
+
+def test_rank_rows_degree_ascending():
+    # equal counts: the short rows first when asked (the adjacency cache's order)
+    counts = torch.tensor([2, 5, 5, 0, 5], dtype=torch.int32)
+    degree = torch.tensor([9, 7, 3, 1, 7], dtype=torch.int64)
+    assert rank_rows(counts, degree, 5, degree_desc=False).tolist() == [2, 1, 4, 0, 3]
+    assert rank_rows(counts, degree, 5).tolist() == [1, 4, 2, 0, 3]
