@@ -139,6 +139,12 @@ def main():
                          "e.g. 5,10,15 for GARDEN's fanout-pattern sweep")
     ap.add_argument("--no-sage", action="store_true",
                     help="skip the GraphSAGE-mean layer measurement")
+    ap.add_argument("--host-indices", action="store_true",
+                    help="the graph's neighbour ids in pinned host memory, read in place by the "
+                         "sampler (indptr stays in HBM)")
+    ap.add_argument("--adj-cache-gb", type=float, default=0.0,
+                    help="with --host-indices: an HBM adjacency cache of this many GB of "
+                         "pre-sampled hot rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU: the mini-batch path is measured on "
@@ -185,6 +191,35 @@ def main():
     K = len(cfg.fanouts)
 
     dg = gm.DeviceGraph(cfg.num_nodes, graph.indptr, graph.indices)
+    adj = None          # host-resident neighbour ids: what the adjacency cache holds
+    if args.host_indices:
+        from graph_mini_pipeline_amd.hotness import presample_adjacency_order
+        t1 = time.perf_counter()
+        ind_host = torch.empty(graph.indices.numel(), dtype=torch.int32, pin_memory=True)
+        ind_host.copy_(graph.indices)
+        adj_entries = int(args.adj_cache_gb * 1e9) // 4
+        adj_cache, cached = None, torch.zeros(cfg.num_nodes, dtype=torch.bool, device=dev)
+        if adj_entries:
+            pre = synth.presample_seeds(cfg, PRESAMPLE_BATCHES, device=dev)
+            if pre.numel() // cfg.batch + steps * G > n_batches:
+                raise SystemExit("pre-sampling seeds would overlap the measured batches")
+            adj_hot = presample_adjacency_order(dg, graph.indptr, pre, cfg.batch, cfg.fanouts,
+                                                synth.sub_seed(cfg.rng_seed, 7))
+            adj_cache = gm.gnn_adjacency_cache_create(
+                gm.DeviceGraph(cfg.num_nodes, graph.indptr, ind_host), adj_hot, adj_entries)
+            # the cache holds the longest prefix of the order that fits (the library's rule)
+            dh = (graph.indptr[1:] - graph.indptr[:-1])[adj_hot.long()]
+            m = int((torch.cumsum(dh, 0) <= adj_entries).sum().item())
+            cached[adj_hot[:m].long()] = True
+        graph = synth.Graph(graph.num_nodes, graph.indptr, ind_host)   # ids leave HBM
+        torch.cuda.empty_cache()
+        dg = gm.DeviceGraph(cfg.num_nodes, graph.indptr, ind_host, adjacency=adj_cache)
+        adj = {"cached": cached, "cache": adj_cache, "entries": adj_entries,
+               "setup_s": time.perf_counter() - t1, "rows_read": 0, "rows_hit": 0,
+               "ids_read": 0, "ids_hit": 0}
+        progress(f"neighbour ids in pinned host memory; adjacency cache "
+                 f"{adj_cache.rows if adj_cache else 0} rows, "
+                 f"{adj_cache.entries if adj_cache else 0} ids, {adj['setup_s']:.1f} s")
     cache_rows, t_rank = 0, 0.0
     hot_order = None
     if cfg.cache_bytes:
@@ -311,6 +346,13 @@ def main():
             u = torch.unique(torch.cat(fr).long())
             dd = deg[u]
             keys += int(dd[dd > cfg.fanouts[l]].sum().item())
+            if adj is not None:   # rows the sampler reads: ids min(deg, k) of each, cached or not
+                ids = dd.clamp(max=cfg.fanouts[l])
+                hit = adj["cached"][u]
+                adj["rows_read"] += int((dd > 0).sum().item())
+                adj["rows_hit"] += int(((dd > 0) & hit).sum().item())
+                adj["ids_read"] += int(ids.sum().item())
+                adj["ids_hit"] += int(ids[hit].sum().item())
         g_s, m_s, p_s = 0, [0] * K, 0
         for _, n, out in mine:
             if cache_rows:   # hits of this batch's gather: the same gather again, counting
@@ -425,6 +467,20 @@ def main():
     gm.gnn_copy_probe(probe_src, probe_dst)
     torch.cuda.synchronize()
     result["copy_probe_bytes"] = probe_src.numel() * 4
+    if adj is not None:
+        c = adj["cache"]
+        result["config"]["neighbour_ids"] = "pinned host memory, read in place"
+        result["adjacency"] = {
+            "cache_rows": c.rows if c else 0, "cache_ids": c.entries if c else 0,
+            "cache_GB": (c.entries if c else 0) * 4 / 1e9,
+            "cache_fraction_of_edges": (c.entries if c else 0) / max(1, graph.indices.numel()),
+            "ranking": f"{PRESAMPLE_BATCHES} pre-sampled batches from seeds the measurement does "
+                       f"not use; host reads saved per cached id, sum over hops of (batches whose "
+                       f"frontier holds the node) * min(deg, k) / deg, desc" if c else None,
+            "setup_s": adj["setup_s"],
+            "hit_rate_rows": adj["rows_hit"] / max(1, adj["rows_read"]),
+            "hit_rate_ids": adj["ids_hit"] / max(1, adj["ids_read"]),
+            "host_ids_per_step": (adj["ids_read"] - adj["ids_hit"]) / steps}
     del probe_src, probe_dst
 
     if cfg.host_features:

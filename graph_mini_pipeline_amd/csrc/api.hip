@@ -790,7 +790,7 @@ gnn_status gnn_adjacency_cache_create(const gnn_graph *g, const int32_t *hot_ord
     if (gs != GNN_OK) return gs;
     if (n_hot < 0 || n_hot > g->num_nodes || max_entries < 0 || (n_hot > 0 && !hot_order))
         return GNN_ERR_INVALID_ARG;
-    // the hot ids and their degrees, on the host, choose the rows that fit (in order)
+    // the hot ids and their degrees, on the host: the longest prefix of the order that fits
     std::vector<int32_t> hot(static_cast<size_t>(n_hot));
     std::vector<int64_t> deg(static_cast<size_t>(n_hot));
     if (n_hot > 0) {
@@ -813,7 +813,8 @@ gnn_status gnn_adjacency_cache_create(const gnn_graph *g, const int32_t *hot_ord
     int64_t used = 0;
     for (int64_t i = 0; i < n_hot; ++i) {
         const int64_t dv = deg[static_cast<size_t>(i)];
-        if (dv <= 0 || used + dv > max_entries) continue;   // empty, or too long for what is left
+        if (used + dv > max_entries) break;   // the hottest rows that fit, in order
+        if (dv <= 0) continue;                // an empty row needs no copy
         node.push_back(hot[static_cast<size_t>(i)]);
         off.push_back(used);
         used += dv;

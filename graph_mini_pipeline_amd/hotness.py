@@ -20,13 +20,15 @@ from . import (Blocks, DeviceGraph, gnn_batch_seed, gnn_capacity, gnn_read_devic
 
 def presample_counts(graph: DeviceGraph, seeds: torch.Tensor, batch: int, fanouts: Sequence[int],
                      rng_seed: int, levels: Optional[Sequence[int]] = None) -> torch.Tensor:
-    """int32 [N]: for each node, the number of (pre-sampled batch, level l in `levels`) with v in
-    V_l; by default levels = [K], i.e. the batches whose gathered set V_K holds v.  Batch p takes
-    seeds[p*batch:(p+1)*batch] and the batch seed gnn_batch_seed(rng_seed, p)."""
+    """int32 [len(levels), N]: for each level l in `levels` and node v, the number of pre-sampled
+    batches with v in V_l (V_0: the seeds); by default levels = [K] (the gathered set V_K) and the
+    result is [N].  Batch p takes seeds[p*batch:(p+1)*batch] and the batch seed
+    gnn_batch_seed(rng_seed, p)."""
     N = graph.num_nodes
     K = len(fanouts)
     dev = seeds.device
-    counts = torch.zeros(N, dtype=torch.int32, device=dev)
+    lv_list = list(levels) if levels is not None else [K]
+    counts = torch.zeros(len(lv_list), N, dtype=torch.int32, device=dev)
     caps = gnn_capacity(batch, fanouts, N)
     blocks = Blocks(caps)
     ws = torch.empty(gnn_workspace_size(caps, N), dtype=torch.uint8, device=dev)
@@ -37,13 +39,14 @@ def presample_counts(graph: DeviceGraph, seeds: torch.Tensor, batch: int, fanout
         st = gnn_read_device_status(ws)
         if st != GNN_OK:
             raise GnnError(st, "pre-sampling")
-        for lv in (levels if levels is not None else [K]):
+        for j, lv in enumerate(lv_list):
             if lv == 0:
                 ids = s
             else:
                 ids = blocks.nodes[lv - 1][:int(blocks.counts[2 * lv - 1].item())]
-            counts.index_add_(0, ids.long(), torch.ones(ids.numel(), dtype=torch.int32, device=dev))
-    return counts
+            counts[j].index_add_(0, ids.long(),
+                                 torch.ones(ids.numel(), dtype=torch.int32, device=dev))
+    return counts if levels is not None else counts[0]
 
 
 def rank_rows(counts: torch.Tensor, degree: torch.Tensor, rows: int,
@@ -76,13 +79,20 @@ def presample_hot_order(graph: DeviceGraph, indptr: torch.Tensor, seeds: torch.T
 
 def presample_adjacency_order(graph: DeviceGraph, indptr: torch.Tensor, seeds: torch.Tensor,
                               batch: int, fanouts: Sequence[int], rng_seed: int) -> torch.Tensor:
-    """Hot order for gnn_adjacency_cache_create.  The sampler reads node v's adjacency row at hop
-    l when v is in the frontier V_{l-1}, so a node counts once per (pre-sampled batch, frontier
-    level 0..K-1) that holds it (GARDEN Sec. IV.B counts accesses along the whole sampling path,
-    eq. (4)); rows with a count are ranked by (count desc, degree asc, id asc): of equally hot
-    rows the short ones first, as they take less of the cache."""
+    """Hot order for gnn_adjacency_cache_create.  At hop l the sampler reads min(deg v, k_l) ids of
+    node v's row when v is in the frontier V_{l-1} (GARDEN Sec. IV.B counts the accesses of the
+    whole sampling path, eq. (4)).  A cached row costs deg v ids of HBM and saves, per pre-sampled
+    batch, sum_l [v in V_{l-1}] * min(deg v, k_l) host reads; rows that save anything are ranked
+    by saved reads per cached id (descending, then id ascending): a hub read k times out of
+    thousands of ids ranks below a short row read whole."""
     K = len(fanouts)
     counts = presample_counts(graph, seeds, batch, fanouts, rng_seed, levels=list(range(K)))
-    degree = indptr[1:] - indptr[:-1]
-    hot = int((counts > 0).sum().item())
-    return rank_rows(counts, degree, hot, degree_desc=False)
+    degree = (indptr[1:] - indptr[:-1]).to(torch.float64)
+    saved = torch.zeros_like(degree)
+    for l in range(K):
+        saved += counts[l].to(torch.float64) * degree.clamp(max=fanouts[l])
+    density = saved / degree.clamp(min=1)
+    live = torch.nonzero(saved > 0).flatten()
+    # stable sort of the live ids (ascending) by density, descending: ties keep id order
+    order = torch.sort(density[live], descending=True, stable=True).indices
+    return live[order].to(torch.int32).contiguous()

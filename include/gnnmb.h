@@ -103,8 +103,8 @@ gnn_status gnn_host_mapped_pointer(const void *host, const void **out_device);
 
 /*
  * Adjacency cache (GARDEN Sec. IV.B, the adjacency part of the cache allocator): the rows of the
- * nodes hot_order[0..n_hot) (device, distinct ids, hottest first) copied into HBM, taken in that
- * order while they fit max_entries neighbour ids in all (a row that does not fit is skipped).
+ * nodes hot_order[0..m) (device, distinct ids, hottest first) copied into HBM, m the largest
+ * count whose rows hold at most max_entries neighbour ids in all.
  * The graph's indices may be host-resident.  Setup call: allocates adj_off [N] (int64) and the
  * rows with hipMalloc and synchronises.  *out_rows / *out_entries (may be NULL) receive the
  * numbers of rows and ids cached.
