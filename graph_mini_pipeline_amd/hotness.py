@@ -87,10 +87,18 @@ def presample_adjacency_order(graph: DeviceGraph, indptr: torch.Tensor, seeds: t
     thousands of ids ranks below a short row read whole."""
     K = len(fanouts)
     counts = presample_counts(graph, seeds, batch, fanouts, rng_seed, levels=list(range(K)))
-    degree = (indptr[1:] - indptr[:-1]).to(torch.float64)
+    return rank_adjacency(counts, indptr[1:] - indptr[:-1], fanouts)
+
+
+def rank_adjacency(counts: torch.Tensor, degree: torch.Tensor,
+                   fanouts: Sequence[int]) -> torch.Tensor:
+    """int32: the nodes whose cached rows save host reads, by saved reads per cached id
+    sum_l counts[l, v] * min(deg v, k_{l+1}) / deg v, descending (ties: id ascending).
+    counts: [K, N], counts[l, v] = batches whose frontier V_l holds v; degree: [N]."""
+    degree = degree.to(torch.float64)
     saved = torch.zeros_like(degree)
-    for l in range(K):
-        saved += counts[l].to(torch.float64) * degree.clamp(max=fanouts[l])
+    for l, k in enumerate(fanouts):
+        saved += counts[l].to(torch.float64) * degree.clamp(max=k)
     density = saved / degree.clamp(min=1)
     live = torch.nonzero(saved > 0).flatten()
     # stable sort of the live ids (ascending) by density, descending: ties keep id order

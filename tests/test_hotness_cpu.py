@@ -1,7 +1,7 @@
 """Host logic of the hot-row ranking (count desc, degree desc, id asc); runs on the CPU."""
 import torch
 
-from graph_mini_pipeline_amd.hotness import rank_rows
+from graph_mini_pipeline_amd.hotness import rank_adjacency, rank_rows
 
 
 def test_rank_order_and_ties():
@@ -36,3 +36,18 @@ def test_rank_rows_degree_ascending():
     degree = torch.tensor([9, 7, 3, 1, 7], dtype=torch.int64)
     assert rank_rows(counts, degree, 5, degree_desc=False).tolist() == [2, 1, 4, 0, 3]
     assert rank_rows(counts, degree, 5).tolist() == [1, 4, 2, 0, 3]
+
+
+def test_rank_adjacency_by_saved_reads_per_cached_id():
+    # fanouts [2, 3]; node: degree, frontier counts at levels 0 and 1
+    #   0: deg 100, counts (5, 5): saved 5*2 + 5*3 = 25, per id 0.25
+    #   1: deg 2,   counts (1, 0): saved 2,              per id 1.0
+    #   2: deg 4,   counts (0, 2): saved 6,              per id 1.5
+    #   3: deg 0,   counts (3, 3): saves nothing (an empty row)
+    #   4: deg 3,   counts (0, 0): never a frontier node
+    #   5: deg 6,   counts (2, 1): saved 4 + 3 = 7,      per id 7/6
+    #   6: deg 1,   counts (0, 1): saved 1,              per id 1.0 (ties with node 1: id order)
+    degree = torch.tensor([100, 2, 4, 0, 3, 6, 1])
+    counts = torch.tensor([[5, 1, 0, 3, 0, 2, 0],
+                           [5, 0, 2, 3, 0, 1, 1]], dtype=torch.int32)
+    assert rank_adjacency(counts, degree, [2, 3]).tolist() == [2, 5, 1, 6, 0]
