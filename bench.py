@@ -147,7 +147,7 @@ def main():
                          "pre-sampled hot rows")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the mini-batch path is measured on "
+        print(json.dumps({"error": "the benchmark runs on one GPU: the mini-batch path is measured on "
                                    "one MI355X; --gpus must be 1"}))
         sys.exit(2)
 

@@ -46,7 +46,7 @@ typedef int32_t gnn_status;
 #define GNN_ERR_CAPACITY (-2)     /* an output or workspace buffer is too small */
 #define GNN_ERR_OUT_OF_RANGE (-3) /* a node id outside [0, num_nodes) (device) */
 #define GNN_ERR_HIP (-4)          /* a HIP runtime call failed */
-#define GNN_ERR_UNSUPPORTED (-5)  /* a size or option this build does not handle */
+#define GNN_ERR_UNSUPPORTED (-5)  /* a size or option the library does not handle */
 #define GNN_ERR_INTERNAL (-6)     /* a device-side invariant failed (never expected) */
 
 typedef void *gnn_stream; /* hipStream_t */
