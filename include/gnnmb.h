@@ -4,8 +4,9 @@
  * The path is the per-iteration pipeline that the three source pages share:
  *   GARDEN: Efficient GPU-Accelerated Billion-Scale GNN Training via Caching-Sampling-Batching
  *     Co-Design -- Sec. II.A eq. (1) (mean AGGREGATE over in-neighbours), Sec. II.B with Fig. 1
- *     (layer-wise sampling, one bipartite block per layer), Sec. IV.B (feature cache with pinned
- *     host fallback), Sec. IV.C (grouping-based parallel sampler, full vs random nodes), Sec. IV.D
+ *     (layer-wise sampling, one bipartite block per layer), Sec. IV.B (feature and adjacency
+ *     caches with pinned host fallback), Sec. IV.C (grouping-based parallel sampler, full vs
+ *     random nodes), Sec. IV.D
  *     with Alg. 1 (super-batch degree classifier);
  *   LEO: Enabling Efficient Communication-Computation Pipeline for GNN via Hierarchical Caching --
  *     Sec. 2.2 (sample, extract features, train) and Sec. 2.3 (zero-copy feature reads from pinned
@@ -16,7 +17,8 @@
  * Conventions for every call:
  *  - Pointers are device pointers unless marked "host".  The caller allocates and owns every
  *    input, output and workspace buffer; the library keeps no pointer after a call returns, except
- *    that a feature store borrows its table.  No call allocates device memory on the hot path.
+ *    that a feature store borrows its table (an adjacency cache holds copies of its rows).  No
+ *    call allocates device memory on the hot path (the stores and caches allocate at set-up).
  *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and return without
  *    waiting.  Outputs are valid once the stream has been synchronised.  Data-dependent sizes stay
  *    in device memory ("counts").
