@@ -476,7 +476,8 @@ def main():
             "cache_fraction_of_edges": (c.entries if c else 0) / max(1, graph.indices.numel()),
             "ranking": f"{PRESAMPLE_BATCHES} pre-sampled batches from seeds the measurement does "
                        f"not use; host reads saved per cached id, sum over hops of (batches whose "
-                       f"frontier holds the node) * min(deg, k) / deg, desc" if c else None,
+                       f"frontier holds the node) * min(deg, k) / deg, desc; then the rows not "
+                       f"reached, by out-degree * min(deg, max k) / deg, desc" if c else None,
             "setup_s": adj["setup_s"],
             "hit_rate_rows": adj["rows_hit"] / max(1, adj["rows_read"]),
             "hit_rate_ids": adj["ids_hit"] / max(1, adj["ids_read"]),

@@ -87,14 +87,19 @@ def presample_adjacency_order(graph: DeviceGraph, indptr: torch.Tensor, seeds: t
     thousands of ids ranks below a short row read whole."""
     K = len(fanouts)
     counts = presample_counts(graph, seeds, batch, fanouts, rng_seed, levels=list(range(K)))
-    return rank_adjacency(counts, indptr[1:] - indptr[:-1], fanouts)
+    # rows the pre-sampling never reached follow, by how many rows list the node (the ways it can
+    # be sampled into a frontier)
+    outdeg = torch.bincount(graph.indices, minlength=graph.num_nodes).to(indptr.device)
+    return rank_adjacency(counts, indptr[1:] - indptr[:-1], fanouts, outdeg)
 
 
-def rank_adjacency(counts: torch.Tensor, degree: torch.Tensor,
-                   fanouts: Sequence[int]) -> torch.Tensor:
+def rank_adjacency(counts: torch.Tensor, degree: torch.Tensor, fanouts: Sequence[int],
+                   outdeg: Optional[torch.Tensor] = None) -> torch.Tensor:
     """int32: the nodes whose cached rows save host reads, by saved reads per cached id
     sum_l counts[l, v] * min(deg v, k_{l+1}) / deg v, descending (ties: id ascending).
-    counts: [K, N], counts[l, v] = batches whose frontier V_l holds v; degree: [N]."""
+    counts: [K, N], counts[l, v] = batches whose frontier V_l holds v; degree: [N].  With outdeg
+    ([N], the number of rows listing each node) the other non-empty rows follow by the estimate
+    outdeg v * min(deg v, max k) / deg v, descending (ties: id ascending)."""
     degree = degree.to(torch.float64)
     saved = torch.zeros_like(degree)
     for l, k in enumerate(fanouts):
@@ -102,5 +107,9 @@ def rank_adjacency(counts: torch.Tensor, degree: torch.Tensor,
     density = saved / degree.clamp(min=1)
     live = torch.nonzero(saved > 0).flatten()
     # stable sort of the live ids (ascending) by density, descending: ties keep id order
-    order = torch.sort(density[live], descending=True, stable=True).indices
-    return live[order].to(torch.int32).contiguous()
+    order = live[torch.sort(density[live], descending=True, stable=True).indices]
+    if outdeg is not None:
+        est = outdeg.to(torch.float64) * degree.clamp(max=max(fanouts)) / degree.clamp(min=1)
+        rest = torch.nonzero((saved == 0) & (est > 0)).flatten()
+        order = torch.cat([order, rest[torch.sort(est[rest], descending=True, stable=True).indices]])
+    return order.to(torch.int32).contiguous()

@@ -51,3 +51,12 @@ def test_rank_adjacency_by_saved_reads_per_cached_id():
     counts = torch.tensor([[5, 1, 0, 3, 0, 2, 0],
                            [5, 0, 2, 3, 0, 1, 1]], dtype=torch.int32)
     assert rank_adjacency(counts, degree, [2, 3]).tolist() == [2, 5, 1, 6, 0]
+
+    # with out-degrees, the rows the pre-sampling never reached follow (largest fanout 3): node 4
+    # (deg 3, listed by 5 rows: 5 * 3 / 3) before node 7 (deg 8, listed by 6 rows: 6 * 3 / 8);
+    # node 8 is in no row, node 3's row is empty
+    degree = torch.tensor([100, 2, 4, 0, 3, 6, 1, 8, 2])
+    counts = torch.tensor([[5, 1, 0, 3, 0, 2, 0, 0, 0],
+                           [5, 0, 2, 3, 0, 1, 1, 0, 0]], dtype=torch.int32)
+    outdeg = torch.tensor([1, 1, 1, 1, 5, 1, 1, 6, 0])
+    assert rank_adjacency(counts, degree, [2, 3], outdeg).tolist() == [2, 5, 1, 6, 0, 4, 7]
