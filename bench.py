@@ -49,8 +49,8 @@ def workload_name(cfg) -> str:
 def kernel_instance(kind: str, d: int, ld: int, batched: bool, union: bool = False) -> str:
     """Name of the template instance the library launches for this row shape: both kernels pick
     lanes per row (16, 32 or 64) and, with 64, chunk groups per lane (up to 4) from the 16-byte
-    chunks per row, and keep a ring of rows (gather: 8 with 64 lanes, else 4) or edges (mean: 4)
-    in flight; a gather of rows that are not 16-byte aligned takes the flat per-element kernel.
+    chunks per row, and keep a ring of rows (gather: 8 with 64 lanes, else 4) or edges (mean: 4
+    with one chunk group per lane, 2 with more) in flight; a gather of rows that are not 16-byte aligned takes the flat per-element kernel.
     Batched, one gather launch serves every sub-batch (k_gather_batch); through the union of the
     sub-batches' node sets, the row engine scatters each union row to its sub-batches."""
     cpr = (d + 3) // 4
@@ -63,7 +63,7 @@ def kernel_instance(kind: str, d: int, ld: int, batched: bool, union: bool = Fal
         if union:
             return f"k_gather_rows<{G}, {CH}, {R}, true>"
         return f"{'k_gather_batch' if batched else 'k_gather_rows'}<{G}, {CH}, {R}>"
-    return f"k_mean_v5<{G}, {CH}, 4>"
+    return f"k_mean_v5<{G}, {CH}, {4 if CH == 1 else 2}>"
 
 
 def batched_gather(cfg, layout: str) -> bool:

@@ -259,14 +259,18 @@ static hipError_t launch_mean_impl(const MeanJob *jobs, int njobs, int64_t ld_sr
             continue;
         }
         const dim3 grid(grid_for(items, 4 * (64 / G), 8192));
-        // 4 edges in flight per group (a deeper ring costs occupancy and measured slower)
+        // edges in flight per group: 4 for one-chunk rows (a deeper ring costs occupancy and
+        // measured slower); 2 for wider rows, whose 2-4 chunks per lane already keep several KB
+        // in flight per wavefront (dense 602-float rows: 88 instead of 136 VGPRs, 5 instead of
+        // 3 wavefronts per SIMD, outermost means of a super-batch of 16 0.262 -> 0.249 ms)
         constexpr int R = 4;
+        constexpr int RW = 2;
         if (G == 16) hipLaunchKernelGGL((k_mean_v5<16, 1, R>), grid, dim3(256), 0, s, m);
         else if (G == 32) hipLaunchKernelGGL((k_mean_v5<32, 1, R>), grid, dim3(256), 0, s, m);
         else if (CH == 1) hipLaunchKernelGGL((k_mean_v5<64, 1, R>), grid, dim3(256), 0, s, m);
-        else if (CH == 2) hipLaunchKernelGGL((k_mean_v5<64, 2, R>), grid, dim3(256), 0, s, m);
-        else if (CH == 3) hipLaunchKernelGGL((k_mean_v5<64, 3, R>), grid, dim3(256), 0, s, m);
-        else hipLaunchKernelGGL((k_mean_v5<64, 4, R>), grid, dim3(256), 0, s, m);
+        else if (CH == 2) hipLaunchKernelGGL((k_mean_v5<64, 2, RW>), grid, dim3(256), 0, s, m);
+        else if (CH == 3) hipLaunchKernelGGL((k_mean_v5<64, 3, RW>), grid, dim3(256), 0, s, m);
+        else hipLaunchKernelGGL((k_mean_v5<64, 4, RW>), grid, dim3(256), 0, s, m);
     }
     return hipGetLastError();
 }

@@ -31,7 +31,7 @@ def test_algorithmic_bytes_by_hand():
 
 def test_kernel_instances_follow_row_shape():
     assert bench.kernel_instance("gather", 602, 604, True) == "k_gather_batch<64, 3, 8>"
-    assert bench.kernel_instance("mean", 602, 604, True) == "k_mean_v5<64, 3, 4>"
+    assert bench.kernel_instance("mean", 602, 604, True) == "k_mean_v5<64, 3, 2>"
     assert bench.kernel_instance("gather", 100, 100, True) == "k_gather_batch<32, 1, 4>"
     assert bench.kernel_instance("gather", 64, 64, False) == "k_gather_rows<16, 1, 4>"
     assert bench.kernel_instance("gather", 13, 13, True) == "k_gather<1, 4>"   # unaligned rows
