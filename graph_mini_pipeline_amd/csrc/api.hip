@@ -997,6 +997,10 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         nsg[gi] = ns;
         ob[gi] = &mo.blocks;
     }
+    // A super-batch samples the union of its sub-batches' frontiers into one block whose offsets
+    // are int32 (like every block): its worst case, G times a sub-batch's frontier bound (at most
+    // N) times the fanout, must fit, although each sub-batch's own caps already do.
+    if (group > 1 && max_union_edges(mc, g->num_nodes, group) > kInt32Max) return GNN_ERR_UNSUPPORTED;
     const SuperMode mode = super_mode(mc, g->num_nodes, group, o.flags);
     const Workspace need = carve(mc, g->num_nodes, group, mode, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;

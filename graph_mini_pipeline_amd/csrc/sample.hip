@@ -422,7 +422,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         const uint64_t m = __ballot(sel) & gmask;
         if (sel) {
             const int64_t o = out0 + outc + __popcll(m & below);
-            if (o < a.E_cap) a.blk_gid[o] = row[jc];
+            if (o >= 0 && o < a.E_cap) a.blk_gid[o] = row[jc];
         }
         outc += __popcll(m);
     }
@@ -542,7 +542,7 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
             r += (pt < 0) & ((pt & 0x7FFFFFFF) < jc);
         }
         const int64_t o = out0 + r;
-        if (o < a.E_cap) a.blk_gid[o] = row[jc];
+        if (o >= 0 && o < a.E_cap) a.blk_gid[o] = row[jc];
     }
     __syncthreads();
 }
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int64_t o = a.blk_indptr[i];
         const int32_t *row = adj_row(a, v, st);
         for (int64_t j = 0; j < deg; ++j)
-            if (o + j < a.E_cap) a.blk_gid[o + j] = row[j];
+            if (o + j >= 0 && o + j < a.E_cap) a.blk_gid[o + j] = row[j];
     }
 }
 

@@ -334,7 +334,9 @@ typedef struct gnn_minibatch_out {
  *   outs: host [group]; outs[g].blocks.caps.n_seeds = batch_ptr[g+1] - batch_ptr[g].
  *   ws: ws_bytes >= gnn_workspace_size(caps >= every sub-batch's caps, N, group).
  *   timer: NULL, or a timer that records the stage boundaries of this call (gnn_timer_*).
- * Errors: as gnn_sample_khop and gnn_gather_features.
+ * Errors: as gnn_sample_khop and gnn_gather_features; GNN_ERR_UNSUPPORTED (host, nothing
+ * enqueued) when group > 1 and the super-batch's union block could exceed int32 offsets:
+ * max over hops of min(N, group * caps.frontier[l]) * fanouts[l] > 2^31 - 1.
  */
 typedef struct gnn_timer gnn_timer;
 gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const int32_t *seeds,

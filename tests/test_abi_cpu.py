@@ -211,3 +211,41 @@ def test_header_constants_match_binding():
     assert consts, "no constants found"
     for name, value in consts.items():
         assert getattr(_abi, name) == value, name
+
+
+def test_superbatch_union_block_must_fit_int32():
+    """Each sub-batch's caps fit int32, but the union block of 16 of them would not: the call is
+    rejected on the host (GNN_ERR_UNSUPPORTED) before any device work; 2 sub-batches fit."""
+    L = gm.lib()
+    N = 2**31 - 1
+    fan = [800]
+    fo = (ctypes.c_int32 * 1)(*fan)
+    caps = gm.gnn_capacity(2**20, fan, N)
+    assert caps.edges[0] == 2**20 * 800 < 2**31
+    g = _abi.gnn_graph()
+    g.num_nodes, g.num_edges, g.indptr, g.indptr_bytes, g.indices = N, 5, 8, 8, 8
+    fs = ctypes.c_void_p()
+    # a store over a (never read) device table: no cache, so creation touches no device
+    assert L.gnn_feature_store_create(8, 0, N, 1, 1, 0, None, ctypes.byref(fs)) == gm.GNN_OK
+
+    def outs(G):
+        arr = (_abi.gnn_minibatch_out * G)()
+        for m in arr:
+            m.blocks.caps = caps
+            m.blocks.counts = 8
+            h = m.blocks.hop[0]
+            h.indptr = h.gid = h.lid = h.dst_lid = h.nodes = 8
+            m.x = 8
+            m.h[0] = 8
+            m.ld_h = 1     # d = 1: rows * d stays within the flat index bound
+        return arr
+
+    try:
+        for G, want in ((16, gm.GNN_ERR_UNSUPPORTED), (2, gm.GNN_ERR_CAPACITY)):
+            ptr = (ctypes.c_int64 * (G + 1))(*[i * 2**20 for i in range(G + 1)])
+            # with a workspace of 16 bytes: the fitting super-batch stops at the workspace check
+            st = L.gnn_minibatch(ctypes.byref(g), fs, 8, ptr, G, fo, 1, 0, outs(G), 8, 16, None,
+                                 None, None)
+            assert st == want, (G, st)
+    finally:
+        L.gnn_feature_store_destroy(fs)
