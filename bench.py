@@ -30,7 +30,7 @@ HBM_PEAK_GBPS = 8000.0
 # adds, four 32-bit compares and five of loop bookkeeping).
 ALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
 VALU_PER_KEY = 19.0
-KEYS_PEAK = ALU_LANE_OPS / VALU_PER_KEY
+KEYS_PEAK_MODEL = ALU_LANE_OPS / VALU_PER_KEY
 PRESAMPLE_BATCHES = 64     # batches pre-sampled to rank the hot-row cache (disjoint seeds)
 
 
@@ -119,7 +119,9 @@ def main():
                          "workload's own where its definition fixes one (mid: 8), else "
                          f"{DEFAULT_GROUP}")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="dense")
+    ap.add_argument("--config", default="large",
+                    help="workload (synth.CONFIGS); default: the largest that fits one GPU's HBM, "
+                         "111M nodes / 1.6B edges / 128-d")
     ap.add_argument("--streams", type=int, default=1,
                     help="streams of the single-stream regions (the stage and kernel timings)")
     ap.add_argument("--pipeline-streams", type=int, default=3,
@@ -134,6 +136,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-g1", action="store_true",
+                    help="skip the region that times the same mini-batches one per call (G = 1)")
     ap.add_argument("--fanouts", default="",
                     help="comma-separated fanouts replacing the workload's (fanouts[0] at hop 1), "
                          "e.g. 5,10,15 for GARDEN's fanout-pattern sweep")
@@ -317,6 +321,57 @@ def main():
     head_wall = wall_p if wall_p is not None else wall
     head_streams = P if wall_p is not None else S
 
+    # Region 4: the same mini-batches, one per call (G = 1), issued round robin on the headline's
+    # streams with workspaces and outputs of their own: what the super-batch adds over plain
+    # mini-batches.  Each mini-batch takes the batch seed of its global index.
+    g1 = None
+    if G > 1 and not args.no_g1:
+        mbs = []
+        for st in range(steps):
+            e, sb = divmod(st, n_super)
+            od = orders[e % len(orders)]
+            for b in batch_range(sb):
+                lo, hi = b * cfg.batch, min(od.numel(), (b + 1) * cfg.batch)
+                mbs.append((od[lo:hi], gm.gnn_batch_seed(cfg.rng_seed, st * G + b - sb * G)))
+        Q = max(1, P)
+        qs = streams[S:S + P] if P else [streams[0]]
+        ws1 = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, 1), dtype=torch.uint8,
+                           device=dev) for _ in range(Q)]
+        outs1 = [{} for _ in range(Q)]
+
+        def step1(i):
+            sd, seed = mbs[i]
+            q = i % Q
+            n = sd.numel()
+            if n not in outs1[q]:
+                outs1[q][n] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
+                                              cfg.d, cfg.ld)
+            gm.gnn_minibatch(dg, fs, sd, [0, n], cfg.fanouts, seed, [outs1[q][n]], ws1[q],
+                             gm.Options(gather=args.gather), stream=qs[q])
+            return outs1[q][n]
+
+        for i in range(min(len(mbs), 2 * Q)):
+            step1(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(len(mbs)):
+            step1(i)
+        torch.cuda.synchronize()
+        wall1 = time.perf_counter() - t0
+        assert all(gm.gnn_read_device_status(w) == gm.GNN_OK for w in ws1)
+        edges1 = 0
+        for i in range(len(mbs)):     # untimed: the sampled edges of each mini-batch
+            o = step1(i)
+            torch.cuda.synchronize()
+            cnt = o.blocks.counts.cpu().tolist()
+            edges1 += sum(cnt[2 * l] for l in range(K))
+        g1 = {"value": edges1 / wall1, "unit": "sampled edges/s", "streams": Q,
+              "minibatches": len(mbs), "ms_per_minibatch": wall1 / len(mbs) * 1e3,
+              "note": "the same mini-batches, one per gnn_minibatch call (no super-batch), each "
+                      "with the batch seed of its global index, round robin on the headline's "
+                      "streams"}
+        progress(f"G = 1 region: {len(mbs)} mini-batches in {wall1:.3f} s")
+
     # Sizes of each timed batch: sampling is a pure function of the batch, so an untimed re-run
     # of the sampling gives the counts.
     tot_edges = 0
@@ -374,6 +429,8 @@ def main():
     mean_outer = np.array([m[K - 1] for m in mean_bytes], dtype=np.float64)
     mean_all = np.array([sum(m) for m in mean_bytes], dtype=np.float64)
 
+    keys_peak = hash_ceiling(gm, dev)
+    progress(f"hash ceiling: {keys_peak / 1e12:.2f}e12 keys/s")
     n_minibatches = sum(len(batch_range(b % n_super)) for b in range(steps))
     batched = batched_gather(cfg, args.gather)
     launches = 1 if batched else G      # gather (and outermost-mean) launches per step
@@ -443,15 +500,20 @@ def main():
                      "algorithmic_bytes_per_launch": alg_per_launch[dom],
                      "avg_launch_ms": avg_ms, "launches_per_step": launches},
         "sampler": {"bound": "alu", "kernel": "k_sample", "achieved": keys / t_hash,
-                    "peak": KEYS_PEAK, "unit": "keys/s", "frac": keys / t_hash / KEYS_PEAK,
+                    "peak": keys_peak, "unit": "keys/s", "frac": keys / t_hash / keys_peak,
                     "keys_per_step": keys / steps, "ms_per_step": t_hash / steps * 1e3,
-                    "peak_derivation": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz / 19 VALU "
-                                       "instructions per key"},
+                    "peak_source": "measured in this run: gnn_hash_probe (the key hashing alone, "
+                                   "every lane of a full grid), best of 3 launches",
+                    "peak_model": KEYS_PEAK_MODEL,
+                    "frac_of_model": keys / t_hash / KEYS_PEAK_MODEL,
+                    "peak_model_derivation": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz / 19 VALU "
+                                             "instructions per key of the candidate loop"},
         "other_kernel": {"name": stage_kernels[other], "achieved_GBps": kern[other][0],
                          "avg_launch_ms": kern[other][1], "launches_per_step": launches,
                          "algorithmic_bytes_per_launch": alg_per_launch[other],
                          "traffic": traffic[other]["bytes"] if traffic[other] else None},
         "ms_per_step_with_stage_events": wall_events / steps * 1e3,
+        "stage_ms_percentiles": percentiles(stages),
         "single_stream": {"streams": S, "value": tot_edges / wall, "unit": "sampled edges/s",
                           "ms_per_step": wall / steps * 1e3,
                           "ms_per_minibatch": wall / n_minibatches * 1e3,
@@ -467,6 +529,8 @@ def main():
     gm.gnn_copy_probe(probe_src, probe_dst)
     torch.cuda.synchronize()
     result["copy_probe_bytes"] = probe_src.numel() * 4
+    if g1 is not None:
+        result["g1"] = g1
     if adj is not None:
         c = adj["cache"]
         result["config"]["neighbour_ids"] = "pinned host memory, read in place"
@@ -513,6 +577,22 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, graph, table, step, args.cpu_seconds,
                                               tot_edges / head_wall)
     print(json.dumps(result), flush=True)
+
+
+STAGE_NAMES = ("sample_relabel", "gather", "mean_outer_block", "mean_other_blocks",
+               "sampling_kernel_only")
+
+
+def percentiles(stages):
+    """Median, p10 and p90 over the timed steps of each stage and of the whole step (HIP events at
+    the stage boundaries, one stream), in ms per step."""
+    import numpy as np
+    out = {}
+    total = stages[:, :4].sum(axis=1)
+    for name, col in list(zip(STAGE_NAMES, stages.T)) + [("step", total)]:
+        p10, p50, p90 = np.percentile(col, [10, 50, 90])
+        out[name] = {"p10": float(p10), "median": float(p50), "p90": float(p90)}
+    return out
 
 
 SAGE_D_OUT = 128            # GraphSAGE hidden width of GARDEN Sec. VI.A
@@ -586,6 +666,25 @@ def sage_layer(gm, cfg, dg, fs, order, dev, reps=20):
                       f"UPDATE alone, on the library's stream"}
 
 
+def hash_ceiling(gm, dev, reps=3):
+    """Keys per second of the sampler's key hashing alone (gnn_hash_probe: SplitMix64 finalisers
+    of a stepped counter on every lane of 4096 workgroups of 256), best of `reps` launches timed
+    with HIP events on the current stream."""
+    import torch
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+    lanes, per_lane = 4096 * 256, 4096
+    gm.gnn_hash_probe(1, 1 << 60, lanes, per_lane, cnt)     # warm-up
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gm.gnn_hash_probe(2, 1 << 60, lanes, per_lane, cnt)
+        e1.record()
+        e1.synchronize()
+        best = max(best, lanes * per_lane / (e0.elapsed_time(e1) / 1e3))
+    return best
+
+
 def host_link(gm, table, dev):
     """Host -> device bandwidth: the best of 5 hipMemcpyAsync copies of 1 GiB from pinned host
     memory (B_link), and the best of 5 zero-copy streaming reads of the same bytes by a kernel."""
@@ -614,9 +713,32 @@ def host_link(gm, table, dev):
     return {"B_link_GBps": best_copy, "zero_copy_read_GBps": best_zc}
 
 
+def cpu_info():
+    """The host's CPU model (lscpu, else /proc/cpuinfo) and its logical CPU count."""
+    import platform
+    import subprocess
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None and os.path.exists("/proc/cpuinfo"):
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    return {"cpu_model": model or platform.processor() or "unknown", "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
 def cpu_baseline(cfg, graph, table, step, budget_s, gpu_value):
     """The oracle (single-threaded C) on the first super-batches of the same epoch, until budget_s
-    of CPU work has been spent; checks its results against the GPU path's on those batches."""
+    of CPU work has been spent; checks its results against the GPU path's on those batches: every
+    block array and X bit for bit, every h within 1e-5 * max|X|."""
     import numpy as np
     import torch
 
@@ -627,6 +749,7 @@ def cpu_baseline(cfg, graph, table, step, budget_s, gpu_value):
     x = table.cpu().numpy()
     K = len(cfg.fanouts)
     spent, edges, batches, parity, st = 0.0, 0, 0, True, 0
+    mismatch = []
     while spent < budget_s and batches < 64:
         s, mine, sb_seeds = step(st)
         torch.cuda.synchronize()
@@ -646,18 +769,36 @@ def cpu_baseline(cfg, graph, table, step, budget_s, gpu_value):
             batches += 1
             host = got.blocks.host()
             for l in range(K):
-                parity &= bool(np.array_equal(host[l][1], ref.blocks[l].gid)
-                               and np.array_equal(host[l][4], ref.blocks[l].nodes))
+                rb = ref.blocks[l]
+                for name, g_arr, r_arr in (("indptr", host[l][0], rb.indptr),
+                                           ("gid", host[l][1], rb.gid), ("lid", host[l][2], rb.lid),
+                                           ("dst_lid", host[l][3], rb.dst_lid),
+                                           ("nodes", host[l][4], rb.nodes)):
+                    if not np.array_equal(g_arr, r_arr):
+                        mismatch.append(f"batch {b} hop {l + 1} {name}")
             nv = len(ref.blocks[-1].nodes)
-            parity &= bool(np.array_equal(got.x[:nv, :cfg.d].cpu().numpy(), ref.x))
-            err = float(np.abs(got.h[0][:n, :cfg.d].cpu().numpy() - ref.h[0]).max())
-            parity &= err <= 1e-5 * float(np.abs(ref.x).max())
+            xg = np.ascontiguousarray(got.x[:nv, :cfg.d].cpu().numpy())
+            if not np.array_equal(xg.view(np.uint32), ref.x.view(np.uint32)):
+                mismatch.append(f"batch {b} X")
+            tol = 1e-5 * float(np.abs(ref.x).max()) if ref.x.size else 0.0
+            for l in range(K):
+                rows = ref.h[l].shape[0]
+                if rows == 0:
+                    continue
+                err = float(np.abs(got.h[l][:rows, :cfg.d].cpu().numpy().astype(np.float64)
+                                   - ref.h[l]).max())
+                if err > tol:
+                    mismatch.append(f"batch {b} h_{l} err {err:.3g} > {tol:.3g}")
+    parity = not mismatch
     value = edges / spent
-    return {"value": value, "unit": "sampled edges/s", "cores": 1, "kind": "oracle",
-            "sample": f"the first {batches} mini-batches of the epoch (same seeds and batch seed as "
-                      f"the GPU run), whole path: sampling, relabel, gather, mean; "
-                      f"{spent:.1f} s single-threaded",
-            "gpu_over_cpu": gpu_value / value, "parity_on_sample": parity}
+    return dict({"value": value, "unit": "sampled edges/s", "cores": 1, "kind": "oracle",
+                 "sample": f"the first {batches} mini-batches of the epoch (same seeds and batch "
+                           f"seed as the GPU run), whole path: sampling, relabel, gather, mean; "
+                           f"{spent:.1f} s single-threaded",
+                 "gpu_over_cpu": gpu_value / value, "parity_on_sample": parity,
+                 "parity_checked": "every block array (indptr, gid, lid, dst_lid, V_l) and X bit "
+                                   "for bit, every h_l within 1e-5 * max|X|",
+                 "parity_mismatches": mismatch[:10]}, **cpu_info())
 
 
 if __name__ == "__main__":

@@ -65,3 +65,62 @@ def compare_with_oracle(out: gm.MinibatchOut, ref: oracle.MiniBatch, d: int, tol
         h = out.h[l][:rows, :d].cpu().numpy()
         err = float(np.abs(h.astype(np.float64) - ref.h[l]).max()) if rows else 0.0
         assert err <= tol, f"h_{l}: max err {err} > {tol}"
+
+
+def oracle_pool(indptr, indices, x, d, jobs, threads=None):
+    """Oracle results of many batches, computed concurrently on host threads (the oracle's C
+    calls release the interpreter lock; no process is forked from this GPU process).
+    jobs: iterable of (key, seeds, fanouts, seed64).  Returns (executor, {key: future})."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    oracle.lib()      # load once, before the threads start
+    n = threads or max(1, min(16, os.cpu_count() or 1))
+    ex = ThreadPoolExecutor(max_workers=n)
+    futs = {key: ex.submit(oracle.minibatch, indptr, indices, x, np.ascontiguousarray(seeds),
+                           list(fanouts), seed64, d=d)
+            for key, seeds, fanouts, seed64 in jobs}
+    return ex, futs
+
+
+def headline_layout(cfg, dg, fs, order, steps, G, P=3, rounds=1, opts=None):
+    """Super-batches issued the way the benchmark's headline issues them: step st (super-batch st
+    of the seed order `order`, batch seed gnn_batch_seed(rng_seed, st)) goes to stream i % P of a
+    window of P * rounds steps, each stream with a workspace of its own, and each (stream, round)
+    with output sets of its own, so `rounds` steps run back to back on every stream while the
+    other streams run theirs; the host synchronises once per window.  Output sets are reused by
+    the next window.  Yields (st, b, seed64, out) for every sub-batch b of every step."""
+    import math
+    caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
+    streams = [torch.cuda.Stream() for _ in range(P)]
+    wss = [torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8,
+                       device="cuda") for _ in range(P)]
+    n_batches = math.ceil(order.numel() / cfg.batch)
+    sets = {}
+    steps = list(steps)
+    window = P * rounds
+    for w0 in range(0, len(steps), window):
+        issued = []
+        for i, st in enumerate(steps[w0:w0 + window]):
+            q, r = i % P, i // P
+            bs = list(range(st * G, min(st * G + G, n_batches)))
+            lo = bs[0] * cfg.batch
+            hi = min(order.numel(), (bs[-1] + 1) * cfg.batch)
+            ptr = [b * cfg.batch - lo for b in bs] + [hi - lo]
+            outs = []
+            for j in range(len(bs)):
+                n = ptr[j + 1] - ptr[j]
+                key = (q, r, j, n)
+                if key not in sets:
+                    sets[key] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
+                                                cfg.d, cfg.ld)
+                outs.append(sets[key])
+            seed64 = gm.gnn_batch_seed(cfg.rng_seed, st)
+            gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, seed64, outs, wss[q], opts,
+                             stream=streams[q])
+            issued.append((st, bs, seed64, outs))
+        torch.cuda.synchronize()
+        for w in wss:
+            assert gm.gnn_read_device_status(w) == gm.GNN_OK
+        for st, bs, seed64, outs in issued:
+            for b, out in zip(bs, outs):
+                yield st, b, seed64, out

@@ -164,3 +164,46 @@ def test_large_single_batch(large):
     seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
     ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
     compare_with_oracle(outs[0], ref, cfg.d)
+
+
+def _headline_parity(workload, steps, G, rounds, label):
+    """Sub-batches of `steps` issued in the benchmark's headline layout (three streams, each with
+    its own workspace and outputs, super-batches of G) against the oracle, which runs on host
+    threads while the GPU works; every block array and X bit for bit, every h within tolerance."""
+    import sys
+    from tests.gpu_util import headline_layout, oracle_pool
+    cfg, g, table, order, (indptr, indices, x, order_h) = workload
+    dg = gm.DeviceGraph(cfg.num_nodes, g.indptr, g.indices)
+    fs = gm.gnn_feature_store_create(table, cfg.d)
+    n_batches = (len(order_h) + cfg.batch - 1) // cfg.batch
+    bs = [b for st in steps for b in range(st * G, min(st * G + G, n_batches))]
+    jobs = [(b, order_h[b * cfg.batch:(b + 1) * cfg.batch], cfg.fanouts,
+             gm.gnn_batch_seed(cfg.rng_seed, b // G)) for b in bs]
+    ex, futs = oracle_pool(indptr, indices, x, cfg.d, jobs)
+    seen = []
+    try:
+        for st, b, seed64, out in headline_layout(cfg, dg, fs, order, steps, G, rounds=rounds):
+            compare_with_oracle(out, futs.pop(b).result(), cfg.d)
+            seen.append(b)
+            if len(seen) % 16 == 0:
+                print(f"[{label}] {len(seen)}/{len(bs)} sub-batches equal the oracle",
+                      file=sys.stderr, flush=True)
+    finally:
+        ex.shutdown(cancel_futures=True)
+        torch.cuda.empty_cache()
+    assert sorted(seen) == sorted(bs)
+
+
+@pytest.mark.timeout(1200)
+def test_dense_full_epoch_in_headline_layout(dense):
+    """All 147 batches of the epoch (146 of 1024 seeds and one of 496): ten super-batches of 16
+    on three streams, two per stream in flight before the host synchronises (GARDEN Sec. IV.D:
+    each mini-batch keeps its own logical result inside a super-batch)."""
+    _headline_parity(dense, range(10), 16, 2, "dense epoch")
+
+
+@pytest.mark.timeout(1200)
+def test_large_three_streams_in_headline_layout(large):
+    """Three super-batches of 16 (48 mini-batches) at once on three streams, as the headline runs
+    them on the 111M-node graph; every sub-batch against the oracle."""
+    _headline_parity(large, range(3), 16, 1, "large")

@@ -46,6 +46,34 @@ def test_tiny_pipeline_matches_oracle(tiny, batch):
     compare_with_oracle(outs[0], ref, cfg.d)
 
 
+@pytest.mark.parametrize("G,rounds", [(16, 2), (1, 3)])
+def test_tiny_every_batch_in_headline_layout(tiny, G, rounds):
+    """All 40 batches of the workload, issued as the benchmark's headline issues them (super-batches
+    of G on three streams, each with its own workspace and outputs, several in flight at once);
+    every sub-batch equals the oracle's separate run with its super-batch's seed (GARDEN Sec.
+    IV.D: each mini-batch keeps its own logical result inside a super-batch)."""
+    from tests.gpu_util import headline_layout, oracle_pool
+    cfg, indptr, indices, x, order = tiny
+    n_batches = (len(order) + cfg.batch - 1) // cfg.batch
+    assert n_batches == 40
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    order_d = torch.from_numpy(order).cuda()
+    n_super = (n_batches + G - 1) // G
+    jobs = [(b, order[b * cfg.batch:(b + 1) * cfg.batch], cfg.fanouts,
+             gm.gnn_batch_seed(cfg.rng_seed, b // G)) for b in range(n_batches)]
+    ex, futs = oracle_pool(indptr, indices, x, cfg.d, jobs)
+    seen = []
+    try:
+        for st, b, seed64, out in headline_layout(cfg, dg, fs, order_d, range(n_super), G,
+                                                  rounds=rounds):
+            compare_with_oracle(out, futs[b].result(), cfg.d)
+            seen.append(b)
+    finally:
+        ex.shutdown(cancel_futures=True)
+    assert sorted(seen) == list(range(n_batches))
+
+
 @pytest.mark.parametrize("fanouts", [[5, 10], [5, 10, 15], [5, 5, 10, 10]])
 @pytest.mark.parametrize("mode", ["full", "compact"])
 def test_fanout_patterns(tiny, fanouts, mode):
