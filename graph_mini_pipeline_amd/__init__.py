@@ -17,6 +17,7 @@ from . import _abi
 from ._abi import (GNN_ERR_CAPACITY, GNN_ERR_HIP, GNN_ERR_INTERNAL, GNN_ERR_INVALID_ARG,  # noqa
                    GNN_ERR_OUT_OF_RANGE, GNN_ERR_UNSUPPORTED, GNN_MAX_HOPS, GNN_OK, GNN_SYNC,
                    GNN_SUPERBATCH_COMPACT, GNN_SUPERBATCH_FULL, GNN_GATHER_BATCHED,
+                   GNN_NOALLOC_MAX_IDS, GNN_NOALLOC_SCRATCH_BYTES,
                    GNN_GATHER_INTERLEAVED,
                    GNN_TIMER_STAGES)
 
@@ -25,7 +26,7 @@ __all__ = [
     "gnn_status_string", "gnn_batch_seed", "gnn_capacity", "gnn_workspace_size", "gnn_sample_khop",
     "gnn_unique_relabel", "gnn_relabel_workspace_size", "gnn_feature_store_create",
     "gnn_feature_store_destroy", "gnn_gather_features", "gnn_mean_aggregate", "gnn_sage_layer",
-    "gnn_sage_update", "gnn_minibatch", "AdjacencyCache", "gnn_adjacency_cache_create",
+    "gnn_sage_update", "gnn_minibatch", "gnn_unique_relabel_noalloc", "AdjacencyCache", "gnn_adjacency_cache_create",
     "gnn_host_mapped_pointer",
     "gnn_read_device_status", "gnn_timer_create", "gnn_timer_destroy", "gnn_timer_reset",
     "gnn_timer_elapsed", "gnn_copy_probe", "gnn_copy_probe_host", "gnn_hash_probe", "lib",
@@ -270,6 +271,27 @@ def gnn_unique_relabel(keep: torch.Tensor, add: torch.Tensor, id_bound: int, uni
                                   _ptr(keep_lid), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream))
     _ok(st, "gnn_unique_relabel")
+
+
+def gnn_unique_relabel_noalloc(keep: torch.Tensor, add: torch.Tensor, id_bound: int,
+                               uniq: torch.Tensor, d_n_uniq: torch.Tensor, add_lid: torch.Tensor,
+                               keep_lid: torch.Tensor, d_status: Optional[torch.Tensor] = None,
+                               d_n_add: Optional[torch.Tensor] = None, stream=None) -> None:
+    """gnn_unique_relabel on the library's fixed per-GPU scratch (no workspace, no allocation;
+    id_bound <= GNN_NOALLOC_MAX_IDS; calls that overlap on one GPU race)."""
+    for t, n in ((keep, "keep"), (add, "add"), (uniq, "uniq"), (add_lid, "add_lid"),
+                 (keep_lid, "keep_lid")):
+        _need(t, torch.int32, n)
+    _need(d_n_uniq, torch.int64, "d_n_uniq")
+    if d_status is not None:
+        _need(d_status, torch.int32, "d_status")
+    if add_lid.numel() < add.numel() or keep_lid.numel() < keep.numel():
+        raise ValueError("add_lid / keep_lid shorter than add / keep")
+    st = lib().gnn_unique_relabel_noalloc(_ptr(keep), keep.numel(), _ptr(add), _ptr(d_n_add),
+                                          add.numel(), id_bound, _ptr(uniq), uniq.numel(),
+                                          _ptr(d_n_uniq), _ptr(add_lid), _ptr(keep_lid),
+                                          _ptr(d_status), _stream(stream))
+    _ok(st, "gnn_unique_relabel_noalloc")
 
 
 class FeatureStore:

@@ -18,6 +18,8 @@ GNN_SUPERBATCH_FULL = 2
 GNN_SUPERBATCH_COMPACT = 4
 GNN_GATHER_INTERLEAVED = 8
 GNN_GATHER_BATCHED = 16
+GNN_NOALLOC_MAX_IDS = 1 << 26
+GNN_NOALLOC_SCRATCH_BYTES = (16 << 20) + (64 << 10)
 
 GNN_OK = 0
 GNN_ERR_INVALID_ARG = -1
@@ -71,6 +73,7 @@ SIGNATURES = {
                               P(gnn_options), vp]),
     "gnn_unique_relabel": (i32, [vp, i64, vp, vp, i64, i64, vp, i64, vp, vp, vp, vp, size_t, vp]),
     "gnn_relabel_workspace_size": (i32, [i64, P(size_t)]),
+    "gnn_unique_relabel_noalloc": (i32, [vp, i64, vp, vp, i64, i64, vp, i64, vp, vp, vp, vp, vp]),
     "gnn_feature_store_create": (i32, [vp, i32, i64, i64, i64, i64, vp, P(vp)]),
     "gnn_feature_store_destroy": (i32, [vp]),
     "gnn_host_mapped_pointer": (i32, [vp, P(vp)]),

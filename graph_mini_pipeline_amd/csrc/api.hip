@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -590,6 +591,74 @@ const int32_t *union_prepare(const gnn_graph &g, const gnn_minibatch_out *outs, 
     return w.uK;
 }
 
+gnn_status check_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t *add,
+                                int64_t n_add, int64_t id_bound, const int32_t *uniq,
+                                int64_t cap_uniq, const int64_t *d_n_uniq, const int32_t *add_lid,
+                                const int32_t *keep_lid) {
+    if (n_keep < 0 || n_add < 0 || cap_uniq < 0 || id_bound < 1 || id_bound > kInt32Max + 1)
+        return GNN_ERR_INVALID_ARG;
+    if ((n_keep > 0 && (!keep || !keep_lid)) || (n_add > 0 && (!add || !add_lid)))
+        return GNN_ERR_INVALID_ARG;
+    if (!d_n_uniq || (cap_uniq > 0 && !uniq)) return GNN_ERR_INVALID_ARG;
+    if (n_keep > kInt32Max || n_add > kInt32Max) return GNN_ERR_UNSUPPORTED;
+    return GNN_OK;
+}
+
+// The relabel of two lists in a carved workspace; device errors go to `status` (cleared first).
+gnn_status unique_relabel_in(const Workspace &w, int32_t *status, const int32_t *keep,
+                             int64_t n_keep, const int32_t *add, const int64_t *d_n_add,
+                             int64_t n_add, int64_t id_bound, int32_t *uniq, int64_t cap_uniq,
+                             int64_t *d_n_uniq, int32_t *add_lid, int32_t *keep_lid,
+                             hipStream_t s) {
+    if (status) GNN_TRY_HIP(launch_fill_i32(status, 1, 0, s));
+    RelabelArgs r{};
+    r.nlist = 2;
+    r.list[0] = IdList{keep, nullptr, n_keep, keep_lid, 0, 0};
+    r.list[1] = IdList{add, d_n_add, n_add, add_lid, 0, 0};
+    r.nbm = 1;
+    r.out[0] = BitmapOut{uniq, cap_uniq, d_n_uniq, nullptr};
+    r.id_bound = id_bound;
+    r.bitmap = w.bitmaps;
+    r.wprefix = w.wprefix;
+    r.bsum = w.bsum_w;
+    r.W = w.W;
+    r.nbw = static_cast<int32_t>(w.nbw);
+    r.status = status;
+    r.bitmap_cleared = 0;
+    GNN_TRY_HIP(launch_relabel(r, s));
+    return GNN_OK;
+}
+
+// Scratch of gnn_unique_relabel_noalloc: one array per GPU for the life of the process, shared
+// by every call on that GPU (calls that overlap on one GPU race).  Host code never passes the
+// array's name to a kernel: its device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and kept here.
+static __device__ __align__(256) unsigned char scratch[GNN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of stream s (the current device for the null stream).
+gnn_status scratch_address(hipStream_t s, void **out) {
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return GNN_ERR_HIP;
+    dev = cur;
+    if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) return GNN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GNN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return GNN_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return GNN_ERR_HIP;
+        if (e != hipSuccess || p == nullptr) return GNN_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GNN_OK;
+}
+
 gnn_status finish(const Opts &o, const Workspace &w, hipStream_t s) {
     if (!(o.flags & GNN_SYNC)) return GNN_OK;
     int32_t st = 0;
@@ -692,34 +761,36 @@ gnn_status gnn_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t
                               int32_t *uniq, int64_t cap_uniq, int64_t *d_n_uniq,
                               int32_t *add_lid, int32_t *keep_lid, void *ws, size_t ws_bytes,
                               gnn_stream stream) {
-    if (n_keep < 0 || n_add < 0 || cap_uniq < 0 || id_bound < 1 || id_bound > kInt32Max + 1)
-        return GNN_ERR_INVALID_ARG;
-    if ((n_keep > 0 && (!keep || !keep_lid)) || (n_add > 0 && (!add || !add_lid)))
-        return GNN_ERR_INVALID_ARG;
-    if (!d_n_uniq || (cap_uniq > 0 && !uniq) || !ws) return GNN_ERR_INVALID_ARG;
-    if (n_keep > kInt32Max || n_add > kInt32Max) return GNN_ERR_UNSUPPORTED;
+    gnn_status st = check_unique_relabel(keep, n_keep, add, n_add, id_bound, uniq, cap_uniq,
+                                         d_n_uniq, add_lid, keep_lid);
+    if (st != GNN_OK) return st;
+    if (!ws) return GNN_ERR_INVALID_ARG;
     gnn_caps none{};
     const Workspace need = carve(none, id_bound, 1, kSuperNone, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
     const Workspace w = carve(none, id_bound, 1, kSuperNone, ws);
+    return unique_relabel_in(w, w.status, keep, n_keep, add, d_n_add, n_add, id_bound, uniq,
+                             cap_uniq, d_n_uniq, add_lid, keep_lid, static_cast<hipStream_t>(stream));
+}
+
+gnn_status gnn_unique_relabel_noalloc(const int32_t *keep, int64_t n_keep, const int32_t *add,
+                                      const int64_t *d_n_add, int64_t n_add, int64_t id_bound,
+                                      int32_t *uniq, int64_t cap_uniq, int64_t *d_n_uniq,
+                                      int32_t *add_lid, int32_t *keep_lid, int32_t *d_status,
+                                      gnn_stream stream) {
+    gnn_status st = check_unique_relabel(keep, n_keep, add, n_add, id_bound, uniq, cap_uniq,
+                                         d_n_uniq, add_lid, keep_lid);
+    if (st != GNN_OK) return st;
+    if (id_bound > GNN_NOALLOC_MAX_IDS) return GNN_ERR_UNSUPPORTED;
+    gnn_caps none{};
+    const Workspace need = carve(none, id_bound, 1, kSuperNone, nullptr);
+    if (need.bytes > sizeof(scratch)) return GNN_ERR_INTERNAL;   // the bound above keeps it in
     hipStream_t s = static_cast<hipStream_t>(stream);
-    GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
-    RelabelArgs r{};
-    r.nlist = 2;
-    r.list[0] = IdList{keep, nullptr, n_keep, keep_lid, 0, 0};
-    r.list[1] = IdList{add, d_n_add, n_add, add_lid, 0, 0};
-    r.nbm = 1;
-    r.out[0] = BitmapOut{uniq, cap_uniq, d_n_uniq, nullptr};
-    r.id_bound = id_bound;
-    r.bitmap = w.bitmaps;
-    r.wprefix = w.wprefix;
-    r.bsum = w.bsum_w;
-    r.W = w.W;
-    r.nbw = static_cast<int32_t>(w.nbw);
-    r.status = w.status;
-    r.bitmap_cleared = 0;
-    GNN_TRY_HIP(launch_relabel(r, s));
-    return GNN_OK;
+    void *base = nullptr;
+    if ((st = scratch_address(s, &base)) != GNN_OK) return st;
+    const Workspace w = carve(none, id_bound, 1, kSuperNone, base);
+    return unique_relabel_in(w, d_status, keep, n_keep, add, d_n_add, n_add, id_bound, uniq,
+                             cap_uniq, d_n_uniq, add_lid, keep_lid, s);
 }
 
 gnn_status gnn_feature_store_create(const float *table, int32_t table_on_host, int64_t num_nodes,

@@ -225,6 +225,27 @@ gnn_status gnn_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t
 gnn_status gnn_relabel_workspace_size(int64_t id_bound, size_t *out_bytes);
 
 /*
+ * gnn_unique_relabel without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same inputs, outputs, results and device errors as gnn_unique_relabel;
+ * the first device error (or GNN_OK) goes to *d_status (device int32, cleared by the call; may be
+ * NULL, then device errors are dropped).
+ * Scratch: a fixed array of GNN_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, held until
+ * the process ends and shared by every call on that GPU; it keeps the last call's contents, and
+ * the call clears what must start at zero.  Calls that overlap on one GPU (other streams, other
+ * host threads) race on it and must be serialised by the caller.
+ * Host errors: GNN_ERR_UNSUPPORTED when id_bound > GNN_NOALLOC_MAX_IDS (nothing enqueued); the
+ * argument checks of gnn_unique_relabel otherwise.
+ */
+#define GNN_NOALLOC_MAX_IDS 67108864          /* 2^26 */
+#define GNN_NOALLOC_SCRATCH_BYTES 16842752    /* 16 MiB + 64 KiB */
+gnn_status gnn_unique_relabel_noalloc(const int32_t *keep, int64_t n_keep, const int32_t *add,
+                                      const int64_t *d_n_add, int64_t n_add, int64_t id_bound,
+                                      int32_t *uniq, int64_t cap_uniq, int64_t *d_n_uniq,
+                                      int32_t *add_lid, int32_t *keep_lid, int32_t *d_status,
+                                      gnn_stream stream);
+
+/*
  * Feature store: the table of node features (fp32, row-major, row stride ld >= d) in HBM, or in
  * pinned host memory read zero-copy (LEO Sec. 2.3; GARDEN Sec. II.B misses served from pinned
  * host memory), optionally with an HBM hot-row cache (GARDEN Sec. IV.B) holding the rows

@@ -249,3 +249,20 @@ def test_superbatch_union_block_must_fit_int32():
             assert st == want, (G, st)
     finally:
         L.gnn_feature_store_destroy(fs)
+
+
+def test_noalloc_relabel_host_checks():
+    """The allocation-free relabel's scratch covers its largest id range, and sizes beyond it are
+    refused on the host before any device work."""
+    need = gm.gnn_relabel_workspace_size(gm.GNN_NOALLOC_MAX_IDS)
+    assert need <= gm.GNN_NOALLOC_SCRATCH_BYTES
+    assert gm.gnn_relabel_workspace_size(2 * gm.GNN_NOALLOC_MAX_IDS) > gm.GNN_NOALLOC_SCRATCH_BYTES
+    L = gm.lib()
+    # id bound above the scratch's maximum
+    assert L.gnn_unique_relabel_noalloc(8, 4, 8, None, 4, gm.GNN_NOALLOC_MAX_IDS + 1, 8, 8, 8, 8,
+                                        8, None, None) == gm.GNN_ERR_UNSUPPORTED
+    # the argument checks of gnn_unique_relabel: missing count output, id bound 0
+    assert L.gnn_unique_relabel_noalloc(8, 4, 8, None, 4, 100, 8, 8, None, 8, 8, None,
+                                        None) == gm.GNN_ERR_INVALID_ARG
+    assert L.gnn_unique_relabel_noalloc(8, 4, 8, None, 4, 0, 8, 8, 8, 8, 8, None,
+                                        None) == gm.GNN_ERR_INVALID_ARG
