@@ -520,6 +520,7 @@ def main():
                           "note": "the same steps one after another on one stream; the stage and "
                                   "kernel timings come from this layout (with events)"},
         "input_generation_s": t_gen,
+        "system": system_fingerprint(dev),
     }
 
     # Counter calibration: one plain 1 GiB device copy by k_copy_probe (untimed).  Profiling runs
@@ -733,6 +734,23 @@ def cpu_info():
                 break
     return {"cpu_model": model or platform.processor() or "unknown", "nproc": os.cpu_count(),
             "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def system_fingerprint(dev):
+    """The GPU (name, architecture, compute units, memory, LDS per workgroup), the ROCm and
+    PyTorch versions and the host CPU of the run."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            rocm = open(path).read().strip()
+            break
+    return dict({"gpu": p.name, "arch": getattr(p, "gcnArchName", None),
+                 "compute_units": p.multi_processor_count, "hbm_bytes": p.total_memory,
+                 "lds_per_workgroup": getattr(p, "shared_memory_per_block", None),
+                 "rocm": rocm, "torch": torch.__version__, "hip": torch.version.hip},
+                **cpu_info())
 
 
 def cpu_baseline(cfg, graph, table, step, budget_s, gpu_value):

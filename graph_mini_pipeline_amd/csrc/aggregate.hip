@@ -39,8 +39,9 @@ struct MeanArgs {
     int32_t d;
     FastDiv cpr;
     // scatter (one segment): destination r's row goes to row scat[r * scat_g + g] - 1 of
-    // scat_out[g] for every g whose entry is > 0, instead of to the segment's out
+    // scat_out[g] for every g whose bit is set in scat_mask[r], instead of to the segment's out
     const int32_t *scat;
+    const uint32_t *scat_mask;
     int32_t scat_g;
     float *scat_out[kMaxGroup];
 };
@@ -102,8 +103,13 @@ __global__ __launch_bounds__(256) void k_mean_v5(MeanArgs m) {
         int64_t e0 = S.indptr[i], e1 = S.indptr[i + 1];
         // lane g of the group: the destination's row in sub-batch g (+1; 0: absent), loaded here so
         // that it arrives with the local ids instead of after the rows
-        const int32_t mypos =
-            m.scat != nullptr && gl < m.scat_g ? m.scat[static_cast<int64_t>(i) * m.scat_g + gl] : 0;
+        int32_t mypos = 0;
+        if (m.scat != nullptr && gl < m.scat_g) {
+            // both loads in flight together: an entry without its mask bit is stale and unused
+            const uint32_t mk = m.scat_mask[i];
+            const int32_t pv = m.scat[static_cast<int64_t>(i) * m.scat_g + gl];
+            mypos = (mk >> gl) & 1u ? pv : 0;
+        }
         e0 = e0 < 0 ? 0 : (e0 > S.e_cap ? S.e_cap : e0);
         e1 = e1 < e0 ? e0 : (e1 > S.e_cap ? S.e_cap : e1);
         const uint32_t ch0 = p * CH * G + gl;  // this lane's first chunk
@@ -209,7 +215,9 @@ __global__ __launch_bounds__(256) void k_mean_v1(MeanArgs m) {
         if (m.scat == nullptr) {
             S.out[static_cast<int64_t>(row) * m.ld_out + col] = val;
         } else {
+            const uint32_t mk = m.scat_mask[row];
             for (int g = 0; g < m.scat_g; ++g) {
+                if (!((mk >> g) & 1u)) continue;
                 const int32_t pos = m.scat[static_cast<int64_t>(row) * m.scat_g + g];
                 if (pos > 0) m.scat_out[g][static_cast<int64_t>(pos - 1) * m.ld_out + col] = val;
             }
@@ -220,8 +228,9 @@ __global__ __launch_bounds__(256) void k_mean_v1(MeanArgs m) {
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 static hipError_t launch_mean_impl(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out,
-                                   int64_t d, int32_t *status, const int32_t *scat, int scat_g,
-                                   float *const *scat_out, hipStream_t s) {
+                                   int64_t d, int32_t *status, const int32_t *scat,
+                                   const uint32_t *scat_mask, int scat_g, float *const *scat_out,
+                                   hipStream_t s) {
     if (njobs <= 0 || d <= 0) return hipSuccess;
     bool v4 = ld_src % 4 == 0 && ld_out % 4 == 0;
     for (int j = 0; j < njobs; ++j) v4 = v4 && aligned16(jobs[j].src) && aligned16(jobs[j].out);
@@ -237,6 +246,7 @@ static hipError_t launch_mean_impl(const MeanJob *jobs, int njobs, int64_t ld_sr
     for (int j0 = 0; j0 < njobs; j0 += kMaxMeanSegs) {
         MeanArgs m{};
         m.scat = scat;
+        m.scat_mask = scat_mask;
         m.scat_g = scat_g;
         for (int g = 0; g < scat_g; ++g) m.scat_out[g] = scat_out[g];
         m.ld_src = ld_src;
@@ -278,14 +288,14 @@ static hipError_t launch_mean_impl(const MeanJob *jobs, int njobs, int64_t ld_sr
 hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out, int64_t d,
                        int32_t max_c, int32_t *status, hipStream_t s) {
     (void)max_c;
-    return launch_mean_impl(jobs, njobs, ld_src, ld_out, d, status, nullptr, 0, nullptr, s);
+    return launch_mean_impl(jobs, njobs, ld_src, ld_out, d, status, nullptr, nullptr, 0, nullptr, s);
 }
 
-hipError_t launch_mean_scatter(const MeanJob &job, const int32_t *inv, int G, float *const *outs,
-                               int64_t ld_src, int64_t ld_out, int64_t d, int32_t *status,
-                               hipStream_t s) {
-    if (G < 1 || G > kMaxGroup || inv == nullptr) return hipErrorInvalidValue;
-    return launch_mean_impl(&job, 1, ld_src, ld_out, d, status, inv, G, outs, s);
+hipError_t launch_mean_scatter(const MeanJob &job, const int32_t *inv, const uint32_t *inv_mask,
+                               int G, float *const *outs, int64_t ld_src, int64_t ld_out, int64_t d,
+                               int32_t *status, hipStream_t s) {
+    if (G < 1 || G > kMaxGroup || inv == nullptr || inv_mask == nullptr) return hipErrorInvalidValue;
+    return launch_mean_impl(&job, 1, ld_src, ld_out, d, status, inv, inv_mask, G, outs, s);
 }
 
 }  // namespace gnnmb

@@ -1,6 +1,7 @@
 // C ABI of the mini-batch library: argument validation, workspace carving, launch sequencing on
 // one stream with no host synchronisation, the feature store and the stage timer.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -50,6 +51,12 @@ namespace {
         if ((expr) != hipSuccess) return GNN_ERR_HIP;    \
     } while (0)
 
+#define GNN_TRY(expr)                                    \
+    do {                                                 \
+        const gnn_status st_ = (expr);                   \
+        if (st_ != GNN_OK) return st_;                   \
+    } while (0)
+
 constexpr int64_t kInt32Max = 2147483647LL;
 // Flattened (row, element) index spaces of the gather and mean kernels stay below 2^31 so that a
 // grid-stride step never wraps a 32-bit index.
@@ -70,30 +77,27 @@ struct Carver {
 
 struct Workspace {
     int32_t *status;       // [1] at offset 0
-    uint32_t *totals;      // [kCols] classification totals
+    uint32_t *totals;      // [kTotalsStride * GNN_MAX_HOPS] classification totals of each hop
     int64_t *d_U;          // [K + 1] |U_l| of a super-batch
     int64_t *d_uE;         // [K] edges of each union block
-    int32_t *packed;       // [FU_max]
-    int32_t *lists;        // [4 FU_max]
-    uint32_t *bsum;        // [kCols nb_max]
+    int32_t *lists;        // [kCats FU_max]
     uint32_t *bitmaps;     // [W] over all node ids, then G more of W words (full super-batch
                            // relabel) or G of Wc words (compact super-batch relabel)
     uint32_t *wprefix;     // same layout
-    uint32_t *bsum_w;      // [nbw], then G * nbw or G * nbwc
+    uint32_t *bsum_w;      // [nbw], then G * nbw or G * nbwc tile popcounts
     uint8_t *bytemaps;     // super-batch: byte maps of the G sub-batch bitmaps (or NULL)
     // super-batch only (the union; the rest: compact relabel only)
     int32_t *U[2];         // U_l, ping-pong by hop parity (full relabel: one buffer)
     int32_t *u_indptr;     // union block
     int32_t *u_gid;
-    int32_t *u_pos;        // position of each union-block id in U_{l+1}
-    int32_t *umap;         // position of each element of U_l in U_{l+1}
     int32_t *upos;         // [G * P] position of each sub-batch frontier node in U_l
     int32_t *f_pos;        // [G * Fs] position of each sub-batch destination in U_{l+1}
     int32_t *e_pos;        // [G * Es] position of each sub-batch sampled id in U_{l+1}
     uint32_t *bsum_dist;
     // shared outermost means of a super-batch: for each node r of the last hop's union frontier
     // and each sub-batch g, 1 + r's position among g's destinations (0: not there)
-    int32_t *inv;          // [U_cap(K-1) * G]
+    int32_t *inv;          // [U_cap(K-1) * G], valid where the bit of inv_mask is set
+    uint32_t *inv_mask;    // [U_cap(K-1)]: bit g set when sub-batch g holds the node
     // union gather of a super-batch (full relabel only; the compact relabel builds U_K as its
     // last union level): U_K, the union of the sub-batches' V_K
     int32_t *uK;           // [U_cap(K)]
@@ -101,7 +105,42 @@ struct Workspace {
     int64_t W, nbw, Wc, nbwc;
     int32_t mode;          // SuperMode
     size_t bytes;
+    // Look-back words of the call's single-pass scans, right after the status word (the call's
+    // first kernel zeroes both); each launch takes its slice in launch order.
+    uint64_t *arena;
+    int64_t arena_words;
+    mutable int64_t arena_used = 0;
+    // A slice of `tiles` look-back words followed by `counters` 32-bit ticket counters; NULL words
+    // when the arena is exhausted (the bound of carve() covers every launch sequence, so this
+    // does not happen).
+    LbSlice take_lb(int64_t tiles, int64_t counters = 1) const {
+        const int64_t need = tiles + (counters + 1) / 2;
+        if (!arena || arena_used + need > arena_words) return LbSlice{nullptr, nullptr};
+        LbSlice sl{arena + arena_used, reinterpret_cast<uint32_t *>(arena + arena_used + tiles)};
+        arena_used += need;
+        return sl;
+    }
+    // Bytes from the start of the workspace that the call's first kernel clears: the status
+    // word, the classification totals and the look-back arena, which the carve lays out back to
+    // back.
+    int64_t cleared_bytes() const {
+        return reinterpret_cast<const char *>(arena + arena_words) - reinterpret_cast<const char *>(status);
+    }
 };
+
+// The classification of one hop with its look-back words taken from the call's arena.
+gnn_status classify_launch(HopArgs h, const Workspace &w, hipStream_t s) {
+    h.lb = w.take_lb(h.nb);
+    if (h.lb.words == nullptr) return GNN_ERR_INTERNAL;
+    return launch_classify(h, s) == hipSuccess ? GNN_OK : GNN_ERR_HIP;
+}
+
+// A relabel launch sequence with its look-back words taken from the call's arena.
+gnn_status relabel_launch(RelabelArgs r, const Workspace &w, hipStream_t s) {
+    r.lb = w.take_lb(relabel_lb_words(r), r.nbm);
+    if (r.lb.words == nullptr) return GNN_ERR_INTERNAL;
+    return launch_relabel(r, s) == hipSuccess ? GNN_OK : GNN_ERR_HIP;
+}
 
 // Union bound of level l of a super-batch (l < K: hop l's frontier; l = K: the last node set):
 // min(N, G * per-sub-batch bound).
@@ -191,14 +230,20 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
         words += static_cast<int64_t>(G) * w.Wc;
         tiles += static_cast<int64_t>(G) * w.nbwc;
     }
+    // Look-back chains of every single-pass scan one call launches: relabels (the seeds' union,
+    // then per hop the union and the sub-batches; the standalone relabel and the union of the
+    // gathered sets), one tile each per 1024 bitmap words of every bitmap, plus a ticket each.
+    // And the classification of every hop: one tile per kClassifyTile frontier nodes.
+    const int64_t sub_tiles = mode == kSuperCompact ? w.nbwc : w.nbw;
+    w.arena_words = (2 * K + 2) * (w.nbw + 1) + K * (static_cast<int64_t>(G) * (sub_tiles + 1) + 1) +
+                    K * (nb_max + 1) + 64;
     w.status = c.take<int32_t>(64);
-    w.totals = c.take<uint32_t>(64);
+    w.totals = c.take<uint32_t>(kTotalsStride * GNN_MAX_HOPS);
+    w.arena = c.take<uint64_t>(w.arena_words);
     int64_t *cnt = c.take<int64_t>(32);
     w.d_U = cnt;
     w.d_uE = cnt ? cnt + 16 : nullptr;
-    w.packed = c.take<int32_t>(FU);
-    w.lists = c.take<int32_t>(4 * FU);
-    w.bsum = c.take<uint32_t>(kCols * nb_max);
+    w.lists = c.take<int32_t>(kCats * FU);
     w.bitmaps = c.take<uint32_t>(words);
     w.wprefix = c.take<uint32_t>(words);
     w.bsum_w = c.take<uint32_t>(tiles);
@@ -214,14 +259,13 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
         w.bsum_dist = c.take<uint32_t>(static_cast<int64_t>(G) * dist_tiles(F_max));
     }
     if (mode == kSuperCompact) {
-        w.u_pos = c.take<int32_t>(uE_max);
-        w.umap = c.take<int32_t>(FU);
         w.upos = c.take<int32_t>(static_cast<int64_t>(G) * w.P);
         w.f_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Fs);
         w.e_pos = c.take<int32_t>(static_cast<int64_t>(G) * w.Es);
     }
     if (G > 1 && K > 0) {
         w.inv = c.take<int32_t>(union_cap(mc, K - 1, G, N) * G);
+        w.inv_mask = c.take<uint32_t>(union_cap(mc, K - 1, G, N));
         if (mode == kSuperFull) w.uK = c.take<int32_t>(union_cap(mc, K, G, N));
     }
     w.bytes = c.off;
@@ -287,9 +331,10 @@ gnn_status check_blocks(const gnn_blocks *b, int64_t n_seeds, const int32_t *fan
     return GNN_OK;
 }
 
-HopArgs hop_args(const gnn_graph &g, const int32_t *front, const int64_t *d_F, int64_t F_cap,
-                 int32_t k, uint64_t hop_seed, int32_t *blk_indptr, int32_t *blk_gid,
-                 int64_t E_cap, int64_t *d_E, const Workspace &w, const Opts &o) {
+HopArgs hop_args(const gnn_graph &g, int l, const int32_t *front, const int64_t *d_F,
+                 int64_t F_cap, int32_t k, uint64_t hop_seed, int32_t *blk_indptr,
+                 int32_t *blk_gid, int64_t E_cap, int64_t *d_E, const Workspace &w,
+                 const Opts &o) {
     HopArgs h{};
     h.indptr = g.indptr;
     h.indices = g.indices;
@@ -308,10 +353,8 @@ HopArgs hop_args(const gnn_graph &g, const int32_t *front, const int64_t *d_F, i
     h.blk_gid = blk_gid;
     h.E_cap = E_cap;
     h.d_E = d_E;
-    h.packed = w.packed;
     h.lists = w.lists;
-    h.bsum = w.bsum;
-    h.totals = w.totals;
+    h.totals = w.totals + kTotalsStride * l;
     h.status = w.status;
     h.nb = static_cast<int32_t>(tiles_for(F_cap));
     return h;
@@ -364,12 +407,10 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
     ru.nlist = G;
     for (int gi = 0; gi < G; ++gi) ru.list[gi] = IdList{front(gi, l), d_F(gi, l), F_cap(gi, l), nullptr, 0, 0};
     ru.out[0] = BitmapOut{w.U[0], Ucap, w.d_U, nullptr};
-    GNN_TRY_HIP(launch_relabel(ru, s));
-    HopArgs h = hop_args(g, w.U[0], w.d_U, Ucap, k, hs, w.u_indptr, w.u_gid, uEcap, w.d_uE, w, o);
-    if (last) {   // the union positions table, filled by the distribution
-        h.inv = w.inv;
-        h.inv_g = G;
-    }
+    ru.bitmap_read_after = 1;   // the distribution ranks destinations in U by this bitmap
+    GNN_TRY(relabel_launch(ru, w, s));
+    HopArgs h = hop_args(g, l, w.U[0], w.d_U, Ucap, k, hs, w.u_indptr, w.u_gid, uEcap, w.d_uE, w, o);
+    if (last) h.inv_mask = w.inv_mask;   // the union positions table's mask, for the distribution
     if (w.bytemaps) {
         // the sub-batch byte maps are zeroed before their relabel; the bitmaps are rewritten
         // whole from them, except that the seeds' duplicate check needs clean bitmaps at hop 0
@@ -380,7 +421,7 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
         h.clear_ptr = w.bitmaps + w.W;  // the sub-batch bitmaps, zeroed before their relabel
         h.clear_n = static_cast<int64_t>(G) * w.W;
     }
-    GNN_TRY_HIP(launch_classify(h, s));
+    GNN_TRY(classify_launch(h, w, s));
     if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
     GNN_TRY_HIP(launch_sample(h, s));
     if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l + 1], s));
@@ -406,7 +447,10 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
     da.U_cap = Ucap;
     da.bsum = w.bsum_dist;
     da.status = w.status;
-    if (last) da.inv = w.inv;
+    if (last) {
+        da.inv = w.inv;
+        da.inv_mask = w.inv_mask;
+    }
     GNN_TRY_HIP(launch_dist(da, s));
     // Per-sub-batch relabel into bitmaps 1..G; the union bitmap is zeroed for the next hop.
     RelabelArgs rs = relabel_args(g, w, 1, G);
@@ -422,7 +466,7 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
     }
     rs.clear_ptr = w.bitmaps;
     rs.clear_n = w.W;
-    GNN_TRY_HIP(launch_relabel(rs, s));
+    GNN_TRY(relabel_launch(rs, w, s));
     return GNN_OK;
 }
 
@@ -459,28 +503,31 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         for (int gi = 0; gi < G; ++gi)
             r0.list[gi] = IdList{seeds_g[gi], nullptr, n_seeds_g[gi], w.upos + gi * w.P, 0, 0};
         r0.out[0] = BitmapOut{w.U[0], union_cap(mc, 0, G, g.num_nodes), w.d_U, nullptr};
-        GNN_TRY_HIP(launch_relabel(r0, s));
+        r0.sort_sets_bits = 1;   // U_0 starts the union that the node-id bitmap accumulates
+        GNN_TRY(relabel_launch(r0, w, s));
     }
     for (int l = 0; l < K; ++l) {
         const uint64_t hs = mix64(seed64 + kGamma * static_cast<uint64_t>(l + 1));
         if (G == 1) {
             gnn_blocks &out = *outs[0];
             const gnn_caps &c = out.caps;
-            HopArgs h = hop_args(g, front(0, l), d_F(0, l), F_cap(0, l), fanouts[l], hs,
+            HopArgs h = hop_args(g, l, front(0, l), d_F(0, l), F_cap(0, l), fanouts[l], hs,
                                  out.hop[l].indptr, out.hop[l].gid, c.edges[l], out.counts + 2 * l,
                                  w, o);
-            h.clear_ptr = w.bitmaps;
-            h.clear_n = w.W;
-            GNN_TRY_HIP(launch_classify(h, s));
-            if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
-            GNN_TRY_HIP(launch_sample(h, s));
-            if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l + 1], s));
             RelabelArgs r = relabel_args(g, w);
             r.nlist = 2;
             r.list[0] = IdList{front(0, l), d_F(0, l), F_cap(0, l), out.hop[l].dst_lid, 0, l == 0 ? 1 : 0};
             r.list[1] = IdList{out.hop[l].gid, out.counts + 2 * l, c.edges[l], out.hop[l].lid, 0, 0};
             r.out[0] = BitmapOut{out.hop[l].nodes, c.nodes[l], out.counts + 2 * l + 1, nullptr};
-            GNN_TRY_HIP(launch_relabel(r, s));
+            if (!relabel_sorts(r)) {   // the bitmap path marks a cleared bitmap
+                h.clear_ptr = w.bitmaps;
+                h.clear_n = w.W;
+            }
+            GNN_TRY(classify_launch(h, w, s));
+            if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
+            GNN_TRY_HIP(launch_sample(h, s));
+            if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l + 1], s));
+            GNN_TRY(relabel_launch(r, w, s));
             continue;
         }
         if (!compact) {
@@ -495,24 +542,29 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         const int64_t uEcap = Ucap * fanouts[l];
         int32_t *Ul = w.U[l & 1];
         int32_t *Ul1 = w.U[(l + 1) & 1];
-        HopArgs h = hop_args(g, Ul, w.d_U + l, Ucap, fanouts[l], hs, w.u_indptr, w.u_gid, uEcap,
+        HopArgs h = hop_args(g, l, Ul, w.d_U + l, Ucap, fanouts[l], hs, w.u_indptr, w.u_gid, uEcap,
                              w.d_uE + l, w, o);
-        if (l == K - 1) {   // the union positions table, filled by the distribution
-            h.inv = w.inv;
-            h.inv_g = G;
-        }
-        GNN_TRY_HIP(launch_classify(h, s));
+        if (l == K - 1) h.inv_mask = w.inv_mask;   // the union positions table's mask
+        h.mark = w.bitmaps;   // the sampled ids join U_l in the node-id bitmap
+        // the sub-batch bitmaps (and byte maps) that this hop's distribution marks, zeroed by the
+        // sampler up to |U_l| + |uE_l| >= |U_{l+1}| ids
+        h.zero_words = w.bitmaps + w.W;
+        h.zero_bytes = reinterpret_cast<uint32_t *>(w.bytemaps);
+        h.zero_stride = w.Wc;
+        h.zero_g = G;
+        h.zero_da = w.d_U + l;
+        h.zero_db = w.d_uE + l;
+        GNN_TRY(classify_launch(h, w, s));
         if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l], s));
         GNN_TRY_HIP(launch_sample(h, s));
         if (sev) GNN_TRY_HIP(hipEventRecord(sev[2 * l + 1], s));
-        // U_{l+1} = U_l + the sampled ids: mark the ids into the accumulated node-id bitmap, rank
-        // both lists in the result.
+        // U_{l+1} = U_l + the sampled ids, whose bits the sampler has set in the accumulated
+        // node-id bitmap: emit its ids (and word prefixes, for ranks in U_{l+1}).
         RelabelArgs ru = relabel_args(g, w);
-        ru.nlist = 2;
-        ru.list[0] = IdList{w.u_gid, w.d_uE + l, uEcap, w.u_pos, 0, 0};
-        ru.list[1] = IdList{Ul, w.d_U + l, Ucap, w.umap, 0, 2};
+        ru.nlist = 0;
         ru.out[0] = BitmapOut{Ul1, U1cap, w.d_U + l + 1, nullptr};
-        GNN_TRY_HIP(launch_relabel(ru, s));
+        ru.bitmap_read_after = 1;   // positions in U_{l+1} are ranks in this bitmap
+        GNN_TRY(relabel_launch(ru, w, s));
         // Each sub-batch's block from the union block, with U_{l+1} positions of its ids.
         DistArgs da{};
         da.G = G;
@@ -529,19 +581,26 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         da.ntiles = tiles;
         da.u_indptr = w.u_indptr;
         da.u_gid = w.u_gid;
-        da.u_pos = w.u_pos;
-        da.umap = w.umap;
+        da.Ul = Ul;
+        da.bm1 = w.bitmaps;
+        da.wprefix1 = w.wprefix;
+        da.id_bound = g.num_nodes;
         da.uE_cap = uEcap;
         da.d_U = w.d_U + l;
         da.U_cap = Ucap;
-        da.clear_ptr = w.bitmaps + w.W;
-        da.clear_bytes = reinterpret_cast<uint32_t *>(w.bytemaps);
-        da.clear_stride = w.Wc;
+        // the sub-batch relabel's marks (positions in U_{l+1}), made by the distribution
+        da.mark_words = w.bitmaps + w.W;
+        da.mark_bytes = w.bytemaps;
+        da.mark_stride = w.Wc;
+        da.mark_dup = l == 0 ? 1 : 0;
         da.d_U1 = w.d_U + l + 1;
         da.U1_cap = U1cap;
         da.bsum = w.bsum_dist;
         da.status = w.status;
-        if (l == K - 1) da.inv = w.inv;
+        if (l == K - 1) {
+            da.inv = w.inv;
+            da.inv_mask = w.inv_mask;
+        }
         GNN_TRY_HIP(launch_dist(da, s));
         // Per-sub-batch relabel in U_{l+1} positions; the positions of V_l become the next hop's.
         RelabelArgs rs = compact_relabel_args(w, G, Ul1, w.d_U + l + 1, U1cap);
@@ -549,14 +608,15 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         rs.nlist = 2 * G;
         for (int gi = 0; gi < G; ++gi) {
             gnn_blocks &out = *outs[gi];
+            // marked by the distribution: ranked only
             rs.list[2 * gi] = IdList{w.f_pos + gi * w.Fs, d_F(gi, l), F_cap(gi, l),
-                                     out.hop[l].dst_lid, gi, l == 0 ? 1 : 0};
+                                     out.hop[l].dst_lid, gi, 2};
             rs.list[2 * gi + 1] = IdList{w.e_pos + gi * w.Es, out.counts + 2 * l, out.caps.edges[l],
-                                         out.hop[l].lid, gi, 0};
+                                         out.hop[l].lid, gi, 2};
             rs.out[gi] = BitmapOut{out.hop[l].nodes, out.caps.nodes[l], out.counts + 2 * l + 1,
                                    w.upos + gi * w.P};
         }
-        GNN_TRY_HIP(launch_relabel(rs, s));
+        GNN_TRY(relabel_launch(rs, w, s));
     }
     return GNN_OK;
 }
@@ -587,9 +647,27 @@ const int32_t *union_prepare(const gnn_graph &g, const gnn_minibatch_out *outs, 
                              nullptr, 0, 0};
     }
     ru.out[0] = BitmapOut{w.uK, union_cap(mc, K, G, g.num_nodes), w.d_U + K, nullptr};
-    if (launch_relabel(ru, s) != hipSuccess) *st = GNN_ERR_HIP;
+    *st = relabel_launch(ru, w, s);
     return w.uK;
 }
+
+// Fault injection for tests of the error paths: GNN_FAULT (read once per process) lists kinds,
+// comma-separated: "alloc" fails every set-up allocation before it is made, "launch" fails every
+// hot-path call after its argument checks, before anything is enqueued; both return GNN_ERR_HIP.
+enum : int { kFaultAlloc = 1, kFaultLaunch = 2 };
+int fault_mask() {
+    static const int mask = [] {
+        const char *e = getenv("GNN_FAULT");
+        int m = 0;
+        if (e != nullptr) {
+            if (strstr(e, "alloc")) m |= kFaultAlloc;
+            if (strstr(e, "launch")) m |= kFaultLaunch;
+        }
+        return m;
+    }();
+    return mask;
+}
+bool fault(int kind) { return (fault_mask() & kind) != 0; }
 
 gnn_status check_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t *add,
                                 int64_t n_add, int64_t id_bound, const int32_t *uniq,
@@ -610,6 +688,7 @@ gnn_status unique_relabel_in(const Workspace &w, int32_t *status, const int32_t 
                              int64_t n_add, int64_t id_bound, int32_t *uniq, int64_t cap_uniq,
                              int64_t *d_n_uniq, int32_t *add_lid, int32_t *keep_lid,
                              hipStream_t s) {
+    GNN_TRY_HIP(launch_fill_u32(reinterpret_cast<uint32_t *>(w.arena), 2 * w.arena_words, 0u, s));
     if (status) GNN_TRY_HIP(launch_fill_i32(status, 1, 0, s));
     RelabelArgs r{};
     r.nlist = 2;
@@ -625,7 +704,7 @@ gnn_status unique_relabel_in(const Workspace &w, int32_t *status, const int32_t 
     r.nbw = static_cast<int32_t>(w.nbw);
     r.status = status;
     r.bitmap_cleared = 0;
-    GNN_TRY_HIP(launch_relabel(r, s));
+    GNN_TRY(relabel_launch(r, w, s));
     return GNN_OK;
 }
 
@@ -738,9 +817,10 @@ gnn_status gnn_sample_khop(const gnn_graph *g, const int32_t *seeds, int64_t n_s
     if (!ws) return GNN_ERR_INVALID_ARG;
     const Workspace need = carve(out->caps, g->num_nodes, 1, kSuperNone, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
     const Workspace w = carve(out->caps, g->num_nodes, 1, kSuperNone, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
+    GNN_TRY_HIP(launch_fill_u32(reinterpret_cast<uint32_t *>(w.status), w.cleared_bytes() / 4, 0u, s));
     const int32_t *sp[1] = {seeds};
     const int64_t ns[1] = {n_seeds};
     gnn_blocks *ob[1] = {out};
@@ -768,6 +848,7 @@ gnn_status gnn_unique_relabel(const int32_t *keep, int64_t n_keep, const int32_t
     gnn_caps none{};
     const Workspace need = carve(none, id_bound, 1, kSuperNone, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
     const Workspace w = carve(none, id_bound, 1, kSuperNone, ws);
     return unique_relabel_in(w, w.status, keep, n_keep, add, d_n_add, n_add, id_bound, uniq,
                              cap_uniq, d_n_uniq, add_lid, keep_lid, static_cast<hipStream_t>(stream));
@@ -785,6 +866,7 @@ gnn_status gnn_unique_relabel_noalloc(const int32_t *keep, int64_t n_keep, const
     gnn_caps none{};
     const Workspace need = carve(none, id_bound, 1, kSuperNone, nullptr);
     if (need.bytes > sizeof(scratch)) return GNN_ERR_INTERNAL;   // the bound above keeps it in
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     void *base = nullptr;
     if ((st = scratch_address(s, &base)) != GNN_OK) return st;
@@ -816,6 +898,10 @@ gnn_status gnn_feature_store_create(const float *table, int32_t table_on_host, i
     fs->d = d;
     fs->ld = ld;
     fs->cache_rows = cache_rows;
+    if (cache_rows > 0 && fault(kFaultAlloc)) {
+        delete fs;
+        return GNN_ERR_HIP;
+    }
     if (cache_rows > 0) {
         int32_t *st_dev = nullptr;
         bool ok = hipMalloc(reinterpret_cast<void **>(&fs->cache),
@@ -861,6 +947,7 @@ gnn_status gnn_adjacency_cache_create(const gnn_graph *g, const int32_t *hot_ord
     if (gs != GNN_OK) return gs;
     if (n_hot < 0 || n_hot > g->num_nodes || max_entries < 0 || (n_hot > 0 && !hot_order))
         return GNN_ERR_INVALID_ARG;
+    if (fault(kFaultAlloc)) return GNN_ERR_HIP;
     // the hot ids and their degrees, on the host: the longest prefix of the order that fits
     std::vector<int32_t> hot(static_cast<size_t>(n_hot));
     std::vector<int64_t> deg(static_cast<size_t>(n_hot));
@@ -961,6 +1048,7 @@ gnn_status gnn_gather_features(const gnn_feature_store *fs, const int32_t *ids,
     if (!fs || n < 0 || ld_out < fs->d) return GNN_ERR_INVALID_ARG;
     if (n > 0 && (!ids || !out)) return GNN_ERR_INVALID_ARG;
     if (n * fs->d > kFlatMax) return GNN_ERR_UNSUPPORTED;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
     GNN_TRY_HIP(launch_gather(fs->table, fs->cache, fs->slot, fs->ld, fs->d, fs->num_nodes, ids,
                               d_n, n, out, ld_out, d_hits, d_status,
                               static_cast<hipStream_t>(stream)));
@@ -976,6 +1064,7 @@ gnn_status gnn_mean_aggregate(const int32_t *indptr, const int32_t *lid, int64_t
     if (n_dst > 0 && (!indptr || !out)) return GNN_ERR_INVALID_ARG;
     if (n_lid > 0 && (!lid || !src)) return GNN_ERR_INVALID_ARG;
     if (n_dst * d > kFlatMax) return GNN_ERR_UNSUPPORTED;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
     const MeanJob job{indptr, lid, n_lid, d_n_dst, n_dst, src, n_src, out};
     GNN_TRY_HIP(launch_mean(&job, 1, ld_src, ld_out, d, 16, d_status,
                             static_cast<hipStream_t>(stream)));
@@ -1004,6 +1093,7 @@ gnn_status gnn_sage_update(const int32_t *dst_lid, const int64_t *d_n_dst, int64
     const gnn_status st =
         check_sage(dst_lid, n_dst, src, ld_src, n_src, d, agg, ld_agg, W, d_out, out, ld_out);
     if (st != GNN_OK) return st;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
     GNN_TRY_HIP(launch_sage_update(dst_lid, d_n_dst, n_dst, src, ld_src, n_src, agg, ld_agg, d, W,
                                    bias, d_out, relu, out, ld_out, d_status,
                                    static_cast<hipStream_t>(stream)));
@@ -1020,6 +1110,7 @@ gnn_status gnn_sage_layer(const int32_t *indptr, const int32_t *lid, int64_t n_l
         check_sage(dst_lid, n_dst, src, ld_src, n_src, d, agg, ld_agg, W, d_out, out, ld_out);
     if (st != GNN_OK) return st;
     if (n_lid < 0 || (n_dst > 0 && !indptr) || (n_lid > 0 && !lid)) return GNN_ERR_INVALID_ARG;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const MeanJob job{indptr, lid, n_lid, d_n_dst, n_dst, src, n_src, agg};
     GNN_TRY_HIP(launch_mean(&job, 1, ld_src, ld_agg, d, 16, d_status, s));
@@ -1075,6 +1166,7 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     const SuperMode mode = super_mode(mc, g->num_nodes, group, o.flags);
     const Workspace need = carve(mc, g->num_nodes, group, mode, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
     // How stages 2 and 3 run (below).  Batched unless interleaving is asked for: one launch's
     // start-up and drain instead of G, G times as many host-link reads in flight for a
     // host-resident table, and (with a table in HBM) the shared outermost means; measured faster
@@ -1098,7 +1190,7 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         timer->cursor += 1;
         GNN_TRY_HIP(hipEventRecord(ev[0], s));
     }
-    GNN_TRY_HIP(launch_fill_i32(w.status, 1, 0, s));
+    GNN_TRY_HIP(launch_fill_u32(reinterpret_cast<uint32_t *>(w.status), w.cleared_bytes() / 4, 0u, s));
     // Stage 1: sampling and relabel of every sub-batch (one shared seed64).
     st = run_sample(*g, sp, nsg, group, fanouts, K, seed64, ob, w, o, s,
                     ev ? ev + kSampleEvents : nullptr);
@@ -1170,7 +1262,8 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
                              fs->num_nodes, nullptr};
             float *hk[GNN_MAX_GROUP];
             for (int gi = 0; gi < group; ++gi) hk[gi] = outs[gi].h[K - 1];
-            GNN_TRY_HIP(launch_mean_scatter(uj, w.inv, group, hk, fs->ld, outs[0].ld_h, d, w.status, s));
+            GNN_TRY_HIP(launch_mean_scatter(uj, w.inv, w.inv_mask, group, hk, fs->ld, outs[0].ld_h, d,
+                                            w.status, s));
         } else {
             GNN_TRY_HIP(launch_mean(jobs, group, from_table ? fs->ld : outs[0].ld_h, outs[0].ld_h, d,
                                     fanouts[K - 1], w.status, s));

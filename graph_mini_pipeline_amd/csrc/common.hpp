@@ -105,6 +105,77 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *total, T *smem) {
     return before + inc - v;
 }
 
+// ---- single-pass scans (decoupled look-back) ----------------------------------------------------
+//
+// A scan over tiles in one launch: each workgroup takes a ticket (an atomic counter, so tiles are
+// handed out in the order workgroups start and every lower tile belongs to a workgroup that is
+// running or done), publishes its tile's aggregate, sums its predecessors' published words back
+// to the nearest inclusive prefix, and publishes its own inclusive prefix.  A tile only waits for
+// lower tiles, which publish their aggregates without waiting, so every wait ends.  Each tile's
+// state and value share one 64-bit word written and read with agent-scope atomics, so no other
+// memory ordering is needed across the chip's L2 caches.  Words and ticket start at zero (the
+// call's first kernel clears them).
+constexpr uint64_t kLbAggregate = 1ull << 62;
+constexpr uint64_t kLbInclusive = 2ull << 62;
+
+__device__ __forceinline__ void lb_publish(uint64_t *word, uint64_t state, uint32_t value) {
+    __hip_atomic_store(word, state | value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The sum of the values of tiles 0 .. t-1 of a chain of words; called by all 64 lanes of one
+// wavefront, returns the same value on every lane.  Each round reads the 256 nearest unsummed
+// predecessors at once (lane L the four at distances 4L .. 4L+3), so that a chain of up to 256
+// tiles needs one round trip to the coherent memory once its words are published.
+constexpr int kLbPerLane = 4;
+__device__ __forceinline__ uint32_t lb_exclusive(const uint64_t *words, int64_t t) {
+    const int lane = lane_id();
+    uint32_t prefix = 0;
+    int64_t end = t;
+    while (end > 0) {
+        uint64_t f[kLbPerLane];
+#pragma unroll
+        for (int q = 0; q < kLbPerLane; ++q) {
+            const int64_t j = end - 1 - (kLbPerLane * lane + q);
+            f[q] = kLbInclusive;            // before tile 0: an inclusive prefix of 0
+            if (j >= 0) {
+                do {
+                    f[q] = __hip_atomic_load(&words[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } while ((f[q] >> 62) == 0);
+            }
+        }
+        // the nearest inclusive word of this lane (kLbPerLane: none), and the lanes that have one
+        int near = kLbPerLane;
+#pragma unroll
+        for (int q = kLbPerLane - 1; q >= 0; --q)
+            if ((f[q] >> 62) == 2) near = q;
+        const uint64_t incl = __ballot(near < kLbPerLane);
+        const int k = incl ? __ffsll(static_cast<long long>(incl)) - 1 : 64;
+        // sum every word up to and including the nearest inclusive one (all of them if none)
+        uint32_t v = 0;
+#pragma unroll
+        for (int q = 0; q < kLbPerLane; ++q)
+            if (lane < k || (lane == k && q <= near)) v += static_cast<uint32_t>(f[q]);
+        prefix += wave_sum(v);
+        if (incl) break;
+        end -= 64 * kLbPerLane;
+    }
+    return prefix;
+}
+
+// Thread 0 of the workgroup takes the next ticket of `ticket`; every thread gets it.
+__device__ __forceinline__ uint32_t lb_ticket(uint32_t *ticket, uint32_t *s_slot) {
+    if (threadIdx.x == 0) *s_slot = atomicAdd(ticket, 1u);
+    __syncthreads();
+    return *s_slot;
+}
+
+// Per-launch chains of look-back words, carved from the workspace's arena (cleared at the start of
+// every call), handed out in launch order on the host.
+struct LbSlice {
+    uint64_t *words;    // one per tile
+    uint32_t *ticket;   // ticket counter (a relabel: one per bitmap)
+};
+
 // ---- launch helpers (host) ----------------------------------------------------------------------
 
 inline unsigned grid_for(int64_t items, int per_block, unsigned max_blocks) {
@@ -121,6 +192,9 @@ enum : int32_t { kFull = 0, kGroup = 1, kWave = 2, kBlock = 3, kNumClasses = 4 }
 // then FULL, GROUP, the buckets and BLOCK).
 constexpr int kWaveBuckets = 6;
 constexpr int kCols = 4 + kWaveBuckets;
+constexpr int kCats = 3 + kWaveBuckets;       // FULL, GROUP, WAVE buckets, BLOCK
+// Per-hop slots of the classification totals in the workspace (kCols used).
+constexpr int kTotalsStride = 16;
 
 // Candidate capacities per class (LDS) and the fanout each supports (capacity >= 4 * fanout).
 // A sampler workgroup holds kBlockCap candidates of 12 bytes (key, position): 3328 of them keep it
@@ -150,16 +224,26 @@ struct HopArgs {
     int32_t *blk_gid;       // [E_cap]
     int64_t E_cap;
     int64_t *d_E;           // receives |E_l|
-    int32_t *packed;        // [F_cap] (c << 4) | category
-    int32_t *lists;         // [4 * F_cap] class work-lists (the WAVE list by degree bucket)
-    uint32_t *bsum;         // [kCols * nb] per-block edge counts then the category counts
-    uint32_t *totals;       // [kCols] |E_l| then the category sizes
+    int32_t *lists;         // [kCats * F_cap] one work-list per category (FULL, GROUP, the WAVE
+                            // degree buckets largest first, BLOCK), each at a multiple of F_cap
+    uint32_t *totals;       // [kCols] |E_l| then the category sizes (zero before the hop)
     uint32_t *clear_ptr;    // words the classification clears (the relabel bitmap of this hop)
     int64_t clear_n;
-    int32_t *inv;           // optional [F * inv_g]: zeroed over the frontier by the classification
-    int32_t inv_g;
+    uint32_t *inv_mask;     // optional [F]: zeroed over the frontier by the classification
+    uint32_t *mark;         // optional bitmap over node ids: the sampler sets the bit of every
+                            // id it emits (a super-batch's accumulated union, compact relabel)
+    // optional: the grid first zeroes zero_g regions of zero_stride words (and their byte maps of
+    // 8 zero_stride words, when given) over the first ceil(bound / 32) words, bound = *zero_da +
+    // *zero_db capped at 32 zero_stride: the sub-batch bitmaps that this hop's distribution marks
+    uint32_t *zero_words;
+    uint32_t *zero_bytes;
+    int64_t zero_stride;
+    int32_t zero_g;
+    const int64_t *zero_da;
+    const int64_t *zero_db;
     int32_t *status;
-    int32_t nb;             // classify blocks
+    int32_t nb;             // classify tiles (workgroups)
+    LbSlice lb;             // look-back words of the classification: nb tiles (zero)
 };
 
 // Largest super-batch (sub-batches per call).
@@ -198,14 +282,23 @@ struct RelabelArgs {
                               // (plain stores) and the popcount pass packs bytes into the bitmap
     uint32_t *bitmap;         // [nbm * W]
     uint32_t *wprefix;        // [nbm * W]
-    uint32_t *bsum;           // [nbm * nbw]
+    uint32_t *bsum;           // [nbm * nbw] tile popcounts (bitmaps of many tiles)
     int64_t W;
     int32_t nbw;              // tiles per bitmap
-    uint32_t *clear_ptr;      // optional region zeroed by the popcount pass
+    uint32_t *clear_ptr;      // optional region zeroed by the emit pass
     int64_t clear_n;
     int32_t *status;
     int32_t bitmap_cleared;   // the bitmaps are already zero on this stream
+    LbSlice lb;               // look-back words of the emit pass: nbm * nbw tiles (zero)
+    int32_t sort_sets_bits;   // the sort path (short lists) also sets the unique ids' bits in the
+                              // bitmap (which it otherwise leaves untouched)
+    int32_t bitmap_read_after; // later kernels rank ids in the bitmap and its word prefixes: the
+                               // bitmap path is required
 };
+
+// Short lists are relabelled by one workgroup that sorts them in LDS (relabel.hip) instead of
+// through the bitmap; whether launch_relabel takes that path for these arguments.
+bool relabel_sorts(const RelabelArgs &a);
 
 __device__ __forceinline__ int64_t relabel_bound(const RelabelArgs &a) {
     if (a.d_bound == nullptr) return a.id_bound;
@@ -242,25 +335,32 @@ struct DistArgs {
     int64_t id_bound;
     const int32_t *u_indptr;   // union block
     const int32_t *u_gid;
-    const int32_t *u_pos;      // position in U_{l+1} of each union-block id
-    const int32_t *umap;       // position in U_{l+1} of each element of U_l
     int64_t uE_cap;
     const int64_t *d_U;        // |U_l|
     int64_t U_cap;
-    uint32_t *clear_ptr;       // optional: G sub-batch bitmaps of stride clear_stride words,
-    int64_t clear_stride;      // zeroed up to ceil(|U_{l+1}| / 32) words each
-    uint32_t *clear_bytes;     // optional: their byte maps (stride 8 clear_stride words), zeroed
-                               // over the same live words
     const int64_t *d_U1;       // |U_{l+1}|
     int64_t U1_cap;
     uint32_t *bsum;            // [ntiles]
     int32_t *status;
     int32_t *inv;              // optional out [U_cap * G]: inv[r * G + g] = 1 + the position of
-                               // union node r among sub-batch g's destinations (0: not there)
+                               // union node r among sub-batch g's destinations, written where
+    uint32_t *inv_mask;        // inv_mask[r] (zero before) gets bit g: entries without it are stale
+    // optional (compact relabel): the sub-batch relabel's marks, made here: sub-batch g's bitmap
+    // at mark_words + g * mark_stride (zero before), or its byte map at mark_bytes + 32 g
+    // mark_stride; destinations at hop 0 are seeds, marked with a duplicate check
+    uint32_t *mark_words;
+    uint8_t *mark_bytes;
+    int64_t mark_stride;
+    int32_t mark_dup;
+    // compact relabel: U_l (global ids) and the node-id bitmap of U_{l+1} with its word prefixes;
+    // a position in U_{l+1} is a rank in that bitmap
+    const int32_t *Ul;
+    const uint32_t *bm1;
+    const uint32_t *wprefix1;
 };
 
 constexpr int kClassifyThreads = 256;
-constexpr int kClassifyItems = 4;
+constexpr int kClassifyItems = 2;   // nodes per thread: two keep enough wavefronts in flight for the row-pointer loads
 constexpr int kClassifyTile = kClassifyThreads * kClassifyItems;
 constexpr int kBitmapThreads = 256;
 // Bitmap words per thread of the popcount and emit passes: 4 keeps more workgroups in flight than
@@ -274,6 +374,8 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s
 hipError_t launch_classify(HopArgs a, hipStream_t s);
 hipError_t launch_sample(const HopArgs &a, hipStream_t s);
 hipError_t launch_relabel(RelabelArgs a, hipStream_t s);
+// Look-back words a launch_relabel call needs in a.lb, besides its nbm ticket counters.
+int64_t relabel_lb_words(const RelabelArgs &a);
 hipError_t launch_dist(const DistArgs &a, hipStream_t s);
 hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
@@ -323,11 +425,11 @@ constexpr int kMaxMeanSegs = 16;
 hipError_t launch_mean(const MeanJob *jobs, int njobs, int64_t ld_src, int64_t ld_out, int64_t d,
                        int32_t max_c, int32_t *status, hipStream_t s);
 // One block whose destinations are the union of G sub-batches' destinations: destination r's mean
-// is stored to row inv[r * G + g] - 1 of outs[g] for every g with inv[r * G + g] > 0 (job.out is
-// not used).
-hipError_t launch_mean_scatter(const MeanJob &job, const int32_t *inv, int G, float *const *outs,
-                               int64_t ld_src, int64_t ld_out, int64_t d, int32_t *status,
-                               hipStream_t s);
+// is stored to row inv[r * G + g] - 1 of outs[g] for every g whose bit is set in inv_mask[r] (job.out
+// is not used; entries without their bit are never used).
+hipError_t launch_mean_scatter(const MeanJob &job, const int32_t *inv, const uint32_t *inv_mask,
+                               int G, float *const *outs, int64_t ld_src, int64_t ld_out, int64_t d,
+                               int32_t *status, hipStream_t s);
 // The dense UPDATE of a GraphSAGE-mean layer: out = act([src[dst_lid] || agg] W + bias) on the
 // matrix cores (fp32); rows beyond *d_n (when given) are skipped.
 hipError_t launch_sage_update(const int32_t *dst_lid, const int64_t *d_n, int64_t n_cap,

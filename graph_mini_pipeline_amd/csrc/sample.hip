@@ -50,7 +50,6 @@ __device__ __forceinline__ int32_t node_class(int64_t deg, int k, int group_max,
 // listed largest first (bucket b holds degrees in [2^(13-b), 2^(14-b)), the last also all smaller
 // ones and the first all larger ones), BLOCK.  The WAVE list is ordered by bucket, so wavefronts
 // that walk it with a snake stride take the largest rows first and balance their loads.
-constexpr int kCats = 3 + kWaveBuckets;       // FULL, GROUP, WAVE buckets, BLOCK
 constexpr int kCatBlock = kCats - 1;
 static_assert(kCols == 1 + kCats, "edges, then one column per category");
 __device__ __forceinline__ int32_t node_cat(int32_t cls, int64_t deg) {
@@ -75,21 +74,59 @@ __device__ __forceinline__ int64_t class_total(const uint32_t *totals, int32_t c
     return n;
 }
 
-__global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) {
-    __shared__ uint32_t red[kCols][kClassifyThreads / 64];
-    // The relabel bitmap of this hop is cleared here, long before the relabel reads it.
+// Item `item` of the one-wavefront class, whose nodes sit in one work-list per degree bucket
+// (largest degrees first): the bucket holding the item, then the item's place in it.
+__device__ __forceinline__ int32_t wave_item(const HopArgs &a, int64_t item) {
+    int64_t off = item;
+    int b = 0;
+#pragma unroll
+    for (int q = 0; q < kWaveBuckets - 1; ++q) {
+        const int64_t c = a.totals[3 + q];
+        const bool past = b == q && off >= c;
+        off -= past ? c : 0;
+        b += past ? 1 : 0;
+    }
+    return a.lists[static_cast<int64_t>(2 + b) * a.F_cap + off];
+}
+
+// Count of category `cat` in counters packed as the classification packs them (categories 0..3
+// in 16-bit fields of c0, 4..8 in 12-bit fields of c1).
+__device__ __forceinline__ uint32_t cat_count(uint64_t c0, uint64_t c1, int cat) {
+    return cat < 4 ? static_cast<uint32_t>((c0 >> (16 * cat)) & 0xFFFF)
+                   : static_cast<uint32_t>((c1 >> (12 * (cat - 4))) & 0xFFF);
+}
+
+// One pass over the frontier, in tiles of kClassifyTile nodes taken by ticket: each node's c and
+// category; the block indptr as an exclusive scan of c (the tile's offset by look-back over the
+// earlier tiles; the last tile writes |E_l|); each node appended to its category's work-list
+// (one atomic reservation per category per tile: the order inside a list does not matter, since
+// every node's outputs are placed by its block indptr).  The grid also zeroes the optional clear
+// region and, for a super-batch's last hop, the union positions table.
+__global__ __launch_bounds__(kClassifyThreads) void k_classify(HopArgs a) {
+    __shared__ uint32_t sm_c[kClassifyThreads / 64];
+    __shared__ uint64_t sm_k0[kClassifyThreads / 64];
+    __shared__ uint64_t sm_k1[kClassifyThreads / 64];
+    __shared__ uint32_t s_ticket, s_prefix;
+    __shared__ uint32_t s_base[kCats];
     for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < a.clear_n;
          t += static_cast<int64_t>(gridDim.x) * blockDim.x)
         a.clear_ptr[t] = 0u;
     const int64_t F = load_count(a.d_F, a.F_cap);
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kClassifyTile +
-                         static_cast<int64_t>(threadIdx.x) * kClassifyItems;
-    uint32_t vals[kCols];
-#pragma unroll
-    for (int t = 0; t < kCols; ++t) vals[t] = 0;
+    const int64_t last = F > 0 ? (F - 1) / kClassifyTile : 0;   // last tile holding nodes
+    // The grid is sized by the frontier bound: workgroups beyond the live tiles leave before
+    // taking a ticket (tickets of one counter are handed out one at a time).  The live ones take
+    // tickets 0 .. last, and ticket t is tile t.
+    if (static_cast<int64_t>(blockIdx.x) > last) return;
+    const int64_t tile = lb_ticket(a.lb.ticket, &s_ticket);
+    const int64_t base = tile * kClassifyTile + static_cast<int64_t>(threadIdx.x) * kClassifyItems;
+    int32_t cq[kClassifyItems], catq[kClassifyItems];
+    uint32_t csum = 0;
+    uint64_t kc0 = 0, kc1 = 0;  // categories 0..3 in 16-bit counters, 4..8 in 12-bit counters
 #pragma unroll
     for (int q = 0; q < kClassifyItems; ++q) {
         const int64_t i = base + q;
+        catq[q] = -1;
+        cq[q] = 0;
         if (i < F) {
             const int32_t v = a.front[i];
             int64_t deg = 0;
@@ -100,135 +137,10 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_count(HopArgs a) 
             }
             const int32_t c = deg <= a.k ? static_cast<int32_t>(deg) : a.k;
             const int32_t cat = node_cat(node_class(deg, a.k, a.group_max, a.wave_max), deg);
-            if (a.inv)
-                for (int g = 0; g < a.inv_g; ++g) a.inv[i * a.inv_g + g] = 0;
-            a.packed[i] = (c << 4) | cat;
-            vals[0] += static_cast<uint32_t>(c);
-#pragma unroll
-            for (int t = 0; t < kCats; ++t) vals[1 + t] += cat == t;
-        }
-    }
-    const int lane = lane_id(), w = threadIdx.x >> 6;
-#pragma unroll
-    for (int t = 0; t < kCols; ++t) {
-        const uint32_t s = wave_sum(vals[t]);
-        if (lane == 0) red[t][w] = s;
-    }
-    __syncthreads();
-    if (threadIdx.x < kCols) {
-        uint32_t s = 0;
-        for (int i = 0; i < kClassifyThreads / 64; ++i) s += red[threadIdx.x][i];
-        a.bsum[static_cast<int64_t>(threadIdx.x) * a.nb + blockIdx.x] = s;
-    }
-}
-
-// Many blocks: one workgroup scans the per-block sums (edges, then the category counts) in place,
-// over the blocks that hold frontier nodes (the grid is sized by the frontier bound; the blocks
-// past the actual frontier place nothing and their sums are not read).
-__global__ __launch_bounds__(1024) void k_classify_scan(HopArgs a) {
-    __shared__ uint32_t smem[16];
-    const int64_t F = load_count(a.d_F, a.F_cap);
-    const int64_t live = (F + kClassifyTile - 1) / kClassifyTile;
-    const int nb = static_cast<int>(live < a.nb ? live : a.nb);
-    const int per = (nb + 1023) / 1024;
-    for (int col = 0; col < kCols; ++col) {
-        uint32_t *arr = a.bsum + static_cast<int64_t>(col) * a.nb;
-        const int b0 = threadIdx.x * per;
-        uint32_t local = 0;
-        for (int t = 0; t < per; ++t)
-            if (b0 + t < nb) local += arr[b0 + t];
-        uint32_t total;
-        uint32_t run = block_exclusive_scan<uint32_t, 1024>(local, &total, smem);
-        for (int t = 0; t < per; ++t) {
-            if (b0 + t < nb) {
-                const uint32_t x = arr[b0 + t];
-                arr[b0 + t] = run;
-                run += x;
-            }
-        }
-        if (threadIdx.x == 0) a.totals[col] = total;
-    }
-}
-
-// Places every frontier node: block indptr (exclusive scan of c) and the stable class lists.
-// With few blocks (pre_scanned = 0) each block sums the partials of the blocks before it;
-// otherwise k_classify_scan has already turned them into offsets and totals.
-__global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a, int32_t pre_scanned) {
-    __shared__ uint32_t sm_c[kClassifyThreads / 64];
-    __shared__ uint64_t sm_k0[kClassifyThreads / 64];
-    __shared__ uint64_t sm_k1[kClassifyThreads / 64];
-    __shared__ uint32_t s_off[kCols];
-    __shared__ uint32_t s_tot[kCols];
-    __shared__ uint32_t s_red[2 * kCols][kClassifyThreads / 64];
-    __shared__ uint32_t s_base[kCats];   // start of each category in its class list
-    const int64_t F = load_count(a.d_F, a.F_cap);
-    if (pre_scanned) {
-        if (threadIdx.x < kCols) {
-            s_off[threadIdx.x] = a.bsum[static_cast<int64_t>(threadIdx.x) * a.nb + blockIdx.x];
-            s_tot[threadIdx.x] = a.totals[threadIdx.x];
-        }
-    } else {
-        uint32_t before[kCols], all[kCols];
-#pragma unroll
-        for (int col = 0; col < kCols; ++col) before[col] = all[col] = 0;
-        for (int b = threadIdx.x; b < a.nb; b += blockDim.x) {
-#pragma unroll
-            for (int col = 0; col < kCols; ++col) {
-                const uint32_t x = a.bsum[static_cast<int64_t>(col) * a.nb + b];
-                all[col] += x;
-                if (b < static_cast<int>(blockIdx.x)) before[col] += x;
-            }
-        }
-        const int lane = lane_id(), w = threadIdx.x >> 6;
-#pragma unroll
-        for (int col = 0; col < kCols; ++col) {
-            const uint32_t s0 = wave_sum(before[col]);
-            const uint32_t s1 = wave_sum(all[col]);
-            if (lane == 0) {
-                s_red[col][w] = s0;
-                s_red[kCols + col][w] = s1;
-            }
-        }
-        __syncthreads();
-        if (threadIdx.x < 2 * kCols) {
-            uint32_t s = 0;
-            for (int i = 0; i < kClassifyThreads / 64; ++i) s += s_red[threadIdx.x][i];
-            if (threadIdx.x < kCols) s_off[threadIdx.x] = s;
-            else s_tot[threadIdx.x - kCols] = s;
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        // the WAVE buckets follow one another in the WAVE list, largest degrees first
-        uint32_t run = 0;
-        for (int c = 0; c < kCats; ++c) {
-            const bool wave = cat_class(c) == kWave;
-            s_base[c] = wave ? run : 0u;
-            if (wave) run += s_tot[1 + c];
-        }
-    }
-    if (blockIdx.x == 0 && threadIdx.x < kCols) {
-        const uint32_t total = s_tot[threadIdx.x];
-        if (!pre_scanned) a.totals[threadIdx.x] = total;
-        if (threadIdx.x == 0) {
-            a.blk_indptr[F] = static_cast<int32_t>(total);
-            *a.d_E = total;
-            if (static_cast<int64_t>(total) > a.E_cap) set_status(a.status, GNN_ERR_CAPACITY);
-        }
-    }
-    __syncthreads();
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kClassifyTile +
-                         static_cast<int64_t>(threadIdx.x) * kClassifyItems;
-    int32_t pk[kClassifyItems];
-    uint32_t csum = 0;
-    uint64_t kc0 = 0, kc1 = 0;  // categories 0..3 in 16-bit counters, 4..8 in 12-bit counters
-#pragma unroll
-    for (int q = 0; q < kClassifyItems; ++q) {
-        const int64_t i = base + q;
-        pk[q] = i < F ? a.packed[i] : -1;
-        if (pk[q] >= 0) {
-            csum += static_cast<uint32_t>(pk[q] >> 4);
-            const int cat = pk[q] & 15;
+            if (a.inv_mask) a.inv_mask[i] = 0u;
+            cq[q] = c;
+            catq[q] = cat;
+            csum += static_cast<uint32_t>(c);
             if (cat < 4) kc0 += 1ull << (16 * cat);
             else kc1 += 1ull << (12 * (cat - 4));
         }
@@ -238,14 +150,40 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a
     uint32_t coff = block_exclusive_scan<uint32_t, kClassifyThreads>(csum, &ctot, sm_c);
     uint64_t koff0 = block_exclusive_scan<uint64_t, kClassifyThreads>(kc0, &ktot0, sm_k0);
     uint64_t koff1 = block_exclusive_scan<uint64_t, kClassifyThreads>(kc1, &ktot1, sm_k1);
-    coff += s_off[0];
+    if (threadIdx.x < 64) {
+        const int lane = lane_id();
+        uint32_t before = 0;
+        if (tile == 0) {
+            if (lane == 0) lb_publish(&a.lb.words[0], kLbInclusive, ctot);
+        } else {
+            if (lane == 0) lb_publish(&a.lb.words[tile], kLbAggregate, ctot);
+            before = lb_exclusive(a.lb.words, tile);
+            if (lane == 0) lb_publish(&a.lb.words[tile], kLbInclusive, before + ctot);
+        }
+        if (lane < kCats) {
+            const uint32_t n = cat_count(ktot0, ktot1, lane);
+            s_base[lane] = n ? atomicAdd(&a.totals[1 + lane], n) : 0u;
+        }
+        if (lane == 0) {
+            s_prefix = before;
+            if (tile == last) {
+                const uint32_t total = before + ctot;
+                a.blk_indptr[F] = static_cast<int32_t>(total);
+                *a.d_E = total;
+                a.totals[0] = total;
+                if (static_cast<int64_t>(total) > a.E_cap) set_status(a.status, GNN_ERR_CAPACITY);
+            }
+        }
+    }
+    __syncthreads();
+    coff += s_prefix;
 #pragma unroll
     for (int q = 0; q < kClassifyItems; ++q) {
-        if (pk[q] < 0) continue;
+        const int32_t cat = catq[q];
+        if (cat < 0) continue;
         const int64_t i = base + q;
-        const int32_t cat = pk[q] & 15;
         a.blk_indptr[i] = static_cast<int32_t>(coff);
-        coff += static_cast<uint32_t>(pk[q] >> 4);
+        coff += static_cast<uint32_t>(cq[q]);
         uint32_t r;
         if (cat < 4) {
             r = static_cast<uint32_t>((koff0 >> (16 * cat)) & 0xFFFF);
@@ -254,13 +192,23 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_scatter(HopArgs a
             r = static_cast<uint32_t>((koff1 >> (12 * (cat - 4))) & 0xFFF);
             koff1 += 1ull << (12 * (cat - 4));
         }
-        a.lists[static_cast<int64_t>(cat_class(cat)) * a.F_cap + s_base[cat] + s_off[1 + cat] + r] =
-            static_cast<int32_t>(i);
+        a.lists[static_cast<int64_t>(cat) * a.F_cap + s_base[cat] + r] = static_cast<int32_t>(i);
     }
 }
 
 // Longest row the sampler handles (positions are int32).
 constexpr int64_t kMaxRowLength = 0x7FFFFFFFLL;
+
+// Output e of the block gets neighbour id `id`; with a union bitmap to accumulate (a super-batch
+// relabelled in the union's positions), the id's bit is set too.  The atomic's result is unused,
+// so the store is posted and the lane does not wait for it.
+__device__ __forceinline__ void emit_id(const HopArgs &a, int64_t e, int32_t id) {
+    if (e >= 0 && e < a.E_cap) a.blk_gid[e] = id;
+    if (a.mark != nullptr) {
+        if (id >= 0 && id < a.num_nodes) atomicOr(&a.mark[id >> 5], 1u << (id & 31));
+        else set_status(a.status, GNN_ERR_OUT_OF_RANGE);
+    }
+}
 
 // ---- threshold selection helpers ----------------------------------------------------------------
 //
@@ -422,7 +370,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         const uint64_t m = __ballot(sel) & gmask;
         if (sel) {
             const int64_t o = out0 + outc + __popcll(m & below);
-            if (o >= 0 && o < a.E_cap) a.blk_gid[o] = row[jc];
+            emit_id(a, o, row[jc]);
         }
         outc += __popcll(m);
     }
@@ -541,8 +489,7 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
             const int32_t pt = s_pos[t];
             r += (pt < 0) & ((pt & 0x7FFFFFFF) < jc);
         }
-        const int64_t o = out0 + r;
-        if (o >= 0 && o < a.E_cap) a.blk_gid[o] = row[jc];
+        emit_id(a, out0 + r, row[jc]);
     }
     __syncthreads();
 }
@@ -559,18 +506,41 @@ static_assert(kWavesPerBlock * kWaveCap == kBlockCap, "WAVE slots fill the share
 static_assert(kWavesPerBlock * (64 / kGroupLanes) * kGroupCap == kBlockCap,
               "GROUP slots fill the shared LDS arrays");
 
+// Zeroes the sub-batch bitmaps (and byte maps) that the hop's distribution marks next; the
+// sampler's grid does it, hidden under its own hashing.
+__device__ __forceinline__ void zero_sub_maps(const HopArgs &a) {
+    if (a.zero_words == nullptr) return;
+    int64_t bound = *a.zero_da + *a.zero_db;
+    bound = bound < 0 ? 0 : (bound > 32 * a.zero_stride ? 32 * a.zero_stride : bound);
+    const int64_t words = (bound + 31) >> 5;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int64_t t = t0; t < words * a.zero_g; t += stride) {
+        const int64_t g = t / words;
+        a.zero_words[g * a.zero_stride + (t - g * words)] = 0u;
+    }
+    if (a.zero_bytes != nullptr) {   // 8 words of bytes per bitmap word
+        const int64_t bw = 8 * words;
+        for (int64_t t = t0; t < bw * a.zero_g; t += stride) {
+            const int64_t g = t / bw;
+            a.zero_bytes[g * 8 * a.zero_stride + (t - g * bw)] = 0u;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t nb_block,
                                                          int32_t nb_wave, int32_t nb_group) {
     __shared__ uint64_t s_key[kBlockCap];
     __shared__ int32_t s_pos[kBlockCap];
     __shared__ uint32_t s_cnt;
+    zero_sub_maps(a);
     const int lane = lane_id();
     const int wv = static_cast<int>(threadIdx.x >> 6);
     const uint64_t below = (1ull << lane) - 1ull;
     int bid = static_cast<int>(blockIdx.x);
     if (bid < nb_block) {
         const int64_t n = class_total(a.totals, kBlock);
-        const int32_t *list = a.lists + static_cast<int64_t>(kBlock) * a.F_cap;
+        const int32_t *list = a.lists + static_cast<int64_t>(kCatBlock) * a.F_cap;
         for (int64_t item = bid; item < n; item += nb_block)
             sample_node_block(a, list[item], s_key, s_pos, &s_cnt);
         return;
@@ -580,13 +550,12 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         // The list is ordered by degree bucket, largest first; wavefront w takes item w of even
         // rounds and item W-1-w of odd ones (W wavefronts), which pairs large rows with small.
         const int64_t n = class_total(a.totals, kWave);
-        const int32_t *list = a.lists + static_cast<int64_t>(kWave) * a.F_cap;
         const int64_t W = static_cast<int64_t>(nb_wave) * kWavesPerBlock;
         const int64_t w = static_cast<int64_t>(bid) * kWavesPerBlock + wv;
         for (int64_t r0 = 0, round = 0; r0 < n; r0 += W, ++round) {
             const int64_t item = r0 + ((round & 1) ? W - 1 - w : w);
             if (item < n)
-                sample_node_lanes<64, kWaveCap>(a, list[item], s_key + wv * kWaveCap,
+                sample_node_lanes<64, kWaveCap>(a, wave_item(a, item), s_key + wv * kWaveCap,
                                                 s_pos + wv * kWaveCap, lane, ~0ull, below);
         }
         return;
@@ -618,8 +587,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - st;
         const int64_t o = a.blk_indptr[i];
         const int32_t *row = adj_row(a, v, st);
-        for (int64_t j = 0; j < deg; ++j)
-            if (o + j >= 0 && o + j < a.E_cap) a.blk_gid[o + j] = row[j];
+        for (int64_t j = 0; j < deg; ++j) emit_id(a, o + j, row[j]);
     }
 }
 
@@ -654,10 +622,6 @@ __global__ __launch_bounds__(256) void k_adj_fill(const void *indptr, int32_t ib
 
 // ---- launchers ---------------------------------------------------------------------------------
 
-// Blocks of the classification at or below which each scatter workgroup sums the partials of the
-// workgroups before it (one launch fewer than a separate scan).
-constexpr int kSelfScanMaxBlocks = 512;
-
 // Words the classification grid clears itself (a few per thread); a larger clear region gets a
 // fill kernel of its own, sized for it.
 constexpr int64_t kClassifyClearPerThread = 16;
@@ -668,10 +632,7 @@ hipError_t launch_classify(HopArgs a, hipStream_t s) {
         if (e != hipSuccess) return e;
         a.clear_n = 0;
     }
-    hipLaunchKernelGGL(k_classify_count, dim3(a.nb), dim3(kClassifyThreads), 0, s, a);
-    const int pre = a.nb > kSelfScanMaxBlocks ? 1 : 0;
-    if (pre) hipLaunchKernelGGL(k_classify_scan, dim3(1), dim3(1024), 0, s, a);
-    hipLaunchKernelGGL(k_classify_scatter, dim3(a.nb), dim3(kClassifyThreads), 0, s, a, pre);
+    hipLaunchKernelGGL(k_classify, dim3(a.nb), dim3(kClassifyThreads), 0, s, a);
     return hipGetLastError();
 }
 

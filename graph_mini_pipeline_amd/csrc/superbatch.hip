@@ -8,14 +8,15 @@
 // Here the G sub-batches of a super-batch share one batch seed, so the sample of node v at hop l
 // is the same in every sub-batch whose frontier holds v.  The union U_l of the G frontiers is
 // classified and sampled once.  (With full-range sub-batch bitmaps, a destination's union row is
-// found by its rank in the union bitmap and only the ids are copied; the compact relabel follows.)  Its sampled ids and U_l itself are relabelled into
-// U_{l+1} = U_l + sampled ids, which is the union of the G node sets V_l, so every id of every
-// sub-batch's block has a position in U_{l+1}.  Each sub-batch then takes, for destination i at
-// union position r = upos[i], the union row [u_indptr[r], u_indptr[r+1]): an exclusive scan of
-// the row lengths within the sub-batch gives its block indptr, and the row's ids and their
-// U_{l+1} positions are copied.  The sub-batch's own relabel then runs on those positions
-// (a bitmap of |U_{l+1}| bits instead of one over every node id), and its result is exactly that
-// of a separate run.
+// found by its rank in the union bitmap and only the ids are copied; the compact relabel follows.)
+// The sampler sets the bits of its sampled ids in the node-id bitmap that already holds U_l, whose
+// set bits are then U_{l+1} = U_l + sampled ids, the union of the G node sets V_l, so every id of
+// every sub-batch's block has a position in U_{l+1}: its rank in that bitmap.  Each sub-batch
+// then takes, for destination i at union position r = upos[i], the union row [u_indptr[r],
+// u_indptr[r+1]): an exclusive scan of the row lengths within the sub-batch gives its block
+// indptr, the row's ids are copied with their U_{l+1} positions, and those positions are marked
+// in the sub-batch's own relabel bitmap (|U_{l+1}| bits instead of one over every node id), whose
+// result is exactly that of a separate run.
 #include "common.hpp"
 
 namespace gnnmb {
@@ -29,6 +30,30 @@ __device__ __forceinline__ int find_sub(const DistArgs &a, int t) {
 __device__ __forceinline__ int32_t union_rank(const DistArgs &a, int32_t v) {
     const uint32_t w = a.bm0[v >> 5];
     return static_cast<int32_t>(a.wprefix0[v >> 5] + __popc(w & ((1u << (v & 31)) - 1u)));
+}
+
+// Position in U_{l+1} of node id v (compact relabel): its rank in U_{l+1}'s node-id bitmap, or -1
+// for an id outside the bitmap or not in it (only after an error already reported).
+__device__ __forceinline__ int32_t next_rank(const DistArgs &a, int32_t v) {
+    if (v < 0 || v >= a.id_bound) return -1;
+    const uint32_t w = a.bm1[v >> 5];
+    const uint32_t bit = 1u << (v & 31);
+    if (!(w & bit)) return -1;
+    return static_cast<int32_t>(a.wprefix1[v >> 5] + __popc(w & (bit - 1u)));
+}
+
+// Position p of sub-batch g's relabel (compact relabel), marked as k_mark marks it: a byte when the
+// byte maps exist, else the bitmap bit; with the duplicate check, the bit with the returned word.
+__device__ __forceinline__ void mark_sub(const DistArgs &a, int g, int32_t p, bool dup) {
+    const uint32_t bit = 1u << (p & 31);
+    uint32_t *word = a.mark_words + static_cast<int64_t>(g) * a.mark_stride + (p >> 5);
+    if (a.mark_bytes) a.mark_bytes[static_cast<int64_t>(g) * 32 * a.mark_stride + p] = 1;
+    if (dup) {
+        const uint32_t old = atomicOr(word, bit);
+        if (old & bit) set_status(a.status, GNN_ERR_INVALID_ARG);   // a seed given twice
+    } else if (!a.mark_bytes) {
+        atomicOr(word, bit);   // result unused: posted
+    }
 }
 
 // Destination i of a sub-batch: its union row [lo, lo + c) and (compact relabel) its position in
@@ -60,33 +85,15 @@ __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, i
     l1 = l1 < l0 ? l0 : (l1 > a.uE_cap ? a.uE_cap : l1);
     lo = l0;
     c = static_cast<int32_t>(l1 - l0);
-    if (a.umap) next_pos = a.umap[r];
+    if (a.Ul) next_pos = next_rank(a, a.Ul[r]);
 }
 
-// Tiles of kDistTile destinations: wavefront 0 handles one destination per lane.  The whole grid
-// first zeroes the live words of the sub-batch bitmaps that the sub-batch relabel marks next.
-// The grid is capped (kDistMaxGrid) and workgroups stride over the tiles, which are sized by the
+// Tiles of kDistTile destinations: wavefront 0 handles one destination per lane (and, with the
+// compact relabel, marks its position in U_{l+1} for the sub-batch relabel).  The grid is capped (kDistMaxGrid) and workgroups stride over the tiles, which are sized by the
 // frontier bounds: tiles past a sub-batch's actual destinations are skipped, not dispatched.
 __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
-    if (a.clear_ptr) {
-        const int64_t n1 = load_count(a.d_U1, a.U1_cap);
-        const int64_t words = (n1 + 31) >> 5;
-        const int64_t total = words * a.G;
-        for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
-             t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-            const int64_t g = t / words;
-            a.clear_ptr[g * a.clear_stride + (t - g * words)] = 0u;
-        }
-        if (a.clear_bytes) {   // 8 words of bytes per bitmap word
-            const int64_t bw = 8 * words;
-            for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < bw * a.G;
-                 t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-                const int64_t g = t / bw;
-                a.clear_bytes[g * 8 * a.clear_stride + (t - g * bw)] = 0u;
-            }
-        }
-    }
     if (threadIdx.x >= kDistTile) return;
+    const int64_t n1 = a.mark_words ? load_count(a.d_U1, a.U1_cap) : 0;   // |U_{l+1}|
     for (int t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
         const int sg = find_sub(a, t);
         const DistSub &S = a.sub[sg];
@@ -99,7 +106,11 @@ __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
         if (i < F) {
             union_row(a, S, i, lo, c, np, r);
             if (S.f_pos) S.f_pos[i] = np;
-            if (a.inv && r >= 0) a.inv[static_cast<int64_t>(r) * a.G + sg] = static_cast<int32_t>(i + 1);
+            if (a.mark_words && np >= 0 && np < n1) mark_sub(a, sg, np, a.mark_dup != 0);
+            if (a.inv && r >= 0) {
+                a.inv[static_cast<int64_t>(r) * a.G + sg] = static_cast<int32_t>(i + 1);
+                atomicOr(&a.inv_mask[r], 1u << sg);
+            }
         }
         const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
         if (threadIdx.x == 0) a.bsum[t] = sum;
@@ -111,8 +122,10 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
     __shared__ uint32_t s_off, s_tot;
     __shared__ uint32_t s_item_off[kDistTile + 1];
     __shared__ int64_t s_item_lo[kDistTile];
+    const int64_t n1 = a.mark_words ? load_count(a.d_U1, a.U1_cap) : 0;   // |U_{l+1}|
     for (int t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
-        const DistSub &S = a.sub[find_sub(a, t)];
+        const int sg = find_sub(a, t);
+        const DistSub &S = a.sub[sg];
         const int lt = t - S.tile0;
         const int64_t F = load_count(S.d_F, S.F_cap);
         // tiles past the actual destinations have nothing to place (tile 0 still writes the totals)
@@ -169,7 +182,11 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
             const int64_t src = s_item_lo[lo_i] + (p - s_item_off[lo_i]);
             if (dst < S.E_cap) {
                 S.blk_gid[dst] = a.u_gid[src];
-                if (S.e_pos) S.e_pos[dst] = a.u_pos[src];
+                if (S.e_pos) {
+                    const int32_t p = next_rank(a, a.u_gid[src]);
+                    S.e_pos[dst] = p;
+                    if (a.mark_words && p >= 0 && p < n1) mark_sub(a, sg, p, false);
+                }
             }
         }
         __syncthreads();   // the shared arrays are rewritten by the next tile

@@ -28,6 +28,10 @@
  *    contents are unspecified.  No exception crosses the ABI and the library never aborts.
  *  - Node ids are int32 (num_nodes < 2^31).  Block-local sizes are int32.
  *  - Concurrent calls on different streams are safe when their workspaces are disjoint.
+ *  - Fault injection (for tests of callers' error paths): the environment variable GNN_FAULT,
+ *    read once per process, may list "alloc" (every set-up allocation of a feature store cache
+ *    or an adjacency cache fails before it is made) and "launch" (every call that enqueues work
+ *    fails after its argument checks, before enqueueing anything); both return GNN_ERR_HIP.
  */
 #ifndef GNNMB_H
 #define GNNMB_H

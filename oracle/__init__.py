@@ -41,6 +41,18 @@ ORC_OK = 0
 _ERRORS = {-1: "invalid argument", -2: "capacity", -3: "id out of range", -7: "out of memory"}
 
 
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer into `path` (a test
+    loads it in place of liboracle.so through GNNMB_ORACLE_LIB, with the ASan runtime preloaded)."""
+    subprocess.check_call(["gcc", *SANITIZE_FLAGS, "-std=c11", "-Wall", "-Wextra", "-fPIC",
+                           "-shared", "-o", path, _SRC])
+    return path
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (plain -O2, no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
@@ -57,8 +69,10 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build(force=False)
-        L = ctypes.CDLL(_LIB)
+        alt = os.environ.get("GNNMB_ORACLE_LIB")   # another build of oracle.c (sanitized)
+        if not alt:
+            build(force=False)
+        L = ctypes.CDLL(alt or _LIB)
         u64, i64, i32, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
         L.orc_mix64.restype = u64
         L.orc_mix64.argtypes = [u64]

@@ -626,3 +626,123 @@ def test_shared_outer_means(tiny, mode, fanouts, ld):
     for g in range(len(parts)):
         ref = oracle.minibatch(indptr, indices, x, parts[g], fanouts, 808)
         compare_with_oracle(outs[g], ref, cfg.d)
+
+
+# Lists far shorter than the id range are relabelled by one workgroup that sorts them in LDS
+# instead of through a bitmap over every id: these cases take that path (and the last one its
+# largest list), and must equal the oracle like every other relabel.
+@pytest.mark.parametrize("n_keep,n_add,bound,distinct",
+                         [(0, 0, 1 << 20, None), (1, 0, 1 << 20, None), (300, 2000, 10_000_000, None),
+                          (700, 7000, 50_000_000, 50), (2000, 6000, 1 << 30, None),
+                          (5000, 11384, 111_000_000, None)])
+def test_unique_relabel_short_lists(n_keep, n_add, bound, distinct):
+    rng = np.random.default_rng(n_add + 17)
+    keep = rng.choice(bound, size=n_keep, replace=False).astype(np.int32) if n_keep else np.zeros(0, np.int32)
+    if distinct:   # many repeats of few ids (a hub sampled by many destinations)
+        pool = rng.choice(bound, size=distinct, replace=False)
+        add = rng.choice(pool, size=n_add).astype(np.int32)
+    else:
+        add = rng.integers(0, bound, size=n_add).astype(np.int32)
+    dev = lambda a: torch.from_numpy(a).cuda() if a.size else torch.zeros(0, dtype=torch.int32, device="cuda")
+    uniq = torch.full((n_keep + n_add + 1,), -7, dtype=torch.int32, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int64, device="cuda")
+    add_lid = torch.empty(max(n_add, 1), dtype=torch.int32, device="cuda")[:n_add]
+    keep_lid = torch.empty(max(n_keep, 1), dtype=torch.int32, device="cuda")[:n_keep]
+    ws = torch.empty(gm.gnn_relabel_workspace_size(bound), dtype=torch.uint8, device="cuda")
+    gm.gnn_unique_relabel(dev(keep), dev(add), bound, uniq, nu, add_lid, keep_lid, ws)
+    assert gm.gnn_read_device_status(ws) == gm.GNN_OK
+    u, lid, dl = oracle.relabel(keep, add)
+    assert nu.item() == len(u)
+    assert np.array_equal(uniq[:len(u)].cpu().numpy(), u)
+    assert np.array_equal(add_lid.cpu().numpy(), lid)
+    assert np.array_equal(keep_lid.cpu().numpy(), dl)
+
+
+@pytest.fixture(scope="module")
+def sparse_wide():
+    """2M nodes, few edges (degrees 0..7, repeats and self-loops allowed): batches of a few dozen
+    seeds have lists far shorter than the id range, so their relabels sort."""
+    rng = np.random.default_rng(2024)
+    n = 2_000_000
+    deg = rng.integers(0, 8, size=n)
+    indptr = np.concatenate([[0], np.cumsum(deg)]).astype(np.int32)
+    indices = rng.integers(0, n, size=int(indptr[-1])).astype(np.int32)
+    x = rng.standard_normal((n, 8)).astype(np.float32)
+    return indptr, indices, x
+
+
+@pytest.mark.parametrize("mode", [None, "compact"])
+def test_short_list_relabel_in_minibatch(sparse_wide, mode):
+    """gnn_minibatch on the wide sparse graph: one batch (every hop's relabel sorts), and a
+    super-batch of three overlapping sub-batches relabelled in the union's positions (the seeds'
+    union sorts and leaves its bits in the node-id bitmap for the later hops)."""
+    indptr, indices, x = sparse_wide
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    rng = np.random.default_rng(5)
+    seeds = rng.choice(len(indptr) - 1, size=96, replace=False).astype(np.int32)
+    fanouts = [4, 3]
+    seed64 = gm.gnn_batch_seed(11, 3)
+    if mode is None:
+        outs, st = run_minibatch(dg, fs, seeds[:64], fanouts, seed64)
+        parts = [seeds[:64]]
+    else:
+        sb = np.concatenate([seeds[:40], seeds[20:70], seeds[60:96]])
+        ptr = [0, 40, 90, 126]
+        outs, st = run_minibatch(dg, fs, sb, fanouts, seed64, gm.Options(superbatch=mode), group_ptr=ptr)
+        parts = [sb[ptr[g]:ptr[g + 1]] for g in range(3)]
+    assert st == gm.GNN_OK
+    for out, sd in zip(outs, parts):
+        ref = oracle.minibatch(indptr, indices, x, sd, fanouts, seed64)
+        compare_with_oracle(out, ref, x.shape[1])
+
+
+def test_short_list_relabel_reports_bad_seeds(sparse_wide):
+    indptr, indices, x = sparse_wide
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    seeds = np.array([5, 77, 123456, 77, 9], dtype=np.int32)        # 77 twice
+    _, st = run_minibatch(dg, fs, seeds, [3, 2], gm.gnn_batch_seed(0, 0))
+    assert st == gm.GNN_ERR_INVALID_ARG
+    seeds = np.array([5, 77, len(indptr) - 1, 9], dtype=np.int32)   # one past the last node
+    _, st = run_minibatch(dg, fs, seeds, [3, 2], gm.gnn_batch_seed(0, 0))
+    assert st == gm.GNN_ERR_OUT_OF_RANGE
+
+
+_FAULT_CHILD = r'''
+import sys
+sys.path.insert(0, %r)
+import numpy as np, torch
+import graph_mini_pipeline_amd as gm, synth
+from tests.gpu_util import device_graph, device_table, run_minibatch
+cfg = synth.CONFIGS["tiny"]
+g = synth.build_graph(cfg)
+x = torch.empty(cfg.num_nodes, cfg.d, dtype=torch.float32)
+synth.make_features(cfg, x)
+dg = device_graph(g.indptr.numpy(), g.indices.numpy())
+fs = gm.gnn_feature_store_create(device_table(x.numpy(), cfg.d), cfg.d)
+seeds = synth.epoch_seed_order(cfg).numpy()[:64]
+try:
+    _, st = run_minibatch(dg, fs, seeds, cfg.fanouts, gm.gnn_batch_seed(0, 0))
+    print("status", st)
+except gm.GnnError as e:
+    print("raised", e.status)
+'''
+
+
+@pytest.mark.parametrize("fault,want", [(None, "status 0"), ("launch", "raised %d" % gm.GNN_ERR_HIP)])
+def test_fault_injection_in_a_child_process(fault, want):
+    """GNN_FAULT=launch makes a mini-batch that otherwise succeeds fail with GNN_ERR_HIP before any
+    work is enqueued (the child process reads the variable; this process is not affected)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ)
+    env.pop("GNN_FAULT", None)
+    if fault:
+        env["GNN_FAULT"] = fault
+    r = subprocess.run([sys.executable, "-c", _FAULT_CHILD % root], env=env, capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == want

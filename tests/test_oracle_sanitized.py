@@ -1,0 +1,35 @@
+"""The oracle under AddressSanitizer and UndefinedBehaviorSanitizer (CPU): oracle.c is built with
+both and the oracle's pin tests run against that build in a subprocess with the ASan runtime
+preloaded; any out-of-bounds access, use after free or undefined behaviour aborts the run."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _runtime(name):
+    p = subprocess.run(["gcc", f"-print-file-name={name}"], capture_output=True, text=True).stdout.strip()
+    return p if os.path.isabs(p) and os.path.exists(p) else None
+
+
+@pytest.mark.timeout(600)
+def test_oracle_pins_under_asan_and_ubsan(tmp_path):
+    asan = _runtime("libasan.so")
+    if asan is None:
+        pytest.skip("no ASan runtime for gcc on this host")
+    lib = oracle.build_sanitized(str(tmp_path / "liboracle_san.so"))
+    env = dict(os.environ, GNNMB_ORACLE_LIB=lib, LD_PRELOAD=asan,
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=550)
+    tail = (r.stdout + r.stderr)[-3000:]
+    assert r.returncode == 0, tail
+    assert "passed" in r.stdout and "ERROR: AddressSanitizer" not in r.stderr, tail
+    assert "runtime error" not in r.stderr, tail
