@@ -17,7 +17,7 @@ from . import _abi
 from ._abi import (GNN_ERR_CAPACITY, GNN_ERR_HIP, GNN_ERR_INTERNAL, GNN_ERR_INVALID_ARG,  # noqa
                    GNN_ERR_OUT_OF_RANGE, GNN_ERR_UNSUPPORTED, GNN_MAX_HOPS, GNN_OK, GNN_SYNC,
                    GNN_SUPERBATCH_COMPACT, GNN_SUPERBATCH_FULL, GNN_GATHER_BATCHED,
-                   GNN_NOALLOC_MAX_IDS, GNN_NOALLOC_SCRATCH_BYTES,
+                   GNN_NOALLOC_MAX_IDS, GNN_NOALLOC_SCRATCH_BYTES, GNN_RELABEL_SORT, GNN_RELABEL_BITMAP,
                    GNN_GATHER_INTERLEAVED,
                    GNN_TIMER_STAGES)
 
@@ -84,6 +84,7 @@ class Options:
     sync: bool = False
     superbatch: str = "auto"    # super-batch relabel: "auto", "full" or "compact"
     gather: str = "auto"        # gather and outermost mean: "auto", "interleaved" or "batched"
+    relabel: str = "auto"       # short id lists: "auto", "sort" (whenever eligible) or "bitmap"
 
     def c(self) -> _abi.gnn_options:
         o = _abi.gnn_options()
@@ -95,7 +96,11 @@ class Options:
         gmodes = {"auto": 0, "interleaved": GNN_GATHER_INTERLEAVED, "batched": GNN_GATHER_BATCHED}
         if self.gather not in gmodes:
             raise ValueError(f"gather must be one of {sorted(gmodes)}")
-        o.flags = (GNN_SYNC if self.sync else 0) | modes[self.superbatch] | gmodes[self.gather]
+        rmodes = {"auto": 0, "sort": GNN_RELABEL_SORT, "bitmap": GNN_RELABEL_BITMAP}
+        if self.relabel not in rmodes:
+            raise ValueError(f"relabel must be one of {sorted(rmodes)}")
+        o.flags = (GNN_SYNC if self.sync else 0) | modes[self.superbatch] | gmodes[self.gather] | \
+            rmodes[self.relabel]
         return o
 
 

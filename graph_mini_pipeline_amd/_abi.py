@@ -18,6 +18,8 @@ GNN_SUPERBATCH_FULL = 2
 GNN_SUPERBATCH_COMPACT = 4
 GNN_GATHER_INTERLEAVED = 8
 GNN_GATHER_BATCHED = 16
+GNN_RELABEL_SORT = 32
+GNN_RELABEL_BITMAP = 64
 GNN_NOALLOC_MAX_IDS = 1 << 26
 GNN_NOALLOC_SCRATCH_BYTES = (16 << 20) + (64 << 10)
 

@@ -110,6 +110,7 @@ struct Workspace {
     uint64_t *arena;
     int64_t arena_words;
     mutable int64_t arena_used = 0;
+    int32_t relabel_force = 0;   // RelabelArgs::force of every relabel of the call
     // A slice of `tiles` look-back words followed by `counters` 32-bit ticket counters; NULL words
     // when the arena is exhausted (the bound of carve() covers every launch sequence, so this
     // does not happen).
@@ -137,6 +138,7 @@ gnn_status classify_launch(HopArgs h, const Workspace &w, hipStream_t s) {
 
 // A relabel launch sequence with its look-back words taken from the call's arena.
 gnn_status relabel_launch(RelabelArgs r, const Workspace &w, hipStream_t s) {
+    r.force = w.relabel_force;
     r.lb = w.take_lb(relabel_lb_words(r), r.nbm);
     if (r.lb.words == nullptr) return GNN_ERR_INTERNAL;
     return launch_relabel(r, s) == hipSuccess ? GNN_OK : GNN_ERR_HIP;
@@ -288,8 +290,13 @@ gnn_status read_opts(const gnn_options *o, Opts *out) {
     if (r.group_max < 1 || r.wave_max < r.group_max) return GNN_ERR_INVALID_ARG;
     if ((r.flags & GNN_SUPERBATCH_FULL) && (r.flags & GNN_SUPERBATCH_COMPACT)) return GNN_ERR_INVALID_ARG;
     if ((r.flags & GNN_GATHER_INTERLEAVED) && (r.flags & GNN_GATHER_BATCHED)) return GNN_ERR_INVALID_ARG;
+    if ((r.flags & GNN_RELABEL_SORT) && (r.flags & GNN_RELABEL_BITMAP)) return GNN_ERR_INVALID_ARG;
     *out = r;
     return GNN_OK;
+}
+
+int32_t relabel_force(const Opts &o) {
+    return (o.flags & GNN_RELABEL_SORT) ? 1 : ((o.flags & GNN_RELABEL_BITMAP) ? 2 : 0);
 }
 
 gnn_status check_graph(const gnn_graph *g) {
@@ -818,7 +825,8 @@ gnn_status gnn_sample_khop(const gnn_graph *g, const int32_t *seeds, int64_t n_s
     const Workspace need = carve(out->caps, g->num_nodes, 1, kSuperNone, nullptr);
     if (ws_bytes < need.bytes) return GNN_ERR_CAPACITY;
     if (fault(kFaultLaunch)) return GNN_ERR_HIP;
-    const Workspace w = carve(out->caps, g->num_nodes, 1, kSuperNone, ws);
+    Workspace w = carve(out->caps, g->num_nodes, 1, kSuperNone, ws);
+    w.relabel_force = relabel_force(o);
     hipStream_t s = static_cast<hipStream_t>(stream);
     GNN_TRY_HIP(launch_fill_u32(reinterpret_cast<uint32_t *>(w.status), w.cleared_bytes() / 4, 0u, s));
     const int32_t *sp[1] = {seeds};
@@ -1178,7 +1186,8 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
     // node's sampled neighbours, hence its mean, are the same in each).
     const bool from_table = batched && !fs->on_host && fs->slot == nullptr;
     const bool shared_means = from_table && group > 1;
-    const Workspace w = carve(mc, g->num_nodes, group, mode, ws);
+    Workspace w = carve(mc, g->num_nodes, group, mode, ws);
+    w.relabel_force = relabel_force(o);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t *ev = nullptr;
     if (timer) {

@@ -294,6 +294,7 @@ struct RelabelArgs {
                               // bitmap (which it otherwise leaves untouched)
     int32_t bitmap_read_after; // later kernels rank ids in the bitmap and its word prefixes: the
                                // bitmap path is required
+    int32_t force;            // 0: the path by size; 1: sort whenever eligible; 2: the bitmap
 };
 
 // Short lists are relabelled by one workgroup that sorts them in LDS (relabel.hip) instead of

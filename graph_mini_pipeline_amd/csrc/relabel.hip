@@ -699,11 +699,16 @@ int64_t sort_capacity() {
     return cached[dev];
 }
 
-// Bitmap words per list entry above which sorting the lists beats the passes over the bitmap.
-constexpr int64_t kSortWordsPerKey = 1024;
+// The sort path pays when its cost, ~42 us + ~7.7 ns per key (one workgroup), is below the
+// bitmap path's, ~25 us + ~4.6 us per million bitmap words (passes spread over the chip):
+// measured on MI355X with gnn_unique_relabel over lists of 256 .. 16384 ids and id ranges of 2^20
+// .. 2^30, both paths forced.  Sort when the bitmap has at least kSortBaseWords plus
+// kSortWordsPerKey words per listed id (short lists over id ranges of ~130M ids and more).
+constexpr int64_t kSortBaseWords = 3700000;
+constexpr int64_t kSortWordsPerKey = 1700;
 
 bool relabel_sorts(const RelabelArgs &a) {
-    if (a.bitmap_read_after) return false;
+    if (a.force == 2 || a.bitmap_read_after) return false;
     if (a.nbm != 1 || a.bytes || a.id_map || a.d_bound || a.out[0].pos) return false;
     if (a.id_bound > (1LL << 30)) return false;   // keys id << 1 | flag below 2^31
     if (a.nlist < 1 || a.nlist > 2 * kMaxGroup) return false;
@@ -713,7 +718,8 @@ bool relabel_sorts(const RelabelArgs &a) {
         n += a.list[l].cap;
     }
     if (n > sort_capacity()) return false;
-    return a.W >= kSortWordsPerKey * (n > 1 ? n : 1);
+    if (a.force == 1) return true;
+    return a.W >= kSortBaseWords + kSortWordsPerKey * n;
 }
 
 // Tiles per bitmap at or below which k_emit_tiles computes its own offsets.

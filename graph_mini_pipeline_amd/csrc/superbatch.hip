@@ -36,10 +36,10 @@ __device__ __forceinline__ int32_t union_rank(const DistArgs &a, int32_t v) {
 // for an id outside the bitmap or not in it (only after an error already reported).
 __device__ __forceinline__ int32_t next_rank(const DistArgs &a, int32_t v) {
     if (v < 0 || v >= a.id_bound) return -1;
-    const uint32_t w = a.bm1[v >> 5];
+    const uint32_t w = a.bm1[v >> 5];          // both loads issued together
+    const uint32_t pre = a.wprefix1[v >> 5];
     const uint32_t bit = 1u << (v & 31);
-    if (!(w & bit)) return -1;
-    return static_cast<int32_t>(a.wprefix1[v >> 5] + __popc(w & (bit - 1u)));
+    return (w & bit) ? static_cast<int32_t>(pre + __popc(w & (bit - 1u))) : -1;
 }
 
 // Position p of sub-batch g's relabel (compact relabel), marked as k_mark marks it: a byte when the
@@ -61,7 +61,7 @@ __device__ __forceinline__ void mark_sub(const DistArgs &a, int g, int32_t p, bo
 // already reported by the union marking).
 __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, int64_t i,
                                           int64_t &lo, int32_t &c, int32_t &next_pos,
-                                          int32_t &r) {
+                                          int32_t &r, bool want_next = true) {
     lo = 0;
     c = 0;
     next_pos = -1;
@@ -85,22 +85,25 @@ __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, i
     l1 = l1 < l0 ? l0 : (l1 > a.uE_cap ? a.uE_cap : l1);
     lo = l0;
     c = static_cast<int32_t>(l1 - l0);
-    if (a.Ul) next_pos = next_rank(a, a.Ul[r]);
+    if (a.Ul && want_next) next_pos = next_rank(a, a.Ul[r]);
 }
 
-// Tiles of kDistTile destinations: wavefront 0 handles one destination per lane (and, with the
-// compact relabel, marks its position in U_{l+1} for the sub-batch relabel).  The grid is capped (kDistMaxGrid) and workgroups stride over the tiles, which are sized by the
+// Tiles of kDistTile destinations: each wavefront takes a tile, one destination per lane (and,
+// with the compact relabel, marks its position in U_{l+1} for the sub-batch relabel).  The grid
+// is capped (kDistMaxGrid) and workgroups stride over the tiles, which are sized by the
 // frontier bounds: tiles past a sub-batch's actual destinations are skipped, not dispatched.
 __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
-    if (threadIdx.x >= kDistTile) return;
+    static_assert(kDistTile == 64, "one destination per lane of a wavefront");
     const int64_t n1 = a.mark_words ? load_count(a.d_U1, a.U1_cap) : 0;   // |U_{l+1}|
-    for (int t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+    const int wv = static_cast<int>(threadIdx.x >> 6);
+    const int lane = lane_id();
+    for (int t = blockIdx.x * 4 + wv; t < a.ntiles; t += gridDim.x * 4) {
         const int sg = find_sub(a, t);
         const DistSub &S = a.sub[sg];
         const int64_t F = load_count(S.d_F, S.F_cap);
         const int64_t i0 = static_cast<int64_t>(t - S.tile0) * kDistTile;
         if (i0 >= F) continue;   // past the destinations: k_dist_scatter reads no sum for it
-        const int64_t i = i0 + threadIdx.x;
+        const int64_t i = i0 + lane;
         int64_t lo;
         int32_t c = 0, np, r;
         if (i < F) {
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
             }
         }
         const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
-        if (threadIdx.x == 0) a.bsum[t] = sum;
+        if (lane == 0) a.bsum[t] = sum;
     }
 }
 
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
             const int64_t i = static_cast<int64_t>(lt) * kDistTile + threadIdx.x;
             int64_t lo = 0;
             int32_t c = 0, np, r;
-            if (i < F) union_row(a, S, i, lo, c, np, r);
+            if (i < F) union_row(a, S, i, lo, c, np, r, false);
             const uint32_t inc = wave_inclusive_scan(static_cast<uint32_t>(c));
             const uint32_t o = inc - static_cast<uint32_t>(c);
             s_item_off[threadIdx.x] = o;
@@ -170,22 +173,41 @@ __global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
             if (i < F) S.blk_indptr[i] = static_cast<int32_t>(s_off + o);
         }
         __syncthreads();
+        // The tile's sampled ids, U rounds of one per thread at a time so that each round's
+        // dependent loads (the id, then its bitmap word and prefix) are in flight together.
         const uint32_t tot = s_tot;
-        for (uint32_t p = threadIdx.x; p < tot; p += blockDim.x) {
-            int lo_i = 0, hi_i = kDistTile;  // last destination whose offset is <= p
-            while (hi_i - lo_i > 1) {
-                const int mid = (lo_i + hi_i) >> 1;
-                if (s_item_off[mid] <= p) lo_i = mid;
-                else hi_i = mid;
+        constexpr int U = 4;
+        for (uint32_t p0 = threadIdx.x; p0 < tot; p0 += U * blockDim.x) {
+            int64_t dst[U], src[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t p = p0 + u * blockDim.x;
+                int lo_i = 0, hi_i = kDistTile;  // last destination whose offset is <= p
+                while (hi_i - lo_i > 1) {
+                    const int mid = (lo_i + hi_i) >> 1;
+                    if (s_item_off[mid] <= p) lo_i = mid;
+                    else hi_i = mid;
+                }
+                dst[u] = static_cast<int64_t>(s_off) + p;
+                src[u] = s_item_lo[lo_i] + (p - s_item_off[lo_i]);
+                ok[u] = p < tot && dst[u] < S.E_cap;
             }
-            const int64_t dst = static_cast<int64_t>(s_off) + p;
-            const int64_t src = s_item_lo[lo_i] + (p - s_item_off[lo_i]);
-            if (dst < S.E_cap) {
-                S.blk_gid[dst] = a.u_gid[src];
-                if (S.e_pos) {
-                    const int32_t p = next_rank(a, a.u_gid[src]);
-                    S.e_pos[dst] = p;
-                    if (a.mark_words && p >= 0 && p < n1) mark_sub(a, sg, p, false);
+            int32_t v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = ok[u] ? a.u_gid[src[u]] : -1;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) S.blk_gid[dst[u]] = v[u];
+            if (S.e_pos) {
+                int32_t q[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) q[u] = ok[u] ? next_rank(a, v[u]) : -1;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (!ok[u]) continue;
+                    S.e_pos[dst[u]] = q[u];
+                    if (a.mark_words && q[u] >= 0 && q[u] < n1) mark_sub(a, sg, q[u], false);
                 }
             }
         }

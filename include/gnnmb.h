@@ -78,6 +78,13 @@ typedef void *gnn_stream; /* hipStream_t */
  *                a node's sampled neighbours and mean are the same in each, and the mean is
  *                stored to the node's row in every sub-batch that holds it. */
 #define GNN_GATHER_INTERLEAVED 8u
+/* How gnn_sample_khop and gnn_minibatch relabel a short id list (results are identical; at most one
+ * may be set; by default the library picks from the sizes, on measured MI355X costs):
+ *   SORT:   one workgroup sorts the list in LDS (radix sort, ballot compaction), when the list
+ *           fits it (at most 16384 ids on gfx950) and no later kernel reads the bitmap;
+ *   BITMAP: always the bitmap over the id range (mark, prefix scan, emit, rank). */
+#define GNN_RELABEL_SORT 32u
+#define GNN_RELABEL_BITMAP 64u
 #define GNN_GATHER_BATCHED 16u
 
 /*

@@ -266,3 +266,24 @@ def test_noalloc_relabel_host_checks():
                                         None) == gm.GNN_ERR_INVALID_ARG
     assert L.gnn_unique_relabel_noalloc(8, 4, 8, None, 4, 0, 8, 8, 8, 8, 8, None,
                                         None) == gm.GNN_ERR_INVALID_ARG
+
+
+def test_relabel_path_flags_exclusive():
+    o = gm.Options(relabel="sort")
+    o.c()
+    with pytest.raises(ValueError):
+        gm.Options(relabel="hash").c()
+    L = gm.lib()
+    caps = gm.gnn_capacity(4, [2], 10)
+    blocks = _abi.gnn_blocks()
+    blocks.caps = caps
+    blocks.counts = 8
+    h = blocks.hop[0]
+    h.indptr = h.gid = h.lid = h.dst_lid = h.nodes = 8
+    g = _abi.gnn_graph()
+    g.num_nodes, g.num_edges, g.indptr, g.indptr_bytes, g.indices = 10, 5, 8, 4, 8
+    fo = (ctypes.c_int32 * 1)(2)
+    both = _abi.gnn_options()
+    both.flags = gm.GNN_RELABEL_SORT | gm.GNN_RELABEL_BITMAP
+    assert L.gnn_sample_khop(ctypes.byref(g), 8, 4, fo, 1, 0, ctypes.byref(blocks), 8, 1 << 20,
+                             ctypes.byref(both), None) == gm.GNN_ERR_INVALID_ARG

@@ -629,12 +629,12 @@ def test_shared_outer_means(tiny, mode, fanouts, ld):
 
 
 # Lists far shorter than the id range are relabelled by one workgroup that sorts them in LDS
-# instead of through a bitmap over every id: these cases take that path (and the last one its
-# largest list), and must equal the oracle like every other relabel.
+# instead of through a bitmap over every id: over 2^30 ids every one of these cases takes that path
+# (the last one with its largest list), and must equal the oracle like every other relabel.
 @pytest.mark.parametrize("n_keep,n_add,bound,distinct",
-                         [(0, 0, 1 << 20, None), (1, 0, 1 << 20, None), (300, 2000, 10_000_000, None),
-                          (700, 7000, 50_000_000, 50), (2000, 6000, 1 << 30, None),
-                          (5000, 11384, 111_000_000, None)])
+                         [(0, 0, 1 << 30, None), (1, 0, 1 << 30, None), (300, 2000, 1 << 30, None),
+                          (700, 7000, 1 << 30, 50), (2000, 6000, 1 << 30, None),
+                          (5000, 11384, 1 << 30, None)])
 def test_unique_relabel_short_lists(n_keep, n_add, bound, distinct):
     rng = np.random.default_rng(n_add + 17)
     keep = rng.choice(bound, size=n_keep, replace=False).astype(np.int32) if n_keep else np.zeros(0, np.int32)
@@ -661,7 +661,7 @@ def test_unique_relabel_short_lists(n_keep, n_add, bound, distinct):
 @pytest.fixture(scope="module")
 def sparse_wide():
     """2M nodes, few edges (degrees 0..7, repeats and self-loops allowed): batches of a few dozen
-    seeds have lists far shorter than the id range, so their relabels sort."""
+    seeds have lists far shorter than the id range."""
     rng = np.random.default_rng(2024)
     n = 2_000_000
     deg = rng.integers(0, 8, size=n)
@@ -671,11 +671,13 @@ def sparse_wide():
     return indptr, indices, x
 
 
+@pytest.mark.parametrize("relabel", ["sort", "bitmap"])
 @pytest.mark.parametrize("mode", [None, "compact"])
-def test_short_list_relabel_in_minibatch(sparse_wide, mode):
-    """gnn_minibatch on the wide sparse graph: one batch (every hop's relabel sorts), and a
-    super-batch of three overlapping sub-batches relabelled in the union's positions (the seeds'
-    union sorts and leaves its bits in the node-id bitmap for the later hops)."""
+def test_short_list_relabel_in_minibatch(sparse_wide, mode, relabel):
+    """gnn_minibatch on the wide sparse graph with either relabel path forced: one batch (every
+    hop's relabel sorts, or none does), and a super-batch of three overlapping sub-batches
+    relabelled in the union's positions (the seeds' union sorts and leaves its bits in the
+    node-id bitmap for the later hops)."""
     indptr, indices, x = sparse_wide
     dg = device_graph(indptr, indices)
     fs = _store(x)
@@ -684,12 +686,13 @@ def test_short_list_relabel_in_minibatch(sparse_wide, mode):
     fanouts = [4, 3]
     seed64 = gm.gnn_batch_seed(11, 3)
     if mode is None:
-        outs, st = run_minibatch(dg, fs, seeds[:64], fanouts, seed64)
+        outs, st = run_minibatch(dg, fs, seeds[:64], fanouts, seed64, gm.Options(relabel=relabel))
         parts = [seeds[:64]]
     else:
         sb = np.concatenate([seeds[:40], seeds[20:70], seeds[60:96]])
         ptr = [0, 40, 90, 126]
-        outs, st = run_minibatch(dg, fs, sb, fanouts, seed64, gm.Options(superbatch=mode), group_ptr=ptr)
+        outs, st = run_minibatch(dg, fs, sb, fanouts, seed64,
+                                 gm.Options(superbatch=mode, relabel=relabel), group_ptr=ptr)
         parts = [sb[ptr[g]:ptr[g + 1]] for g in range(3)]
     assert st == gm.GNN_OK
     for out, sd in zip(outs, parts):
@@ -701,11 +704,12 @@ def test_short_list_relabel_reports_bad_seeds(sparse_wide):
     indptr, indices, x = sparse_wide
     dg = device_graph(indptr, indices)
     fs = _store(x)
+    sort = gm.Options(relabel="sort")
     seeds = np.array([5, 77, 123456, 77, 9], dtype=np.int32)        # 77 twice
-    _, st = run_minibatch(dg, fs, seeds, [3, 2], gm.gnn_batch_seed(0, 0))
+    _, st = run_minibatch(dg, fs, seeds, [3, 2], gm.gnn_batch_seed(0, 0), sort)
     assert st == gm.GNN_ERR_INVALID_ARG
     seeds = np.array([5, 77, len(indptr) - 1, 9], dtype=np.int32)   # one past the last node
-    _, st = run_minibatch(dg, fs, seeds, [3, 2], gm.gnn_batch_seed(0, 0))
+    _, st = run_minibatch(dg, fs, seeds, [3, 2], gm.gnn_batch_seed(0, 0), sort)
     assert st == gm.GNN_ERR_OUT_OF_RANGE
 
 
