@@ -42,6 +42,7 @@ KERNEL_SOURCES = {
     "k_popc": "csrc/relabel.hip",
     "k_dist": "csrc/superbatch.hip",
     "k_copy_probe": "csrc/probe.hip",
+    "k_hash_probe": "csrc/probe.hip",
     "k_fill": "csrc/relabel.hip",
     "k_sage_update": "csrc/sage.hip",
 }
