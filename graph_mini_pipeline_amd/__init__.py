@@ -85,9 +85,13 @@ class Options:
     superbatch: str = "auto"    # super-batch relabel: "auto", "full" or "compact"
     gather: str = "auto"        # gather and outermost mean: "auto", "interleaved" or "batched"
     relabel: str = "auto"       # short id lists: "auto", "sort" (whenever eligible) or "bitmap"
+    d_hits: Optional[torch.Tensor] = None   # int64 [1] device: rows read from the HBM caches
 
     def c(self) -> _abi.gnn_options:
         o = _abi.gnn_options()
+        if self.d_hits is not None:
+            _need(self.d_hits, torch.int64, "d_hits")
+            o.d_hits = self.d_hits.data_ptr()
         o.group_max_deg = self.group_max_deg
         o.wave_max_deg = self.wave_max_deg
         modes = {"auto": 0, "full": GNN_SUPERBATCH_FULL, "compact": GNN_SUPERBATCH_COMPACT}
@@ -339,6 +343,52 @@ def gnn_feature_store_create(table: torch.Tensor, d: int, cache_rows: int = 0,
 
 def gnn_feature_store_destroy(fs: FeatureStore) -> None:
     fs.close()
+
+
+def gnn_feature_store_enable_dynamic(fs: FeatureStore, gamma: float, k_dyn: int, t_update: int,
+                                     max_refreshes: int = 0, auto: bool = False) -> None:
+    """GARDEN's Dynamic-Cache on the store: k_dyn more HBM rows for residual hot rows, ranked by
+    the EWMA of their accesses (decay gamma) and refreshed every t_update mini-batches; frozen
+    after max_refreshes refreshes (0: never).  auto: gathers refresh when due, on their stream."""
+    p = _abi.gnn_dyn_cache_params(float(gamma), int(k_dyn), int(t_update), int(max_refreshes),
+                                  _abi.GNN_DYN_AUTO if auto else 0)
+    _ok(lib().gnn_feature_store_enable_dynamic(fs.handle, ctypes.byref(p)),
+        "gnn_feature_store_enable_dynamic")
+    fs.dynamic = dict(gamma=float(gamma), k_dyn=int(k_dyn), t_update=int(t_update),
+                      max_refreshes=int(max_refreshes), auto=bool(auto))
+
+
+def gnn_dyn_cache_update(fs: FeatureStore, d_status: Optional[torch.Tensor] = None,
+                         stream=None) -> bool:
+    """Refresh the Dynamic-Cache on the stream if one is due; True if it ran."""
+    r = ctypes.c_int32(0)
+    _ok(lib().gnn_dyn_cache_update(fs.handle, ctypes.byref(r), _ptr(d_status), _stream(stream)),
+        "gnn_dyn_cache_update")
+    return bool(r.value)
+
+
+def gnn_dyn_cache_query(fs: FeatureStore) -> dict:
+    """Dynamic-Cache counters (synchronises the device)."""
+    info = _abi.gnn_dyn_cache_info()
+    _ok(lib().gnn_dyn_cache_query(fs.handle, ctypes.byref(info)), "gnn_dyn_cache_query")
+    return {name: getattr(info, name) for name, _ in info._fields_ if name != "reserved"}
+
+
+def gnn_dyn_cache_state(fs: FeatureStore, score: Optional[torch.Tensor] = None,
+                        member: Optional[torch.Tensor] = None, stream=None) -> None:
+    """score: float64 [N] device (Score(v, t) after the last observed mini-batch); member: uint8
+    [N] device (1: holds a Dynamic-Cache row)."""
+    n = fs.table.shape[0]
+    if score is not None:
+        _need(score, torch.float64, "score")
+        if score.numel() < n:
+            raise ValueError("score: [num_nodes]")
+    if member is not None:
+        _need(member, torch.uint8, "member")
+        if member.numel() < n:
+            raise ValueError("member: [num_nodes]")
+    _ok(lib().gnn_dyn_cache_state(fs.handle, _ptr(score), _ptr(member), _stream(stream)),
+        "gnn_dyn_cache_state")
 
 
 def gnn_gather_features(fs: FeatureStore, ids: torch.Tensor, out: torch.Tensor,

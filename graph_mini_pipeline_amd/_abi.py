@@ -22,6 +22,7 @@ GNN_RELABEL_SORT = 32
 GNN_RELABEL_BITMAP = 64
 GNN_NOALLOC_MAX_IDS = 1 << 26
 GNN_NOALLOC_SCRATCH_BYTES = (16 << 20) + (64 << 10)
+GNN_DYN_AUTO = 1
 
 GNN_OK = 0
 GNN_ERR_INVALID_ARG = -1
@@ -56,7 +57,18 @@ class gnn_blocks(ctypes.Structure):
 
 class gnn_options(ctypes.Structure):
     _fields_ = [("group_max_deg", i32), ("wave_max_deg", i32), ("flags", u32),
-                ("reserved", i32 * 5)]
+                ("reserved0", i32), ("d_hits", vp), ("reserved", i32 * 2)]
+
+
+class gnn_dyn_cache_params(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_double), ("k_dyn", i64), ("t_update", i32),
+                ("max_refreshes", i32), ("flags", u32)]
+
+
+class gnn_dyn_cache_info(ctypes.Structure):
+    _fields_ = [("steps", i64), ("since_refresh", i64), ("refreshes", i32), ("due", i32),
+                ("frozen", i32), ("reserved", i32), ("members", i64), ("last_candidates", i64),
+                ("last_admitted", i64), ("last_evicted", i64)]
 
 
 class gnn_minibatch_out(ctypes.Structure):
@@ -78,6 +90,10 @@ SIGNATURES = {
     "gnn_unique_relabel_noalloc": (i32, [vp, i64, vp, vp, i64, i64, vp, i64, vp, vp, vp, vp, vp]),
     "gnn_feature_store_create": (i32, [vp, i32, i64, i64, i64, i64, vp, P(vp)]),
     "gnn_feature_store_destroy": (i32, [vp]),
+    "gnn_feature_store_enable_dynamic": (i32, [vp, P(gnn_dyn_cache_params)]),
+    "gnn_dyn_cache_update": (i32, [vp, P(i32), vp, vp]),
+    "gnn_dyn_cache_query": (i32, [vp, P(gnn_dyn_cache_info)]),
+    "gnn_dyn_cache_state": (i32, [vp, vp, vp, vp]),
     "gnn_host_mapped_pointer": (i32, [vp, P(vp)]),
     "gnn_adjacency_cache_create": (i32, [P(gnn_graph), vp, i64, i64, P(vp), P(i64), P(i64)]),
     "gnn_adjacency_cache_attach": (i32, [vp, P(gnn_graph)]),

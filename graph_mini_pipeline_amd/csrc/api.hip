@@ -12,13 +12,31 @@
 
 using namespace gnnmb;
 
+// Dynamic-Cache (GARDEN Sec. IV.B): host bookkeeping of the mini-batch count and weights, and
+// the device arrays of the scores and of the refresh.
+struct DynCache {
+    gnn_dyn_cache_params p;
+    std::mutex mu;
+    double w_next = 1.0;          // weight of the next observed mini-batch: W * gamma^-t
+    int64_t steps = 0, steps_at_refresh = 0;
+    int32_t refreshes = 0;
+    double *score = nullptr;      // [num_nodes] scaled scores
+    uint32_t *touched = nullptr;  // [ceil(num_nodes / 32)]
+    int32_t *cand = nullptr;      // [num_nodes]
+    uint64_t *keys = nullptr;     // [num_nodes]
+    int32_t *free_rows = nullptr; // [k_dyn]
+    int32_t *admit = nullptr;     // [k_dyn]
+    DynState *state = nullptr;
+};
+
 struct gnn_feature_store {
     const float *table;  // device-addressable table (mapped pointer for pinned host memory)
     int32_t on_host;
     int64_t num_nodes, d, ld;
-    int64_t cache_rows;
-    float *cache;   // [cache_rows, ld] in HBM, or NULL
+    int64_t cache_rows;  // static-cache rows (slots 0..cache_rows-1)
+    float *cache;   // [cache_rows (+ k_dyn), ld] in HBM, or NULL
     int32_t *slot;  // [num_nodes] cache slot of each node, -1 if not cached; NULL if no cache
+    DynCache *dyn;  // NULL: no Dynamic-Cache
 };
 
 struct gnn_adjacency_cache {
@@ -278,6 +296,7 @@ struct Opts {
     int32_t group_max = 256;
     int32_t wave_max = 16384;   // measured best of 1024 .. 65536 on the four large workloads
     uint32_t flags = 0;
+    int64_t *d_hits = nullptr;
 };
 
 gnn_status read_opts(const gnn_options *o, Opts *out) {
@@ -286,6 +305,7 @@ gnn_status read_opts(const gnn_options *o, Opts *out) {
         if (o->group_max_deg) r.group_max = o->group_max_deg;
         if (o->wave_max_deg) r.wave_max = o->wave_max_deg;
         r.flags = o->flags;
+        r.d_hits = o->d_hits;
     }
     if (r.group_max < 1 || r.wave_max < r.group_max) return GNN_ERR_INVALID_ARG;
     if ((r.flags & GNN_SUPERBATCH_FULL) && (r.flags & GNN_SUPERBATCH_COMPACT)) return GNN_ERR_INVALID_ARG;
@@ -883,6 +903,96 @@ gnn_status gnn_unique_relabel_noalloc(const int32_t *keep, int64_t n_keep, const
                              cap_uniq, d_n_uniq, add_lid, keep_lid, s);
 }
 
+namespace {
+
+// Scaled scores are brought back by 2^-512 (exact for normal doubles) once the weights reach
+// 2^512: at a refresh, or -- when no refresh comes -- on the stream of the observing call (with
+// observations from other streams in flight this may mix scales for a node, which moves the
+// ranking but never a gathered row).
+constexpr double kDynRescaleAt = 0x1p512;
+constexpr double kDynRescaleBy = 0x1p-512;
+
+bool dyn_frozen(const DynCache *dc) {
+    return dc->p.max_refreshes > 0 && dc->refreshes >= dc->p.max_refreshes;
+}
+
+// Observation weights of the next n mini-batches of the store, w[0..n) (GARDEN Sec. IV.B, eq.
+// (5) in the scaled form S(v) = w_t * Score(v, t), w_t = W * gamma^-t).  *obs.score stays NULL
+// when nothing is observed: no Dynamic-Cache, or a frozen one.
+gnn_status dyn_observe_steps(const gnn_feature_store *fs, int n, double *w, DynObserve *obs,
+                             hipStream_t s) {
+    *obs = DynObserve{};
+    DynCache *dc = fs->dyn;
+    if (!dc) return GNN_OK;
+    std::lock_guard<std::mutex> lk(dc->mu);
+    if (dyn_frozen(dc)) return GNN_OK;
+    if (dc->w_next >= kDynRescaleAt) {
+        GNN_TRY_HIP(launch_dyn_rescale(dc->score, fs->num_nodes, kDynRescaleBy, s));
+        dc->w_next *= kDynRescaleBy;
+    }
+    for (int i = 0; i < n; ++i) {
+        w[i] = dc->w_next;
+        dc->w_next /= dc->p.gamma;
+    }
+    dc->steps += n;
+    *obs = DynObserve{dc->score, dc->touched, static_cast<int32_t>(fs->cache_rows)};
+    return GNN_OK;
+}
+
+// A refresh (eq. (6)) on s if one is due: at least t_update mini-batches since the last one.
+gnn_status dyn_refresh(const gnn_feature_store *fs, int32_t *d_status, hipStream_t s,
+                       int32_t *refreshed) {
+    if (refreshed) *refreshed = 0;
+    DynCache *dc = fs->dyn;
+    std::lock_guard<std::mutex> lk(dc->mu);
+    if (dyn_frozen(dc) || dc->steps - dc->steps_at_refresh < dc->p.t_update) return GNN_OK;
+    if (dc->w_next >= kDynRescaleAt) {
+        GNN_TRY_HIP(launch_dyn_rescale(dc->score, fs->num_nodes, kDynRescaleBy, s));
+        dc->w_next *= kDynRescaleBy;
+    }
+    DynRefreshArgs a{};
+    a.st = dc->state;
+    a.score = dc->score;
+    a.touched = dc->touched;
+    a.num_rows = fs->num_nodes;
+    a.cand = dc->cand;
+    a.keys = dc->keys;
+    a.free_rows = dc->free_rows;
+    a.admit = dc->admit;
+    a.k_dyn = dc->p.k_dyn;
+    a.static_rows = static_cast<int32_t>(fs->cache_rows);
+    a.slot = fs->slot;
+    a.cache = fs->cache;
+    a.table = fs->table;
+    a.ld = fs->ld;
+    a.d = fs->d;
+    a.status = d_status;
+    GNN_TRY_HIP(launch_dyn_refresh(a, s));
+    dc->steps_at_refresh = dc->steps;
+    dc->refreshes += 1;
+    if (refreshed) *refreshed = 1;
+    return GNN_OK;
+}
+
+gnn_status dyn_auto_refresh(const gnn_feature_store *fs, int32_t *d_status, hipStream_t s) {
+    if (!fs->dyn || !(fs->dyn->p.flags & GNN_DYN_AUTO)) return GNN_OK;
+    return dyn_refresh(fs, d_status, s, nullptr);
+}
+
+void dyn_free(DynCache *dc) {
+    if (!dc) return;
+    if (dc->score) (void)hipFree(dc->score);
+    if (dc->touched) (void)hipFree(dc->touched);
+    if (dc->cand) (void)hipFree(dc->cand);
+    if (dc->keys) (void)hipFree(dc->keys);
+    if (dc->free_rows) (void)hipFree(dc->free_rows);
+    if (dc->admit) (void)hipFree(dc->admit);
+    if (dc->state) (void)hipFree(dc->state);
+    delete dc;
+}
+
+}  // namespace
+
 gnn_status gnn_feature_store_create(const float *table, int32_t table_on_host, int64_t num_nodes,
                                     int64_t d, int64_t ld, int64_t cache_rows,
                                     const int32_t *hot_order, gnn_feature_store **out) {
@@ -1046,7 +1156,104 @@ gnn_status gnn_feature_store_destroy(gnn_feature_store *fs) {
     if (!fs) return GNN_OK;
     if (fs->cache) (void)hipFree(fs->cache);
     if (fs->slot) (void)hipFree(fs->slot);
+    dyn_free(fs->dyn);
     delete fs;
+    return GNN_OK;
+}
+
+gnn_status gnn_feature_store_enable_dynamic(gnn_feature_store *fs, const gnn_dyn_cache_params *p) {
+    if (!fs || !p || fs->dyn) return GNN_ERR_INVALID_ARG;
+    if (!(p->gamma > 0.0 && p->gamma < 1.0) || p->k_dyn < 1 || p->t_update < 1 ||
+        p->max_refreshes < 0 || (p->flags & ~GNN_DYN_AUTO) != 0)
+        return GNN_ERR_INVALID_ARG;
+    if (p->k_dyn > fs->num_nodes - fs->cache_rows) return GNN_ERR_INVALID_ARG;
+    if (fault(kFaultAlloc)) return GNN_ERR_HIP;
+    DynCache *dc = new (std::nothrow) DynCache();
+    if (!dc) return GNN_ERR_HIP;
+    dc->p = *p;
+    const int64_t N = fs->num_nodes;
+    const int64_t words = (N + 31) / 32;
+    const int64_t rows = fs->cache_rows + p->k_dyn;
+    float *cache = nullptr;
+    int32_t *slot = nullptr;
+    bool ok = hipDeviceSynchronize() == hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&cache),
+                         static_cast<size_t>(rows) * fs->ld * sizeof(float)) == hipSuccess;
+    if (ok && fs->cache_rows > 0)
+        ok = hipMemcpy(cache, fs->cache, static_cast<size_t>(fs->cache_rows) * fs->ld * sizeof(float),
+                       hipMemcpyDeviceToDevice) == hipSuccess;
+    if (ok && !fs->slot) {
+        ok = hipMalloc(reinterpret_cast<void **>(&slot), static_cast<size_t>(N) * sizeof(int32_t)) ==
+             hipSuccess;
+        ok = ok && launch_fill_i32(slot, N, -1, nullptr) == hipSuccess;
+    }
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&dc->score), static_cast<size_t>(N) * 8) == hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&dc->touched), static_cast<size_t>(words) * 4) == hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&dc->cand), static_cast<size_t>(N) * 4) == hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&dc->keys), static_cast<size_t>(N) * 8) == hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&dc->free_rows),
+                         static_cast<size_t>(p->k_dyn) * 4) == hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&dc->admit), static_cast<size_t>(p->k_dyn) * 4) ==
+               hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&dc->state), sizeof(DynState)) == hipSuccess;
+    ok = ok && launch_fill_u32(reinterpret_cast<uint32_t *>(dc->score), 2 * N, 0u, nullptr) == hipSuccess;
+    ok = ok && launch_fill_u32(dc->touched, words, 0u, nullptr) == hipSuccess;
+    ok = ok && launch_dyn_init(dc->state, dc->free_rows, p->k_dyn, nullptr) == hipSuccess;
+    ok = ok && hipDeviceSynchronize() == hipSuccess;
+    if (!ok) {
+        if (cache) (void)hipFree(cache);
+        if (slot) (void)hipFree(slot);
+        dyn_free(dc);
+        return GNN_ERR_HIP;
+    }
+    if (fs->cache) (void)hipFree(fs->cache);
+    fs->cache = cache;
+    if (slot) fs->slot = slot;
+    fs->dyn = dc;
+    return GNN_OK;
+}
+
+gnn_status gnn_dyn_cache_update(const gnn_feature_store *fs, int32_t *refreshed, int32_t *d_status,
+                                gnn_stream stream) {
+    if (refreshed) *refreshed = 0;
+    if (!fs || !fs->dyn) return GNN_ERR_INVALID_ARG;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
+    return dyn_refresh(fs, d_status, static_cast<hipStream_t>(stream), refreshed);
+}
+
+gnn_status gnn_dyn_cache_query(const gnn_feature_store *fs, gnn_dyn_cache_info *out) {
+    if (!fs || !fs->dyn || !out) return GNN_ERR_INVALID_ARG;
+    DynCache *dc = fs->dyn;
+    DynState st;
+    GNN_TRY_HIP(hipDeviceSynchronize());
+    GNN_TRY_HIP(hipMemcpy(&st, dc->state, sizeof(st), hipMemcpyDeviceToHost));
+    std::lock_guard<std::mutex> lk(dc->mu);
+    *out = gnn_dyn_cache_info{};
+    out->steps = dc->steps;
+    out->since_refresh = dc->steps - dc->steps_at_refresh;
+    out->refreshes = dc->refreshes;
+    out->frozen = dyn_frozen(dc) ? 1 : 0;
+    out->due = !out->frozen && out->since_refresh >= dc->p.t_update ? 1 : 0;
+    out->members = st.members;
+    out->last_candidates = st.n_cand;
+    out->last_admitted = st.n_admit;
+    out->last_evicted = st.n_evict;
+    return GNN_OK;
+}
+
+gnn_status gnn_dyn_cache_state(const gnn_feature_store *fs, double *score, uint8_t *member,
+                               gnn_stream stream) {
+    if (!fs || !fs->dyn) return GNN_ERR_INVALID_ARG;
+    DynCache *dc = fs->dyn;
+    double scale;
+    {
+        std::lock_guard<std::mutex> lk(dc->mu);
+        // Score(v, t) = S(v) / w_t, and the last observed mini-batch's weight is w_next * gamma
+        scale = dc->steps > 0 ? 1.0 / (dc->w_next * dc->p.gamma) : 0.0;
+    }
+    GNN_TRY_HIP(launch_dyn_state(dc->score, fs->num_nodes, scale, fs->slot,
+                                 static_cast<int32_t>(fs->cache_rows), score, member,
+                                 static_cast<hipStream_t>(stream)));
     return GNN_OK;
 }
 
@@ -1057,10 +1264,14 @@ gnn_status gnn_gather_features(const gnn_feature_store *fs, const int32_t *ids,
     if (n > 0 && (!ids || !out)) return GNN_ERR_INVALID_ARG;
     if (n * fs->d > kFlatMax) return GNN_ERR_UNSUPPORTED;
     if (fault(kFaultLaunch)) return GNN_ERR_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    double w = 0.0;
+    DynObserve obs;
+    GNN_TRY(dyn_observe_steps(fs, 1, &w, &obs, s));
     GNN_TRY_HIP(launch_gather(fs->table, fs->cache, fs->slot, fs->ld, fs->d, fs->num_nodes, ids,
-                              d_n, n, out, ld_out, d_hits, d_status,
-                              static_cast<hipStream_t>(stream)));
-    return GNN_OK;
+                              d_n, n, out, ld_out, d_hits, d_status, s,
+                              obs.score ? &obs : nullptr, w));
+    return dyn_auto_refresh(fs, d_status, s);
 }
 
 gnn_status gnn_mean_aggregate(const int32_t *indptr, const int32_t *lid, int64_t n_lid,
@@ -1218,6 +1429,10 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         if (st != GNN_OK) return st;
     }
     if (ev) GNN_TRY_HIP(hipEventRecord(ev[1], s));
+    // With a Dynamic-Cache, each sub-batch's gather is one observed mini-batch.
+    double obs_w[GNN_MAX_GROUP] = {};
+    DynObserve obs;
+    GNN_TRY(dyn_observe_steps(fs, group, obs_w, &obs, s));
     // Stages 2 and 3: gather X = rows of V_K, then the outermost block's mean.  Batched: every
     // sub-batch's gather in one launch, then every outermost mean in one launch.  Interleaved: per
     // sub-batch, so the mean reads X while it is still in the caches.
@@ -1232,13 +1447,15 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
         ga.num_rows = fs->num_nodes;
         ga.ld_out = outs[0].ld_h;
         ga.status = w.status;
+        ga.obs = obs;
+        ga.d_hits = o.d_hits;
         int64_t rows_cap = 0;
         MeanJob jobs[GNN_MAX_GROUP];
         for (int gi = 0; gi < group; ++gi) {
             gnn_minibatch_out &mo = outs[gi];
             const gnn_caps &c = mo.blocks.caps;
             ga.seg[gi] = GatherSeg{mo.blocks.hop[K - 1].nodes, mo.blocks.counts + 2 * (K - 1) + 1,
-                                   c.nodes[K - 1], mo.x};
+                                   c.nodes[K - 1], mo.x, obs_w[gi]};
             rows_cap += c.nodes[K - 1];
             const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
             if (from_table)   // X[lid[e]] is table row gid[e], bit for bit
@@ -1284,7 +1501,8 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
             const gnn_caps &c = mo.blocks.caps;
             GNN_TRY_HIP(launch_gather(fs->table, fs->cache, fs->slot, fs->ld, d, fs->num_nodes,
                                       mo.blocks.hop[K - 1].nodes, mo.blocks.counts + 2 * (K - 1) + 1,
-                                      c.nodes[K - 1], mo.x, mo.ld_h, nullptr, w.status, s));
+                                      c.nodes[K - 1], mo.x, mo.ld_h, o.d_hits, w.status, s,
+                                      obs.score ? &obs : nullptr, obs_w[gi]));
             if (ev) GNN_TRY_HIP(hipEventRecord(ev[2 + 2 * gi], s));
             const int64_t *d_n = K == 1 ? nullptr : mo.blocks.counts + 2 * (K - 2) + 1;
             const MeanJob job{mo.blocks.hop[K - 1].indptr, mo.blocks.hop[K - 1].lid, c.edges[K - 1],
@@ -1307,6 +1525,7 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
                                 w.status, s));
     }
     if (ev) GNN_TRY_HIP(hipEventRecord(ev[2 + 2 * group], s));
+    GNN_TRY(dyn_auto_refresh(fs, w.status, s));
     return finish(o, w, s);
 }
 

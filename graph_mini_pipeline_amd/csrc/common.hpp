@@ -369,6 +369,45 @@ constexpr int kBitmapThreads = 256;
 constexpr int kBitmapWordsPerThread = 4;
 constexpr int kBitmapTile = kBitmapThreads * kBitmapWordsPerThread;
 
+// ---- Dynamic-Cache observation (GARDEN, Sec. IV.B, eq. 5) ---------------------------------------
+//
+// Each mini-batch t adds its weight w_t = W * gamma^-t to the scaled score S(v) of every node v
+// whose row it requests and the static cache does not hold, so S(v) = w_t * Score(v, t) at any
+// step t: all scores decay by the same factor per step, none has to be touched to decay, and the
+// order of the S(v) is the order of the Score(v, t).  Observed nodes are marked in the touched
+// bitmap, which also holds the current Dynamic-Cache members (set at each refresh).
+struct DynObserve {
+    double *score;        // [num_rows] scaled scores; NULL: no observation
+    uint32_t *touched;    // [ceil(num_rows / 32)]
+    int32_t static_rows;  // cache slots below this one hold the static cache
+};
+
+// Observation of the requested row of node v (0 <= v < num_rows) whose cache slot is sl.
+__device__ __forceinline__ void dyn_observe(const DynObserve &o, int32_t v, int32_t sl, double w) {
+    if (sl >= 0 && sl < o.static_rows) return;   // a static-cache hit: not residual
+    unsafeAtomicAdd(o.score + v, w);
+    uint32_t *word = o.touched + (v >> 5);
+    const uint32_t bit = 1u << (v & 31);
+    if (!(*word & bit)) atomicOr(word, bit);
+}
+
+// Device state of a Dynamic-Cache refresh (eq. 6): the top-k selection's radix digits, the
+// candidate count and the free-row stack.  Written by the refresh kernels only.
+struct DynState {
+    int64_t n_cand;       // candidates of this refresh (touched nodes)
+    int64_t remaining;    // rank still to place within the digits chosen so far
+    uint64_t key_prefix;  // digits chosen so far of the k-th largest key, then that key
+    uint64_t key_mask;
+    uint32_t id_prefix;   // among keys equal to it: digits of the largest id taken
+    uint32_t id_mask;
+    int64_t n_admit;      // nodes entering the cache in this refresh
+    int64_t n_evict;      // members leaving it
+    int64_t free_top;     // rows on the free-row stack
+    int64_t members;      // rows in use after the refresh
+    int64_t refreshes;
+    uint32_t hist[256];
+};
+
 // Kernel launchers (each returns hipGetLastError()).
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);
@@ -381,13 +420,16 @@ hipError_t launch_dist(const DistArgs &a, hipStream_t s);
 hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
-                         int32_t *status, hipStream_t s);
-// One sub-batch of a batched gather: out[r] = row ids[r] for r < n (n = *d_n, or n_cap).
+                         int32_t *status, hipStream_t s, const DynObserve *obs = nullptr,
+                         double obs_w = 0.0);
+// One sub-batch of a batched gather: out[r] = row ids[r] for r < n (n = *d_n, or n_cap); obs_w:
+// its Dynamic-Cache observation weight.
 struct GatherSeg {
     const int32_t *ids;
     const int64_t *d_n;
     int64_t n_cap;
     float *out;
+    double obs_w;
 };
 
 struct GatherBatchArgs {
@@ -402,6 +444,8 @@ struct GatherBatchArgs {
     int64_t ld_out;
     int32_t *status;
     uint32_t cpr;      // set by the launcher
+    DynObserve obs;    // obs.score NULL: no observation
+    int64_t *d_hits;   // rows read from the cache are added here (NULL: not counted)
 };
 
 // Gather of up to kMaxGroup sub-batches in one launch (rows_cap: the sub-batches' total row
@@ -459,5 +503,36 @@ hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_
 hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                              const int32_t *hot, int64_t rows, float *cache, int32_t *slot,
                              int32_t *status, hipStream_t s);
+
+// Dynamic-Cache (GARDEN, Sec. IV.B, eq. 6).  Set-up: free rows 0..k-1 on the stack, state zero.
+hipError_t launch_dyn_init(DynState *st, int32_t *free_rows, int64_t k, hipStream_t s);
+// score[v] *= factor for every node (factor a power of two: exact for normal numbers).
+hipError_t launch_dyn_rescale(double *score, int64_t n, double factor, hipStream_t s);
+// One refresh: the k_dyn touched nodes of largest scaled score (ties: smaller id first) become
+// the members; members left out lose their slot and row, nodes taken in get a free row (copied
+// from the table) and their slot.  The touched bitmap is left holding exactly the members.
+struct DynRefreshArgs {
+    DynState *st;
+    double *score;
+    uint32_t *touched;
+    int64_t num_rows;
+    int32_t *cand;        // [num_rows] candidate ids
+    uint64_t *keys;       // [num_rows] their scaled scores' bits
+    int32_t *free_rows;   // [k_dyn] free-row stack
+    int32_t *admit;       // [k_dyn] nodes taken in
+    int64_t k_dyn;
+    int32_t static_rows;
+    int32_t *slot;
+    float *cache;
+    const float *table;
+    int64_t ld, d;
+    int32_t *status;
+};
+hipError_t launch_dyn_refresh(const DynRefreshArgs &a, hipStream_t s);
+// Inspection: out_score[v] = score[v] * scale and out_member[v] = 1 for Dynamic-Cache members
+// (either output may be NULL).
+hipError_t launch_dyn_state(const double *score, int64_t n, double scale, const int32_t *slot,
+                            int32_t static_rows, double *out_score, uint8_t *out_member,
+                            hipStream_t s);
 
 }  // namespace gnnmb

@@ -13,7 +13,9 @@
 // flight (a row's chunks are stored as its slot is refilled with the row R places later).  A row
 // is read from the HBM hot-row cache when slot[v] >= 0, else from the table (HBM, or pinned host
 // memory through its mapped device address).  Bandwidth bound: no arithmetic.  Rows that are not
-// 16-byte aligned take a flat (row, element) kernel.
+// 16-byte aligned take a flat (row, element) kernel.  With the Dynamic-Cache on (Sec. IV.B, eq.
+// 5), the lane that loads a row's id and slot also records the row's observation when the static
+// cache does not hold it.
 #include "common.hpp"
 
 namespace gnnmb {
@@ -43,6 +45,8 @@ struct GatherArgs {
     int32_t scat_g;
     float *scat_out[kMaxGroup];
     int32_t rpu;  // rows per work unit (<= G; G unless the rows are few and fat)
+    DynObserve obs;  // Dynamic-Cache observation (obs.score NULL: none), weight obs_w
+    double obs_w;
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -92,6 +96,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
                 }
                 const float *src;
                 const int32_t sl = g.slot ? g.slot[v] : -1;
+                if (g.obs.score && ch == 0) dyn_observe(g.obs, v, sl, g.obs_w);
                 if (sl >= 0) {
                     src = g.cache + static_cast<int64_t>(sl) * g.ld;
                     hits += ch == 0;
@@ -156,6 +161,8 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
                 set_status(g.status, GNN_ERR_OUT_OF_RANGE);
             } else {
                 const int32_t sl = g.slot ? g.slot[v] : -1;
+                if constexpr (!SCAT)
+                    if (g.obs.score && p == 0) dyn_observe(g.obs, v, sl, g.obs_w);
                 if (sl >= 0) {
                     mine = -2 - sl;
                     hits += p == 0;
@@ -288,6 +295,7 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
     const uint32_t units = s_u0[a.nseg];
     const uint32_t g0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (64 / G) + grp;
     const uint32_t gstride = gridDim.x * 4u * (64 / G);
+    uint32_t hits = 0;
     for (uint32_t it = g0; it < units; it += gstride) {
         const uint32_t it0 = __builtin_amdgcn_readfirstlane(it);
         int sg = 0;
@@ -308,6 +316,8 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
                 set_status(a.status, GNN_ERR_OUT_OF_RANGE);
             } else {
                 const int32_t sl = a.slot ? a.slot[v] : -1;
+                if (a.obs.score && p == 0) dyn_observe(a.obs, v, sl, S.obs_w);
+                hits += sl >= 0 && p == 0;
                 mine = sl >= 0 ? -2 - sl : v;
             }
         }
@@ -361,6 +371,11 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
             }
         }
     }
+    if (a.d_hits) {
+        hits = wave_sum(hits);
+        if (lane_id() == 0 && hits) atomicAdd(reinterpret_cast<unsigned long long *>(a.d_hits),
+                                              static_cast<unsigned long long>(hits));
+    }
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -384,7 +399,7 @@ void launch_rows(const GatherArgs &g, int G, int CH, dim3 grid, hipStream_t s) {
 hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
-                         int32_t *status, hipStream_t s) {
+                         int32_t *status, hipStream_t s, const DynObserve *obs, double obs_w) {
     if (n_cap <= 0 || d <= 0) return hipSuccess;
     const bool v4 = ld % 4 == 0 && ld_out % 4 == 0 && aligned16(table) && aligned16(out) &&
                     (cache == nullptr || aligned16(cache));
@@ -392,7 +407,11 @@ hipError_t launch_gather(const float *table, const float *cache, const int32_t *
     const int64_t cpr = (d + vec - 1) / vec;
     GatherArgs g{table, cache, slot, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
                  out, ld_out, d_hits, status, make_fastdiv(static_cast<uint32_t>(cpr)),
-                 nullptr, nullptr, 0, 0, 0, {}, 0};
+                 nullptr, nullptr, 0, 0, 0, {}, 0, {}, 0.0};
+    if (obs) {
+        g.obs = *obs;
+        g.obs_w = obs_w;
+    }
     if (!v4) {
         constexpr int U = 4;
         hipLaunchKernelGGL((k_gather<1, U>), dim3(grid_for(n_cap * cpr, 256 * U, 2048)), dim3(256),
@@ -423,7 +442,7 @@ hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_
     const int64_t cpr = (d + 3) / 4;
     GatherArgs g{table, nullptr, nullptr, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
                  nullptr, ld_out, nullptr, status, make_fastdiv(static_cast<uint32_t>(cpr)),
-                 bm, wp, words, by_id, G_sb, {}, 0};
+                 bm, wp, words, by_id, G_sb, {}, 0, {}, 0.0};
     for (int sg = 0; sg < G_sb; ++sg) g.scat_out[sg] = outs[sg];
     const int G = cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64);
     const int CH = G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);
@@ -448,7 +467,8 @@ hipError_t launch_gather_batch(GatherBatchArgs a, int64_t rows_cap, hipStream_t 
         for (int sg = 0; sg < a.nseg; ++sg) {
             const GatherSeg &S = a.seg[sg];
             const hipError_t e = launch_gather(a.table, a.cache, a.slot, a.ld, a.d, a.num_rows, S.ids,
-                                               S.d_n, S.n_cap, S.out, a.ld_out, nullptr, a.status, s);
+                                               S.d_n, S.n_cap, S.out, a.ld_out, a.d_hits, a.status, s,
+                                               &a.obs, S.obs_w);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;

@@ -166,7 +166,10 @@ typedef struct gnn_options {
     int32_t wave_max_deg;  /* degree bound of the one-wavefront class (default 16384); higher
                               degrees take one workgroup per node */
     uint32_t flags;        /* GNN_SYNC, GNN_SUPERBATCH_*, GNN_GATHER_* */
-    int32_t reserved[5];
+    int32_t reserved0;
+    int64_t *d_hits;       /* gnn_minibatch: device int64 increased by the feature rows read from
+                              the HBM caches (static or Dynamic-Cache); NULL: not counted */
+    int32_t reserved[2];
 } gnn_options;
 
 /* Text for a status code (static storage). */
@@ -272,6 +275,73 @@ gnn_status gnn_feature_store_create(const float *table, int32_t table_on_host, i
                                     int64_t d, int64_t ld, int64_t cache_rows,
                                     const int32_t *hot_order, gnn_feature_store **out);
 gnn_status gnn_feature_store_destroy(gnn_feature_store *fs);
+
+/*
+ * Dynamic-Cache (GARDEN Sec. IV.B, eq. (5)-(6)): a bounded secondary HBM cache of k_dyn rows, after
+ * the static cache's rows, for residual hot rows, i.e. rows that the static cache misses and that
+ * recur.  Every gather from the store (gnn_gather_features, and gnn_minibatch once per
+ * sub-batch) is one mini-batch t: for each requested row of a node v outside the static cache,
+ * Score(v, t) = gamma * Score(v, t-1) + (occurrences of v among the requested rows), eq. (5);
+ * every other node's score only decays.  A refresh, once at least t_update mini-batches have been
+ * observed since the last one, makes the cache hold the k_dyn nodes of highest score, eq. (6)
+ * (ties: the smaller id; only nodes with a positive score; fewer than k_dyn if fewer have one).
+ * After max_refreshes refreshes (0: no limit) the cache is frozen and nothing more is observed.
+ * Results never change: a gather returns the table's rows whichever cache holds them.
+ *   gamma: 0 < gamma < 1; k_dyn >= 1 and cache_rows + k_dyn <= num_nodes; t_update >= 1.
+ *   flags: GNN_DYN_AUTO -- the gather call that completes an interval refreshes at its end, on its
+ *     own stream; else only gnn_dyn_cache_update refreshes.
+ * Memory: k_dyn * ld floats of cache, and 20.125 bytes per node (score, candidate list and key,
+ * touched bitmap); the cache is re-allocated (static rows copied).  Setup call: allocates,
+ * synchronises the device, and must not overlap any use of the store.
+ * Ordering: a refresh rewrites cache rows and slots on its stream; no gather from the store may
+ * run concurrently with it on another stream (join the streams around gnn_dyn_cache_update).
+ * Observations from several streams may overlap one another.  Calls that use one store are made
+ * from one host thread at a time.
+ * Errors: GNN_ERR_INVALID_ARG (bad parameters, or already enabled), GNN_ERR_HIP (allocation).
+ */
+#define GNN_DYN_AUTO 1u
+typedef struct gnn_dyn_cache_params {
+    double gamma;
+    int64_t k_dyn;
+    int32_t t_update;
+    int32_t max_refreshes;
+    uint32_t flags;
+} gnn_dyn_cache_params;
+gnn_status gnn_feature_store_enable_dynamic(gnn_feature_store *fs, const gnn_dyn_cache_params *p);
+
+/*
+ * Refresh of the Dynamic-Cache on `stream` if one is due (see above); *refreshed (host, may be
+ * NULL) = 1 if it ran.  Enqueues only; device errors (GNN_ERR_INTERNAL, never expected) go to
+ * *d_status when not NULL.  Errors: GNN_ERR_INVALID_ARG (no Dynamic-Cache).
+ */
+gnn_status gnn_dyn_cache_update(const gnn_feature_store *fs, int32_t *refreshed, int32_t *d_status,
+                                gnn_stream stream);
+
+/*
+ * Dynamic-Cache counters (host struct).  Synchronises the device for the device-side counts
+ * (members, and the last refresh's candidates, admissions and evictions).
+ */
+typedef struct gnn_dyn_cache_info {
+    int64_t steps;           /* mini-batches observed */
+    int64_t since_refresh;   /* of which after the last refresh */
+    int32_t refreshes;
+    int32_t due;             /* a refresh would run now */
+    int32_t frozen;          /* max_refreshes reached: no more observation */
+    int32_t reserved;
+    int64_t members;
+    int64_t last_candidates;
+    int64_t last_admitted;
+    int64_t last_evicted;
+} gnn_dyn_cache_info;
+gnn_status gnn_dyn_cache_query(const gnn_feature_store *fs, gnn_dyn_cache_info *out);
+
+/*
+ * Inspection on `stream`: score[v] = Score(v, t) after the last observed mini-batch t (device
+ * double [num_nodes], or NULL) and member[v] = 1 if v holds a Dynamic-Cache row, else 0 (device
+ * uint8 [num_nodes], or NULL).  Errors: GNN_ERR_INVALID_ARG (no Dynamic-Cache).
+ */
+gnn_status gnn_dyn_cache_state(const gnn_feature_store *fs, double *score, uint8_t *member,
+                               gnn_stream stream);
 
 /*
  * Feature-row gather (GARDEN Sec. II.B "Nfeat-selecting"; LEO Sec. 2.2 feature extraction):

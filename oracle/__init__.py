@@ -19,6 +19,12 @@ One GraphSAGE-mean layer over a block (sage_layer; GARDEN Sec. II.A eq. (1)-(2),
 Sec. VI.A): out[i] = relu([h[dst_lid[i]] || mean of h over i's sampled neighbours] @ W + bias),
 in double.
 
+The Dynamic-Cache (DynCache; GARDEN Sec. IV.B eq. (5)-(6)): each mini-batch multiplies every
+node's score by gamma and adds one per requested row of a node outside the static cache; a refresh,
+at the first update call after at least t_update mini-batches, makes the cache the k_dyn nodes of
+highest positive score (ties: smaller id); after max_refreshes refreshes (0: no limit) nothing more
+is observed or refreshed.
+
 Every function here is pinned by the CPU tests (published SplitMix64 outputs, brute force on
 hand-built graphs, BFS and dense-matrix special cases, uniformity statistics, exact rationals).
 """
@@ -99,6 +105,10 @@ def lib():
         L.orc_mean.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp, i64]
         L.orc_sage_layer.restype = i32
         L.orc_sage_layer.argtypes = [vp, vp, vp, i64, vp, i64, i64, i64, vp, vp, i64, i32, vp, vp]
+        L.orc_dyn_ewma_step.restype = i32
+        L.orc_dyn_ewma_step.argtypes = [vp, i64, ctypes.c_double, vp, i64, vp]
+        L.orc_dyn_topk.restype = i64
+        L.orc_dyn_topk.argtypes = [vp, i64, i64, vp]
         _lib = L
     return _lib
 
@@ -313,3 +323,59 @@ def superbatch(indptr, indices, table, seeds_concat, batch_ptr: Sequence[int],
     """G sub-batches sharing one batch seed: by definition G independent runs."""
     return [minibatch(indptr, indices, table, seeds_concat[batch_ptr[g]:batch_ptr[g + 1]],
                       fanouts, seed64, d) for g in range(len(batch_ptr) - 1)]
+
+
+# ---- Dynamic-Cache (GARDEN Sec. IV.B, eq. (5)-(6)) --------------------------------------------
+
+def dyn_ewma_step(score: np.ndarray, gamma: float, ids, is_static: Optional[np.ndarray]) -> None:
+    """Eq. (5) for one mini-batch, in place on score (float64 [N])."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    st = None if is_static is None else np.ascontiguousarray(is_static, dtype=np.uint8)
+    _check(lib().orc_dyn_ewma_step(_p(score), score.shape[0], float(gamma),
+                                   _p(ids) if ids.size else None, ids.size,
+                                   _p(st) if st is not None else None), "dyn ewma step")
+
+
+def dyn_topk(score: np.ndarray, k: int) -> np.ndarray:
+    """Eq. (6): ids (ascending) of the k nodes of highest positive score, smaller id on ties."""
+    out = np.zeros(max(1, min(k, score.shape[0])), dtype=np.int32)
+    c = lib().orc_dyn_topk(_p(score), score.shape[0], int(k), _p(out))
+    if c < 0:
+        _check(int(c), "dyn topk")
+    return out[:c].copy()
+
+
+class DynCache:
+    """The Dynamic-Cache's policy, step by step: observe() is one mini-batch, update() refreshes
+    when at least t_update mini-batches were observed since the last refresh."""
+
+    def __init__(self, num_nodes: int, static_ids, gamma: float, k_dyn: int, t_update: int,
+                 max_refreshes: int = 0):
+        self.score = np.zeros(num_nodes, dtype=np.float64)
+        self.is_static = np.zeros(num_nodes, dtype=np.uint8)
+        self.is_static[np.asarray(static_ids, dtype=np.int64)] = 1
+        self.gamma, self.k_dyn, self.t_update = gamma, k_dyn, t_update
+        self.max_refreshes = max_refreshes
+        self.steps = 0
+        self.since = 0
+        self.refreshes = 0
+        self.members = np.zeros(0, dtype=np.int32)
+
+    @property
+    def frozen(self) -> bool:
+        return self.max_refreshes > 0 and self.refreshes >= self.max_refreshes
+
+    def observe(self, ids) -> None:
+        if self.frozen:
+            return
+        dyn_ewma_step(self.score, self.gamma, ids, self.is_static)
+        self.steps += 1
+        self.since += 1
+
+    def update(self) -> bool:
+        if self.frozen or self.since < self.t_update:
+            return False
+        self.members = dyn_topk(self.score, self.k_dyn)
+        self.since = 0
+        self.refreshes += 1
+        return True

@@ -26,6 +26,10 @@
  * the mean over the sampled neighbours, UPDATE a dense layer on the concatenation of the node's
  * own previous state and that mean, then a ReLU (the layer GraphSAGE defines and GARDEN Sec. VI.A
  * evaluates).  It is computed in double throughout and is not rounded to float.
+ *
+ * The Dynamic-Cache (orc_dyn_ewma_step, orc_dyn_topk) follows GARDEN Sec. IV.B eq. (5)-(6): an
+ * exponentially weighted count of each node's residual accesses, in double, and the K nodes of
+ * highest count.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -271,4 +275,64 @@ int orc_sage_layer(const int32_t *indptr, const int32_t *lid, const int32_t *dst
     }
     free(a);
     return ORC_OK;
+}
+
+/*
+ * Dynamic-Cache hotness (GARDEN Sec. IV.B, eq. (5)) for one mini-batch t:
+ *   Score(v, t) = gamma * Score(v, t-1) + (number of i in B_t with i = v),
+ * where B_t is read as the mini-batch's requested feature rows that the static cache does not
+ * hold (the residual accesses the Dynamic-Cache is for); ids[0..n) are the requested rows, with
+ * repeats, and is_static[v] != 0 marks static-cache rows (NULL: no static cache).  Every score is
+ * scaled by gamma first, then 1 is added once per occurrence.
+ */
+int orc_dyn_ewma_step(double *score, int64_t num_nodes, double gamma, const int32_t *ids,
+                      int64_t n, const uint8_t *is_static) {
+    if (num_nodes < 0 || n < 0 || !(gamma > 0.0 && gamma < 1.0)) return ORC_ERR_ARG;
+    for (int64_t v = 0; v < num_nodes; ++v) score[v] = gamma * score[v];
+    for (int64_t i = 0; i < n; ++i) {
+        const int32_t v = ids[i];
+        if (v < 0 || v >= num_nodes) return ORC_ERR_RANGE;
+        if (is_static && is_static[v]) continue;
+        score[v] += 1.0;
+    }
+    return ORC_OK;
+}
+
+typedef struct {
+    double score;
+    int32_t id;
+} orc_scored;
+
+/* Larger score first; equal scores: smaller id first. */
+static int cmp_scored(const void *a, const void *b) {
+    const orc_scored *x = (const orc_scored *)a, *y = (const orc_scored *)b;
+    if (x->score != y->score) return x->score > y->score ? -1 : 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+/*
+ * Dynamic-Cache contents (GARDEN Sec. IV.B, eq. (6)): TopK of the scores with K = k.  Only nodes
+ * with a positive score take part (a node never requested has nothing to cache); among equal
+ * scores the smaller id comes first.  Writes the chosen ids in ascending order to out (room for
+ * min(k, num_nodes)) and returns their count (negative: error).
+ */
+int64_t orc_dyn_topk(const double *score, int64_t num_nodes, int64_t k, int32_t *out) {
+    if (num_nodes < 0 || k < 0) return ORC_ERR_ARG;
+    int64_t m = 0;
+    for (int64_t v = 0; v < num_nodes; ++v) m += score[v] > 0.0;
+    orc_scored *all = (orc_scored *)malloc(((size_t)m + 1) * sizeof(orc_scored));
+    if (!all) return ORC_ERR_NOMEM;
+    m = 0;
+    for (int64_t v = 0; v < num_nodes; ++v)
+        if (score[v] > 0.0) {
+            all[m].score = score[v];
+            all[m].id = (int32_t)v;
+            ++m;
+        }
+    qsort(all, (size_t)m, sizeof(orc_scored), cmp_scored);
+    const int64_t c = m < k ? m : k;
+    for (int64_t i = 0; i < c; ++i) out[i] = all[i].id;
+    free(all);
+    qsort(out, (size_t)c, sizeof(int32_t), cmp_i32);
+    return c;
 }

@@ -42,8 +42,10 @@ def test_ctypes_layout_matches_header(tmp_path):
 #define O(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
 int main(void) {
   S(gnn_graph) S(gnn_caps) S(gnn_block) S(gnn_blocks) S(gnn_options) S(gnn_minibatch_out)
+  S(gnn_dyn_cache_params) S(gnn_dyn_cache_info)
   O(gnn_graph, indices) O(gnn_graph, adj_rows) O(gnn_caps, nodes) O(gnn_blocks, counts) O(gnn_minibatch_out, ld_h)
-  O(gnn_minibatch_out, x) O(gnn_options, flags) return 0; }
+  O(gnn_minibatch_out, x) O(gnn_options, flags) O(gnn_options, d_hits) O(gnn_dyn_cache_params, flags)
+  O(gnn_dyn_cache_info, members) O(gnn_dyn_cache_info, last_evicted) return 0; }
 ''')
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
@@ -61,6 +63,12 @@ int main(void) {
         "gnn_minibatch_out.ld_h": _abi.gnn_minibatch_out.ld_h.offset,
         "gnn_minibatch_out.x": _abi.gnn_minibatch_out.x.offset,
         "gnn_options.flags": _abi.gnn_options.flags.offset,
+        "gnn_options.d_hits": _abi.gnn_options.d_hits.offset,
+        "gnn_dyn_cache_params": ctypes.sizeof(_abi.gnn_dyn_cache_params),
+        "gnn_dyn_cache_info": ctypes.sizeof(_abi.gnn_dyn_cache_info),
+        "gnn_dyn_cache_params.flags": _abi.gnn_dyn_cache_params.flags.offset,
+        "gnn_dyn_cache_info.members": _abi.gnn_dyn_cache_info.members.offset,
+        "gnn_dyn_cache_info.last_evicted": _abi.gnn_dyn_cache_info.last_evicted.offset,
     }
     for k, v in py.items():
         assert int(got[k]) == v, k
@@ -287,3 +295,17 @@ def test_relabel_path_flags_exclusive():
     both.flags = gm.GNN_RELABEL_SORT | gm.GNN_RELABEL_BITMAP
     assert L.gnn_sample_khop(ctypes.byref(g), 8, 4, fo, 1, 0, ctypes.byref(blocks), 8, 1 << 20,
                              ctypes.byref(both), None) == gm.GNN_ERR_INVALID_ARG
+
+
+def test_dynamic_cache_host_checks():
+    """The Dynamic-Cache entry points refuse a missing store or parameters before any device work."""
+    L = gm.lib()
+    p = _abi.gnn_dyn_cache_params(0.9, 10, 2, 0, 0)
+    assert L.gnn_feature_store_enable_dynamic(None, ctypes.byref(p)) == gm.GNN_ERR_INVALID_ARG
+    assert L.gnn_feature_store_enable_dynamic(8, None) == gm.GNN_ERR_INVALID_ARG
+    r = ctypes.c_int32(7)
+    assert L.gnn_dyn_cache_update(None, ctypes.byref(r), None, None) == gm.GNN_ERR_INVALID_ARG
+    assert r.value == 0
+    info = _abi.gnn_dyn_cache_info()
+    assert L.gnn_dyn_cache_query(None, ctypes.byref(info)) == gm.GNN_ERR_INVALID_ARG
+    assert L.gnn_dyn_cache_state(None, None, None, None) == gm.GNN_ERR_INVALID_ARG
