@@ -146,6 +146,19 @@ def main():
     ap.add_argument("--host-indices", action="store_true",
                     help="the graph's neighbour ids in pinned host memory, read in place by the "
                          "sampler (indptr stays in HBM)")
+    ap.add_argument("--dyn-passes", type=int, default=-1,
+                    help="Dynamic-Cache region: passes of --steps fresh super-batches each, measured "
+                         "with the static cache alone and then with the Dynamic-Cache on (default: 4 "
+                         "for a workload with host-resident features, else 0 = off)")
+    ap.add_argument("--cache-gb", type=float, default=-1.0,
+                    help="static hot-row cache size in GB replacing the workload's (a sensitivity "
+                         "run; the workload's own size is the measured configuration)")
+    ap.add_argument("--dyn-gamma", type=float, default=DYN_GAMMA)
+    ap.add_argument("--dyn-rows", type=int, default=0,
+                    help="Dynamic-Cache rows (default: 1/8 of the static cache's rows)")
+    ap.add_argument("--dyn-t-update", type=int, default=0,
+                    help="mini-batches between refreshes (default: one super-batch)")
+    ap.add_argument("--dyn-max-refreshes", type=int, default=0)
     ap.add_argument("--adj-cache-gb", type=float, default=0.0,
                     help="with --host-indices: an HBM adjacency cache of this many GB of "
                          "pre-sampled hot rows")
@@ -226,6 +239,9 @@ def main():
                  f"{adj_cache.entries if adj_cache else 0} ids, {adj['setup_s']:.1f} s")
     cache_rows, t_rank = 0, 0.0
     hot_order = None
+    if args.cache_gb >= 0:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, cache_bytes=int(args.cache_gb * 1e9))
     if cfg.cache_bytes:
         from graph_mini_pipeline_amd.hotness import presample_hot_order
         t1 = time.perf_counter()
@@ -573,6 +589,11 @@ def main():
     if not args.no_sage:
         result["sage_layer"] = sage_layer(gm, cfg, dg, fs, order, dev)
         progress("GraphSAGE layer timed")
+    dyn_passes = args.dyn_passes if args.dyn_passes >= 0 else (4 if cfg.host_features else 0)
+    if dyn_passes > 0:
+        result["dynamic_cache"] = dynamic_cache_region(gm, cfg, args, dg, fs, order, G, steps,
+                                                       cache_rows, hot_order, dyn_passes, dev)
+        progress("Dynamic-Cache region done")
     progress("stage timing and counts done")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, graph, table, step, args.cpu_seconds,
@@ -582,6 +603,132 @@ def main():
 
 STAGE_NAMES = ("sample_relabel", "gather", "mean_outer_block", "mean_other_blocks",
                "sampling_kernel_only")
+
+
+# Dynamic-Cache policy (the pages leave gamma, K_dyn and T_update open); measured on the
+# billion-edge workload over gamma 0.98-0.999, T_update 16-128 mini-batches and K_dyn 1/32 to 1/2
+# of the static cache's rows: the refresh costs about 0.5 ms whatever its interval, so the longest
+# interval measured costs least per step, and the longer memory keeps more of the recurring rows.
+DYN_GAMMA = 0.995                # per mini-batch: a node's weight halves after 138 mini-batches
+DYN_T_UPDATE_SUPERBATCHES = 8    # refresh interval in super-batches
+
+
+def dynamic_cache_region(gm, cfg, args, dg, fs, order, G, steps, cache_rows, hot_order, passes,
+                         dev):
+    """GARDEN Sec. IV.B, eq. (5)-(6), measured: pass r runs super-batches r*steps .. (r+1)*steps-1
+    of the seed order (batch seed = super-batch index), one stream.  First every pass with the
+    static cache alone: an untimed pass for the sizes, the cache hits and the set of rows it
+    misses, then a timed pass.  Then the Dynamic-Cache is enabled on the same store and every
+    pass is timed again, the refresh due after each super-batch included, so pass r > 0 runs on a
+    cache adapted to passes 0..r-1 (the static cache is never changed).  Misses cross the host
+    link; the gathered rows are the same either way."""
+    import numpy as np
+    import torch
+    K = len(cfg.fanouts)
+    n_batches = (order.numel() + cfg.batch - 1) // cfg.batch
+    if passes * steps * G + PRESAMPLE_BATCHES > n_batches:
+        raise SystemExit("Dynamic-Cache passes would reach the pre-sampling seeds")
+    k_dyn = args.dyn_rows or max(1, cache_rows // 8)
+    t_update = args.dyn_t_update or DYN_T_UPDATE_SUPERBATCHES * G
+    caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, cfg.num_nodes)
+    ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, G), dtype=torch.uint8, device=dev)
+    outs = {}
+    hits = torch.zeros(1, dtype=torch.int64, device=dev)
+    opts = gm.Options(d_hits=hits)
+    is_static = torch.zeros(cfg.num_nodes, dtype=torch.bool, device=dev)
+    if cache_rows:
+        is_static[hot_order[:cache_rows].long()] = True
+
+    def run(sb):
+        bs = list(range(sb * G, min(sb * G + G, n_batches)))
+        lo, hi = bs[0] * cfg.batch, min(order.numel(), (bs[-1] + 1) * cfg.batch)
+        ptr = [b * cfg.batch - lo for b in bs] + [hi - lo]
+        mine = []
+        for j in range(len(bs)):
+            n = ptr[j + 1] - ptr[j]
+            if (j, n) not in outs:
+                outs[(j, n)] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
+                                               cfg.d, cfg.ld)
+            mine.append(outs[(j, n)])
+        gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts,
+                         gm.gnn_batch_seed(cfg.rng_seed, sb), mine, ws, opts)
+        return mine
+
+    def timed_pass(r, dynamic):
+        ev = []
+        hits.zero_()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for sb in range(r * steps, (r + 1) * steps):
+            run(sb)
+            if dynamic:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                gm.gnn_dyn_cache_update(fs)
+                e1.record()
+                ev.append((e0, e1))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        assert gm.gnn_read_device_status(ws) == gm.GNN_OK
+        refresh_ms = sum(a.elapsed_time(b) for a, b in ev)
+        return wall, int(hits.item()), refresh_ms
+
+    rows, static_hits, recur, static_wall = [], [], [], []
+    prev_miss = None
+    for r in range(passes):
+        n_rows = 0
+        hits.zero_()
+        miss = torch.zeros(cfg.num_nodes, dtype=torch.bool, device=dev)
+        for sb in range(r * steps, (r + 1) * steps):
+            for out in run(sb):
+                torch.cuda.synchronize()
+                nk = int(out.blocks.counts[2 * K - 1].item())
+                vk = out.blocks.nodes[K - 1][:nk].long()
+                n_rows += nk
+                miss[vk[~is_static[vk]]] = True
+        rows.append(n_rows)
+        static_hits.append(int(hits.item()))
+        if prev_miss is not None:
+            recur.append(int((miss & prev_miss).sum().item()) / max(1, int(miss.sum().item())))
+        prev_miss = miss
+        static_wall.append(timed_pass(r, False)[0])
+    del miss, prev_miss
+    t1 = time.perf_counter()
+    gm.gnn_feature_store_enable_dynamic(fs, args.dyn_gamma, k_dyn, t_update,
+                                        max_refreshes=args.dyn_max_refreshes)
+    setup_s = time.perf_counter() - t1
+    out = []
+    for r in range(passes):
+        wall, h, refresh_ms = timed_pass(r, True)
+        info = gm.gnn_dyn_cache_query(fs)
+        miss_s = (rows[r] - static_hits[r]) * cfg.d * 4
+        miss_d = (rows[r] - h) * cfg.d * 4
+        out.append({
+            "pass": r, "superbatches": [r * steps, (r + 1) * steps], "rows": rows[r],
+            "static": {"hit_rate": static_hits[r] / max(1, rows[r]),
+                       "ms_per_step": static_wall[r] / steps * 1e3,
+                       "host_link_GB_per_step": miss_s / steps / 1e9},
+            "dynamic": {"hit_rate": h / max(1, rows[r]),
+                        "ms_per_step": wall / steps * 1e3,
+                        "host_link_GB_per_step": miss_d / steps / 1e9,
+                        "refresh_ms_per_step": refresh_ms / steps,
+                        "refreshes": info["refreshes"], "members": info["members"],
+                        "resident": info["resident"], "last_published": info["last_published"],
+                        "last_candidates": info["last_candidates"],
+                        "last_admitted": info["last_admitted"],
+                        "last_evicted": info["last_evicted"]},
+            "static_miss_recurrence": recur[r - 1] if r > 0 else None})
+        progress(f"Dynamic-Cache pass {r}: hit rate {static_hits[r] / max(1, rows[r]):.4f} -> "
+                 f"{h / max(1, rows[r]):.4f}, {static_wall[r] / steps * 1e3:.2f} -> "
+                 f"{wall / steps * 1e3:.2f} ms per step")
+    return {"gamma": args.dyn_gamma, "k_dyn": k_dyn, "t_update": t_update,
+            "max_refreshes": args.dyn_max_refreshes,
+            "rows_GB": k_dyn * cfg.ld * 4 / 1e9,
+            "bookkeeping_GB": (cfg.num_nodes * 20 + (cfg.num_nodes + 31) // 32 * 8 + k_dyn * 13) / 1e9,
+            "setup_s": setup_s, "passes": out,
+            "static_miss_recurrence": "fraction of the distinct nodes missed by the static cache "
+                                      "in a pass that it also missed in the pass before",
+            "note": "one stream; pass r > 0 runs on the Dynamic-Cache as pass r - 1 left it"}
 
 
 def percentiles(stages):

@@ -68,7 +68,8 @@ class gnn_dyn_cache_params(ctypes.Structure):
 class gnn_dyn_cache_info(ctypes.Structure):
     _fields_ = [("steps", i64), ("since_refresh", i64), ("refreshes", i32), ("due", i32),
                 ("frozen", i32), ("reserved", i32), ("members", i64), ("last_candidates", i64),
-                ("last_admitted", i64), ("last_evicted", i64)]
+                ("last_admitted", i64), ("last_evicted", i64), ("resident", i64),
+                ("last_published", i64)]
 
 
 class gnn_minibatch_out(ctypes.Structure):

@@ -376,11 +376,21 @@ constexpr int kBitmapTile = kBitmapThreads * kBitmapWordsPerThread;
 // step t: all scores decay by the same factor per step, none has to be touched to decay, and the
 // order of the S(v) is the order of the Score(v, t).  Observed nodes are marked in the touched
 // bitmap, which also holds the current Dynamic-Cache members (set at each refresh).
+//
+// Slots: s >= 0 -- the row is in cache row s; -1 -- not cached; s <= -2 -- a Dynamic-Cache member
+// whose row (-2 - s of the Dynamic-Cache region) is reserved but not filled yet.  Such a row is
+// read from the table, and the gather that reads it also writes it to the reserved row and marks
+// it filled (fill on miss: taking a node in moves no row by itself); the next refresh, after
+// which no gather of before it still runs, makes filled rows resident (slot >= 0).
 struct DynObserve {
     double *score;        // [num_rows] scaled scores; NULL: no observation
     uint32_t *touched;    // [ceil(num_rows / 32)]
     int32_t static_rows;  // cache slots below this one hold the static cache
+    uint8_t *filled;      // [k_dyn] reserved rows written by a gather; NULL: no Dynamic-Cache
 };
+
+// The reserved Dynamic-Cache row of a pending member's slot value, else -1.
+__device__ __forceinline__ int32_t dyn_pending_row(int32_t sl) { return sl <= -2 ? -2 - sl : -1; }
 
 // Observation of the requested row of node v (0 <= v < num_rows) whose cache slot is sl.
 __device__ __forceinline__ void dyn_observe(const DynObserve &o, int32_t v, int32_t sl, double w) {
@@ -393,19 +403,22 @@ __device__ __forceinline__ void dyn_observe(const DynObserve &o, int32_t v, int3
 
 // Device state of a Dynamic-Cache refresh (eq. 6): the top-k selection's radix digits, the
 // candidate count and the free-row stack.  Written by the refresh kernels only.
+constexpr int kDynBins = 2048;   // 11-bit digits
 struct DynState {
-    int64_t n_cand;       // candidates of this refresh (touched nodes)
+    int64_t n_cand;       // candidates of this refresh (touched nodes and members)
     int64_t remaining;    // rank still to place within the digits chosen so far
-    uint64_t key_prefix;  // digits chosen so far of the k-th largest key, then that key
-    uint64_t key_mask;
-    uint32_t id_prefix;   // among keys equal to it: digits of the largest id taken
-    uint32_t id_mask;
+    uint32_t hi_prefix, hi_mask;   // digits chosen so far of the k-th largest key (high word),
+    uint32_t lo_prefix, lo_mask;   // (low word), then among keys equal to it, of the largest
+    uint32_t id_prefix, id_mask;   // id taken
     int64_t n_admit;      // nodes entering the cache in this refresh
     int64_t n_evict;      // members leaving it
+    int64_t n_evict_resident;      // of which resident
+    int64_t n_published;  // filled rows made resident by this refresh
+    int64_t n_resident;   // members resident after it (the others wait for their fill)
     int64_t free_top;     // rows on the free-row stack
     int64_t members;      // rows in use after the refresh
     int64_t refreshes;
-    uint32_t hist[256];
+    uint32_t hist[kDynBins];
 };
 
 // Kernel launchers (each returns hipGetLastError()).
@@ -417,7 +430,7 @@ hipError_t launch_relabel(RelabelArgs a, hipStream_t s);
 // Look-back words a launch_relabel call needs in a.lb, besides its nbm ticket counters.
 int64_t relabel_lb_words(const RelabelArgs &a);
 hipError_t launch_dist(const DistArgs &a, hipStream_t s);
-hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
+hipError_t launch_gather(const float *table, float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
                          int32_t *status, hipStream_t s, const DynObserve *obs = nullptr,
@@ -436,7 +449,7 @@ struct GatherBatchArgs {
     GatherSeg seg[kMaxGroup];
     int32_t nseg;
     const float *table;
-    const float *cache;
+    float *cache;      // written only to fill reserved Dynamic-Cache rows
     const int32_t *slot;
     int64_t ld;
     int32_t d;
@@ -504,33 +517,37 @@ hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t 
                              const int32_t *hot, int64_t rows, float *cache, int32_t *slot,
                              int32_t *status, hipStream_t s);
 
-// Dynamic-Cache (GARDEN, Sec. IV.B, eq. 6).  Set-up: free rows 0..k-1 on the stack, state zero.
-hipError_t launch_dyn_init(DynState *st, int32_t *free_rows, int64_t k, hipStream_t s);
+// Dynamic-Cache (GARDEN, Sec. IV.B, eq. 6).  Set-up: free rows 0..k-1 on the stack, no row held
+// or filled, state zero.
+hipError_t launch_dyn_init(DynState *st, int32_t *free_rows, int32_t *row_node, uint8_t *filled,
+                           int64_t k, hipStream_t s);
 // score[v] *= factor for every node (factor a power of two: exact for normal numbers).
 hipError_t launch_dyn_rescale(double *score, int64_t n, double factor, hipStream_t s);
-// One refresh: the k_dyn touched nodes of largest scaled score (ties: smaller id first) become
-// the members; members left out lose their slot and row, nodes taken in get a free row (copied
-// from the table) and their slot.  The touched bitmap is left holding exactly the members.
+// One refresh: filled rows become resident; then the k_dyn touched nodes of largest scaled score
+// (ties: smaller id first) become the members; members left out lose their slot and row, nodes
+// taken in get a reserved row (filled by a later gather).  The touched bitmap is left holding
+// exactly the members.  publish_only: only the first step (a frozen cache).
 struct DynRefreshArgs {
     DynState *st;
     double *score;
     uint32_t *touched;
+    uint32_t *member;     // [ceil(num_rows / 32)] Dynamic-Cache members
     int64_t num_rows;
-    int32_t *cand;        // [num_rows] candidate ids
-    uint64_t *keys;       // [num_rows] their scaled scores' bits
+    uint32_t *cand;       // [num_rows] candidate ids, bit 31 set for members
+    uint32_t *key_hi;     // [num_rows] high and low words of the bits of their scaled scores
+    uint32_t *key_lo;
     int32_t *free_rows;   // [k_dyn] free-row stack
     int32_t *admit;       // [k_dyn] nodes taken in
+    int32_t *row_node;    // [k_dyn] member holding each row, -1 if free
+    uint8_t *filled;      // [k_dyn rounded up to 4]
     int64_t k_dyn;
     int32_t static_rows;
     int32_t *slot;
-    float *cache;
-    const float *table;
-    int64_t ld, d;
     int32_t *status;
 };
-hipError_t launch_dyn_refresh(const DynRefreshArgs &a, hipStream_t s);
-// Inspection: out_score[v] = score[v] * scale and out_member[v] = 1 for Dynamic-Cache members
-// (either output may be NULL).
+hipError_t launch_dyn_refresh(const DynRefreshArgs &a, bool publish_only, hipStream_t s);
+// Inspection: out_score[v] = score[v] * scale and out_member[v] = 1 for resident Dynamic-Cache
+// members, 2 for members waiting for their fill, else 0 (either output may be NULL).
 hipError_t launch_dyn_state(const double *score, int64_t n, double scale, const int32_t *slot,
                             int32_t static_rows, double *out_score, uint8_t *out_member,
                             hipStream_t s);

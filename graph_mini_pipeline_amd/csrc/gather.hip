@@ -22,7 +22,7 @@ namespace gnnmb {
 
 struct GatherArgs {
     const float *table;
-    const float *cache;
+    float *cache;   // written only to fill reserved Dynamic-Cache rows
     const int32_t *slot;
     int64_t ld;
     int32_t d;
@@ -70,6 +70,25 @@ __device__ __forceinline__ const float *row_ptr(const float *table, const float 
                   : cache + static_cast<int64_t>(-2 - c) * ld;
 }
 
+// A row's chunks held by one lane (CH chunks, G lanes apart) written to a reserved Dynamic-Cache
+// row: ordinary stores, as the row is read again from there.
+template <int CH>
+__device__ __forceinline__ void store_cache_row(float *c, const f32x4 (&v)[CH], const bool (&act)[CH],
+                                                uint32_t ch0, int G, int d) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        if (!act[q]) continue;
+        const int col = static_cast<int>(ch0 + q * G) * 4;
+        const int rem = d - col;
+        if (rem >= 4) {
+            *reinterpret_cast<f32x4 *>(c + col) = v[q];
+        } else {
+            const float t[4] = {v[q][0], v[q][1], v[q][2], v[q][3]};
+            for (int w = 0; w < rem; ++w) c[col + w] = t[w];
+        }
+    }
+}
+
 template <int VEC, int U>
 __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
     using vec_t = typename std::conditional<VEC == 4, f32x4, float>::type;
@@ -80,11 +99,13 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
     for (uint32_t base = blockIdx.x * 256u * U + threadIdx.x; base < total; base += stride) {
         vec_t val[U];
         float *dst[U];
+        float *fill[U];   // the reserved Dynamic-Cache row of a pending member, else NULL
         int rem[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t idx = base + u * 256u;
             dst[u] = nullptr;
+            fill[u] = nullptr;
             rem[u] = 0;
             if (idx < total) {
                 const uint32_t row = fast_div(idx, g.cpr);
@@ -104,6 +125,11 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
                     src = g.table + static_cast<int64_t>(v) * g.ld;
                 }
                 const int col = static_cast<int>(ch) * VEC;
+                const int32_t fr = g.obs.filled ? dyn_pending_row(sl) : -1;
+                if (fr >= 0) {
+                    fill[u] = g.cache + (static_cast<int64_t>(g.obs.static_rows) + fr) * g.ld + col;
+                    if (ch == 0) g.obs.filled[fr] = 1;
+                }
                 dst[u] = g.out + static_cast<int64_t>(row) * g.ld_out + col;
                 rem[u] = g.d - col;
                 if (VEC == 1 || rem[u] >= VEC) {
@@ -120,9 +146,12 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
             if (dst[u] == nullptr) continue;
             if (VEC == 1 || rem[u] >= VEC) {
                 *reinterpret_cast<vec_t *>(dst[u]) = val[u];
+                if (fill[u]) *reinterpret_cast<vec_t *>(fill[u]) = val[u];
             } else if constexpr (VEC == 4) {
                 const float t[4] = {val[u][0], val[u][1], val[u][2], val[u][3]};
                 for (int q = 0; q < rem[u]; ++q) dst[u][q] = t[q];
+                if (fill[u])
+                    for (int q = 0; q < rem[u]; ++q) fill[u][q] = t[q];
             }
         }
     }
@@ -151,9 +180,11 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
         const uint32_t p = it - rb * slabs;     // slab of the row
         const int64_t r0 = static_cast<int64_t>(rb) * rpu;
         const int nb = static_cast<int>(n - r0 < rpu ? n - r0 : rpu);
-        // lane t: id and source row code of output row r0 + t (-1: invalid id)
+        // lane t: id and source row code of output row r0 + t (-1: invalid id), and the reserved
+        // Dynamic-Cache row the row also goes to (-1: none)
         int32_t mine = -1;
         int32_t vid = -1;
+        int32_t fill = -1;
         if (gl < nb) {
             const int32_t v = g.ids[r0 + gl];
             vid = v;
@@ -161,8 +192,13 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
                 set_status(g.status, GNN_ERR_OUT_OF_RANGE);
             } else {
                 const int32_t sl = g.slot ? g.slot[v] : -1;
-                if constexpr (!SCAT)
+                if constexpr (!SCAT) {
                     if (g.obs.score && p == 0) dyn_observe(g.obs, v, sl, g.obs_w);
+                    if (g.obs.filled) {
+                        fill = dyn_pending_row(sl);
+                        if (fill >= 0 && p == 0) g.obs.filled[fill] = 1;
+                    }
+                }
                 if (sl >= 0) {
                     mine = -2 - sl;
                     hits += p == 0;
@@ -237,6 +273,14 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
                         }
                     } else {
                         store_row(g.out + (r0 + er) * g.ld_out);
+                        if (g.obs.filled) {
+                            int32_t fr;
+                            if constexpr (G == 64) fr = __builtin_amdgcn_readlane(fill, er);
+                            else fr = __shfl(fill, grp * G + er, 64);
+                            if (fr >= 0)
+                                store_cache_row(g.cache + (static_cast<int64_t>(g.obs.static_rows) + fr) * g.ld,
+                                                v[r], act, ch0, G, g.d);
+                        }
                     }
                 }
                 const int en = er + R;
@@ -308,8 +352,10 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
         const int64_t r0 = static_cast<int64_t>(rb) * G;
         const int64_t n = s_n[sg];
         const int nb = static_cast<int>(n - r0 < G ? n - r0 : G);
-        // lane t: source row of output row r0 + t (NULL: invalid id)
+        // lane t: source row of output row r0 + t (NULL: invalid id), and the reserved Dynamic-Cache
+        // row the row also goes to (-1: none)
         int32_t mine = -1;
+        int32_t fill = -1;
         if (gl < nb) {
             const int32_t v = S.ids[r0 + gl];
             if (v < 0 || v >= a.num_rows) {
@@ -317,6 +363,10 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
             } else {
                 const int32_t sl = a.slot ? a.slot[v] : -1;
                 if (a.obs.score && p == 0) dyn_observe(a.obs, v, sl, S.obs_w);
+                if (a.obs.filled) {
+                    fill = dyn_pending_row(sl);
+                    if (fill >= 0 && p == 0) a.obs.filled[fill] = 1;
+                }
                 hits += sl >= 0 && p == 0;
                 mine = sl >= 0 ? -2 - sl : v;
             }
@@ -359,6 +409,14 @@ __global__ __launch_bounds__(256) void k_gather_batch(GatherBatchArgs a) {
                             for (int w = 0; w < rem; ++w) o[col + w] = t[w];
                         }
                     }
+                    if (a.obs.filled) {
+                        int32_t fr;
+                        if constexpr (G == 64) fr = __builtin_amdgcn_readlane(fill, er);
+                        else fr = __shfl(fill, grp * G + er, 64);
+                        if (fr >= 0)
+                            store_cache_row(a.cache + (static_cast<int64_t>(a.obs.static_rows) + fr) * a.ld,
+                                            v[r], act, ch0, G, a.d);
+                    }
                 }
                 const int en = er + R;
                 const int32_t c = code_of(en);
@@ -396,7 +454,7 @@ void launch_rows(const GatherArgs &g, int G, int CH, dim3 grid, hipStream_t s) {
     else hipLaunchKernelGGL((k_gather_rows<64, 4, 8, SCAT>), grid, dim3(256), 0, s, g);
 }
 
-hipError_t launch_gather(const float *table, const float *cache, const int32_t *slot, int64_t ld,
+hipError_t launch_gather(const float *table, float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
                          int32_t *status, hipStream_t s, const DynObserve *obs, double obs_w) {

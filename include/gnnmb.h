@@ -286,13 +286,18 @@ gnn_status gnn_feature_store_destroy(gnn_feature_store *fs);
  * observed since the last one, makes the cache hold the k_dyn nodes of highest score, eq. (6)
  * (ties: the smaller id; only nodes with a positive score; fewer than k_dyn if fewer have one).
  * After max_refreshes refreshes (0: no limit) the cache is frozen and nothing more is observed.
+ * Residency: a refresh reserves a row for each node it takes in but copies nothing; the next
+ * gather that reads the node's row from the table (a miss) also writes it to the reserved row, and
+ * the next refresh due (or, frozen, the next gnn_dyn_cache_update after t_update more
+ * mini-batches) makes such rows resident, so a member's row is read from the cache from then on.
  * Results never change: a gather returns the table's rows whichever cache holds them.
  *   gamma: 0 < gamma < 1; k_dyn >= 1 and cache_rows + k_dyn <= num_nodes; t_update >= 1.
  *   flags: GNN_DYN_AUTO -- the gather call that completes an interval refreshes at its end, on its
  *     own stream; else only gnn_dyn_cache_update refreshes.
- * Memory: k_dyn * ld floats of cache, and 20.125 bytes per node (score, candidate list and key,
- * touched bitmap); the cache is re-allocated (static rows copied).  Setup call: allocates,
- * synchronises the device, and must not overlap any use of the store.
+ * Memory: k_dyn * ld floats of cache and 13 bytes per row of bookkeeping, and 20.25 bytes per
+ * node (score, candidate list and key, touched and member bitmaps); the cache is re-allocated
+ * (static rows copied).  Setup call: allocates, synchronises the device, and must not overlap
+ * any use of the store.
  * Ordering: a refresh rewrites cache rows and slots on its stream; no gather from the store may
  * run concurrently with it on another stream (join the streams around gnn_dyn_cache_update).
  * Observations from several streams may overlap one another.  Calls that use one store are made
@@ -322,7 +327,7 @@ gnn_status gnn_dyn_cache_update(const gnn_feature_store *fs, int32_t *refreshed,
  * (members, and the last refresh's candidates, admissions and evictions).
  */
 typedef struct gnn_dyn_cache_info {
-    int64_t steps;           /* mini-batches observed */
+    int64_t steps;           /* mini-batches gathered from the store since enabled */
     int64_t since_refresh;   /* of which after the last refresh */
     int32_t refreshes;
     int32_t due;             /* a refresh would run now */
@@ -332,13 +337,16 @@ typedef struct gnn_dyn_cache_info {
     int64_t last_candidates;
     int64_t last_admitted;
     int64_t last_evicted;
+    int64_t resident;        /* members whose row is filled and used */
+    int64_t last_published;  /* rows the last refresh made resident */
 } gnn_dyn_cache_info;
 gnn_status gnn_dyn_cache_query(const gnn_feature_store *fs, gnn_dyn_cache_info *out);
 
 /*
  * Inspection on `stream`: score[v] = Score(v, t) after the last observed mini-batch t (device
- * double [num_nodes], or NULL) and member[v] = 1 if v holds a Dynamic-Cache row, else 0 (device
- * uint8 [num_nodes], or NULL).  Errors: GNN_ERR_INVALID_ARG (no Dynamic-Cache).
+ * double [num_nodes], or NULL) and member[v] = 1 if v is a member whose row is resident, 2 if a
+ * member whose row is not filled yet, else 0 (device uint8 [num_nodes], or NULL).
+ * Errors: GNN_ERR_INVALID_ARG (no Dynamic-Cache).
  */
 gnn_status gnn_dyn_cache_state(const gnn_feature_store *fs, double *score, uint8_t *member,
                                gnn_stream stream);

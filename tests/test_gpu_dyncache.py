@@ -7,7 +7,10 @@ oracle's scores at that refresh -- every node scored clearly above the K-th larg
 member, every member is scored no lower than it (up to the same relative 1e-10), and the count is
 min(K_dyn, nodes with a positive score) -- since near-equal scores may round either way.  Gathered
 rows: bit-exact with the table whatever the cache holds, and the cache-hit count equals the rows
-held by the static cache or by the members at the time of the gather.
+held by the static cache or by the resident members at the time of the gather.  Residency: a
+refresh reserves rows for the nodes it takes in and copies nothing; a member's row becomes
+resident at the first refresh (or, frozen, publish) after a gather read it while it was a member,
+and stays so while it remains a member (Residency below).
 """
 import numpy as np
 import pytest
@@ -40,6 +43,23 @@ def check_members(members, score, is_static, k):
     assert missing.size == 0, f"{missing.size} nodes ranked above the K-th score left out"
 
 
+class Residency:
+    """Expected resident members: the rows of the members requested since the last refresh become
+    resident at the next one (before its new membership), and residents stay while members."""
+
+    def __init__(self):
+        self.members, self.resident, self.requested = set(), set(), set()
+
+    def gathered(self, ids):
+        self.requested |= set(np.asarray(ids).tolist()) & self.members
+
+    def refreshed(self, new_members):
+        filled = self.resident | (self.members & self.requested)
+        self.members = set(np.asarray(new_members).tolist())
+        self.resident = filled & self.members
+        self.requested = set()
+
+
 def skewed_ids(rng, n_nodes, n, perm):
     """Requested rows of one mini-batch: Zipf-like ranks (with repeats) mapped through a fixed
     permutation, so some nodes recur across mini-batches and within one."""
@@ -52,7 +72,8 @@ def device_state(fs, n):
     member = torch.empty(n, dtype=torch.uint8, device="cuda")
     gm.gnn_dyn_cache_state(fs, score, member)
     torch.cuda.synchronize()
-    return score.cpu().numpy(), np.nonzero(member.cpu().numpy())[0]
+    m = member.cpu().numpy()
+    return score.cpu().numpy(), np.nonzero(m)[0], np.nonzero(m == 1)[0]
 
 
 @pytest.mark.parametrize("d,ld", [(16, 16), (13, 13), (200, 200)],
@@ -73,15 +94,17 @@ def test_gather_observations_and_refreshes_match_the_oracle(d, ld, auto):
     ref = oracle.DynCache(N, hot, gamma, K, T)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     hits = torch.zeros(1, dtype=torch.int64, device="cuda")
-    members = np.zeros(0, dtype=np.int64)
+    members = resident = np.zeros(0, dtype=np.int64)
+    res = Residency()
     refreshes = 0
     for step in range(16):
         ids = skewed_ids(rng, N, 700 + 37 * step, perm)
-        held = np.union1d(hot, members)
+        held = np.union1d(hot, resident)
         hits.zero_()
         out = torch.full((ids.size, ld), float("nan"), dtype=torch.float32, device="cuda")
         gm.gnn_gather_features(fs, torch.from_numpy(ids).cuda(), out, d_hits=hits, d_status=status)
         ref.observe(ids)
+        res.gathered(ids)
         if auto:
             did = ref.update()
         else:
@@ -93,19 +116,22 @@ def test_gather_observations_and_refreshes_match_the_oracle(d, ld, auto):
         got = out[:, :d].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), x[ids].view(np.uint32)), "gathered rows"
         assert int(hits.item()) == int(np.isin(ids, held).sum()), "cache hits"
-        score, members = device_state(fs, N)
+        score, members, resident = device_state(fs, N)
         np.testing.assert_allclose(score, ref.score, rtol=RTOL, atol=0)
         if did:
             check_members(members, ref.score, ref.is_static, K)
             snap = ref.score.copy()
+            res.refreshed(members)
         elif refreshes:
             check_members(members, snap, ref.is_static, K)
         else:
             assert members.size == 0
+        assert set(members.tolist()) == res.members and set(resident.tolist()) == res.resident
         info = gm.gnn_dyn_cache_query(fs)
         assert info["steps"] == ref.steps and info["refreshes"] == ref.refreshes == refreshes
-        assert info["members"] == members.size
+        assert info["members"] == members.size and info["resident"] == resident.size
     assert refreshes == 16 // T
+    assert 0 < len(res.resident) < len(res.members)
     fs.close()
 
 
@@ -116,19 +142,32 @@ def test_refreshes_stop_after_max_refreshes():
     fs = gm.gnn_feature_store_create(device_table(x, d), d)
     gm.gnn_feature_store_enable_dynamic(fs, 0.9, 100, 2, max_refreshes=2)
     ref = oracle.DynCache(N, [], 0.9, 100, 2, max_refreshes=2)
+    res = Residency()
     perm = rng.permutation(N)
+    since = 0
     for step in range(9):
         ids = skewed_ids(rng, N, 500, perm)
         out = torch.empty(ids.size, d, dtype=torch.float32, device="cuda")
         gm.gnn_gather_features(fs, torch.from_numpy(ids).cuda(), out)
         ref.observe(ids)
-        assert gm.gnn_dyn_cache_update(fs) == ref.update()
+        res.gathered(ids)
+        since += 1
+        frozen = ref.frozen
+        did = gm.gnn_dyn_cache_update(fs)
+        assert did == ref.update()
         assert np.array_equal(out.cpu().numpy(), x[ids])
-    score, members = device_state(fs, N)
+        if did or (frozen and since >= 2):   # a refresh, or (frozen) a publish
+            since = 0
+            _, members, _ = device_state(fs, N)
+            res.refreshed(members)
+        _, members, resident = device_state(fs, N)
+        assert set(resident.tolist()) == res.resident
+    score, members, resident = device_state(fs, N)
     info = gm.gnn_dyn_cache_query(fs)
-    assert info["frozen"] == 1 and info["refreshes"] == 2 and info["steps"] == 4
+    assert info["frozen"] == 1 and info["refreshes"] == 2 and info["steps"] == 9
     np.testing.assert_allclose(score, ref.score, rtol=RTOL, atol=0)
     check_members(members, ref.score, ref.is_static, 100)
+    assert info["resident"] == resident.size > 0
     fs.close()
 
 
@@ -150,7 +189,7 @@ def test_scores_stay_exact_across_the_weight_rescale():
         did = gm.gnn_dyn_cache_update(fs)
         assert did == ref.update()
         if did:
-            score, members = device_state(fs, N)
+            score, members, _ = device_state(fs, N)
             live = ref.score > 1e-250          # far below any member's score
             np.testing.assert_allclose(score[live], ref.score[live], rtol=1e-9, atol=0)
             check_members(members, ref.score, ref.is_static, K)
@@ -185,9 +224,10 @@ def test_superbatches_observe_each_sub_batch(tiny, interleaved):
     hits = torch.zeros(1, dtype=torch.int64, device="cuda")
     opts = gm.Options(gather="interleaved" if interleaved else "auto", d_hits=hits)
     snap = None
-    members = np.zeros(0, dtype=np.int64)
+    resident = np.zeros(0, dtype=np.int64)
+    res = Residency()
     for call in range(7):
-        held = np.union1d(hot, members)
+        held = np.union1d(hot, resident)
         hits.zero_()
         lo = call * G * batch
         seeds = order[lo:lo + G * batch]
@@ -199,14 +239,18 @@ def test_superbatches_observe_each_sub_batch(tiny, interleaved):
         for g in range(G):
             compare_with_oracle(outs[g], refs[g], d)
             ref.observe(refs[g].blocks[-1].nodes)
+            res.gathered(refs[g].blocks[-1].nodes)
         want = sum(int(np.isin(r.blocks[-1].nodes, held).sum()) for r in refs)
         assert int(hits.item()) == want, "cache hits"
-        if ref.update():
+        did = ref.update()
+        score, members, resident = device_state(fs, N)
+        if did:
             snap = ref.score.copy()
-        score, members = device_state(fs, N)
+            res.refreshed(members)
         np.testing.assert_allclose(score, ref.score, rtol=RTOL, atol=0)
         if snap is not None:
             check_members(members, snap, ref.is_static, K)
+        assert set(resident.tolist()) == res.resident
         info = gm.gnn_dyn_cache_query(fs)
         assert info["steps"] == ref.steps and info["refreshes"] == ref.refreshes
     assert ref.refreshes == 3      # after the calls that end at mini-batches 8, 16 and 24
@@ -223,6 +267,7 @@ def test_three_streams_joined_around_the_refresh(tiny):
     K, T, gamma = 300, 6, 0.85
     gm.gnn_feature_store_enable_dynamic(fs, gamma, K, T)
     ref = oracle.DynCache(N, [], gamma, K, T)
+    res = Residency()
     streams = [torch.cuda.Stream() for _ in range(3)]
     caps = gm.gnn_capacity(batch, cfg.fanouts, N)
     wss = [torch.empty(gm.gnn_workspace_size(caps, N, G), dtype=torch.uint8, device="cuda")
@@ -247,18 +292,21 @@ def test_three_streams_joined_around_the_refresh(tiny):
             for g in range(G):
                 compare_with_oracle(outs[g], refs[g], d)
                 ref.observe(refs[g].blocks[-1].nodes)
+                res.gathered(refs[g].blocks[-1].nodes)
         for w in wss:
             assert gm.gnn_read_device_status(w) == gm.GNN_OK
         did = gm.gnn_dyn_cache_update(fs, stream=streams[0])
         assert did == ref.update()
+        torch.cuda.synchronize()
+        score, members, resident = device_state(fs, N)
         if did:
             snap = ref.score.copy()
-        torch.cuda.synchronize()
-        score, members = device_state(fs, N)
+            res.refreshed(members)
         np.testing.assert_allclose(score, ref.score, rtol=RTOL, atol=0)
         if snap is not None:
             check_members(members, snap, ref.is_static, K)
-    assert ref.refreshes == 3
+        assert set(resident.tolist()) == res.resident
+    assert ref.refreshes == 3 and res.resident
     fs.close()
 
 
