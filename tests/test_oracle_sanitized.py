@@ -1,5 +1,5 @@
 """The oracle under AddressSanitizer and UndefinedBehaviorSanitizer (CPU): oracle.c is built with
-both and the oracle's pin tests run against that build in a subprocess with the ASan runtime
+both and the oracle's pin tests (the path's and the Dynamic-Cache's) run against that build in a subprocess with the ASan runtime
 preloaded; any out-of-bounds access, use after free or undefined behaviour aborts the run."""
 import os
 import subprocess
@@ -27,7 +27,8 @@ def test_oracle_pins_under_asan_and_ubsan(tmp_path):
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_dyncache.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=550)
     tail = (r.stdout + r.stderr)[-3000:]
     assert r.returncode == 0, tail
