@@ -636,12 +636,19 @@ hipError_t launch_classify(HopArgs a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Workgroups per role, capped.  Four sampler workgroups fit a CU, so 1024 are resident at a time:
+// the one-wavefront role's 2048 run as two generations, the second taking the CUs that the first
+// frees, which balances their uneven rows at workgroup granularity; the 16-lane role's 1024 fill
+// the machine once the one-wavefront rows are done.  Measured (k_sample per super-batch, caps
+// block/wave/group/full): 2048/1024/512/128 -> 256/2048/1024/256: 111M-node 0.724 -> 0.700 ms,
+// dense 0.187 -> 0.174, mid 0.251 -> 0.240; 4096 or 8192 one-wavefront workgroups, 2048 16-lane
+// ones, or 128 giant-row ones measured equal or slower.
 hipError_t launch_sample(const HopArgs &a, hipStream_t s) {
     const int64_t F = a.F_cap;
-    const int nb_block = static_cast<int>(grid_for(F, 1, 2048));
-    const int nb_wave = static_cast<int>(grid_for(F, kWavesPerBlock, 1024));
-    const int nb_group = static_cast<int>(grid_for(F, kWavesPerBlock * (64 / kGroupLanes), 512));
-    const int nb_full = static_cast<int>(grid_for(F, kBlockThreads, 128));
+    const int nb_block = static_cast<int>(grid_for(F, 1, 256));
+    const int nb_wave = static_cast<int>(grid_for(F, kWavesPerBlock, 2048));
+    const int nb_group = static_cast<int>(grid_for(F, kWavesPerBlock * (64 / kGroupLanes), 1024));
+    const int nb_full = static_cast<int>(grid_for(F, kBlockThreads, 256));
     hipLaunchKernelGGL(k_sample, dim3(nb_block + nb_wave + nb_group + nb_full), dim3(kBlockThreads),
                        0, s, a, nb_block, nb_wave, nb_group);
     return hipGetLastError();
