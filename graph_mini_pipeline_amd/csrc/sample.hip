@@ -227,13 +227,16 @@ __device__ __forceinline__ uint32_t key_high(uint64_t w) {
 }
 __device__ __forceinline__ uint64_t key_full(uint64_t w) { return w ^ (w >> 31); }
 
-// T whose expected number of keys <= tau among deg uniform keys is ~ k + 3 sqrt(k) + 6.
+// T whose expected number of keys <= tau among deg uniform keys is ~ k + 3 sqrt(k) + 6.  Only
+// the number of threshold passes depends on T (any T gives the exact selection), so it is taken
+// in single precision with a fast reciprocal.
 __device__ __forceinline__ uint32_t initial_tau(int64_t deg, int k) {
-    const double mu = static_cast<double>(k) + 3.0 * sqrt(static_cast<double>(k)) + 6.0;
-    const double p = mu / static_cast<double>(deg);
-    if (p >= 1.0) return 0xFFFFFFFFu;
-    const double t = p * 4294967296.0;
-    if (t >= 4294967295.0) return 0xFFFFFFFFu;
+    const float kf = static_cast<float>(k);
+    const float mu = kf + 3.0f * sqrtf(kf) + 6.0f;
+    const float p = __fdividef(mu, static_cast<float>(deg));
+    if (!(p < 1.0f)) return 0xFFFFFFFFu;
+    const float t = p * 4294967296.0f;
+    if (!(t < 4294967040.0f)) return 0xFFFFFFFFu;   // the largest float below 2^32
     return static_cast<uint32_t>(t);
 }
 
@@ -322,6 +325,55 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
     return cnt;
 }
 
+// ---- candidate ranking ------------------------------------------------------------------------------
+//
+// Rank of candidate (kc, jc) among the cnt candidates in s_key / s_pos: how many precede it in
+// (key, position) order.  Eight candidates per round, their LDS loads issued together, so one LDS
+// round trip serves eight comparisons (one per candidate had left a wavefront waiting on LDS for
+// most of its per-node selection).
+__device__ __forceinline__ int rank_of(const uint64_t *s_key, const int32_t *s_pos, int cnt,
+                                       uint64_t kc, int32_t jc) {
+    constexpr int R = 8;
+    int r = 0;
+    int t = 0;
+    for (; t + R <= cnt; t += R) {
+        uint64_t kt[R];
+        int32_t jt[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            kt[q] = s_key[t + q];
+            jt[q] = s_pos[t + q];
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q) r += (kt[q] < kc) | ((kt[q] == kc) & (jt[q] < jc));
+    }
+    for (; t < cnt; ++t) {
+        const uint64_t kt = s_key[t];
+        r += (kt < kc) | ((kt == kc) & (s_pos[t] < jc));
+    }
+    return r;
+}
+
+// Among the cnt positions in s_pos whose sign bit marks them selected, how many selected ones lie
+// before position jc; eight per round as above.
+__device__ __forceinline__ int selected_before(const int32_t *s_pos, int cnt, int32_t jc) {
+    constexpr int R = 8;
+    int r = 0;
+    int t = 0;
+    for (; t + R <= cnt; t += R) {
+        int32_t pt[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) pt[q] = s_pos[t + q];
+#pragma unroll
+        for (int q = 0; q < R; ++q) r += (pt[q] < 0) & ((pt[q] & 0x7FFFFFFF) < jc);
+    }
+    for (; t < cnt; ++t) {
+        const int32_t pt = s_pos[t];
+        r += (pt < 0) & ((pt & 0x7FFFFFFF) < jc);
+    }
+    return r;
+}
+
 // ---- one random node on G lanes of a wavefront ---------------------------------------------------
 //
 // Control flow is uniform across the G lanes of the group; other groups of the same wavefront may
@@ -359,13 +411,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         if (c < cnt) {
             const uint64_t kc = s_key[c];
             jc = s_pos[c];
-            int r = 0;
-            for (int t = 0; t < cnt; ++t) {
-                const uint64_t kt = s_key[t];
-                const int32_t jt = s_pos[t];
-                r += (kt < kc) | ((kt == kc) & (jt < jc));
-            }
-            sel = r < k;
+            sel = rank_of(s_key, s_pos, cnt, kc, jc) < k;
         }
         const uint64_t m = __ballot(sel) & gmask;
         if (sel) {
@@ -467,16 +513,8 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
     // sign bit of their position (positions are < 2^31), then each is placed by position.
     static_assert((kBlockCap + NT - 1) / NT <= 32, "selection bits fit one word");
     uint32_t sel = 0;
-    for (int c = threadIdx.x, b = 0; c < cnt; c += NT, ++b) {
-        const uint64_t kc = s_key[c];
-        const int32_t jc = s_pos[c];
-        int r = 0;
-        for (int t = 0; t < cnt; ++t) {
-            const uint64_t kt = s_key[t];
-            r += (kt < kc) | ((kt == kc) & (s_pos[t] < jc));
-        }
-        if (r < k) sel |= 1u << b;
-    }
+    for (int c = threadIdx.x, b = 0; c < cnt; c += NT, ++b)
+        if (rank_of(s_key, s_pos, cnt, s_key[c], s_pos[c]) < k) sel |= 1u << b;
     __syncthreads();
     for (int c = threadIdx.x, b = 0; c < cnt; c += NT, ++b)
         if (sel & (1u << b)) s_pos[c] |= static_cast<int32_t>(0x80000000u);
@@ -484,12 +522,7 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
     for (int c = threadIdx.x, b = 0; c < cnt; c += NT, ++b) {
         if (!(sel & (1u << b))) continue;
         const int32_t jc = s_pos[c] & 0x7FFFFFFF;
-        int r = 0;
-        for (int t = 0; t < cnt; ++t) {
-            const int32_t pt = s_pos[t];
-            r += (pt < 0) & ((pt & 0x7FFFFFFF) < jc);
-        }
-        emit_id(a, out0 + r, row[jc]);
+        emit_id(a, out0 + selected_before(s_pos, cnt, jc), row[jc]);
     }
     __syncthreads();
 }
