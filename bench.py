@@ -285,7 +285,7 @@ def main():
             n = ptr[j + 1] - ptr[j]
             if (j, n) not in outs[q]:
                 outs[q][(j, n)] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
-                                                  cfg.d, cfg.ld)
+                                                  cfg.d, cfg.ld, stream=streams[q])
             mine.append((b, n, outs[q][(j, n)]))
         gm.gnn_minibatch(dg, fs, od[lo:hi], ptr, cfg.fanouts, gm.gnn_batch_seed(cfg.rng_seed, st),
                          [m[2] for m in mine], wss[q], gm.Options(superbatch=args.superbatch, gather=args.gather),
@@ -361,7 +361,7 @@ def main():
             n = sd.numel()
             if n not in outs1[q]:
                 outs1[q][n] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
-                                              cfg.d, cfg.ld)
+                                              cfg.d, cfg.ld, stream=qs[q])
             gm.gnn_minibatch(dg, fs, sd, [0, n], cfg.fanouts, seed, [outs1[q][n]], ws1[q],
                              gm.Options(gather=args.gather), stream=qs[q])
             return outs1[q][n]

@@ -7,6 +7,7 @@ names of include/gnnmb.h and raise GnnError on a negative status.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence
@@ -209,18 +210,23 @@ def gnn_relabel_workspace_size(id_bound: int) -> int:
 class Blocks:
     """Device buffers of the K blocks of one batch, allocated at the given caps."""
 
-    def __init__(self, caps: _abi.gnn_caps, device="cuda"):
+    def __init__(self, caps: _abi.gnn_caps, device="cuda", stream=None):
+        """`stream`: the stream the blocks are first written on.  The counts are zeroed by a kernel
+        queued on it, so that the zeroing is ordered before that stream's calls (queued on the
+        current stream instead, it could run after the counts of a call on a non-blocking side
+        stream, and wipe them)."""
         self.caps = caps
         K = caps.num_hops
         i32 = torch.int32
-        self.counts = torch.zeros(2 * K, dtype=torch.int64, device=device)
-        self.indptr, self.gid, self.lid, self.dst_lid, self.nodes = [], [], [], [], []
-        for l in range(K):
-            self.indptr.append(torch.empty(caps.frontier[l] + 1, dtype=i32, device=device))
-            self.gid.append(torch.empty(max(caps.edges[l], 1), dtype=i32, device=device))
-            self.lid.append(torch.empty(max(caps.edges[l], 1), dtype=i32, device=device))
-            self.dst_lid.append(torch.empty(max(caps.frontier[l], 1), dtype=i32, device=device))
-            self.nodes.append(torch.empty(max(caps.nodes[l], 1), dtype=i32, device=device))
+        with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+            self.counts = torch.zeros(2 * K, dtype=torch.int64, device=device)
+            self.indptr, self.gid, self.lid, self.dst_lid, self.nodes = [], [], [], [], []
+            for l in range(K):
+                self.indptr.append(torch.empty(caps.frontier[l] + 1, dtype=i32, device=device))
+                self.gid.append(torch.empty(max(caps.edges[l], 1), dtype=i32, device=device))
+                self.lid.append(torch.empty(max(caps.edges[l], 1), dtype=i32, device=device))
+                self.dst_lid.append(torch.empty(max(caps.frontier[l], 1), dtype=i32, device=device))
+                self.nodes.append(torch.empty(max(caps.nodes[l], 1), dtype=i32, device=device))
 
     def c(self) -> _abi.gnn_blocks:
         b = _abi.gnn_blocks()
@@ -476,15 +482,18 @@ def gnn_sage_update(dst_lid: torch.Tensor, src: torch.Tensor, d: int, agg: torch
 class MinibatchOut:
     """Blocks plus X and h_0..h_{K-1} of one (sub-)batch."""
 
-    def __init__(self, caps: _abi.gnn_caps, d: int, ld_h: Optional[int] = None, device="cuda"):
-        self.blocks = Blocks(caps, device)
+    def __init__(self, caps: _abi.gnn_caps, d: int, ld_h: Optional[int] = None, device="cuda",
+                 stream=None):
+        """`stream`: the stream the outputs are first written on (as for Blocks)."""
+        self.blocks = Blocks(caps, device, stream)
         self.d = d
         self.ld_h = ld_h if ld_h is not None else (d + 3) // 4 * 4
         K = caps.num_hops
         f32 = torch.float32
-        self.x = torch.empty(max(caps.nodes[K - 1], 1), self.ld_h, dtype=f32, device=device)
-        self.h = [torch.empty(max(caps.n_seeds if l == 0 else caps.nodes[l - 1], 1), self.ld_h,
-                              dtype=f32, device=device) for l in range(K)]
+        with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+            self.x = torch.empty(max(caps.nodes[K - 1], 1), self.ld_h, dtype=f32, device=device)
+            self.h = [torch.empty(max(caps.n_seeds if l == 0 else caps.nodes[l - 1], 1), self.ld_h,
+                                  dtype=f32, device=device) for l in range(K)]
 
     def c(self) -> _abi.gnn_minibatch_out:
         m = _abi.gnn_minibatch_out()

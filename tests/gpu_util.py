@@ -112,7 +112,7 @@ def headline_layout(cfg, dg, fs, order, steps, G, P=3, rounds=1, opts=None):
                 key = (q, r, j, n)
                 if key not in sets:
                     sets[key] = gm.MinibatchOut(gm.gnn_capacity(n, cfg.fanouts, cfg.num_nodes),
-                                                cfg.d, cfg.ld)
+                                                cfg.d, cfg.ld, stream=streams[q])
                 outs.append(sets[key])
             seed64 = gm.gnn_batch_seed(cfg.rng_seed, st)
             gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, seed64, outs, wss[q], opts,

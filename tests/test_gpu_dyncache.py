@@ -280,9 +280,10 @@ def test_three_streams_joined_around_the_refresh(tiny):
             lo = (call * G * batch) % (order.size - G * batch)
             seeds = order[lo:lo + G * batch]
             ptr = [0, batch, 2 * batch]
-            outs = [gm.MinibatchOut(caps, d, cfg.ld) for _ in range(G)]
+            outs = [gm.MinibatchOut(caps, d, cfg.ld, stream=s) for _ in range(G)]
             seed64 = gm.gnn_batch_seed(cfg.rng_seed, 100 + call)
             seeds_t = torch.from_numpy(seeds).cuda()    # kept alive until the join
+            s.wait_stream(torch.cuda.current_stream())  # the seeds' copy, before the side stream reads them
             gm.gnn_minibatch(dg, fs, seeds_t, ptr, cfg.fanouts, seed64, outs, wss[q], None,
                              stream=s)
             issued.append((seeds, ptr, seed64, outs, seeds_t))
