@@ -580,16 +580,37 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
     }
     bid -= nb_block;
     if (bid < nb_wave) {
-        // The list is ordered by degree bucket, largest first; wavefront w takes item w of even
-        // rounds and item W-1-w of odd ones (W wavefronts), which pairs large rows with small.
+        // The list is ordered by degree bucket, largest first.  Rows of 1024 positions or more
+        // take a wavefront each: wavefront w takes item w of even rounds and item W-1-w of odd ones
+        // (W wavefronts), which pairs large rows with small.  With fanouts up to 10, rows of the
+        // two smallest buckets (fewer than 1024 positions) go two to a wavefront, 32 lanes each,
+        // consecutive items of one bucket together (degrees within 2x of each other), so the
+        // per-row work -- row bounds, threshold, ranking, output -- is shared by two rows
+        // (k_sample per super-batch: 111M-node 0.690 -> 0.673 ms, mid 0.237 -> 0.230; with the
+        // dense workload's fanout 25 pairs measured 5% slower: each row then has ~46 candidates).
         const int64_t n = class_total(a.totals, kWave);
+        const bool pairs_fit = 4 * a.k <= kWaveCap / 2 && a.k <= 10;
+        const int64_t n_pair = pairs_fit ? static_cast<int64_t>(a.totals[3 + kWaveBuckets - 2]) +
+                                               static_cast<int64_t>(a.totals[3 + kWaveBuckets - 1])
+                                         : 0;
+        const int64_t n_one = n - n_pair;
         const int64_t W = static_cast<int64_t>(nb_wave) * kWavesPerBlock;
         const int64_t w = static_cast<int64_t>(bid) * kWavesPerBlock + wv;
-        for (int64_t r0 = 0, round = 0; r0 < n; r0 += W, ++round) {
+        for (int64_t r0 = 0, round = 0; r0 < n_one; r0 += W, ++round) {
             const int64_t item = r0 + ((round & 1) ? W - 1 - w : w);
-            if (item < n)
+            if (item < n_one)
                 sample_node_lanes<64, kWaveCap>(a, wave_item(a, item), s_key + wv * kWaveCap,
                                                 s_pos + wv * kWaveCap, lane, ~0ull, below);
+        }
+        const int half = lane >> 5;
+        const uint64_t hmask = half ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
+        for (int64_t p = w; 2 * p < n_pair; p += W) {
+            const int64_t item = n_one + 2 * p + half;
+            if (item < n)
+                sample_node_lanes<32, kWaveCap / 2>(a, wave_item(a, item),
+                                                    s_key + wv * kWaveCap + half * (kWaveCap / 2),
+                                                    s_pos + wv * kWaveCap + half * (kWaveCap / 2),
+                                                    lane & 31, hmask, below);
         }
         return;
     }
@@ -675,10 +696,12 @@ hipError_t launch_classify(HopArgs a, hipStream_t s) {
 // the machine once the one-wavefront rows are done.  Measured (k_sample per super-batch, caps
 // block/wave/group/full): 2048/1024/512/128 -> 256/2048/1024/256: 111M-node 0.724 -> 0.700 ms,
 // dense 0.187 -> 0.174, mid 0.251 -> 0.240; 4096 or 8192 one-wavefront workgroups, 2048 16-lane
-// ones, or 128 giant-row ones measured equal or slower.
+// ones, or 128 giant-row ones measured equal or slower.  With two short rows to a wavefront, 512
+// giant-row workgroups instead of 256: 111M-node 0.667 -> 0.649 ms, dense and mid unchanged
+// (1024: 0.645, the others unchanged or slower).
 hipError_t launch_sample(const HopArgs &a, hipStream_t s) {
     const int64_t F = a.F_cap;
-    const int nb_block = static_cast<int>(grid_for(F, 1, 256));
+    const int nb_block = static_cast<int>(grid_for(F, 1, 512));
     const int nb_wave = static_cast<int>(grid_for(F, kWavesPerBlock, 2048));
     const int nb_group = static_cast<int>(grid_for(F, kWavesPerBlock * (64 / kGroupLanes), 1024));
     const int nb_full = static_cast<int>(grid_for(F, kBlockThreads, 256));
