@@ -21,7 +21,7 @@ GNN_GATHER_BATCHED = 16
 GNN_RELABEL_SORT = 32
 GNN_RELABEL_BITMAP = 64
 GNN_NOALLOC_MAX_IDS = 1 << 26
-GNN_NOALLOC_SCRATCH_BYTES = (16 << 20) + (64 << 10)
+GNN_NOALLOC_SCRATCH_BYTES = (24 << 20) + (64 << 10)
 GNN_DYN_AUTO = 1
 
 GNN_OK = 0

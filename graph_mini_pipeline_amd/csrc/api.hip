@@ -105,7 +105,7 @@ struct Workspace {
     int32_t *lists;        // [kCats FU_max]
     uint32_t *bitmaps;     // [W] over all node ids, then G more of W words (full super-batch
                            // relabel) or G of Wc words (compact super-batch relabel)
-    uint32_t *wprefix;     // same layout
+    uint2 *rdir;           // rank directory of every bitmap (word prefix, word), same layout
     uint32_t *bsum_w;      // [nbw], then G * nbw or G * nbwc tile popcounts
     uint8_t *bytemaps;     // super-batch: byte maps of the G sub-batch bitmaps (or NULL)
     // super-batch only (the union; the rest: compact relabel only)
@@ -115,7 +115,6 @@ struct Workspace {
     int32_t *upos;         // [G * P] position of each sub-batch frontier node in U_l
     int32_t *f_pos;        // [G * Fs] position of each sub-batch destination in U_{l+1}
     int32_t *e_pos;        // [G * Es] position of each sub-batch sampled id in U_{l+1}
-    uint32_t *bsum_dist;
     // shared outermost means of a super-batch: for each node r of the last hop's union frontier
     // and each sub-batch g, 1 + r's position among g's destinations (0: not there)
     int32_t *inv;          // [U_cap(K-1) * G], valid where the bit of inv_mask is set
@@ -164,6 +163,13 @@ gnn_status relabel_launch(RelabelArgs r, const Workspace &w, hipStream_t s) {
     r.lb = w.take_lb(relabel_lb_words(r), r.nbm);
     if (r.lb.words == nullptr) return GNN_ERR_INTERNAL;
     return launch_relabel(r, s) == hipSuccess ? GNN_OK : GNN_ERR_HIP;
+}
+
+// A super-batch distribution with its look-back words taken from the call's arena.
+gnn_status dist_launch(DistArgs a, const Workspace &w, hipStream_t s) {
+    a.lb = w.take_lb(a.ntiles, a.G);
+    if (a.lb.words == nullptr) return GNN_ERR_INTERNAL;
+    return launch_dist(a, s) == hipSuccess ? GNN_OK : GNN_ERR_HIP;
 }
 
 // Union bound of level l of a super-batch (l < K: hop l's frontier; l = K: the last node set):
@@ -257,10 +263,13 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
     // Look-back chains of every single-pass scan one call launches: relabels (the seeds' union,
     // then per hop the union and the sub-batches; the standalone relabel and the union of the
     // gathered sets), one tile each per 1024 bitmap words of every bitmap, plus a ticket each.
-    // And the classification of every hop: one tile per kClassifyTile frontier nodes.
+    // And the classification of every hop: one tile per kClassifyTile frontier nodes; and a
+    // super-batch's distribution of every hop: one tile per kDistTile destinations of each
+    // sub-batch, plus a ticket each.
     const int64_t sub_tiles = mode == kSuperCompact ? w.nbwc : w.nbw;
+    const int64_t dist_words = G > 1 ? K * (static_cast<int64_t>(G) * (dist_tiles(F_max) + 1) + 1) : 0;
     w.arena_words = (2 * K + 2) * (w.nbw + 1) + K * (static_cast<int64_t>(G) * (sub_tiles + 1) + 1) +
-                    K * (nb_max + 1) + 64;
+                    K * (nb_max + 1) + dist_words + 64;
     w.status = c.take<int32_t>(64);
     w.totals = c.take<uint32_t>(kTotalsStride * GNN_MAX_HOPS);
     w.arena = c.take<uint64_t>(w.arena_words);
@@ -269,7 +278,7 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
     w.d_uE = cnt ? cnt + 16 : nullptr;
     w.lists = c.take<int32_t>(kCats * FU);
     w.bitmaps = c.take<uint32_t>(words);
-    w.wprefix = c.take<uint32_t>(words);
+    w.rdir = c.take<uint2>(words);
     w.bsum_w = c.take<uint32_t>(tiles);
     if (mode != kSuperNone) {
         // byte maps of the sub-batch relabels: marks become plain byte stores
@@ -280,7 +289,6 @@ Workspace carve(const gnn_caps &mc, int64_t N, int G, SuperMode mode, void *ws) 
         w.U[1] = mode == kSuperCompact ? c.take<int32_t>(U_max) : w.U[0];
         w.u_indptr = c.take<int32_t>(FU + 1);
         w.u_gid = c.take<int32_t>(uE_max);
-        w.bsum_dist = c.take<uint32_t>(static_cast<int64_t>(G) * dist_tiles(F_max));
     }
     if (mode == kSuperCompact) {
         w.upos = c.take<int32_t>(static_cast<int64_t>(G) * w.P);
@@ -397,7 +405,7 @@ RelabelArgs relabel_args(const gnn_graph &g, const Workspace &w, int first = 0, 
     r.nbm = nbm;
     r.id_bound = g.num_nodes;
     r.bitmap = w.bitmaps + first * w.W;
-    r.wprefix = w.wprefix + first * w.W;
+    r.rdir = w.rdir + first * w.W;
     r.bsum = w.bsum_w + first * w.nbw;
     r.W = w.W;
     r.nbw = static_cast<int32_t>(w.nbw);
@@ -415,7 +423,7 @@ RelabelArgs compact_relabel_args(const Workspace &w, int G, const int32_t *ulist
     r.d_bound = d_n;
     r.id_map = ulist;
     r.bitmap = w.bitmaps + w.W;
-    r.wprefix = w.wprefix + w.W;
+    r.rdir = w.rdir + w.W;
     r.bsum = w.bsum_w + w.nbw;
     r.W = w.Wc;
     r.nbw = static_cast<int32_t>(w.nbwc);
@@ -468,21 +476,19 @@ gnn_status run_super_full_hop(const gnn_graph &g, FrontFn front, CountFn d_F, Ca
         tiles += nt;
     }
     da.ntiles = tiles;
-    da.bm0 = w.bitmaps;
-    da.wprefix0 = w.wprefix;
+    da.rdir0 = w.rdir;
     da.id_bound = g.num_nodes;
     da.u_indptr = w.u_indptr;
     da.u_gid = w.u_gid;
     da.uE_cap = uEcap;
     da.d_U = w.d_U;
     da.U_cap = Ucap;
-    da.bsum = w.bsum_dist;
     da.status = w.status;
     if (last) {
         da.inv = w.inv;
         da.inv_mask = w.inv_mask;
     }
-    GNN_TRY_HIP(launch_dist(da, s));
+    GNN_TRY(dist_launch(da, w, s));
     // Per-sub-batch relabel into bitmaps 1..G; the union bitmap is zeroed for the next hop.
     RelabelArgs rs = relabel_args(g, w, 1, G);
     rs.bytes = w.bytemaps;
@@ -613,8 +619,7 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         da.u_indptr = w.u_indptr;
         da.u_gid = w.u_gid;
         da.Ul = Ul;
-        da.bm1 = w.bitmaps;
-        da.wprefix1 = w.wprefix;
+        da.rdir1 = w.rdir;
         da.id_bound = g.num_nodes;
         da.uE_cap = uEcap;
         da.d_U = w.d_U + l;
@@ -626,13 +631,12 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
         da.mark_dup = l == 0 ? 1 : 0;
         da.d_U1 = w.d_U + l + 1;
         da.U1_cap = U1cap;
-        da.bsum = w.bsum_dist;
         da.status = w.status;
         if (l == K - 1) {
             da.inv = w.inv;
             da.inv_mask = w.inv_mask;
         }
-        GNN_TRY_HIP(launch_dist(da, s));
+        GNN_TRY(dist_launch(da, w, s));
         // Per-sub-batch relabel in U_{l+1} positions; the positions of V_l become the next hop's.
         RelabelArgs rs = compact_relabel_args(w, G, Ul1, w.d_U + l + 1, U1cap);
         rs.bytes = w.bytemaps;
@@ -729,7 +733,7 @@ gnn_status unique_relabel_in(const Workspace &w, int32_t *status, const int32_t 
     r.out[0] = BitmapOut{uniq, cap_uniq, d_n_uniq, nullptr};
     r.id_bound = id_bound;
     r.bitmap = w.bitmaps;
-    r.wprefix = w.wprefix;
+    r.rdir = w.rdir;
     r.bsum = w.bsum_w;
     r.W = w.W;
     r.nbw = static_cast<int32_t>(w.nbw);
@@ -1495,11 +1499,11 @@ gnn_status gnn_minibatch(const gnn_graph *g, const gnn_feature_store *fs, const 
             float *xs[GNN_MAX_GROUP];
             for (int gi = 0; gi < group; ++gi) xs[gi] = outs[gi].x;
             // the sub-batch relabel bitmaps of the last hop: over U_K positions (compact) or node
-            // ids (full), with their word prefixes
+            // ids (full), by their rank directories
             const bool compact = w.mode == kSuperCompact;
             GNN_TRY_HIP(launch_gather_union(fs->table, fs->ld, d, fs->num_nodes, uK, w.d_U + K,
-                                            union_cap(mc, K, group, g->num_nodes), w.bitmaps + w.W,
-                                            w.wprefix + w.W, compact ? w.Wc : w.W, compact ? 0 : 1,
+                                            union_cap(mc, K, group, g->num_nodes), w.rdir + w.W,
+                                            compact ? w.Wc : w.W, compact ? 0 : 1,
                                             group, xs, outs[0].ld_h, w.status, s));
         } else {
             GNN_TRY_HIP(launch_gather_batch(ga, rows_cap, s));

@@ -281,7 +281,9 @@ struct RelabelArgs {
     uint8_t *bytes;           // optional [nbm * W * 32], zero: lists of pass 0 set byte[id] = 1
                               // (plain stores) and the popcount pass packs bytes into the bitmap
     uint32_t *bitmap;         // [nbm * W]
-    uint32_t *wprefix;        // [nbm * W]
+    uint2 *rdir;              // [nbm * W] rank directory, written by the emit pass: entry w holds
+                              // the set bits before word w and word w itself, so that an id's rank
+                              // is one 8-byte load
     uint32_t *bsum;           // [nbm * nbw] tile popcounts (bitmaps of many tiles)
     int64_t W;
     int32_t nbw;              // tiles per bitmap
@@ -301,14 +303,22 @@ struct RelabelArgs {
 // through the bitmap; whether launch_relabel takes that path for these arguments.
 bool relabel_sorts(const RelabelArgs &a);
 
+// Rank of bit v in a bitmap by its rank directory (entry w: set bits before word w, word w), or
+// -1 when the bit is clear.
+__device__ __forceinline__ int32_t rdir_rank(const uint2 *rd, int64_t v) {
+    const uint2 e = rd[v >> 5];
+    const uint32_t bit = 1u << (v & 31);
+    return (e.y & bit) ? static_cast<int32_t>(e.x + __popc(e.y & (bit - 1u))) : -1;
+}
+
 __device__ __forceinline__ int64_t relabel_bound(const RelabelArgs &a) {
     if (a.d_bound == nullptr) return a.id_bound;
     const int64_t b = *a.d_bound;
     return b < 0 ? 0 : (b < a.id_bound ? b : a.id_bound);
 }
 
-// Destinations per workgroup of the super-batch distribution (one wavefront's lanes).
-constexpr int kDistTile = 64;
+// Destinations per tile of the super-batch distribution: one per thread of its workgroup.
+constexpr int kDistTile = 256;
 
 // One sub-batch of a super-batch hop: its destinations and the block it receives.
 struct DistSub {
@@ -331,8 +341,7 @@ struct DistArgs {
     DistSub sub[kMaxGroup];
     int32_t G;
     int32_t ntiles;
-    const uint32_t *bm0;       // union bitmap and its word prefixes (destinations without upos)
-    const uint32_t *wprefix0;
+    const uint2 *rdir0;        // union bitmap's rank directory (destinations without upos)
     int64_t id_bound;
     const int32_t *u_indptr;   // union block
     const int32_t *u_gid;
@@ -341,7 +350,8 @@ struct DistArgs {
     int64_t U_cap;
     const int64_t *d_U1;       // |U_{l+1}|
     int64_t U1_cap;
-    uint32_t *bsum;            // [ntiles]
+    LbSlice lb;                // look-back words, one per tile (sub-batch g's chain at tile0),
+                               // and one ticket counter per sub-batch
     int32_t *status;
     int32_t *inv;              // optional out [U_cap * G]: inv[r * G + g] = 1 + the position of
                                // union node r among sub-batch g's destinations, written where
@@ -353,11 +363,10 @@ struct DistArgs {
     uint8_t *mark_bytes;
     int64_t mark_stride;
     int32_t mark_dup;
-    // compact relabel: U_l (global ids) and the node-id bitmap of U_{l+1} with its word prefixes;
-    // a position in U_{l+1} is a rank in that bitmap
+    // compact relabel: U_l (global ids) and the rank directory of U_{l+1}'s node-id bitmap; a
+    // position in U_{l+1} is a rank in that bitmap
     const int32_t *Ul;
-    const uint32_t *bm1;
-    const uint32_t *wprefix1;
+    const uint2 *rdir1;
 };
 
 constexpr int kClassifyThreads = 256;
@@ -510,7 +519,7 @@ hipError_t launch_adj_fill(const void *indptr, int32_t ib, const int32_t *indice
                            int64_t *adj_off, hipStream_t s);
 hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                                const int32_t *ids, const int64_t *d_n, int64_t n_cap,
-                               const uint32_t *bm, const uint32_t *wp, int64_t words, int by_id,
+                               const uint2 *rd, int64_t words, int by_id,
                                int G, float *const *outs, int64_t ld_out, int32_t *status,
                                hipStream_t s);
 hipError_t launch_cache_fill(const float *table, int64_t ld, int64_t d, int64_t num_rows,

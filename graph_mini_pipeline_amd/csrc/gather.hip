@@ -36,10 +36,9 @@ struct GatherArgs {
     int32_t *status;
     FastDiv cpr;  // chunks per row
     // scatter (union gather of a super-batch): row r goes to scat_out[s] for every sub-batch s
-    // whose relabel bitmap (scat_bm + s * scat_w, word prefixes scat_wp + s * scat_w) holds the
-    // row's key -- its id (scat_by_id) or r itself -- at the key's rank in that bitmap
-    const uint32_t *scat_bm;
-    const uint32_t *scat_wp;
+    // whose relabel bitmap (rank directory scat_rd + s * scat_w) holds the row's key -- its id
+    // (scat_by_id) or r itself -- at the key's rank in that bitmap
+    const uint2 *scat_rd;
     int64_t scat_w;
     int32_t scat_by_id;
     int32_t scat_g;
@@ -215,11 +214,8 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
             for (int s2 = 0; s2 < kMaxGroup; ++s2) {
                 dest[s2] = 0;
                 if (s2 < g.scat_g && gl < nb && key >= 0 && (key >> 5) < g.scat_w) {
-                    const int64_t wi = s2 * g.scat_w + (key >> 5);
-                    const uint32_t w = g.scat_bm[wi];
-                    const uint32_t b = static_cast<uint32_t>(key & 31);
-                    if ((w >> b) & 1u)
-                        dest[s2] = static_cast<int32_t>(g.scat_wp[wi] + __popc(w & ((1u << b) - 1u))) + 1;
+                    const int32_t r = rdir_rank(g.scat_rd + s2 * g.scat_w, key);
+                    if (r >= 0) dest[s2] = r + 1;
                 }
             }
         }
@@ -465,7 +461,7 @@ hipError_t launch_gather(const float *table, float *cache, const int32_t *slot, 
     const int64_t cpr = (d + vec - 1) / vec;
     GatherArgs g{table, cache, slot, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
                  out, ld_out, d_hits, status, make_fastdiv(static_cast<uint32_t>(cpr)),
-                 nullptr, nullptr, 0, 0, 0, {}, 0, {}, 0.0};
+                 nullptr, 0, 0, 0, {}, 0, {}, 0.0};
     if (obs) {
         g.obs = *obs;
         g.obs_w = obs_w;
@@ -489,7 +485,7 @@ hipError_t launch_gather(const float *table, float *cache, const int32_t *slot, 
 
 hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_t num_rows,
                                const int32_t *ids, const int64_t *d_n, int64_t n_cap,
-                               const uint32_t *bm, const uint32_t *wp, int64_t words, int by_id,
+                               const uint2 *rd, int64_t words, int by_id,
                                int G_sb, float *const *outs, int64_t ld_out, int32_t *status,
                                hipStream_t s) {
     if (G_sb < 1 || G_sb > kMaxGroup) return hipErrorInvalidValue;
@@ -500,7 +496,7 @@ hipError_t launch_gather_union(const float *table, int64_t ld, int64_t d, int64_
     const int64_t cpr = (d + 3) / 4;
     GatherArgs g{table, nullptr, nullptr, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
                  nullptr, ld_out, nullptr, status, make_fastdiv(static_cast<uint32_t>(cpr)),
-                 bm, wp, words, by_id, G_sb, {}, 0, {}, 0.0};
+                 rd, words, by_id, G_sb, {}, 0, {}, 0.0};
     for (int sg = 0; sg < G_sb; ++sg) g.scat_out[sg] = outs[sg];
     const int G = cpr <= 16 ? 16 : (cpr <= 32 ? 32 : 64);
     const int CH = G < 64 ? 1 : static_cast<int>((cpr + 63) / 64 < 4 ? (cpr + 63) / 64 : 4);

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kBitmapThreads) void k_emit_tiles(RelabelArgs a, in
     }
     __syncthreads();
     const uint32_t *words = a.bitmap + static_cast<int64_t>(bm) * a.W;
-    uint32_t *wpre = a.wprefix + static_cast<int64_t>(bm) * a.W;
+    uint2 *rdir = a.rdir + static_cast<int64_t>(bm) * a.W;
     const int64_t tile0 = static_cast<int64_t>(lt) * kBitmapTile;
     const int64_t Wl = live_words(a);
     if (tile0 >= Wl) return;  // whole workgroup: nothing live
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kBitmapThreads) void k_emit_tiles(RelabelArgs a, in
         uint32_t run = base + before + inc[q] - __popc(wd[q]);
         base += tot;
         if (w >= Wl) continue;
-        wpre[w] = run;
+        rdir[w] = make_uint2(run, wd[q]);
         uint32_t bits = wd[q];
         while (bits) {
             const int b = __ffs(bits) - 1;
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a) {
     }
     __syncthreads();
     uint32_t base = s_base;
-    uint32_t *wpre = a.wprefix + static_cast<int64_t>(bm) * a.W;
+    uint2 *rdir = a.rdir + static_cast<int64_t>(bm) * a.W;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         uint32_t before = 0, tot = 0;
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kBitmapThreads) void k_emit(RelabelArgs a) {
         uint32_t run = base + before + inc[q] - __popc(wd[q]);
         base += tot;
         if (w >= Wl) continue;
-        wpre[w] = run;
+        rdir[w] = make_uint2(run, wd[q]);
         uint32_t bits = wd[q];
         while (bits) {
             const int b = __ffs(bits) - 1;
@@ -461,8 +461,8 @@ __global__ __launch_bounds__(256) void k_rank(RelabelArgs a) {
         const int32_t v = L.ids[i];
         int32_t r = -1;
         if (v >= 0 && v < bound) {
-            const int64_t w = static_cast<int64_t>(L.bitmap) * a.W + (v >> 5);
-            r = static_cast<int32_t>(a.wprefix[w] + __popc(a.bitmap[w] & ((1u << (v & 31)) - 1u)));
+            const uint2 e = a.rdir[static_cast<int64_t>(L.bitmap) * a.W + (v >> 5)];
+            r = static_cast<int32_t>(e.x + __popc(e.y & ((1u << (v & 31)) - 1u)));
         }
         L.lid[i] = r;
     }

@@ -28,18 +28,15 @@ __device__ __forceinline__ int find_sub(const DistArgs &a, int t) {
 }
 
 __device__ __forceinline__ int32_t union_rank(const DistArgs &a, int32_t v) {
-    const uint32_t w = a.bm0[v >> 5];
-    return static_cast<int32_t>(a.wprefix0[v >> 5] + __popc(w & ((1u << (v & 31)) - 1u)));
+    const uint2 e = a.rdir0[v >> 5];
+    return static_cast<int32_t>(e.x + __popc(e.y & ((1u << (v & 31)) - 1u)));
 }
 
 // Position in U_{l+1} of node id v (compact relabel): its rank in U_{l+1}'s node-id bitmap, or -1
 // for an id outside the bitmap or not in it (only after an error already reported).
 __device__ __forceinline__ int32_t next_rank(const DistArgs &a, int32_t v) {
     if (v < 0 || v >= a.id_bound) return -1;
-    const uint32_t w = a.bm1[v >> 5];          // both loads issued together
-    const uint32_t pre = a.wprefix1[v >> 5];
-    const uint32_t bit = 1u << (v & 31);
-    return (w & bit) ? static_cast<int32_t>(pre + __popc(w & (bit - 1u))) : -1;
+    return rdir_rank(a.rdir1, v);
 }
 
 // Position p of sub-batch g's relabel (compact relabel), marked as k_mark marks it: a byte when the
@@ -88,139 +85,120 @@ __device__ __forceinline__ void union_row(const DistArgs &a, const DistSub &S, i
     if (a.Ul && want_next) next_pos = next_rank(a, a.Ul[r]);
 }
 
-// Tiles of kDistTile destinations: each wavefront takes a tile, one destination per lane (and,
-// with the compact relabel, marks its position in U_{l+1} for the sub-batch relabel).  The grid
-// is capped (kDistMaxGrid) and workgroups stride over the tiles, which are sized by the
-// frontier bounds: tiles past a sub-batch's actual destinations are skipped, not dispatched.
-__global__ __launch_bounds__(256) void k_dist_count(DistArgs a) {
-    static_assert(kDistTile == 64, "one destination per lane of a wavefront");
-    const int64_t n1 = a.mark_words ? load_count(a.d_U1, a.U1_cap) : 0;   // |U_{l+1}|
-    const int wv = static_cast<int>(threadIdx.x >> 6);
-    const int lane = lane_id();
-    for (int t = blockIdx.x * 4 + wv; t < a.ntiles; t += gridDim.x * 4) {
-        const int sg = find_sub(a, t);
-        const DistSub &S = a.sub[sg];
-        const int64_t F = load_count(S.d_F, S.F_cap);
-        const int64_t i0 = static_cast<int64_t>(t - S.tile0) * kDistTile;
-        if (i0 >= F) continue;   // past the destinations: k_dist_scatter reads no sum for it
-        const int64_t i = i0 + lane;
-        int64_t lo;
-        int32_t c = 0, np, r;
-        if (i < F) {
-            union_row(a, S, i, lo, c, np, r);
-            if (S.f_pos) S.f_pos[i] = np;
-            if (a.mark_words && np >= 0 && np < n1) mark_sub(a, sg, np, a.mark_dup != 0);
-            if (a.inv && r >= 0) {
-                a.inv[static_cast<int64_t>(r) * a.G + sg] = static_cast<int32_t>(i + 1);
-                atomicOr(&a.inv_mask[r], 1u << sg);
-            }
-        }
-        const uint32_t sum = wave_sum(static_cast<uint32_t>(c));
-        if (lane == 0) a.bsum[t] = sum;
-    }
-}
-
-__global__ __launch_bounds__(256) void k_dist_scatter(DistArgs a) {
-    __shared__ uint32_t s_red[2][4];
-    __shared__ uint32_t s_off, s_tot;
-    __shared__ uint32_t s_item_off[kDistTile + 1];
+// One pass over the destinations, in tiles of kDistTile (one per thread): each tile finds its
+// destinations' union rows (and, with the compact relabel, marks their positions in U_{l+1}), sums
+// their lengths, takes the sum of the earlier tiles of its sub-batch by look-back, writes its
+// part of the block indptr and copies its rows' ids.  Workgroup b serves the sub-batch whose
+// tiles hold b; those past the sub-batch's actual destinations leave before taking a ticket (a
+// sub-batch without destinations keeps one tile, which writes the empty block), and the live ones
+// take tickets 0 .. live - 1 from the sub-batch's counter, ticket t being tile t, so that a tile
+// only waits for tiles already running.  The last live tile writes the block's edge count.
+__global__ __launch_bounds__(kDistTile) void k_dist(DistArgs a) {
+    constexpr int NW = kDistTile / 64;
+    __shared__ uint32_t s_wave[NW];
+    __shared__ uint32_t s_ticket, s_base;
+    __shared__ uint32_t s_item_off[kDistTile];
     __shared__ int64_t s_item_lo[kDistTile];
+    const int b = static_cast<int>(blockIdx.x);
+    const int sg = find_sub(a, b);
+    const DistSub &S = a.sub[sg];
+    const int64_t F = load_count(S.d_F, S.F_cap);
+    const int64_t live = (F + kDistTile - 1) / kDistTile;
+    if (b - S.tile0 >= (live > 0 ? live : 1)) return;
     const int64_t n1 = a.mark_words ? load_count(a.d_U1, a.U1_cap) : 0;   // |U_{l+1}|
-    for (int t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
-        const int sg = find_sub(a, t);
-        const DistSub &S = a.sub[sg];
-        const int lt = t - S.tile0;
-        const int64_t F = load_count(S.d_F, S.F_cap);
-        // tiles past the actual destinations have nothing to place (tile 0 still writes the totals)
-        const int live = static_cast<int>((F + kDistTile - 1) / kDistTile);
-        if (lt > 0 && lt >= live) continue;
-        // the sums of the earlier tiles (tile 0: of all tiles, for the sub-batch's total)
-        uint32_t before = 0, all = 0;
-        const int upto = lt == 0 ? live : lt;
-        for (int b = threadIdx.x; b < upto; b += blockDim.x) {
-            const uint32_t x = a.bsum[S.tile0 + b];
-            all += x;
-            if (b < lt) before += x;
+    const int64_t lt = lb_ticket(a.lb.ticket + sg, &s_ticket);
+    const int lane = lane_id();
+    const int wv = static_cast<int>(threadIdx.x >> 6);
+    const int64_t i = lt * kDistTile + threadIdx.x;
+    int64_t lo = 0;
+    int32_t c = 0, np, r;
+    if (i < F) {
+        union_row(a, S, i, lo, c, np, r);
+        if (S.f_pos) S.f_pos[i] = np;
+        if (a.mark_words && np >= 0 && np < n1) mark_sub(a, sg, np, a.mark_dup != 0);
+        if (a.inv && r >= 0) {
+            a.inv[static_cast<int64_t>(r) * a.G + sg] = static_cast<int32_t>(i + 1);
+            atomicOr(&a.inv_mask[r], 1u << sg);
         }
-        before = wave_sum(before);
-        all = wave_sum(all);
-        if (lane_id() == 0) {
-            s_red[0][threadIdx.x >> 6] = before;
-            s_red[1][threadIdx.x >> 6] = all;
+    }
+    // the tile's row lengths: offsets within the tile, then the tile's base by look-back
+    const uint32_t inc = wave_inclusive_scan(static_cast<uint32_t>(c));
+    if (lane == 63) s_wave[wv] = inc;
+    __syncthreads();
+    uint32_t wbefore = 0, agg = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+        const uint32_t v = s_wave[q];
+        if (q < wv) wbefore += v;
+        agg += v;
+    }
+    if (wv == 0) {
+        uint64_t *chain = a.lb.words + S.tile0;
+        uint32_t before = 0;
+        if (lt == 0) {
+            if (lane == 0) lb_publish(&chain[0], kLbInclusive, agg);
+        } else {
+            if (lane == 0) lb_publish(&chain[lt], kLbAggregate, agg);
+            before = lb_exclusive(chain, lt);
+            if (lane == 0) lb_publish(&chain[lt], kLbInclusive, before + agg);
         }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t b0 = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
-            const uint32_t tot = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-            s_off = b0;
-            if (lt == 0) {
+        if (lane == 0) {
+            s_base = before;
+            if (lt == (live > 0 ? live - 1 : 0)) {
+                const uint32_t tot = before + agg;
                 S.blk_indptr[F] = static_cast<int32_t>(tot);
                 *S.d_E = tot;
                 if (static_cast<int64_t>(tot) > S.E_cap) set_status(a.status, GNN_ERR_CAPACITY);
             }
         }
-        __syncthreads();
-        if (threadIdx.x < kDistTile) {
-            const int64_t i = static_cast<int64_t>(lt) * kDistTile + threadIdx.x;
-            int64_t lo = 0;
-            int32_t c = 0, np, r;
-            if (i < F) union_row(a, S, i, lo, c, np, r, false);
-            const uint32_t inc = wave_inclusive_scan(static_cast<uint32_t>(c));
-            const uint32_t o = inc - static_cast<uint32_t>(c);
-            s_item_off[threadIdx.x] = o;
-            s_item_lo[threadIdx.x] = lo;
-            if (threadIdx.x == kDistTile - 1) s_tot = inc;
-            if (i < F) S.blk_indptr[i] = static_cast<int32_t>(s_off + o);
+    }
+    const uint32_t o = wbefore + inc - static_cast<uint32_t>(c);
+    s_item_off[threadIdx.x] = o;
+    s_item_lo[threadIdx.x] = lo;
+    __syncthreads();
+    const uint32_t base = s_base;
+    if (i < F) S.blk_indptr[i] = static_cast<int32_t>(base + o);
+    // The tile's sampled ids, U rounds of one per thread at a time so that each round's dependent
+    // loads (the id, then its bitmap word and prefix) are in flight together.
+    constexpr int U = 4;
+    for (uint32_t p0 = threadIdx.x; p0 < agg; p0 += U * kDistTile) {
+        int64_t dst[U], src[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t p = p0 + u * kDistTile;
+            int lo_i = 0, hi_i = kDistTile;  // last destination whose offset is <= p
+            while (hi_i - lo_i > 1) {
+                const int mid = (lo_i + hi_i) >> 1;
+                if (s_item_off[mid] <= p) lo_i = mid;
+                else hi_i = mid;
+            }
+            dst[u] = static_cast<int64_t>(base) + p;
+            src[u] = s_item_lo[lo_i] + (p - s_item_off[lo_i]);
+            ok[u] = p < agg && dst[u] < S.E_cap;
         }
-        __syncthreads();
-        // The tile's sampled ids, U rounds of one per thread at a time so that each round's
-        // dependent loads (the id, then its bitmap word and prefix) are in flight together.
-        const uint32_t tot = s_tot;
-        constexpr int U = 4;
-        for (uint32_t p0 = threadIdx.x; p0 < tot; p0 += U * blockDim.x) {
-            int64_t dst[U], src[U];
-            bool ok[U];
+        int32_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = ok[u] ? a.u_gid[src[u]] : -1;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ok[u]) S.blk_gid[dst[u]] = v[u];
+        if (S.e_pos) {
+            int32_t q[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) q[u] = ok[u] ? next_rank(a, v[u]) : -1;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t p = p0 + u * blockDim.x;
-                int lo_i = 0, hi_i = kDistTile;  // last destination whose offset is <= p
-                while (hi_i - lo_i > 1) {
-                    const int mid = (lo_i + hi_i) >> 1;
-                    if (s_item_off[mid] <= p) lo_i = mid;
-                    else hi_i = mid;
-                }
-                dst[u] = static_cast<int64_t>(s_off) + p;
-                src[u] = s_item_lo[lo_i] + (p - s_item_off[lo_i]);
-                ok[u] = p < tot && dst[u] < S.E_cap;
-            }
-            int32_t v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = ok[u] ? a.u_gid[src[u]] : -1;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (ok[u]) S.blk_gid[dst[u]] = v[u];
-            if (S.e_pos) {
-                int32_t q[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) q[u] = ok[u] ? next_rank(a, v[u]) : -1;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (!ok[u]) continue;
-                    S.e_pos[dst[u]] = q[u];
-                    if (a.mark_words && q[u] >= 0 && q[u] < n1) mark_sub(a, sg, q[u], false);
-                }
+                if (!ok[u]) continue;
+                S.e_pos[dst[u]] = q[u];
+                if (a.mark_words && q[u] >= 0 && q[u] < n1) mark_sub(a, sg, q[u], false);
             }
         }
-        __syncthreads();   // the shared arrays are rewritten by the next tile
     }
 }
 
-constexpr int kDistMaxGrid = 4096;
-
 hipError_t launch_dist(const DistArgs &a, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(a.ntiles < kDistMaxGrid ? a.ntiles : kDistMaxGrid);
-    hipLaunchKernelGGL(k_dist_count, dim3(grid), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_dist_scatter, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_dist, dim3(a.ntiles), dim3(kDistTile), 0, s, a);
     return hipGetLastError();
 }
 

@@ -252,7 +252,7 @@ gnn_status gnn_relabel_workspace_size(int64_t id_bound, size_t *out_bytes);
  * argument checks of gnn_unique_relabel otherwise.
  */
 #define GNN_NOALLOC_MAX_IDS 67108864          /* 2^26 */
-#define GNN_NOALLOC_SCRATCH_BYTES 16842752    /* 16 MiB + 64 KiB */
+#define GNN_NOALLOC_SCRATCH_BYTES 25231360    /* 24 MiB + 64 KiB */
 gnn_status gnn_unique_relabel_noalloc(const int32_t *keep, int64_t n_keep, const int32_t *add,
                                       const int64_t *d_n_add, int64_t n_add, int64_t id_bound,
                                       int32_t *uniq, int64_t cap_uniq, int64_t *d_n_uniq,
