@@ -533,7 +533,25 @@ gnn_status run_sample(const gnn_graph &g, const int32_t *const *seeds_g, const i
     auto F_cap = [&](int gi, int l) { return l == 0 ? n_seeds_g[gi] : outs[gi]->caps.frontier[l]; };
     const bool compact = w.mode == kSuperCompact;
     if (G > 1) GNN_TRY_HIP(launch_fill_u32(w.bitmaps, w.W, 0u, s));
-    if (compact) {
+    // U_0 as the concatenation of the seeds where it fits the level's bound (G times the
+    // per-sub-batch seed bound at most N), else their sorted union.
+    const bool concat0 = compact && static_cast<int64_t>(G) * mc.frontier[0] <= g.num_nodes;
+    if (concat0) {
+        SeedConcatArgs sc{};
+        sc.G = G;
+        sc.off[0] = 0;
+        for (int gi = 0; gi < G; ++gi) {
+            sc.seeds[gi] = seeds_g[gi];
+            sc.off[gi + 1] = sc.off[gi] + n_seeds_g[gi];
+        }
+        sc.U0 = w.U[0];
+        sc.d_U0 = w.d_U;
+        sc.upos = w.upos;
+        sc.P = w.P;
+        sc.bitmap = w.bitmaps;
+        sc.num_nodes = g.num_nodes;
+        GNN_TRY_HIP(launch_seed_concat(sc, s));
+    } else if (compact) {
         // U_0: the union of the seeds, and each seed's position in it.
         RelabelArgs r0 = relabel_args(g, w);
         r0.nlist = G;

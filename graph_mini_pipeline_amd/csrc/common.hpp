@@ -439,6 +439,20 @@ hipError_t launch_relabel(RelabelArgs a, hipStream_t s);
 // Look-back words a launch_relabel call needs in a.lb, besides its nbm ticket counters.
 int64_t relabel_lb_words(const RelabelArgs &a);
 hipError_t launch_dist(const DistArgs &a, hipStream_t s);
+
+// The first union level of a super-batch as the concatenation of its sub-batches' seeds.
+struct SeedConcatArgs {
+    const int32_t *seeds[kMaxGroup];
+    int64_t off[kMaxGroup + 1];   // sub-batch g's seeds go to positions off[g] .. off[g+1] - 1
+    int32_t G;
+    int32_t *U0;                  // [off[G]] out
+    int64_t *d_U0;                // out: off[G]
+    int32_t *upos;                // out: upos[g * P + i] = off[g] + i
+    int64_t P;
+    uint32_t *bitmap;             // node-id bitmap: each valid seed's bit is set
+    int64_t num_nodes;
+};
+hipError_t launch_seed_concat(const SeedConcatArgs &a, hipStream_t s);
 hipError_t launch_gather(const float *table, float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,

@@ -197,6 +197,34 @@ __global__ __launch_bounds__(kDistTile) void k_dist(DistArgs a) {
     }
 }
 
+// The first union level U_0 of a compact super-batch, when the sub-batches' seeds fit its bound
+// as they are: their concatenation, in sub-batch order, instead of their sorted union.  A seed
+// held by several sub-batches appears once per sub-batch, and each copy's row is sampled with
+// the same result (the sample depends only on the node and the hop seed), so every sub-batch
+// gets exactly the rows a sorted union would give it; from U_1 on, the levels are the ranks of
+// the accumulated node-id bitmap as before, into which each seed's bit is set here.  Ids out of
+// range are left unmarked (the classification reports them).
+__global__ __launch_bounds__(256) void k_seed_concat(SeedConcatArgs a) {
+    const int64_t total = a.off[a.G];
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t0 == 0) *a.d_U0 = total;
+    for (int64_t t = t0; t < total; t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        int g = 0;
+        while (g + 1 < a.G && a.off[g + 1] <= t) ++g;
+        const int64_t i = t - a.off[g];
+        const int32_t v = a.seeds[g][i];
+        a.U0[t] = v;
+        a.upos[g * a.P + i] = static_cast<int32_t>(t);
+        if (v >= 0 && v < a.num_nodes) atomicOr(&a.bitmap[v >> 5], 1u << (v & 31));
+    }
+}
+
+hipError_t launch_seed_concat(const SeedConcatArgs &a, hipStream_t s) {
+    const int64_t total = a.off[a.G];
+    hipLaunchKernelGGL(k_seed_concat, dim3(grid_for(total, 256, 1024)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_dist(const DistArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_dist, dim3(a.ntiles), dim3(kDistTile), 0, s, a);
     return hipGetLastError();

@@ -475,6 +475,23 @@ def test_superbatch_single_node_graph_regions(mode):
         compare_with_oracle(outs[g], ref, 8)
 
 
+def test_superbatch_compact_seeds_beyond_the_id_range():
+    # G times the per-sub-batch seed count exceeds the number of nodes, so the first union level
+    # is the sorted union of the seeds rather than their concatenation; sub-batches overlap
+    indptr, indices = H.random_csr(300, 6.0, 41)
+    x = np.random.default_rng(41).standard_normal((300, 16)).astype(np.float32)
+    perm = np.random.default_rng(42).permutation(300).astype(np.int32)
+    parts = [perm[i * 60:i * 60 + 110] for i in range(4)]     # 4 x 110 > 300 ids
+    seeds = np.concatenate(parts)
+    ptr = np.concatenate([[0], np.cumsum([len(p) for p in parts])]).tolist()
+    outs, st = run_minibatch(device_graph(indptr, indices), _store(x), seeds, [5, 3], 4242,
+                             group_ptr=ptr, opts=gm.Options(superbatch="compact"))
+    assert st == gm.GNN_OK
+    for g in range(4):
+        ref = oracle.minibatch(indptr, indices, x, parts[g], [5, 3], 4242)
+        compare_with_oracle(outs[g], ref, 16)
+
+
 class _BothModes(gm.Options):
     def c(self):
         o = super().c()
