@@ -18,7 +18,7 @@ from . import _abi
 from ._abi import (GNN_ERR_CAPACITY, GNN_ERR_HIP, GNN_ERR_INTERNAL, GNN_ERR_INVALID_ARG,  # noqa
                    GNN_ERR_OUT_OF_RANGE, GNN_ERR_UNSUPPORTED, GNN_MAX_HOPS, GNN_OK, GNN_SYNC,
                    GNN_SUPERBATCH_COMPACT, GNN_SUPERBATCH_FULL, GNN_GATHER_BATCHED,
-                   GNN_NOALLOC_MAX_IDS, GNN_NOALLOC_SCRATCH_BYTES, GNN_RELABEL_SORT, GNN_RELABEL_BITMAP,
+                   GNN_NOALLOC_MAX_IDS, GNN_NOALLOC_SCRATCH_BYTES, GNN_RELABEL_SORT, GNN_RELABEL_BITMAP, GNN_SAMPLE_EXACT_RANK,
                    GNN_GATHER_INTERLEAVED,
                    GNN_TIMER_STAGES)
 
@@ -86,6 +86,7 @@ class Options:
     superbatch: str = "auto"    # super-batch relabel: "auto", "full" or "compact"
     gather: str = "auto"        # gather and outermost mean: "auto", "interleaved" or "batched"
     relabel: str = "auto"       # short id lists: "auto", "sort" (whenever eligible) or "bitmap"
+    exact_rank: bool = False    # rank every node's candidates by the full (key, position) order
     d_hits: Optional[torch.Tensor] = None   # int64 [1] device: rows read from the HBM caches
 
     def c(self) -> _abi.gnn_options:
@@ -105,7 +106,7 @@ class Options:
         if self.relabel not in rmodes:
             raise ValueError(f"relabel must be one of {sorted(rmodes)}")
         o.flags = (GNN_SYNC if self.sync else 0) | modes[self.superbatch] | gmodes[self.gather] | \
-            rmodes[self.relabel]
+            rmodes[self.relabel] | (GNN_SAMPLE_EXACT_RANK if self.exact_rank else 0)
         return o
 
 

@@ -20,6 +20,7 @@ GNN_GATHER_INTERLEAVED = 8
 GNN_GATHER_BATCHED = 16
 GNN_RELABEL_SORT = 32
 GNN_RELABEL_BITMAP = 64
+GNN_SAMPLE_EXACT_RANK = 128
 GNN_NOALLOC_MAX_IDS = 1 << 26
 GNN_NOALLOC_SCRATCH_BYTES = (24 << 20) + (64 << 10)
 GNN_DYN_AUTO = 1

@@ -388,6 +388,7 @@ HopArgs hop_args(const gnn_graph &g, int l, const int32_t *front, const int64_t 
     h.hop_seed = hop_seed;
     h.group_max = o.group_max;
     h.wave_max = o.wave_max;
+    h.exact_rank = (o.flags & GNN_SAMPLE_EXACT_RANK) ? 1 : 0;
     h.blk_indptr = blk_indptr;
     h.blk_gid = blk_gid;
     h.E_cap = E_cap;

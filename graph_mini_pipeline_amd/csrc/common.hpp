@@ -220,6 +220,8 @@ struct HopArgs {
     int32_t k;              // fanout
     uint64_t hop_seed;
     int32_t group_max, wave_max;
+    int32_t exact_rank;     // rank every node's candidates by (key, position), skipping the
+                            // ranking by the keys' high words
     int32_t *blk_indptr;    // [F_cap+1]
     int32_t *blk_gid;       // [E_cap]
     int64_t E_cap;

@@ -374,6 +374,24 @@ __device__ __forceinline__ int selected_before(const int32_t *s_pos, int cnt, in
     return r;
 }
 
+// Rank of high word hc among the high words of the cnt candidates (the odd 32-bit halves of the
+// 64-bit keys in s_key): how many are smaller.  Eight per round, as in rank_of.
+__device__ __forceinline__ int rank_hi(const uint64_t *s_key, int cnt, uint32_t hc) {
+    const uint32_t *s_hi = reinterpret_cast<const uint32_t *>(s_key) + 1;
+    constexpr int R = 8;
+    int r = 0;
+    int t = 0;
+    for (; t + R <= cnt; t += R) {
+        uint32_t h[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) h[q] = s_hi[2 * (t + q)];
+#pragma unroll
+        for (int q = 0; q < R; ++q) r += h[q] < hc;
+    }
+    for (; t < cnt; ++t) r += s_hi[2 * t] < hc;
+    return r;
+}
+
 // ---- one random node on G lanes of a wavefront ---------------------------------------------------
 //
 // Control flow is uniform across the G lanes of the group; other groups of the same wavefront may
@@ -402,21 +420,41 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         cnt = 0;
     }
     wave_lds_sync();
-    // Candidates sit in ascending position; keep those of rank < k among (key, pos).
-    int outc = 0;
-    for (int c0 = 0; c0 < cnt; c0 += G) {
-        const int c = c0 + gl;
-        bool sel = false;
-        int32_t jc = 0;
-        if (c < cnt) {
-            const uint64_t kc = s_key[c];
-            jc = s_pos[c];
-            sel = rank_of(s_key, s_pos, cnt, kc, jc) < k;
+    // Candidates sit in ascending position; keep those of rank < k among (key, pos).  First by
+    // the keys' high words alone: the candidates with fewer than k smaller high words include the
+    // k first in (key, pos) order (a candidate of rank < k has fewer than k candidates before it,
+    // and every candidate with a smaller high word is before it), so when there are exactly k of
+    // them they are those k.  More than k means high words tied at the k-th place: the node is
+    // ranked again by (key, pos).  Bit b of sel_bits is this lane's candidate of round b.
+    static_assert((CAP + G - 1) / G <= 32, "selection rounds fit one word");
+    uint32_t sel_bits = 0;
+    int n_sel = k + 1;
+    if (!a.exact_rank) {
+        n_sel = 0;
+        for (int c0 = 0, b = 0; c0 < cnt; c0 += G, ++b) {
+            const int c = c0 + gl;
+            bool sel = false;
+            if (c < cnt) sel = rank_hi(s_key, cnt, static_cast<uint32_t>(s_key[c] >> 32)) < k;
+            n_sel += __popcll(__ballot(sel) & gmask);
+            sel_bits |= static_cast<uint32_t>(sel) << b;
         }
+    }
+    if (n_sel != k) {
+        sel_bits = 0;
+        for (int c0 = 0, b = 0; c0 < cnt; c0 += G, ++b) {
+            const int c = c0 + gl;
+            bool sel = false;
+            if (c < cnt) sel = rank_of(s_key, s_pos, cnt, s_key[c], s_pos[c]) < k;
+            sel_bits |= static_cast<uint32_t>(sel) << b;
+        }
+    }
+    int outc = 0;
+    for (int c0 = 0, b = 0; c0 < cnt; c0 += G, ++b) {
+        const bool sel = (sel_bits >> b) & 1u;
         const uint64_t m = __ballot(sel) & gmask;
         if (sel) {
             const int64_t o = out0 + outc + __popcll(m & below);
-            emit_id(a, o, row[jc]);
+            emit_id(a, o, row[s_pos[c0 + gl]]);
         }
         outc += __popcll(m);
     }

@@ -86,6 +86,11 @@ typedef void *gnn_stream; /* hipStream_t */
 #define GNN_RELABEL_SORT 32u
 #define GNN_RELABEL_BITMAP 64u
 #define GNN_GATHER_BATCHED 16u
+/* How the sampler picks each node's fanout smallest keys among its candidates (results are
+ * identical): by default the candidates are ranked by their keys' high 32 bits, and a node whose
+ * high words tie at the fanout-th place is ranked again by the full (key, position) order;
+ * EXACT_RANK ranks every node by the full order (a check of the default). */
+#define GNN_SAMPLE_EXACT_RANK 128u
 
 /*
  * Graph in CSR form by destination: row v lists the sources u of the edges (u, v), which is the

@@ -51,7 +51,7 @@ def large():
     torch.cuda.empty_cache()
 
 
-def _run(cfg, g, table, order, batches, seed64, mode="auto"):
+def _run(cfg, g, table, order, batches, seed64, mode="auto", exact_rank=False):
     dg = gm.DeviceGraph(cfg.num_nodes, g.indptr, g.indices)
     fs = gm.gnn_feature_store_create(table, cfg.d)
     lo = batches[0] * cfg.batch
@@ -63,7 +63,7 @@ def _run(cfg, g, table, order, batches, seed64, mode="auto"):
     ws = torch.empty(gm.gnn_workspace_size(caps, cfg.num_nodes, len(batches)), dtype=torch.uint8,
                      device="cuda")
     gm.gnn_minibatch(dg, fs, order[lo:hi], ptr, cfg.fanouts, seed64, outs, ws,
-                     gm.Options(superbatch=mode))
+                     gm.Options(superbatch=mode, exact_rank=exact_rank))
     assert gm.gnn_read_device_status(ws) == gm.GNN_OK
     return outs, ptr
 
@@ -164,6 +164,22 @@ def test_large_single_batch(large):
     seeds = order_h[b * cfg.batch:(b + 1) * cfg.batch]
     ref = oracle.minibatch(indptr, indices, x, seeds, cfg.fanouts, seed64, d=cfg.d)
     compare_with_oracle(outs[0], ref, cfg.d)
+
+
+@pytest.mark.parametrize("wl", ["dense", "mid"])
+def test_high_word_ranking_equals_exact_ranking_full_size(request, wl):
+    # one super-batch of 16 (dense) or 8 (mid) sampled with the default selection and with every
+    # node ranked by (key, position): identical blocks for every sub-batch
+    cfg, g, table, order, _ = request.getfixturevalue(wl)
+    G = 16 if wl == "dense" else 8
+    seed64 = gm.gnn_batch_seed(cfg.rng_seed, 3)
+    batches = list(range(3 * G, 4 * G))
+    fast, _ = _run(cfg, g, table, order, batches, seed64)
+    exact, _ = _run(cfg, g, table, order, batches, seed64, exact_rank=True)
+    for a, b in zip(fast, exact):
+        for ha, hb in zip(a.blocks.host(), b.blocks.host()):
+            for u, v in zip(ha, hb):
+                assert np.array_equal(u, v)
 
 
 def _headline_parity(workload, steps, G, rounds, label):

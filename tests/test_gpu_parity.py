@@ -475,6 +475,24 @@ def test_superbatch_single_node_graph_regions(mode):
         compare_with_oracle(outs[g], ref, 8)
 
 
+@pytest.mark.parametrize("fanouts", [[10, 5], [25, 10], [3, 3, 3]])
+def test_high_word_ranking_equals_exact_ranking(tiny, fanouts):
+    # the sampler's default selection (ranks by the keys' high words, full order on a tie at the
+    # fanout-th place) against ranking every node by (key, position); both against the oracle
+    cfg, indptr, indices, x, order = tiny
+    dg = device_graph(indptr, indices)
+    fs = _store(x)
+    seeds = order[:512]
+    fast, st = run_minibatch(dg, fs, seeds, fanouts, 31337)
+    assert st == gm.GNN_OK
+    exact, st = run_minibatch(dg, fs, seeds, fanouts, 31337, opts=gm.Options(exact_rank=True))
+    assert st == gm.GNN_OK
+    for hf, he in zip(fast[0].blocks.host(), exact[0].blocks.host()):
+        for u, v in zip(hf, he):
+            assert np.array_equal(u, v)
+    compare_with_oracle(fast[0], oracle.minibatch(indptr, indices, x, seeds, fanouts, 31337), cfg.d)
+
+
 def test_superbatch_compact_seeds_beyond_the_id_range():
     # G times the per-sub-batch seed count exceeds the number of nodes, so the first union level
     # is the sorted union of the seeds rather than their concatenation; sub-batches overlap
