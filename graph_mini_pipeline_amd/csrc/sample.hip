@@ -77,13 +77,13 @@ __device__ __forceinline__ int64_t class_total(const uint32_t *totals, int32_t c
 // Item `item` of the one-wavefront class, whose nodes sit in one work-list per degree bucket
 // (largest degrees first): the bucket holding the item, then the item's place in it.
 __device__ __forceinline__ int32_t wave_item(const HopArgs &a, int64_t item) {
-    int64_t off = item;
+    uint32_t off = static_cast<uint32_t>(item);   // list positions are below 2^31
     int b = 0;
 #pragma unroll
     for (int q = 0; q < kWaveBuckets - 1; ++q) {
-        const int64_t c = a.totals[3 + q];
+        const uint32_t c = a.totals[3 + q];
         const bool past = b == q && off >= c;
-        off -= past ? c : 0;
+        off -= past ? c : 0u;
         b += past ? 1 : 0;
     }
     return a.lists[static_cast<int64_t>(2 + b) * a.F_cap + off];
