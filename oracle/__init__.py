@@ -25,6 +25,10 @@ at the first update call after at least t_update mini-batches, makes the cache t
 highest positive score (ties: smaller id); after max_refreshes refreshes (0: no limit) nothing more
 is observed or refreshed.
 
+Match and Greedy Reorder (FastGL, "The idea" and "What it costs"): match_positions gives each id's
+position in the previous batch's node list (or -1: read from the store); batch_overlap the full
+pairwise overlap matrix of a group of batches; greedy_order their nearest-overlap-first order.
+
 Every function here is pinned by the CPU tests (published SplitMix64 outputs, brute force on
 hand-built graphs, BFS and dense-matrix special cases, uniformity statistics, exact rationals).
 """
@@ -379,3 +383,46 @@ class DynCache:
         self.since = 0
         self.refreshes += 1
         return True
+
+
+# ---- Match and Greedy Reorder (FastGL: A GPU-Efficient Framework for Accelerating Sampling-Based
+# GNN Training at Large Scale, "The idea" and "What it costs") ------------------------------------
+#
+# Match is result-transparent: a batch's X is gather(table, V_K) whichever rows are copied from the
+# previous batch, so its oracle is gather() above; what Match changes is which rows are read from
+# the store, namely those of V_K^b outside V_K^{b-1}.
+
+def match_positions(ids, prev_ids) -> np.ndarray:
+    """For each id, its position in the previous batch's node list prev_ids, or -1 (a row read from
+    the store).  Written as the definition: a dictionary of prev_ids' positions."""
+    where = {int(v): p for p, v in enumerate(np.asarray(prev_ids).tolist())}
+    return np.array([where.get(int(v), -1) for v in np.asarray(ids).tolist()], dtype=np.int32)
+
+
+def batch_overlap(lists) -> np.ndarray:
+    """The group's full pairwise overlap matrix: entry (a, b) = |L_a ∩ L_b| (|L_a| on the diagonal)."""
+    B = len(lists)
+    sets = [set(np.asarray(l).tolist()) for l in lists]
+    m = np.zeros((B, B), dtype=np.int64)
+    for a in range(B):
+        for b in range(B):
+            m[a, b] = len(sets[a] & sets[b])
+    return m
+
+
+def greedy_order(overlap, first: int = 0) -> List[int]:
+    """Nearest-overlap-first: start with batch `first`; each next batch is the one not yet placed
+    that shares the most nodes with the last placed (ties: the smaller index)."""
+    m = np.asarray(overlap)
+    B = m.shape[0]
+    order = [first]
+    left = [b for b in range(B) if b != first]
+    while left:
+        last = order[-1]
+        best = left[0]
+        for b in left[1:]:
+            if m[last, b] > m[last, best]:
+                best = b
+        order.append(best)
+        left.remove(best)
+    return order
