@@ -410,6 +410,64 @@ def gnn_gather_features(fs: FeatureStore, ids: torch.Tensor, out: torch.Tensor,
     _ok(st, "gnn_gather_features")
 
 
+def gnn_gather_features_match(fs: FeatureStore, ids: torch.Tensor, out: torch.Tensor,
+                              prev_ids: torch.Tensor, prev_x: torch.Tensor, match: torch.Tensor,
+                              d_n: Optional[torch.Tensor] = None,
+                              d_prev_n: Optional[torch.Tensor] = None,
+                              d_matched: Optional[torch.Tensor] = None,
+                              d_hits: Optional[torch.Tensor] = None,
+                              d_status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """gnn_gather_features, with the rows whose ids are in prev_ids (strictly ascending) copied from
+    prev_x (row p = features of prev_ids[p]); match[i] receives p or -1."""
+    _need(ids, torch.int32, "ids")
+    _need(out, torch.float32, "out")
+    _need(prev_ids, torch.int32, "prev_ids")
+    _need(prev_x, torch.float32, "prev_x")
+    _need(match, torch.int32, "match")
+    if out.dim() != 2 or out.shape[0] < ids.numel() or match.numel() < ids.numel():
+        raise ValueError("out: [>= len(ids), ld_out]; match: [>= len(ids)]")
+    if prev_x.dim() != 2 or prev_x.shape[0] < prev_ids.numel():
+        raise ValueError("prev_x: [>= len(prev_ids), ld_prev]")
+    st = lib().gnn_gather_features_match(fs.handle, _ptr(ids), _ptr(d_n), ids.numel(), _ptr(out),
+                                         out.shape[1], _ptr(prev_ids), _ptr(d_prev_n),
+                                         prev_ids.numel(), _ptr(prev_x), prev_x.shape[1],
+                                         _ptr(match), _ptr(d_matched), _ptr(d_hits),
+                                         _ptr(d_status), _stream(stream))
+    _ok(st, "gnn_gather_features_match")
+
+
+def gnn_batch_overlap(lists: Sequence[torch.Tensor], out: torch.Tensor,
+                      counts: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                      stream=None) -> None:
+    """out[a * B + b] = |lists[a] ∩ lists[b]| (device int64 [B * B]); each list strictly ascending,
+    counts[a] (device int64 [1]) its actual length if given, else the whole tensor."""
+    B = len(lists)
+    _need(out, torch.int64, "out")
+    if out.numel() < B * B:
+        raise ValueError("out: [B * B]")
+    for t in lists:
+        _need(t, torch.int32, "lists")
+    ids = (ctypes.c_void_p * B)(*[t.data_ptr() if t.numel() else None for t in lists])
+    dn = None
+    if counts is not None:
+        dn = (ctypes.c_void_p * B)(*[c.data_ptr() if c is not None else None for c in counts])
+    n = (ctypes.c_int64 * B)(*[t.numel() for t in lists])
+    _ok(lib().gnn_batch_overlap(ids, dn, n, B, _ptr(out), _stream(stream)), "gnn_batch_overlap")
+
+
+def gnn_greedy_order(overlap, first: int = 0) -> List[int]:
+    """Nearest-overlap-first order of B batches from their overlap matrix (host array-like B x B)."""
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(overlap, dtype=np.int64))
+    B = m.shape[0]
+    if m.shape != (B, B):
+        raise ValueError("overlap: B x B")
+    order = (ctypes.c_int32 * B)()
+    _ok(lib().gnn_greedy_order(m.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), B, first, order),
+        "gnn_greedy_order")
+    return list(order)
+
+
 def gnn_mean_aggregate(indptr: torch.Tensor, lid: torch.Tensor, src: torch.Tensor, d: int,
                        out: torch.Tensor, d_n_dst: Optional[torch.Tensor] = None,
                        d_status: Optional[torch.Tensor] = None, stream=None) -> None:

@@ -101,6 +101,10 @@ SIGNATURES = {
     "gnn_adjacency_cache_attach": (i32, [vp, P(gnn_graph)]),
     "gnn_adjacency_cache_destroy": (i32, [vp]),
     "gnn_gather_features": (i32, [vp, vp, vp, i64, vp, i64, vp, vp, vp]),
+    "gnn_gather_features_match": (i32, [vp, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp,
+                                        vp, vp]),
+    "gnn_batch_overlap": (i32, [P(vp), P(vp), P(i64), i32, vp, vp]),
+    "gnn_greedy_order": (i32, [P(i64), i32, i32, P(i32)]),
     "gnn_mean_aggregate": (i32, [vp, vp, i64, vp, i64, vp, i64, i64, i64, vp, i64, vp, vp]),
     "gnn_sage_update": (i32, [vp, vp, i64, vp, i64, i64, i64, vp, i64, vp, vp, i64, i32, vp, i64,
                               vp, vp]),

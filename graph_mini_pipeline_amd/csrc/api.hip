@@ -1323,6 +1323,71 @@ gnn_status gnn_gather_features(const gnn_feature_store *fs, const int32_t *ids,
     return dyn_auto_refresh(fs, d_status, s);
 }
 
+gnn_status gnn_gather_features_match(const gnn_feature_store *fs, const int32_t *ids,
+                                     const int64_t *d_n, int64_t n, float *out, int64_t ld_out,
+                                     const int32_t *prev_ids, const int64_t *d_prev_n,
+                                     int64_t prev_n, const float *prev_x, int64_t ld_prev,
+                                     int32_t *match, int64_t *d_matched, int64_t *d_hits,
+                                     int32_t *d_status, gnn_stream stream) {
+    if (!fs || n < 0 || ld_out < fs->d || prev_n < 0 || ld_prev < fs->d) return GNN_ERR_INVALID_ARG;
+    if (n > 0 && (!ids || !out || !match)) return GNN_ERR_INVALID_ARG;
+    if (prev_n > 0 && (!prev_ids || !prev_x)) return GNN_ERR_INVALID_ARG;
+    if (n * fs->d > kFlatMax) return GNN_ERR_UNSUPPORTED;
+    if (fs->dyn != nullptr) return GNN_ERR_UNSUPPORTED;
+    if (fs->cache_rows >= kPrevCodeBound || prev_n >= kPrevCodeBound) return GNN_ERR_UNSUPPORTED;
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const MatchArgs ma{ids, d_n, n, prev_ids, d_prev_n, prev_n, match, d_matched};
+    GNN_TRY_HIP(launch_match(ma, s));
+    GNN_TRY_HIP(launch_gather(fs->table, fs->cache, fs->slot, fs->ld, fs->d, fs->num_nodes, ids,
+                              d_n, n, out, ld_out, d_hits, d_status, s, nullptr, 0.0,
+                              prev_n > 0 ? match : nullptr, prev_x, ld_prev));
+    return GNN_OK;
+}
+
+gnn_status gnn_batch_overlap(const int32_t *const *ids, const int64_t *const *d_n, const int64_t *n,
+                             int32_t B, int64_t *overlap, gnn_stream stream) {
+    if (B < 1 || B > GNN_MAX_GROUP || !ids || !n || !overlap) return GNN_ERR_INVALID_ARG;
+    OverlapArgs a{};
+    a.B = B;
+    for (int l = 0; l < B; ++l) {
+        if (n[l] < 0 || (n[l] > 0 && !ids[l])) return GNN_ERR_INVALID_ARG;
+        a.ids[l] = ids[l];
+        a.d_n[l] = d_n ? d_n[l] : nullptr;
+        a.cap[l] = n[l];
+    }
+    for (int x = 0; x < B; ++x)
+        for (int y = x + 1; y < B; ++y) {
+            a.pa[a.npairs] = static_cast<uint8_t>(x);
+            a.pb[a.npairs] = static_cast<uint8_t>(y);
+            ++a.npairs;
+        }
+    a.out = reinterpret_cast<unsigned long long *>(overlap);
+    if (fault(kFaultLaunch)) return GNN_ERR_HIP;
+    GNN_TRY_HIP(launch_overlap(a, static_cast<hipStream_t>(stream)));
+    return GNN_OK;
+}
+
+gnn_status gnn_greedy_order(const int64_t *overlap, int32_t B, int32_t first, int32_t *order) {
+    if (!overlap || !order || B < 1 || first < 0 || first >= B) return GNN_ERR_INVALID_ARG;
+    std::vector<char> placed(static_cast<size_t>(B), 0);
+    order[0] = first;
+    placed[static_cast<size_t>(first)] = 1;
+    for (int i = 1; i < B; ++i) {
+        const int last = order[i - 1];
+        int best = -1;
+        for (int b = 0; b < B; ++b) {
+            if (placed[static_cast<size_t>(b)]) continue;
+            if (best < 0 || overlap[static_cast<int64_t>(last) * B + b] >
+                                overlap[static_cast<int64_t>(last) * B + best])
+                best = b;
+        }
+        order[i] = best;
+        placed[static_cast<size_t>(best)] = 1;
+    }
+    return GNN_OK;
+}
+
 gnn_status gnn_mean_aggregate(const int32_t *indptr, const int32_t *lid, int64_t n_lid,
                               const int64_t *d_n_dst, int64_t n_dst, const float *src,
                               int64_t ld_src, int64_t n_src, int64_t d, float *out,

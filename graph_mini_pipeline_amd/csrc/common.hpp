@@ -442,6 +442,36 @@ hipError_t launch_relabel(RelabelArgs a, hipStream_t s);
 int64_t relabel_lb_words(const RelabelArgs &a);
 hipError_t launch_dist(const DistArgs &a, hipStream_t s);
 
+// Match: each id's position in the previous batch's (ascending) node list, or -1.  The gather
+// codes such a row past the cache rows, so cache rows and list positions stay below kPrevCode.
+constexpr int32_t kPrevCode = 1 << 30;
+constexpr int64_t kPrevCodeBound = kPrevCode;
+struct MatchArgs {
+    const int32_t *ids;
+    const int64_t *d_n;
+    int64_t n_cap;
+    const int32_t *prev_ids;
+    const int64_t *d_prev_n;
+    int64_t prev_cap;
+    int32_t *match;        // [n_cap] out
+    int64_t *d_matched;    // optional: += rows found
+};
+hipError_t launch_match(const MatchArgs &a, hipStream_t s);
+
+// Overlap matrix of B ascending node lists: pairs (pa[y], pb[y]), pa < pb, one grid row each.
+constexpr int64_t kOverlapChunk = 4096;   // elements of L_a per workgroup
+struct OverlapArgs {
+    const int32_t *ids[kMaxGroup];
+    const int64_t *d_n[kMaxGroup];
+    int64_t cap[kMaxGroup];
+    int32_t B;
+    int32_t npairs;
+    uint8_t pa[kMaxGroup * (kMaxGroup - 1) / 2];
+    uint8_t pb[kMaxGroup * (kMaxGroup - 1) / 2];
+    unsigned long long *out;   // [B * B]
+};
+hipError_t launch_overlap(const OverlapArgs &a, hipStream_t s);
+
 // The first union level of a super-batch as the concatenation of its sub-batches' seeds.
 struct SeedConcatArgs {
     const int32_t *seeds[kMaxGroup];
@@ -459,7 +489,8 @@ hipError_t launch_gather(const float *table, float *cache, const int32_t *slot, 
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
                          int32_t *status, hipStream_t s, const DynObserve *obs = nullptr,
-                         double obs_w = 0.0);
+                         double obs_w = 0.0, const int32_t *match = nullptr,
+                         const float *prev = nullptr, int64_t ld_prev = 0);
 // One sub-batch of a batched gather: out[r] = row ids[r] for r < n (n = *d_n, or n_cap); obs_w:
 // its Dynamic-Cache observation weight.
 struct GatherSeg {

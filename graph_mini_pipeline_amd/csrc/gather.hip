@@ -46,7 +46,15 @@ struct GatherArgs {
     int32_t rpu;  // rows per work unit (<= G; G unless the rows are few and fat)
     DynObserve obs;  // Dynamic-Cache observation (obs.score NULL: none), weight obs_w
     double obs_w;
+    // Match: output row i is row match[i] of prev (stride ld_prev) when match[i] >= 0 (match NULL:
+    // none); such a row has the code -2 - (kPrevCode + match[i])
+    const int32_t *match;
+    const float *prev;
+    int64_t ld_prev;
 };
+
+// Row codes of k_gather_rows: c >= 0 table row c; -1 none; -2 - k cache row k (k < kPrevCode) or
+// row k - kPrevCode of the previous batch's X (Match).
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -67,6 +75,12 @@ __device__ __forceinline__ const float *row_ptr(const float *table, const float 
                                                 int32_t c) {
     return c >= 0 ? table + static_cast<int64_t>(c) * ld
                   : cache + static_cast<int64_t>(-2 - c) * ld;
+}
+__device__ __forceinline__ const float *row_src(const GatherArgs &g, int32_t c) {
+    if (c >= 0) return g.table + static_cast<int64_t>(c) * g.ld;
+    const int32_t k = -2 - c;
+    return k >= kPrevCode ? g.prev + static_cast<int64_t>(k - kPrevCode) * g.ld_prev
+                          : g.cache + static_cast<int64_t>(k) * g.ld;
 }
 
 // A row's chunks held by one lane (CH chunks, G lanes apart) written to a reserved Dynamic-Cache
@@ -115,9 +129,12 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs g) {
                     continue;
                 }
                 const float *src;
-                const int32_t sl = g.slot ? g.slot[v] : -1;
+                const int32_t pm = g.match ? g.match[row] : -1;
+                const int32_t sl = pm < 0 && g.slot ? g.slot[v] : -1;
                 if (g.obs.score && ch == 0) dyn_observe(g.obs, v, sl, g.obs_w);
-                if (sl >= 0) {
+                if (pm >= 0) {
+                    src = g.prev + static_cast<int64_t>(pm) * g.ld_prev;
+                } else if (sl >= 0) {
                     src = g.cache + static_cast<int64_t>(sl) * g.ld;
                     hits += ch == 0;
                 } else {
@@ -187,8 +204,11 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
         if (gl < nb) {
             const int32_t v = g.ids[r0 + gl];
             vid = v;
+            const int32_t pm = !SCAT && g.match ? g.match[r0 + gl] : -1;
             if (v < 0 || v >= g.num_rows) {
                 set_status(g.status, GNN_ERR_OUT_OF_RANGE);
+            } else if (pm >= 0) {
+                mine = -2 - (kPrevCode + pm);
             } else {
                 const int32_t sl = g.slot ? g.slot[v] : -1;
                 if constexpr (!SCAT) {
@@ -232,7 +252,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int32_t c = code_of(r);
-            const float *row = row_ptr(g.table, g.cache, g.ld, c);
+            const float *row = row_src(g, c);
 #pragma unroll
             for (int q = 0; q < CH; ++q)
                 v[r][q] = (r < nb && c != -1 && act[q])
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
                 }
                 const int en = er + R;
                 const int32_t c = code_of(en);
-                const float *row = row_ptr(g.table, g.cache, g.ld, c);
+                const float *row = row_src(g, c);
 #pragma unroll
                 for (int q = 0; q < CH; ++q)
                     v[r][q] = (en < nb && c != -1 && act[q])
@@ -453,10 +473,12 @@ void launch_rows(const GatherArgs &g, int G, int CH, dim3 grid, hipStream_t s) {
 hipError_t launch_gather(const float *table, float *cache, const int32_t *slot, int64_t ld,
                          int64_t d, int64_t num_rows, const int32_t *ids, const int64_t *d_n,
                          int64_t n_cap, float *out, int64_t ld_out, int64_t *d_hits,
-                         int32_t *status, hipStream_t s, const DynObserve *obs, double obs_w) {
+                         int32_t *status, hipStream_t s, const DynObserve *obs, double obs_w,
+                         const int32_t *match, const float *prev, int64_t ld_prev) {
     if (n_cap <= 0 || d <= 0) return hipSuccess;
     const bool v4 = ld % 4 == 0 && ld_out % 4 == 0 && aligned16(table) && aligned16(out) &&
-                    (cache == nullptr || aligned16(cache));
+                    (cache == nullptr || aligned16(cache)) &&
+                    (match == nullptr || (ld_prev % 4 == 0 && aligned16(prev)));
     const int vec = v4 ? 4 : 1;
     const int64_t cpr = (d + vec - 1) / vec;
     GatherArgs g{table, cache, slot, ld, static_cast<int32_t>(d), num_rows, ids, d_n, n_cap,
@@ -466,6 +488,9 @@ hipError_t launch_gather(const float *table, float *cache, const int32_t *slot, 
         g.obs = *obs;
         g.obs_w = obs_w;
     }
+    g.match = match;
+    g.prev = prev;
+    g.ld_prev = ld_prev;
     if (!v4) {
         constexpr int U = 4;
         hipLaunchKernelGGL((k_gather<1, U>), dim3(grid_for(n_cap * cpr, 256 * U, 2048)), dim3(256),

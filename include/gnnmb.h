@@ -370,6 +370,50 @@ gnn_status gnn_gather_features(const gnn_feature_store *fs, const int32_t *ids,
                                int64_t *d_hits, int32_t *d_status, gnn_stream stream);
 
 /*
+ * Match (FastGL: A GPU-Efficient Framework for Accelerating Sampling-Based GNN Training at Large
+ * Scale, "The idea": a new batch's nodes are intersected with the batch still on the GPU and only
+ * the remainder is shipped; "What it costs": only the immediately previous batch is used):
+ * gnn_gather_features with the previous batch's gathered rows as a second source.
+ *   out[i, 0..d) = table row ids[i], bit for bit, for i < n: exactly gnn_gather_features' result.
+ *   A row whose id is prev_ids[p] is copied from prev_x row p instead of being read from the
+ *   store; match[i] receives p, or -1 for a row read from the store.
+ *   prev_ids: device [prev_n] strictly ascending ids (the node lists V_l of gnn_sample_khop and
+ *     gnn_minibatch are), *d_prev_n (device int64, may be NULL) the actual count; prev_x: device
+ *     [prev_n, ld_prev], row p holding the features of prev_ids[p] (the previous batch's X).
+ *   ids need not be sorted; n and d_n as in gnn_gather_features; match: device int32 [n];
+ *   d_matched (device int64, may be NULL) is increased by the number of rows copied from prev_x;
+ *   d_hits as in gnn_gather_features (rows read from the HBM cache).  prev_x must not overlap out.
+ * Errors: GNN_ERR_UNSUPPORTED with a Dynamic-Cache (a copied row is no request to the store) or
+ * when the store's cache rows or prev_n reach 2^30; device errors as gnn_gather_features.
+ */
+gnn_status gnn_gather_features_match(const gnn_feature_store *fs, const int32_t *ids,
+                                     const int64_t *d_n, int64_t n, float *out, int64_t ld_out,
+                                     const int32_t *prev_ids, const int64_t *d_prev_n,
+                                     int64_t prev_n, const float *prev_x, int64_t ld_prev,
+                                     int32_t *match, int64_t *d_matched, int64_t *d_hits,
+                                     int32_t *d_status, gnn_stream stream);
+
+/*
+ * Greedy Reorder, its overlap matrix (FastGL, "What it costs": a full pairwise overlap matrix for
+ * each group of sampled batches): overlap[a * B + b] = |L_a ∩ L_b| for a != b and |L_a| for
+ * a = b, for B node lists L_a = ids[a][0 .. count_a), each strictly ascending; count_a = *d_n[a]
+ * (device int64) when d_n[a] is not NULL, else n[a] (n[a] is always the bound).  ids, d_n, n:
+ * host arrays of B entries (d_n may be NULL: every count is n[a]).  overlap: device int64 [B * B].
+ * 1 <= B <= GNN_MAX_GROUP.  Enqueued on `stream`; no host synchronisation.
+ */
+gnn_status gnn_batch_overlap(const int32_t *const *ids, const int64_t *const *d_n, const int64_t *n,
+                             int32_t B, int64_t *overlap, gnn_stream stream);
+
+/*
+ * Greedy Reorder, the order (FastGL, "The idea": each batch follows the batch it shares the most
+ * with; "What it costs": nearest-overlap-first, not optimal).  Host code: order[0] = first, and
+ * each next batch is the one not yet placed with the largest overlap[last * B + b] (ties: the
+ * smaller b).  overlap: host int64 [B * B] (from gnn_batch_overlap); order: host int32 [B].
+ * Errors: GNN_ERR_INVALID_ARG (B < 1, first outside [0, B), NULL arrays).
+ */
+gnn_status gnn_greedy_order(const int64_t *overlap, int32_t B, int32_t first, int32_t *order);
+
+/*
  * Mean aggregation of one block (GARDEN Sec. II.A eq. (1) with AGGREGATE = mean):
  *   out[i, 0..d) = (1/c_i) * sum_{e in [indptr[i], indptr[i+1])} src[lid[e], 0..d),
  *   c_i = indptr[i+1] - indptr[i]; the zero vector when c_i = 0.  fp32 accumulation in
