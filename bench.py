@@ -159,6 +159,10 @@ def main():
     ap.add_argument("--dyn-t-update", type=int, default=0,
                     help="mini-batches between refreshes (default: one super-batch)")
     ap.add_argument("--dyn-max-refreshes", type=int, default=0)
+    ap.add_argument("--match-window", type=int, default=8,
+                    help="Match + Greedy Reorder region: a window of this many consecutive "
+                         "mini-batches (G = 1), gathered plainly, with Match in sampling order and "
+                         "with Match in greedy order (0 = off; at most 16)")
     ap.add_argument("--adj-cache-gb", type=float, default=0.0,
                     help="with --host-indices: an HBM adjacency cache of this many GB of "
                          "pre-sampled hot rows")
@@ -589,6 +593,10 @@ def main():
     if not args.no_sage:
         result["sage_layer"] = sage_layer(gm, cfg, dg, fs, order, dev)
         progress("GraphSAGE layer timed")
+    if args.match_window > 1:
+        result["match_reorder"] = match_reorder_region(gm, cfg, dg, fs, order, dev,
+                                                       min(args.match_window, 16))
+        progress("Match + Greedy Reorder region done")
     dyn_passes = args.dyn_passes if args.dyn_passes >= 0 else (4 if cfg.host_features else 0)
     if dyn_passes > 0:
         result["dynamic_cache"] = dynamic_cache_region(gm, cfg, args, dg, fs, order, G, steps,
@@ -729,6 +737,92 @@ def dynamic_cache_region(gm, cfg, args, dg, fs, order, G, steps, cache_rows, hot
             "static_miss_recurrence": "fraction of the distinct nodes missed by the static cache "
                                       "in a pass that it also missed in the pass before",
             "note": "one stream; pass r > 0 runs on the Dynamic-Cache as pass r - 1 left it"}
+
+
+def match_reorder_region(gm, cfg, dg, fs, order, dev, B):
+    """FastGL's Match and Greedy Reorder ("The idea", "What it costs") on B consecutive mini-batches
+    of the epoch order, one per call (G = 1): each batch's X gathered plainly, then again with
+    Match (rows the previous batch's X holds are copied from it) in sampling order and in the
+    greedy nearest-overlap-first order of the batches' overlap matrix.  Reports the share of each
+    batch's rows found in its predecessor, the rows read from the store (HBM table or cache; with a
+    host table, the misses of the HBM cache cross the host link), the gather times from HIP events,
+    and whether every X equals the plain one bit for bit."""
+    import numpy as np
+    import torch
+    K = len(cfg.fanouts)
+    N = cfg.num_nodes
+    caps = gm.gnn_capacity(cfg.batch, cfg.fanouts, N)
+    ws = torch.empty(gm.gnn_workspace_size(caps, N), dtype=torch.uint8, device=dev)
+    blocks = []
+    for b in range(B):
+        bl = gm.Blocks(caps)
+        gm.gnn_sample_khop(dg, order[b * cfg.batch:(b + 1) * cfg.batch], cfg.fanouts,
+                           gm.gnn_batch_seed(cfg.rng_seed, b), bl, ws)
+        blocks.append(bl)
+    torch.cuda.synchronize()
+    del ws
+    ids = [bl.nodes[K - 1] for bl in blocks]
+    cnt = [bl.counts[2 * K - 1:2 * K] for bl in blocks]
+    rows = [int(c.item()) for c in cnt]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1)
+
+    ov = torch.empty(B * B, dtype=torch.int64, device=dev)
+    t_ov = min(timed(lambda: gm.gnn_batch_overlap(ids, ov, counts=cnt)) for _ in range(3))
+    M = ov.cpu().numpy().reshape(B, B)
+    t0 = time.perf_counter()
+    greedy = gm.gnn_greedy_order(M, 0)
+    t_greedy = (time.perf_counter() - t0) * 1e3
+    hits = torch.zeros(1, dtype=torch.int64, device=dev)
+    X = [torch.empty(max(caps.nodes[K - 1], 1), cfg.ld, dtype=torch.float32, device=dev)
+         for _ in range(B)]
+    t_plain = sum(timed(lambda i=i: gm.gnn_gather_features(fs, ids[i], X[i], d_n=cnt[i], d_hits=hits))
+                  for i in range(B))
+    hits_plain = int(hits.item())
+
+    def with_match(o):
+        Y = [torch.empty_like(X[0]) for _ in range(B)]
+        match = torch.empty(max(caps.nodes[K - 1], 1), dtype=torch.int32, device=dev)
+        matched = torch.zeros(1, dtype=torch.int64, device=dev)
+        hits.zero_()
+        t = 0.0
+        for j, i in enumerate(o):
+            if j == 0:
+                t += timed(lambda: gm.gnn_gather_features(fs, ids[i], Y[i], d_n=cnt[i], d_hits=hits))
+            else:
+                p = o[j - 1]
+                t += timed(lambda: gm.gnn_gather_features_match(
+                    fs, ids[i], Y[i], ids[p], Y[p], match, d_n=cnt[i], d_prev_n=cnt[p],
+                    d_matched=matched, d_hits=hits))
+        same = all(torch.equal(Y[i][:rows[i], :cfg.d], X[i][:rows[i], :cfg.d]) for i in range(B))
+        m = int(matched.item())
+        follow = sum(rows[i] for i in o[1:])
+        r = {"order": list(o), "rows_found_in_predecessor": m,
+             "share_of_rows_found": m / max(1, follow),
+             "overlap_from_matrix": int(sum(M[o[j - 1], o[j]] for j in range(1, B))),
+             "rows_read_from_store": sum(rows) - m,
+             "gather_ms_per_batch": t / B, "identical_X": bool(same)}
+        if cfg.host_features:
+            r["rows_over_host_link"] = sum(rows) - m - int(hits.item())
+        del Y
+        return r
+
+    seq = with_match(list(range(B)))
+    grd = with_match(greedy)
+    out = {"window": B, "batches": f"0..{B - 1} of the epoch order, batch seed of each index",
+           "rows": sum(rows), "plain_gather_ms_per_batch": t_plain / B,
+           "overlap_matrix_ms": t_ov, "greedy_order_host_ms": t_greedy,
+           "mean_pairwise_share": float((M.sum() - np.trace(M)) / max(1, (B - 1) * sum(rows))),
+           "sampling_order": seq, "greedy_order": grd}
+    if cfg.host_features:
+        out["plain_rows_over_host_link"] = sum(rows) - hits_plain
+    return out
 
 
 def percentiles(stages):
