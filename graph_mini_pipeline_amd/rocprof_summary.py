@@ -41,6 +41,11 @@ KERNEL_SOURCES = {
     "k_rank": "csrc/relabel.hip",
     "k_popc": "csrc/relabel.hip",
     "k_dist": "csrc/superbatch.hip",
+    "k_seed_concat": "csrc/superbatch.hip",
+    "k_relabel_sort": "csrc/relabel.hip",
+    "k_match": "csrc/match.hip",
+    "k_overlap": "csrc/match.hip",
+    "k_dyn": "csrc/dyncache.hip",
     "k_copy_probe": "csrc/probe.hip",
     "k_hash_probe": "csrc/probe.hip",
     "k_fill": "csrc/relabel.hip",
