@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int32_t c = code_of(r);
-            const float *row = row_src(g, c);
+            const float *row = SCAT ? row_ptr(g.table, g.cache, g.ld, c) : row_src(g, c);   // union rows: no Match
 #pragma unroll
             for (int q = 0; q < CH; ++q)
                 v[r][q] = (r < nb && c != -1 && act[q])
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(GatherArgs g) {
                 }
                 const int en = er + R;
                 const int32_t c = code_of(en);
-                const float *row = row_src(g, c);
+                const float *row = SCAT ? row_ptr(g.table, g.cache, g.ld, c) : row_src(g, c);   // union rows: no Match
 #pragma unroll
                 for (int q = 0; q < CH; ++q)
                     v[r][q] = (en < nb && c != -1 && act[q])
