@@ -584,18 +584,23 @@ __device__ __forceinline__ void zero_sub_maps(const HopArgs &a) {
     int64_t bound = *a.zero_da + *a.zero_db;
     bound = bound < 0 ? 0 : (bound > 32 * a.zero_stride ? 32 * a.zero_stride : bound);
     const int64_t words = (bound + 31) >> 5;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    for (int64_t t = t0; t < words * a.zero_g; t += stride) {
-        const int64_t g = t / words;
-        a.zero_words[g * a.zero_stride + (t - g * words)] = 0u;
-    }
-    if (a.zero_bytes != nullptr) {   // 8 words of bytes per bitmap word
-        const int64_t bw = 8 * words;
-        for (int64_t t = t0; t < bw * a.zero_g; t += stride) {
-            const int64_t g = t / bw;
-            a.zero_bytes[g * 8 * a.zero_stride + (t - g * bw)] = 0u;
-        }
+    // The grid's threads in zero_g equal shares, share g clearing sub-batch g's region (one
+    // division per thread, none per store): its bitmap words, and its byte map (32 bytes a word,
+    // two 16-byte stores; each byte map starts 32-byte aligned).
+    const int64_t threads = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    int64_t share = threads / a.zero_g;
+    share = share > 0 ? share : 1;
+    const int64_t g = t / share;
+    if (g >= a.zero_g) return;
+    uint32_t *zw = a.zero_words + g * a.zero_stride;
+    uint4 *zb = a.zero_bytes != nullptr
+                    ? reinterpret_cast<uint4 *>(a.zero_bytes + g * 8 * a.zero_stride)
+                    : nullptr;
+    const int64_t n = zb != nullptr ? 2 * words : words;
+    for (int64_t i = t - g * share; i < n; i += share) {
+        if (i < words) zw[i] = 0u;
+        if (zb != nullptr) zb[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
