@@ -23,10 +23,19 @@
 
 namespace gnnmb {
 
+// Words up to the first 16-byte boundary one at a time, then 16-byte stores, then the tail.
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t *p, int64_t n, uint32_t value) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        p[i] = value;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    int64_t head = static_cast<int64_t>((16u - (reinterpret_cast<uintptr_t>(p) & 15u)) & 15u) / 4;
+    head = head < n ? head : n;
+    if (t0 < head) p[t0] = value;
+    const int64_t nq = (n - head) / 4;
+    uint4 *q = reinterpret_cast<uint4 *>(p + head);
+    const uint4 v = make_uint4(value, value, value, value);
+    for (int64_t i = t0; i < nq; i += stride) q[i] = v;
+    const int64_t done = head + 4 * nq;
+    if (t0 < n - done) p[done + t0] = value;
 }
 
 __global__ __launch_bounds__(256) void k_fill_i32(int32_t *p, int64_t n, int32_t value) {
