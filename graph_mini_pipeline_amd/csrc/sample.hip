@@ -267,16 +267,44 @@ __device__ __forceinline__ bool next_tau(int cnt, int k, int cap, uint32_t &tau,
 
 // ---- candidate collection --------------------------------------------------------------------
 //
+// Lanes of this lane's group below it whose bit is set in the wavefront ballot b (gbelow: those
+// lanes' bits); for a whole-wavefront group, the lane-mask count instruction pair.
+template <int G>
+__device__ __forceinline__ int group_lanes_below(uint64_t b, uint64_t gbelow) {
+    if constexpr (G == 64)
+        return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(b >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
+    else
+        return __popcll(b & gbelow);
+}
+
+// Lanes of this lane's group whose bit is set in the wavefront ballot b (gmask: the group's bits);
+// for two 32-lane groups, the scalar counts of the two halves.
+template <int G>
+__device__ __forceinline__ int group_lanes(uint64_t b, uint64_t gmask) {
+    if constexpr (G == 64) {
+        return __popcll(b);
+    } else if constexpr (G == 32) {
+        const int lo = __popc(static_cast<uint32_t>(b)), hi = __popc(static_cast<uint32_t>(b >> 32));
+        return lane_id() >= 32 ? hi : lo;
+    } else {
+        return __popcll(b & gmask);
+    }
+}
+
 // Keys of positions j = gl, gl + G, ... of a row of length deg (G lanes, lane gl); the ones
 // <= tau are appended, in ascending position, to s_key / s_pos (first CAP kept).  Returns the
 // number of keys <= tau.  Four keys per lane per step (positions j0 + q G + gl, q = 0..3); the
 // position bound is checked only in the tail.  Rows are shorter than 2^31 (checked by the caller).
+// The step's candidates are placed only when some lane of the wavefront has one (a scalar test of
+// the unmasked ballots); each lane's place counts its group's lanes only.
 template <int G, int CAP>
 __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t tau, int gl,
                                              uint64_t gmask, uint64_t below, uint64_t *s_key,
                                              int32_t *s_pos) {
     constexpr int U = 4;
     const uint64_t step = kGamma * static_cast<uint64_t>(G);
+    const uint64_t gbelow = gmask & below;
     uint64_t z = ns + kGamma * static_cast<uint64_t>(gl + 1);
     int cnt = 0;
     const int32_t main_end = deg / (U * G) * (U * G);
@@ -292,18 +320,18 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
         z += step * U;
         uint64_t m[U];
 #pragma unroll
-        for (int q = 0; q < U; ++q) m[q] = __ballot(p[q]) & gmask;
+        for (int q = 0; q < U; ++q) m[q] = __ballot(p[q]);
         if (m[0] | m[1] | m[2] | m[3]) {
 #pragma unroll
             for (int q = 0; q < U; ++q) {
                 if (p[q]) {
-                    const int pos = cnt + __popcll(m[q] & below);
+                    const int pos = cnt + group_lanes_below<G>(m[q], gbelow);
                     if (pos < CAP) {
                         s_key[pos] = key_full(w[q]);
                         s_pos[pos] = j0 + q * G + gl;
                     }
                 }
-                cnt += __popcll(m[q]);
+                cnt += group_lanes<G>(m[q], gmask);
             }
         }
     }
@@ -312,15 +340,15 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
         const uint64_t w = mix64_pre(z);
         z += step;
         const bool p = j < deg && key_high(w) <= tau;
-        const uint64_t m = __ballot(p) & gmask;
+        const uint64_t m = __ballot(p);
         if (p) {
-            const int pos = cnt + __popcll(m & below);
+            const int pos = cnt + group_lanes_below<G>(m, gbelow);
             if (pos < CAP) {
                 s_key[pos] = key_full(w);
                 s_pos[pos] = j;
             }
         }
-        cnt += __popcll(m);
+        cnt += group_lanes<G>(m, gmask);
     }
     return cnt;
 }
