@@ -292,16 +292,25 @@ __device__ __forceinline__ int group_lanes(uint64_t b, uint64_t gmask) {
     }
 }
 
+// A candidate as the lanes' classes keep it while collecting: its key's high word above its
+// position, one 8-byte LDS entry (the full key is formed again from the position only when the
+// high words cannot decide the selection).
+__device__ __forceinline__ uint64_t pack_cand(uint32_t hi, int32_t j) {
+    return (static_cast<uint64_t>(hi) << 32) | static_cast<uint32_t>(j);
+}
+__device__ __forceinline__ int32_t cand_pos(uint64_t e) {
+    return static_cast<int32_t>(static_cast<uint32_t>(e));
+}
+
 // Keys of positions j = gl, gl + G, ... of a row of length deg (G lanes, lane gl); the ones
-// <= tau are appended, in ascending position, to s_key / s_pos (first CAP kept).  Returns the
-// number of keys <= tau.  Four keys per lane per step (positions j0 + q G + gl, q = 0..3); the
-// position bound is checked only in the tail.  Rows are shorter than 2^31 (checked by the caller).
-// The step's candidates are placed only when some lane of the wavefront has one (a scalar test of
-// the unmasked ballots); each lane's place counts its group's lanes only.
+// <= tau are appended, in ascending position, to s_cand (first CAP kept) as packed entries.
+// Returns the number of keys <= tau.  Four keys per lane per step (positions j0 + q G + gl,
+// q = 0..3); the position bound is checked only in the tail.  Rows are shorter than 2^31 (checked
+// by the caller).  The step's candidates are placed only when some lane of the wavefront has one
+// (a scalar test of the unmasked ballots); each lane's place counts its group's lanes only.
 template <int G, int CAP>
 __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t tau, int gl,
-                                             uint64_t gmask, uint64_t below, uint64_t *s_key,
-                                             int32_t *s_pos) {
+                                             uint64_t gmask, uint64_t below, uint64_t *s_cand) {
     constexpr int U = 4;
     const uint64_t step = kGamma * static_cast<uint64_t>(G);
     const uint64_t gbelow = gmask & below;
@@ -310,12 +319,12 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
     const int32_t main_end = deg / (U * G) * (U * G);
     int32_t j0 = 0;
     for (; j0 < main_end; j0 += U * G) {
-        uint64_t w[U];
+        uint32_t h[U];
         bool p[U];
 #pragma unroll
         for (int q = 0; q < U; ++q) {
-            w[q] = mix64_pre(z + step * q);
-            p[q] = key_high(w[q]) <= tau;
+            h[q] = key_high(mix64_pre(z + step * q));
+            p[q] = h[q] <= tau;
         }
         z += step * U;
         uint64_t m[U];
@@ -326,10 +335,7 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
             for (int q = 0; q < U; ++q) {
                 if (p[q]) {
                     const int pos = cnt + group_lanes_below<G>(m[q], gbelow);
-                    if (pos < CAP) {
-                        s_key[pos] = key_full(w[q]);
-                        s_pos[pos] = j0 + q * G + gl;
-                    }
+                    if (pos < CAP) s_cand[pos] = pack_cand(h[q], j0 + q * G + gl);
                 }
                 cnt += group_lanes<G>(m[q], gmask);
             }
@@ -337,16 +343,13 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
     }
     for (; j0 < deg; j0 += G) {
         const int32_t j = j0 + gl;
-        const uint64_t w = mix64_pre(z);
+        const uint32_t h = key_high(mix64_pre(z));
         z += step;
-        const bool p = j < deg && key_high(w) <= tau;
+        const bool p = j < deg && h <= tau;
         const uint64_t m = __ballot(p);
         if (p) {
             const int pos = cnt + group_lanes_below<G>(m, gbelow);
-            if (pos < CAP) {
-                s_key[pos] = key_full(w);
-                s_pos[pos] = j;
-            }
+            if (pos < CAP) s_cand[pos] = pack_cand(h, j);
         }
         cnt += group_lanes<G>(m, gmask);
     }
@@ -403,7 +406,7 @@ __device__ __forceinline__ int selected_before(const int32_t *s_pos, int cnt, in
 }
 
 // Rank of high word hc among the high words of the cnt candidates (the odd 32-bit halves of the
-// 64-bit keys in s_key): how many are smaller.  Eight per round, as in rank_of.
+// packed entries in s_key): how many are smaller.  Eight per round, as in rank_of.
 __device__ __forceinline__ int rank_hi(const uint64_t *s_key, int cnt, uint32_t hc) {
     const uint32_t *s_hi = reinterpret_cast<const uint32_t *>(s_key) + 1;
     constexpr int R = 8;
@@ -440,7 +443,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
     if (fail && gl == 0) set_status(a.status, GNN_ERR_UNSUPPORTED);   // positions are int32
     int cnt = 0;
     for (int it = 0; it < 128 && !fail; ++it) {
-        cnt = collect_lanes<G, CAP>(ns, static_cast<int32_t>(deg), tau, gl, gmask, below, s_key, s_pos);
+        cnt = collect_lanes<G, CAP>(ns, static_cast<int32_t>(deg), tau, gl, gmask, below, s_key);
         if (!next_tau(cnt, k, CAP, tau, lo, hi, has_lo, has_hi, fail)) break;
     }
     if (fail || cnt < k || cnt > CAP) {
@@ -448,12 +451,14 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         cnt = 0;
     }
     wave_lds_sync();
-    // Candidates sit in ascending position; keep those of rank < k among (key, pos).  First by
-    // the keys' high words alone: the candidates with fewer than k smaller high words include the
-    // k first in (key, pos) order (a candidate of rank < k has fewer than k candidates before it,
-    // and every candidate with a smaller high word is before it), so when there are exactly k of
-    // them they are those k.  More than k means high words tied at the k-th place: the node is
-    // ranked again by (key, pos).  Bit b of sel_bits is this lane's candidate of round b.
+    // Candidates sit in ascending position (packed: high word, position); keep those of rank < k
+    // among (key, pos).  First by the keys' high words alone: the candidates with fewer than k
+    // smaller high words include the k first in (key, pos) order (a candidate of rank < k has
+    // fewer than k candidates before it, and every candidate with a smaller high word is before
+    // it), so when there are exactly k of them they are those k.  More than k means high words
+    // tied at the k-th place: the candidates' full keys are formed again from their positions
+    // (into s_key, positions into s_pos) and the node is ranked by (key, pos).  Bit b of sel_bits
+    // is this lane's candidate of round b.
     static_assert((CAP + G - 1) / G <= 32, "selection rounds fit one word");
     uint32_t sel_bits = 0;
     int n_sel = k + 1;
@@ -467,7 +472,17 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
             sel_bits |= static_cast<uint32_t>(sel) << b;
         }
     }
-    if (n_sel != k) {
+    const bool exact = n_sel != k;
+    if (exact) {
+        for (int c0 = 0; c0 < cnt; c0 += G) {   // each lane its own candidates, in place
+            const int c = c0 + gl;
+            if (c < cnt) {
+                const int32_t j = cand_pos(s_key[c]);
+                s_key[c] = key_full(mix64_pre(ns + kGamma * static_cast<uint64_t>(j + 1)));
+                s_pos[c] = j;
+            }
+        }
+        wave_lds_sync();
         sel_bits = 0;
         for (int c0 = 0, b = 0; c0 < cnt; c0 += G, ++b) {
             const int c = c0 + gl;
@@ -482,7 +497,8 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         const uint64_t m = __ballot(sel) & gmask;
         if (sel) {
             const int64_t o = out0 + outc + __popcll(m & below);
-            emit_id(a, o, row[s_pos[c0 + gl]]);
+            const int c = c0 + gl;
+            emit_id(a, o, row[exact ? s_pos[c] : cand_pos(s_key[c])]);
         }
         outc += __popcll(m);
     }
