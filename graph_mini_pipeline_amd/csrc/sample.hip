@@ -292,11 +292,14 @@ __device__ __forceinline__ int group_lanes(uint64_t b, uint64_t gmask) {
     }
 }
 
-// A candidate as the lanes' classes keep it while collecting: its key's high word above its
-// position, one 8-byte LDS entry (the full key is formed again from the position only when the
-// high words cannot decide the selection).
-__device__ __forceinline__ uint64_t pack_cand(uint32_t hi, int32_t j) {
-    return (static_cast<uint64_t>(hi) << 32) | static_cast<uint32_t>(j);
+// A candidate as the lanes' classes keep it while collecting: one 8-byte LDS entry, its key's
+// high word above its position (the full key is formed again from the position only when the
+// high words cannot decide the selection).  Stored as its two 32-bit halves: one paired LDS
+// store, no 64-bit register pair to build.
+__device__ __forceinline__ void put_cand(uint64_t *s_cand, int pos, uint32_t hi, int32_t j) {
+    uint32_t *w = reinterpret_cast<uint32_t *>(s_cand + pos);
+    w[0] = static_cast<uint32_t>(j);
+    w[1] = hi;
 }
 __device__ __forceinline__ int32_t cand_pos(uint64_t e) {
     return static_cast<int32_t>(static_cast<uint32_t>(e));
@@ -335,7 +338,7 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
             for (int q = 0; q < U; ++q) {
                 if (p[q]) {
                     const int pos = cnt + group_lanes_below<G>(m[q], gbelow);
-                    if (pos < CAP) s_cand[pos] = pack_cand(h[q], j0 + q * G + gl);
+                    if (pos < CAP) put_cand(s_cand, pos, h[q], j0 + q * G + gl);
                 }
                 cnt += group_lanes<G>(m[q], gmask);
             }
@@ -349,7 +352,7 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
         const uint64_t m = __ballot(p);
         if (p) {
             const int pos = cnt + group_lanes_below<G>(m, gbelow);
-            if (pos < CAP) s_cand[pos] = pack_cand(h, j);
+            if (pos < CAP) put_cand(s_cand, pos, h, j);
         }
         cnt += group_lanes<G>(m, gmask);
     }
