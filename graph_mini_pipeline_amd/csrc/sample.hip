@@ -267,28 +267,22 @@ __device__ __forceinline__ bool next_tau(int cnt, int k, int cap, uint32_t &tau,
 
 // ---- candidate collection --------------------------------------------------------------------
 //
-// Lanes of this lane's group below it whose bit is set in the wavefront ballot b (gbelow: those
-// lanes' bits); for a whole-wavefront group, the lane-mask count instruction pair.
-template <int G>
-__device__ __forceinline__ int group_lanes_below(uint64_t b, uint64_t gbelow) {
-    if constexpr (G == 64)
-        return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-            static_cast<uint32_t>(b >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
-    else
-        return __popcll(b & gbelow);
+// Set bits of x in the lanes below this one (the lane-mask count instruction pair); with x a
+// ballot restricted to this lane's group, the group's lanes below it.
+__device__ __forceinline__ int lanes_below(uint64_t x) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(x >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(x), 0u)));
 }
 
-// Lanes of this lane's group whose bit is set in the wavefront ballot b (gmask: the group's bits);
-// for two 32-lane groups, the scalar counts of the two halves.
+// Lanes of this lane's group whose bit is set in the wavefront ballot b, given x = b restricted
+// to the group; for two 32-lane groups, the scalar counts of the ballot's two halves.
 template <int G>
-__device__ __forceinline__ int group_lanes(uint64_t b, uint64_t gmask) {
-    if constexpr (G == 64) {
-        return __popcll(b);
-    } else if constexpr (G == 32) {
+__device__ __forceinline__ int group_lanes(uint64_t b, uint64_t x) {
+    if constexpr (G == 32) {
         const int lo = __popc(static_cast<uint32_t>(b)), hi = __popc(static_cast<uint32_t>(b >> 32));
         return lane_id() >= 32 ? hi : lo;
     } else {
-        return __popcll(b & gmask);
+        return __popcll(x);
     }
 }
 
@@ -313,10 +307,9 @@ __device__ __forceinline__ int32_t cand_pos(uint64_t e) {
 // (a scalar test of the unmasked ballots); each lane's place counts its group's lanes only.
 template <int G, int CAP>
 __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t tau, int gl,
-                                             uint64_t gmask, uint64_t below, uint64_t *s_cand) {
+                                             uint64_t gmask, uint64_t *s_cand) {
     constexpr int U = 4;
     const uint64_t step = kGamma * static_cast<uint64_t>(G);
-    const uint64_t gbelow = gmask & below;
     uint64_t z = ns + kGamma * static_cast<uint64_t>(gl + 1);
     int cnt = 0;
     const int32_t main_end = deg / (U * G) * (U * G);
@@ -336,11 +329,12 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
         if (m[0] | m[1] | m[2] | m[3]) {
 #pragma unroll
             for (int q = 0; q < U; ++q) {
+                const uint64_t x = G == 64 ? m[q] : (m[q] & gmask);
                 if (p[q]) {
-                    const int pos = cnt + group_lanes_below<G>(m[q], gbelow);
+                    const int pos = cnt + lanes_below(x);
                     if (pos < CAP) put_cand(s_cand, pos, h[q], j0 + q * G + gl);
                 }
-                cnt += group_lanes<G>(m[q], gmask);
+                cnt += group_lanes<G>(m[q], x);
             }
         }
     }
@@ -350,11 +344,12 @@ __device__ __forceinline__ int collect_lanes(uint64_t ns, int32_t deg, uint32_t 
         z += step;
         const bool p = j < deg && h <= tau;
         const uint64_t m = __ballot(p);
+        const uint64_t x = G == 64 ? m : (m & gmask);
         if (p) {
-            const int pos = cnt + group_lanes_below<G>(m, gbelow);
+            const int pos = cnt + lanes_below(x);
             if (pos < CAP) put_cand(s_cand, pos, h, j);
         }
-        cnt += group_lanes<G>(m, gmask);
+        cnt += group_lanes<G>(m, x);
     }
     return cnt;
 }
@@ -446,7 +441,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
     if (fail && gl == 0) set_status(a.status, GNN_ERR_UNSUPPORTED);   // positions are int32
     int cnt = 0;
     for (int it = 0; it < 128 && !fail; ++it) {
-        cnt = collect_lanes<G, CAP>(ns, static_cast<int32_t>(deg), tau, gl, gmask, below, s_key);
+        cnt = collect_lanes<G, CAP>(ns, static_cast<int32_t>(deg), tau, gl, gmask, s_key);
         if (!next_tau(cnt, k, CAP, tau, lo, hi, has_lo, has_hi, fail)) break;
     }
     if (fail || cnt < k || cnt > CAP) {
