@@ -427,8 +427,7 @@ __device__ __forceinline__ int rank_hi(const uint64_t *s_key, int cnt, uint32_t 
 // be elsewhere.  s_key / s_pos are the group's private LDS candidate arrays of CAP entries.
 template <int G, int CAP>
 __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, uint64_t *s_key,
-                                                  int32_t *s_pos, int gl, uint64_t gmask,
-                                                  uint64_t below) {
+                                                  int32_t *s_pos, int gl, uint64_t gmask) {
     const int k = a.k;
     const int32_t v = a.front[i];
     const int64_t start = row_ptr(a.indptr, a.ib, v);
@@ -494,7 +493,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         const bool sel = (sel_bits >> b) & 1u;
         const uint64_t m = __ballot(sel) & gmask;
         if (sel) {
-            const int64_t o = out0 + outc + __popcll(m & below);
+            const int64_t o = out0 + outc + lanes_below(m);
             const int c = c0 + gl;
             emit_id(a, o, row[exact ? s_pos[c] : cand_pos(s_key[c])]);
         }
@@ -510,7 +509,6 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
     constexpr int CAP = kBlockCap;
     constexpr int U = 4;
     const int lane = lane_id();
-    const uint64_t below = (1ull << lane) - 1ull;
     const int k = a.k;
     const int32_t v = a.front[i];
     const int64_t start = row_ptr(a.indptr, a.ib, v);
@@ -551,7 +549,7 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
 #pragma unroll
                 for (int q = 0; q < U; ++q) {
                     if (p[q]) {
-                        const uint32_t pos = wbase + __popcll(m[q] & below);
+                        const uint32_t pos = wbase + static_cast<uint32_t>(lanes_below(m[q]));
                         if (pos < CAP) {
                             s_key[pos] = key_full(w[q]);
                             s_pos[pos] = j0 + q * NT + static_cast<int32_t>(threadIdx.x);
@@ -572,7 +570,7 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
                 if (lane == 0) wbase = atomicAdd(s_cnt, static_cast<uint32_t>(__popcll(m)));
                 wbase = __shfl(wbase, 0, 64);
                 if (p) {
-                    const uint32_t pos = wbase + __popcll(m & below);
+                    const uint32_t pos = wbase + static_cast<uint32_t>(lanes_below(m));
                     if (pos < CAP) {
                         s_key[pos] = key_full(w);
                         s_pos[pos] = j;
@@ -654,7 +652,6 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
     zero_sub_maps(a);
     const int lane = lane_id();
     const int wv = static_cast<int>(threadIdx.x >> 6);
-    const uint64_t below = (1ull << lane) - 1ull;
     int bid = static_cast<int>(blockIdx.x);
     if (bid < nb_block) {
         const int64_t n = class_total(a.totals, kBlock);
@@ -685,7 +682,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
             const int64_t item = r0 + ((round & 1) ? W - 1 - w : w);
             if (item < n_one)
                 sample_node_lanes<64, kWaveCap>(a, wave_item(a, item), s_key + wv * kWaveCap,
-                                                s_pos + wv * kWaveCap, lane, ~0ull, below);
+                                                s_pos + wv * kWaveCap, lane, ~0ull);
         }
         const int half = lane >> 5;
         const uint64_t hmask = half ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
@@ -695,7 +692,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
                 sample_node_lanes<32, kWaveCap / 2>(a, wave_item(a, item),
                                                     s_key + wv * kWaveCap + half * (kWaveCap / 2),
                                                     s_pos + wv * kWaveCap + half * (kWaveCap / 2),
-                                                    lane & 31, hmask, below);
+                                                    lane & 31, hmask);
         }
         return;
     }
@@ -711,7 +708,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         for (int64_t item = static_cast<int64_t>(bid) * SLOTS + slot; item < n;
              item += static_cast<int64_t>(nb_group) * SLOTS)
             sample_node_lanes<G, kGroupCap>(a, list[item], s_key + slot * kGroupCap,
-                                            s_pos + slot * kGroupCap, lane % G, gmask, below);
+                                            s_pos + slot * kGroupCap, lane % G, gmask);
         return;
     }
     bid -= nb_group;
