@@ -31,12 +31,20 @@ namespace gnnmb {
 
 // Node v's neighbour ids: its row in the HBM adjacency cache when the cache holds it, else its
 // CSR row (HBM, or pinned host memory read in place).
+template <bool ADJ>
 __device__ __forceinline__ const int32_t *adj_row(const HopArgs &a, int32_t v, int64_t start) {
-    if (a.adj_off != nullptr) {
+    if (ADJ && a.adj_off != nullptr) {
         const int64_t o = a.adj_off[v];
         if (o >= 0) return a.adj_rows + o;
     }
     return a.indices + start;
+}
+
+// Entry v of a CSR indptr of IB-byte entries (the sampler is compiled for each width).
+template <int IB>
+__device__ __forceinline__ int64_t row_at(const void *indptr, int64_t v) {
+    if constexpr (IB == 8) return static_cast<const int64_t *>(indptr)[v];
+    else return static_cast<int64_t>(static_cast<const int32_t *>(indptr)[v]);
 }
 
 __device__ __forceinline__ int32_t node_class(int64_t deg, int k, int group_max, int wave_max) {
@@ -425,14 +433,14 @@ __device__ __forceinline__ int rank_hi(const uint64_t *s_key, int cnt, uint32_t 
 //
 // Control flow is uniform across the G lanes of the group; other groups of the same wavefront may
 // be elsewhere.  s_key / s_pos are the group's private LDS candidate arrays of CAP entries.
-template <int G, int CAP>
+template <int G, int CAP, int IB, bool ADJ>
 __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, uint64_t *s_key,
                                                   int32_t *s_pos, int gl, uint64_t gmask) {
     const int k = a.k;
     const int32_t v = a.front[i];
-    const int64_t start = row_ptr(a.indptr, a.ib, v);
-    const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - start;
-    const int32_t *row = adj_row(a, v, start);
+    const int64_t start = row_at<IB>(a.indptr, v);
+    const int64_t deg = row_at<IB>(a.indptr, v + 1) - start;
+    const int32_t *row = adj_row<ADJ>(a, v, start);
     const int64_t out0 = a.blk_indptr[i];
     const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
     uint32_t tau = initial_tau(deg, k), lo = 0, hi = 0;
@@ -503,6 +511,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
 }
 
 // ---- one giant-row node on a whole workgroup -------------------------------------------------------
+template <int IB, bool ADJ>
 __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, uint64_t *s_key,
                                                   int32_t *s_pos, uint32_t *s_cnt) {
     constexpr int NT = kBlockThreads;
@@ -511,9 +520,9 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
     const int lane = lane_id();
     const int k = a.k;
     const int32_t v = a.front[i];
-    const int64_t start = row_ptr(a.indptr, a.ib, v);
-    const int64_t deg64 = row_ptr(a.indptr, a.ib, v + 1) - start;
-    const int32_t *row = adj_row(a, v, start);
+    const int64_t start = row_at<IB>(a.indptr, v);
+    const int64_t deg64 = row_at<IB>(a.indptr, v + 1) - start;
+    const int32_t *row = adj_row<ADJ>(a, v, start);
     const int64_t out0 = a.blk_indptr[i];
     const uint64_t ns = mix64(a.hop_seed ^ static_cast<uint64_t>(static_cast<uint32_t>(v)));
     uint32_t tau = initial_tau(deg64, k), lo = 0, hi = 0;
@@ -644,6 +653,9 @@ __device__ __forceinline__ void zero_sub_maps(const HopArgs &a) {
     }
 }
 
+// Compiled for each indptr width (IB bytes) and for graphs with and without the HBM adjacency
+// cache (ADJ), so that no per-node code tests either.
+template <int IB, bool ADJ>
 __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t nb_block,
                                                          int32_t nb_wave, int32_t nb_group) {
     __shared__ uint64_t s_key[kBlockCap];
@@ -657,7 +669,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int64_t n = class_total(a.totals, kBlock);
         const int32_t *list = a.lists + static_cast<int64_t>(kCatBlock) * a.F_cap;
         for (int64_t item = bid; item < n; item += nb_block)
-            sample_node_block(a, list[item], s_key, s_pos, &s_cnt);
+            sample_node_block<IB, ADJ>(a, list[item], s_key, s_pos, &s_cnt);
         return;
     }
     bid -= nb_block;
@@ -681,7 +693,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         for (int64_t r0 = 0, round = 0; r0 < n_one; r0 += W, ++round) {
             const int64_t item = r0 + ((round & 1) ? W - 1 - w : w);
             if (item < n_one)
-                sample_node_lanes<64, kWaveCap>(a, wave_item(a, item), s_key + wv * kWaveCap,
+                sample_node_lanes<64, kWaveCap, IB, ADJ>(a, wave_item(a, item), s_key + wv * kWaveCap,
                                                 s_pos + wv * kWaveCap, lane, ~0ull);
         }
         const int half = lane >> 5;
@@ -689,7 +701,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         for (int64_t p = w; 2 * p < n_pair; p += W) {
             const int64_t item = n_one + 2 * p + half;
             if (item < n)
-                sample_node_lanes<32, kWaveCap / 2>(a, wave_item(a, item),
+                sample_node_lanes<32, kWaveCap / 2, IB, ADJ>(a, wave_item(a, item),
                                                     s_key + wv * kWaveCap + half * (kWaveCap / 2),
                                                     s_pos + wv * kWaveCap + half * (kWaveCap / 2),
                                                     lane & 31, hmask);
@@ -707,7 +719,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int32_t *list = a.lists + static_cast<int64_t>(kGroup) * a.F_cap;
         for (int64_t item = static_cast<int64_t>(bid) * SLOTS + slot; item < n;
              item += static_cast<int64_t>(nb_group) * SLOTS)
-            sample_node_lanes<G, kGroupCap>(a, list[item], s_key + slot * kGroupCap,
+            sample_node_lanes<G, kGroupCap, IB, ADJ>(a, list[item], s_key + slot * kGroupCap,
                                             s_pos + slot * kGroupCap, lane % G, gmask);
         return;
     }
@@ -719,10 +731,10 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int32_t i = a.lists[t];
         const int32_t v = a.front[i];
         if (v < 0 || v >= a.num_nodes) continue;
-        const int64_t st = row_ptr(a.indptr, a.ib, v);
-        const int64_t deg = row_ptr(a.indptr, a.ib, v + 1) - st;
+        const int64_t st = row_at<IB>(a.indptr, v);
+        const int64_t deg = row_at<IB>(a.indptr, v + 1) - st;
         const int64_t o = a.blk_indptr[i];
-        const int32_t *row = adj_row(a, v, st);
+        const int32_t *row = adj_row<ADJ>(a, v, st);
         for (int64_t j = 0; j < deg; ++j) emit_id(a, o + j, row[j]);
     }
 }
@@ -787,8 +799,15 @@ hipError_t launch_sample(const HopArgs &a, hipStream_t s) {
     const int nb_wave = static_cast<int>(grid_for(F, kWavesPerBlock, 2048));
     const int nb_group = static_cast<int>(grid_for(F, kWavesPerBlock * (64 / kGroupLanes), 1024));
     const int nb_full = static_cast<int>(grid_for(F, kBlockThreads, 256));
-    hipLaunchKernelGGL(k_sample, dim3(nb_block + nb_wave + nb_group + nb_full), dim3(kBlockThreads),
-                       0, s, a, nb_block, nb_wave, nb_group);
+    const dim3 grid(nb_block + nb_wave + nb_group + nb_full);
+    const bool adj = a.adj_off != nullptr;
+    if (a.ib == 8) {
+        if (adj) hipLaunchKernelGGL((k_sample<8, true>), grid, dim3(kBlockThreads), 0, s, a, nb_block, nb_wave, nb_group);
+        else hipLaunchKernelGGL((k_sample<8, false>), grid, dim3(kBlockThreads), 0, s, a, nb_block, nb_wave, nb_group);
+    } else {
+        if (adj) hipLaunchKernelGGL((k_sample<4, true>), grid, dim3(kBlockThreads), 0, s, a, nb_block, nb_wave, nb_group);
+        else hipLaunchKernelGGL((k_sample<4, false>), grid, dim3(kBlockThreads), 0, s, a, nb_block, nb_wave, nb_group);
+    }
     return hipGetLastError();
 }
 
