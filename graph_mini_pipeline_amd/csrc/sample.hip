@@ -210,9 +210,10 @@ constexpr int64_t kMaxRowLength = 0x7FFFFFFFLL;
 // Output e of the block gets neighbour id `id`; with a union bitmap to accumulate (a super-batch
 // relabelled in the union's positions), the id's bit is set too.  The atomic's result is unused,
 // so the store is posted and the lane does not wait for it.
+template <bool MARK>
 __device__ __forceinline__ void emit_id(const HopArgs &a, int64_t e, int32_t id) {
     if (e >= 0 && e < a.E_cap) a.blk_gid[e] = id;
-    if (a.mark != nullptr) {
+    if (MARK) {
         if (id >= 0 && id < a.num_nodes) atomicOr(&a.mark[id >> 5], 1u << (id & 31));
         else set_status(a.status, GNN_ERR_OUT_OF_RANGE);
     }
@@ -433,7 +434,7 @@ __device__ __forceinline__ int rank_hi(const uint64_t *s_key, int cnt, uint32_t 
 //
 // Control flow is uniform across the G lanes of the group; other groups of the same wavefront may
 // be elsewhere.  s_key / s_pos are the group's private LDS candidate arrays of CAP entries.
-template <int G, int CAP, int IB, bool ADJ>
+template <int G, int CAP, int IB, bool ADJ, bool MARK>
 __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, uint64_t *s_key,
                                                   int32_t *s_pos, int gl, uint64_t gmask) {
     const int k = a.k;
@@ -503,7 +504,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
         if (sel) {
             const int64_t o = out0 + outc + lanes_below(m);
             const int c = c0 + gl;
-            emit_id(a, o, row[exact ? s_pos[c] : cand_pos(s_key[c])]);
+            emit_id<MARK>(a, o, row[exact ? s_pos[c] : cand_pos(s_key[c])]);
         }
         outc += __popcll(m);
     }
@@ -511,7 +512,7 @@ __device__ __forceinline__ void sample_node_lanes(const HopArgs &a, int32_t i, u
 }
 
 // ---- one giant-row node on a whole workgroup -------------------------------------------------------
-template <int IB, bool ADJ>
+template <int IB, bool ADJ, bool MARK>
 __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, uint64_t *s_key,
                                                   int32_t *s_pos, uint32_t *s_cnt) {
     constexpr int NT = kBlockThreads;
@@ -609,7 +610,7 @@ __device__ __forceinline__ void sample_node_block(const HopArgs &a, int32_t i, u
     for (int c = threadIdx.x, b = 0; c < cnt; c += NT, ++b) {
         if (!(sel & (1u << b))) continue;
         const int32_t jc = s_pos[c] & 0x7FFFFFFF;
-        emit_id(a, out0 + selected_before(s_pos, cnt, jc), row[jc]);
+        emit_id<MARK>(a, out0 + selected_before(s_pos, cnt, jc), row[jc]);
     }
     __syncthreads();
 }
@@ -653,9 +654,10 @@ __device__ __forceinline__ void zero_sub_maps(const HopArgs &a) {
     }
 }
 
-// Compiled for each indptr width (IB bytes) and for graphs with and without the HBM adjacency
-// cache (ADJ), so that no per-node code tests either.
-template <int IB, bool ADJ>
+// Compiled for each indptr width (IB bytes), for graphs with and without the HBM adjacency cache
+// (ADJ) and for hops with and without a union bitmap to mark (MARK), so that no per-node code
+// tests any of them.
+template <int IB, bool ADJ, bool MARK>
 __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t nb_block,
                                                          int32_t nb_wave, int32_t nb_group) {
     __shared__ uint64_t s_key[kBlockCap];
@@ -669,7 +671,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int64_t n = class_total(a.totals, kBlock);
         const int32_t *list = a.lists + static_cast<int64_t>(kCatBlock) * a.F_cap;
         for (int64_t item = bid; item < n; item += nb_block)
-            sample_node_block<IB, ADJ>(a, list[item], s_key, s_pos, &s_cnt);
+            sample_node_block<IB, ADJ, MARK>(a, list[item], s_key, s_pos, &s_cnt);
         return;
     }
     bid -= nb_block;
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         for (int64_t r0 = 0, round = 0; r0 < n_one; r0 += W, ++round) {
             const int64_t item = r0 + ((round & 1) ? W - 1 - w : w);
             if (item < n_one)
-                sample_node_lanes<64, kWaveCap, IB, ADJ>(a, wave_item(a, item), s_key + wv * kWaveCap,
+                sample_node_lanes<64, kWaveCap, IB, ADJ, MARK>(a, wave_item(a, item), s_key + wv * kWaveCap,
                                                 s_pos + wv * kWaveCap, lane, ~0ull);
         }
         const int half = lane >> 5;
@@ -701,7 +703,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         for (int64_t p = w; 2 * p < n_pair; p += W) {
             const int64_t item = n_one + 2 * p + half;
             if (item < n)
-                sample_node_lanes<32, kWaveCap / 2, IB, ADJ>(a, wave_item(a, item),
+                sample_node_lanes<32, kWaveCap / 2, IB, ADJ, MARK>(a, wave_item(a, item),
                                                     s_key + wv * kWaveCap + half * (kWaveCap / 2),
                                                     s_pos + wv * kWaveCap + half * (kWaveCap / 2),
                                                     lane & 31, hmask);
@@ -719,7 +721,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int32_t *list = a.lists + static_cast<int64_t>(kGroup) * a.F_cap;
         for (int64_t item = static_cast<int64_t>(bid) * SLOTS + slot; item < n;
              item += static_cast<int64_t>(nb_group) * SLOTS)
-            sample_node_lanes<G, kGroupCap, IB, ADJ>(a, list[item], s_key + slot * kGroupCap,
+            sample_node_lanes<G, kGroupCap, IB, ADJ, MARK>(a, list[item], s_key + slot * kGroupCap,
                                             s_pos + slot * kGroupCap, lane % G, gmask);
         return;
     }
@@ -735,7 +737,7 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
         const int64_t deg = row_at<IB>(a.indptr, v + 1) - st;
         const int64_t o = a.blk_indptr[i];
         const int32_t *row = adj_row<ADJ>(a, v, st);
-        for (int64_t j = 0; j < deg; ++j) emit_id(a, o + j, row[j]);
+        for (int64_t j = 0; j < deg; ++j) emit_id<MARK>(a, o + j, row[j]);
     }
 }
 
@@ -800,13 +802,17 @@ hipError_t launch_sample(const HopArgs &a, hipStream_t s) {
     const int nb_group = static_cast<int>(grid_for(F, kWavesPerBlock * (64 / kGroupLanes), 1024));
     const int nb_full = static_cast<int>(grid_for(F, kBlockThreads, 256));
     const dim3 grid(nb_block + nb_wave + nb_group + nb_full);
-    const bool adj = a.adj_off != nullptr;
-    if (a.ib == 8) {
-        if (adj) hipLaunchKernelGGL((k_sample<8, true>), grid, dim3(kBlockThreads), 0, s, a, nb_block, nb_wave, nb_group);
-        else hipLaunchKernelGGL((k_sample<8, false>), grid, dim3(kBlockThreads), 0, s, a, nb_block, nb_wave, nb_group);
-    } else {
-        if (adj) hipLaunchKernelGGL((k_sample<4, true>), grid, dim3(kBlockThreads), 0, s, a, nb_block, nb_wave, nb_group);
-        else hipLaunchKernelGGL((k_sample<4, false>), grid, dim3(kBlockThreads), 0, s, a, nb_block, nb_wave, nb_group);
+    const dim3 block(kBlockThreads);
+    const int shape = (a.ib == 8 ? 4 : 0) | (a.adj_off != nullptr ? 2 : 0) | (a.mark != nullptr ? 1 : 0);
+    switch (shape) {
+    case 0: hipLaunchKernelGGL((k_sample<4, false, false>), grid, block, 0, s, a, nb_block, nb_wave, nb_group); break;
+    case 1: hipLaunchKernelGGL((k_sample<4, false, true>), grid, block, 0, s, a, nb_block, nb_wave, nb_group); break;
+    case 2: hipLaunchKernelGGL((k_sample<4, true, false>), grid, block, 0, s, a, nb_block, nb_wave, nb_group); break;
+    case 3: hipLaunchKernelGGL((k_sample<4, true, true>), grid, block, 0, s, a, nb_block, nb_wave, nb_group); break;
+    case 4: hipLaunchKernelGGL((k_sample<8, false, false>), grid, block, 0, s, a, nb_block, nb_wave, nb_group); break;
+    case 5: hipLaunchKernelGGL((k_sample<8, false, true>), grid, block, 0, s, a, nb_block, nb_wave, nb_group); break;
+    case 6: hipLaunchKernelGGL((k_sample<8, true, false>), grid, block, 0, s, a, nb_block, nb_wave, nb_group); break;
+    default: hipLaunchKernelGGL((k_sample<8, true, true>), grid, block, 0, s, a, nb_block, nb_wave, nb_group); break;
     }
     return hipGetLastError();
 }
