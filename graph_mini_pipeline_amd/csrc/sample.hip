@@ -665,7 +665,9 @@ __global__ __launch_bounds__(kBlockThreads, 8) void k_sample(HopArgs a, int32_t 
     __shared__ uint32_t s_cnt;
     zero_sub_maps(a);
     const int lane = lane_id();
-    const int wv = static_cast<int>(threadIdx.x >> 6);
+    // the wavefront's index as a scalar, so that a whole-wavefront row's bounds, seed and
+    // threshold are computed once in scalar registers rather than by every lane
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     int bid = static_cast<int>(blockIdx.x);
     if (bid < nb_block) {
         const int64_t n = class_total(a.totals, kBlock);
