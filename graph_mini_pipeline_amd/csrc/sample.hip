@@ -284,15 +284,12 @@ __device__ __forceinline__ int lanes_below(uint64_t x) {
 }
 
 // Lanes of this lane's group whose bit is set in the wavefront ballot b, given x = b restricted
-// to the group; for two 32-lane groups, the scalar counts of the ballot's two halves.
+// to the group: a scalar count for a whole-wavefront group, else the population count of x (two
+// count instructions that also add it to the running total).
 template <int G>
 __device__ __forceinline__ int group_lanes(uint64_t b, uint64_t x) {
-    if constexpr (G == 32) {
-        const int lo = __popc(static_cast<uint32_t>(b)), hi = __popc(static_cast<uint32_t>(b >> 32));
-        return lane_id() >= 32 ? hi : lo;
-    } else {
-        return __popcll(x);
-    }
+    if constexpr (G == 64) return __popcll(b);
+    else return __popcll(x);
 }
 
 // A candidate as the lanes' classes keep it while collecting: one 8-byte LDS entry, its key's
