@@ -69,9 +69,6 @@ __device__ __forceinline__ int32_t node_cat(int32_t cls, int64_t deg) {
     b = b < 0 ? 0 : (b >= kWaveBuckets ? kWaveBuckets - 1 : b);
     return 2 + b;
 }
-__device__ __forceinline__ int32_t cat_class(int32_t cat) {
-    return cat == 0 ? kFull : (cat == 1 ? kGroup : (cat == kCatBlock ? kBlock : kWave));
-}
 // Nodes of a class (totals: edges, then the categories' sizes).
 __device__ __forceinline__ int64_t class_total(const uint32_t *totals, int32_t cls) {
     if (cls == kFull) return totals[1];
