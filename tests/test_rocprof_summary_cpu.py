@@ -94,3 +94,13 @@ def test_metrics_summary_averages_per_kernel(tmp_path):
     assert lines["k_sample"][1] == "2" and float(lines["k_sample"][3]) == 65.0   # VALUBusy column
     assert float(lines["k_sage_update"][2]) == 40.0                             # MfmaUtil column
     assert lines["k_sage_update"][3] == "-"
+
+
+def test_source_of_template_instances():
+    """Kernel instances (template arguments, the outer/inner tag) map to the file of their
+    kernel, and a name that no library file defines maps to nothing."""
+    assert rs.source_of("k_sample<8, false, true>") == "csrc/sample.hip"
+    assert rs.source_of("k_sample<4, true, false>") == "csrc/sample.hip"
+    assert rs.source_of("k_mean_v5<32, 1, 4>@outer") == "csrc/aggregate.hip"
+    assert rs.source_of("k_gather_rows<64, 3, 8, true>") == "csrc/gather.hip"
+    assert rs.source_of("Cijk_Ailk_Bljk_SB_MT64x64") is None
